@@ -1,0 +1,385 @@
+/*
+ * kvarn_oracle.c -- plain, slow CPU oracle for the KVarN KV-cache hot path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may load, call or
+ * link this file; only the tests, the smoke check and the CPU-baseline leg of
+ * the benchmark use it.  It shares no code, header, table or constant with the
+ * HIP library.
+ *
+ * What it computes, and where the method is stated:
+ *   - SharpInference issue #180 "Implement KVarN variance-normalized KV-cache
+ *     quantization (2-bit values)", section "Algorithm (per 128-token tile)":
+ *     step 1 Hadamard rotation along the channel dim (orthonormal), step 2
+ *     dual-axis "Sinkhorn" variance normalisation (alternating per-channel /
+ *     per-token std normalisation), step 3 asymmetric RTN (per-channel keys,
+ *     per-token values, group 128), step 4 scales folded at read time,
+ *     preset kvarn_k4v2_g128 (4-bit K / 2-bit V).
+ *   - SharpInference PR #434 "KVarN variance-normalized KV-cache quantization:
+ *     CPU + CUDA (#180)", commit list: channel-major K / token-major V packing
+ *     in 128-token tiles, 2-bit bit packing; "Measured" table: the capacity
+ *     figure that fixes the record size.
+ *
+ * Precision.  Compression is an encoding: the packed codes are decided in
+ * fp32, and both this oracle and the GPU path must make every decision in the
+ * same precision with the same operation order.  So the compressor below is a
+ * literal fp32 program with a fixed order: one IEEE operation per line, no
+ * fused multiply-add (compile with -ffp-contract=off), no reassociation.
+ * The dequantised cache and attention are evaluated in fp64.
+ *
+ * Readings of the pages (the pages give no formulas; these are the plain
+ * readings, listed in the design notes):
+ *   WHT: Sylvester Hadamard, butterfly stages in ascending stride h = 1..d/2,
+ *        then one multiply by fp32(1/sqrt(d)); no random signs (self-inverse).
+ *   Sum order: every fp32 sum is a pairwise sum over contiguous halves.
+ *   Sinkhorn: std read as RMS about zero; alternation written as
+ *        Sinkhorn-Knopp scaling of the squared tile X*X to unit row and column
+ *        means (the log-space alternation is the same map without logs);
+ *        8 iterations, channel step then token step; a mean below FLT_MIN
+ *        (all-zero row or column) is replaced by 1.
+ *   RTN: delta = (max-min)/(2^b-1), code = clamp(rint((x-min)*(1/delta))),
+ *        round half to even; delta below FLT_MIN gives all codes 0.
+ */
+#include <float.h>
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define TILE 128 /* tokens per tile */
+
+/* ------------------------------------------------------------------ */
+/* Sizes and record layout (byte offsets inside one tile-head record)   */
+/* ------------------------------------------------------------------ */
+
+static int valid_dim(int d) { return d == 128 || d == 256 || d == 512; }
+
+long long oracle_tile_bytes(int d) {
+  if (!valid_dim(d)) return 0;
+  return 116LL * d + 512;
+}
+
+/* offsets: K codes, V codes, ktok, kscale, kmin, vchan, vscale, vmin, end */
+static void layout(int d, long long off[9]) {
+  off[0] = 0;                 /* K codes  uint8[d][64]         */
+  off[1] = 64LL * d;          /* V codes  uint8[128][d/4]      */
+  off[2] = 96LL * d;          /* ktok     f32[128]             */
+  off[3] = 96LL * d + 512;    /* kscale   f32[d]               */
+  off[4] = 100LL * d + 512;   /* kmin     f32[d]               */
+  off[5] = 104LL * d + 512;   /* vchan    f32[d]               */
+  off[6] = 108LL * d + 512;   /* vscale   f32[128][d/128]      */
+  off[7] = 112LL * d + 512;   /* vmin     f32[128][d/128]      */
+  off[8] = 116LL * d + 512;   /* end                           */
+}
+
+void oracle_layout(int d, long long* off) { layout(d, off); }
+
+/* ------------------------------------------------------------------ */
+/* Walsh-Hadamard transform (fp32, fixed order)                         */
+/* ------------------------------------------------------------------ */
+
+/* fp32(1/sqrt(d)) for d = 2^k: 2^(-k/2) exactly when k is even, otherwise
+ * fp32(sqrt(2)) * 2^(-(k+1)/2), which is exact scaling of the rounded sqrt(2)
+ * and therefore the correctly rounded value of 2^(-k/2). */
+float oracle_wht_scale(int d) {
+  int k = 0;
+  while ((1 << k) < d) k++;
+  if ((k & 1) == 0) return ldexpf(1.0f, -k / 2);
+  return ldexpf(0x1.6a09e6p+0f, -(k + 1) / 2);
+}
+
+void oracle_wht_f32(float* x, int d) {
+  for (int h = 1; h < d; h <<= 1) {
+    for (int i = 0; i < d; i++) {
+      if ((i & h) == 0) {
+        float a = x[i];
+        float b = x[i + h];
+        x[i] = a + b;
+        x[i + h] = a - b;
+      }
+    }
+  }
+  float c = oracle_wht_scale(d);
+  for (int i = 0; i < d; i++) x[i] = x[i] * c;
+}
+
+/* ------------------------------------------------------------------ */
+/* Pairwise sum over contiguous halves (n a power of two)               */
+/* ------------------------------------------------------------------ */
+
+float oracle_pairwise_sum_f32(const float* y, int n) {
+  if (n == 1) return y[0];
+  float left = oracle_pairwise_sum_f32(y, n / 2);
+  float right = oracle_pairwise_sum_f32(y + n / 2, n / 2);
+  return left + right;
+}
+
+/* ------------------------------------------------------------------ */
+/* Sinkhorn variance normalisation of one rotated tile X[128][d]        */
+/* ------------------------------------------------------------------ */
+
+/* Outputs the per-token spread r[128] and the per-channel spread s[d] such
+ * that X[t][c] / (r[t] * s[c]) has unit mean square along both axes (the
+ * token axis exactly after the last step, the channel axis to convergence). */
+void oracle_sinkhorn_f32(const float* X, int d, int iters, float* r, float* s) {
+  float* Q = (float*)malloc(sizeof(float) * TILE * d);
+  float* buf = (float*)malloc(sizeof(float) * (d > TILE ? d : TILE));
+  float u[TILE];   /* 1 / r^2 */
+  float mt[TILE];  /* token mean squares (r^2) */
+  float* v = (float*)malloc(sizeof(float) * d);   /* 1 / s^2 */
+  float* mc = (float*)malloc(sizeof(float) * d);  /* channel mean squares (s^2) */
+  const float inv_t = 1.0f / (float)TILE; /* exact power of two */
+  const float inv_d = 1.0f / (float)d;    /* exact power of two */
+
+  for (int t = 0; t < TILE; t++)
+    for (int c = 0; c < d; c++) Q[t * d + c] = X[t * d + c] * X[t * d + c];
+  for (int t = 0; t < TILE; t++) { u[t] = 1.0f; mt[t] = 1.0f; }
+  for (int c = 0; c < d; c++) { v[c] = 1.0f; mc[c] = 1.0f; }
+
+  for (int it = 0; it < iters; it++) {
+    /* channel step: mean over tokens of Q * u */
+    for (int c = 0; c < d; c++) {
+      for (int t = 0; t < TILE; t++) buf[t] = Q[t * d + c] * u[t];
+      float m = oracle_pairwise_sum_f32(buf, TILE) * inv_t;
+      if (!(m >= FLT_MIN)) m = 1.0f;
+      mc[c] = m;
+      v[c] = 1.0f / m;
+    }
+    /* token step: mean over channels of Q * v */
+    for (int t = 0; t < TILE; t++) {
+      for (int c = 0; c < d; c++) buf[c] = Q[t * d + c] * v[c];
+      float m = oracle_pairwise_sum_f32(buf, d) * inv_d;
+      if (!(m >= FLT_MIN)) m = 1.0f;
+      mt[t] = m;
+      u[t] = 1.0f / m;
+    }
+  }
+  for (int c = 0; c < d; c++) s[c] = sqrtf(mc[c]);
+  for (int t = 0; t < TILE; t++) r[t] = sqrtf(mt[t]);
+  free(Q); free(buf); free(v); free(mc);
+}
+
+/* Xn[t][c] = (X[t][c] * (1/r[t])) * (1/s[c]) */
+void oracle_normalise_f32(const float* X, int d, const float* r, const float* s,
+                          float* Xn) {
+  for (int t = 0; t < TILE; t++) {
+    float ir = 1.0f / r[t];
+    for (int c = 0; c < d; c++) {
+      float is = 1.0f / s[c];
+      Xn[t * d + c] = (X[t * d + c] * ir) * is;
+    }
+  }
+}
+
+/* ------------------------------------------------------------------ */
+/* Asymmetric round-to-nearest over one group                           */
+/* ------------------------------------------------------------------ */
+
+/* x[i * stride] for i < n; levels = 2^bits - 1.  Writes codes[i * cstride]. */
+void oracle_rtn_group(const float* x, int n, int stride, int levels,
+                      float* lo_out, float* delta_out,
+                      uint8_t* codes, int cstride) {
+  float lo = x[0], hi = x[0];
+  for (int i = 1; i < n; i++) {
+    float e = x[i * stride];
+    if (e < lo) lo = e;
+    if (e > hi) hi = e;
+  }
+  float delta = (hi - lo) / (float)levels;
+  float inv = (delta >= FLT_MIN) ? 1.0f / delta : 0.0f;
+  for (int i = 0; i < n; i++) {
+    float q = (x[i * stride] - lo) * inv;
+    float z = rintf(q); /* round half to even in the default rounding mode */
+    if (!(z >= 0.0f)) z = 0.0f;
+    if (z > (float)levels) z = (float)levels;
+    codes[i * cstride] = (uint8_t)z;
+  }
+  *lo_out = lo;
+  *delta_out = delta;
+}
+
+/* ------------------------------------------------------------------ */
+/* Whole-tile compression into one record                               */
+/* ------------------------------------------------------------------ */
+
+/* Everything the compressor decides for one tile-head, before packing. */
+typedef struct {
+  float rK[TILE], sK[512], rV[TILE], sV[512];
+  float loK[512], dK[512];
+  float loV[TILE * 4], dV[TILE * 4];
+  uint8_t zK[TILE * 512], zV[TILE * 512]; /* [t][c] */
+} tile_parts;
+
+static void compress_one(const float* src, long long tok_stride, int d, int iters,
+                         float* r, float* s, uint8_t* z, float* lo, float* dl,
+                         int is_key) {
+  float* X = (float*)malloc(sizeof(float) * TILE * d);
+  float* Xn = (float*)malloc(sizeof(float) * TILE * d);
+  for (int t = 0; t < TILE; t++) {
+    for (int c = 0; c < d; c++) X[t * d + c] = src[(long long)t * tok_stride + c];
+    oracle_wht_f32(X + t * d, d);
+  }
+  oracle_sinkhorn_f32(X, d, iters, r, s);
+  oracle_normalise_f32(X, d, r, s, Xn);
+  if (is_key) {
+    /* per channel over the tile's 128 tokens, 4 bits */
+    for (int c = 0; c < d; c++)
+      oracle_rtn_group(Xn + c, TILE, d, 15, &lo[c], &dl[c], z + c, d);
+  } else {
+    /* per token over each group of 128 channels, 2 bits */
+    int ng = d / 128;
+    for (int t = 0; t < TILE; t++)
+      for (int g = 0; g < ng; g++)
+        oracle_rtn_group(Xn + t * d + 128 * g, 128, 1, 3, &lo[t * ng + g],
+                         &dl[t * ng + g], z + t * d + 128 * g, 1);
+  }
+  free(X);
+  free(Xn);
+}
+
+static void put_f32(uint8_t* rec, long long off, int i, float v) {
+  memcpy(rec + off + 4LL * i, &v, 4);
+}
+
+/* Compress the K and V tiles of one (tile, kv head).  k and v point at token
+ * 0 channel 0; token t starts tok_stride floats later.  Writes 116*d+512
+ * bytes to rec.  Returns 0 on success, -1 for an unsupported head_dim. */
+int oracle_compress_tile(const float* k, const float* v, long long tok_stride,
+                         int d, int iters, uint8_t* rec) {
+  if (!valid_dim(d)) return -1;
+  tile_parts* P = (tile_parts*)calloc(1, sizeof(tile_parts));
+  compress_one(k, tok_stride, d, iters, P->rK, P->sK, P->zK, P->loK, P->dK, 1);
+  compress_one(v, tok_stride, d, iters, P->rV, P->sV, P->zV, P->loV, P->dV, 0);
+
+  long long off[9];
+  layout(d, off);
+  memset(rec, 0, (size_t)off[8]);
+  /* K codes, channel-major: byte j of channel c = tokens 2j (low), 2j+1 (high) */
+  for (int c = 0; c < d; c++)
+    for (int j = 0; j < TILE / 2; j++)
+      rec[off[0] + 64LL * c + j] =
+          (uint8_t)(P->zK[(2 * j) * d + c] | (P->zK[(2 * j + 1) * d + c] << 4));
+  /* V codes, token-major: byte j of token t = channels 4j+i at bits 2i */
+  for (int t = 0; t < TILE; t++)
+    for (int j = 0; j < d / 4; j++) {
+      int b = 0;
+      for (int i = 0; i < 4; i++) b |= P->zV[t * d + 4 * j + i] << (2 * i);
+      rec[off[1] + (long long)t * (d / 4) + j] = (uint8_t)b;
+    }
+  /* folded scales: single fp32 multiplies */
+  for (int t = 0; t < TILE; t++) put_f32(rec, off[2], t, P->rK[t]);
+  for (int c = 0; c < d; c++) {
+    put_f32(rec, off[3], c, P->dK[c] * P->sK[c]);
+    put_f32(rec, off[4], c, P->loK[c] * P->sK[c]);
+    put_f32(rec, off[5], c, P->sV[c]);
+  }
+  int ng = d / 128;
+  for (int t = 0; t < TILE; t++)
+    for (int g = 0; g < ng; g++) {
+      put_f32(rec, off[6], t * ng + g, P->dV[t * ng + g] * P->rV[t]);
+      put_f32(rec, off[7], t * ng + g, P->loV[t * ng + g] * P->rV[t]);
+    }
+  free(P);
+  return 0;
+}
+
+/* The unpacked codes of a record: zK[t][c] and zV[t][c]. */
+void oracle_unpack_codes(const uint8_t* rec, int d, uint8_t* zK, uint8_t* zV) {
+  long long off[9];
+  layout(d, off);
+  for (int c = 0; c < d; c++)
+    for (int j = 0; j < TILE / 2; j++) {
+      uint8_t b = rec[off[0] + 64LL * c + j];
+      zK[(2 * j) * d + c] = b & 15;
+      zK[(2 * j + 1) * d + c] = b >> 4;
+    }
+  for (int t = 0; t < TILE; t++)
+    for (int c = 0; c < d; c++) {
+      uint8_t b = rec[off[1] + (long long)t * (d / 4) + c / 4];
+      zV[t * d + c] = (b >> (2 * (c % 4))) & 3;
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* Dequantised cache in fp64                                            */
+/* ------------------------------------------------------------------ */
+
+static double get_f32(const uint8_t* rec, long long off, int i) {
+  float v;
+  memcpy(&v, rec + off + 4LL * i, 4);
+  return (double)v;
+}
+
+/* H[i][j] = (-1)^popcount(i & j) / sqrt(d), applied to one fp64 row. */
+static void hadamard_f64(const double* x, double* y, int d) {
+  double c = 1.0 / sqrt((double)d);
+  for (int i = 0; i < d; i++) {
+    double acc = 0.0;
+    for (int j = 0; j < d; j++) {
+      double h = (__builtin_popcount((unsigned)(i & j)) & 1) ? -1.0 : 1.0;
+      acc += h * x[j];
+    }
+    y[i] = acc * c;
+  }
+}
+
+/* Dequantise one record to the raw (unrotated) domain:
+ *   k'[t][c] = ktok[t] * (zK[t][c] * kscale[c] + kmin[c])
+ *   v'[t][c] = vchan[c] * (zV[t][c] * vscale[t][g] + vmin[t][g])
+ *   khat = H k', vhat = H v'  (H is its own inverse)
+ * If rotated_only is nonzero the rotation is skipped (k', v' are returned). */
+void oracle_dequant_f64(const uint8_t* rec, int d, int rotated_only,
+                        double* khat, double* vhat) {
+  long long off[9];
+  layout(d, off);
+  uint8_t* zK = (uint8_t*)malloc((size_t)TILE * d);
+  uint8_t* zV = (uint8_t*)malloc((size_t)TILE * d);
+  double* row = (double*)malloc(sizeof(double) * d);
+  oracle_unpack_codes(rec, d, zK, zV);
+  int ng = d / 128;
+  for (int t = 0; t < TILE; t++) {
+    double ktok = get_f32(rec, off[2], t);
+    for (int c = 0; c < d; c++)
+      row[c] = ktok * ((double)zK[t * d + c] * get_f32(rec, off[3], c) +
+                       get_f32(rec, off[4], c));
+    if (rotated_only) memcpy(khat + (long long)t * d, row, sizeof(double) * d);
+    else hadamard_f64(row, khat + (long long)t * d, d);
+    for (int c = 0; c < d; c++) {
+      int g = c / 128;
+      row[c] = get_f32(rec, off[5], c) *
+               ((double)zV[t * d + c] * get_f32(rec, off[6], t * ng + g) +
+                get_f32(rec, off[7], t * ng + g));
+    }
+    if (rotated_only) memcpy(vhat + (long long)t * d, row, sizeof(double) * d);
+    else hadamard_f64(row, vhat + (long long)t * d, d);
+  }
+  free(zK); free(zV); free(row);
+}
+
+/* ------------------------------------------------------------------ */
+/* Textbook softmax attention in fp64                                   */
+/* ------------------------------------------------------------------ */
+
+/* One query over n keys/values (rows of d doubles):
+ *   s_j = scale * (q . k_j),  p = softmax(s),  out = sum_j p_j v_j.
+ * Writes the natural-log LSE of the scaled scores to *lse if non-null. */
+void oracle_attend_f64(const double* q, const double* keys, const double* vals,
+                       long long n, int d, double scale, double* out, double* lse) {
+  double* s = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+  double m = -INFINITY;
+  for (long long j = 0; j < n; j++) {
+    double acc = 0.0;
+    for (int c = 0; c < d; c++) acc += q[c] * keys[j * d + c];
+    s[j] = scale * acc;
+    if (s[j] > m) m = s[j];
+  }
+  double l = 0.0;
+  for (int c = 0; c < d; c++) out[c] = 0.0;
+  for (long long j = 0; j < n; j++) {
+    double p = exp(s[j] - m);
+    l += p;
+    for (int c = 0; c < d; c++) out[c] += p * vals[j * d + c];
+  }
+  for (int c = 0; c < d; c++) out[c] /= l;
+  if (lse) *lse = m + log(l);
+  free(s);
+}

@@ -1,0 +1,404 @@
+"""Pins of the CPU oracle to facts outside itself: closed forms, textbook and
+library special cases, invariants the pages state, and the one numeric figure
+the pages print that fixes the record size.  CPU only."""
+import decimal
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.linalg
+
+import oracle
+from quantized_attention_tok_amd import synth
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+DIMS = [128, 256, 512]
+
+
+# --------------------------------------------------------------------------
+# Walsh-Hadamard rotation (issue #180, Algorithm step 1: orthonormal, so it
+# preserves attention scores)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d", DIMS)
+def test_wht_scale_is_correctly_rounded(d):
+    decimal.getcontext().prec = 60
+    exact = decimal.Decimal(1) / decimal.Decimal(d).sqrt()
+    c = oracle.wht_scale(d)
+    # the neighbours of c in fp32 must both be farther from the exact value
+    up = np.nextafter(c, np.float32(1))
+    dn = np.nextafter(c, np.float32(0))
+    err = abs(decimal.Decimal(float(c)) - exact)
+    assert err <= abs(decimal.Decimal(float(up)) - exact)
+    assert err <= abs(decimal.Decimal(float(dn)) - exact)
+
+
+@pytest.mark.parametrize("d", DIMS)
+def test_hadamard_matches_library(d):
+    H = oracle.hadamard_f64(d)
+    assert np.array_equal(H, scipy.linalg.hadamard(d) / np.sqrt(d))
+    assert np.allclose(H @ H, np.eye(d), atol=1e-13)
+    e0 = np.zeros(d); e0[0] = 1
+    assert np.allclose(H @ e0, np.full(d, 1 / np.sqrt(d)), atol=1e-15)
+
+
+@pytest.mark.parametrize("d", DIMS)
+def test_wht_f32_matches_library_transform(d):
+    rng = np.random.default_rng(d)
+    x = rng.standard_normal((8, d)).astype(np.float32) * 3
+    y = oracle.wht_f32(x)
+    ref = x.astype(np.float64) @ (scipy.linalg.hadamard(d) / np.sqrt(d)).T
+    bound = (math.log2(d) + 2) * np.finfo(np.float32).eps * np.abs(x).sum(1, keepdims=True) / np.sqrt(d)
+    assert np.all(np.abs(y - ref) <= bound)
+
+
+@pytest.mark.parametrize("d", DIMS)
+def test_wht_integer_inputs_single_final_scale(d):
+    # Integer inputs make every butterfly exact, so the result must be the
+    # exact integer transform times c_d with one rounding: this pins a single
+    # scale at the end (not a 1/sqrt(2) per stage).
+    rng = np.random.default_rng(1 + d)
+    x = rng.integers(-50, 50, size=(4, d)).astype(np.float32)
+    exact = (x.astype(np.float64) @ scipy.linalg.hadamard(d).T).astype(np.float32)
+    want = exact * oracle.wht_scale(d)
+    assert np.array_equal(oracle.wht_f32(x), want)
+
+
+@pytest.mark.parametrize("d", DIMS)
+def test_wht_self_inverse_and_preserves_dot(d):
+    rng = np.random.default_rng(7 + d)
+    q = rng.standard_normal(d).astype(np.float32)
+    k = rng.standard_normal(d).astype(np.float32)
+    qq = oracle.wht_f32(oracle.wht_f32(q))
+    assert np.max(np.abs(qq - q)) <= 4 * math.log2(d) * np.finfo(np.float32).eps * np.abs(q).max() * 4
+    dot = float(np.dot(q.astype(np.float64), k))
+    dot_rot = float(np.dot(oracle.wht_f32(q).astype(np.float64), oracle.wht_f32(k)))
+    assert abs(dot - dot_rot) <= 1e-5 * np.linalg.norm(q) * np.linalg.norm(k)
+
+
+# --------------------------------------------------------------------------
+# Pairwise summation order
+# --------------------------------------------------------------------------
+
+def test_pairwise_sum_worked_cases():
+    e = np.float32(2.0 ** -24)
+    # contiguous halves: (1 + e) + (e + e) = 1 + 2^-23 ; a sequential sum gives 1
+    assert oracle.pairwise_sum_f32(np.array([1, e, e, e], np.float32)) == np.float32(1 + 2.0 ** -23)
+    # contiguous halves: (1 + e) + (0 + e) = 1 ; pairing 0 with 2 would give 1 + 2^-23
+    assert oracle.pairwise_sum_f32(np.array([1, e, 0, e], np.float32)) == np.float32(1.0)
+
+
+@pytest.mark.parametrize("n", [128, 256, 512])
+def test_pairwise_sum_error_bound(n):
+    rng = np.random.default_rng(n)
+    y = (rng.standard_normal(n) * np.exp(rng.standard_normal(n) * 2)).astype(np.float32)
+    exact = math.fsum(float(v) for v in y)
+    got = float(oracle.pairwise_sum_f32(y))
+    assert abs(got - exact) <= math.log2(n) * np.finfo(np.float32).eps * np.abs(y.astype(np.float64)).sum()
+
+
+# --------------------------------------------------------------------------
+# Sinkhorn (issue #180, Algorithm step 2: dual-axis alternation of per-channel
+# and per-token std normalisation)
+# --------------------------------------------------------------------------
+
+def _rotated_tile(seed, d, n_out):
+    K, V = synth.make_kv(seed, 128, 1, d, n_out)
+    return oracle.wht_f32(K[:, 0]), oracle.wht_f32(V[:, 0])
+
+
+@pytest.mark.parametrize("d,n_out", [(128, 4), (128, 2), (256, 4), (512, 4)])
+def test_sinkhorn_drives_both_axes_to_unit_spread(d, n_out):
+    for X in _rotated_tile(10 + d + n_out, d, n_out):
+        r, s = oracle.sinkhorn_f32(X, 8)
+        Y = X.astype(np.float64) / (r[:, None].astype(np.float64) * s[None, :])
+        row = np.abs(np.log(np.sqrt(np.mean(Y * Y, axis=1))))
+        col = np.abs(np.log(np.sqrt(np.mean(Y * Y, axis=0))))
+        assert row.max() < 1e-6
+        assert col.max() < 1e-5
+
+
+def test_sinkhorn_converges_geometrically():
+    X, _ = _rotated_tile(3, 128, 2)
+    errs = []
+    for it in (1, 2, 4, 8):
+        r, s = oracle.sinkhorn_f32(X, it)
+        Y = X.astype(np.float64) / (r[:, None].astype(np.float64) * s[None, :])
+        errs.append(np.abs(np.log(np.mean(Y * Y, axis=0))).max())
+    assert errs[0] > errs[1] > errs[2] > errs[3]
+    assert errs[3] < 1e-5
+
+
+@pytest.mark.parametrize("d", DIMS)
+def test_sinkhorn_rank_one_sign_pattern_closed_form(d):
+    # X = u_t v_c eps_tc with eps = +-1 normalises to eps after one iteration:
+    # s_c = v_c sqrt(mean u^2), r_t = u_t / sqrt(mean u^2).
+    rng = np.random.default_rng(d)
+    u = np.exp(rng.standard_normal(128)).astype(np.float32)
+    v = np.exp(rng.standard_normal(d)).astype(np.float32)
+    eps = np.where(rng.random((128, d)) < 0.5, -1.0, 1.0).astype(np.float32)
+    X = (u[:, None] * v[None, :] * eps).astype(np.float32)
+    r, s = oracle.sinkhorn_f32(X, 8)
+    mu = np.sqrt(np.mean(u.astype(np.float64) ** 2))
+    assert np.allclose(s, v * mu, rtol=2e-6)
+    assert np.allclose(r, u / mu, rtol=2e-6)
+    Xn = oracle.normalise_f32(X, r, s)
+    assert np.allclose(Xn, eps, rtol=0, atol=4e-6)
+
+
+def test_sinkhorn_power_of_two_equivariance():
+    # The channel step comes first, so scaling one channel by 2^k scales its
+    # s_c by exactly 2^k and changes no other bit (codes included).
+    X, V = _rotated_tile(5, 128, 4)
+    r, s = oracle.sinkhorn_f32(X, 8)
+    Y = X.copy()
+    Y[:, 17] *= np.float32(8.0)
+    r2, s2 = oracle.sinkhorn_f32(Y, 8)
+    assert s2[17] == s[17] * 8
+    mask = np.ones(128, bool); mask[17] = False
+    assert np.array_equal(s2[mask], s[mask]) and np.array_equal(r2, r)
+    assert np.array_equal(oracle.normalise_f32(Y, r2, s2), oracle.normalise_f32(X, r, s))
+    # A token scaled by 2^k reaches the same normalised tile (the fixed point is
+    # unique up to the r/s gauge), to the fp32 convergence floor.
+    Z = X.copy()
+    Z[40, :] *= np.float32(0.25)
+    r3, s3 = oracle.sinkhorn_f32(Z, 8)
+    assert np.allclose(oracle.normalise_f32(Z, r3, s3), oracle.normalise_f32(X, r, s),
+                       rtol=2e-5, atol=1e-6)
+
+
+@pytest.mark.parametrize("d", [128, 512])
+def test_sinkhorn_matches_independent_fp64_alternation(d):
+    # The literal alternation in fp64: Y <- Y / colrms(Y), then Y <- Y / rowrms(Y),
+    # accumulating the divisors; same fixed point and iterates as the oracle.
+    X, _ = _rotated_tile(21, d, 4)
+    Y = X.astype(np.float64)
+    racc = np.ones(128); sacc = np.ones(d)
+    for _ in range(8):
+        cs = np.sqrt(np.mean(Y * Y, axis=0)); Y /= cs[None, :]; sacc *= cs
+        rs = np.sqrt(np.mean(Y * Y, axis=1)); Y /= rs[:, None]; racc *= rs
+    r, s = oracle.sinkhorn_f32(X, 8)
+    # the oracle reports s from the last channel step alone: the fp64 divisor
+    # product, divided by the token factors common to every channel
+    assert np.allclose(r * s[0], racc * sacc[0], rtol=2e-5)
+    assert np.allclose(s / s[0], sacc / sacc[0], rtol=2e-5)
+    assert np.allclose(np.outer(r, s), np.outer(racc, sacc), rtol=2e-5)
+
+
+def test_sinkhorn_degenerate_zero_column_and_row():
+    X, _ = _rotated_tile(9, 128, 4)
+    X = X.copy()
+    X[:, 5] = 0
+    X[77, :] = 0
+    r, s = oracle.sinkhorn_f32(X, 8)
+    assert np.all(np.isfinite(r)) and np.all(np.isfinite(s))
+    assert s[5] == 1.0 and r[77] == 1.0
+    assert np.all(np.isfinite(oracle.normalise_f32(X, r, s)))
+
+
+# --------------------------------------------------------------------------
+# Asymmetric RTN (issue #180, Algorithm step 3; codes in [0,15] and [0,3])
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_rtn_range_endpoints_and_error_bound(bits):
+    L = (1 << bits) - 1
+    rng = np.random.default_rng(bits)
+    for _ in range(20):
+        x = (rng.standard_normal(128) * rng.exponential()).astype(np.float32)
+        lo, dl, z = oracle.rtn_group(x, bits)
+        assert lo == x.min() and z.min() == 0 and z.max() == L
+        assert z[np.argmin(x)] == 0 and z[np.argmax(x)] == L
+        deq = lo.astype(np.float64) + z * np.float64(dl)
+        assert np.all(np.abs(deq - x) <= dl / 2 * (1 + 1e-5) + 1e-30)
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_rtn_arithmetic_progression_round_trips(bits):
+    L = (1 << bits) - 1
+    lo, step = np.float32(-1.5), np.float32(0.125)
+    k = np.arange(L + 1)
+    x = (lo + k * step).astype(np.float32)
+    glo, dl, z = oracle.rtn_group(np.resize(x, 128), bits)
+    assert glo == lo and dl == step
+    assert np.array_equal(np.unique(z), k)
+
+
+def test_rtn_ties_round_to_even_and_constant_group():
+    x = np.zeros(128, np.float32)
+    x[0], x[1] = 0.0, 15.0    # lo = 0, delta = 1 exactly
+    x[2], x[3], x[4] = 2.5, 3.5, 14.5
+    lo, dl, z = oracle.rtn_group(x, 4)
+    assert dl == 1.0 and (z[2], z[3], z[4]) == (2, 4, 14)
+    lo, dl, z = oracle.rtn_group(np.full(128, 0.75, np.float32), 2)
+    assert lo == np.float32(0.75) and dl == 0 and not z.any()
+
+
+# --------------------------------------------------------------------------
+# Record layout and size (PR #434 commit list: channel-major K, token-major V,
+# 2-bit bit packing; "Measured" table: capacity figure)
+# --------------------------------------------------------------------------
+
+def test_record_size_reproduces_capacity_figure():
+    pin = json.load(open(os.path.join(HERE, "golden", "capacity_pin.json")))
+    d, W = pin["head_dim"], pin["window"]
+    fp32_token = 2 * d * 4
+    budget = pin["fp32_context"] * fp32_token
+    tiles = (budget - W * fp32_token) // oracle.tile_bytes(d)
+    assert tiles * 128 + W == pin["kvarn_context"]
+    # a layout with two more f32 vectors per tile-head would not reproduce it
+    alt = oracle.tile_bytes(d) + 2 * 128 * 4
+    assert ((budget - W * fp32_token) // alt) * 128 + W != pin["kvarn_context"]
+    assert [oracle.tile_bytes(x) for x in DIMS] == [15360, 30208, 59904]
+
+
+@pytest.mark.parametrize("d", DIMS)
+def test_layout_sections_aligned_and_contiguous(d):
+    off = oracle.layout(d)
+    vals = list(off.values())
+    assert vals == sorted(vals) and all(v % 16 == 0 for v in vals)
+    assert off["vcode"] - off["kcode"] == d * 128 // 2
+    assert off["ktok"] - off["vcode"] == d * 128 // 4
+    assert off["end"] == oracle.tile_bytes(d)
+
+
+def test_packing_nibble_and_crumb_order():
+    K, V = synth.make_kv(11, 128, 1, 128, 4)
+    rec = oracle.compress_tile(K[:, 0], V[:, 0])
+    zK, zV = oracle.unpack_codes(rec, 128)
+    off = oracle.layout(128)
+    for c in (0, 3, 127):
+        for j in (0, 5, 63):
+            b = rec[off["kcode"] + 64 * c + j]
+            assert b & 15 == zK[2 * j, c] and b >> 4 == zK[2 * j + 1, c]
+    for t in (0, 64, 127):
+        for j in (0, 9, 31):
+            b = int(rec[off["vcode"] + 32 * t + j])
+            assert [(b >> (2 * i)) & 3 for i in range(4)] == list(zV[t, 4 * j:4 * j + 4])
+    assert zK.max() <= 15 and zV.max() <= 3
+
+
+@pytest.mark.parametrize("d", DIMS)
+def test_codes_match_rtn_of_normalised_tile(d):
+    K, V = synth.make_kv(12 + d, 128, 1, d, 4)
+    rec = oracle.compress_tile(K[:, 0], V[:, 0])
+    zK, zV = oracle.unpack_codes(rec, d)
+    sc = oracle.record_scales(rec, d)
+    X = oracle.wht_f32(K[:, 0])
+    r, s = oracle.sinkhorn_f32(X, 8)
+    Xn = oracle.normalise_f32(X, r, s)
+    for c in (0, d // 3, d - 1):
+        lo, dl, z = oracle.rtn_group(Xn[:, c], 4)
+        assert np.array_equal(z, zK[:, c])
+        assert sc["kscale"][c] == dl * s[c] and sc["kmin"][c] == lo * s[c]
+    assert np.array_equal(sc["ktok"], r)
+    Xv = oracle.wht_f32(V[:, 0])
+    rv, sv = oracle.sinkhorn_f32(Xv, 8)
+    Xvn = oracle.normalise_f32(Xv, rv, sv)
+    for t in (0, 77):
+        for g in range(d // 128):
+            lo, dl, z = oracle.rtn_group(Xvn[t, 128 * g:128 * (g + 1)], 2)
+            assert np.array_equal(z, zV[t, 128 * g:128 * (g + 1)])
+            assert sc["vscale"][t, g] == dl * rv[t] and sc["vmin"][t, g] == lo * rv[t]
+    assert np.array_equal(sc["vchan"], sv)
+
+
+# --------------------------------------------------------------------------
+# Dequantised cache and attention
+# --------------------------------------------------------------------------
+
+def _lossless_tile(d, seed):
+    """Raw K whose rotated tile is u_t v_c eps_tc: it sits on the 4-bit and
+    2-bit grids after normalisation, so compression is exact up to fp32
+    rounding."""
+    rng = np.random.default_rng(seed)
+    u = np.exp(0.5 * rng.standard_normal(128))
+    v = np.exp(rng.standard_normal(d))
+    eps = np.where(rng.random((128, d)) < 0.5, -1.0, 1.0)
+    Xrot = u[:, None] * v[None, :] * eps
+    H = oracle.hadamard_f64(d)
+    return (Xrot @ H.T).astype(np.float32)
+
+
+@pytest.mark.parametrize("d", DIMS)
+def test_lossless_tile_round_trips_through_record(d):
+    K = _lossless_tile(d, 30 + d)
+    V = _lossless_tile(d, 31 + d)
+    rec = oracle.compress_tile(K, V)
+    kh, vh = oracle.dequant(rec, d)
+    assert np.linalg.norm(kh - K) / np.linalg.norm(K) < 2e-5
+    assert np.linalg.norm(vh - V) / np.linalg.norm(V) < 2e-5
+
+
+def test_attention_special_cases_and_lossless_equivalence():
+    d, G = 128, 4
+    rng = np.random.default_rng(5)
+    K = _lossless_tile(d, 40)[:, None, :]
+    V = _lossless_tile(d, 41)[:, None, :]
+    rec = oracle.compress_tile(K[:, 0], V[:, 0])[None, None]
+    kh, vh = oracle.dequant_records(rec, d)
+    q = rng.standard_normal((G, d)).astype(np.float32)
+    empty = np.zeros((0, 1, d), np.float32)
+    tau = 1 / np.sqrt(d)
+    out = oracle.decode(q, kh, vh, 1, empty, empty, tau)
+    # textbook attention on the raw (uncompressed) tile
+    s = tau * (q.astype(np.float64) @ K[:, 0].astype(np.float64).T)
+    p = np.exp(s - s.max(1, keepdims=True)); p /= p.sum(1, keepdims=True)
+    ref = p @ V[:, 0].astype(np.float64)
+    assert np.linalg.norm(out - ref) / np.linalg.norm(ref) < 1e-5
+    # q = 0: plain mean of the visible values
+    out0 = oracle.decode(np.zeros((1, d), np.float32), kh, vh, 1, empty, empty, tau)
+    assert np.allclose(out0[0], vh[:, 0].mean(0), atol=1e-12)
+    # one dominant key
+    qd = (kh[37, 0] * 1e3).astype(np.float32)[None]
+    outd = oracle.decode(qd, kh, vh, 1, empty, empty, tau)
+    assert np.allclose(outd[0], vh[37, 0], atol=1e-9)
+
+
+def test_attention_python_and_c_agree_and_rotated_identity():
+    d = 128
+    K, V = synth.make_kv(13, 256, 1, d, 4)
+    rec = oracle.compress_tile(K[:128, 0], V[:128, 0])
+    kd, vd = oracle.dequant_rotated(rec, d)
+    kh, vh = oracle.dequant(rec, d)
+    rng = np.random.default_rng(0)
+    q = rng.standard_normal(d)
+    H = oracle.hadamard_f64(d)
+    # q . khat == (H q) . k'   (orthogonal rotation; colibri PR #399 review note)
+    assert np.allclose(kh @ q, kd @ (H @ q), rtol=1e-12, atol=1e-12)
+    keys = np.concatenate([kh, K[128:, 0]]); vals = np.concatenate([vh, V[128:, 0]])
+    o1, l1 = oracle.attend(q, keys, vals, 0.1)
+    o2, l2 = oracle.attend_c(q, keys, vals, 0.1)
+    assert np.allclose(o1, o2, rtol=1e-12, atol=1e-14) and abs(l1 - l2) < 1e-12
+    # window-only attention (no tiles) is plain softmax attention on raw K, V
+    empty = np.zeros((0, 1, d))
+    q32 = q.astype(np.float32)
+    out = oracle.decode(q32[None], empty, empty, 0, K[:, :1], V[:, :1], 0.1)
+    s = 0.1 * (K[:, 0].astype(np.float64) @ q32.astype(np.float64))
+    p = np.exp(s - s.max()); p /= p.sum()
+    assert np.allclose(out[0], p @ V[:, 0], rtol=1e-12, atol=1e-14)
+
+
+def test_sinkhorn_reduces_reconstruction_error_on_outlier_keys():
+    # sanity (comparative): normalisation helps per-channel 4-bit keys
+    K, V = synth.make_kv(14, 128, 1, 128, 4)
+    err = []
+    for iters in (0, 8):
+        rec = oracle.compress_tile(K[:, 0], V[:, 0], iters)
+        kh, vh = oracle.dequant(rec, 128)
+        err.append(np.linalg.norm(vh - V[:, 0]) / np.linalg.norm(V[:, 0]))
+    assert err[1] < err[0]
+
+
+def test_visible_tile_rule_fits_the_workloads():
+    # FP32 window of W tokens, promote the oldest 128 when it reaches W + 128
+    assert oracle.visible_tiles(511, 0) == 4                         # tiny: 512 tokens, window 0
+    for total, tiles in [(4096, 30), (15488, 119), (32768, 254)]:
+        assert oracle.visible_tiles(total - 1, 256) == tiles
+        assert total - 128 * tiles == 256
+    # 24 tiles + 256 window + 64 appended tokens: no promotion inside the run
+    assert oracle.visible_tiles(3072 + 256 + 63, 256) == 24
+    assert oracle.visible_tiles(3072 + 256 + 127, 256) == 25
+    assert oracle.visible_tiles(254, 256) == 0
