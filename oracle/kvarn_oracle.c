@@ -37,7 +37,8 @@
  *        8 iterations, channel step then token step; a mean below FLT_MIN
  *        (all-zero row or column) is replaced by 1.
  *   RTN: delta = (max-min)/(2^b-1), code = clamp(rint((x-min)*(1/delta))),
- *        round half to even; delta below FLT_MIN gives all codes 0.
+ *        round half to even; delta below FLT_MIN gives all codes 0; a zero
+ *        min or max is taken as +0.
  */
 #include <float.h>
 #include <math.h>
@@ -184,6 +185,10 @@ void oracle_rtn_group(const float* x, int n, int stride, int levels,
     if (e < lo) lo = e;
     if (e > hi) hi = e;
   }
+  /* -0 and +0 compare equal; adding +0 makes a zero endpoint +0 so the
+   * stored min and step have one bit pattern whatever order found it. */
+  lo = lo + 0.0f;
+  hi = hi + 0.0f;
   float delta = (hi - lo) / (float)levels;
   float inv = (delta >= FLT_MIN) ? 1.0f / delta : 0.0f;
   for (int i = 0; i < n; i++) {

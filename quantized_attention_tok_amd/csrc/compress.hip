@@ -1,0 +1,388 @@
+// compress.hip -- KVarN tile compressor for gfx950.
+//
+// One workgroup compresses the K tile or the V tile of one (tile, KV head):
+// Walsh-Hadamard rotation of every token row, dual-axis Sinkhorn
+// normalisation, asymmetric RTN and packing into the tile record
+// (SharpInference issue #180, "Algorithm (per 128-token tile)" steps 1-4;
+// SharpInference PR #434 commit list: channel-major K / token-major V packing,
+// 2-bit bit packing, codes byte-identical to the CPU compressor).
+//
+// Every value that decides a code is computed with the same fp32 operations in
+// the same order as the CPU oracle, so records are byte-identical:
+//   - WHT butterflies in ascending stride, then one multiply by fp32(1/sqrt(D));
+//   - every sum is a pairwise sum over contiguous halves;
+//   - Sinkhorn is Sinkhorn-Knopp scaling of X*X (channel step, then token step,
+//     8 iterations), means below FLT_MIN replaced by 1;
+//   - IEEE division and square root (HIP's default correctly rounded forms),
+//     round-half-even rint, no fused multiply-add (contraction off below).
+//
+// Thread layout (D = 32*W, W waves, 64*W threads): lane l holds tokens 2l and
+// 2l+1, wave w holds channels [32w, 32w+32); each thread keeps its 2x32 tile
+// values in registers.  Token sums are in-thread trees plus a W-way tree across
+// waves through LDS; channel sums are one in-lane add plus a six-stage
+// cross-lane tree whose first five stages halve the number of live values.
+#include <float.h>
+
+#include "kvarn_launch.h"
+
+#pragma clang fp contract(off)
+
+namespace kvarn {
+namespace {
+
+// Pairwise sum over contiguous halves of p[OFF .. OFF+N).
+template <int N, int OFF, int LEN>
+__device__ __forceinline__ float psum(const float (&p)[LEN]) {
+  if constexpr (N == 1) {
+    return p[OFF];
+  } else {
+    float left = psum<N / 2, OFF, LEN>(p);
+    float right = psum<N / 2, OFF + N / 2, LEN>(p);
+    return left + right;
+  }
+}
+
+struct OpAdd { __device__ float operator()(float a, float b) const { return a + b; } };
+struct OpMin { __device__ float operator()(float a, float b) const { return b < a ? b : a; } };
+struct OpMax { __device__ float operator()(float a, float b) const { return b > a ? b : a; } };
+
+// One halving stage across lanes l and l^M for the first N live values.
+template <int N, int M, typename Op>
+__device__ __forceinline__ void halve_stage(float (&a)[32], int lane, Op op) {
+  const bool up = (lane & M) != 0;
+#pragma unroll
+  for (int i = 0; i < N / 2; ++i) {
+    float send = up ? a[i] : a[i + N / 2];
+    float keep = up ? a[i + N / 2] : a[i];
+    float recv = shfl_xor(send, M);
+    a[i] = op(keep, recv);
+  }
+}
+
+// Combine a[0..32) over all 64 lanes of the wave.  Lane pairs (l, l^1),
+// (l, l^2), ... (l, l^32) are joined in that order, i.e. the pairwise tree over
+// contiguous token blocks when lane l holds tokens 2l, 2l+1.  Returns the
+// value for channel brev5(lane & 31) of the wave's 32.
+template <typename Op>
+__device__ __forceinline__ float halve32(float (&a)[32], int lane, Op op) {
+  halve_stage<32, 1>(a, lane, op);
+  halve_stage<16, 2>(a, lane, op);
+  halve_stage<8, 4>(a, lane, op);
+  halve_stage<4, 8>(a, lane, op);
+  halve_stage<2, 16>(a, lane, op);
+  return op(a[0], shfl_xor(a[0], 32));
+}
+
+__device__ __forceinline__ int brev5(int l) {
+  return ((l & 1) << 4) | ((l & 2) << 2) | (l & 4) | ((l & 8) >> 2) | ((l & 16) >> 4);
+}
+
+__device__ __forceinline__ float code_of(float xn, float lo, float inv, float levels) {
+  float z = __builtin_rintf((xn - lo) * inv);
+  if (!(z >= 0.0f)) z = 0.0f;
+  if (z > levels) z = levels;
+  return z;
+}
+
+template <int D>
+__global__ void __launch_bounds__(2 * D)
+compress_kernel(const float* __restrict__ kin, const float* __restrict__ vin,
+                int64_t tok_stride, int64_t head_stride, int n_kv,
+                uint8_t* __restrict__ records) {
+  constexpr int W = D / 32;        // waves
+  constexpr int J = kTile / W;     // channel offsets per LDS exchange round
+  constexpr bool kStoreQ = D <= 256;
+  using R = Rec<D>;
+
+  __shared__ float smem[16384];    // 64 KB, reused by every phase
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int job = blockIdx.x;
+  const int head = blockIdx.y;
+  const bool is_key = blockIdx.z == 0;
+
+  const float* src = (is_key ? kin : vin) + (int64_t)job * kTile * tok_stride +
+                     (int64_t)head * head_stride;
+  uint8_t* rec = records + ((int64_t)job * n_kv + head) * R::bytes;
+
+  // ---- load rows 2l, 2l+1, channels [32w, 32w+32) ----
+  float x[2][32];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const float4* row = reinterpret_cast<const float4*>(src + (int64_t)(2 * lane + i) * tok_stride + 32 * w);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      float4 f = row[q];
+      x[i][4 * q + 0] = f.x; x[i][4 * q + 1] = f.y; x[i][4 * q + 2] = f.z; x[i][4 * q + 3] = f.w;
+    }
+  }
+
+  // ---- WHT: strides 1..16 inside the thread ----
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+#pragma unroll
+    for (int h = 1; h < 32; h <<= 1) {
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        if ((j & h) == 0) {
+          float a = x[i][j], b = x[i][j + h];
+          x[i][j] = a + b;
+          x[i][j + h] = a - b;
+        }
+      }
+    }
+  }
+  // ---- WHT: strides 32..D/2 across waves, J channel offsets per round ----
+  if constexpr (W > 1) {
+    float* xch = smem;  // [W][128][J]
+    constexpr int kPer = 2 * J / W;  // (token, offset) columns per thread
+#pragma unroll
+    for (int r = 0; r < 32 / J; ++r) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int jj = 0; jj < J; ++jj)
+          xch[(w * kTile + 2 * lane + i) * J + jj] = x[i][r * J + jj];
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) {
+        const int idx = tid * kPer + k;
+        const int t = idx / J, jj = idx % J;
+        float y[W];
+#pragma unroll
+        for (int u = 0; u < W; ++u) y[u] = xch[(u * kTile + t) * J + jj];
+#pragma unroll
+        for (int hs = 1; hs < W; hs <<= 1) {
+#pragma unroll
+          for (int u = 0; u < W; ++u) {
+            if ((u & hs) == 0) {
+              float a = y[u], b = y[u + hs];
+              y[u] = a + b;
+              y[u + hs] = a - b;
+            }
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < W; ++u) xch[(u * kTile + t) * J + jj] = y[u];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int jj = 0; jj < J; ++jj)
+          x[i][r * J + jj] = xch[(w * kTile + 2 * lane + i) * J + jj];
+      __syncthreads();
+    }
+  }
+  {
+    const float c = wht_scale<D>();
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 32; ++j) x[i][j] = x[i][j] * c;
+  }
+
+  // ---- Sinkhorn-Knopp on Q = X*X ----
+  float Qs[kStoreQ ? 2 : 1][kStoreQ ? 32 : 1];
+  if constexpr (kStoreQ) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 32; ++j) Qs[i][j] = x[i][j] * x[i][j];
+  }
+  auto Qv = [&](int i, int j) -> float {
+    if constexpr (kStoreQ) return Qs[i][j];
+    else return x[i][j] * x[i][j];
+  };
+
+  float* bc_v = smem;               // [D] per-channel broadcast
+  float* bc_x = smem + D;           // [D] second per-channel broadcast
+  float* tp = smem + 2 * D;         // [W][128] per-wave token partials
+
+  float u[2] = {1.0f, 1.0f};        // 1 / r^2 for tokens 2l, 2l+1
+  float mt[2] = {1.0f, 1.0f};
+  float mc_own = 1.0f;              // channel mean square owned by this lane
+  const int ch_own = 32 * w + brev5(lane & 31);
+  const bool owner = lane < 32;
+  constexpr float kInvT = 1.0f / 128.0f;
+  constexpr float kInvD = 1.0f / (float)D;
+
+  for (int it = 0; it < 8; ++it) {
+    // channel step: mean over tokens of Q * u
+    {
+      float a[32];
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        float p0 = Qv(0, j) * u[0];
+        float p1 = Qv(1, j) * u[1];
+        a[j] = p0 + p1;
+      }
+      float sum = halve32(a, lane, OpAdd{});
+      float m = sum * kInvT;
+      if (!(m >= FLT_MIN)) m = 1.0f;
+      mc_own = m;
+      if (owner) bc_v[ch_own] = 1.0f / m;
+    }
+    __syncthreads();
+    // token step: mean over channels of Q * v
+    {
+      float v[32];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        float4 f = reinterpret_cast<const float4*>(bc_v + 32 * w)[q];
+        v[4 * q + 0] = f.x; v[4 * q + 1] = f.y; v[4 * q + 2] = f.z; v[4 * q + 3] = f.w;
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        float p[32];
+#pragma unroll
+        for (int j = 0; j < 32; ++j) p[j] = Qv(i, j) * v[j];
+        tp[w * kTile + 2 * lane + i] = psum<32, 0, 32>(p);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      float pw[W];
+#pragma unroll
+      for (int ww = 0; ww < W; ++ww) pw[ww] = tp[ww * kTile + 2 * lane + i];
+      float m = psum<W, 0, W>(pw) * kInvD;
+      if (!(m >= FLT_MIN)) m = 1.0f;
+      mt[i] = m;
+      u[i] = 1.0f / m;
+    }
+  }
+
+  // ---- final spreads and normalised tile ----
+  const float s_own = __builtin_sqrtf(mc_own);
+  if (owner) bc_v[ch_own] = 1.0f / s_own;
+  __syncthreads();
+  float r[2], ir[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    r[i] = __builtin_sqrtf(mt[i]);
+    ir[i] = 1.0f / r[i];
+  }
+  {
+    float is[32];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      float4 f = reinterpret_cast<const float4*>(bc_v + 32 * w)[q];
+      is[4 * q + 0] = f.x; is[4 * q + 1] = f.y; is[4 * q + 2] = f.z; is[4 * q + 3] = f.w;
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 32; ++j) x[i][j] = (x[i][j] * ir[i]) * is[j];
+  }
+  __syncthreads();  // bc_v is rewritten below
+
+  if (is_key) {
+    // ---- keys: per channel over the 128 tokens, 4 bits ----
+    float lo_a[32], hi_a[32];
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      lo_a[j] = OpMin{}(x[0][j], x[1][j]);
+      hi_a[j] = OpMax{}(x[0][j], x[1][j]);
+    }
+    float lo = halve32(lo_a, lane, OpMin{}) + 0.0f;
+    float hi = halve32(hi_a, lane, OpMax{}) + 0.0f;
+    float delta = (hi - lo) / 15.0f;
+    float inv = (delta >= FLT_MIN) ? 1.0f / delta : 0.0f;
+    if (owner) {
+      bc_v[ch_own] = lo;
+      bc_x[ch_own] = inv;
+      reinterpret_cast<float*>(rec + R::kscale)[ch_own] = delta * s_own;
+      reinterpret_cast<float*>(rec + R::kmin)[ch_own] = lo * s_own;
+    }
+    if (w == 0) {
+      reinterpret_cast<float2*>(rec + R::ktok)[lane] = make_float2(r[0], r[1]);
+    }
+    __syncthreads();
+    uint8_t* kst = reinterpret_cast<uint8_t*>(smem + 2 * D);  // [D][64] bytes
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const float lj = bc_v[32 * w + j], ij = bc_x[32 * w + j];
+      int z0 = (int)code_of(x[0][j], lj, ij, 15.0f);
+      int z1 = (int)code_of(x[1][j], lj, ij, 15.0f);
+      kst[(32 * w + j) * 64 + lane] = (uint8_t)(z0 | (z1 << 4));
+    }
+    __syncthreads();
+    // coalesced copy of the D*64 code bytes: 32 bytes per thread
+    const uint4* s4 = reinterpret_cast<const uint4*>(kst);
+    uint4* d4 = reinterpret_cast<uint4*>(rec + R::kcode);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) d4[tid * 2 + q] = s4[tid * 2 + q];
+  } else {
+    // ---- values: per token over each 128-channel group, 2 bits ----
+    float* mm = smem + 2 * D;  // [W][128][2]
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      float lo = x[i][0], hi = x[i][0];
+#pragma unroll
+      for (int j = 1; j < 32; ++j) { lo = OpMin{}(lo, x[i][j]); hi = OpMax{}(hi, x[i][j]); }
+      mm[(w * kTile + 2 * lane + i) * 2 + 0] = lo;
+      mm[(w * kTile + 2 * lane + i) * 2 + 1] = hi;
+    }
+    if (owner) reinterpret_cast<float*>(rec + R::vchan)[ch_own] = s_own;
+    __syncthreads();
+    const int g = w / 4;  // channel group of this wave
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int t = 2 * lane + i;
+      float lo = mm[((4 * g) * kTile + t) * 2 + 0];
+      float hi = mm[((4 * g) * kTile + t) * 2 + 1];
+#pragma unroll
+      for (int ww = 1; ww < 4; ++ww) {
+        lo = OpMin{}(lo, mm[((4 * g + ww) * kTile + t) * 2 + 0]);
+        hi = OpMax{}(hi, mm[((4 * g + ww) * kTile + t) * 2 + 1]);
+      }
+      lo = lo + 0.0f;
+      hi = hi + 0.0f;
+      float delta = (hi - lo) / 3.0f;
+      float inv = (delta >= FLT_MIN) ? 1.0f / delta : 0.0f;
+      uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        uint32_t z = (uint32_t)code_of(x[i][j], lo, inv, 3.0f);
+        packed[j / 16] |= z << (2 * (j % 16));
+      }
+      reinterpret_cast<uint2*>(rec + R::vcode + t * (D / 4) + 8 * w)[0] = make_uint2(packed[0], packed[1]);
+      if ((w & 3) == 0) {
+        reinterpret_cast<float*>(rec + R::vscale)[t * R::groups + g] = delta * r[i];
+        reinterpret_cast<float*>(rec + R::vmin)[t * R::groups + g] = lo * r[i];
+      }
+    }
+  }
+}
+
+}  // namespace
+
+// Launch the compressor for n_tiles x n_kv tile-heads (keys and values).
+hipError_t launch_compress(int d, int n_tiles, int n_kv, const float* k, const float* v,
+                           int64_t tok_stride, int64_t head_stride, void* records,
+                           hipStream_t stream) {
+  dim3 grid(n_tiles, n_kv, 2);
+  uint8_t* rec = static_cast<uint8_t*>(records);
+  switch (d) {
+    case 128:
+      hipLaunchKernelGGL(compress_kernel<128>, grid, dim3(256), 0, stream, k, v, tok_stride,
+                         head_stride, n_kv, rec);
+      break;
+    case 256:
+      hipLaunchKernelGGL(compress_kernel<256>, grid, dim3(512), 0, stream, k, v, tok_stride,
+                         head_stride, n_kv, rec);
+      break;
+    case 512:
+      hipLaunchKernelGGL(compress_kernel<512>, grid, dim3(1024), 0, stream, k, v, tok_stride,
+                         head_stride, n_kv, rec);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kvarn

@@ -1,0 +1,385 @@
+// decode.hip -- KVarN split-tile decode attention for gfx950.
+//
+// Per sequence b and query head h (KV head h/G), one query attends the
+// sequence's compressed tiles and its raw FP32 window:
+//   tiles  (rotated domain): q~_c = q'_c kscale_c, bias = sum_c q'_c kmin_c,
+//          score_t = tau * ktok_t * (sum_c q~_c zK_tc + bias);
+//          w_t = p_t vscale_{t,g}, u_g = sum_t p_t vmin_{t,g},
+//          o'_c += vchan_c (sum_t w_t zV_tc + u_g)
+//   window (raw domain):     score_t = tau * q . k_t,  o_c += p_t v_tc
+// (issue #180 Algorithm step 4: scales folded at read time; PR #434 commit
+// list: single streaming softmax over compressed tiles + FP32 window with a
+// deferred inverse WHT.)
+//
+// Split-tile schedule (issue #433 item 2): a fixed worst-case grid of
+// (split, KV head, sequence) workgroups; splits beyond a sequence's tiles or
+// window exit early with an empty partial.  Each workgroup keeps an online
+// softmax (running max, sum, rescaled accumulator; state initialised to
+// m = -inf, l = 0 before the first tile -- the hazard the PR #434 review
+// points at) and writes (m, l, o) per query head.  The combine kernel merges
+// the partials with log-sum-exp weights, applies the inverse WHT once to the
+// merged rotated-domain tile part, adds the raw-domain window part and
+// normalises.
+#include <float.h>
+
+#include "kvarn_launch.h"
+
+namespace kvarn {
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// partial kernel: one (split, kv head, sequence)
+// ---------------------------------------------------------------------------
+template <int D, int G>
+__global__ void __launch_bounds__(kDecThreads) decode_partial_kernel(DecodeParams P) {
+  using R = Rec<D>;
+  constexpr int NG = D / 128;                 // value channel groups
+  constexpr int HH = (G >= 2 && D == 128) ? 2 : 1;   // head halves (K: 128 tokens x HH)
+  constexpr int GH = G / HH;                  // heads per thread in the K phase
+  constexpr int CPT = (D >= kDecThreads) ? D / kDecThreads : 1;  // V channels per thread
+  constexpr int VH = (D * HH >= kDecThreads) ? HH : 1;            // V head split
+  constexpr int GV = G / VH;                  // heads per thread in the V phase
+  static_assert(CPT * kDecThreads / VH >= D || D == 128, "layout");
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const int split = blockIdx.x;
+  const int kvh = blockIdx.y;
+  const int b = blockIdx.z;
+  const int n_split = P.n_tsplit + P.n_wsplit;
+
+  __shared__ float s_q[G][D];                 // rotated (tiles) or raw (window) query
+  __shared__ float s_qt[D][G];                // q~ for the current tile, [channel][head]
+  __shared__ float s_sc[G][kTile];            // scores, then probabilities
+  __shared__ float s_w[G][NG][kTile];         // p * vscale
+  __shared__ float s_u[G][NG];                // sum p * vmin
+  __shared__ float s_bias[G];
+  __shared__ float s_m[G], s_l[G], s_alpha[G];
+  __shared__ __attribute__((aligned(16))) uint8_t s_code[64 * D];  // K codes, then V codes
+  __shared__ float s_scale[3 * D + 128];      // kscale, kmin, ktok  |  vchan, vscale, vmin
+
+  const SeqView sv = seq_view(P, b);
+  const int nt = sv.nt;
+  const int nw = sv.nw;
+  const bool is_tile = split < P.n_tsplit;
+  int t_begin = 0, t_end = 0, w_begin = 0, w_end = 0;
+  if (is_tile) {
+    t_begin = split * P.tps;
+    t_end = min(nt, t_begin + P.tps);
+  } else {
+    w_begin = (split - P.n_tsplit) * kWinChunk;
+    w_end = min(nw, w_begin + kWinChunk);
+  }
+
+  float* part = P.part + (((int64_t)b * P.n_q + (int64_t)kvh * G) * n_split + split) * (D + 4);
+  const bool empty = is_tile ? (t_begin >= t_end) : (w_begin >= w_end);
+  if (empty) {
+    // empty partial: m = -inf, l = 0, o = 0
+    for (int i = tid; i < G * (D + 4); i += kDecThreads) {
+      const int h = i / (D + 4), c = i % (D + 4);
+      float val = (c == D) ? -INFINITY : 0.0f;
+      part[(int64_t)h * n_split * (D + 4) + c] = val;
+    }
+    return;
+  }
+
+  // query rows for this KV head's G heads
+  const float* qsrc = (is_tile ? P.q_rot : P.q) + ((int64_t)b * P.n_q + (int64_t)kvh * G) * D;
+  for (int i = tid; i < G * D; i += kDecThreads) s_q[i / D][i % D] = qsrc[i];
+  if (tid < G) { s_m[tid] = -INFINITY; s_l[tid] = 0.0f; s_alpha[tid] = 1.0f; }
+
+  // V accumulators: thread owns channels c = (tid % (256/VH)) + k*(256/VH), heads hv*GV..
+  constexpr int VSTRIDE = kDecThreads / VH;
+  const int vc0 = tid % VSTRIDE;
+  const int hv = tid / VSTRIDE;
+  constexpr int VC = (D + VSTRIDE - 1) / VSTRIDE;   // channels per thread
+  float acc[GV][VC];
+#pragma unroll
+  for (int h = 0; h < GV; ++h)
+#pragma unroll
+    for (int k = 0; k < VC; ++k) acc[h][k] = 0.0f;
+  __syncthreads();
+
+  if (is_tile) {
+    const uint8_t* base = P.records + ((sv.rec_row0 + t_begin) * (int64_t)P.n_kv + kvh) * R::bytes;
+    for (int tile = t_begin; tile < t_end; ++tile, base += (int64_t)P.n_kv * R::bytes) {
+      // ---- stage K codes and key scales ----
+      {
+        const uint4* src = reinterpret_cast<const uint4*>(base + R::kcode);
+        uint4* dst = reinterpret_cast<uint4*>(s_code);
+        for (int i = tid; i < 4 * D; i += kDecThreads) dst[i] = src[i];
+        const float* ks = reinterpret_cast<const float*>(base + R::kscale);
+        const float* km = reinterpret_cast<const float*>(base + R::kmin);
+        const float* kt = reinterpret_cast<const float*>(base + R::ktok);
+        for (int i = tid; i < D; i += kDecThreads) { s_scale[i] = ks[i]; s_scale[D + i] = km[i]; }
+        if (tid < kTile) s_scale[2 * D + tid] = kt[tid];
+      }
+      __syncthreads();
+      // q~ = q' * kscale and bias = q' . kmin
+      for (int i = tid; i < G * D; i += kDecThreads) {
+        const int h = i / D, c = i % D;
+        s_qt[c][h] = s_q[h][c] * s_scale[c];
+      }
+      for (int h = wv; h < G; h += kDecThreads / 64) {
+        float a = 0.0f;
+        for (int c = lane; c < D; c += 64) a += s_q[h][c] * s_scale[D + c];
+        a = wave_sum(a);
+        if (lane == 0) s_bias[h] = a;
+      }
+      __syncthreads();
+      // ---- K scores: thread = (token, head half) ----
+      {
+        const int t = tid % kTile;
+        const int hh = tid / kTile;
+        if (hh < HH) {
+          float sacc[GH];
+#pragma unroll
+          for (int h = 0; h < GH; ++h) sacc[h] = 0.0f;
+          for (int c = 0; c < D; ++c) {
+            const uint32_t byte = s_code[c * 64 + (t >> 1)];
+            const float z = (float)((byte >> ((t & 1) * 4)) & 15u);
+#pragma unroll
+            for (int h = 0; h < GH; ++h) sacc[h] += s_qt[c][hh * GH + h] * z;
+          }
+          const float ktok = s_scale[2 * D + t];
+#pragma unroll
+          for (int h = 0; h < GH; ++h) {
+            const int hg = hh * GH + h;
+            s_sc[hg][t] = P.scale * ktok * (sacc[h] + s_bias[hg]);
+          }
+        }
+      }
+      __syncthreads();
+      // ---- stage V codes and value scales (K buffers are free) ----
+      {
+        const uint4* src = reinterpret_cast<const uint4*>(base + R::vcode);
+        uint4* dst = reinterpret_cast<uint4*>(s_code);
+        for (int i = tid; i < 2 * D; i += kDecThreads) dst[i] = src[i];
+        const float* vch = reinterpret_cast<const float*>(base + R::vchan);
+        const float* vs = reinterpret_cast<const float*>(base + R::vscale);
+        const float* vm = reinterpret_cast<const float*>(base + R::vmin);
+        for (int i = tid; i < D; i += kDecThreads) s_scale[i] = vch[i];
+        for (int i = tid; i < kTile * NG; i += kDecThreads) {
+          s_scale[D + i] = vs[i];
+          s_scale[2 * D + i] = vm[i];
+        }
+      }
+      // ---- online softmax over this tile: one wave per head ----
+      for (int h = wv; h < G; h += kDecThreads / 64) {
+        const float s0 = s_sc[h][lane], s1 = s_sc[h][lane + 64];
+        const float mt = wave_max(fmaxf(s0, s1));
+        const float m_old = s_m[h];
+        const float m_new = fmaxf(m_old, mt);
+        const float p0 = __expf(s0 - m_new), p1 = __expf(s1 - m_new);
+        const float psum = wave_sum(p0 + p1);
+        s_sc[h][lane] = p0;
+        s_sc[h][lane + 64] = p1;
+        if (lane == 0) {
+          const float alpha = __expf(m_old - m_new);   // 0 on the first tile (m_old = -inf)
+          s_alpha[h] = alpha;
+          s_l[h] = s_l[h] * alpha + psum;
+          s_m[h] = m_new;
+        }
+      }
+      __syncthreads();
+      // w = p * vscale, u = sum p * vmin  (value scales are staged now)
+      for (int i = tid; i < G * NG * kTile; i += kDecThreads) {
+        const int h = i / (NG * kTile), r = i % (NG * kTile), g = r / kTile, t = r % kTile;
+        s_w[h][g][t] = s_sc[h][t] * s_scale[D + t * NG + g];
+      }
+      for (int i = wv; i < G * NG; i += kDecThreads / 64) {
+        const int h = i / NG, g = i % NG;
+        float a = s_sc[h][lane] * s_scale[2 * D + lane * NG + g] +
+                  s_sc[h][lane + 64] * s_scale[2 * D + (lane + 64) * NG + g];
+        a = wave_sum(a);
+        if (lane == 0) s_u[h][g] = a;
+      }
+      __syncthreads();
+      // ---- V aggregate: thread = (channels, head part) ----
+#pragma unroll
+      for (int k = 0; k < VC; ++k) {
+        const int c = vc0 + k * VSTRIDE;
+        if (c < D) {
+          const int g = c / 128;
+          const int sh = 2 * (c & 3);
+          float pacc[GV];
+#pragma unroll
+          for (int h = 0; h < GV; ++h) pacc[h] = 0.0f;
+          for (int t = 0; t < kTile; ++t) {
+            const float z = (float)((s_code[t * (D / 4) + (c >> 2)] >> sh) & 3u);
+#pragma unroll
+            for (int h = 0; h < GV; ++h) pacc[h] += s_w[hv * GV + h][g][t] * z;
+          }
+          const float vch = s_scale[c];
+#pragma unroll
+          for (int h = 0; h < GV; ++h) {
+            const int hg = hv * GV + h;
+            acc[h][k] = acc[h][k] * s_alpha[hg] + vch * (pacc[h] + s_u[hg][g]);
+          }
+        }
+      }
+      __syncthreads();
+    }
+  } else {
+    // ---- raw window chunk [w_begin, w_end) ----
+    const float* kb = P.k_win + sv.win_off + (int64_t)kvh * P.win_head_stride;
+    const float* vb = P.v_win + sv.win_off + (int64_t)kvh * P.win_head_stride;
+    const int n = w_end - w_begin;
+    // scores: thread = (token in chunk, head group of 4)
+    {
+      const int t = tid % kWinChunk;
+      const int hg0 = tid / kWinChunk;
+      if (t < n) {
+        const float* krow = kb + (int64_t)(w_begin + t) * P.win_tok_stride;
+        for (int h = hg0; h < G; h += kDecThreads / kWinChunk) {
+          float a = 0.0f;
+          for (int c = 0; c < D; c += 4) {
+            const float4 kk = *reinterpret_cast<const float4*>(krow + c);
+            a += s_q[h][c] * kk.x + s_q[h][c + 1] * kk.y + s_q[h][c + 2] * kk.z + s_q[h][c + 3] * kk.w;
+          }
+          s_sc[h][t] = P.scale * a;
+        }
+      } else {
+        for (int h = hg0; h < G; h += kDecThreads / kWinChunk) s_sc[h][t] = -INFINITY;
+      }
+    }
+    __syncthreads();
+    for (int h = wv; h < G; h += kDecThreads / 64) {
+      const float s0 = s_sc[h][lane];
+      const float m = wave_max(s0);
+      const float p = (lane < n) ? __expf(s0 - m) : 0.0f;
+      const float l = wave_sum(p);
+      s_sc[h][lane] = p;
+      if (lane == 0) { s_m[h] = m; s_l[h] = l; s_alpha[h] = 0.0f; }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < VC; ++k) {
+      const int c = vc0 + k * VSTRIDE;
+      if (c < D) {
+        float pacc[GV];
+#pragma unroll
+        for (int h = 0; h < GV; ++h) pacc[h] = 0.0f;
+        for (int t = 0; t < n; ++t) {
+          const float v = vb[(int64_t)(w_begin + t) * P.win_tok_stride + c];
+#pragma unroll
+          for (int h = 0; h < GV; ++h) pacc[h] += s_sc[hv * GV + h][t] * v;
+        }
+#pragma unroll
+        for (int h = 0; h < GV; ++h) acc[h][k] = pacc[h];
+      }
+    }
+  }
+
+  // ---- write the partial (m, l, o) per query head ----
+#pragma unroll
+  for (int k = 0; k < VC; ++k) {
+    const int c = vc0 + k * VSTRIDE;
+    if (c < D) {
+#pragma unroll
+      for (int h = 0; h < GV; ++h) {
+        const int hg = hv * GV + h;
+        part[(int64_t)hg * n_split * (D + 4) + c] = acc[h][k];
+      }
+    }
+  }
+  if (tid < G) {
+    part[(int64_t)tid * n_split * (D + 4) + D] = s_m[tid];
+    part[(int64_t)tid * n_split * (D + 4) + D + 1] = s_l[tid];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// combine kernel: one wave per (query head, sequence)
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ void __launch_bounds__(64) decode_combine_kernel(DecodeParams P) {
+  constexpr int K = D / 64;
+  const int hq = blockIdx.x;
+  const int b = blockIdx.y;
+  const int lane = threadIdx.x;
+  const int n_split = P.n_tsplit + P.n_wsplit;
+  const float* part = P.part + ((int64_t)b * P.n_q + hq) * n_split * (D + 4);
+
+  float M = -INFINITY;
+  for (int s = 0; s < n_split; ++s) M = fmaxf(M, part[(int64_t)s * (D + 4) + D]);
+  float L = 0.0f;
+  float orot[K], oraw[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) { orot[k] = 0.0f; oraw[k] = 0.0f; }
+  for (int s = 0; s < n_split; ++s) {
+    const float* ps = part + (int64_t)s * (D + 4);
+    const float m = ps[D];
+    const float wgt = (m == -INFINITY) ? 0.0f : __expf(m - M);
+    L += wgt * ps[D + 1];
+    if (s < P.n_tsplit) {
+#pragma unroll
+      for (int k = 0; k < K; ++k) orot[k] += wgt * ps[lane + 64 * k];
+    } else {
+#pragma unroll
+      for (int k = 0; k < K; ++k) oraw[k] += wgt * ps[lane + 64 * k];
+    }
+  }
+  // inverse WHT (the WHT itself) of the merged rotated-domain part
+#pragma unroll
+  for (int h = 1; h < 64; h <<= 1) {
+    const bool up = (lane & h) != 0;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      float p = shfl_xor(orot[k], h);
+      orot[k] = up ? (p - orot[k]) : (orot[k] + p);
+    }
+  }
+#pragma unroll
+  for (int hk = 1; hk < K; hk <<= 1) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      if ((k & hk) == 0) {
+        float a = orot[k], c = orot[k + hk];
+        orot[k] = a + c;
+        orot[k + hk] = a - c;
+      }
+    }
+  }
+  const float c = wht_scale<D>();
+  const float invL = 1.0f / L;
+  float* o = P.out + ((int64_t)b * P.n_q + hq) * D;
+#pragma unroll
+  for (int k = 0; k < K; ++k) o[lane + 64 * k] = (orot[k] * c + oraw[k]) * invL;
+}
+
+template <int D, int G>
+hipError_t launch_decode_dg(const DecodeParams& P, int batch, hipStream_t stream) {
+  dim3 grid(P.n_tsplit + P.n_wsplit, P.n_kv, batch);
+  hipLaunchKernelGGL((decode_partial_kernel<D, G>), grid, dim3(kDecThreads), 0, stream, P);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(P.n_q, batch), dim3(64), 0, stream, P);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_decode_d(const DecodeParams& P, int batch, hipStream_t stream) {
+  switch (P.G) {
+    case 1: return launch_decode_dg<D, 1>(P, batch, stream);
+    case 2: return launch_decode_dg<D, 2>(P, batch, stream);
+    case 4: return launch_decode_dg<D, 4>(P, batch, stream);
+    case 8: return launch_decode_dg<D, 8>(P, batch, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode(int d, const DecodeParams& P, int batch, hipStream_t stream) {
+  switch (d) {
+    case 128: return launch_decode_d<128>(P, batch, stream);
+    case 256: return launch_decode_d<256>(P, batch, stream);
+    case 512: return launch_decode_d<512>(P, batch, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace kvarn

@@ -1,0 +1,243 @@
+// kvarn_api.hip -- the C ABI declared in include/kvarn.h: host-side argument
+// validation (before anything is enqueued), split planning, and launches.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/kvarn.h"
+#include "kvarn_launch.h"
+
+
+namespace {
+
+bool dim_ok(int32_t d) { return d == 128 || d == 256 || d == 512; }
+bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool st16(int64_t floats) { return (floats % 4) == 0; }
+
+// Work target for the split plan: enough workgroups to cover the 256 CUs a
+// few times over.
+constexpr int64_t kTargetGroups = 2048;
+
+struct DecodePlan {
+  int tps, n_tsplit, n_wsplit;
+};
+
+DecodePlan plan_decode(int batch, int n_kv, int max_tiles, int max_win) {
+  DecodePlan p;
+  const int64_t units = (int64_t)batch * n_kv * (max_tiles > 0 ? max_tiles : 0);
+  int64_t tps = (units + kTargetGroups - 1) / kTargetGroups;
+  if (tps < 1) tps = 1;
+  p.tps = (int)tps;
+  p.n_tsplit = max_tiles > 0 ? (int)((max_tiles + tps - 1) / tps) : 0;
+  p.n_wsplit = max_win > 0 ? (max_win + kvarn::kWinChunk - 1) / kvarn::kWinChunk : 0;
+  return p;
+}
+
+int validate_decode(const kvarn_decode_args* a, DecodePlan* plan) {
+  if (!a) return KVARN_E_INVALID;
+  if (!dim_ok(a->head_dim)) return KVARN_E_UNSUPPORTED;
+  if (a->batch < 1 || a->n_q_heads < 1 || a->n_kv_heads < 1) return KVARN_E_INVALID;
+  if (a->batch > KVARN_MAX_BATCH) return KVARN_E_UNSUPPORTED;
+  if (a->n_q_heads % a->n_kv_heads != 0) return KVARN_E_UNSUPPORTED;
+  const int G = a->n_q_heads / a->n_kv_heads;
+  if (!(G == 1 || G == 2 || G == 4 || G == 8)) return KVARN_E_UNSUPPORTED;
+  if (a->max_tiles < 0 || a->max_win < 0 || a->n_record_rows < 0) return KVARN_E_INVALID;
+  if (!a->q || !a->q_rot || !a->out || !a->n_tiles || !a->n_win || !a->rec_start)
+    return KVARN_E_INVALID;
+  bool any_tiles = false, any_win = false;
+  for (int b = 0; b < a->batch; ++b) {
+    const int nt = a->n_tiles[b], nw = a->n_win[b];
+    if (nt < 0 || nw < 0 || nt > a->max_tiles || nw > a->max_win) return KVARN_E_INVALID;
+    if (a->win_start && a->win_start[b] < 0) return KVARN_E_INVALID;
+    if (nt + nw == 0) return KVARN_E_INVALID;
+    if (nt > 0) {
+      if (a->rec_start[b] < 0 || a->rec_start[b] + nt > a->n_record_rows) return KVARN_E_INVALID;
+      any_tiles = true;
+    }
+    if (nw > 0) any_win = true;
+  }
+  if (any_tiles && !a->records) return KVARN_E_INVALID;
+  if (any_win && (!a->k_win || !a->v_win)) return KVARN_E_INVALID;
+  if (any_win && (a->win_tok_stride < a->head_dim || a->win_head_stride < 0 || a->win_seq_stride < 0))
+    return KVARN_E_INVALID;
+  if (!al16(a->q) || !al16(a->q_rot) || !al16(a->out) || !al16(a->records) ||
+      !al16(a->k_win) || !al16(a->v_win))
+    return KVARN_E_ALIGN;
+  if (!st16(a->win_seq_stride) || !st16(a->win_tok_stride) || !st16(a->win_head_stride))
+    return KVARN_E_ALIGN;
+  if (plan) *plan = plan_decode(a->batch, a->n_kv_heads, a->max_tiles, a->max_win);
+  return KVARN_OK;
+}
+
+size_t decode_ws(int batch, int n_q, int d, const DecodePlan& p) {
+  return (size_t)batch * n_q * (size_t)(p.n_tsplit + p.n_wsplit) * (size_t)(d + 4) * sizeof(float);
+}
+
+int64_t prefill_tiles_at(int64_t pos, int window) {
+  const int64_t ahead = pos + 1 - window;
+  return ahead > 0 ? ahead / KVARN_TILE_TOKENS : 0;
+}
+
+int validate_prefill(const kvarn_prefill_args* a, DecodePlan* plan) {
+  if (!a) return KVARN_E_INVALID;
+  if (a->head_dim != 128) return dim_ok(a->head_dim) ? KVARN_E_UNSUPPORTED : KVARN_E_UNSUPPORTED;
+  if (a->n_q_heads < 1 || a->n_kv_heads < 1 || a->chunk < 1 || a->pos0 < 0 || a->window < 0)
+    return KVARN_E_INVALID;
+  if (a->n_q_heads % a->n_kv_heads != 0) return KVARN_E_UNSUPPORTED;
+  const int G = a->n_q_heads / a->n_kv_heads;
+  if (!(G == 1 || G == 2 || G == 4 || G == 8)) return KVARN_E_UNSUPPORTED;
+  if (!a->q || !a->q_rot || !a->out || !a->k || !a->v) return KVARN_E_INVALID;
+  const int64_t last = a->pos0 + a->chunk - 1;
+  const int64_t t_first = prefill_tiles_at(a->pos0, a->window);
+  const int64_t t_last = prefill_tiles_at(last, a->window);
+  if (t_last > 0 && !a->records) return KVARN_E_INVALID;
+  if (a->n_record_rows < t_last) return KVARN_E_INVALID;
+  if (a->raw_base < 0 || a->raw_base > KVARN_TILE_TOKENS * t_first) return KVARN_E_INVALID;
+  if (a->tok_stride < a->head_dim || a->head_stride < 0) return KVARN_E_INVALID;
+  if (!al16(a->q) || !al16(a->q_rot) || !al16(a->out) || !al16(a->records) || !al16(a->k) ||
+      !al16(a->v))
+    return KVARN_E_ALIGN;
+  if (!st16(a->tok_stride) || !st16(a->head_stride)) return KVARN_E_ALIGN;
+  if (plan) {
+    // window tokens of a row are at most W + 127 (fewer when the prompt is short)
+    int64_t max_win = a->window + KVARN_TILE_TOKENS - 1;
+    if (last + 1 < max_win) max_win = last + 1;
+    *plan = plan_decode(a->chunk, a->n_kv_heads, (int)t_last, (int)max_win);
+  }
+  return KVARN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kvarn_status_string(int status) {
+  switch (status) {
+    case KVARN_OK: return "KVARN_OK";
+    case KVARN_E_INVALID: return "KVARN_E_INVALID";
+    case KVARN_E_UNSUPPORTED: return "KVARN_E_UNSUPPORTED";
+    case KVARN_E_ALIGN: return "KVARN_E_ALIGN";
+    case KVARN_E_WORKSPACE: return "KVARN_E_WORKSPACE";
+    case KVARN_E_DEVICE: return "KVARN_E_DEVICE";
+    default: return "KVARN_E_UNKNOWN";
+  }
+}
+
+size_t kvarn_tile_bytes(int32_t head_dim) {
+  return dim_ok(head_dim) ? (size_t)(116 * head_dim + 512) : 0;
+}
+
+int kvarn_compress_tile(int32_t head_dim, int32_t n_tiles, int32_t n_kv_heads, const float* k,
+                        const float* v, int64_t tok_stride, int64_t head_stride, void* records,
+                        void* stream) {
+  if (!dim_ok(head_dim)) return KVARN_E_UNSUPPORTED;
+  if (n_tiles < 0 || n_kv_heads < 1) return KVARN_E_INVALID;
+  if (n_tiles == 0) return KVARN_OK;
+  if (!k || !v || !records) return KVARN_E_INVALID;
+  if (tok_stride < head_dim || head_stride < 0) return KVARN_E_INVALID;
+  if (n_kv_heads > 65535) return KVARN_E_UNSUPPORTED;
+  if (!al16(k) || !al16(v) || !al16(records) || !st16(tok_stride) || !st16(head_stride))
+    return KVARN_E_ALIGN;
+  hipError_t e = kvarn::launch_compress(head_dim, n_tiles, n_kv_heads, k, v, tok_stride,
+                                        head_stride, records, (hipStream_t)stream);
+  return e == hipSuccess ? KVARN_OK : KVARN_E_DEVICE;
+}
+
+int kvarn_rotate_query(int32_t head_dim, int64_t n_rows, const float* q, float* q_rot,
+                       void* stream) {
+  if (!dim_ok(head_dim)) return KVARN_E_UNSUPPORTED;
+  if (n_rows < 0) return KVARN_E_INVALID;
+  if (n_rows == 0) return KVARN_OK;
+  if (!q || !q_rot) return KVARN_E_INVALID;
+  if (!al16(q) || !al16(q_rot)) return KVARN_E_ALIGN;
+  if ((n_rows + 3) / 4 > 0x7fffffffLL) return KVARN_E_UNSUPPORTED;
+  hipError_t e = kvarn::launch_rotate(head_dim, n_rows, q, q_rot, (hipStream_t)stream);
+  return e == hipSuccess ? KVARN_OK : KVARN_E_DEVICE;
+}
+
+size_t kvarn_decode_workspace_bytes(const kvarn_decode_args* a) {
+  DecodePlan p;
+  if (validate_decode(a, &p) != KVARN_OK) return 0;
+  return decode_ws(a->batch, a->n_q_heads, a->head_dim, p);
+}
+
+int kvarn_decode_attention(const kvarn_decode_args* a, void* workspace, size_t ws_bytes,
+                           void* stream) {
+  DecodePlan p;
+  int st = validate_decode(a, &p);
+  if (st != KVARN_OK) return st;
+  const size_t need = decode_ws(a->batch, a->n_q_heads, a->head_dim, p);
+  if (!workspace || ws_bytes < need) return KVARN_E_WORKSPACE;
+  if (!al16(workspace)) return KVARN_E_ALIGN;
+  kvarn::DecodeParams P;
+  memset(&P, 0, sizeof(P));
+  P.q = a->q;
+  P.q_rot = a->q_rot;
+  P.records = static_cast<const uint8_t*>(a->records);
+  P.k_win = a->k_win;
+  P.v_win = a->v_win;
+  P.part = static_cast<float*>(workspace);
+  P.out = a->out;
+  P.win_seq_stride = a->win_seq_stride;
+  P.win_tok_stride = a->win_tok_stride;
+  P.win_head_stride = a->win_head_stride;
+  P.scale = a->softmax_scale;
+  P.n_q = a->n_q_heads;
+  P.n_kv = a->n_kv_heads;
+  P.G = a->n_q_heads / a->n_kv_heads;
+  P.tps = p.tps;
+  P.n_tsplit = p.n_tsplit;
+  P.n_wsplit = p.n_wsplit;
+  P.mode = 0;
+  for (int b = 0; b < a->batch; ++b) {
+    P.rec_start[b] = a->rec_start[b];
+    P.win_start[b] = a->win_start ? a->win_start[b] : 0;
+    P.n_tiles[b] = a->n_tiles[b];
+    P.n_win[b] = a->n_win[b];
+  }
+  hipError_t e = kvarn::launch_decode(a->head_dim, P, a->batch, (hipStream_t)stream);
+  return e == hipSuccess ? KVARN_OK : KVARN_E_DEVICE;
+}
+
+size_t kvarn_prefill_workspace_bytes(const kvarn_prefill_args* a) {
+  DecodePlan p;
+  if (validate_prefill(a, &p) != KVARN_OK) return 0;
+  return decode_ws(a->chunk, a->n_q_heads, a->head_dim, p);
+}
+
+int kvarn_prefill_attention(const kvarn_prefill_args* a, void* workspace, size_t ws_bytes,
+                            void* stream) {
+  DecodePlan p;
+  int st = validate_prefill(a, &p);
+  if (st != KVARN_OK) return st;
+  const size_t need = decode_ws(a->chunk, a->n_q_heads, a->head_dim, p);
+  if (!workspace || ws_bytes < need) return KVARN_E_WORKSPACE;
+  if (!al16(workspace)) return KVARN_E_ALIGN;
+  kvarn::DecodeParams P;
+  memset(&P, 0, sizeof(P));
+  P.q = a->q;
+  P.q_rot = a->q_rot;
+  P.records = static_cast<const uint8_t*>(a->records);
+  P.k_win = a->k;
+  P.v_win = a->v;
+  P.part = static_cast<float*>(workspace);
+  P.out = a->out;
+  P.win_seq_stride = 0;
+  P.win_tok_stride = a->tok_stride;
+  P.win_head_stride = a->head_stride;
+  P.scale = a->softmax_scale;
+  P.n_q = a->n_q_heads;
+  P.n_kv = a->n_kv_heads;
+  P.G = a->n_q_heads / a->n_kv_heads;
+  P.tps = p.tps;
+  P.n_tsplit = p.n_tsplit;
+  P.n_wsplit = p.n_wsplit;
+  P.mode = 1;
+  P.window = a->window;
+  P.pos0 = a->pos0;
+  P.raw_base = a->raw_base;
+  hipError_t e = kvarn::launch_decode(a->head_dim, P, a->chunk, (hipStream_t)stream);
+  return e == hipSuccess ? KVARN_OK : KVARN_E_DEVICE;
+}
+
+}  // extern "C"

@@ -1,0 +1,71 @@
+// kvarn_launch.h -- host/device interface between the C ABI layer and the
+// HIP kernels: parameter blocks and launch entry points.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvarn_device.h"
+
+namespace kvarn {
+
+constexpr int kDecThreads = 256;
+constexpr int kWinChunk = 64;      // window tokens per split
+
+struct DecodeParams {
+  const float* q;
+  const float* q_rot;
+  const uint8_t* records;
+  const float* k_win;
+  const float* v_win;
+  float* part;                     // [B][Hq][n_split][D + 4]
+  float* out;                      // [B][Hq][D]
+  int64_t win_seq_stride, win_tok_stride, win_head_stride;
+  float scale;
+  int n_q, n_kv, G;
+  int tps, n_tsplit, n_wsplit;
+  // prefill view (mode 1): "sequence" b is query position pos0 + b of one
+  // sequence; it sees T(p) tiles and raw rows [128 T(p), p] of k_win/v_win,
+  // where raw row p lives at (p - raw_base) * win_tok_stride.
+  int mode;
+  int window;
+  int64_t pos0, raw_base;
+  int64_t rec_start[64];
+  int64_t win_start[64];
+  int n_tiles[64];
+  int n_win[64];
+};
+
+// Tiles, window tokens, first record row and window base of sequence b.
+struct SeqView {
+  int nt, nw;
+  int64_t rec_row0;
+  int64_t win_off;   // float offset of window token 0, KV head 0
+};
+
+__device__ __forceinline__ SeqView seq_view(const DecodeParams& P, int b) {
+  SeqView v;
+  if (P.mode == 0) {
+    v.nt = P.n_tiles[b];
+    v.nw = P.n_win[b];
+    v.rec_row0 = P.rec_start[b];
+    v.win_off = (int64_t)b * P.win_seq_stride + P.win_start[b] * P.win_tok_stride;
+  } else {
+    const int64_t p = P.pos0 + b;
+    const int64_t ahead = p + 1 - P.window;
+    const int64_t T = ahead > 0 ? ahead / kTile : 0;
+    v.nt = (int)T;
+    v.nw = (int)(p + 1 - kTile * T);
+    v.rec_row0 = 0;
+    v.win_off = (kTile * T - P.raw_base) * P.win_tok_stride;
+  }
+  return v;
+}
+
+hipError_t launch_compress(int d, int n_tiles, int n_kv, const float* k, const float* v,
+                           int64_t tok_stride, int64_t head_stride, void* records,
+                           hipStream_t stream);
+hipError_t launch_rotate(int d, int64_t n_rows, const float* q, float* q_rot, hipStream_t stream);
+hipError_t launch_decode(int d, const DecodeParams& P, int batch, hipStream_t stream);
+
+}  // namespace kvarn

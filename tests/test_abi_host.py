@@ -1,0 +1,134 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every function include/kvarn.h declares, and rejects bad arguments before
+anything is enqueued (no call here reaches a launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvarn.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    from quantized_attention_tok_amd import build_lib, kvarn
+    if not os.path.exists(kvarn.LIB_PATH):
+        build_lib.build()
+    return kvarn.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvarn_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_function_is_exported(L):
+    names = declared_functions()
+    assert len(names) == 8, names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_tile_bytes_and_status_strings(L):
+    assert [L.kvarn_tile_bytes(d) for d in (128, 256, 512)] == [15360, 30208, 59904]
+    assert L.kvarn_tile_bytes(64) == 0 and L.kvarn_tile_bytes(1024) == 0
+    assert L.kvarn_status_string(0) == b"KVARN_OK"
+    assert L.kvarn_status_string(4) == b"KVARN_E_WORKSPACE"
+    assert L.kvarn_status_string(99) == b"KVARN_E_UNKNOWN"
+
+
+FAKE = 0x10000  # aligned but never dereferenced: every call below fails validation first
+# A status of KVARN_OK (0) or KVARN_E_DEVICE (5) would mean a launch was
+# attempted with FAKE pointers; the tests assert specific validation errors.
+
+
+def test_compress_validation(L):
+    f = L.kvarn_compress_tile
+    vp = ctypes.c_void_p
+    assert f(100, 1, 1, vp(FAKE), vp(FAKE), 128, 128, vp(FAKE), None) == 2
+    assert f(128, -1, 1, vp(FAKE), vp(FAKE), 128, 128, vp(FAKE), None) == 1
+    assert f(128, 1, 0, vp(FAKE), vp(FAKE), 128, 128, vp(FAKE), None) == 1
+    assert f(128, 1, 1, None, vp(FAKE), 128, 128, vp(FAKE), None) == 1
+    assert f(128, 1, 1, vp(FAKE), vp(FAKE), 64, 128, vp(FAKE), None) == 1
+    assert f(128, 1, 1, vp(FAKE + 4), vp(FAKE), 128, 128, vp(FAKE), None) == 3
+    assert f(128, 1, 1, vp(FAKE), vp(FAKE), 130, 128, vp(FAKE), None) == 3
+    assert f(128, 0, 1, None, None, 0, 0, None, None) == 0   # empty is a no-op
+
+
+def test_rotate_validation(L):
+    f = L.kvarn_rotate_query
+    vp = ctypes.c_void_p
+    assert f(96, 4, vp(FAKE), vp(FAKE), None) == 2
+    assert f(128, -2, vp(FAKE), vp(FAKE), None) == 1
+    assert f(128, 4, None, vp(FAKE), None) == 1
+    assert f(128, 4, vp(FAKE + 8), vp(FAKE), None) == 3
+    assert f(128, 0, None, None, None) == 0
+
+
+def _decode_args(**over):
+    from quantized_attention_tok_amd.kvarn import DecodeArgs
+    a = DecodeArgs()
+    B = over.pop("batch", 1)
+    nt = over.pop("n_tiles", [4] * B)
+    nw = over.pop("n_win", [0] * B)
+    rs = over.pop("rec_start", [0] * B)
+    a.head_dim, a.batch, a.n_q_heads, a.n_kv_heads = 128, B, 4, 1
+    a.softmax_scale = 0.1
+    a.max_tiles, a.max_win = max(nt), max(nw)
+    a.q = a.q_rot = a.out = a.records = a.k_win = a.v_win = FAKE
+    a.n_record_rows = 4 * B
+    a.win_tok_stride, a.win_head_stride, a.win_seq_stride = 128, 128, 128 * 128
+    keep = [(ctypes.c_int32 * B)(*nt), (ctypes.c_int32 * B)(*nw), (ctypes.c_int64 * B)(*rs)]
+    a.n_tiles, a.n_win, a.rec_start = keep
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a, keep
+
+
+def test_decode_validation_and_workspace_query(L):
+    a, keep = _decode_args()
+    need = L.kvarn_decode_workspace_bytes(ctypes.byref(a))
+    assert need > 0
+    # too-small workspace is rejected before any launch
+    assert L.kvarn_decode_attention(ctypes.byref(a), ctypes.c_void_p(FAKE), need - 16, None) == 4
+    assert L.kvarn_decode_attention(ctypes.byref(a), None, need, None) == 4
+    bad = [
+        (dict(head_dim=100), 2), (dict(n_q_heads=6), 2), (dict(n_q_heads=48, n_kv_heads=3), 2),
+        (dict(batch=65, n_tiles=[1] * 65, n_win=[0] * 65, rec_start=[0] * 65), 2),
+        (dict(n_tiles=[0], n_win=[0]), 1),               # no visible key
+        (dict(max_tiles=2), 1),                           # n_tiles > bound
+        (dict(n_record_rows=3), 1),                       # tiles beyond the pool
+        (dict(q=FAKE + 4), 3), (dict(win_tok_stride=130), 3),
+        (dict(q_rot=None), 1),
+    ]
+    for over, want in bad:
+        b, k2 = _decode_args(**over)
+        assert L.kvarn_decode_attention(ctypes.byref(b), ctypes.c_void_p(FAKE), 1 << 30, None) == want, over
+        assert L.kvarn_decode_workspace_bytes(ctypes.byref(b)) == 0
+
+
+def test_prefill_validation(L):
+    from quantized_attention_tok_amd.kvarn import PrefillArgs
+
+    def args(**over):
+        a = PrefillArgs()
+        a.head_dim, a.n_q_heads, a.n_kv_heads, a.window = 128, 8, 2, 256
+        a.pos0, a.chunk, a.softmax_scale = 512, 256, 0.1
+        a.q = a.q_rot = a.out = a.records = a.k = a.v = FAKE
+        a.n_record_rows = 4
+        a.tok_stride, a.head_stride, a.raw_base = 256, 128, 256
+        for k, v in over.items():
+            setattr(a, k, v)
+        return a
+    a = args()
+    assert L.kvarn_prefill_workspace_bytes(ctypes.byref(a)) > 0
+    bad = [(dict(head_dim=256), 2), (dict(chunk=0), 1), (dict(pos0=-1), 1),
+           (dict(n_record_rows=3), 1), (dict(raw_base=384), 1), (dict(k=FAKE + 4), 3),
+           (dict(tok_stride=258), 3), (dict(n_q_heads=6), 2)]
+    for over, want in bad:
+        b = args(**over)
+        assert L.kvarn_prefill_attention(ctypes.byref(b), ctypes.c_void_p(FAKE), 1 << 30, None) == want, over
+    assert L.kvarn_prefill_attention(ctypes.byref(a), ctypes.c_void_p(FAKE), 16, None) == 4

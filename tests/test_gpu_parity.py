@@ -1,0 +1,317 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.  Records must be byte-identical; attention must be within
+1e-4 relative L2 of the fp64 oracle on the dequantised cache."""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from quantized_attention_tok_amd import kvarn, synth
+from quantized_attention_tok_amd.cache import SequenceCache
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-4
+DEV = "cuda:0"
+
+
+def say(*a):
+    print("[case]", *a, file=sys.stderr, flush=True)
+
+
+def rel_l2(got, ref):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    return float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+
+
+def to_dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    kvarn.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def gpu_compress(K, V, n_tiles):
+    d, n_kv = K.shape[2], K.shape[1]
+    rec = torch.zeros(max(n_tiles, 1), n_kv, kvarn.tile_bytes(d), dtype=torch.uint8, device=DEV)
+    kvarn.compress_tile(to_dev(K), to_dev(V), rec, n_tiles)
+    torch.cuda.synchronize()
+    return rec[:n_tiles].cpu().numpy()
+
+
+# --------------------------------------------------------------------------
+# compression: byte parity
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d,n_kv,n_tiles,n_out", [(128, 1, 4, 4), (128, 8, 6, 2), (256, 4, 3, 4),
+                                                  (512, 1, 3, 4), (512, 2, 2, 4)])
+def test_compress_bytes_identical(d, n_kv, n_tiles, n_out):
+    say("compress", d, n_kv, n_tiles)
+    K, V = synth.make_kv(100 + d + n_kv, 128 * n_tiles, n_kv, d, n_out)
+    got = gpu_compress(K, V, n_tiles)
+    want = oracle.compress_tiles(K, V, n_tiles)
+    mism = np.argwhere(got != want)
+    assert mism.size == 0, f"{len(mism)} bytes differ, first at {mism[:5].tolist()}"
+
+
+def test_compress_strided_input_and_degenerate_tiles():
+    say("compress degenerate")
+    d, n_kv = 128, 2
+    K, V = synth.make_kv(7, 128 * 4, n_kv, d, 4)
+    K[:, 0, 5] = 0.0                        # all-zero channel in head 0
+    K[128 + 17, 1, :] = 0.0                 # all-zero token
+    V[256:384, 0, :] = 1.5                  # constant tile
+    K[384:512, 1, :] *= np.float32(1e-30)   # tiny (subnormal squares)
+    V[384:512, 1, ::3] = 0.0
+    # strided: heads interleaved with a padding head
+    Kp = np.zeros((128 * 4, n_kv + 1, d), np.float32); Kp[:, :n_kv] = K
+    Vp = np.zeros((128 * 4, n_kv + 1, d), np.float32); Vp[:, :n_kv] = V
+    rec = torch.zeros(4, n_kv, kvarn.tile_bytes(d), dtype=torch.uint8, device=DEV)
+    kd, vd = to_dev(Kp), to_dev(Vp)
+    kvarn.compress_tile(kd[:, :n_kv], vd[:, :n_kv], rec, 4)
+    torch.cuda.synchronize()
+    want = oracle.compress_tiles(K, V, 4)
+    assert np.array_equal(rec.cpu().numpy(), want)
+
+
+def test_compress_prefill_prompt_all_tiles():
+    # the full 8B-shaped prompt: 119 tiles x 8 KV heads = 952 records
+    say("compress 952 records")
+    K, V = synth.make_kv(4, 15488, 8, 128, 2)
+    got = gpu_compress(K, V, 119)
+    want = oracle.compress_tiles(K, V, 119)
+    assert np.array_equal(got, want)
+
+
+# --------------------------------------------------------------------------
+# query rotation
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d", [128, 256, 512])
+def test_rotate_query_matches_oracle_transform(d):
+    say("rotate", d)
+    q = synth.make_q(d, 37, 3, d)
+    got = kvarn.rotate_query(to_dev(q))
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy(), oracle.wht_f32(q))
+
+
+# --------------------------------------------------------------------------
+# decode attention
+# --------------------------------------------------------------------------
+
+def run_decode(q, recs, n_tiles, kw, vw, scale, **kw_args):
+    """q [B][Hq][d]; recs [rows][Hkv][bytes] (numpy); kw/vw [B][cap][Hkv][d]."""
+    qd = to_dev(q)
+    qr = kvarn.rotate_query(qd)
+    rd = to_dev(recs) if recs is not None and recs.size else None
+    out = kvarn.decode_attention(qd, qr, rd, kw_args.pop("rec_start"), n_tiles, to_dev(kw),
+                                 to_dev(vw), kw_args.pop("n_win"), scale, **kw_args)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def test_decode_tiny_tiles_only():
+    say("decode tiny")
+    d = 128
+    K, V = synth.make_kv(0, 512, 1, d, 4)
+    q = synth.make_q(0, 1, 1, d)
+    recs = gpu_compress(K, V, 4)
+    assert np.array_equal(recs, oracle.compress_tiles(K, V, 4))
+    kh, vh = oracle.dequant_records(recs, d)
+    empty = np.zeros((1, 1, 1, d), np.float32)
+    got = run_decode(q, recs, [4], empty, empty, 1 / math.sqrt(d), rec_start=[0], n_win=[0])
+    ref = oracle.decode(q[0], kh, vh, 4, np.zeros((0, 1, d)), np.zeros((0, 1, d)), 1 / math.sqrt(d))
+    assert rel_l2(got[0], ref) < TOL
+
+
+@pytest.mark.parametrize("ctx", [4096, 15488, 32768])
+def test_decode_8b_shape(ctx):
+    say("decode 8b", ctx)
+    d, Hq, Hkv, W = 128, 32, 8, 256
+    T = oracle.visible_tiles(ctx - 1, W)
+    K, V = synth.make_kv(2, ctx, Hkv, d, 2)
+    q = synth.make_q(2, 1, Hq, d)
+    recs = gpu_compress(K, V, T)
+    kh, vh = oracle.dequant_records(recs, d)
+    kw = K[128 * T:][None]
+    vw = V[128 * T:][None]
+    scale = 1 / math.sqrt(d)
+    got = run_decode(q, recs, [T], kw, vw, scale, rec_start=[0], n_win=[ctx - 128 * T])
+    ref = oracle.decode(q[0], kh, vh, T, K[128 * T:], V[128 * T:], scale)
+    err = rel_l2(got[0], ref)
+    say("rel_l2", err)
+    assert err < TOL
+    # spot-check byte parity of a few records against the oracle compressor
+    for j in (0, T // 2, T - 1):
+        want = oracle.compress_tiles(K[128 * j:128 * (j + 1)], V[128 * j:128 * (j + 1)], 1)
+        assert np.array_equal(recs[j:j + 1], want)
+
+
+def test_decode_qwen06b_64_steps_with_appends():
+    say("decode 0.6b steps")
+    d, Hq, Hkv, W = 128, 16, 8, 256
+    steps = 64
+    n0 = 3072 + 256
+    K, V = synth.make_kv(1, n0 + steps, Hkv, d, 4)
+    Q = synth.make_q(1, steps, Hq, d)
+    cache = SequenceCache(Hkv, d, W, capacity=n0 + steps + 128, device=DEV)
+    cache.append(to_dev(K[:n0]), to_dev(V[:n0]))
+    assert cache.n_tiles == 24 and cache.n_win == 256
+    recs_all = cache.records[:24].cpu().numpy()
+    assert np.array_equal(recs_all, oracle.compress_tiles(K, V, 24))
+    kh, vh = oracle.dequant_records(recs_all, d)
+    scale = 1 / math.sqrt(d)
+    worst = 0.0
+    for s in range(steps):
+        cache.append(to_dev(K[n0 + s:n0 + s + 1]), to_dev(V[n0 + s:n0 + s + 1]))
+        qd = to_dev(Q[s:s + 1])
+        qr = kvarn.rotate_query(qd)
+        out = kvarn.decode_attention(qd, qr, cache.records, [0], [cache.n_tiles],
+                                     cache.k[None], cache.v[None], [cache.n_win], scale,
+                                     win_start=[128 * cache.n_tiles])
+        if s % 9 == 0 or s == steps - 1:
+            lo = 128 * cache.n_tiles
+            ref = oracle.decode(Q[s], kh, vh, cache.n_tiles, K[lo:n0 + s + 1], V[lo:n0 + s + 1], scale)
+            worst = max(worst, rel_l2(out[0].cpu().numpy(), ref))
+    assert cache.n_tiles == 24
+    assert worst < TOL
+
+
+@pytest.mark.parametrize("d,Hq,Hkv", [(256, 16, 4), (512, 8, 1)])
+def test_decode_ragged_batch_with_promotions(d, Hq, Hkv):
+    say("decode ragged", d)
+    B, W = 6, 256
+    rng = np.random.default_rng(d)
+    tiles0 = rng.integers(1, 12, size=B)          # small contexts keep the oracle quick
+    caches, KV = [], []
+    for b in range(B):
+        n = int(128 * tiles0[b] + W + rng.integers(0, 128))
+        K, V = synth.make_kv(300 + 10 * b + d, n + 140, Hkv, d, 4)
+        c = SequenceCache(Hkv, d, W, capacity=n + 300, device=DEV)
+        c.append(to_dev(K[:n]), to_dev(V[:n]))
+        caches.append(c)
+        KV.append((K, V, n))
+    scale = 1 / math.sqrt(d)
+    # one shared record pool and window buffer, as the ABI takes them
+    steps = 140
+    for s in range(steps):
+        for b in range(B):
+            K, V, n = KV[b]
+            caches[b].append(to_dev(K[n + s:n + s + 1]), to_dev(V[n + s:n + s + 1]))
+        if s not in (0, 70, steps - 1):
+            continue
+        rows = max(c.n_tiles for c in caches)
+        pool = torch.zeros(B * rows, Hkv, kvarn.tile_bytes(d), dtype=torch.uint8, device=DEV)
+        cap = max(c.n_win for c in caches)
+        kw = torch.zeros(B, cap, Hkv, d, device=DEV)
+        vw = torch.zeros_like(kw)
+        for b, c in enumerate(caches):
+            pool[b * rows:b * rows + c.n_tiles] = c.records[:c.n_tiles]
+            k_, v_ = c.window_views()
+            kw[b, :c.n_win] = k_
+            vw[b, :c.n_win] = v_
+        q = synth.make_q(d + s, B, Hq, d)
+        qd = to_dev(q)
+        out = kvarn.decode_attention(qd, kvarn.rotate_query(qd), pool, [b * rows for b in range(B)],
+                                     [c.n_tiles for c in caches], kw, vw, [c.n_win for c in caches], scale)
+        torch.cuda.synchronize()
+        out = out.cpu().numpy()
+        errs = []
+        for b, c in enumerate(caches):
+            K, V, n = KV[b]
+            recs = c.records[:c.n_tiles].cpu().numpy()
+            assert np.array_equal(recs, oracle.compress_tiles(K, V, c.n_tiles))
+            kh, vh = oracle.dequant_records(recs, d)
+            lo = 128 * c.n_tiles
+            ref = oracle.decode(q[b], kh, vh, c.n_tiles, K[lo:n + s + 1], V[lo:n + s + 1], scale)
+            errs.append(rel_l2(out[b], ref))
+        say("step", s, "max rel_l2", max(errs))
+        assert max(errs) < TOL
+    assert all(c.n_tiles > t for c, t in zip(caches, tiles0))   # every sequence promoted
+
+
+def test_decode_split_plan_invariance_and_determinism():
+    say("decode splits")
+    d, Hq, Hkv, W = 128, 32, 8, 256
+    ctx = 8192
+    T = oracle.visible_tiles(ctx - 1, W)
+    K, V = synth.make_kv(9, ctx, Hkv, d, 2)
+    q = synth.make_q(9, 1, Hq, d)
+    recs = gpu_compress(K, V, T)
+    kw, vw = K[128 * T:][None], V[128 * T:][None]
+    outs = []
+    for max_tiles in (T, T + 5, 4 * T):
+        outs.append(run_decode(q, recs, [T], kw, vw, 0.1, rec_start=[0], n_win=[ctx - 128 * T],
+                               max_tiles=max_tiles, max_win=ctx - 128 * T + 70))
+    assert rel_l2(outs[1], outs[0]) < 1e-6 and rel_l2(outs[2], outs[0]) < 1e-6
+    again = run_decode(q, recs, [T], kw, vw, 0.1, rec_start=[0], n_win=[ctx - 128 * T],
+                       max_tiles=T + 5, max_win=ctx - 128 * T + 70)
+    assert np.array_equal(again, outs[1])
+
+
+# --------------------------------------------------------------------------
+# chunked prefill
+# --------------------------------------------------------------------------
+
+def prefill_run(K, V, Q, W, chunk, Hkv, d):
+    """Feed the prompt in chunks: compress due tiles, rotate, attend."""
+    n = K.shape[0]
+    cache = SequenceCache(Hkv, d, W, capacity=n + 128, device=DEV)
+    outs = []
+    scale = 1 / math.sqrt(d)
+    for p0 in range(0, n, chunk):
+        c = min(chunk, n - p0)
+        cache.append(to_dev(K[p0:p0 + c]), to_dev(V[p0:p0 + c]))
+        qd = to_dev(Q[p0:p0 + c])
+        qr = kvarn.rotate_query(qd)
+        t_first = kvarn.visible_tiles(p0, W)
+        raw_base = 128 * t_first
+        o = kvarn.prefill_attention(qd, qr, cache.records, cache.n_tiles, cache.k[raw_base:],
+                                    cache.v[raw_base:], raw_base, p0, W, scale)
+        outs.append(o)
+    torch.cuda.synchronize()
+    return torch.cat(outs).cpu().numpy(), cache.records[:cache.n_tiles].cpu().numpy()
+
+
+def test_prefill_small_prompt_every_row():
+    say("prefill small")
+    d, Hq, Hkv, W = 128, 8, 2, 256
+    n = 1100
+    K, V = synth.make_kv(21, n, Hkv, d, 2)
+    Q = synth.make_q(21, n, Hq, d)
+    out, recs = prefill_run(K, V, Q, W, 256, Hkv, d)
+    assert np.array_equal(recs, oracle.compress_tiles(K, V, recs.shape[0]))
+    kh, vh = oracle.dequant_records(recs, d)
+    ref = np.stack([oracle.prefill_row(Q[p], p, W, kh, vh, K, V, 1 / math.sqrt(d)) for p in range(n)])
+    assert rel_l2(out, ref) < TOL
+
+
+def test_prefill_8b_prompt_sampled_rows_and_rechunk_identity():
+    say("prefill 8b")
+    d, Hq, Hkv, W = 128, 32, 8, 256
+    n = 15488
+    K, V = synth.make_kv(4, n, Hkv, d, 2)
+    Q = synth.make_q(4, n, Hq, d)
+    out512, recs512 = prefill_run(K, V, Q, W, 512, Hkv, d)
+    assert recs512.shape[0] == 119
+    for chunk in (256, 1024):
+        out_c, recs_c = prefill_run(K, V, Q, W, chunk, Hkv, d)
+        assert np.array_equal(recs_c, recs512)          # tiles are schedule-independent
+        assert rel_l2(out_c, out512) < 1e-6
+    kh, vh = oracle.dequant_records(recs512, d)
+    rows = sorted(set(list(range(0, 1024, 37)) + [383, 384, 511, 512, 639, 640, 8191, 8192, n - 1]
+                      + list(range(0, n, 61))[:60]))
+    ref = np.stack([oracle.prefill_row(Q[p], p, W, kh, vh, K, V, 1 / math.sqrt(d)) for p in rows])
+    err = rel_l2(out512[rows], ref)
+    say("prefill sampled rel_l2", err)
+    assert err < TOL
