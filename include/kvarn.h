@@ -130,7 +130,9 @@ typedef struct kvarn_decode_args {
   float softmax_scale;     /* tau: scores are tau * q.k                         */
   int32_t max_tiles;       /* grid bound: >= n_tiles[b] for every b             */
   const float* q;          /* device [batch][n_q_heads][head_dim] raw query     */
-  const float* q_rot;      /* device [batch][n_q_heads][head_dim] rotated query */
+  const float* q_rot;      /* device [batch][n_q_heads][head_dim] rotated query;
+                              may be NULL when head_dim is 128: the kernel then
+                              rotates q itself                                  */
   const void* records;     /* device record pool; record (b, j, h) at
                               ((rec_start[b] + j)*n_kv_heads + h)*tile_bytes    */
   int64_t n_record_rows;   /* rows in the pool (a row = n_kv_heads records)     */
@@ -151,7 +153,8 @@ typedef struct kvarn_decode_args {
 
 /* Workspace bytes kvarn_decode_attention needs for these arguments (0 on
  * invalid arguments).  The workspace is device memory owned by the caller;
- * its contents need no initialisation and are scratch after the call. */
+ * its contents need no initialisation and are scratch after the call.  Calls
+ * that share a workspace must not overlap in time. */
 size_t kvarn_decode_workspace_bytes(const kvarn_decode_args* args);
 
 /* Errors: KVARN_E_INVALID (null pointers, counts out of range, a sequence with

@@ -14,24 +14,31 @@ bool dim_ok(int32_t d) { return d == 128 || d == 256 || d == 512; }
 bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool st16(int64_t floats) { return (floats % 4) == 0; }
 
-// Work target for the split plan: enough workgroups to cover the 256 CUs a
-// few times over.
+// Work targets for the split plan.  Vector-unit kernels: one workgroup per
+// tile range, enough to cover the 256 CUs several times.  Fused head_dim-128
+// kernel: about two resident workgroups per CU, each streaming its tiles.
 constexpr int64_t kTargetGroups = 2048;
+constexpr int64_t kTargetGroupsFused = 512;
 
 struct DecodePlan {
-  int tps, n_tsplit, n_wsplit;
+  int tps, n_tsplit, n_wsplit, wchunk;
 };
 
-DecodePlan plan_decode(int batch, int n_kv, int max_tiles, int max_win) {
+// target: number of tile workgroups; wchunk: window tokens per window split
+DecodePlan plan_decode(int batch, int n_kv, int max_tiles, int max_win, int64_t target, int wchunk) {
   DecodePlan p;
   const int64_t units = (int64_t)batch * n_kv * (max_tiles > 0 ? max_tiles : 0);
-  int64_t tps = (units + kTargetGroups - 1) / kTargetGroups;
+  int64_t tps = (units + target - 1) / target;
   if (tps < 1) tps = 1;
   p.tps = (int)tps;
   p.n_tsplit = max_tiles > 0 ? (int)((max_tiles + tps - 1) / tps) : 0;
-  p.n_wsplit = max_win > 0 ? (max_win + kvarn::kWinChunk - 1) / kvarn::kWinChunk : 0;
+  p.n_wsplit = max_win > 0 ? (max_win + wchunk - 1) / wchunk : 0;
+  p.wchunk = wchunk;
   return p;
 }
+
+// head_dim 128 decode runs the matrix-core split kernel plus its combine.
+bool fused_decode(int d) { return d == 128; }
 
 int validate_decode(const kvarn_decode_args* a, DecodePlan* plan) {
   if (!a) return KVARN_E_INVALID;
@@ -42,8 +49,8 @@ int validate_decode(const kvarn_decode_args* a, DecodePlan* plan) {
   const int G = a->n_q_heads / a->n_kv_heads;
   if (!(G == 1 || G == 2 || G == 4 || G == 8)) return KVARN_E_UNSUPPORTED;
   if (a->max_tiles < 0 || a->max_win < 0 || a->n_record_rows < 0) return KVARN_E_INVALID;
-  if (!a->q || !a->q_rot || !a->out || !a->n_tiles || !a->n_win || !a->rec_start)
-    return KVARN_E_INVALID;
+  if (!a->q || !a->out || !a->n_tiles || !a->n_win || !a->rec_start) return KVARN_E_INVALID;
+  if (!a->q_rot && !fused_decode(a->head_dim)) return KVARN_E_INVALID;
   bool any_tiles = false, any_win = false;
   for (int b = 0; b < a->batch; ++b) {
     const int nt = a->n_tiles[b], nw = a->n_win[b];
@@ -65,12 +72,26 @@ int validate_decode(const kvarn_decode_args* a, DecodePlan* plan) {
     return KVARN_E_ALIGN;
   if (!st16(a->win_seq_stride) || !st16(a->win_tok_stride) || !st16(a->win_head_stride))
     return KVARN_E_ALIGN;
-  if (plan) *plan = plan_decode(a->batch, a->n_kv_heads, a->max_tiles, a->max_win);
+  if (plan) {
+    const bool f = fused_decode(a->head_dim);
+    const int wchunk = f ? kvarn::kWinChunkFused : kvarn::kWinChunk;
+    int64_t target = kTargetGroups;
+    if (f) {
+      // keep tile + window workgroups within one resident round (2 per CU)
+      const int64_t win_groups = (int64_t)a->batch * a->n_kv_heads * ((a->max_win + wchunk - 1) / wchunk);
+      target = kTargetGroupsFused - win_groups;
+      if (target < kTargetGroupsFused / 2) target = kTargetGroupsFused / 2;
+    }
+    *plan = plan_decode(a->batch, a->n_kv_heads, a->max_tiles, a->max_win, target, wchunk);
+  }
   return KVARN_OK;
 }
 
+size_t decode_part_floats(int batch, int n_q, int d, const DecodePlan& p) {
+  return (size_t)batch * n_q * (size_t)(p.n_tsplit + p.n_wsplit) * (size_t)(d + 4);
+}
 size_t decode_ws(int batch, int n_q, int d, const DecodePlan& p) {
-  return (size_t)batch * n_q * (size_t)(p.n_tsplit + p.n_wsplit) * (size_t)(d + 4) * sizeof(float);
+  return decode_part_floats(batch, n_q, d, p) * sizeof(float);
 }
 
 int64_t prefill_tiles_at(int64_t pos, int window) {
@@ -102,7 +123,8 @@ int validate_prefill(const kvarn_prefill_args* a, DecodePlan* plan) {
     // window tokens of a row are at most W + 127 (fewer when the prompt is short)
     int64_t max_win = a->window + KVARN_TILE_TOKENS - 1;
     if (last + 1 < max_win) max_win = last + 1;
-    *plan = plan_decode(a->chunk, a->n_kv_heads, (int)t_last, (int)max_win);
+    *plan = plan_decode(a->chunk, a->n_kv_heads, (int)t_last, (int)max_win, kTargetGroups,
+                        kvarn::kWinChunk);
   }
   return KVARN_OK;
 }
@@ -166,6 +188,7 @@ int kvarn_decode_attention(const kvarn_decode_args* a, void* workspace, size_t w
   DecodePlan p;
   int st = validate_decode(a, &p);
   if (st != KVARN_OK) return st;
+  const bool fused = fused_decode(a->head_dim);
   const size_t need = decode_ws(a->batch, a->n_q_heads, a->head_dim, p);
   if (!workspace || ws_bytes < need) return KVARN_E_WORKSPACE;
   if (!al16(workspace)) return KVARN_E_ALIGN;
@@ -188,6 +211,7 @@ int kvarn_decode_attention(const kvarn_decode_args* a, void* workspace, size_t w
   P.tps = p.tps;
   P.n_tsplit = p.n_tsplit;
   P.n_wsplit = p.n_wsplit;
+  P.wchunk = p.wchunk;
   P.mode = 0;
   for (int b = 0; b < a->batch; ++b) {
     P.rec_start[b] = a->rec_start[b];
@@ -195,7 +219,8 @@ int kvarn_decode_attention(const kvarn_decode_args* a, void* workspace, size_t w
     P.n_tiles[b] = a->n_tiles[b];
     P.n_win[b] = a->n_win[b];
   }
-  hipError_t e = kvarn::launch_decode(a->head_dim, P, a->batch, (hipStream_t)stream);
+  hipError_t e = fused ? kvarn::launch_decode_fused(P, a->batch, (hipStream_t)stream)
+                       : kvarn::launch_decode(a->head_dim, P, a->batch, (hipStream_t)stream);
   return e == hipSuccess ? KVARN_OK : KVARN_E_DEVICE;
 }
 
@@ -232,6 +257,7 @@ int kvarn_prefill_attention(const kvarn_prefill_args* a, void* workspace, size_t
   P.tps = p.tps;
   P.n_tsplit = p.n_tsplit;
   P.n_wsplit = p.n_wsplit;
+  P.wchunk = p.wchunk;
   P.mode = 1;
   P.window = a->window;
   P.pos0 = a->pos0;

@@ -10,7 +10,8 @@
 namespace kvarn {
 
 constexpr int kDecThreads = 256;
-constexpr int kWinChunk = 64;      // window tokens per split
+constexpr int kWinChunk = 64;      // window tokens per split (vector-unit kernels)
+constexpr int kWinChunkFused = 32; // window tokens per split (fused head_dim-128 kernel)
 
 struct DecodeParams {
   const float* q;
@@ -24,6 +25,7 @@ struct DecodeParams {
   float scale;
   int n_q, n_kv, G;
   int tps, n_tsplit, n_wsplit;
+  int wchunk;                      // window tokens per window split
   // prefill view (mode 1): "sequence" b is query position pos0 + b of one
   // sequence; it sees T(p) tiles and raw rows [128 T(p), p] of k_win/v_win,
   // where raw row p lives at (p - raw_base) * win_tok_stride.
@@ -67,5 +69,6 @@ hipError_t launch_compress(int d, int n_tiles, int n_kv, const float* k, const f
                            hipStream_t stream);
 hipError_t launch_rotate(int d, int64_t n_rows, const float* q, float* q_rot, hipStream_t stream);
 hipError_t launch_decode(int d, const DecodeParams& P, int batch, hipStream_t stream);
+hipError_t launch_decode_fused(const DecodeParams& P, int batch, hipStream_t stream);
 
 }  // namespace kvarn

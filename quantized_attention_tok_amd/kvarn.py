@@ -149,7 +149,7 @@ def _decode_args(q, q_rot, records, n_record_rows, rec_start, n_tiles, k_win, v_
     a.head_dim, a.batch, a.n_q_heads, a.n_kv_heads = d, B, Hq, n_kv
     a.softmax_scale = scale
     a.max_tiles = int(max(n_tiles)) if max_tiles is None else int(max_tiles)
-    a.q, a.q_rot = _ptr(q), _ptr(q_rot)
+    a.q, a.q_rot = _ptr(q), (_ptr(q_rot) if q_rot is not None else None)
     a.records = _ptr(records) if records is not None else None
     a.n_record_rows = n_record_rows
     a.rec_start, a.n_tiles, a.n_win, a.win_start = rs, nt, nw, ws
@@ -166,7 +166,8 @@ def decode_attention(q, q_rot, records, rec_start, n_tiles, k_win, v_win, n_win,
                      win_start=None):
     """Decode attention for a batch.
 
-    q, q_rot: [B][Hq][d] fp32.  records: uint8 pool [rows][Hkv][tile_bytes];
+    q, q_rot: [B][Hq][d] fp32 (q_rot may be None for head_dim 128: the kernel
+    rotates q itself).  records: uint8 pool [rows][Hkv][tile_bytes];
     sequence b's tile j is row rec_start[b] + j.  k_win, v_win: [B][cap][Hkv][d]
     raw windows (strided views allowed, channels contiguous); n_tiles, n_win:
     per-sequence counts (host sequences); win_start: first window row of each
@@ -178,7 +179,7 @@ def decode_attention(q, q_rot, records, rec_start, n_tiles, k_win, v_win, n_win,
                            scale, out, max_tiles, max_win, win_start)
     need = int(lib().kvarn_decode_workspace_bytes(ctypes.byref(a)))
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(max(need, 16), dtype=torch.uint8, device=q.device)
     _check("kvarn_decode_attention", lib().kvarn_decode_attention(
         ctypes.byref(a), _ptr(workspace), workspace.numel(), _stream(stream)))
     return out

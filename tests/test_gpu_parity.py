@@ -315,3 +315,32 @@ def test_prefill_8b_prompt_sampled_rows_and_rechunk_identity():
     err = rel_l2(out512[rows], ref)
     say("prefill sampled rel_l2", err)
     assert err < TOL
+
+
+def test_decode_inkernel_rotation_and_workspace_reuse():
+    say("decode q_rot=None, reused workspace")
+    d, Hq, Hkv, W = 128, 32, 8, 256
+    ctx = 2048 + 256 + 77
+    T = oracle.visible_tiles(ctx - 1, W)
+    K, V = synth.make_kv(31, ctx, Hkv, d, 2)
+    recs = gpu_compress(K, V, T)
+    kh, vh = oracle.dequant_records(recs, d)
+    qd_all = synth.make_q(31, 3, Hq, d)
+    kw = to_dev(K[128 * T:][None]); vw = to_dev(V[128 * T:][None]); rd = to_dev(recs)
+    nb = kvarn.decode_workspace_bytes(to_dev(qd_all[:1]), None, rd, [0], [T], kw, vw, [ctx - 128 * T], 0.1)
+    ws = torch.zeros(nb, dtype=torch.uint8, device=DEV)
+    outs = []
+    for r in range(3):
+        qd = to_dev(qd_all[r:r + 1])
+        outs.append(kvarn.decode_attention(qd, None, rd, [0], [T], kw, vw, [ctx - 128 * T], 0.1,
+                                           workspace=ws))
+    torch.cuda.synchronize()
+    for r in range(3):
+        ref = oracle.decode(qd_all[r], kh, vh, T, K[128 * T:], V[128 * T:], 0.1)
+        assert rel_l2(outs[r][0].cpu().numpy(), ref) < TOL
+    # with an explicit rotated query the result is the same to rounding
+    qd = to_dev(qd_all[:1])
+    o2 = kvarn.decode_attention(qd, kvarn.rotate_query(qd), rd, [0], [T], kw, vw, [ctx - 128 * T], 0.1,
+                                workspace=ws)
+    torch.cuda.synchronize()
+    assert rel_l2(o2[0].cpu().numpy(), outs[0][0].cpu().numpy()) < 1e-6
