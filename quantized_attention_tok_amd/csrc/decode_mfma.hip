@@ -87,75 +87,83 @@ __device__ __forceinline__ float wave_sum16(float v) {
   return v + __shfl_xor(v, 32, 64);
 }
 
-// Per-wave running state of the online softmax for the query heads this lane
-// holds as a column (lane & 15) and the output accumulator for the rows
-// (lane >> 4)*4 + i.
-struct WaveState {
-  float m;          // running max (log2 domain) of head (lane & 15)
-  float l;          // running sum of head (lane & 15)
-  floatx4 o[8];     // o'[head 4*(lane>>4)+i][channel of instance nb]
+// fp16 hi/lo MFMA operands of one tile in LDS, [32-step][hi, lo][row group g]
+// [head] x 8 halves.  Scores: q~ = q' kscale, channels 32 step + 8 g .. + 7 of
+// one head (B operand).  Values: w = p vscale, tokens 32 step + 8 g .. + 7 of
+// one head (A operand).  The two uses never overlap in time, so they share
+// the storage.
+template <int G>
+struct OpTile {
+  uint4 v[4][2][4][G];
 };
 
-// Process one quarter of a tile held in LDS at `rec` (15360 bytes): wave w
-// handles the 32 tokens {8r + 2w, 8r + 2w + 1 : r < 16}, i.e. QK token blocks
-// 2w and 2w+1 and PV token step w, with its own online-softmax stream.  qrot
-// holds the rotated query rows (LDS, [G][128]).
+// Step 1 of a tile, all 256 threads: q~ hi/lo for the G real heads into the
+// operand tile, and the bias b_h = sum_c q'_c kmin_c.  fp16 scale per head
+// from a bound on |q~|: max|q'| of the head times the tile's max kscale
+// (kscale >= 0); the bound only has to keep the hi part finite, the hi/lo
+// split keeps each element's relative precision.
 template <int G>
-__device__ __forceinline__ void tile_quarter(const uint8_t* rec, const float* qrot, float scale_log2,
-                                             WaveState& st, int lane, int w) {
-  const int n = lane & 15;   // MFMA column: query head (QK) / channel slot (PV)
-  const int g = lane >> 4;   // K group / output row group
-  const bool real_head = n < G;
-
-  // ---- q~ = q' * kscale for this lane's head n and channels 32 k4 + 8 g + e ----
-  float qt[4][8];
-  float bias_part = 0.0f;
-  float amax = 0.0f;
+__device__ __forceinline__ void tile_qtilde(const uint8_t* rec, const float* qrot, const float* qmax,
+                                            float kmx, int tid, OpTile<G>& Q, float* s_bias) {
   const float* ks = reinterpret_cast<const float*>(rec + kOffKscale);
   const float* km = reinterpret_cast<const float*>(rec + kOffKmin);
+  constexpr int kItems = G * 32;   // (head, 4 channels)
+  for (int e = tid; e < kItems; e += 256) {
+    const int h = e >> 5, c0 = 4 * (e & 31);
+    const float4 q = *reinterpret_cast<const float4*>(qrot + h * D + c0);
+    const float4 sc = *reinterpret_cast<const float4*>(ks + c0);
+    const float4 mn = *reinterpret_cast<const float4*>(km + c0);
+    float bias = q.x * mn.x + q.y * mn.y + q.z * mn.z + q.w * mn.w;
+    const float f16inv = pow2i(fp16_scale_exp(kmx * qmax[h]) - 4);   // q~ * f / 16
+    const float x0 = q.x * sc.x * f16inv, x1 = q.y * sc.y * f16inv;
+    const float x2 = q.z * sc.z * f16inv, x3 = q.w * sc.w * f16inv;
+    const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1, h2 = (_Float16)x2, h3 = (_Float16)x3;
+    const int k4 = c0 >> 5, g = (c0 >> 3) & 3, part = (c0 >> 2) & 1;
+    reinterpret_cast<uint2*>(&Q.v[k4][0][g][h])[part] = make_uint2(pack_h2(h0, h1), pack_h2(h2, h3));
+    reinterpret_cast<uint2*>(&Q.v[k4][1][g][h])[part] =
+        make_uint2(pack_h2((_Float16)(x0 - (float)h0), (_Float16)(x1 - (float)h1)),
+                   pack_h2((_Float16)(x2 - (float)h2), (_Float16)(x3 - (float)h3)));
 #pragma unroll
-  for (int k4 = 0; k4 < 4; ++k4) {
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-      const int c0 = 32 * k4 + 8 * g + 4 * h2;
-      const float4 sc = *reinterpret_cast<const float4*>(ks + c0);
-      const float4 mn = *reinterpret_cast<const float4*>(km + c0);
-      const float4 q = real_head ? *reinterpret_cast<const float4*>(qrot + n * D + c0) : make_float4(0, 0, 0, 0);
-      qt[k4][4 * h2 + 0] = q.x * sc.x; qt[k4][4 * h2 + 1] = q.y * sc.y;
-      qt[k4][4 * h2 + 2] = q.z * sc.z; qt[k4][4 * h2 + 3] = q.w * sc.w;
-      bias_part += q.x * mn.x + q.y * mn.y + q.z * mn.z + q.w * mn.w;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(qt[k4][4 * h2 + i]));
-    }
+    for (int m = 1; m < 32; m <<= 1) bias += __shfl_xor(bias, m, 64);   // the head's 32 items
+    if ((e & 31) == 0) s_bias[h] = bias;
   }
-  amax = wave_max16(amax);
-  const float bias = wave_sum16(bias_part);
-  const int fexp = fp16_scale_exp(amax);
-  const float f16inv = pow2i(fexp - 4);     // q~ * f / 16
-  const float unscale = pow2i(24 - fexp);   // S = acc * 2^24 / f
+}
 
-  // ---- QK for token blocks 2w (low nibble of byte w) and 2w+1 (high nibble) ----
+// Scores of one tile held in LDS at `rec` for the 32 tokens [32w, 32w + 32)
+// of wave w: lane (g, n) gets s[j][i] = log2-domain score of token
+// 32w + 8g + 2i + j for query head n (columns n >= G are padding).
+//   S^T[t][h] = sum_c zK[t][c] * q~[h][c]
+// on v_mfma_f32_16x16x32_f16, 16 tokens (the low or the high nibble of one
+// code byte) per MFMA row block.
+template <int G>
+__device__ __forceinline__ void tile_scores(const uint8_t* rec, const OpTile<G>& Q, const float* s_bias,
+                                            float qmax_n, float kmx, float scale_log2, int lane, int w,
+                                            float (&s)[2][4]) {
+  const int n = lane & 15;   // MFMA row (A: code byte 16w + n) / column (query head)
+  const int g = lane >> 4;   // K group
+  const float unscale = pow2i(24 - fp16_scale_exp(kmx * qmax_n));   // S = acc * 2^24 / f
   floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  const uint32_t sel = (uint32_t)w | (12u << 8) | ((uint32_t)(4 + w) << 16) | (12u << 24);
+  // byte (n & 3) of two channels' code dwords into the low bytes of two halves
+  const uint32_t nb = (uint32_t)(n & 3);
+  const uint32_t sel = nb | (12u << 8) | ((4u + nb) << 16) | (12u << 24);
+  const int boff = 16 * w + 4 * (n >> 2);
 #pragma unroll
   for (int k4 = 0; k4 < 4; ++k4) {
-    uint32_t bh[4], bl[4];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const float x0 = qt[k4][2 * p] * f16inv, x1 = qt[k4][2 * p + 1] * f16inv;
-      const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
-      bh[p] = pack_h2(h0, h1);
-      bl[p] = pack_h2((_Float16)(x0 - (float)h0), (_Float16)(x1 - (float)h1));
+    uint4 bh = make_uint4(0, 0, 0, 0), bl = make_uint4(0, 0, 0, 0);
+    if (n < G) {
+      bh = Q.v[k4][0][g][n];
+      bl = Q.v[k4][1][g][n];
     }
-    const half8 Bh = as_half8(bh[0], bh[1], bh[2], bh[3]);
-    const half8 Bl = as_half8(bl[0], bl[1], bl[2], bl[3]);
+    const half8 Bh = as_half8(bh.x, bh.y, bh.z, bh.w);
+    const half8 Bl = as_half8(bl.x, bl.y, bl.z, bl.w);
     uint32_t ae[4], ao[4];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      const uint32_t c0 = *reinterpret_cast<const uint32_t*>(rec + (32 * k4 + 8 * g + 2 * p) * 64 + 4 * n);
-      const uint32_t c1 = *reinterpret_cast<const uint32_t*>(rec + (32 * k4 + 8 * g + 2 * p + 1) * 64 + 4 * n);
-      ae[p] = __builtin_amdgcn_perm(c1 << 4, c0 << 4, sel) & 0x00F000F0u;   // 16 z, token 8n + 2w
-      ao[p] = __builtin_amdgcn_perm(c1, c0, sel) & 0x00F000F0u;             // 16 z, token 8n + 2w + 1
+      const int c = 32 * k4 + 8 * g + 2 * p;
+      const uint32_t c0 = *reinterpret_cast<const uint32_t*>(rec + c * 64 + boff);
+      const uint32_t c1 = *reinterpret_cast<const uint32_t*>(rec + (c + 1) * 64 + boff);
+      ae[p] = __builtin_amdgcn_perm(c1 << 4, c0 << 4, sel) & 0x00F000F0u;   // 16 z, token 32w + 2n
+      ao[p] = __builtin_amdgcn_perm(c1, c0, sel) & 0x00F000F0u;             // 16 z, token 32w + 2n + 1
     }
     const half8 Ae = as_half8(ae[0], ae[1], ae[2], ae[3]);
     const half8 Ao = as_half8(ao[0], ao[1], ao[2], ao[3]);
@@ -164,119 +172,70 @@ __device__ __forceinline__ void tile_quarter(const uint8_t* rec, const float* qr
     acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ao, Bh, acc1, 0, 0, 0);
     acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ao, Bl, acc1, 0, 0, 0);
   }
-
-  // ---- scores (log2 domain): s[j][i] is token 8(4g + i) + 2w + j, head n ----
-  const float* ktok = reinterpret_cast<const float*>(rec + kOffKtok);
-  const float* vsc = reinterpret_cast<const float*>(rec + kOffVscale);
-  const float* vmn = reinterpret_cast<const float*>(rec + kOffVmin);
-  float s[2][4], vs[2][4], vm[2][4];
-  float tmax = -INFINITY;
+  const float bias = (n < G) ? s_bias[n] : 0.0f;
+  const float* ktok = reinterpret_cast<const float*>(rec + kOffKtok) + 32 * w + 8 * g;
+  const float4 k0 = *reinterpret_cast<const float4*>(ktok);
+  const float4 k1 = *reinterpret_cast<const float4*>(ktok + 4);
+  const float kt[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int t0 = 8 * (4 * g + i) + 2 * w;
-    const float2 kt = *reinterpret_cast<const float2*>(ktok + t0);
-    const float2 va = *reinterpret_cast<const float2*>(vsc + t0);
-    const float2 ma = *reinterpret_cast<const float2*>(vmn + t0);
-    s[0][i] = scale_log2 * kt.x * (acc0[i] * unscale + bias);
-    s[1][i] = scale_log2 * kt.y * (acc1[i] * unscale + bias);
-    vs[0][i] = va.x; vs[1][i] = va.y; vm[0][i] = ma.x; vm[1][i] = ma.y;
-    tmax = fmaxf(tmax, fmaxf(s[0][i], s[1][i]));
-  }
-  tmax = wave_max16(tmax);
-  const float m_new = fmaxf(st.m, tmax);
-  const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);   // 0 on the first tile
-  float psum = 0.0f, upart = 0.0f, wmax = 0.0f;
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float pj = __builtin_amdgcn_exp2f(s[j][i] - m_new);
-      psum += pj;
-      upart += pj * vm[j][i];
-      wmax = fmaxf(wmax, vs[j][i]);
-      s[j][i] = pj * vs[j][i];          // w = p * vscale
-    }
-  psum = wave_sum16(psum);
-  const float u = wave_sum16(upart);
-  st.l = st.l * alpha + psum;
-  st.m = m_new;
-  wmax = wave_max16(wmax);
-  const int vexp = fp16_scale_exp(wmax);
-  const float fv = pow2i(vexp);
-
-  // ---- PV over token step w: O = W * ZV, 8 channel blocks x (hi, lo) ----
-  uint32_t wh[4], wl[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const float x0 = s[0][q] * fv, x1 = s[1][q] * fv;
-    const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
-    wh[q] = pack_h2(h0, h1);
-    wl[q] = pack_h2((_Float16)(x0 - (float)h0), (_Float16)(x1 - (float)h1));
-  }
-  const half8 Wh = as_half8(wh[0], wh[1], wh[2], wh[3]);
-  const half8 Wl = as_half8(wl[0], wl[1], wl[2], wl[3]);
-  floatx4 po[8];
-  const uint8_t* vcode = rec + kOffV;
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int dw = 4 * qb + (n >> 2);
-    const uint32_t bsel = (uint32_t)(n & 3);
-    const uint32_t vsel = bsel | (12u << 8) | ((4u + bsel) << 16) | (12u << 24);
-    uint32_t pr[4], prs[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int ta = 8 * (4 * g + q) + 2 * w;
-      const uint32_t da = *reinterpret_cast<const uint32_t*>(vcode + ta * (D / 4) + 4 * dw);
-      const uint32_t db = *reinterpret_cast<const uint32_t*>(vcode + (ta + 1) * (D / 4) + 4 * dw);
-      pr[q] = __builtin_amdgcn_perm(db, da, vsel);
-      prs[q] = pr[q] << 4;
-    }
-    // crumb kk lands in bits 4-5 (kk even) or 6-7 (kk odd) of each half
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const uint32_t mask = (kk & 1) ? 0x00C000C0u : 0x00300030u;
-      const half8 Bv = (kk < 2) ? as_half8(prs[0] & mask, prs[1] & mask, prs[2] & mask, prs[3] & mask)
-                                : as_half8(pr[0] & mask, pr[1] & mask, pr[2] & mask, pr[3] & mask);
-      floatx4 z = {0.f, 0.f, 0.f, 0.f};
-      z = __builtin_amdgcn_mfma_f32_16x16x32_f16(Wh, Bv, z, 0, 0, 0);
-      po[4 * qb + kk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Wl, Bv, z, 0, 0, 0);
-    }
-  }
-
-  // ---- fold: o' = o' * alpha_h + vchan_c * (O * 2^24 / (fv 2^shift) + u_h) ----
-  const float* vch = reinterpret_cast<const float*>(rec + kOffVchan);
-  float alpha_r[4], u_r[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    alpha_r[i] = __shfl(alpha, 4 * g + i, 64);
-    u_r[i] = __shfl(u, 4 * g + i, 64);
-  }
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const float4 vc = *reinterpret_cast<const float4*>(vch + 4 * (16 * qb + n));
-    const float vcv[4] = {vc.x, vc.y, vc.z, vc.w};
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int nb = 4 * qb + kk;
-      const float un = pow2i(24 - vexp - ((kk & 1) ? 6 : 4));
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        st.o[nb][i] = st.o[nb][i] * alpha_r[i] + vcv[kk] * (po[nb][i] * un + u_r[i]);
-    }
+    s[0][i] = scale_log2 * kt[2 * i] * (acc0[i] * unscale + bias);
+    s[1][i] = scale_log2 * kt[2 * i + 1] * (acc1[i] * unscale + bias);
   }
 }
 
-// Channel held by output instance nb of lane column n.
-__device__ __forceinline__ int out_channel(int nb, int n) { return 4 * (16 * (nb >> 2) + n) + (nb & 3); }
+// Value aggregate of one tile for wave w's two channel blocks: channels
+// 4(16 qb + n) + kk with qb = w / 2 and kk = 2 (w % 2) + {0, 1}, over all 128
+// tokens (four 32-token steps):  O[h][c] = sum_t w[h][t] zV[t][c].  z2 gets
+// the raw MFMA sums (2-bit codes in bits 4-5 / 6-7 of an fp16 subnormal).
+template <int G>
+__device__ __forceinline__ void tile_values(const uint8_t* rec, const OpTile<G>& W, int lane, int w,
+                                            floatx4& z0, floatx4& z1) {
+  const int n = lane & 15, g = lane >> 4;
+  const uint8_t* vcode = rec + kOffV;
+  const int qb = w >> 1;
+  const uint32_t bsel = (uint32_t)(n & 3);
+  const uint32_t vsel = bsel | (12u << 8) | ((4u + bsel) << 16) | (12u << 24);
+  const int doff = 16 * qb + 4 * (n >> 2);
+  const bool shift = (w & 1) == 0;   // crumbs 0, 1 move up by 4; crumbs 2, 3 are in place
+  z0 = (floatx4){0.f, 0.f, 0.f, 0.f};
+  z1 = (floatx4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ts = 0; ts < 4; ++ts) {
+    uint4 ah = make_uint4(0, 0, 0, 0), al = make_uint4(0, 0, 0, 0);
+    if (n < G) {
+      ah = W.v[ts][0][g][n];
+      al = W.v[ts][1][g][n];
+    }
+    const half8 Ah = as_half8(ah.x, ah.y, ah.z, ah.w);
+    const half8 Al = as_half8(al.x, al.y, al.z, al.w);
+    uint32_t pr[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int t = 32 * ts + 8 * g + 2 * q;
+      const uint32_t da = *reinterpret_cast<const uint32_t*>(vcode + t * (D / 4) + doff);
+      const uint32_t db = *reinterpret_cast<const uint32_t*>(vcode + (t + 1) * (D / 4) + doff);
+      const uint32_t x = __builtin_amdgcn_perm(db, da, vsel);
+      pr[q] = shift ? (x << 4) : x;
+    }
+    const half8 B0 = as_half8(pr[0] & 0x00300030u, pr[1] & 0x00300030u, pr[2] & 0x00300030u, pr[3] & 0x00300030u);
+    const half8 B1 = as_half8(pr[0] & 0x00C000C0u, pr[1] & 0x00C000C0u, pr[2] & 0x00C000C0u, pr[3] & 0x00C000C0u);
+    z0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, B0, z0, 0, 0, 0);
+    z0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(Al, B0, z0, 0, 0, 0);
+    z1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, B1, z1, 0, 0, 0);
+    z1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(Al, B1, z1, 0, 0, 0);
+  }
+}
 
 constexpr int kRow = D + 4;                 // padded window row (528 bytes)
 constexpr int kWinRowsLds = kWinChunkFused; // window rows staged per workgroup
-constexpr int kMax3(int a, int b, int c) { return a > b ? (a > c ? a : c) : (b > c ? b : c); }
-// double-buffered records | window K and V rows | combine reduction [4][2][8][D]
-constexpr int kLdsBytes = kMax3(2 * kRecBytes, 2 * kWinRowsLds * kRow * 4, 4 * 2 * 8 * D * 4);
+constexpr int kMax(int a, int b) { return a > b ? a : b; }
+// tile path: double-buffered records + operand tile; window path: K and V rows
+template <int G>
+constexpr int lds_bytes() { return kMax(2 * kRecBytes + (int)sizeof(OpTile<G>), 2 * kWinRowsLds * kRow * 4); }
 
 template <int G>
-__global__ void __launch_bounds__(256) decode_fused_kernel(DecodeParams P) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) decode_fused_kernel(DecodeParams P) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
@@ -285,9 +244,12 @@ __global__ void __launch_bounds__(256) decode_fused_kernel(DecodeParams P) {
   const int b = blockIdx.z;
   const int n_split = P.n_tsplit + P.n_wsplit;
 
-  __shared__ __attribute__((aligned(16))) uint8_t s_buf[kLdsBytes];   // records / window rows / scratch
+  __shared__ __attribute__((aligned(16))) uint8_t s_buf[lds_bytes<G>()];   // records + w / window rows
   __shared__ __attribute__((aligned(16))) float s_q[G][D];
-  __shared__ float s_ml[4][G][2];
+  __shared__ float s_red[3][4][G];   // per wave: tile max, sum p, sum p * vmin
+  __shared__ float s_ml[G][2];
+  __shared__ float s_qmax[G];
+  __shared__ float s_bias[G];
 
   const SeqView sv = seq_view(P, b);
   const bool is_tile = split < P.n_tsplit;
@@ -333,11 +295,9 @@ __global__ void __launch_bounds__(256) decode_fused_kernel(DecodeParams P) {
     KVARN_LOAD_REC(t_begin);
     // rotated query rows for the G heads
     const float* qsrc = (P.q_rot ? P.q_rot : P.q) + ((int64_t)b * P.n_q + (int64_t)kvh * G) * D;
-    if (P.q_rot) {
-      for (int i = tid; i < G * D; i += 256) s_q[i / D][i % D] = qsrc[i];
-    } else {
-      for (int h = wv; h < G; h += 4) {
-        float x0 = qsrc[h * D + lane], x1 = qsrc[h * D + lane + 64];
+    for (int h = wv; h < G; h += 4) {
+      float x0 = qsrc[h * D + lane], x1 = qsrc[h * D + lane + 64];
+      if (!P.q_rot) {
 #pragma unroll
         for (int m = 1; m < 64; m <<= 1) {
           const bool up = (lane & m) != 0;
@@ -346,61 +306,135 @@ __global__ void __launch_bounds__(256) decode_fused_kernel(DecodeParams P) {
           x1 = up ? (p1 - x1) : (x1 + p1);
         }
         const float a = x0, c = x1;
-        s_q[h][lane] = (a + c) * wht_scale<D>();
-        s_q[h][lane + 64] = (a - c) * wht_scale<D>();
+        x0 = (a + c) * wht_scale<D>();
+        x1 = (a - c) * wht_scale<D>();
       }
+      s_q[h][lane] = x0;
+      s_q[h][lane + 64] = x1;
+      // max |q'| per head (bound for the fp16 operand scale)
+      const float mq = wave_max(fmaxf(fabsf(x0), fabsf(x1)));
+      if (lane == 0) s_qmax[h] = mq;
     }
     KVARN_STORE_REC(0);
     __syncthreads();
-    WaveState st;
-    st.m = -INFINITY;
-    st.l = 0.0f;
-#pragma unroll
-    for (int nb = 0; nb < 8; ++nb) st.o[nb] = (floatx4){0.f, 0.f, 0.f, 0.f};
+    const int n = lane & 15, g = lane >> 4;
+    const float qmax_n = (n < G) ? s_qmax[n] : 0.0f;
     const float scale_log2 = P.scale * kLog2e;
+    OpTile<G>& Op = *reinterpret_cast<OpTile<G>*>(s_buf + 2 * kRecBytes);
+    float m_run = -INFINITY, l_run = 0.0f;   // softmax state of head n (same in every wave)
+    floatx4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = {0.f, 0.f, 0.f, 0.f};   // o'[head 4g + i][channel block]
     int cur = 0;
     for (int tile = t_begin; tile < t_end; ++tile) {
       const bool more = tile + 1 < t_end;
       if (more) KVARN_LOAD_REC(tile + 1);            // in flight during the compute
-      tile_quarter<G>(s_buf + cur * kRecBytes, &s_q[0][0], scale_log2, st, lane, wv);
+      const uint8_t* rec = s_buf + cur * kRecBytes;
+      const float2 kk2 = *reinterpret_cast<const float2*>(rec + kOffKscale + 8 * lane);
+      const float kmx = wave_max(fmaxf(kk2.x, kk2.y));   // tile max kscale
+      tile_qtilde<G>(rec, &s_q[0][0], s_qmax, kmx, tid, Op, s_bias);
+      __syncthreads();
+      float s[2][4];
+      tile_scores<G>(rec, Op, s_bias, qmax_n, kmx, scale_log2, lane, wv, s);
+      float tmax = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                         fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+      tmax = wave_max16(tmax);
+      if (g == 0 && n < G) s_red[0][wv][n] = tmax;
+      // tile-wide fp16 scale for w = p * vscale (p <= 1): max vscale over 128 tokens
+      const float* vsc = reinterpret_cast<const float*>(rec + kOffVscale);
+      const float* vmn = reinterpret_cast<const float*>(rec + kOffVmin);
+      const float2 vv = *reinterpret_cast<const float2*>(vsc + 2 * lane);
+      const int vexp = fp16_scale_exp(wave_max(fmaxf(vv.x, vv.y)));
+      const float fv = pow2i(vexp);
+      __syncthreads();
+      float m_new = m_run;
+      if (n < G) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) m_new = fmaxf(m_new, s_red[0][k][n]);
+      }
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 on the first tile
+      const float* vs8 = vsc + 32 * wv + 8 * g;
+      const float* vm8 = vmn + 32 * wv + 8 * g;
+      const float4 va = *reinterpret_cast<const float4*>(vs8), vb = *reinterpret_cast<const float4*>(vs8 + 4);
+      const float4 ma = *reinterpret_cast<const float4*>(vm8), mb = *reinterpret_cast<const float4*>(vm8 + 4);
+      const float vsv[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
+      const float vmv[8] = {ma.x, ma.y, ma.z, ma.w, mb.x, mb.y, mb.z, mb.w};
+      float psum = 0.0f, upart = 0.0f;
+      uint32_t wh[4], wl[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float x[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const float pj = __builtin_amdgcn_exp2f(s[j][i] - m_new);
+          psum += pj;
+          upart += pj * vmv[2 * i + j];
+          x[j] = pj * vsv[2 * i + j] * fv;
+        }
+        const _Float16 h0 = (_Float16)x[0], h1 = (_Float16)x[1];
+        wh[i] = pack_h2(h0, h1);
+        wl[i] = pack_h2((_Float16)(x[0] - (float)h0), (_Float16)(x[1] - (float)h1));
+      }
+      psum = wave_sum16(psum);
+      upart = wave_sum16(upart);
+      if (n < G) {
+        Op.v[wv][0][g][n] = make_uint4(wh[0], wh[1], wh[2], wh[3]);
+        Op.v[wv][1][g][n] = make_uint4(wl[0], wl[1], wl[2], wl[3]);
+        if (g == 0) {
+          s_red[1][wv][n] = psum;
+          s_red[2][wv][n] = upart;
+        }
+      }
+      __syncthreads();
+      float lsum = 0.0f, u = 0.0f;
+      if (n < G) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) { lsum += s_red[1][k][n]; u += s_red[2][k][n]; }
+      }
+      l_run = l_run * alpha + lsum;
+      m_run = m_new;
+      floatx4 z0, z1;
+      tile_values<G>(rec, Op, lane, wv, z0, z1);
+      // o' = o' alpha_h + vchan_c (O 2^24 / (fv 2^shift) + u_h), shift 4 / 6 for the two crumbs
+      const float4 vc4 = *reinterpret_cast<const float4*>(
+          reinterpret_cast<const float*>(rec + kOffVchan) + 4 * (16 * (wv >> 1) + n));
+      const int kk0 = 2 * (wv & 1);
+      const float vc0 = (wv & 1) ? vc4.z : vc4.x, vc1 = (wv & 1) ? vc4.w : vc4.y;
+      const float un0 = pow2i(24 - vexp - 4), un1 = pow2i(24 - vexp - 6);
+      (void)kk0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float ar = __shfl(alpha, 4 * g + i, 64);
+        const float ur = __shfl(u, 4 * g + i, 64);
+        o0[i] = o0[i] * ar + vc0 * (z0[i] * un0 + ur);
+        o1[i] = o1[i] * ar + vc1 * (z1[i] * un1 + ur);
+      }
       if (more) KVARN_STORE_REC(cur ^ 1);
       __syncthreads();
       cur ^= 1;
     }
 #undef KVARN_LOAD_REC
 #undef KVARN_STORE_REC
-    // ---- merge the 4 waves' streams into one partial ----
-    float* s_o = reinterpret_cast<float*>(s_buf);   // [4][G][D]
-    const int n = lane & 15, g = lane >> 4;
-    if (n < G && g == 0) {
-      s_ml[wv][n][0] = st.m;
-      s_ml[wv][n][1] = st.l;
-    }
+    // ---- the workgroup's partial: o' through LDS for coalesced stores ----
+    float* s_o = reinterpret_cast<float*>(s_buf);   // [G][D]
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int h = 4 * g + i;
-        if (h < G) s_o[(wv * G + h) * D + out_channel(nb, n)] = st.o[nb][i];
+    for (int i = 0; i < 4; ++i) {
+      const int h = 4 * g + i;
+      const int c = 4 * (16 * (wv >> 1) + n) + 2 * (wv & 1);
+      if (h < G) {
+        s_o[h * D + c] = o0[i];
+        s_o[h * D + c + 1] = o1[i];
       }
+    }
+    if (wv == 0 && g == 0 && n < G) {
+      s_ml[n][0] = m_run;
+      s_ml[n][1] = l_run;
+    }
     __syncthreads();
     for (int i = tid; i < G * D; i += 256) {
       const int h = i / D, c = i % D;
-      float M = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) M = fmaxf(M, s_ml[w][h][0]);
-      float L = 0.0f, o = 0.0f;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float mw = s_ml[w][h][0];
-        const float wt = (mw == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
-        L += wt * s_ml[w][h][1];
-        o += wt * s_o[(w * G + h) * D + c];
-      }
-      st_part(&part[h * hs + c], o);
+      st_part(&part[h * hs + c], s_o[i]);
       if (c == 0) {
-        st_part(&part[h * hs + D], M);        // log2 domain
-        st_part(&part[h * hs + D + 1], L);
+        st_part(&part[h * hs + D], s_ml[h][0]);        // log2 domain
+        st_part(&part[h * hs + D + 1], s_ml[h][1]);
       }
     }
   } else {
@@ -468,7 +502,7 @@ __global__ void __launch_bounds__(256) decode_fused_kernel(DecodeParams P) {
       const float p = (lane < nw) ? __builtin_amdgcn_exp2f(sc - m) : 0.0f;
       const float l = wave_sum(p);
       if (lane < kWinRowsLds) s_sc[h * kWinRowsLds + lane] = p;
-      if (lane == 0) { s_ml[0][h][0] = m; s_ml[0][h][1] = l; }
+      if (lane == 0) { s_ml[h][0] = m; s_ml[h][1] = l; }
     }
     __syncthreads();
     for (int i = tid; i < G * D; i += 256) {
@@ -478,8 +512,8 @@ __global__ void __launch_bounds__(256) decode_fused_kernel(DecodeParams P) {
       for (int t = 0; t < kWinRowsLds; ++t) o += s_sc[h * kWinRowsLds + t] * s_v[t * kRow + c];
       st_part(&part[h * hs + c], o);
       if (c == 0) {
-        st_part(&part[h * hs + D], s_ml[0][h][0]);
-        st_part(&part[h * hs + D + 1], s_ml[0][h][1]);
+        st_part(&part[h * hs + D], s_ml[h][0]);
+        st_part(&part[h * hs + D + 1], s_ml[h][1]);
       }
     }
   }
@@ -487,11 +521,16 @@ __global__ void __launch_bounds__(256) decode_fused_kernel(DecodeParams P) {
 }
 
 // ---------------------------------------------------------------------------
-// Combine: one workgroup per (query head, sequence).  Thread (quarter sq, channel
-// pair c2) folds the splits s = sq, sq+4, ... with an online log-sum-exp; the
-// four quarters are merged in LDS; the rotated tile part gets one inverse WHT,
-// the raw window part is added, and the result is divided by L.
+// Combine: one workgroup per (query head, sequence).  Thread (quarter sq,
+// channel pair c2) folds the splits sq, sq + 4, ... with an online
+// log-sum-exp, 128 splits per pass: the pass's (m, l) go through LDS while
+// every thread's 32 partial loads are in flight, so a pass costs one memory
+// round trip.  The four quarters are merged in LDS; the rotated tile part
+// gets one inverse WHT, the raw window part is added, and the result is
+// divided by L.
 // ---------------------------------------------------------------------------
+constexpr int kCombinePass = 128;
+
 __global__ void __launch_bounds__(256) decode_combine128_kernel(DecodeParams P) {
   const int hq = blockIdx.x;
   const int b = blockIdx.y;
@@ -499,42 +538,43 @@ __global__ void __launch_bounds__(256) decode_combine128_kernel(DecodeParams P) 
   const int sq = tid >> 6, c2 = (tid & 63) * 2;
   const int n_split = P.n_tsplit + P.n_wsplit;
   const float* ph = P.part + ((int64_t)b * P.n_q + hq) * (int64_t)n_split * (D + 4);
+  __shared__ float s_pm[kCombinePass], s_pl[kCombinePass];
   __shared__ float s_m[4][64], s_l[4][64];
   __shared__ __attribute__((aligned(16))) float s_o[4][2][D];
-  __shared__ float s_rot[D];
 
   float M = -INFINITY, L = 0.0f;
   float t0 = 0.f, t1 = 0.f, w0 = 0.f, w1 = 0.f;
-  auto fold = [&](int s, float m, float l, float2 v) {
-    if (m == -INFINITY) return;
-    if (m > M) {
-      const float r = __builtin_amdgcn_exp2f(M - m);   // 0 when M = -inf
+  for (int base = 0; base < n_split; base += kCombinePass) {
+    float2 v[kCombinePass / 4];
+#pragma unroll
+    for (int j = 0; j < kCombinePass / 4; ++j) {
+      const int s = base + sq + 4 * j;
+      v[j] = (s < n_split) ? *reinterpret_cast<const float2*>(ph + (int64_t)s * (D + 4) + c2)
+                           : make_float2(0.f, 0.f);
+    }
+    if (tid < kCombinePass) {
+      const int s = base + tid;
+      s_pm[tid] = (s < n_split) ? ph[(int64_t)s * (D + 4) + D] : -INFINITY;
+      s_pl[tid] = (s < n_split) ? ph[(int64_t)s * (D + 4) + D + 1] : 0.0f;
+    }
+    __syncthreads();
+    float mc = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kCombinePass / 4; ++j) mc = fmaxf(mc, s_pm[sq + 4 * j]);
+    if (mc > M) {
+      const float r = __builtin_amdgcn_exp2f(M - mc);   // 0 when M = -inf
       L *= r; t0 *= r; t1 *= r; w0 *= r; w1 *= r;
-      M = m;
-    }
-    const float wt = __builtin_amdgcn_exp2f(m - M);
-    L += wt * l;
-    if (s < P.n_tsplit) { t0 += wt * v.x; t1 += wt * v.y; }
-    else { w0 += wt * v.x; w1 += wt * v.y; }
-  };
-  int s = sq;
-  // batches of 4 splits per thread: all loads of a batch are issued first
-  for (; s + 12 < n_split; s += 16) {
-    float m[4], l[4];
-    float2 v[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float* ps = ph + (int64_t)(s + 4 * j) * (D + 4);
-      m[j] = ps[D];
-      l[j] = ps[D + 1];
-      v[j] = *reinterpret_cast<const float2*>(ps + c2);
+      M = mc;
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) fold(s + 4 * j, m[j], l[j], v[j]);
-  }
-  for (; s < n_split; s += 4) {
-    const float* ps = ph + (int64_t)s * (D + 4);
-    fold(s, ps[D], ps[D + 1], *reinterpret_cast<const float2*>(ps + c2));
+    for (int j = 0; j < kCombinePass / 4; ++j) {
+      const float m = s_pm[sq + 4 * j];
+      const float wt = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - M);
+      L += wt * s_pl[sq + 4 * j];
+      if (base + sq + 4 * j < P.n_tsplit) { t0 += wt * v[j].x; t1 += wt * v[j].y; }
+      else { w0 += wt * v[j].x; w1 += wt * v[j].y; }
+    }
+    __syncthreads();   // s_pm / s_pl are rewritten by the next pass
   }
   s_m[sq][tid & 63] = M;
   s_l[sq][tid & 63] = L;
@@ -578,7 +618,6 @@ __global__ void __launch_bounds__(256) decode_combine128_kernel(DecodeParams P) 
     o[lane] = (r0 + a0) * invL;
     o[lane + 64] = (r1 + a1) * invL;
   }
-  (void)s_rot;
 }
 
 }  // namespace

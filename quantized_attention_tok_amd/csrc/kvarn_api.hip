@@ -18,7 +18,7 @@ bool st16(int64_t floats) { return (floats % 4) == 0; }
 // tile range, enough to cover the 256 CUs several times.  Fused head_dim-128
 // kernel: about two resident workgroups per CU, each streaming its tiles.
 constexpr int64_t kTargetGroups = 2048;
-constexpr int64_t kTargetGroupsFused = 512;
+constexpr int64_t kTargetGroupsFused = 1024;
 
 struct DecodePlan {
   int tps, n_tsplit, n_wsplit, wchunk;
@@ -77,7 +77,7 @@ int validate_decode(const kvarn_decode_args* a, DecodePlan* plan) {
     const int wchunk = f ? kvarn::kWinChunkFused : kvarn::kWinChunk;
     int64_t target = kTargetGroups;
     if (f) {
-      // keep tile + window workgroups within one resident round (2 per CU)
+      // keep tile + window workgroups within one resident round (4 per CU)
       const int64_t win_groups = (int64_t)a->batch * a->n_kv_heads * ((a->max_win + wchunk - 1) / wchunk);
       target = kTargetGroupsFused - win_groups;
       if (target < kTargetGroupsFused / 2) target = kTargetGroupsFused / 2;
