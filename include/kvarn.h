@@ -197,10 +197,13 @@ typedef struct kvarn_prefill_args {
   float* out;              /* device [C][n_q_heads][head_dim]                   */
 } kvarn_prefill_args;
 
+/* Workspace bytes kvarn_prefill_attention needs: 0 (every partial result
+ * stays in registers and LDS); workspace may be NULL. */
 size_t kvarn_prefill_workspace_bytes(const kvarn_prefill_args* args);
 
 /* Errors: KVARN_E_INVALID (null pointers, chunk < 1, pos0 < 0, missing tiles
- * or raw rows), KVARN_E_UNSUPPORTED, KVARN_E_ALIGN, KVARN_E_WORKSPACE. */
+ * or raw rows), KVARN_E_UNSUPPORTED, KVARN_E_ALIGN.  The raw rows
+ * [raw_base, pos0 + C) must be readable. */
 int kvarn_prefill_attention(const kvarn_prefill_args* args, void* workspace,
                             size_t workspace_bytes, void* stream);
 

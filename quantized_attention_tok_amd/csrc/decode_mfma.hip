@@ -36,56 +36,14 @@
 #include <float.h>
 
 #include "kvarn_launch.h"
+#include "kvarn_mfma.h"
 
 namespace kvarn {
 namespace {
 
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef float floatx4 __attribute__((ext_vector_type(4)));
-
-constexpr int D = 128;
-constexpr int kRecBytes = 116 * D + 512;   // 15360
-constexpr int kOffV = 64 * D;              // V codes
-constexpr int kOffKtok = 96 * D;
-constexpr int kOffKscale = 96 * D + 512;
-constexpr int kOffKmin = 100 * D + 512;
-constexpr int kOffVchan = 104 * D + 512;
-constexpr int kOffVscale = 108 * D + 512;
-constexpr int kOffVmin = 112 * D + 512;
-constexpr float kLog2e = 1.4426950408889634f;
-
-__device__ __forceinline__ half8 as_half8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
-  typedef uint32_t u4 __attribute__((ext_vector_type(4)));
-  u4 v = {a, b, c, d};
-  return __builtin_bit_cast(half8, v);
-}
-
-__device__ __forceinline__ uint32_t pack_h2(_Float16 lo, _Float16 hi) {
-  return (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-}
-
-// 2^k as a float for k in [-126, 127].
-__device__ __forceinline__ float pow2i(int k) { return __uint_as_float((uint32_t)(k + 127) << 23); }
-
-// Scale 2^(14-E) that brings max|x| into [2^13, 2^14) (fp16 range with room
-// for the hi/lo split); 1 when max is zero or tiny.
-__device__ __forceinline__ int fp16_scale_exp(float amax) {
-  const int eb = (int)((__float_as_uint(amax) >> 23) & 0xff);   // amax in [2^(eb-127), 2^(eb-126))
-  int k = 140 - eb;
-  if (eb == 0 || k > 100) k = 0;
-  return k;
-}
+using namespace mfma;
 
 __device__ __forceinline__ void st_part(float* p, float v) { *p = v; }
-
-__device__ __forceinline__ float wave_max16(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16, 64));
-  return fmaxf(v, __shfl_xor(v, 32, 64));
-}
-__device__ __forceinline__ float wave_sum16(float v) {
-  v += __shfl_xor(v, 16, 64);
-  return v + __shfl_xor(v, 32, 64);
-}
 
 // fp16 hi/lo MFMA operands of one tile in LDS, [32-step][hi, lo][row group g]
 // [head] x 8 halves.  Scores: q~ = q' kscale, channels 32 step + 8 g .. + 7 of

@@ -225,44 +225,35 @@ int kvarn_decode_attention(const kvarn_decode_args* a, void* workspace, size_t w
 }
 
 size_t kvarn_prefill_workspace_bytes(const kvarn_prefill_args* a) {
-  DecodePlan p;
-  if (validate_prefill(a, &p) != KVARN_OK) return 0;
-  return decode_ws(a->chunk, a->n_q_heads, a->head_dim, p);
+  (void)a;
+  return 0;   // the matrix-core prefill keeps all of its state on chip
 }
 
 int kvarn_prefill_attention(const kvarn_prefill_args* a, void* workspace, size_t ws_bytes,
                             void* stream) {
-  DecodePlan p;
-  int st = validate_prefill(a, &p);
+  (void)workspace;
+  (void)ws_bytes;
+  int st = validate_prefill(a, nullptr);
   if (st != KVARN_OK) return st;
-  const size_t need = decode_ws(a->chunk, a->n_q_heads, a->head_dim, p);
-  if (!workspace || ws_bytes < need) return KVARN_E_WORKSPACE;
-  if (!al16(workspace)) return KVARN_E_ALIGN;
-  kvarn::DecodeParams P;
+  kvarn::PrefillParams P;
   memset(&P, 0, sizeof(P));
   P.q = a->q;
   P.q_rot = a->q_rot;
   P.records = static_cast<const uint8_t*>(a->records);
-  P.k_win = a->k;
-  P.v_win = a->v;
-  P.part = static_cast<float*>(workspace);
+  P.k = a->k;
+  P.v = a->v;
   P.out = a->out;
-  P.win_seq_stride = 0;
-  P.win_tok_stride = a->tok_stride;
-  P.win_head_stride = a->head_stride;
+  P.tok_stride = a->tok_stride;
+  P.head_stride = a->head_stride;
+  P.pos0 = a->pos0;
+  P.raw_base = a->raw_base;
   P.scale = a->softmax_scale;
+  P.chunk = a->chunk;
+  P.window = a->window;
   P.n_q = a->n_q_heads;
   P.n_kv = a->n_kv_heads;
   P.G = a->n_q_heads / a->n_kv_heads;
-  P.tps = p.tps;
-  P.n_tsplit = p.n_tsplit;
-  P.n_wsplit = p.n_wsplit;
-  P.wchunk = p.wchunk;
-  P.mode = 1;
-  P.window = a->window;
-  P.pos0 = a->pos0;
-  P.raw_base = a->raw_base;
-  hipError_t e = kvarn::launch_decode(a->head_dim, P, a->chunk, (hipStream_t)stream);
+  hipError_t e = kvarn::launch_prefill_mfma(P, (hipStream_t)stream);
   return e == hipSuccess ? KVARN_OK : KVARN_E_DEVICE;
 }
 

@@ -38,6 +38,20 @@ struct DecodeParams {
   int n_win[64];
 };
 
+// Chunked prefill of one sequence (head_dim 128 matrix-core kernel).
+struct PrefillParams {
+  const float* q;                  // [chunk][n_q][128] raw
+  const float* q_rot;              // [chunk][n_q][128] rotated
+  const uint8_t* records;          // record (j, h) at (j * n_kv + h) * tile bytes
+  const float* k;                  // raw row of position p, KV head h at
+  const float* v;                  //   (p - raw_base) * tok_stride + h * head_stride
+  float* out;                      // [chunk][n_q][128]
+  int64_t tok_stride, head_stride;
+  int64_t pos0, raw_base;
+  float scale;
+  int chunk, window, n_q, n_kv, G;
+};
+
 // Tiles, window tokens, first record row and window base of sequence b.
 struct SeqView {
   int nt, nw;
@@ -70,5 +84,6 @@ hipError_t launch_compress(int d, int n_tiles, int n_kv, const float* k, const f
 hipError_t launch_rotate(int d, int64_t n_rows, const float* q, float* q_rot, hipStream_t stream);
 hipError_t launch_decode(int d, const DecodeParams& P, int batch, hipStream_t stream);
 hipError_t launch_decode_fused(const DecodeParams& P, int batch, hipStream_t stream);
+hipError_t launch_prefill_mfma(const PrefillParams& P, hipStream_t stream);
 
 }  // namespace kvarn
