@@ -1,0 +1,591 @@
+// decode_split.hip -- split-tile decode attention for head_dim 128 on gfx950.
+//
+// One decode step is two launches (SharpInference issue #433 item 2: fixed
+// worst-case grid with early exit, log-sum-exp combine, inverse WHT applied
+// once to the combined rotated partials; PR #434 commit list: a single
+// streaming softmax over the compressed tiles and the FP32 window):
+//
+//   decode_split_kernel<G, TPW>: workgroup = (split, KV head, sequence) with
+//     4 TPW waves.  Split s owns the tiles [TPW s, TPW s + TPW) and the raw
+//     window tokens [16 s, 16 s + 16) of its sequence.
+//     Tiles: wave (tau, wq) owns the 32-token quarter wq of tile tau from
+//     loads to value aggregate.  It loads only its own slice (the 16 code
+//     bytes of its tokens in every channel row, its 32 V-code rows, its
+//     per-token scales straight into registers), stages the codes in a
+//     private LDS area and needs no barrier once the shared q~ operands are
+//     written, so every wave computes as soon as its own bytes land.
+//       S[(h,part)][t] = sum_c q~[(h,part)][c] zK[t][c]     q~ = q' kscale
+//       O[(h,part)][c] = sum_t w[(h,part)][t] zV[t][c]      w  = p vscale
+//     (issue #180 Algorithm step 4: scales folded in at read time; colibri PR
+//     #399 review note: q . xhat = rotate(q) . code, the cache is never
+//     reconstructed).  Both contractions run on v_mfma_f32_16x16x32_f16.  The
+//     fp32 operand is split into fp16 hi and lo parts that occupy adjacent
+//     MFMA rows, so one MFMA yields both halves of a product for two query
+//     heads and a lane adds them in registers.  Codes enter as fp16
+//     subnormals with the code in bits 4-7 (16 z 2^-24 for nibbles, z 2^-20 or
+//     z 2^-18 for 2-bit codes): products of such subnormals are exact on
+//     gfx950, while codes in bits 0-3 lose precision.
+//     Window tokens: one wave per token scores the raw key with the raw
+//     query (q . k needs no rotation) and rotates the value row (H v), so
+//     every partial of the launch is in the rotated domain.
+//     The waves merge their (m, l, o) states in LDS into one partial per
+//     query head.
+//   decode_combine_kernel: per (query head, sequence), 4 waves merge the
+//     partials with an online log-sum-exp; the sum gets one inverse WHT and
+//     is divided by L.
+//
+// LDS bank conflicts: a wave's K-code rows are stored at channel
+// c ^ ((c / 8) mod 4) and its V-code rows at token t ^ ((t / 8) mod 4), so
+// the byte gathers of one MFMA operand hit distinct banks; the hi/lo operand
+// rows of w use an 80-byte stride.
+//
+// If q_rot is NULL the workgroups rotate the query themselves (the same
+// Walsh-Hadamard butterflies as kvarn_rotate_query).
+#include <float.h>
+
+#include "kvarn_launch.h"
+#include "kvarn_mfma.h"
+
+namespace kvarn {
+namespace {
+
+using namespace mfma;
+
+typedef __fp16 half2v __attribute__((ext_vector_type(2)));
+
+constexpr int kWRow = 20;            // dwords per hi/lo operand row of w (80 bytes)
+constexpr int kKCodeWave = 2048;     // K codes of 32 tokens: 128 channel rows of 16 bytes
+constexpr int kVCodeWave = 1024;     // V codes of 32 tokens: 32 rows of 32 bytes
+constexpr int kCodeWave = kKCodeWave + kVCodeWave;
+
+constexpr int align16(int x) { return (x + 15) / 16 * 16; }
+
+// LDS layout of a split workgroup (G query heads per KV head, TPW tiles).
+template <int G, int TPW>
+struct Lds {
+  static constexpr int kNW = 4 * TPW;                       // waves
+  static constexpr int kRows = 2 * G;                       // operand rows (head, hi|lo)
+  static constexpr int code = 0;                            // [wave] K and V codes of its tokens
+  static constexpr int wop = kNW * kCodeWave;               // [wave][row][kWRow] dwords: w hi/lo
+  static constexpr int wop_wave = kRows * kWRow * 4;
+  static constexpr int qt = wop + kNW * wop_wave;           // [TPW][k4][row][4] uint4: q~ hi/lo
+  static constexpr int qt_tile = 4 * kRows * 64;
+  static constexpr int wins = qt + TPW * qt_tile;           // [G][16] f32: window scores (log2)
+  static constexpr int winw = wins + G * kWinPerSplit * 4;  // [G][16] f32: window weights
+  static constexpr int winv = winw + G * kWinPerSplit * 4;  // [16][D] f32: rotated window values
+  static constexpr int us = winv + kWinPerSplit * D * 4;    // [TPW][G] f32: score unscale
+  static constexpr int bias = us + TPW * G * 4;             // [TPW][G] f32: sum_c q'_c kmin_c
+  static constexpr int fv = bias + TPW * G * 4;             // [TPW] int: w fp16 scale exponent
+  static constexpr int ml = align16(fv + TPW * 4);          // [G][wave] float2: m, l
+  static constexpr int mx = ml + kNW * G * 8;               // [G] f32: workgroup max
+  static constexpr int bytes = mx + G * 4;
+  static constexpr int mo = 0;                              // merge: [wave][G][D] f32 (over codes, w, q~)
+  static_assert(kNW * G * D * 4 <= wins, "merge area fits below the window entries");
+  static_assert((wop % 16) == 0 && (qt % 16) == 0 && (winv % 16) == 0, "aligned sections");
+};
+
+// fp16 hi + lo parts of (a, b): hi rounds toward zero, lo holds the rest.
+__device__ __forceinline__ void split_pair(float a, float b, uint32_t& hi, uint32_t& lo) {
+  const half2v h = __builtin_amdgcn_cvt_pkrtz(a, b);
+  const half2v l = __builtin_amdgcn_cvt_pkrtz(a - (float)h.x, b - (float)h.y);
+  hi = __builtin_bit_cast(uint32_t, h);
+  lo = __builtin_bit_cast(uint32_t, l);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// value of lane (lane ^ M)
+template <int M>
+__device__ __forceinline__ float xshfl(float v) {
+  if constexpr (M == 1) return dpp_f<0xB1>(v);        // quad_perm [1,0,3,2]
+  else if constexpr (M == 2) return dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]
+  else if constexpr (M == 8) return dpp_f<0x128>(v);  // row_ror:8
+  else if constexpr (M == 4 || M == 16)
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), (M << 10) | 0x1F));
+  else return __shfl_xor(v, 32, 64);
+}
+// Walsh-Hadamard butterfly on lane bit M: lower lane a + b, upper lane a - b.
+template <int M>
+__device__ __forceinline__ float bfly(float x, int lane) {
+  const float p = xshfl<M>(x);
+  return (lane & M) ? (p - x) : (x + p);
+}
+// x holds element lane, y element lane + 64 of a 128-vector: y <- H_128 x / sqrt(128)
+__device__ __forceinline__ void wht128(float& x, float& y, int lane) {
+  x = bfly<1>(x, lane); y = bfly<1>(y, lane);
+  x = bfly<2>(x, lane); y = bfly<2>(y, lane);
+  x = bfly<4>(x, lane); y = bfly<4>(y, lane);
+  x = bfly<8>(x, lane); y = bfly<8>(y, lane);
+  x = bfly<16>(x, lane); y = bfly<16>(y, lane);
+  x = bfly<32>(x, lane); y = bfly<32>(y, lane);
+  const float a = x, c = y;
+  x = (a + c) * wht_scale<D>();
+  y = (a - c) * wht_scale<D>();
+}
+
+// Reductions over the 16 lanes of a DPP row (every lane of the row gets it).
+__device__ __forceinline__ float row_max16(float v) {
+  v = fmaxf(v, dpp_f<0x128>(v));   // row_ror:8
+  v = fmaxf(v, dpp_f<0x124>(v));   // row_ror:4
+  v = fmaxf(v, dpp_f<0x122>(v));   // row_ror:2
+  return fmaxf(v, dpp_f<0x121>(v));  // row_ror:1
+}
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dpp_f<0x128>(v);
+  v += dpp_f<0x124>(v);
+  v += dpp_f<0x122>(v);
+  return v + dpp_f<0x121>(v);
+}
+__device__ __forceinline__ float lane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+// whole-wave reductions, uniform result
+__device__ __forceinline__ float wmax(float v) {
+  v = row_max16(v);
+  return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
+}
+__device__ __forceinline__ float wsum(float v) {
+  v = row_sum16(v);
+  return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
+}
+
+template <int G, int TPW>
+__global__ void __launch_bounds__(256 * TPW) decode_split_kernel(DecodeParams P) {
+  using L = Lds<G, TPW>;
+  constexpr int NW = L::kNW;
+  constexpr int NT = 64 * NW;
+  constexpr int kRows = L::kRows;
+  constexpr int PPW = (TPW * G + NW - 1) / NW;         // (tile, head) prep pairs per wave
+  constexpr int KW = (kWinPerSplit + NW - 1) / NW;     // window tokens per wave
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int split = blockIdx.x;
+  const int kvh = blockIdx.y;
+  const int b = blockIdx.z;
+  const int n_split = P.n_tsplit;
+
+  __shared__ __attribute__((aligned(16))) uint8_t lds[L::bytes];
+  float2* s_ml = reinterpret_cast<float2*>(lds + L::ml);
+  float* s_mx = reinterpret_cast<float*>(lds + L::mx);
+  float* s_mo = reinterpret_cast<float*>(lds + L::mo);
+  float* s_wins = reinterpret_cast<float*>(lds + L::wins);
+  float* s_winw = reinterpret_cast<float*>(lds + L::winw);
+  float* s_winv = reinterpret_cast<float*>(lds + L::winv);
+
+  const SeqView sv = seq_view(P, b);
+  float* part = P.part + (((int64_t)b * P.n_q + (int64_t)kvh * G) * n_split + split) * (D + 4);
+  const int64_t hs = (int64_t)n_split * (D + 4);   // partial of head h at part + h * hs
+  const int j0 = split * TPW;
+  const int ntl = max(0, min(TPW, sv.nt - j0));                     // tiles of this split
+  const int nwt = max(0, min(kWinPerSplit, sv.nw - kWinPerSplit * split));   // window tokens
+  if (ntl == 0 && nwt == 0) {
+    for (int i = tid; i < G * (D + 2); i += NT) {
+      const int h = i / (D + 2), c = i % (D + 2);
+      part[h * hs + c] = (c == D) ? -INFINITY : 0.0f;
+    }
+    return;
+  }
+  const float c_log2 = P.scale * kLog2e;
+  const int tau = wv >> 2, wq = wv & 3;
+  const bool has_tile = tau < ntl;
+  const int64_t rstride = (int64_t)P.n_kv * kRecBytes;
+  const uint8_t* recs = P.records + ((sv.rec_row0 + j0) * (int64_t)P.n_kv + kvh) * kRecBytes;
+  const float* qsrc = (P.q_rot ? P.q_rot : P.q) + ((int64_t)b * P.n_q + (int64_t)kvh * G) * D;
+  const float* qraw = P.q + ((int64_t)b * P.n_q + (int64_t)kvh * G) * D;
+
+  // ---- 1. loads, in the order they are consumed ----
+  // (a) prep pairs (tile tt, head h): query row, the tile's kscale / kmin, vscale
+  float pq0[PPW], pq1[PPW], pks0[PPW], pks1[PPW], pkm0[PPW], pkm1[PPW];
+  float2 pvs[PPW];
+#pragma unroll
+  for (int k = 0; k < PPW; ++k) {
+    const int pr = wv + NW * k, tt = pr / G, h = pr % G;
+    pq0[k] = pq1[k] = pks0[k] = pks1[k] = pkm0[k] = pkm1[k] = 0.0f;
+    pvs[k] = make_float2(0.f, 0.f);
+    if (pr < TPW * G && tt < ntl) {
+      const uint8_t* rg = recs + tt * rstride;
+      const float* ks = reinterpret_cast<const float*>(rg + kOffKscale);
+      const float* km = reinterpret_cast<const float*>(rg + kOffKmin);
+      pq0[k] = qsrc[h * D + lane];
+      pq1[k] = qsrc[h * D + lane + 64];
+      pks0[k] = ks[lane];
+      pks1[k] = ks[lane + 64];
+      pkm0[k] = km[lane];
+      pkm1[k] = km[lane + 64];
+      if (h == 0) pvs[k] = *reinterpret_cast<const float2*>(rg + kOffVscale + 8 * lane);
+    }
+  }
+  // (b) own tile slice: K codes of channels lane, lane + 64 (16 bytes each), V codes,
+  //     per-token scales of tokens 32 wq + 2 n, +1, value channel scales
+  const uint8_t* rg = recs + tau * rstride;
+  uint4 kc0 = make_uint4(0, 0, 0, 0), kc1 = kc0, vcd = kc0;
+  float2 kt = make_float2(0.f, 0.f), vsc = kt, vmn = kt;
+  float4 vca = make_float4(0.f, 0.f, 0.f, 0.f), vcb = vca;
+  if (has_tile) {
+    kc0 = *reinterpret_cast<const uint4*>(rg + lane * 64 + 16 * wq);
+    kc1 = *reinterpret_cast<const uint4*>(rg + (lane + 64) * 64 + 16 * wq);
+    vcd = *reinterpret_cast<const uint4*>(rg + kOffV + 32 * 32 * wq + 16 * lane);
+    const int tok = 32 * wq + 2 * n;
+    kt = *reinterpret_cast<const float2*>(rg + kOffKtok + 4 * tok);
+    vsc = *reinterpret_cast<const float2*>(rg + kOffVscale + 4 * tok);
+    vmn = *reinterpret_cast<const float2*>(rg + kOffVmin + 4 * tok);
+    const float* vch = reinterpret_cast<const float*>(rg + kOffVchan) + 16 * (n & 7) + 8 * (n >> 3);
+    vca = *reinterpret_cast<const float4*>(vch);
+    vcb = *reinterpret_cast<const float4*>(vch + 4);
+  }
+  // (c) window tokens wv + NW k of this split: raw key and value rows (elements lane, lane + 64)
+  float wk0[KW], wk1[KW], wv0[KW], wv1[KW], qw0[G], qw1[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    qw0[h] = qw1[h] = 0.0f;
+    if (wv < nwt) {
+      qw0[h] = qraw[h * D + lane];
+      qw1[h] = qraw[h * D + lane + 64];
+    }
+  }
+  const float* kwin = P.k_win + sv.win_off + (int64_t)kvh * P.win_head_stride;
+  const float* vwin = P.v_win + sv.win_off + (int64_t)kvh * P.win_head_stride;
+#pragma unroll
+  for (int k = 0; k < KW; ++k) {
+    wk0[k] = wk1[k] = wv0[k] = wv1[k] = 0.0f;
+    const int tr = wv + NW * k;
+    if (tr < nwt) {
+      const int64_t row = (int64_t)(kWinPerSplit * split + tr) * P.win_tok_stride;
+      wk0[k] = kwin[row + lane];
+      wk1[k] = kwin[row + lane + 64];
+      wv0[k] = vwin[row + lane];
+      wv1[k] = vwin[row + lane + 64];
+    }
+  }
+
+  // ---- 2. prep: rotated query, q~ hi/lo operand rows, unscale, bias, w scale ----
+#pragma unroll
+  for (int k = 0; k < PPW; ++k) {
+    const int pr = wv + NW * k, tt = pr / G, h = pr % G;
+    if (pr < TPW * G && tt < ntl) {   // wave-uniform
+      float x0 = pq0[k], x1 = pq1[k];
+      if (!P.q_rot) wht128(x0, x1, lane);
+      const float y0 = x0 * pks0[k], y1 = x1 * pks1[k];
+      const float amax = wmax(fmaxf(fabsf(y0), fabsf(y1)));
+      const float bias = wsum(x0 * pkm0[k] + x1 * pkm1[k]);
+      const int fe = fp16_scale_exp(amax);   // amax 2^fe in [2^13, 2^14)
+      const float f = pow2i(fe - 4);
+      uint32_t hi, lo;
+      split_pair(y0 * f, y1 * f, hi, lo);   // halves: channel lane, channel lane + 64
+      // channel c -> uint4 [k4 = c / 32][row][g' = (c / 8) % 4], half c % 8
+      uint16_t* qt = reinterpret_cast<uint16_t*>(lds + L::qt + tt * L::qt_tile);
+      const int i0 = (((lane >> 5) * kRows + 2 * h) * 4 + ((lane >> 3) & 3)) * 8 + (lane & 7);
+      const int i1 = i0 + 2 * kRows * 32;   // channel + 64: k4 + 2
+      qt[i0] = (uint16_t)(hi & 0xFFFFu);
+      qt[i0 + 32] = (uint16_t)(lo & 0xFFFFu);   // row 2h + 1
+      qt[i1] = (uint16_t)(hi >> 16);
+      qt[i1 + 32] = (uint16_t)(lo >> 16);
+      if (lane == 0) {
+        reinterpret_cast<float*>(lds + L::us)[tt * G + h] = pow2i(24 - fe);
+        reinterpret_cast<float*>(lds + L::bias)[tt * G + h] = bias;
+      }
+      if (h == 0) {
+        const float vmax = wmax(fmaxf(pvs[k].x, pvs[k].y));   // p <= 1, so w <= max vscale
+        if (lane == 0) reinterpret_cast<int*>(lds + L::fv)[tt] = fp16_scale_exp(vmax);
+      }
+    }
+  }
+  __syncthreads();   // q~ operands and per-tile scalars are ready; codes may still be in flight
+
+  // ---- 3. the wave's tile quarter: tokens 32 wq .. 32 wq + 31 of tile tau ----
+  float m_w[2] = {-INFINITY, -INFINITY}, l_w[2] = {0.f, 0.f};
+  float o_w[2][8];
+#pragma unroll
+  for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+    for (int qb = 0; qb < 8; ++qb) o_w[jj][qb] = 0.0f;
+  if (has_tile) {
+    uint8_t* kcs = lds + L::code + wv * kCodeWave;   // [channel ^ ((channel / 8) % 4)][16 bytes]
+    uint8_t* vcs = kcs + kKCodeWave;                 // [token ^ ((token / 8) % 4)][32 bytes]
+    {
+      const int c0 = lane, c1 = lane + 64;
+      *reinterpret_cast<uint4*>(kcs + (c0 ^ ((c0 >> 3) & 3)) * 16) = kc0;
+      *reinterpret_cast<uint4*>(kcs + (c1 ^ ((c1 >> 3) & 3)) * 16) = kc1;
+      const int t = lane >> 1;
+      *reinterpret_cast<uint4*>(vcs + (t ^ ((t >> 3) & 3)) * 32 + 16 * (lane & 1)) = vcd;
+    }
+    const uint4* qtu = reinterpret_cast<const uint4*>(lds + L::qt + tau * L::qt_tile);
+    // scores: A = q~ rows, B = code nibbles of tokens 2 n, 2 n + 1 (of the quarter)
+    floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k4 = 0; k4 < 4; ++k4) {
+      uint4 a = make_uint4(0, 0, 0, 0);
+      if (n < kRows) a = qtu[(k4 * kRows + n) * 4 + g];
+      const half8 A = as_half8(a.x, a.y, a.z, a.w);
+      uint32_t e[4], o[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int c = 32 * k4 + 8 * g + 2 * i;   // (c >> 3) & 3 == g for c and c + 1
+        const uint32_t x = (uint32_t)kcs[((c ^ g) << 4) + n] | ((uint32_t)kcs[(((c + 1) ^ g) << 4) + n] << 16);
+        e[i] = (x << 4) & 0x00F000F0u;   // token 2 n
+        o[i] = x & 0x00F000F0u;          // token 2 n + 1
+      }
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, as_half8(e[0], e[1], e[2], e[3]), acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, as_half8(o[0], o[1], o[2], o[3]), acc1, 0, 0, 0);
+    }
+    // lane (g, n): rows 4 g + i = (head 2 g + i / 2, part i % 2)
+    const int vexp = reinterpret_cast<const int*>(lds + L::fv)[tau];
+    const float fv = pow2i(vexp);
+    const float k0 = kt.x * c_log2, k1 = kt.y * c_log2;
+    const float vs0 = vsc.x * fv, vs1 = vsc.y * fv;
+    uint32_t* wrow = reinterpret_cast<uint32_t*>(lds + L::wop + wv * L::wop_wave);
+    float u_w[2];
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const int h = 2 * g + jj;
+      const int hc = h < G ? h : G - 1;
+      const float us = reinterpret_cast<const float*>(lds + L::us)[tau * G + hc];
+      const float bi = reinterpret_cast<const float*>(lds + L::bias)[tau * G + hc];
+      const float s0 = k0 * fmaf(acc0[2 * jj] + acc0[2 * jj + 1], us, bi);
+      const float s1 = k1 * fmaf(acc1[2 * jj] + acc1[2 * jj + 1], us, bi);
+      const float mt = row_max16(fmaxf(s0, s1));
+      const float p0 = __builtin_amdgcn_exp2f(s0 - mt), p1 = __builtin_amdgcn_exp2f(s1 - mt);
+      m_w[jj] = mt;
+      l_w[jj] = p0 + p1;                                  // summed over the row in the merge
+      u_w[jj] = row_sum16(p0 * vmn.x + p1 * vmn.y);       // sum_t p vmin over the quarter
+      uint32_t hi, lo;
+      split_pair(p0 * vs0, p1 * vs1, hi, lo);
+      if (h < G) {
+        wrow[(2 * h) * kWRow + n] = hi;
+        wrow[(2 * h + 1) * kWRow + n] = lo;
+      }
+    }
+    // value aggregate: A = w rows of the quarter, B = crumbs of tokens 8 g + j,
+    // channels 16 (n % 8) + 8 (n / 8) + qb
+    uint4 wa = make_uint4(0, 0, 0, 0);
+    if (n < kRows) wa = *reinterpret_cast<const uint4*>(wrow + n * kWRow + 4 * g);
+    const half8 A = as_half8(wa.x, wa.y, wa.z, wa.w);
+    const int vb = 4 * (n & 7) + 2 * (n >> 3);   // first of this lane's two bytes in a token row
+    uint32_t x[2][4];
+#pragma unroll
+    for (int pq = 0; pq < 4; ++pq) {
+      const int t = 8 * g + 2 * pq;
+      const int ra = (t ^ g) * 32 + vb, rb = ((t + 1) ^ g) * 32 + vb;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) x[e][pq] = (uint32_t)vcs[ra + e] | ((uint32_t)vcs[rb + e] << 16);
+    }
+    const float vch[8] = {vca.x, vca.y, vca.z, vca.w, vcb.x, vcb.y, vcb.z, vcb.w};
+    const float un_lo = pow2i(24 - vexp - 4), un_hi = pow2i(24 - vexp - 6);
+#pragma unroll
+    for (int qb = 0; qb < 8; ++qb) {
+      const int e = qb >> 2, cr = qb & 3;
+      const uint32_t mask = (cr & 1) ? 0x00C000C0u : 0x00300030u;
+      uint32_t bv[4];
+#pragma unroll
+      for (int pq = 0; pq < 4; ++pq) bv[pq] = ((cr < 2) ? (x[e][pq] << 4) : x[e][pq]) & mask;
+      const floatx4 z = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, as_half8(bv[0], bv[1], bv[2], bv[3]),
+                                                             (floatx4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      const float un = (cr & 1) ? un_hi : un_lo;
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) o_w[jj][qb] = vch[qb] * fmaf(z[2 * jj] + z[2 * jj + 1], un, u_w[jj]);
+    }
+  }
+
+  // ---- 4. window tokens: raw scores, rotated values ----
+#pragma unroll
+  for (int k = 0; k < KW; ++k) {
+    const int tr = wv + NW * k;
+    if (tr < nwt) {   // wave-uniform
+      float sc[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) sc[h] = qw0[h] * wk0[k] + qw1[h] * wk1[k];
+#pragma unroll
+      for (int h = 0; h < G; ++h) sc[h] = wsum(sc[h]) * c_log2;
+      float v0 = wv0[k], v1 = wv1[k];
+      wht128(v0, v1, lane);
+      s_winv[tr * D + lane] = v0;
+      s_winv[tr * D + lane + 64] = v1;
+      if (lane < G) {
+        float s = sc[0];
+#pragma unroll
+        for (int h = 1; h < G; ++h) s = (lane == h) ? sc[h] : s;
+        s_wins[lane * kWinPerSplit + tr] = s;
+      }
+    }
+  }
+
+  // ---- 5. merge the workgroup's states ----
+  const int n_act = 4 * ntl;   // waves holding a tile state
+#pragma unroll
+  for (int jj = 0; jj < 2; ++jj) {
+    const int h = 2 * g + jj;
+    const float lt = row_sum16(l_w[jj]);
+    if (wv < n_act && n == 0 && h < G) s_ml[h * NW + wv] = make_float2(m_w[jj], lt);
+  }
+  __syncthreads();   // every wave is done with its codes and w rows: the merge area may be written
+  auto head_max = [&](int h) {
+    float M = -INFINITY;
+    for (int w = 0; w < n_act; ++w) M = fmaxf(M, s_ml[h * NW + w].x);
+    for (int t = 0; t < nwt; ++t) M = fmaxf(M, s_wins[h * kWinPerSplit + t]);
+    return M;
+  };
+  if (wv < n_act) {
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const int h = 2 * g + jj;
+      if (h < G) {
+        const float sc = __builtin_amdgcn_exp2f(m_w[jj] - head_max(h));
+        float* dst = s_mo + (wv * G + h) * D + 16 * (n & 7) + 8 * (n >> 3);
+        *reinterpret_cast<float4*>(dst) =
+            make_float4(o_w[jj][0] * sc, o_w[jj][1] * sc, o_w[jj][2] * sc, o_w[jj][3] * sc);
+        *reinterpret_cast<float4*>(dst + 4) =
+            make_float4(o_w[jj][4] * sc, o_w[jj][5] * sc, o_w[jj][6] * sc, o_w[jj][7] * sc);
+      }
+    }
+  }
+  if (tid < G * kWinPerSplit) {
+    const int h = tid / kWinPerSplit, t = tid % kWinPerSplit;
+    if (t < nwt) s_winw[h * kWinPerSplit + t] = __builtin_amdgcn_exp2f(s_wins[h * kWinPerSplit + t] - head_max(h));
+  }
+  if (tid < G) s_mx[tid] = head_max(tid);
+  __syncthreads();
+  for (int i = tid; i < G * D; i += NT) {
+    const int h = i / D, c = i % D;
+    float o = 0.0f;
+    for (int w = 0; w < n_act; ++w) o += s_mo[(w * G + h) * D + c];
+    for (int t = 0; t < nwt; ++t) o += s_winw[h * kWinPerSplit + t] * s_winv[t * D + c];
+    part[h * hs + c] = o;
+    if (c < 2) {
+      const float M = s_mx[h];
+      if (c == 0) {
+        part[h * hs + D] = M;   // log2 domain
+      } else {
+        float l = 0.0f;
+        for (int w = 0; w < n_act; ++w) {
+          const float2 ml = s_ml[h * NW + w];
+          l += __builtin_amdgcn_exp2f(ml.x - M) * ml.y;
+        }
+        for (int t = 0; t < nwt; ++t) l += s_winw[h * kWinPerSplit + t];
+        part[h * hs + D + 1] = l;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Combine: one workgroup of 4 waves per (query head, sequence); lane l owns
+// channels 2l, 2l+1.  Wave w folds splits [32 w + 128 k, +32) with an online
+// log-sum-exp (all loads of a pass in flight, the pass's weights through
+// LDS); the four wave states merge in LDS, wave 0 applies the inverse WHT
+// and divides by L.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) decode_combine_kernel(DecodeParams P) {
+  const int hq = blockIdx.x;
+  const int b = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  const int ns = P.n_tsplit;
+  const float* ph = P.part + ((int64_t)b * P.n_q + hq) * (int64_t)ns * (D + 4);
+  __shared__ float s_w[4][32];
+  __shared__ float s_st[4][2];
+  __shared__ __attribute__((aligned(16))) float s_o[4][D];
+  float M = -INFINITY, Lt = 0.0f, t0 = 0.f, t1 = 0.f;
+  for (int base = 32 * w; base < ns; base += 128) {
+    float2 v[32];
+#pragma unroll
+    for (int j = 0; j < 32; ++j)
+      v[j] = (base + j < ns) ? *reinterpret_cast<const float2*>(ph + (int64_t)(base + j) * (D + 4) + 2 * lane)
+                             : make_float2(0.f, 0.f);
+    float m = -INFINITY, l = 0.0f;
+    if (lane < 32 && base + lane < ns) {
+      const float2 ml = *reinterpret_cast<const float2*>(ph + (int64_t)(base + lane) * (D + 4) + D);
+      m = ml.x;
+      l = ml.y;
+    }
+    const float mc = wmax(m);
+    if (mc > M) {
+      const float r = __builtin_amdgcn_exp2f(M - mc);   // 0 while M = -inf
+      Lt *= r; t0 *= r; t1 *= r;
+      M = mc;
+    }
+    const float wgt = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - M);
+    Lt += wsum(wgt * l);
+    if (lane < 32) s_w[w][lane] = wgt;   // read back by this wave only
+    float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+    for (int j = 0; j < 32; j += 2) {
+      const float w0 = s_w[w][j], w1 = s_w[w][j + 1];
+      t0 += w0 * v[j].x;
+      t1 += w0 * v[j].y;
+      a0 += w1 * v[j + 1].x;
+      a1 += w1 * v[j + 1].y;
+    }
+    t0 += a0;
+    t1 += a1;
+  }
+  if (lane == 0) { s_st[w][0] = M; s_st[w][1] = Lt; }
+  __syncthreads();
+  float Mall = fmaxf(fmaxf(s_st[0][0], s_st[1][0]), fmaxf(s_st[2][0], s_st[3][0]));
+  const float sc = (M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(M - Mall);
+  *reinterpret_cast<float2*>(&s_o[w][2 * lane]) = make_float2(t0 * sc, t1 * sc);
+  __syncthreads();
+  if (w == 0) {
+    float Lall = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float mk = s_st[k][0];
+      Lall += (mk == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mk - Mall) * s_st[k][1];
+    }
+    float x = 0.f, y = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float2 o = *reinterpret_cast<const float2*>(&s_o[k][2 * lane]);
+      x += o.x;
+      y += o.y;
+    }
+    // inverse WHT: channel bit 0 in-lane, bits 1-6 across lanes
+    {
+      const float a = x, c = y;
+      x = a + c;
+      y = a - c;
+    }
+    x = bfly<1>(x, lane); y = bfly<1>(y, lane);
+    x = bfly<2>(x, lane); y = bfly<2>(y, lane);
+    x = bfly<4>(x, lane); y = bfly<4>(y, lane);
+    x = bfly<8>(x, lane); y = bfly<8>(y, lane);
+    x = bfly<16>(x, lane); y = bfly<16>(y, lane);
+    x = bfly<32>(x, lane); y = bfly<32>(y, lane);
+    const float inv = 1.0f / Lall;
+    float* o = P.out + ((int64_t)b * P.n_q + hq) * D + 2 * lane;
+    *reinterpret_cast<float2*>(o) = make_float2(x * wht_scale<D>() * inv, y * wht_scale<D>() * inv);
+  }
+}
+
+template <int G>
+hipError_t launch_split_g(const DecodeParams& P, int batch, hipStream_t stream) {
+  dim3 grid(P.n_tsplit, P.n_kv, batch);
+  switch (P.tps) {
+    case 1: hipLaunchKernelGGL((decode_split_kernel<G, 1>), grid, dim3(256), 0, stream, P); break;
+    case 2: hipLaunchKernelGGL((decode_split_kernel<G, 2>), grid, dim3(512), 0, stream, P); break;
+    case 4: hipLaunchKernelGGL((decode_split_kernel<G, 4>), grid, dim3(1024), 0, stream, P); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode_fused(const DecodeParams& P, int batch, hipStream_t stream) {
+  hipError_t e;
+  switch (P.G) {
+    case 1: e = launch_split_g<1>(P, batch, stream); break;
+    case 2: e = launch_split_g<2>(P, batch, stream); break;
+    case 4: e = launch_split_g<4>(P, batch, stream); break;
+    case 8: e = launch_split_g<8>(P, batch, stream); break;
+    default: return hipErrorInvalidValue;
+  }
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(decode_combine_kernel, dim3(P.n_q, batch), dim3(256), 0, stream, P);
+  return hipGetLastError();
+}
+
+}  // namespace kvarn

@@ -14,11 +14,9 @@ bool dim_ok(int32_t d) { return d == 128 || d == 256 || d == 512; }
 bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool st16(int64_t floats) { return (floats % 4) == 0; }
 
-// Work targets for the split plan.  Vector-unit kernels: one workgroup per
-// tile range, enough to cover the 256 CUs several times.  Fused head_dim-128
-// kernel: about two resident workgroups per CU, each streaming its tiles.
+// Work target for the vector-unit split plan: one workgroup per tile range,
+// enough to cover the 256 CUs several times.
 constexpr int64_t kTargetGroups = 2048;
-constexpr int64_t kTargetGroupsFused = 1024;
 
 struct DecodePlan {
   int tps, n_tsplit, n_wsplit, wchunk;
@@ -39,6 +37,23 @@ DecodePlan plan_decode(int batch, int n_kv, int max_tiles, int max_win, int64_t 
 
 // head_dim 128 decode runs the matrix-core split kernel plus its combine.
 bool fused_decode(int d) { return d == 128; }
+
+// Matrix-core split plan: TPW tiles per workgroup (4 waves per tile): 2 once
+// the batch has enough tiles for 256 such workgroups (measured fastest at the
+// 8B shape for contexts 15488 and 32768), else 1; each split also takes up
+// to 16 window tokens, so there are enough splits for the longest window.
+DecodePlan plan_fused(int batch, int n_kv, int max_tiles, int max_win) {
+  const int64_t units = (int64_t)batch * n_kv * (max_tiles > 0 ? max_tiles : 0);
+  const int tpw = units >= 2 * 256 ? 2 : 1;
+  DecodePlan p;
+  p.tps = tpw;
+  const int nt = max_tiles > 0 ? (max_tiles + tpw - 1) / tpw : 0;
+  const int nw = max_win > 0 ? (max_win + kvarn::kWinPerSplit - 1) / kvarn::kWinPerSplit : 0;
+  p.n_tsplit = nt > nw ? nt : nw;
+  p.n_wsplit = 0;
+  p.wchunk = kvarn::kWinPerSplit;
+  return p;
+}
 
 int validate_decode(const kvarn_decode_args* a, DecodePlan* plan) {
   if (!a) return KVARN_E_INVALID;
@@ -73,16 +88,10 @@ int validate_decode(const kvarn_decode_args* a, DecodePlan* plan) {
   if (!st16(a->win_seq_stride) || !st16(a->win_tok_stride) || !st16(a->win_head_stride))
     return KVARN_E_ALIGN;
   if (plan) {
-    const bool f = fused_decode(a->head_dim);
-    const int wchunk = f ? kvarn::kWinChunkFused : kvarn::kWinChunk;
-    int64_t target = kTargetGroups;
-    if (f) {
-      // keep tile + window workgroups within one resident round (4 per CU)
-      const int64_t win_groups = (int64_t)a->batch * a->n_kv_heads * ((a->max_win + wchunk - 1) / wchunk);
-      target = kTargetGroupsFused - win_groups;
-      if (target < kTargetGroupsFused / 2) target = kTargetGroupsFused / 2;
-    }
-    *plan = plan_decode(a->batch, a->n_kv_heads, a->max_tiles, a->max_win, target, wchunk);
+    *plan = fused_decode(a->head_dim)
+                ? plan_fused(a->batch, a->n_kv_heads, a->max_tiles, a->max_win)
+                : plan_decode(a->batch, a->n_kv_heads, a->max_tiles, a->max_win, kTargetGroups,
+                              kvarn::kWinChunk);
   }
   return KVARN_OK;
 }
