@@ -34,10 +34,9 @@
 //     partials with an online log-sum-exp; the sum gets one inverse WHT and
 //     is divided by L.
 //
-// LDS bank conflicts: a wave's K-code rows are stored at channel
-// c ^ ((c / 8) mod 4) and its V-code rows at token t ^ ((t / 8) mod 4), so
-// the byte gathers of one MFMA operand hit distinct banks; the hi/lo operand
-// rows of w use an 80-byte stride.
+// LDS bank conflicts: a wave's K-code channel rows and V-code token rows are
+// padded by one row every 8 rows, so the byte gathers of one MFMA operand hit
+// distinct banks; the hi/lo operand rows of w use an 80-byte stride.
 //
 // If q_rot is NULL the workgroups rotate the query themselves (the same
 // Walsh-Hadamard butterflies as kvarn_rotate_query).
@@ -54,8 +53,13 @@ using namespace mfma;
 typedef __fp16 half2v __attribute__((ext_vector_type(2)));
 
 constexpr int kWRow = 20;            // dwords per hi/lo operand row of w (80 bytes)
-constexpr int kKCodeWave = 2048;     // K codes of 32 tokens: 128 channel rows of 16 bytes
-constexpr int kVCodeWave = 1024;     // V codes of 32 tokens: 32 rows of 32 bytes
+constexpr int kMRows = 16;           // MFMA operand rows; rows >= 2G stay zero
+// A wave's codes in LDS: K-code channel row c (16 bytes, its 32 tokens) at
+// 16 c + 16 (c / 8); V-code token row t (32 bytes) at 32 (t + t / 8).  The
+// padding puts the rows one MFMA operand gathers in distinct banks while every
+// gather address stays a per-lane base plus a constant offset.
+constexpr int kKCodeWave = 16 * 144;          // 2304
+constexpr int kVCodeWave = 4 * 9 * 32;        // 1152
 constexpr int kCodeWave = kKCodeWave + kVCodeWave;
 
 constexpr int align16(int x) { return (x + 15) / 16 * 16; }
@@ -64,16 +68,21 @@ constexpr int align16(int x) { return (x + 15) / 16 * 16; }
 template <int G, int TPW>
 struct Lds {
   static constexpr int kNW = 4 * TPW;                       // waves
-  static constexpr int kRows = 2 * G;                       // operand rows (head, hi|lo)
+  // MFMA operand rows: head h's fp16 hi and lo parts sit in rows RPH h and
+  // RPH h + 1, so lane group g of an MFMA result holds heads HPL g .. + HPL - 1
+  // (one head per lane group for G <= 4; the other rows stay zero)
+  static constexpr int HPL = G > 4 ? 2 : 1;
+  static constexpr int RPH = 4 / HPL;
   static constexpr int code = 0;                            // [wave] K and V codes of its tokens
-  static constexpr int wop = kNW * kCodeWave;               // [wave][row][kWRow] dwords: w hi/lo
-  static constexpr int wop_wave = kRows * kWRow * 4;
-  static constexpr int qt = wop + kNW * wop_wave;           // [TPW][k4][row][4] uint4: q~ hi/lo
-  static constexpr int qt_tile = 4 * kRows * 64;
+  static constexpr int wop = kNW * kCodeWave;               // [wave][16 rows][kWRow] dwords: w hi/lo
+  static constexpr int wop_wave = kMRows * kWRow * 4;
+  static constexpr int qt = wop + kNW * wop_wave;           // [TPW][k4][16 rows][4] uint4: q~ hi/lo
+  static constexpr int qt_tile = 4 * kMRows * 64;
   static constexpr int wins = qt + TPW * qt_tile;           // [G][16] f32: window scores (log2)
   static constexpr int winw = wins + G * kWinPerSplit * 4;  // [G][16] f32: window weights
   static constexpr int winv = winw + G * kWinPerSplit * 4;  // [16][D] f32: rotated window values
-  static constexpr int us = winv + kWinPerSplit * D * 4;    // [TPW][G] f32: score unscale
+  static constexpr int winp = winv + kWinPerSplit * D * 4;  // [G][16][4] f32: window q . k row sums
+  static constexpr int us = winp + G * kWinPerSplit * 16;   // [TPW][G] f32: score unscale
   static constexpr int bias = us + TPW * G * 4;             // [TPW][G] f32: sum_c q'_c kmin_c
   static constexpr int fv = bias + TPW * G * 4;             // [TPW] int: w fp16 scale exponent
   static constexpr int ml = align16(fv + TPW * 4);          // [G][wave] float2: m, l
@@ -106,11 +115,12 @@ __device__ __forceinline__ float xshfl(float v) {
     return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), (M << 10) | 0x1F));
   else return __shfl_xor(v, 32, 64);
 }
-// Walsh-Hadamard butterfly on lane bit M: lower lane a + b, upper lane a - b.
+// Walsh-Hadamard butterfly on lane bit M: lower lane a + b, upper lane a - b
+// (partner + sign * own, the sign +1 / -1 from the lane's bit M).
 template <int M>
 __device__ __forceinline__ float bfly(float x, int lane) {
-  const float p = xshfl<M>(x);
-  return (lane & M) ? (p - x) : (x + p);
+  const float sg = __int_as_float(0x3F800000 | ((lane & M) ? 0x80000000 : 0));
+  return xshfl<M>(x) + x * sg;
 }
 // x holds element lane, y element lane + 64 of a 128-vector: y <- H_128 x / sqrt(128)
 __device__ __forceinline__ void wht128(float& x, float& y, int lane) {
@@ -125,12 +135,21 @@ __device__ __forceinline__ void wht128(float& x, float& y, int lane) {
   y = (a - c) * wht_scale<D>();
 }
 
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
 // Reductions over the 16 lanes of a DPP row (every lane of the row gets it).
+// The max runs on an integer key with the order of the floats (negative
+// values have their magnitude bits flipped), which needs no NaN handling.
 __device__ __forceinline__ float row_max16(float v) {
-  v = fmaxf(v, dpp_f<0x128>(v));   // row_ror:8
-  v = fmaxf(v, dpp_f<0x124>(v));   // row_ror:4
-  v = fmaxf(v, dpp_f<0x122>(v));   // row_ror:2
-  return fmaxf(v, dpp_f<0x121>(v));  // row_ror:1
+  int k = __float_as_int(v);
+  k ^= (k >> 31) & 0x7FFFFFFF;
+  k = max(k, dpp_i<0x128>(k));   // row_ror:8
+  k = max(k, dpp_i<0x124>(k));   // row_ror:4
+  k = max(k, dpp_i<0x122>(k));   // row_ror:2
+  k = max(k, dpp_i<0x121>(k));   // row_ror:1
+  return __int_as_float(k ^ ((k >> 31) & 0x7FFFFFFF));
 }
 __device__ __forceinline__ float row_sum16(float v) {
   v += dpp_f<0x128>(v);
@@ -156,7 +175,7 @@ __global__ void __launch_bounds__(256 * TPW) decode_split_kernel(DecodeParams P)
   using L = Lds<G, TPW>;
   constexpr int NW = L::kNW;
   constexpr int NT = 64 * NW;
-  constexpr int kRows = L::kRows;
+  constexpr int HPL = L::HPL, RPH = L::RPH;
   constexpr int PPW = (TPW * G + NW - 1) / NW;         // (tile, head) prep pairs per wave
   constexpr int KW = (kWinPerSplit + NW - 1) / NW;     // window tokens per wave
   const int tid = threadIdx.x;
@@ -175,6 +194,7 @@ __global__ void __launch_bounds__(256 * TPW) decode_split_kernel(DecodeParams P)
   float* s_wins = reinterpret_cast<float*>(lds + L::wins);
   float* s_winw = reinterpret_cast<float*>(lds + L::winw);
   float* s_winv = reinterpret_cast<float*>(lds + L::winv);
+  float* s_winp = reinterpret_cast<float*>(lds + L::winp);
 
   const SeqView sv = seq_view(P, b);
   float* part = P.part + (((int64_t)b * P.n_q + (int64_t)kvh * G) * n_split + split) * (D + 4);
@@ -197,51 +217,13 @@ __global__ void __launch_bounds__(256 * TPW) decode_split_kernel(DecodeParams P)
   const float* qsrc = (P.q_rot ? P.q_rot : P.q) + ((int64_t)b * P.n_q + (int64_t)kvh * G) * D;
   const float* qraw = P.q + ((int64_t)b * P.n_q + (int64_t)kvh * G) * D;
 
-  // ---- 1. loads, in the order they are consumed ----
-  // (a) prep pairs (tile tt, head h): query row, the tile's kscale / kmin, vscale
-  float pq0[PPW], pq1[PPW], pks0[PPW], pks1[PPW], pkm0[PPW], pkm1[PPW];
-  float2 pvs[PPW];
-#pragma unroll
-  for (int k = 0; k < PPW; ++k) {
-    const int pr = wv + NW * k, tt = pr / G, h = pr % G;
-    pq0[k] = pq1[k] = pks0[k] = pks1[k] = pkm0[k] = pkm1[k] = 0.0f;
-    pvs[k] = make_float2(0.f, 0.f);
-    if (pr < TPW * G && tt < ntl) {
-      const uint8_t* rg = recs + tt * rstride;
-      const float* ks = reinterpret_cast<const float*>(rg + kOffKscale);
-      const float* km = reinterpret_cast<const float*>(rg + kOffKmin);
-      pq0[k] = qsrc[h * D + lane];
-      pq1[k] = qsrc[h * D + lane + 64];
-      pks0[k] = ks[lane];
-      pks1[k] = ks[lane + 64];
-      pkm0[k] = km[lane];
-      pkm1[k] = km[lane + 64];
-      if (h == 0) pvs[k] = *reinterpret_cast<const float2*>(rg + kOffVscale + 8 * lane);
-    }
-  }
-  // (b) own tile slice: K codes of channels lane, lane + 64 (16 bytes each), V codes,
-  //     per-token scales of tokens 32 wq + 2 n, +1, value channel scales
-  const uint8_t* rg = recs + tau * rstride;
-  uint4 kc0 = make_uint4(0, 0, 0, 0), kc1 = kc0, vcd = kc0;
-  float2 kt = make_float2(0.f, 0.f), vsc = kt, vmn = kt;
-  float4 vca = make_float4(0.f, 0.f, 0.f, 0.f), vcb = vca;
-  if (has_tile) {
-    kc0 = *reinterpret_cast<const uint4*>(rg + lane * 64 + 16 * wq);
-    kc1 = *reinterpret_cast<const uint4*>(rg + (lane + 64) * 64 + 16 * wq);
-    vcd = *reinterpret_cast<const uint4*>(rg + kOffV + 32 * 32 * wq + 16 * lane);
-    const int tok = 32 * wq + 2 * n;
-    kt = *reinterpret_cast<const float2*>(rg + kOffKtok + 4 * tok);
-    vsc = *reinterpret_cast<const float2*>(rg + kOffVscale + 4 * tok);
-    vmn = *reinterpret_cast<const float2*>(rg + kOffVmin + 4 * tok);
-    const float* vch = reinterpret_cast<const float*>(rg + kOffVchan) + 16 * (n & 7) + 8 * (n >> 3);
-    vca = *reinterpret_cast<const float4*>(vch);
-    vcb = *reinterpret_cast<const float4*>(vch + 4);
-  }
-  // (c) window tokens wv + NW k of this split: raw key and value rows (elements lane, lane + 64)
+  // ---- 1. loads.  Window rows first: the waits for the tile loads below then
+  //      never include them.  Inside a split with tiles every wave issues the
+  //      same loads (missing tiles and pairs read tile 0), so the waits are exact.
+  // (read only under the conditions they are loaded under)
   float wk0[KW], wk1[KW], wv0[KW], wv1[KW], qw0[G], qw1[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    qw0[h] = qw1[h] = 0.0f;
     if (wv < nwt) {
       qw0[h] = qraw[h * D + lane];
       qw1[h] = qraw[h * D + lane + 64];
@@ -251,7 +233,6 @@ __global__ void __launch_bounds__(256 * TPW) decode_split_kernel(DecodeParams P)
   const float* vwin = P.v_win + sv.win_off + (int64_t)kvh * P.win_head_stride;
 #pragma unroll
   for (int k = 0; k < KW; ++k) {
-    wk0[k] = wk1[k] = wv0[k] = wv1[k] = 0.0f;
     const int tr = wv + NW * k;
     if (tr < nwt) {
       const int64_t row = (int64_t)(kWinPerSplit * split + tr) * P.win_tok_stride;
@@ -261,92 +242,141 @@ __global__ void __launch_bounds__(256 * TPW) decode_split_kernel(DecodeParams P)
       wv1[k] = vwin[row + lane + 64];
     }
   }
-
-  // ---- 2. prep: rotated query, q~ hi/lo operand rows, unscale, bias, w scale ----
+  uint4 kc0, kc1, vcd;   // (read only by waves with a tile)
+  float2 kt, vsc, vmn;
+  float4 vca, vcb;
+  if (ntl > 0) {   // workgroup-uniform
+    // (a) prep pairs (tile tt, head h): query row, the tile's kscale / kmin / vscale
+    float pq0[PPW], pq1[PPW], pks0[PPW], pks1[PPW], pkm0[PPW], pkm1[PPW];
+    float2 pvs[PPW];
 #pragma unroll
-  for (int k = 0; k < PPW; ++k) {
-    const int pr = wv + NW * k, tt = pr / G, h = pr % G;
-    if (pr < TPW * G && tt < ntl) {   // wave-uniform
-      float x0 = pq0[k], x1 = pq1[k];
-      if (!P.q_rot) wht128(x0, x1, lane);
-      const float y0 = x0 * pks0[k], y1 = x1 * pks1[k];
-      const float amax = wmax(fmaxf(fabsf(y0), fabsf(y1)));
-      const float bias = wsum(x0 * pkm0[k] + x1 * pkm1[k]);
-      const int fe = fp16_scale_exp(amax);   // amax 2^fe in [2^13, 2^14)
-      const float f = pow2i(fe - 4);
-      uint32_t hi, lo;
-      split_pair(y0 * f, y1 * f, hi, lo);   // halves: channel lane, channel lane + 64
-      // channel c -> uint4 [k4 = c / 32][row][g' = (c / 8) % 4], half c % 8
-      uint16_t* qt = reinterpret_cast<uint16_t*>(lds + L::qt + tt * L::qt_tile);
-      const int i0 = (((lane >> 5) * kRows + 2 * h) * 4 + ((lane >> 3) & 3)) * 8 + (lane & 7);
-      const int i1 = i0 + 2 * kRows * 32;   // channel + 64: k4 + 2
-      qt[i0] = (uint16_t)(hi & 0xFFFFu);
-      qt[i0 + 32] = (uint16_t)(lo & 0xFFFFu);   // row 2h + 1
-      qt[i1] = (uint16_t)(hi >> 16);
-      qt[i1 + 32] = (uint16_t)(lo >> 16);
-      if (lane == 0) {
-        reinterpret_cast<float*>(lds + L::us)[tt * G + h] = pow2i(24 - fe);
-        reinterpret_cast<float*>(lds + L::bias)[tt * G + h] = bias;
-      }
-      if (h == 0) {
+    for (int k = 0; k < PPW; ++k) {
+      const int pr = wv + NW * k;
+      const bool ok = pr < TPW * G && pr / G < ntl;
+      const int tt = ok ? pr / G : 0, h = ok ? pr % G : 0;
+      const uint8_t* rp = recs + tt * rstride;
+      const float* ks = reinterpret_cast<const float*>(rp + kOffKscale);
+      const float* km = reinterpret_cast<const float*>(rp + kOffKmin);
+      pq0[k] = qsrc[h * D + lane];
+      pq1[k] = qsrc[h * D + lane + 64];
+      pks0[k] = ks[lane];
+      pks1[k] = ks[lane + 64];
+      pkm0[k] = km[lane];
+      pkm1[k] = km[lane + 64];
+      pvs[k] = *reinterpret_cast<const float2*>(rp + kOffVscale + 8 * lane);
+    }
+    // keep the prep loads ahead of the tile loads in the memory queue
+    asm volatile("" ::: "memory");
+    // (b) own tile slice: K codes of channels lane, lane + 64 (16 bytes each), V codes,
+    //     per-token scales of tokens 32 wq + 2 n, +1, value channel scales
+    {
+      const uint8_t* rg = recs + (has_tile ? tau : 0) * rstride;
+      kc0 = *reinterpret_cast<const uint4*>(rg + lane * 64 + 16 * wq);
+      kc1 = *reinterpret_cast<const uint4*>(rg + (lane + 64) * 64 + 16 * wq);
+      vcd = *reinterpret_cast<const uint4*>(rg + kOffV + 32 * 32 * wq + 16 * lane);
+      const int tok = 32 * wq + 2 * n;
+      kt = *reinterpret_cast<const float2*>(rg + kOffKtok + 4 * tok);
+      vsc = *reinterpret_cast<const float2*>(rg + kOffVscale + 4 * tok);
+      vmn = *reinterpret_cast<const float2*>(rg + kOffVmin + 4 * tok);
+      const float* vch = reinterpret_cast<const float*>(rg + kOffVchan) + 16 * (n & 7) + 8 * (n >> 3);
+      vca = *reinterpret_cast<const float4*>(vch);
+      vcb = *reinterpret_cast<const float4*>(vch + 4);
+    }
+
+    // ---- 2. prep: rotated query, q~ hi/lo operand rows, unscale, bias, w scale ----
+#pragma unroll
+    for (int k = 0; k < PPW; ++k) {
+      const int pr = wv + NW * k, tt = pr / G, h = pr % G;
+      const bool ok = pr < TPW * G && tt < ntl;   // wave-uniform; the math runs either way
+      {
+        float x0 = pq0[k], x1 = pq1[k];
+        if (!P.q_rot) wht128(x0, x1, lane);
+        const float y0 = x0 * pks0[k], y1 = x1 * pks1[k];
+        const float amax = wmax(fmaxf(fabsf(y0), fabsf(y1)));
+        const float bias = wsum(x0 * pkm0[k] + x1 * pkm1[k]);
+        const int fe = fp16_scale_exp(amax);   // amax 2^fe in [2^13, 2^14)
+        const float f = pow2i(fe - 4);
+        uint32_t hi, lo;
+        split_pair(y0 * f, y1 * f, hi, lo);   // halves: channel lane, channel lane + 64
+        // channel c -> uint4 [k4 = c / 32][row][g' = (c / 8) % 4], half c % 8
         const float vmax = wmax(fmaxf(pvs[k].x, pvs[k].y));   // p <= 1, so w <= max vscale
-        if (lane == 0) reinterpret_cast<int*>(lds + L::fv)[tt] = fp16_scale_exp(vmax);
+        if (ok) {
+          uint16_t* qt = reinterpret_cast<uint16_t*>(lds + L::qt + tt * L::qt_tile);
+          const int i0 = (((lane >> 5) * kMRows + RPH * h) * 4 + ((lane >> 3) & 3)) * 8 + (lane & 7);
+          const int i1 = i0 + 2 * kMRows * 32;   // channel + 64: k4 + 2
+          qt[i0] = (uint16_t)(hi & 0xFFFFu);
+          qt[i0 + 32] = (uint16_t)(lo & 0xFFFFu);   // row RPH h + 1
+          qt[i1] = (uint16_t)(hi >> 16);
+          qt[i1 + 32] = (uint16_t)(lo >> 16);
+          if (lane == 0) {
+            reinterpret_cast<float*>(lds + L::us)[tt * G + h] = pow2i(24 - fe);
+            reinterpret_cast<float*>(lds + L::bias)[tt * G + h] = bias;
+            if (h == 0) reinterpret_cast<int*>(lds + L::fv)[tt] = fp16_scale_exp(vmax);
+          }
+        }
       }
+    }
+  }
+  // q~ operand rows that hold no head part stay zero
+  if constexpr (RPH > 2 || G < 8) {
+    for (int i = tid; i < TPW * 4 * kMRows * 4; i += NT) {
+      const int r = (i >> 2) & (kMRows - 1);
+      if ((r % RPH) >= 2 || r / RPH >= G) reinterpret_cast<uint4*>(lds + L::qt)[i] = make_uint4(0, 0, 0, 0);
     }
   }
   __syncthreads();   // q~ operands and per-tile scalars are ready; codes may still be in flight
 
   // ---- 3. the wave's tile quarter: tokens 32 wq .. 32 wq + 31 of tile tau ----
-  float m_w[2] = {-INFINITY, -INFINITY}, l_w[2] = {0.f, 0.f};
-  float o_w[2][8];
-#pragma unroll
-  for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-    for (int qb = 0; qb < 8; ++qb) o_w[jj][qb] = 0.0f;
+  float m_w[HPL], l_w[HPL], o_w[HPL][8];   // (set and read only by waves with a tile)
   if (has_tile) {
-    uint8_t* kcs = lds + L::code + wv * kCodeWave;   // [channel ^ ((channel / 8) % 4)][16 bytes]
-    uint8_t* vcs = kcs + kKCodeWave;                 // [token ^ ((token / 8) % 4)][32 bytes]
+    uint8_t* kcs = lds + L::code + wv * kCodeWave;   // channel row c at 16 c + 16 (c / 8)
+    uint8_t* vcs = kcs + kKCodeWave;                 // token row t at 32 (t + t / 8)
     {
       const int c0 = lane, c1 = lane + 64;
-      *reinterpret_cast<uint4*>(kcs + (c0 ^ ((c0 >> 3) & 3)) * 16) = kc0;
-      *reinterpret_cast<uint4*>(kcs + (c1 ^ ((c1 >> 3) & 3)) * 16) = kc1;
+      *reinterpret_cast<uint4*>(kcs + 16 * c0 + 16 * (c0 >> 3)) = kc0;
+      *reinterpret_cast<uint4*>(kcs + 16 * c1 + 16 * (c1 >> 3)) = kc1;
       const int t = lane >> 1;
-      *reinterpret_cast<uint4*>(vcs + (t ^ ((t >> 3) & 3)) * 32 + 16 * (lane & 1)) = vcd;
+      *reinterpret_cast<uint4*>(vcs + 32 * (t + (t >> 3)) + 16 * (lane & 1)) = vcd;
     }
     const uint4* qtu = reinterpret_cast<const uint4*>(lds + L::qt + tau * L::qt_tile);
     // scores: A = q~ rows, B = code nibbles of tokens 2 n, 2 n + 1 (of the quarter)
     floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    const uint8_t* kg = kcs + 144 * g + n;   // channel 32 k4 + 8 g + j at kg[576 k4 + 16 j]
 #pragma unroll
     for (int k4 = 0; k4 < 4; ++k4) {
-      uint4 a = make_uint4(0, 0, 0, 0);
-      if (n < kRows) a = qtu[(k4 * kRows + n) * 4 + g];
+      const uint4 a = qtu[(k4 * kMRows + n) * 4 + g];
       const half8 A = as_half8(a.x, a.y, a.z, a.w);
       uint32_t e[4], o[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int c = 32 * k4 + 8 * g + 2 * i;   // (c >> 3) & 3 == g for c and c + 1
-        const uint32_t x = (uint32_t)kcs[((c ^ g) << 4) + n] | ((uint32_t)kcs[(((c + 1) ^ g) << 4) + n] << 16);
+        const uint32_t x = (uint32_t)kg[576 * k4 + 32 * i] | ((uint32_t)kg[576 * k4 + 32 * i + 16] << 16);
         e[i] = (x << 4) & 0x00F000F0u;   // token 2 n
         o[i] = x & 0x00F000F0u;          // token 2 n + 1
       }
       acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, as_half8(e[0], e[1], e[2], e[3]), acc0, 0, 0, 0);
       acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, as_half8(o[0], o[1], o[2], o[3]), acc1, 0, 0, 0);
     }
-    // lane (g, n): rows 4 g + i = (head 2 g + i / 2, part i % 2)
+    // lane (g, n): rows 4 g + i = (head HPL g + i / RPH, part i % RPH)
     const int vexp = reinterpret_cast<const int*>(lds + L::fv)[tau];
     const float fv = pow2i(vexp);
     const float k0 = kt.x * c_log2, k1 = kt.y * c_log2;
     const float vs0 = vsc.x * fv, vs1 = vsc.y * fv;
     uint32_t* wrow = reinterpret_cast<uint32_t*>(lds + L::wop + wv * L::wop_wave);
-    float u_w[2];
+    if constexpr (RPH > 2 || G < 8) {   // w rows that hold no head part stay zero
+      for (int i = lane; i < kMRows * (kWRow / 4); i += 64) {
+        const int r = i / (kWRow / 4);
+        if ((r % RPH) >= 2 || r / RPH >= G) reinterpret_cast<uint4*>(wrow)[i] = make_uint4(0, 0, 0, 0);
+      }
+    }
+    float u_w[HPL];
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-      const int h = 2 * g + jj;
+    for (int jj = 0; jj < HPL; ++jj) {
+      const int h = HPL * g + jj;
       const int hc = h < G ? h : G - 1;
       const float us = reinterpret_cast<const float*>(lds + L::us)[tau * G + hc];
       const float bi = reinterpret_cast<const float*>(lds + L::bias)[tau * G + hc];
-      const float s0 = k0 * fmaf(acc0[2 * jj] + acc0[2 * jj + 1], us, bi);
-      const float s1 = k1 * fmaf(acc1[2 * jj] + acc1[2 * jj + 1], us, bi);
+      const float s0 = k0 * fmaf(acc0[RPH * jj] + acc0[RPH * jj + 1], us, bi);
+      const float s1 = k1 * fmaf(acc1[RPH * jj] + acc1[RPH * jj + 1], us, bi);
       const float mt = row_max16(fmaxf(s0, s1));
       const float p0 = __builtin_amdgcn_exp2f(s0 - mt), p1 = __builtin_amdgcn_exp2f(s1 - mt);
       m_w[jj] = mt;
@@ -355,23 +385,21 @@ __global__ void __launch_bounds__(256 * TPW) decode_split_kernel(DecodeParams P)
       uint32_t hi, lo;
       split_pair(p0 * vs0, p1 * vs1, hi, lo);
       if (h < G) {
-        wrow[(2 * h) * kWRow + n] = hi;
-        wrow[(2 * h + 1) * kWRow + n] = lo;
+        wrow[(RPH * h) * kWRow + n] = hi;
+        wrow[(RPH * h + 1) * kWRow + n] = lo;
       }
     }
     // value aggregate: A = w rows of the quarter, B = crumbs of tokens 8 g + j,
     // channels 16 (n % 8) + 8 (n / 8) + qb
-    uint4 wa = make_uint4(0, 0, 0, 0);
-    if (n < kRows) wa = *reinterpret_cast<const uint4*>(wrow + n * kWRow + 4 * g);
+    const uint4 wa = *reinterpret_cast<const uint4*>(wrow + n * kWRow + 4 * g);
     const half8 A = as_half8(wa.x, wa.y, wa.z, wa.w);
-    const int vb = 4 * (n & 7) + 2 * (n >> 3);   // first of this lane's two bytes in a token row
+    // token 8 g + j at vg[32 j]; this lane's two bytes at + 0, + 1
+    const uint8_t* vg = vcs + 288 * g + 4 * (n & 7) + 2 * (n >> 3);
     uint32_t x[2][4];
 #pragma unroll
     for (int pq = 0; pq < 4; ++pq) {
-      const int t = 8 * g + 2 * pq;
-      const int ra = (t ^ g) * 32 + vb, rb = ((t + 1) ^ g) * 32 + vb;
 #pragma unroll
-      for (int e = 0; e < 2; ++e) x[e][pq] = (uint32_t)vcs[ra + e] | ((uint32_t)vcs[rb + e] << 16);
+      for (int e = 0; e < 2; ++e) x[e][pq] = (uint32_t)vg[64 * pq + e] | ((uint32_t)vg[64 * pq + 32 + e] << 16);
     }
     const float vch[8] = {vca.x, vca.y, vca.z, vca.w, vcb.x, vcb.y, vcb.z, vcb.w};
     const float un_lo = pow2i(24 - vexp - 4), un_hi = pow2i(24 - vexp - 6);
@@ -386,7 +414,7 @@ __global__ void __launch_bounds__(256 * TPW) decode_split_kernel(DecodeParams P)
                                                              (floatx4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
       const float un = (cr & 1) ? un_hi : un_lo;
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj) o_w[jj][qb] = vch[qb] * fmaf(z[2 * jj] + z[2 * jj + 1], un, u_w[jj]);
+      for (int jj = 0; jj < HPL; ++jj) o_w[jj][qb] = vch[qb] * fmaf(z[RPH * jj] + z[RPH * jj + 1], un, u_w[jj]);
     }
   }
 
@@ -397,43 +425,47 @@ __global__ void __launch_bounds__(256 * TPW) decode_split_kernel(DecodeParams P)
     if (tr < nwt) {   // wave-uniform
       float sc[G];
 #pragma unroll
-      for (int h = 0; h < G; ++h) sc[h] = qw0[h] * wk0[k] + qw1[h] * wk1[k];
-#pragma unroll
-      for (int h = 0; h < G; ++h) sc[h] = wsum(sc[h]) * c_log2;
+      for (int h = 0; h < G; ++h) sc[h] = row_sum16(qw0[h] * wk0[k] + qw1[h] * wk1[k]);
       float v0 = wv0[k], v1 = wv1[k];
       wht128(v0, v1, lane);
       s_winv[tr * D + lane] = v0;
       s_winv[tr * D + lane + 64] = v1;
-      if (lane < G) {
-        float s = sc[0];
+      if (n == 0) {   // the four row sums of each head's q . k
 #pragma unroll
-        for (int h = 1; h < G; ++h) s = (lane == h) ? sc[h] : s;
-        s_wins[lane * kWinPerSplit + tr] = s;
+        for (int h = 0; h < G; ++h) s_winp[(h * kWinPerSplit + tr) * 4 + g] = sc[h];
       }
     }
   }
 
   // ---- 5. merge the workgroup's states ----
   const int n_act = 4 * ntl;   // waves holding a tile state
-#pragma unroll
-  for (int jj = 0; jj < 2; ++jj) {
-    const int h = 2 * g + jj;
-    const float lt = row_sum16(l_w[jj]);
-    if (wv < n_act && n == 0 && h < G) s_ml[h * NW + wv] = make_float2(m_w[jj], lt);
-  }
-  __syncthreads();   // every wave is done with its codes and w rows: the merge area may be written
-  auto head_max = [&](int h) {
-    float M = -INFINITY;
-    for (int w = 0; w < n_act; ++w) M = fmaxf(M, s_ml[h * NW + w].x);
-    for (int t = 0; t < nwt; ++t) M = fmaxf(M, s_wins[h * kWinPerSplit + t]);
-    return M;
-  };
   if (wv < n_act) {
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-      const int h = 2 * g + jj;
+    for (int jj = 0; jj < HPL; ++jj) {
+      const int h = HPL * g + jj;
+      const float lt = row_sum16(l_w[jj]);
+      if (n == 0 && h < G) s_ml[h * NW + wv] = make_float2(m_w[jj], lt);
+    }
+  }
+  __syncthreads();   // every wave is done with its codes and w rows: the merge area may be written
+  if (tid < G) {   // head max; window scores (log2 domain) from their row sums
+    float M = -INFINITY;
+    for (int w = 0; w < n_act; ++w) M = fmaxf(M, s_ml[tid * NW + w].x);
+    for (int t = 0; t < nwt; ++t) {
+      const float4 r = *reinterpret_cast<const float4*>(s_winp + 4 * (tid * kWinPerSplit + t));
+      const float sc = ((r.x + r.y) + (r.z + r.w)) * c_log2;
+      s_wins[tid * kWinPerSplit + t] = sc;
+      M = fmaxf(M, sc);
+    }
+    s_mx[tid] = M;
+  }
+  __syncthreads();
+  if (wv < n_act) {
+#pragma unroll
+    for (int jj = 0; jj < HPL; ++jj) {
+      const int h = HPL * g + jj;
       if (h < G) {
-        const float sc = __builtin_amdgcn_exp2f(m_w[jj] - head_max(h));
+        const float sc = __builtin_amdgcn_exp2f(m_w[jj] - s_mx[h]);
         float* dst = s_mo + (wv * G + h) * D + 16 * (n & 7) + 8 * (n >> 3);
         *reinterpret_cast<float4*>(dst) =
             make_float4(o_w[jj][0] * sc, o_w[jj][1] * sc, o_w[jj][2] * sc, o_w[jj][3] * sc);
@@ -444,9 +476,20 @@ __global__ void __launch_bounds__(256 * TPW) decode_split_kernel(DecodeParams P)
   }
   if (tid < G * kWinPerSplit) {
     const int h = tid / kWinPerSplit, t = tid % kWinPerSplit;
-    if (t < nwt) s_winw[h * kWinPerSplit + t] = __builtin_amdgcn_exp2f(s_wins[h * kWinPerSplit + t] - head_max(h));
+    if (t < nwt) s_winw[h * kWinPerSplit + t] = __builtin_amdgcn_exp2f(s_wins[h * kWinPerSplit + t] - s_mx[h]);
   }
-  if (tid < G) s_mx[tid] = head_max(tid);
+  if (tid >= NT - G) {   // L of head h (any lane of the last wave)
+    const int h = tid - (NT - G);
+    const float M = s_mx[h];
+    float l = 0.0f;
+    for (int w = 0; w < n_act; ++w) {
+      const float2 ml = s_ml[h * NW + w];
+      l += __builtin_amdgcn_exp2f(ml.x - M) * ml.y;
+    }
+    for (int t = 0; t < nwt; ++t) l += __builtin_amdgcn_exp2f(s_wins[h * kWinPerSplit + t] - M);
+    part[h * hs + D] = M;   // log2 domain
+    part[h * hs + D + 1] = l;
+  }
   __syncthreads();
   for (int i = tid; i < G * D; i += NT) {
     const int h = i / D, c = i % D;
@@ -454,20 +497,6 @@ __global__ void __launch_bounds__(256 * TPW) decode_split_kernel(DecodeParams P)
     for (int w = 0; w < n_act; ++w) o += s_mo[(w * G + h) * D + c];
     for (int t = 0; t < nwt; ++t) o += s_winw[h * kWinPerSplit + t] * s_winv[t * D + c];
     part[h * hs + c] = o;
-    if (c < 2) {
-      const float M = s_mx[h];
-      if (c == 0) {
-        part[h * hs + D] = M;   // log2 domain
-      } else {
-        float l = 0.0f;
-        for (int w = 0; w < n_act; ++w) {
-          const float2 ml = s_ml[h * NW + w];
-          l += __builtin_amdgcn_exp2f(ml.x - M) * ml.y;
-        }
-        for (int t = 0; t < nwt; ++t) l += s_winw[h * kWinPerSplit + t];
-        part[h * hs + D + 1] = l;
-      }
-    }
   }
 }
 
