@@ -4,21 +4,28 @@
 Headline workload: Qwen3-8B-shaped single-layer batch-1 decode at a context of
 15488 tokens (119 compressed 128-token tiles + a 256-token FP32 window; 32
 query heads, 8 KV heads, head_dim 128).  One step = one kvarn_decode_attention
-launch that rotates the query, scores and aggregates every tile on the matrix
-cores and the window on the vector units, and combines the split partials with
-LSE weights and one inverse WHT.  To keep
-the caches honest the timed loop cycles through enough distinct layers (records
-+ windows + queries) to exceed the 256 MB last-level cache, all resident in HBM
-before timing starts; the step sequence is captured once in a HIP graph.
+call: the split kernel (query rotation, every tile on the matrix cores, the
+window tokens) and the log-sum-exp combine with its inverse WHT.  To keep the
+caches honest the timed loop cycles through enough distinct layers (records +
+windows + queries) to exceed twice the 256 MB last-level cache, all resident
+in HBM before timing starts; the step sequence is captured once in a HIP
+graph and timed with events on the replay stream, so the per-step time is the
+device time of the two kernels back to back.
 
-The same JSON line carries: the decode attention launch's achieved HBM
-bandwidth against the 8 TB/s peak (roofline), chunked-prefill throughput of
-the 15488-token prompt (512-token chunks), compression throughput, and the CPU
-oracle timed on a bounded sample of the decode workload (cpu_baseline).
+The same JSON line carries: the decode call's achieved algorithmic HBM
+bandwidth against the 8 TB/s peak (roofline), decode at contexts 4096 and
+32768, chunked-prefill throughput of the 15488-token prompt in 512-token
+chunks (compress + rotate + prefill attention, one graph), compression
+throughput, and the CPU oracle timed on a bounded sample of the decode
+workload (cpu_baseline).
+
+--calibration-copy adds one device-to-device copy of a known size, for
+scaling hardware byte counters taken over the same run.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -31,7 +38,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+INT8_MFMA_PEAK_TOPS = 5000.0
 LLC_BYTES = 256 << 20
+CSRC = os.path.join(ROOT, "quantized_attention_tok_amd", "csrc")
+DECODE_SOURCES = ["decode_split.hip", "kvarn_mfma.h", "kvarn_launch.h", "kvarn_device.h", "kvarn_api.hip"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic_ctx15488.json")
 
 
 def log(*a):
@@ -39,20 +50,101 @@ def log(*a):
 
 
 def decode_bytes(T, n_w, Hq, Hkv, d, tile_bytes):
-    """Algorithmic bytes of one decode attention launch: every record and window
-    row read once, the query read once, the output written once."""
-    return T * Hkv * tile_bytes + 2 * n_w * Hkv * d * 4 + 2 * Hq * d * 4 + Hq * d * 4
+    """Algorithmic bytes of one decode call: every record and window row read
+    once, the query read once, the output written once."""
+    return T * Hkv * tile_bytes + 2 * n_w * Hkv * d * 4 + Hq * d * 4 + Hq * d * 4
 
 
-def time_graph(torch, g, replays):
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+def decode_sources_sha():
+    h = hashlib.sha256()
+    for f in DECODE_SOURCES:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per decode call from the committed counter summary, if it was
+    taken on the current decode sources; else None."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("decode_sources_sha") != decode_sources_sha():
+        return None
+    return t.get("hbm_bytes_per_call")
+
+
+def graph_ms(torch, fn, n_inner, reps):
+    """Capture fn() (n_inner steps) in a graph; return ms per step over reps replays."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    g.replay()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     s.record()
-    for _ in range(replays):
+    for _ in range(reps):
         g.replay()
     e.record()
     e.synchronize()
-    return s.elapsed_time(e)
+    return s.elapsed_time(e) / (reps * n_inner), g
+
+
+def decode_case(torch, kvarn, synth, ctx, steps, warmup, seed=2):
+    d, Hq, Hkv, W = 128, 32, 8, 256
+    dev = "cuda:0"
+    T = kvarn.visible_tiles(ctx - 1, W)
+    n_w = ctx - 128 * T
+    tb = kvarn.tile_bytes(d)
+    scale = 1.0 / math.sqrt(d)
+    per_layer = T * Hkv * tb + 2 * n_w * Hkv * d * 4
+    L = max(8, int(math.ceil(2 * LLC_BYTES / per_layer)))
+    K, V = synth.make_kv(seed, ctx, Hkv, d, synth.outliers_for(d, 0.01))
+    kd = torch.from_numpy(K).to(dev)
+    vd = torch.from_numpy(V).to(dev)
+    rec0 = torch.empty(T, Hkv, tb, dtype=torch.uint8, device=dev)
+    kvarn.compress_tile(kd, vd, rec0, T)
+    recs = [rec0.clone() for _ in range(L)]
+    kw = [kd[128 * T:].clone()[None] for _ in range(L)]
+    vw = [vd[128 * T:].clone()[None] for _ in range(L)]
+    qs = torch.from_numpy(synth.make_q(seed, L, Hq, d)).to(dev).reshape(L, 1, Hq, d)
+    outs = torch.empty_like(qs)
+    ws_bytes = kvarn.decode_workspace_bytes(qs[0], None, recs[0], [0], [T], kw[0], vw[0], [n_w], scale)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def run():
+        for l in range(L):
+            # q_rot=None: the split kernel rotates q itself
+            kvarn.decode_attention(qs[l], None, recs[l], [0], [T], kw[l], vw[l], [n_w], scale,
+                                   out=outs[l], workspace=ws)
+
+    reps = max(1, int(math.ceil(steps / L)))
+    warm = max(1, int(math.ceil(warmup / L)))
+    _, g = graph_ms(torch, run, L, 1)
+    for _ in range(warm):
+        g.replay()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        g.replay()
+    e.record()
+    e.synchronize()
+    ms = s.elapsed_time(e) / (reps * L)
+    alg = decode_bytes(T, n_w, Hq, Hkv, d, tb)
+    info = {"context": ctx, "tiles": T, "window": n_w, "layers_cycled": L, "us_per_step": ms * 1e3,
+            "kv_tokens_per_s": ctx / (ms * 1e-3), "algorithmic_bytes": alg,
+            "achieved_GBps": alg / (ms * 1e-3) / 1e9}
+    return info, reps * L, warm * L, (K, V, rec0, T, n_w, qs, scale)
 
 
 def main():
@@ -62,7 +154,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=64)
     ap.add_argument("--context", type=int, default=15488)
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-extra-contexts", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibration-copy", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
@@ -76,98 +170,42 @@ def main():
     dev = "cuda:0"
     kvarn.lib()  # fails loudly if the HIP library is missing
     d, Hq, Hkv, W = 128, 32, 8, 256
-    ctx = args.context
-    T = kvarn.visible_tiles(ctx - 1, W)
-    n_w = ctx - 128 * T
-    tb = kvarn.tile_bytes(d)
-    scale = 1.0 / math.sqrt(d)
-    per_layer = T * Hkv * tb + 2 * n_w * Hkv * d * 4
-    L = max(8, int(math.ceil(2 * LLC_BYTES / per_layer)))
-    steps = int(math.ceil(args.steps / L)) * L
-    warm = int(math.ceil(max(args.warmup, 1) / L)) * L
-    log(f"context {ctx}: {T} tiles + {n_w} window tokens; {L} layers of {per_layer / 2**20:.1f} MiB")
 
-    # ---- inputs resident in HBM ----
-    K, V = synth.make_kv(2, ctx, Hkv, d, synth.outliers_for(d, 0.01))
-    kd = torch.from_numpy(K).to(dev)
-    vd = torch.from_numpy(V).to(dev)
-    rec0 = torch.empty(T, Hkv, tb, dtype=torch.uint8, device=dev)
-    kvarn.compress_tile(kd, vd, rec0, T)
-    recs = [rec0.clone() for _ in range(L)]
-    kw = [kd[128 * T:].clone()[None] for _ in range(L)]
-    vw = [vd[128 * T:].clone()[None] for _ in range(L)]
-    qs = torch.from_numpy(synth.make_q(2, L, Hq, d)).to(dev).reshape(L, 1, Hq, d)
-    qr = torch.empty_like(qs)
-    outs = torch.empty_like(qs)
-    ws_bytes = kvarn.decode_workspace_bytes(qs[0], qs[0], recs[0], [0], [T], kw[0], vw[0], [n_w], scale)
-    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
-    torch.cuda.synchronize()
-
-    def step(l):
-        # one launch: query rotation, tile and window partials, LSE combine,
-        # inverse WHT (q_rot=None makes the kernel rotate q itself)
-        kvarn.decode_attention(qs[l], None, recs[l], [0], [T], kw[l], vw[l], [n_w], scale,
-                               out=outs[l], workspace=ws)
-
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        for l in range(L):
-            step(l)
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
-
-    g_step = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g_step):
-        for l in range(L):
-            step(l)
-
-    time_graph(torch, g_step, warm // L)
-    ms = time_graph(torch, g_step, steps // L)
-    ms_step = ms / steps
-    # per-launch kernel time: HIP events bracketing each launch on its stream
-    n_ev = 4 * L
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_ev)]
-    torch.cuda.synchronize()
-    for i in range(n_ev):
-        ev[i][0].record()
-        step(i % L)
-        ev[i][1].record()
-    torch.cuda.synchronize()
-    ms_attn = sorted(a.elapsed_time(e) for a, e in ev)[n_ev // 2]
-    alg = decode_bytes(T, n_w, Hq, Hkv, d, tb)
-    achieved = alg / (ms_attn * 1e-3) / 1e9
-    value = ctx / (ms_step * 1e-3)
-    log(f"step {ms_step * 1e3:.2f} us (graph), launch {ms_attn * 1e3:.2f} us (events, median), "
-        f"{achieved:.0f} GB/s algorithmic")
+    head, steps, warm, keep = decode_case(torch, kvarn, synth, args.context, args.steps, args.warmup)
+    log(f"decode context {head['context']}: {head['us_per_step']:.2f} us per call, "
+        f"{head['achieved_GBps']:.0f} GB/s algorithmic")
+    extra = []
+    if not args.no_extra_contexts:
+        for c in (4096, 32768):
+            if c != args.context:
+                info, _, _, _ = decode_case(torch, kvarn, synth, c, 320, 32)
+                extra.append(info)
+                log(f"decode context {c}: {info['us_per_step']:.2f} us per call, "
+                    f"{info['achieved_GBps']:.0f} GB/s algorithmic")
 
     # ---- compression throughput (the prompt's 119 x 8 tile-heads in one launch) ----
+    K, V, rec0, T, n_w, qs, scale = keep
+    kd = torch.from_numpy(K).to(dev)
+    vd = torch.from_numpy(V).to(dev)
     recc = torch.empty_like(rec0)
-    g_c = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(side):
-        kvarn.compress_tile(kd, vd, recc, T)
-    torch.cuda.synchronize()
-    with torch.cuda.graph(g_c):
-        kvarn.compress_tile(kd, vd, recc, T)
-    time_graph(torch, g_c, 3)
-    n_c = 20
-    ms_c = time_graph(torch, g_c, n_c) / n_c
-    c_bytes = T * Hkv * (2 * 128 * d * 4 + tb)
-    compress = {"tile_heads_per_s": T * Hkv / (ms_c * 1e-3), "ms_per_launch": ms_c,
-                "achieved_GBps": c_bytes / (ms_c * 1e-3) / 1e9}
-    log(f"compress {T * Hkv} tile-heads: {ms_c:.3f} ms")
+    ms_c, _ = graph_ms(torch, lambda: kvarn.compress_tile(kd, vd, recc, T), 1, 20)
+    c_bytes = T * Hkv * (2 * 128 * d * 4 + kvarn.tile_bytes(d))
+    compress = {"tile_heads": T * Hkv, "us_per_launch": ms_c * 1e3,
+                "tile_heads_per_s": T * Hkv / (ms_c * 1e-3), "achieved_GBps": c_bytes / (ms_c * 1e-3) / 1e9}
+    log(f"compress {T * Hkv} tile-heads: {ms_c * 1e3:.1f} us")
 
-    # ---- chunked prefill of the 15488-token prompt ----
+    # ---- chunked prefill of the 15488-token prompt (one graph of all chunks) ----
     prefill = None
     if not args.no_prefill:
         n, chunk = 15488, 512
         Kp, Vp = synth.make_kv(4, n, Hkv, d, synth.outliers_for(d, 0.01))
         Qp = synth.make_q(4, n, Hq, d)
         kp, vp, qp = (torch.from_numpy(x).to(dev) for x in (Kp, Vp, Qp))
-        pre_ws = torch.empty(1 << 28, dtype=torch.uint8, device=dev)
+        outp = torch.empty_like(qp)
+        cache = SequenceCache(Hkv, d, W, capacity=n + 128, device=dev)
 
         def run_prefill():
-            cache = SequenceCache(Hkv, d, W, capacity=n + 128, device=dev)
+            cache.n_tokens = cache.n_tiles = 0
             for p0 in range(0, n, chunk):
                 c = min(chunk, n - p0)
                 cache.append(kp[p0:p0 + c], vp[p0:p0 + c])
@@ -175,19 +213,24 @@ def main():
                 q_r = kvarn.rotate_query(q_c)
                 rb = 128 * kvarn.visible_tiles(p0, W)
                 kvarn.prefill_attention(q_c, q_r, cache.records, cache.n_tiles, cache.k[rb:],
-                                        cache.v[rb:], rb, p0, W, scale, workspace=pre_ws)
-            return cache
+                                        cache.v[rb:], rb, p0, W, 1.0 / math.sqrt(d), out=outp[p0:p0 + c])
 
-        run_prefill()
+        ms_p, _ = graph_ms(torch, run_prefill, 1, 3)
+        pairs = n * (n + 1) // 2                            # causal (query, key) pairs per head
+        ops = 2 * 2 * d * pairs * Hq                         # Q.K and P.V multiply-adds as 2 ops each
+        prefill = {"tokens_per_s": n / (ms_p * 1e-3), "ms": ms_p, "prompt": n, "chunk": chunk,
+                   "algorithmic_TOPS": ops / (ms_p * 1e-3) / 1e12,
+                   "int8_mfma_frac": ops / (ms_p * 1e-3) / 1e12 / INT8_MFMA_PEAK_TOPS,
+                   "includes": "raw row copies, tile compression, query rotation, prefill attention"}
+        log(f"prefill {n} tokens: {ms_p:.2f} ms")
+
+    if args.calibration_copy:
+        src = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
         torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        reps = 2
-        for _ in range(reps):
-            run_prefill()
+        dst.copy_(src)
         torch.cuda.synchronize()
-        sec = (time.perf_counter() - t0) / reps
-        prefill = {"tokens_per_s": n / sec, "ms": sec * 1e3, "prompt": n, "chunk": chunk}
-        log(f"prefill {n} tokens: {sec * 1e3:.1f} ms")
+        log("calibration copy: 64 MiB device to device")
 
     # ---- CPU oracle baseline on a bounded sample ----
     cpu = None
@@ -206,15 +249,20 @@ def main():
         sec = time.perf_counter() - t0
         if lim is not None:
             lim.unregister()
+        ctx = head["context"]
         cpu = {"value": ctx / sec, "unit": "KV tokens/s", "cores": 1, "kind": "oracle",
                "sample": f"one decode step of the 8B-shaped layer at context {ctx}: dequantise "
                          f"{T * Hkv} records to fp64 and attend 32 heads over {ctx} keys "
-                         f"({sec:.1f} s on one host core)"}
-        log(f"cpu oracle: {sec:.1f} s per decode step")
+                         f"({sec:.2f} s on one host core)"}
+        log(f"cpu oracle: {sec:.2f} s per decode step")
 
+    ms_step = head["us_per_step"] * 1e-3
+    alg = head["algorithmic_bytes"]
+    achieved = head["achieved_GBps"]
+    traffic = measured_traffic()
     line = {
         "metric": "KV tokens attended/s (8B-shape decode @16k) + achieved HBM GB/s; prefill t/s",
-        "value": value,
+        "value": head["kv_tokens_per_s"],
         "unit": "KV tokens/s",
         "n_gpus": 1,
         "steps": steps,
@@ -226,14 +274,15 @@ def main():
         "dtype": "f32",
         "data": "synthetic: seeded N(0,1) K/V/Q, lognormal per-channel K scales, 1% outlier "
                 "channels at 10x",
-        "config": {"workload": f"qwen3-8b-shape single-layer decode, batch 1, context {ctx} "
-                               f"({T} tiles + {n_w} window), Hq 32, Hkv 8, head_dim 128",
-                   "layers_cycled": L},
+        "config": {"workload": f"qwen3-8b-shape single-layer decode, batch 1, context {head['context']} "
+                               f"({head['tiles']} tiles + {head['window']} window), Hq 32, Hkv 8, head_dim 128",
+                   "layers_cycled": head["layers_cycled"]},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "decode_fused_kernel (kvarn_decode_attention, one launch)",
-                     "algorithmic_bytes_per_launch": alg, "launch_us": ms_attn * 1e3},
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "kvarn_decode_attention: decode_split_kernel + decode_combine_kernel",
+                     "algorithmic_bytes_per_launch": alg, "launch_us": ms_step * 1e3},
         "hbm_GBps": achieved,
+        "decode_contexts": [head] + extra,
         "prefill": prefill,
         "compress": compress,
         "cpu_baseline": cpu,
