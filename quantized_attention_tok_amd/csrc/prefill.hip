@@ -9,22 +9,31 @@
 // compressed tiles + FP32 window and a deferred inverse WHT; issue #433 item 1:
 // the Q.K score block of the compressed tiles belongs on the matrix units).
 //
-// Work split: one wave owns 16 query rows (16 consecutive positions of one
-// query head: one MFMA column block) for the whole computation, so the online
-// softmax never leaves the wave; a workgroup is 4 such waves of one KV head
-// sharing the staged tile records (double-buffered in LDS) and raw K/V rows.
-// Per compressed tile and wave:
-//   S^T[t][r] = sum_c zK[t][c] q~[r][c],   q~ = q' kscale      (fp16 MFMA,
-//               code nibbles and hi/lo q~, 8 row blocks of 16 tokens)
-//   O'[r][c] += sum_t w[r][t] zV[t][c],    w = p vscale        (fp16 MFMA,
-//               hi/lo w and 2-bit codes, 4 token steps x 8 channel blocks)
+// Work split: a workgroup owns four groups of 16 query rows of one KV head
+// (each group: 16 consecutive positions of one query head, one MFMA column
+// block) and runs 8 waves, two per row group.  Wave (r, h) takes tokens
+// 64 h .. 64 h + 63 of every compressed tile and the raw 16-token blocks of
+// parity h, with a streaming softmax of its own; the two partial results of a
+// row group are merged at the end.  Two waves per SIMD let the matrix work of
+// one run under the vector work of the other.
+//
+// Per compressed tile the 8 waves first unpack the tile once, together, into
+// LDS operand tiles in the fp16 layout the MFMAs read (one 16-byte read per
+// operand) plus a few per-tile constants, then each wave computes, for its 16
+// rows r and its 64 tokens t,
+//   S^T[t][r] = sum_c zK[t][c] q~[c][r] + b[r]     (fp16 MFMA; q~ = q' kscale
+//               as hi + lo parts, b = sum_c q'_c kmin_c by a small MFMA too)
+//   O^T[c][r] += sum_t zV[t][c] w[r][t]            (fp16 MFMA; w = p vscale
+//               as hi + lo parts)
 // The score layout of the first product (lane (g, r) holds tokens
-// 32 s + 8 g .. + 7 of row r) is exactly the A-operand layout of the second,
-// so the probabilities go from one to the other without data movement.
+// 16 b + 4 g .. + 3 of row r) is the B-operand layout of the second once the
+// V operands list their tokens in that order, and the second leaves row r in
+// lane r again, so the softmax state of a row never moves between lanes.
 // After the last tile each row's O' is rotated back with the WHT butterflies
-// (in-lane and across the 16 lanes of a row), then the raw tokens are added
-// with fp32 MFMAs (v_mfma_f32_16x16x4_f32): scores from the raw query and raw
-// keys, and the aggregate of raw values straight into the same accumulator.
+// (in-lane, and across the four 16-lane rows with the gfx950 permlane swaps),
+// then the raw tokens are added with fp32 MFMAs (v_mfma_f32_16x16x4_f32):
+// scores from the raw query and raw keys, and the aggregate of raw values
+// straight into the same accumulator.
 #include <float.h>
 
 #include "kvarn_launch.h"
@@ -35,36 +44,228 @@ namespace {
 
 using namespace mfma;
 
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef __fp16 fp16x2 __attribute__((ext_vector_type(2)));   // cvt_pkrtz result
+
 constexpr int kRows = 16;                          // query rows per wave
-constexpr int kQRow = D + 4;                       // padded LDS row of q' (floats)
+constexpr int kThreads = 512;                      // 8 waves
 constexpr int kRawTok = 32;                        // raw tokens staged per step
 constexpr int kRawRow = D + 4;                     // padded LDS row of raw K / V (floats)
-constexpr int kLdsRec = 2 * kRecBytes;             // double-buffered records
-constexpr int kLdsQ = 4 * kRows * kQRow * 4;       // q' rows of the 4 waves
-constexpr int kLdsRaw = 2 * kRawTok * kRawRow * 4; // raw K and V rows
-constexpr int kLdsBytes = (kLdsRec + kLdsQ) > kLdsRaw ? (kLdsRec + kLdsQ) : kLdsRaw;
+constexpr int kOpBytes = 32768;                    // one tile's K or V operands (fp16)
+// per-tile constants after the operands: f32 alpha, vsf, vmin, vcu; f16 kh, kl, mh, ml
+constexpr int kCAlpha = 2 * kOpBytes, kCVsf = kCAlpha + 512, kCVmin = kCVsf + 512, kCVcu = kCVmin + 512;
+constexpr int kCKh = kCVcu + 512, kCKl = kCKh + 256, kCMh = kCKl + 256, kCMl = kCMh + 256;
+constexpr int kBufBytes = kCMl + 256;              // one tile: operands + constants
+constexpr int kLdsBytes = 2 * kBufBytes;           // double-buffered tiles
+constexpr int kLdsRaw = 2 * kRawTok * kRawRow * 4; // raw K and V rows (over the tiles)
+constexpr int kMergeO = 4 * 8 * 64 * 16;           // merge: O of the h = 1 waves, then (m, l)
+static_assert(kLdsRaw <= kLdsBytes && kMergeO + 4 * 64 * 8 <= kLdsBytes, "staging fits");
+// Lazy softmax rescaling: a row's running maximum is raised only when a tile's
+// maximum exceeds it by more than kTau (log2 units), so probabilities stay
+// below 2^kTau and the output is rescaled only on those tiles.
+constexpr float kTau = 8.0f;
+
+// floor(log2 x) of a non-negative float, clamped to [lo, hi] (zero -> lo)
+__device__ __forceinline__ int exp_floor(float x, int lo, int hi) {
+  const int e = (int)((__float_as_uint(x) >> 23) & 0xff) - 127;
+  return e < lo ? lo : (e > hi ? hi : e);
+}
+
+// Sums and maxima over the four 16-lane rows of a wave (lanes n, n + 16,
+// n + 32, n + 48); every lane gets the result.  A permlane swap of a value
+// with itself gives each lane its own and its partner's value.
+__device__ __forceinline__ float rows_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+__device__ __forceinline__ float rows_max(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+// WHT butterfly across lanes 16 (M = 16) or 32 (M = 32) apart: the lower lane
+// gets a + b, the upper a - b.
+template <int M>
+__device__ __forceinline__ float bfly_rows(float x, int lane) {
+  const auto r = (M == 32) ? __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false)
+                           : __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float sg = (lane & M) ? -1.0f : 1.0f;
+  return fmaf(sg, __uint_as_float(r[1]), __uint_as_float(r[0]));
+}
+// Maximum of a non-negative value over the wave (bit order = float order).
+__device__ __forceinline__ float wave_max_nn(float v) {
+  int k = __float_as_int(v);
+  k = max(k, __builtin_amdgcn_update_dpp(0, k, 0x128, 0xF, 0xF, false));   // row_ror:8
+  k = max(k, __builtin_amdgcn_update_dpp(0, k, 0x124, 0xF, 0xF, false));   // row_ror:4
+  k = max(k, __builtin_amdgcn_update_dpp(0, k, 0x122, 0xF, 0xF, false));   // row_ror:2
+  k = max(k, __builtin_amdgcn_update_dpp(0, k, 0x121, 0xF, 0xF, false));   // row_ror:1
+  k = max(max(__builtin_amdgcn_readlane(k, 0), __builtin_amdgcn_readlane(k, 16)),
+          max(__builtin_amdgcn_readlane(k, 32), __builtin_amdgcn_readlane(k, 48)));
+  return __int_as_float(k);
+}
+
+// Operand tiles in LDS, 16-byte chunks, one tile (128 tokens x 128 channels)
+// each.  K (A operand of the scores): chunk (k4, b, g, n) holds token
+// 16 b + n, channels 32 k4 + 8 g .. + 7, at 16-byte index
+//   (k4 * 8 + b) * 64 + 16 g + (n ^ swk(b, n)).
+// V (A operand of the aggregate): chunk (s, q, g, n) holds channel
+// 64 (q / 4) + 4 n + q % 4 of tokens 32 s + 16 (j / 4) + 4 g + j % 4 (K slot
+// j = 0..7), at (s * 8 + q) * 64 + 16 g + (n ^ swv(q, n)).  A 4-bit code sits
+// in bits 4-7 of its fp16 half, a 2-bit code in bits 4-5 (crumbs 0, 2 of a
+// byte) or 6-7 (crumbs 1, 3).  The XOR swizzles keep both the cooperative
+// writes and the per-lane MFMA reads free of LDS bank conflicts (each group of
+// 16 lanes touches 16 distinct 16-byte bank groups).
+__device__ __forceinline__ int swk(int b, int n) { return ((b & 3) << 1) | ((n >> 3) & 1) | (((b >> 2) & 1) << 3); }
+__device__ __forceinline__ int swv(int q, int n) { return ((q >> 2) & 1) ^ ((n >> 3) & 1); }
+
+// What one thread loads of a record for the unpack: waves 0-3 one dword of
+// 8 K channel rows, waves 4-7 two bytes of 8 V token rows, every lane two
+// scale pairs for the tile maxima and up to two inputs of the constants.
+struct TileRegs {
+  uint32_t c[8];
+  float2 k2, v2, m2;
+  float c0, c1;
+};
+
+__device__ __forceinline__ void load_tile(const uint8_t* rec, int lane, int wv, TileRegs& r) {
+  const int hi4 = lane >> 4, lo4 = lane & 15;
+  if (wv < 4) {
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(rec + (8 * (4 * wv + hi4)) * 64) + lo4;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r.c[e] = src[16 * e];
+  } else {
+    const uint8_t* vcode = rec + kOffV;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        r.c[4 * h + i] = *reinterpret_cast<const uint16_t*>(vcode + (32 * (wv - 4) + 16 * h + 4 * hi4 + i) * (D / 4) + 2 * lo4);
+  }
+  const float* ks = reinterpret_cast<const float*>(rec + kOffKscale);
+  const float* vs = reinterpret_cast<const float*>(rec + kOffVscale);
+  const float* km = reinterpret_cast<const float*>(rec + kOffKmin);
+  r.k2 = *reinterpret_cast<const float2*>(ks + 2 * lane);
+  r.v2 = *reinterpret_cast<const float2*>(vs + 2 * lane);
+  r.m2 = *reinterpret_cast<const float2*>(km + 2 * lane);
+  const int idx = 16 * wv + lo4;
+  const int arr = hi4;   // 0: ktok, 1: vscale + vmin, 2: kscale + vchan, 3: kmin
+  const float* s0 = reinterpret_cast<const float*>(rec + (arr == 0 ? kOffKtok : arr == 1 ? kOffVscale : arr == 2 ? kOffKscale : kOffKmin));
+  const float* s1 = reinterpret_cast<const float*>(rec + (arr == 1 ? kOffVmin : kOffVchan));
+  r.c0 = s0[idx];
+  r.c1 = s1[idx];
+}
+
+// Unpack one tile (from TileRegs) into an operand buffer and its constants:
+//   alpha[t] = scale log2(e) ktok[t] 2^(7 + ek)        (score factor)
+//   vsf[t]   = vscale[t] 2^(13 - tau - ev)             (w = p vsf < 2^14)
+//   vmin[t]  = vmin[t]
+//   vcu[c]   = vchan[c] 2^(24 - shift(c)) / 2^(13 - tau - ev)
+//   kh + kl  = kscale[c] 2^(13 - ek)                   (fp16 hi, lo)
+//   mh + ml  = kmin[c] 2^(13 - em)                     (fp16 hi, lo)
+// with ek, ev, em the floor(log2) of the tile's largest kscale, vscale, |kmin|,
+// shift 4 for even channels and 6 for odd ones (the crumb's bit position).
+// Waves 0-3 unpack K channel groups 4 w + lane/16, tokens 8 (lane % 16) .. + 7;
+// waves 4-7 V token step w - 4, token group lane/16, channels 8 (lane % 16) .. + 7.
+__device__ __forceinline__ void unpack_tile(const TileRegs& r, uint8_t* buf, int lane, int wv,
+                                            float scale_log2, int& ek, int& ev, int& em) {
+  const int hi4 = lane >> 4, lo4 = lane & 15;
+  if (wv < 4) {
+    const int b0 = lo4 >> 1, n3 = lo4 & 1;   // token 8 lo4 + tt: block lo4 / 2, n = 8 n3 + tt
+    uint4* dst = reinterpret_cast<uint4*>(buf) + (wv * 8 + b0) * 64 + 16 * hi4;
+    const int sw = swk(b0, 8 * n3);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t sel = (uint32_t)j | (0x0Cu << 8) | ((uint32_t)(4 + j) << 16) | (0x0Cu << 24);
+      uint32_t ev4[4], od4[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t x = __builtin_amdgcn_perm(r.c[2 * k + 1], r.c[2 * k], sel);
+        ev4[k] = (x << 4) & 0x00F000F0u;
+        od4[k] = x & 0x00F000F0u;
+      }
+      const int n0 = 8 * n3 + 2 * j;
+      dst[n0 ^ sw] = make_uint4(ev4[0], ev4[1], ev4[2], ev4[3]);
+      dst[(n0 + 1) ^ sw] = make_uint4(od4[0], od4[1], od4[2], od4[3]);
+    }
+  } else {
+    uint4* dst = reinterpret_cast<uint4*>(buf + kOpBytes) + ((wv - 4) * 8) * 64 + 16 * hi4;
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb) {
+      const uint32_t sel = (uint32_t)bb | (0x0Cu << 8) | ((uint32_t)(4 + bb) << 16) | (0x0Cu << 24);
+      uint32_t x[4];   // pair p: tokens of K slots 2p, 2p + 1
+#pragma unroll
+      for (int pq = 0; pq < 4; ++pq) x[pq] = __builtin_amdgcn_perm(r.c[2 * pq + 1], r.c[2 * pq], sel);
+      const int n = (2 * lo4 + bb) & 15;
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) {
+        const uint32_t mask = (kc & 1) ? 0x00C000C0u : 0x00300030u;
+        uint32_t d[4];
+#pragma unroll
+        for (int pq = 0; pq < 4; ++pq) d[pq] = ((kc < 2) ? (x[pq] << 4) : x[pq]) & mask;
+        const int q8 = 4 * (lo4 >> 3) + kc;
+        dst[q8 * 64 + (n ^ swv(q8, n))] = make_uint4(d[0], d[1], d[2], d[3]);
+      }
+    }
+  }
+  // every wave finds the maxima and writes one eighth of the constants
+  ek = exp_floor(wave_max_nn(fmaxf(r.k2.x, r.k2.y)), -114, 120);
+  ev = exp_floor(wave_max_nn(fmaxf(r.v2.x, r.v2.y)), -100, 100);
+  em = exp_floor(wave_max_nn(fmaxf(fabsf(r.m2.x), fabsf(r.m2.y))), -100, 100);
+  const int idx = 16 * wv + lo4;
+  const int fvexp = 13 - (int)kTau - ev;
+  switch (hi4) {
+    case 0:
+      reinterpret_cast<float*>(buf + kCAlpha)[idx] = scale_log2 * r.c0 * pow2i(7 + ek);
+      break;
+    case 1:
+      reinterpret_cast<float*>(buf + kCVsf)[idx] = r.c0 * pow2i(fvexp);
+      reinterpret_cast<float*>(buf + kCVmin)[idx] = r.c1;
+      break;
+    case 2: {
+      const float x = r.c0 * pow2i(13 - ek);
+      const _Float16 h = (_Float16)x;
+      reinterpret_cast<_Float16*>(buf + kCKh)[idx] = h;
+      reinterpret_cast<_Float16*>(buf + kCKl)[idx] = (_Float16)(x - (float)h);
+      reinterpret_cast<float*>(buf + kCVcu)[idx] = r.c1 * pow2i(24 - ((idx & 1) ? 6 : 4) - fvexp);
+      break;
+    }
+    default: {
+      const float x = r.c0 * pow2i(13 - em);
+      const _Float16 h = (_Float16)x;
+      reinterpret_cast<_Float16*>(buf + kCMh)[idx] = h;
+      reinterpret_cast<_Float16*>(buf + kCMl)[idx] = (_Float16)(x - (float)h);
+    }
+  }
+}
 
 __device__ __forceinline__ int tiles_at(int64_t p, int window) {
   const int64_t ahead = p + 1 - window;
   return ahead > 0 ? (int)(ahead / kTile) : 0;
 }
 
-__global__ void __launch_bounds__(256) prefill_mfma_kernel(PrefillParams P) {
+__device__ __forceinline__ half2v as_h2(uint32_t x) { return __builtin_bit_cast(half2v, x); }
+__device__ __forceinline__ uint32_t as_u(half2v x) { return __builtin_bit_cast(uint32_t, x); }
+
+__global__ void __launch_bounds__(kThreads) prefill_mfma_kernel(PrefillParams P) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
+  const int rg = wv & 3, th = wv >> 2;   // row group, token half
   const int n = lane & 15, g = lane >> 4;
   const int kvh = blockIdx.y;
   const int G = P.G;
   const int n_blk = ((P.chunk + kRows - 1) / kRows) * G;   // (position group, head) column blocks
   const int blk_first = blockIdx.x * 4;
   const int blk_last = min(blk_first + 3, n_blk - 1);
-  const int blk = blk_first + wv;
+  const int blk = blk_first + rg;
   const bool active = blk < n_blk;
   const int pg = (active ? blk : blk_last) / G;
   const int hq = kvh * G + (active ? blk : blk_last) % G;
   const int r0 = kRows * pg;                                // chunk row of column 0
-  const int64_t prow = P.pos0 + r0 + n;                     // position of this lane's column
+  const int64_t prow = P.pos0 + r0 + n;                     // position of this lane's row
   const bool row_ok = active && (r0 + n < P.chunk);
   const int T_row = row_ok ? tiles_at(prow, P.window) : 0;
   const int64_t p_wlast = P.pos0 + min(r0 + kRows - 1, P.chunk - 1);
@@ -75,242 +276,243 @@ __global__ void __launch_bounds__(256) prefill_mfma_kernel(PrefillParams P) {
   const int T_wg = tiles_at(p_last, P.window);
 
   __shared__ __attribute__((aligned(16))) uint8_t s_lds[kLdsBytes];
-  float* s_q = reinterpret_cast<float*>(s_lds + kLdsRec) + wv * kRows * kQRow;
   const float scale_log2 = P.scale * kLog2e;
-
-  // ---- stage the first record and this wave's rotated query rows ----
   const uint8_t* recs = P.records + (int64_t)kvh * kRecBytes;
   const int64_t rstride = (int64_t)P.n_kv * kRecBytes;
-  constexpr int kU4 = kRecBytes / 16;
-  uint4 t0v, t1v, t2v, t3v;
-#define KVARN_LOAD_REC(tile_)                                                              \
-  do {                                                                                     \
-    const uint4* src_ = reinterpret_cast<const uint4*>(recs + (int64_t)(tile_) * rstride); \
-    t0v = src_[tid];                                                                       \
-    t1v = src_[tid + 256];                                                                 \
-    t2v = src_[tid + 512];                                                                 \
-    if (tid + 768 < kU4) t3v = src_[tid + 768];                                            \
-  } while (0)
-#define KVARN_STORE_REC(buf_)                                                              \
-  do {                                                                                     \
-    uint4* dst_ = reinterpret_cast<uint4*>(s_lds + (buf_) * kRecBytes);                    \
-    dst_[tid] = t0v;                                                                       \
-    dst_[tid + 256] = t1v;                                                                 \
-    dst_[tid + 512] = t2v;                                                                 \
-    if (tid + 768 < kU4) dst_[tid + 768] = t3v;                                            \
-  } while (0)
-  if (T_wg > 0) KVARN_LOAD_REC(0);
-  for (int i = lane; i < kRows * (D / 4); i += 64) {
-    const int r = i >> 5, c4 = i & 31;
-    float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (active && r0 + r < P.chunk)
-      x = *reinterpret_cast<const float4*>(P.q_rot + ((int64_t)(r0 + r) * P.n_q + hq) * D + 4 * c4);
-    *reinterpret_cast<float4*>(s_q + r * kQRow + 4 * c4) = x;
+
+  // ---- tile 0 unpacked, tile 1 in registers; this lane's rotated query:
+  // row n, channels 32 k4 + 8 g .. + 7 ----
+  TileRegs tr;
+  int ek = 0, ev = 0, em = 0;   // exponents of the tile being computed
+  if (T_wg > 0) load_tile(recs, lane, wv, tr);
+  float qv[4][8];
+  {
+    const float* qp = P.q_rot + ((int64_t)(row_ok ? r0 + n : 0) * P.n_q + hq) * D + 8 * g;
+#pragma unroll
+    for (int k4 = 0; k4 < 4; ++k4) {
+      float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
+      if (row_ok) {
+        a = *reinterpret_cast<const float4*>(qp + 32 * k4);
+        b = *reinterpret_cast<const float4*>(qp + 32 * k4 + 4);
+      }
+      qv[k4][0] = a.x; qv[k4][1] = a.y; qv[k4][2] = a.z; qv[k4][3] = a.w;
+      qv[k4][4] = b.x; qv[k4][5] = b.y; qv[k4][6] = b.z; qv[k4][7] = b.w;
+    }
   }
-  if (T_wg > 0) KVARN_STORE_REC(0);
+  if (T_wg > 0) {
+    unpack_tile(tr, s_lds, lane, wv, scale_log2, ek, ev, em);
+    if (T_wg > 1) load_tile(recs + rstride, lane, wv, tr);
+  }
   __syncthreads();
-  // max |q'| of row n (bound for the fp16 scale of q~)
+  // q' of row n scaled into (-1, 1) by 2^-eq, as fp16 hi + lo pairs
   float qmax = 0.0f;
 #pragma unroll
   for (int k4 = 0; k4 < 4; ++k4)
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-      const float4 x = *reinterpret_cast<const float4*>(s_q + n * kQRow + 32 * k4 + 8 * g + 4 * h2);
-      qmax = fmaxf(qmax, fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w))));
-    }
-  qmax = wave_max16(qmax);
+    for (int j = 0; j < 8; ++j) qmax = fmaxf(qmax, fabsf(qv[k4][j]));
+  const int eq = exp_floor(rows_max(qmax), -100, 99) + 1;
+  const float beta = pow2i(eq);
+  uint32_t qh[4][4], ql[4][4];   // [k4][pair]: channels 32 k4 + 8 g + 2 i, + 1
+  {
+    const float inv = pow2i(-eq);
+#pragma unroll
+    for (int k4 = 0; k4 < 4; ++k4)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float a = qv[k4][2 * i] * inv, b = qv[k4][2 * i + 1] * inv;
+        const _Float16 ha = (_Float16)a, hb = (_Float16)b;
+        qh[k4][i] = pack_h2(ha, hb);
+        ql[k4][i] = pack_h2((_Float16)(a - (float)ha), (_Float16)(b - (float)hb));
+      }
+  }
+  // operand read offsets (16-byte units) of lane (g, n): K blocks 4 th + bb, V channel halves
+  int offk[4], offv[2];
+#pragma unroll
+  for (int bb = 0; bb < 4; ++bb) offk[bb] = 16 * g + (n ^ swk(4 * th + bb, n));
+#pragma unroll
+  for (int h = 0; h < 2; ++h) offv[h] = 16 * g + (n ^ swv(4 * h, n));
 
-  float m_run = -INFINITY, l_run = 0.0f;       // softmax state of row n (log2 domain)
-  floatx4 O[2][4];                              // rows 4g + i, channel 64 qb + 4 n + kk
+  float m_run = -INFINITY, l_run = 0.0f;   // softmax state of row n (log2 domain)
+  floatx4 O[2][4];                          // row n; channel 64 qb + 16 g + 4 i + kk in O[qb][kk][i]
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) O[qb][kk] = (floatx4){0.f, 0.f, 0.f, 0.f};
 
-  // byte (n & 3) of two code dwords into the low bytes of two halves
-  const uint32_t nb = (uint32_t)(n & 3);
-  const uint32_t sel = nb | (12u << 8) | ((4u + nb) << 16) | (12u << 24);
-
-  // ---- compressed tiles ----
-  int cur = 0;
+  // ---- compressed tiles: compute tile j while unpacking tile j + 1 into the
+  // other buffer and loading tile j + 2 ----
   for (int j = 0; j < T_wg; ++j) {
-    const bool more = j + 1 < T_wg;
-    if (more) KVARN_LOAD_REC(j + 1);   // in flight during the compute
+    const uint8_t* cst = s_lds + (j & 1) * kBufBytes;
+    const uint4* kop = reinterpret_cast<const uint4*>(cst);
+    const uint4* vop = reinterpret_cast<const uint4*>(cst + kOpBytes);
+    int ekn = 0, evn = 0, emn = 0;
+    if (j + 1 < T_wg) {
+      unpack_tile(tr, s_lds + ((j + 1) & 1) * kBufBytes, lane, wv, scale_log2, ekn, evn, emn);
+      if (j + 2 < T_wg) load_tile(recs + (int64_t)(j + 2) * rstride, lane, wv, tr);
+    }
     if (j < T_wave) {
-      const uint8_t* rec = s_lds + cur * kRecBytes;
-      const float* ks = reinterpret_cast<const float*>(rec + kOffKscale);
-      const float* km = reinterpret_cast<const float*>(rec + kOffKmin);
-      const float2 kk2 = *reinterpret_cast<const float2*>(ks + 2 * lane);
-      const float kmx = wave_max(fmaxf(kk2.x, kk2.y));   // tile max kscale (>= 0)
-      const int fexp = fp16_scale_exp(kmx * qmax);
-      const float f16inv = pow2i(fexp - 4);
-      const float unscale = pow2i(24 - fexp);
-      floatx4 acc[4][2];
-#pragma unroll
-      for (int bg = 0; bg < 4; ++bg) acc[bg][0] = acc[bg][1] = (floatx4){0.f, 0.f, 0.f, 0.f};
-      float bias_part = 0.0f;
+      // B operands: q~ = q' kscale 2^(13 - ek - eq) = (qh + ql)(kh + kl) as hi + lo,
+      // by packed fp16 arithmetic (hi rounded, lo = exact product rest + cross terms)
+      half8 Bh[4], Bl[4];
 #pragma unroll
       for (int k4 = 0; k4 < 4; ++k4) {
-        // B: q~ of row n, channels 32 k4 + 8 g .. + 7, hi and lo
+        const uint4 kh4 = *reinterpret_cast<const uint4*>(cst + kCKh + 2 * (32 * k4 + 8 * g));
+        const uint4 kl4 = *reinterpret_cast<const uint4*>(cst + kCKl + 2 * (32 * k4 + 8 * g));
+        const uint32_t khv[4] = {kh4.x, kh4.y, kh4.z, kh4.w};
+        const uint32_t klv[4] = {kl4.x, kl4.y, kl4.z, kl4.w};
         uint32_t bh[4], bl[4];
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          const int c0 = 32 * k4 + 8 * g + 4 * h2;
-          const float4 q = *reinterpret_cast<const float4*>(s_q + n * kQRow + c0);
-          const float4 sc = *reinterpret_cast<const float4*>(ks + c0);
-          const float4 mn = *reinterpret_cast<const float4*>(km + c0);
-          bias_part += q.x * mn.x + q.y * mn.y + q.z * mn.z + q.w * mn.w;
-          _Float16 h0, h1, h2_, h3, l0, l1, l2, l3;
-          split_h(q.x * sc.x * f16inv, h0, l0);
-          split_h(q.y * sc.y * f16inv, h1, l1);
-          split_h(q.z * sc.z * f16inv, h2_, l2);
-          split_h(q.w * sc.w * f16inv, h3, l3);
-          bh[2 * h2] = pack_h2(h0, h1);
-          bh[2 * h2 + 1] = pack_h2(h2_, h3);
-          bl[2 * h2] = pack_h2(l0, l1);
-          bl[2 * h2 + 1] = pack_h2(l2, l3);
+        for (int i = 0; i < 4; ++i) {
+          const half2v a = as_h2(qh[k4][i]), a2 = as_h2(ql[k4][i]), k = as_h2(khv[i]), k2 = as_h2(klv[i]);
+          const half2v hi = a * k;
+          half2v lo = __builtin_elementwise_fma(a, k, -hi);
+          lo = __builtin_elementwise_fma(a, k2, lo);
+          lo = __builtin_elementwise_fma(a2, k, lo);
+          bh[i] = as_u(hi);
+          bl[i] = as_u(lo);
         }
-        const half8 Bh = as_half8(bh[0], bh[1], bh[2], bh[3]);
-        const half8 Bl = as_half8(bl[0], bl[1], bl[2], bl[3]);
-#pragma unroll
-        for (int bg = 0; bg < 4; ++bg) {
-          // A: code byte 16 bg + n (tokens 32 bg + 2n, + 1) of channels 32 k4 + 8 g .. + 7
-          uint32_t ae[4], ao[4];
-#pragma unroll
-          for (int p = 0; p < 4; ++p) {
-            const int c = 32 * k4 + 8 * g + 2 * p;
-            const uint32_t d0 = *reinterpret_cast<const uint32_t*>(rec + c * 64 + 16 * bg + 4 * (n >> 2));
-            const uint32_t d1 = *reinterpret_cast<const uint32_t*>(rec + (c + 1) * 64 + 16 * bg + 4 * (n >> 2));
-            const uint32_t x = __builtin_amdgcn_perm(d1, d0, sel);
-            ae[p] = nib_lo(x);
-            ao[p] = nib_hi(x);
-          }
-          const half8 Ae = as_half8(ae[0], ae[1], ae[2], ae[3]);
-          const half8 Ao = as_half8(ao[0], ao[1], ao[2], ao[3]);
-          acc[bg][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ae, Bh, acc[bg][0], 0, 0, 0);
-          acc[bg][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ae, Bl, acc[bg][0], 0, 0, 0);
-          acc[bg][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ao, Bh, acc[bg][1], 0, 0, 0);
-          acc[bg][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ao, Bl, acc[bg][1], 0, 0, 0);
-        }
+        Bh[k4] = as_half8(bh[0], bh[1], bh[2], bh[3]);
+        Bl[k4] = as_half8(bl[0], bl[1], bl[2], bl[3]);
       }
-      const float bias = wave_sum16(bias_part);
-      // scores (log2 domain): token 32 bg + 8 g + 2 i + nib of row n
+      // bias b = sum_c q'_c kmin_c: every row of A is kmin 2^(13 - em) (hi, lo),
+      // B is q' 2^-eq (hi, lo); rescaled to the score accumulator's 2^(-7 - ek - eq)
+      floatx4 bacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k4 = 0; k4 < 4; ++k4) {
+        const uint4 mh4 = *reinterpret_cast<const uint4*>(cst + kCMh + 2 * (32 * k4 + 8 * g));
+        const uint4 ml4 = *reinterpret_cast<const uint4*>(cst + kCMl + 2 * (32 * k4 + 8 * g));
+        const half8 Amh = as_half8(mh4.x, mh4.y, mh4.z, mh4.w);
+        const half8 Aml = as_half8(ml4.x, ml4.y, ml4.z, ml4.w);
+        const half8 Qh = as_half8(qh[k4][0], qh[k4][1], qh[k4][2], qh[k4][3]);
+        const half8 Ql = as_half8(ql[k4][0], ql[k4][1], ql[k4][2], ql[k4][3]);
+        bacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(Amh, Qh, bacc, 0, 0, 0);
+        bacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(Amh, Ql, bacc, 0, 0, 0);
+        bacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(Aml, Qh, bacc, 0, 0, 0);
+      }
+      const int bexp = em - 20 - ek;
+      const float bsc = pow2i(bexp < -126 ? -126 : (bexp > 127 ? 127 : bexp));
+      const floatx4 acc0 = {bacc[0] * bsc, bacc[1] * bsc, bacc[2] * bsc, bacc[3] * bsc};
+      // scores / beta (log2 domain): y = alpha_t acc, token 16 b + 4 g + i of row n
+      const float* alp = reinterpret_cast<const float*>(cst + kCAlpha);
+      float y[4][4];
+      float ymax = -INFINITY;
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) {
+        const int b = 4 * th + bb;
+        floatx4 acc = acc0;
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4) {
+          const uint4 a = kop[(k4 * 8 + b) * 64 + offk[bb]];
+          const half8 A = as_half8(a.x, a.y, a.z, a.w);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bh[k4], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bl[k4], acc, 0, 0, 0);
+        }
+        const float4 al = *reinterpret_cast<const float4*>(alp + 16 * b + 4 * g);
+        y[bb][0] = acc[0] * al.x;
+        y[bb][1] = acc[1] * al.y;
+        y[bb][2] = acc[2] * al.z;
+        y[bb][3] = acc[3] * al.w;
+        ymax = fmaxf(fmaxf(ymax, y[bb][0]), y[bb][1]);
+        ymax = fmaxf(fmaxf(ymax, y[bb][2]), y[bb][3]);
+      }
+      // lazy running maximum: raised only when the tile exceeds it by > tau
       const bool vis = j < T_row;
-      const float* ktok = reinterpret_cast<const float*>(rec + kOffKtok);
-      float tmax = -INFINITY;
+      const float tmax = rows_max(ymax) * beta;
+      const bool raise = vis && !(tmax <= m_run + kTau);
+      const float m_new = raise ? tmax : m_run;
+      const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;   // 0 from -inf
+      m_run = m_new;
+      const float negm = vis ? -m_run : -INFINITY;
+      l_run *= alpha;
+      if (__builtin_amdgcn_ballot_w64(raise) != 0) {
 #pragma unroll
-      for (int bg = 0; bg < 4; ++bg) {
-        const float4 ka = *reinterpret_cast<const float4*>(ktok + 32 * bg + 8 * g);
-        const float4 kb = *reinterpret_cast<const float4*>(ktok + 32 * bg + 8 * g + 4);
-        const float kt[8] = {ka.x, ka.y, ka.z, ka.w, kb.x, kb.y, kb.z, kb.w};
+        for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+          for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-          for (int nib = 0; nib < 2; ++nib) {
-            const float sv = vis ? scale_log2 * kt[2 * i + nib] * (acc[bg][nib][i] * unscale + bias) : -INFINITY;
-            acc[bg][nib][i] = sv;
-            tmax = fmaxf(tmax, sv);
-          }
+            for (int i = 0; i < 4; ++i) O[qb][kk][i] *= alpha;
       }
-      tmax = wave_max16(tmax);
-      const float m_new = fmaxf(m_run, tmax);
-      const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);   // 0 while nothing was seen
-      const float* vsc = reinterpret_cast<const float*>(rec + kOffVscale);
-      const float* vmn = reinterpret_cast<const float*>(rec + kOffVmin);
-      const float2 vv = *reinterpret_cast<const float2*>(vsc + 2 * lane);
-      const int vexp = fp16_scale_exp(wave_max(fmaxf(vv.x, vv.y)));   // p <= 1, w <= max vscale
-      const float fv = pow2i(vexp);
-      // PV: token step bg uses the probabilities this lane already holds
+      // probabilities p (<= 2^tau), their sums, and w = p vsf as hi / lo B operands
+      const float* vsf = reinterpret_cast<const float*>(cst + kCVsf);
+      const float* vmn = reinterpret_cast<const float*>(cst + kCVmin);
       float psum = 0.0f, upart = 0.0f;
-      floatx4 z[2][4];
+      uint32_t wh[4][2], wl[4][2];
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) z[qb][kk] = (floatx4){0.f, 0.f, 0.f, 0.f};
-      const uint8_t* vcode = rec + kOffV;
-#pragma unroll
-      for (int bg = 0; bg < 4; ++bg) {
-        const float4 va = *reinterpret_cast<const float4*>(vsc + 32 * bg + 8 * g);
-        const float4 vb = *reinterpret_cast<const float4*>(vsc + 32 * bg + 8 * g + 4);
-        const float4 ma = *reinterpret_cast<const float4*>(vmn + 32 * bg + 8 * g);
-        const float4 mb = *reinterpret_cast<const float4*>(vmn + 32 * bg + 8 * g + 4);
-        const float vs8[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
-        const float vm8[8] = {ma.x, ma.y, ma.z, ma.w, mb.x, mb.y, mb.z, mb.w};
-        uint32_t wh[4], wl[4];
+      for (int bb = 0; bb < 4; ++bb) {
+        const int b = 4 * th + bb;
+        const float4 va = *reinterpret_cast<const float4*>(vsf + 16 * b + 4 * g);
+        const float4 ma = *reinterpret_cast<const float4*>(vmn + 16 * b + 4 * g);
+        const float vs4[4] = {va.x, va.y, va.z, va.w};
+        const float vm4[4] = {ma.x, ma.y, ma.z, ma.w};
+        float w4[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          _Float16 hh[2], ll[2];
-#pragma unroll
-          for (int nib = 0; nib < 2; ++nib) {
-            const float pj = __builtin_amdgcn_exp2f(acc[bg][nib][i] - m_use);
-            psum += pj;
-            upart += pj * vm8[2 * i + nib];
-            split_h(pj * vs8[2 * i + nib] * fv, hh[nib], ll[nib]);
-          }
-          wh[i] = pack_h2(hh[0], hh[1]);
-          wl[i] = pack_h2(ll[0], ll[1]);
+          const float pj = __builtin_amdgcn_exp2f(fmaf(beta, y[bb][i], negm));
+          psum += pj;
+          upart = fmaf(pj, vm4[i], upart);
+          w4[i] = pj * vs4[i];
         }
-        const half8 Wh = as_half8(wh[0], wh[1], wh[2], wh[3]);
-        const half8 Wl = as_half8(wl[0], wl[1], wl[2], wl[3]);
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          // B: byte 16 qb + n of tokens 32 bg + 8 g .. + 7; crumb kk is channel 64 qb + 4 n + kk
-          uint32_t pr[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int t = 32 * bg + 8 * g + 2 * q;
-            const uint32_t da = *reinterpret_cast<const uint32_t*>(vcode + t * (D / 4) + 16 * qb + 4 * (n >> 2));
-            const uint32_t db = *reinterpret_cast<const uint32_t*>(vcode + (t + 1) * (D / 4) + 16 * qb + 4 * (n >> 2));
-            pr[q] = __builtin_amdgcn_perm(db, da, sel);
-          }
-#pragma unroll
-          for (int kk = 0; kk < 4; ++kk) {
-            const uint32_t mask = (kk & 1) ? 0x00C000C0u : 0x00300030u;
-            const int sh = (kk < 2) ? 4 : 0;   // crumbs 0, 1 move up into bits 4-7
-            const half8 Bv = as_half8((pr[0] << sh) & mask, (pr[1] << sh) & mask, (pr[2] << sh) & mask,
-                                      (pr[3] << sh) & mask);
-            z[qb][kk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Wh, Bv, z[qb][kk], 0, 0, 0);
-            z[qb][kk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Wl, Bv, z[qb][kk], 0, 0, 0);
-          }
+        for (int pr = 0; pr < 2; ++pr) {
+          const fp16x2 h = __builtin_amdgcn_cvt_pkrtz(w4[2 * pr], w4[2 * pr + 1]);
+          const fp16x2 l = __builtin_amdgcn_cvt_pkrtz(w4[2 * pr] - (float)h.x, w4[2 * pr + 1] - (float)h.y);
+          wh[bb][pr] = __builtin_bit_cast(uint32_t, h);
+          wl[bb][pr] = __builtin_bit_cast(uint32_t, l);
         }
       }
-      l_run = l_run * alpha + wave_sum16(psum);
-      const float u = wave_sum16(upart);
-      m_run = m_new;
-      // o' = o' alpha_r + vchan_c (Z 2^24 / (fv 2^shift) + u_r)
-      const float* vch = reinterpret_cast<const float*>(rec + kOffVchan);
-      float ar[4], ur[4];
+      l_run += rows_sum(psum);
+      const float u = rows_sum(upart);
+      // O'^T[c][n] += vcu_c z_c, z_c starting at u fv 2^-(24 - shift(c)) so that
+      // vcu_c z_c = vchan_c (sum_t p_t vscale_t zV_tc + sum_t p_t vmin_t)
+      const float ufv = u * pow2i(13 - (int)kTau - ev);
+      const float zi0 = ufv * pow2i(-20), zi1 = ufv * pow2i(-18);
+      half8 Wh[2], Wl[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        ar[i] = __shfl(alpha, 4 * g + i, 64);
-        ur[i] = __shfl(u, 4 * g + i, 64);
+      for (int tt = 0; tt < 2; ++tt) {
+        Wh[tt] = as_half8(wh[2 * tt][0], wh[2 * tt][1], wh[2 * tt + 1][0], wh[2 * tt + 1][1]);
+        Wl[tt] = as_half8(wl[2 * tt][0], wl[2 * tt][1], wl[2 * tt + 1][0], wl[2 * tt + 1][1]);
       }
+      const float* vcu = reinterpret_cast<const float*>(cst + kCVcu);
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        const float4 vc = *reinterpret_cast<const float4*>(vch + 64 * qb + 4 * n);
-        const float vcv[4] = {vc.x, vc.y, vc.z, vc.w};
+        float4 vc[4];   // channels 64 qb + 16 g + 4 i .. + 3
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vc[i] = *reinterpret_cast<const float4*>(vcu + 64 * qb + 16 * g + 4 * i);
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-          const float un = pow2i(24 - vexp - ((kk & 1) ? 6 : 4));
+          const int q8 = 4 * qb + kk;
+          const float zi = (kk & 1) ? zi1 : zi0;
+          floatx4 z = {zi, zi, zi, zi};
 #pragma unroll
-          for (int i = 0; i < 4; ++i) O[qb][kk][i] = O[qb][kk][i] * ar[i] + vcv[kk] * (z[qb][kk][i] * un + ur[i]);
+          for (int tt = 0; tt < 2; ++tt) {
+            const uint4 av = vop[((2 * th + tt) * 8 + q8) * 64 + offv[qb]];
+            const half8 Av = as_half8(av.x, av.y, av.z, av.w);
+            z = __builtin_amdgcn_mfma_f32_16x16x32_f16(Av, Wh[tt], z, 0, 0, 0);
+            z = __builtin_amdgcn_mfma_f32_16x16x32_f16(Av, Wl[tt], z, 0, 0, 0);
+          }
+          const float vk[4] = {kk == 0 ? vc[0].x : kk == 1 ? vc[0].y : kk == 2 ? vc[0].z : vc[0].w,
+                               kk == 0 ? vc[1].x : kk == 1 ? vc[1].y : kk == 2 ? vc[1].z : vc[1].w,
+                               kk == 0 ? vc[2].x : kk == 1 ? vc[2].y : kk == 2 ? vc[2].z : vc[2].w,
+                               kk == 0 ? vc[3].x : kk == 1 ? vc[3].y : kk == 2 ? vc[3].z : vc[3].w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) O[qb][kk][i] = fmaf(vk[i], z[i], O[qb][kk][i]);
         }
       }
     }
-    if (more) KVARN_STORE_REC(cur ^ 1);
+    // tile j + 1 is in place and every wave is done with tile j's buffer
     __syncthreads();
-    cur ^= 1;
+    ek = ekn;
+    ev = evn;
+    em = emn;
   }
-#undef KVARN_LOAD_REC
-#undef KVARN_STORE_REC
 
-  // ---- inverse WHT of the tile part: channel 64 qb + 4 n + kk of row 4 g + i ----
+  // ---- inverse rotation of the tile part: channel bits kk (0, 1), i (2, 3),
+  // g (4, 5: across 16-lane rows), qb (6) ----
   if (T_wave > 0) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {   // channel bits 0, 1 (kk)
+      for (int i = 0; i < 4; ++i) {
         const float a0 = O[qb][0][i], a1 = O[qb][1][i], a2 = O[qb][2][i], a3 = O[qb][3][i];
         const float b0 = a0 + a1, b1 = a0 - a1, b2 = a2 + a3, b3 = a2 - a3;
         O[qb][0][i] = b0 + b2;
@@ -319,36 +521,36 @@ __global__ void __launch_bounds__(256) prefill_mfma_kernel(PrefillParams P) {
         O[qb][3][i] = b1 - b3;
       }
 #pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const float a0 = O[qb][kk][0], a1 = O[qb][kk][1], a2 = O[qb][kk][2], a3 = O[qb][kk][3];
+        const float b0 = a0 + a1, b1 = a0 - a1, b2 = a2 + a3, b3 = a2 - a3;
+        O[qb][kk][0] = b0 + b2;
+        O[qb][kk][1] = b1 + b3;
+        O[qb][kk][2] = b0 - b2;
+        O[qb][kk][3] = b1 - b3;
+      }
+#pragma unroll
     for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {   // channel bit 6 (qb)
+      for (int i = 0; i < 4; ++i) {
         const float a = O[0][kk][i], b = O[1][kk][i];
         O[0][kk][i] = a + b;
         O[1][kk][i] = a - b;
       }
 #pragma unroll
-    for (int m = 1; m < 16; m <<= 1) {   // channel bits 2-5 (lane n)
-      const bool up = (n & m) != 0;
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float x = O[qb][kk][i];
-            const float y = __shfl_xor(x, m, 64);
-            O[qb][kk][i] = up ? (y - x) : (x + y);
-          }
-    }
-#pragma unroll
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) O[qb][kk][i] *= wht_scale<D>();
+        for (int i = 0; i < 4; ++i) {
+          const float x = bfly_rows<16>(O[qb][kk][i], lane);
+          O[qb][kk][i] = bfly_rows<32>(x, lane) * wht_scale<D>();
+        }
   }
 
-  // ---- raw tokens [128 T(p), p] on fp32 MFMA ----
+  // ---- raw tokens [128 T(p), p] on fp32 MFMA, 16-token blocks of parity th ----
   float4 qr[8];   // raw query of row n, channels 16 jj + 4 g .. + 3
 #pragma unroll
   for (int jj = 0; jj < 8; ++jj) {
@@ -356,7 +558,7 @@ __global__ void __launch_bounds__(256) prefill_mfma_kernel(PrefillParams P) {
     if (row_ok)
       qr[jj] = *reinterpret_cast<const float4*>(P.q + ((int64_t)(r0 + n) * P.n_q + hq) * D + 16 * jj + 4 * g);
   }
-  float* s_k = reinterpret_cast<float*>(s_lds);
+  float* s_k = reinterpret_cast<float*>(s_lds);   // over the tile buffers
   float* s_v = s_k + kRawTok * kRawRow;
   const int64_t raw_lo = (int64_t)kTile * tiles_at(p_first, P.window);
   const int64_t wave_lo = (int64_t)kTile * tiles_at(P.pos0 + r0, P.window);
@@ -366,105 +568,123 @@ __global__ void __launch_bounds__(256) prefill_mfma_kernel(PrefillParams P) {
   for (int64_t t0 = raw_lo; t0 <= p_last; t0 += kRawTok) {
     __syncthreads();   // previous readers of the staging rows are done
     {
-      const int r = tid >> 3, c4 = tid & 7;
+      const int r = tid >> 4, c4 = tid & 15;
       const int64_t t = t0 + r;
-      float4 kx[4], vx[4];
+      float4 kx[2], vx[2];
       if (t <= p_last) {
         const float4* rk = reinterpret_cast<const float4*>(kbase + (t - P.raw_base) * P.tok_stride);
         const float4* rv = reinterpret_cast<const float4*>(vbase + (t - P.raw_base) * P.tok_stride);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          kx[e] = rk[c4 + 8 * e];
-          vx[e] = rv[c4 + 8 * e];
+        for (int e = 0; e < 2; ++e) {
+          kx[e] = rk[c4 + 16 * e];
+          vx[e] = rv[c4 + 16 * e];
         }
       } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
+        for (int e = 0; e < 2; ++e) {
           kx[e] = make_float4(0.f, 0.f, 0.f, 0.f);
           vx[e] = kx[e];
         }
       }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        *reinterpret_cast<float4*>(s_k + r * kRawRow + 4 * (c4 + 8 * e)) = kx[e];
-        *reinterpret_cast<float4*>(s_v + r * kRawRow + 4 * (c4 + 8 * e)) = vx[e];
+      for (int e = 0; e < 2; ++e) {
+        *reinterpret_cast<float4*>(s_k + r * kRawRow + 4 * (c4 + 16 * e)) = kx[e];
+        *reinterpret_cast<float4*>(s_v + r * kRawRow + 4 * (c4 + 16 * e)) = vx[e];
       }
     }
     __syncthreads();
-#pragma unroll 1
-    for (int sb = 0; sb < kRawTok / 16; ++sb) {
-      const int64_t tb = t0 + 16 * sb;
-      if (!active || tb > p_wlast || tb + 15 < wave_lo) continue;   // wave-uniform
-      // S^T[t][r]: A = raw keys (row n = token tb + n), B = raw query of row n;
-      // MFMA (jj, e) contracts channels 16 jj + 4 g' + e over K slots g'
-      floatx4 sacc = {0.f, 0.f, 0.f, 0.f};
+    const int sb = th;
+    const int64_t tb = t0 + 16 * sb;
+    if (!active || tb > p_wlast || tb + 15 < wave_lo) continue;   // wave-uniform
+    // S^T[t][r]: A = raw keys (row n = token tb + n), B = raw query of row n;
+    // MFMA (jj, e) contracts channels 16 jj + 4 g' + e over K slots g'
+    floatx4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        const float4 ka = *reinterpret_cast<const float4*>(s_k + (16 * sb + n) * kRawRow + 16 * jj + 4 * g);
-        sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(ka.x, qr[jj].x, sacc, 0, 0, 0);
-        sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(ka.y, qr[jj].y, sacc, 0, 0, 0);
-        sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(ka.z, qr[jj].z, sacc, 0, 0, 0);
-        sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(ka.w, qr[jj].w, sacc, 0, 0, 0);
-      }
-      // lane (g, n): tokens tb + 4 g + i of row n
-      float sv[4];
-      float tmax = -INFINITY;
+    for (int jj = 0; jj < 8; ++jj) {
+      const float4 ka = *reinterpret_cast<const float4*>(s_k + (16 * sb + n) * kRawRow + 16 * jj + 4 * g);
+      sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(ka.x, qr[jj].x, sacc, 0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(ka.y, qr[jj].y, sacc, 0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(ka.z, qr[jj].z, sacc, 0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(ka.w, qr[jj].w, sacc, 0, 0, 0);
+    }
+    // lane (g, n): tokens tb + 4 g + i of row n
+    float sv[4];
+    float tmax = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t t = tb + 4 * g + i;
-        const bool vis = row_ok && t >= row_lo && t <= prow;
-        sv[i] = vis ? sacc[i] * scale_log2 : -INFINITY;
-        tmax = fmaxf(tmax, sv[i]);
-      }
-      tmax = wave_max16(tmax);
-      const float m_new = fmaxf(m_run, tmax);
-      const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-      float pv[4], psum = 0.0f;
+    for (int i = 0; i < 4; ++i) {
+      const int64_t t = tb + 4 * g + i;
+      const bool vis = row_ok && t >= row_lo && t <= prow;
+      sv[i] = vis ? sacc[i] * scale_log2 : -INFINITY;
+      tmax = fmaxf(tmax, sv[i]);
+    }
+    tmax = rows_max(tmax);
+    const float m_new = fmaxf(m_run, tmax);
+    const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    float pv[4], psum = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pv[i] = __builtin_amdgcn_exp2f(sv[i] - m_use);
-        psum += pv[i];
-      }
-      l_run = l_run * alpha + wave_sum16(psum);
-      m_run = m_new;
-      float ar[4];
+    for (int i = 0; i < 4; ++i) {
+      pv[i] = __builtin_amdgcn_exp2f(sv[i] - m_use);
+      psum += pv[i];
+    }
+    l_run = l_run * alpha + rows_sum(psum);
+    m_run = m_new;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ar[i] = __shfl(alpha, 4 * g + i, 64);
+    for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
+      for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
+        for (int i = 0; i < 4; ++i) O[qb][kk][i] *= alpha;
+    // O^T[c][n] += sum_t v[t][c] p[n][t]; step i: K slot g is token tb + 4 g + i,
+    // A row n' is channel 64 qb + 4 n' + kk
 #pragma unroll
-          for (int i = 0; i < 4; ++i) O[qb][kk][i] *= ar[i];
-      // O[r][c] += sum_t p[r][t] v[t][c]; step i: K slot g is token tb + 4 g + i
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          const float4 vv = *reinterpret_cast<const float4*>(s_v + (16 * sb + 4 * g + i) * kRawRow + 64 * qb + 4 * n);
-          O[qb][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(pv[i], vv.x, O[qb][0], 0, 0, 0);
-          O[qb][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(pv[i], vv.y, O[qb][1], 0, 0, 0);
-          O[qb][2] = __builtin_amdgcn_mfma_f32_16x16x4f32(pv[i], vv.z, O[qb][2], 0, 0, 0);
-          O[qb][3] = __builtin_amdgcn_mfma_f32_16x16x4f32(pv[i], vv.w, O[qb][3], 0, 0, 0);
-        }
+      for (int qb = 0; qb < 2; ++qb) {
+        const float4 vv = *reinterpret_cast<const float4*>(s_v + (16 * sb + 4 * g + i) * kRawRow + 64 * qb + 4 * n);
+        O[qb][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(vv.x, pv[i], O[qb][0], 0, 0, 0);
+        O[qb][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(vv.y, pv[i], O[qb][1], 0, 0, 0);
+        O[qb][2] = __builtin_amdgcn_mfma_f32_16x16x4f32(vv.z, pv[i], O[qb][2], 0, 0, 0);
+        O[qb][3] = __builtin_amdgcn_mfma_f32_16x16x4f32(vv.w, pv[i], O[qb][3], 0, 0, 0);
       }
     }
   }
 
-  // ---- normalise and store rows 4 g + i ----
-  if (!active) return;
+  // ---- merge the two token halves of each row group, normalise, store ----
+  __syncthreads();   // the raw staging rows are free
+  float4* mo = reinterpret_cast<float4*>(s_lds);
+  float2* mml = reinterpret_cast<float2*>(s_lds + kMergeO);
+  if (th == 1 && active) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float li = __shfl(l_run, 4 * g + i, 64);
-    const int r = r0 + 4 * g + i;
-    if (r < P.chunk) {
-      const float inv = 1.0f / li;
-      float* o = P.out + ((int64_t)r * P.n_q + hq) * D;
+    for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-        *reinterpret_cast<float4*>(o + 64 * qb + 4 * n) =
-            make_float4(O[qb][0][i] * inv, O[qb][1][i] * inv, O[qb][2][i] * inv, O[qb][3][i] * inv);
+      for (int kk = 0; kk < 4; ++kk)
+        mo[(rg * 8 + 4 * qb + kk) * 64 + lane] = make_float4(O[qb][kk][0], O[qb][kk][1], O[qb][kk][2], O[qb][kk][3]);
+    mml[rg * 64 + lane] = make_float2(m_run, l_run);
+  }
+  __syncthreads();
+  if (th == 1 || !row_ok) return;
+  const float2 ml2 = mml[rg * 64 + lane];
+  const float M = fmaxf(m_run, ml2.x);   // finite: every row sees its own position
+  const float fa = (m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run - M);
+  const float fb = (ml2.x == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(ml2.x - M);
+  const float inv = 1.0f / (l_run * fa + ml2.y * fb);
+  const float ca = fa * inv, cb = fb * inv;
+  float* o = P.out + ((int64_t)(r0 + n) * P.n_q + hq) * D;
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    float4 ob[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) ob[kk] = mo[(rg * 8 + 4 * qb + kk) * 64 + lane];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float b0 = i == 0 ? ob[0].x : i == 1 ? ob[0].y : i == 2 ? ob[0].z : ob[0].w;
+      const float b1 = i == 0 ? ob[1].x : i == 1 ? ob[1].y : i == 2 ? ob[1].z : ob[1].w;
+      const float b2 = i == 0 ? ob[2].x : i == 1 ? ob[2].y : i == 2 ? ob[2].z : ob[2].w;
+      const float b3 = i == 0 ? ob[3].x : i == 1 ? ob[3].y : i == 2 ? ob[3].z : ob[3].w;
+      *reinterpret_cast<float4*>(o + 64 * qb + 16 * g + 4 * i) =
+          make_float4(O[qb][0][i] * ca + b0 * cb, O[qb][1][i] * ca + b1 * cb,
+                      O[qb][2][i] * ca + b2 * cb, O[qb][3][i] * ca + b3 * cb);
     }
   }
 }
@@ -474,7 +694,7 @@ __global__ void __launch_bounds__(256) prefill_mfma_kernel(PrefillParams P) {
 hipError_t launch_prefill_mfma(const PrefillParams& P, hipStream_t stream) {
   const int n_blk = ((P.chunk + kRows - 1) / kRows) * P.G;
   dim3 grid((n_blk + 3) / 4, P.n_kv);
-  hipLaunchKernelGGL(prefill_mfma_kernel, grid, dim3(256), 0, stream, P);
+  hipLaunchKernelGGL(prefill_mfma_kernel, grid, dim3(kThreads), 0, stream, P);
   return hipGetLastError();
 }
 
