@@ -52,11 +52,15 @@ constexpr int kThreads = 512;                      // 8 waves
 constexpr int kRawTok = 32;                        // raw tokens staged per step
 constexpr int kRawRow = D + 4;                     // padded LDS row of raw K / V (floats)
 constexpr int kOpBytes = 32768;                    // one tile's K or V operands (fp16)
-// per-tile constants after the operands: f32 alpha, vsf, vmin, vcu; f16 kh, kl, mh, ml
-constexpr int kCAlpha = 2 * kOpBytes, kCVsf = kCAlpha + 512, kCVmin = kCVsf + 512, kCVcu = kCVmin + 512;
-constexpr int kCKh = kCVcu + 512, kCKl = kCKh + 256, kCMh = kCKl + 256, kCMl = kCMh + 256;
-constexpr int kBufBytes = kCMl + 256;              // one tile: operands + constants
-constexpr int kLdsBytes = 2 * kBufBytes;           // double-buffered tiles
+// LDS: K operands of buffers 0 and 1, V operands of buffers 0 and 1, then the
+// two constant areas, so that every read of a tile is a lane offset plus an
+// immediate below 64 KB.  Constants: f32 alpha, vsf, vmin, vcu; f16 kh, kl, mh, ml
+constexpr int kCAlpha = 0, kCVsf = 512, kCVmin = 1024, kCVcu = 1536;
+constexpr int kCKh = 2048, kCKl = 2304, kCMh = 2560, kCMl = 2816;
+constexpr int kCExp = 3072;                        // int ek, ev, em
+constexpr int kConstBytes = 3088;
+constexpr int kLdsK = 0, kLdsV = 2 * kOpBytes, kLdsC = 4 * kOpBytes;
+constexpr int kLdsBytes = kLdsC + 2 * kConstBytes;
 constexpr int kLdsRaw = 2 * kRawTok * kRawRow * 4; // raw K and V rows (over the tiles)
 constexpr int kMergeO = 4 * 8 * 64 * 16;           // merge: O of the h = 1 waves, then (m, l)
 static_assert(kLdsRaw <= kLdsBytes && kMergeO + 4 * 64 * 8 <= kLdsBytes, "staging fits");
@@ -122,12 +126,15 @@ __device__ __forceinline__ int swk(int b, int n) { return ((b & 3) << 1) | ((n >
 __device__ __forceinline__ int swv(int q, int n) { return ((q >> 2) & 1) ^ ((n >> 3) & 1); }
 
 // What one thread loads of a record for the unpack: waves 0-3 one dword of
-// 8 K channel rows, waves 4-7 two bytes of 8 V token rows, every lane two
-// scale pairs for the tile maxima and up to two inputs of the constants.
+// 8 K channel rows, waves 4-7 two bytes of 8 V token rows; every lane the
+// pair(s) of the scale array(s) whose tile maximum its wave needs and the
+// input(s) of its share of the constants.  Constant work by wave:
+//   0, 1: alpha (needs ek)         2, 3: kh, kl (ek)
+//   4, 5: vsf, vmin (ev)           6, 7: vcu (ev), mh, ml (em)
 struct TileRegs {
   uint32_t c[8];
-  float2 k2, v2, m2;
-  float c0, c1;
+  float2 xa, xb;
+  float c0, c1, c2;
 };
 
 __device__ __forceinline__ void load_tile(const uint8_t* rec, int lane, int wv, TileRegs& r) {
@@ -144,54 +151,56 @@ __device__ __forceinline__ void load_tile(const uint8_t* rec, int lane, int wv, 
       for (int i = 0; i < 4; ++i)
         r.c[4 * h + i] = *reinterpret_cast<const uint16_t*>(vcode + (32 * (wv - 4) + 16 * h + 4 * hi4 + i) * (D / 4) + 2 * lo4);
   }
-  const float* ks = reinterpret_cast<const float*>(rec + kOffKscale);
-  const float* vs = reinterpret_cast<const float*>(rec + kOffVscale);
-  const float* km = reinterpret_cast<const float*>(rec + kOffKmin);
-  r.k2 = *reinterpret_cast<const float2*>(ks + 2 * lane);
-  r.v2 = *reinterpret_cast<const float2*>(vs + 2 * lane);
-  r.m2 = *reinterpret_cast<const float2*>(km + 2 * lane);
-  const int idx = 16 * wv + lo4;
-  const int arr = hi4;   // 0: ktok, 1: vscale + vmin, 2: kscale + vchan, 3: kmin
-  const float* s0 = reinterpret_cast<const float*>(rec + (arr == 0 ? kOffKtok : arr == 1 ? kOffVscale : arr == 2 ? kOffKscale : kOffKmin));
-  const float* s1 = reinterpret_cast<const float*>(rec + (arr == 1 ? kOffVmin : kOffVchan));
-  r.c0 = s0[idx];
-  r.c1 = s1[idx];
+  const float* f = reinterpret_cast<const float*>(rec);
+  const int idx = 64 * (wv & 1) + lane;
+  const int role = wv >> 1;
+  r.xa = *reinterpret_cast<const float2*>(f + (role < 2 ? kOffKscale : kOffVscale) / 4 + 2 * lane);
+  r.xb = *reinterpret_cast<const float2*>(f + kOffKmin / 4 + 2 * lane);
+  r.c0 = f[(role == 0 ? kOffKtok : role == 1 ? kOffKscale : role == 2 ? kOffVscale : kOffVchan) / 4 + idx];
+  r.c1 = f[(role == 2 ? kOffVmin : kOffKmin) / 4 + idx];
+  r.c2 = 0.0f;
 }
 
-// Unpack one tile (from TileRegs) into an operand buffer and its constants:
+// Unpack one tile (from TileRegs) into K / V operand buffers and a constant area:
 //   alpha[t] = scale log2(e) ktok[t] 2^(7 + ek)        (score factor)
 //   vsf[t]   = vscale[t] 2^(13 - tau - ev)             (w = p vsf < 2^14)
 //   vmin[t]  = vmin[t]
 //   vcu[c]   = vchan[c] 2^(24 - shift(c)) / 2^(13 - tau - ev)
 //   kh + kl  = kscale[c] 2^(13 - ek)                   (fp16 hi, lo)
 //   mh + ml  = kmin[c] 2^(13 - em)                     (fp16 hi, lo)
-// with ek, ev, em the floor(log2) of the tile's largest kscale, vscale, |kmin|,
-// shift 4 for even channels and 6 for odd ones (the crumb's bit position).
-// Waves 0-3 unpack K channel groups 4 w + lane/16, tokens 8 (lane % 16) .. + 7;
-// waves 4-7 V token step w - 4, token group lane/16, channels 8 (lane % 16) .. + 7.
-__device__ __forceinline__ void unpack_tile(const TileRegs& r, uint8_t* buf, int lane, int wv,
-                                            float scale_log2, int& ek, int& ev, int& em) {
+// with ek, ev, em the floor(log2) of the tile's largest kscale, vscale, |kmin|
+// (stored for the compute), shift 4 for even channels and 6 for odd ones (the
+// crumb's bit position).  Waves 0-3 unpack K channel groups 4 w + lane/16,
+// tokens 8 (lane % 16) .. + 7; waves 4-7 V token step w - 4, token group
+// lane/16, channels 8 (lane % 16) .. + 7.
+__device__ __forceinline__ void unpack_tile(const TileRegs& r, uint8_t* kdst, uint8_t* vdst, uint8_t* buf,
+                                            int lane, int wv, float scale_log2) {
   const int hi4 = lane >> 4, lo4 = lane & 15;
   if (wv < 4) {
     const int b0 = lo4 >> 1, n3 = lo4 & 1;   // token 8 lo4 + tt: block lo4 / 2, n = 8 n3 + tt
-    uint4* dst = reinterpret_cast<uint4*>(buf) + (wv * 8 + b0) * 64 + 16 * hi4;
+    uint4* dst = reinterpret_cast<uint4*>(kdst) + (wv * 8 + b0) * 64 + 16 * hi4;
     const int sw = swk(b0, 8 * n3);
+    uint32_t lo[8], hi[8];   // low / high nibbles of every byte, in bits 4-7
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      lo[e] = (r.c[e] << 4) & 0xF0F0F0F0u;
+      hi[e] = r.c[e] & 0xF0F0F0F0u;
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const uint32_t sel = (uint32_t)j | (0x0Cu << 8) | ((uint32_t)(4 + j) << 16) | (0x0Cu << 24);
       uint32_t ev4[4], od4[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const uint32_t x = __builtin_amdgcn_perm(r.c[2 * k + 1], r.c[2 * k], sel);
-        ev4[k] = (x << 4) & 0x00F000F0u;
-        od4[k] = x & 0x00F000F0u;
+        ev4[k] = __builtin_amdgcn_perm(lo[2 * k + 1], lo[2 * k], sel);
+        od4[k] = __builtin_amdgcn_perm(hi[2 * k + 1], hi[2 * k], sel);
       }
       const int n0 = 8 * n3 + 2 * j;
       dst[n0 ^ sw] = make_uint4(ev4[0], ev4[1], ev4[2], ev4[3]);
       dst[(n0 + 1) ^ sw] = make_uint4(od4[0], od4[1], od4[2], od4[3]);
     }
   } else {
-    uint4* dst = reinterpret_cast<uint4*>(buf + kOpBytes) + ((wv - 4) * 8) * 64 + 16 * hi4;
+    uint4* dst = reinterpret_cast<uint4*>(vdst) + ((wv - 4) * 8) * 64 + 16 * hi4;
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb) {
       const uint32_t sel = (uint32_t)bb | (0x0Cu << 8) | ((uint32_t)(4 + bb) << 16) | (0x0Cu << 24);
@@ -210,34 +219,31 @@ __device__ __forceinline__ void unpack_tile(const TileRegs& r, uint8_t* buf, int
       }
     }
   }
-  // every wave finds the maxima and writes one eighth of the constants
-  ek = exp_floor(wave_max_nn(fmaxf(r.k2.x, r.k2.y)), -114, 120);
-  ev = exp_floor(wave_max_nn(fmaxf(r.v2.x, r.v2.y)), -100, 100);
-  em = exp_floor(wave_max_nn(fmaxf(fabsf(r.m2.x), fabsf(r.m2.y))), -100, 100);
-  const int idx = 16 * wv + lo4;
-  const int fvexp = 13 - (int)kTau - ev;
-  switch (hi4) {
-    case 0:
-      reinterpret_cast<float*>(buf + kCAlpha)[idx] = scale_log2 * r.c0 * pow2i(7 + ek);
-      break;
-    case 1:
-      reinterpret_cast<float*>(buf + kCVsf)[idx] = r.c0 * pow2i(fvexp);
-      reinterpret_cast<float*>(buf + kCVmin)[idx] = r.c1;
-      break;
-    case 2: {
-      const float x = r.c0 * pow2i(13 - ek);
-      const _Float16 h = (_Float16)x;
-      reinterpret_cast<_Float16*>(buf + kCKh)[idx] = h;
-      reinterpret_cast<_Float16*>(buf + kCKl)[idx] = (_Float16)(x - (float)h);
-      reinterpret_cast<float*>(buf + kCVcu)[idx] = r.c1 * pow2i(24 - ((idx & 1) ? 6 : 4) - fvexp);
-      break;
-    }
-    default: {
-      const float x = r.c0 * pow2i(13 - em);
-      const _Float16 h = (_Float16)x;
-      reinterpret_cast<_Float16*>(buf + kCMh)[idx] = h;
-      reinterpret_cast<_Float16*>(buf + kCMl)[idx] = (_Float16)(x - (float)h);
-    }
+  // constants: each wave needs one or two tile maxima
+  const int role = wv >> 1;
+  const int idx = 64 * (wv & 1) + lane;
+  const int ea = exp_floor(wave_max_nn(fmaxf(r.xa.x, r.xa.y)), role < 2 ? -114 : -100, role < 2 ? 120 : 100);
+  int* ex = reinterpret_cast<int*>(buf + kCExp);
+  if (role == 0) {
+    reinterpret_cast<float*>(buf + kCAlpha)[idx] = scale_log2 * r.c0 * pow2i(7 + ea);
+    if (wv == 0 && lane == 0) ex[0] = ea;
+  } else if (role == 1) {
+    const float x = r.c0 * pow2i(13 - ea);
+    const _Float16 h = (_Float16)x;
+    reinterpret_cast<_Float16*>(buf + kCKh)[idx] = h;
+    reinterpret_cast<_Float16*>(buf + kCKl)[idx] = (_Float16)(x - (float)h);
+  } else if (role == 2) {
+    reinterpret_cast<float*>(buf + kCVsf)[idx] = r.c0 * pow2i(13 - (int)kTau - ea);
+    reinterpret_cast<float*>(buf + kCVmin)[idx] = r.c1;
+    if (wv == 4 && lane == 0) ex[1] = ea;
+  } else {
+    reinterpret_cast<float*>(buf + kCVcu)[idx] = r.c0 * pow2i(24 - ((idx & 1) ? 6 : 4) - (13 - (int)kTau - ea));
+    const int em = exp_floor(wave_max_nn(fmaxf(fabsf(r.xb.x), fabsf(r.xb.y))), -100, 100);
+    const float x = r.c1 * pow2i(13 - em);
+    const _Float16 h = (_Float16)x;
+    reinterpret_cast<_Float16*>(buf + kCMh)[idx] = h;
+    reinterpret_cast<_Float16*>(buf + kCMl)[idx] = (_Float16)(x - (float)h);
+    if (wv == 6 && lane == 0) ex[2] = em;
   }
 }
 
@@ -283,7 +289,6 @@ __global__ void __launch_bounds__(kThreads) prefill_mfma_kernel(PrefillParams P)
   // ---- tile 0 unpacked, tile 1 in registers; this lane's rotated query:
   // row n, channels 32 k4 + 8 g .. + 7 ----
   TileRegs tr;
-  int ek = 0, ev = 0, em = 0;   // exponents of the tile being computed
   if (T_wg > 0) load_tile(recs, lane, wv, tr);
   float qv[4][8];
   {
@@ -300,7 +305,7 @@ __global__ void __launch_bounds__(kThreads) prefill_mfma_kernel(PrefillParams P)
     }
   }
   if (T_wg > 0) {
-    unpack_tile(tr, s_lds, lane, wv, scale_log2, ek, ev, em);
+    unpack_tile(tr, s_lds + kLdsK, s_lds + kLdsV, s_lds + kLdsC, lane, wv, scale_log2);
     if (T_wg > 1) load_tile(recs + rstride, lane, wv, tr);
   }
   __syncthreads();
@@ -340,17 +345,27 @@ __global__ void __launch_bounds__(kThreads) prefill_mfma_kernel(PrefillParams P)
     for (int kk = 0; kk < 4; ++kk) O[qb][kk] = (floatx4){0.f, 0.f, 0.f, 0.f};
 
   // ---- compressed tiles: compute tile j while unpacking tile j + 1 into the
-  // other buffer and loading tile j + 2 ----
+  // other buffer and loading tile j + 2.  The two waves on a SIMD (token
+  // halves 0 and 1 of a row group) unpack at opposite ends of the iteration,
+  // so the matrix work of one meets the vector work of the other. ----
   for (int j = 0; j < T_wg; ++j) {
-    const uint8_t* cst = s_lds + (j & 1) * kBufBytes;
-    const uint4* kop = reinterpret_cast<const uint4*>(cst);
-    const uint4* vop = reinterpret_cast<const uint4*>(cst + kOpBytes);
-    int ekn = 0, evn = 0, emn = 0;
-    if (j + 1 < T_wg) {
-      unpack_tile(tr, s_lds + ((j + 1) & 1) * kBufBytes, lane, wv, scale_log2, ekn, evn, emn);
+    const int pb = j & 1;   // buffer of tile j
+    const uint8_t* cst = s_lds + kLdsC + pb * kConstBytes;
+    const uint4* kop = reinterpret_cast<const uint4*>(s_lds + kLdsK + pb * kOpBytes);
+    const uint4* vop = reinterpret_cast<const uint4*>(s_lds + kLdsV + pb * kOpBytes);
+    const bool next = j + 1 < T_wg;
+    auto unpack_next = [&]() {
+      const int nb = pb ^ 1;
+      unpack_tile(tr, s_lds + kLdsK + nb * kOpBytes, s_lds + kLdsV + nb * kOpBytes, s_lds + kLdsC + nb * kConstBytes,
+                  lane, wv, scale_log2);
       if (j + 2 < T_wg) load_tile(recs + (int64_t)(j + 2) * rstride, lane, wv, tr);
-    }
+    };
+    if (th == 0 && next) unpack_next();
     if (j < T_wave) {
+      const int* ex = reinterpret_cast<const int*>(cst + kCExp);
+      const int ek = __builtin_amdgcn_readfirstlane(ex[0]);
+      const int ev = __builtin_amdgcn_readfirstlane(ex[1]);
+      const int em = __builtin_amdgcn_readfirstlane(ex[2]);
       // B operands: q~ = q' kscale 2^(13 - ek - eq) = (qh + ql)(kh + kl) as hi + lo,
       // by packed fp16 arithmetic (hi rounded, lo = exact product rest + cross terms)
       half8 Bh[4], Bl[4];
@@ -499,11 +514,9 @@ __global__ void __launch_bounds__(kThreads) prefill_mfma_kernel(PrefillParams P)
         }
       }
     }
+    if (th == 1 && next) unpack_next();
     // tile j + 1 is in place and every wave is done with tile j's buffer
     __syncthreads();
-    ek = ekn;
-    ev = evn;
-    em = emn;
   }
 
   // ---- inverse rotation of the tile part: channel bits kk (0, 1), i (2, 3),
