@@ -147,6 +147,42 @@ def decode_case(torch, kvarn, synth, ctx, steps, warmup, seed=2):
     return info, reps * L, warm * L, (K, V, rec0, T, n_w, qs, scale)
 
 
+def verify_case(torch, kvarn, synth, ctx, width, reps=20, seed=2):
+    """Multi-query verify of `width` draft rows at the 8B decode shape: one call
+    reads every record once for all rows (the workload of a decode step)."""
+    d, Hq, Hkv, W = 128, 32, 8, 256
+    dev = "cuda:0"
+    T = kvarn.visible_tiles(ctx - 1, W)
+    n_w = ctx - 128 * T
+    tb = kvarn.tile_bytes(d)
+    scale = 1.0 / math.sqrt(d)
+    per_layer = T * Hkv * tb + 2 * n_w * Hkv * d * 4
+    L = max(8, int(math.ceil(2 * LLC_BYTES / per_layer)))
+    K, V = synth.make_kv(seed, ctx, Hkv, d, synth.outliers_for(d, 0.01))
+    kd = torch.from_numpy(K).to(dev)
+    vd = torch.from_numpy(V).to(dev)
+    rec0 = torch.empty(T, Hkv, tb, dtype=torch.uint8, device=dev)
+    kvarn.compress_tile(kd, vd, rec0, T)
+    recs = [rec0.clone() for _ in range(L)]
+    kw = [kd[128 * T:].clone()[None] for _ in range(L)]
+    vw = [vd[128 * T:].clone()[None] for _ in range(L)]
+    qs = torch.from_numpy(synth.make_q(seed, L * width, Hq, d)).to(dev).reshape(L, 1, width, Hq, d)
+    outs = torch.empty_like(qs)
+    ws_bytes = kvarn.decode_workspace_bytes(qs[0], None, recs[0], [0], [T], kw[0], vw[0], [n_w], scale)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def run():
+        for l in range(L):
+            kvarn.decode_attention(qs[l], None, recs[l], [0], [T], kw[l], vw[l], [n_w], scale,
+                                   out=outs[l], workspace=ws)
+
+    ms, _ = graph_ms(torch, run, L, reps)
+    return {"width": width, "context": ctx, "us_per_call": ms * 1e3,
+            "query_rows_per_s": width / (ms * 1e-3), "layers_cycled": L,
+            "algorithmic_bytes": decode_bytes(T, n_w, Hq, Hkv, d, tb)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -182,6 +218,12 @@ def main():
                 extra.append(info)
                 log(f"decode context {c}: {info['us_per_step']:.2f} us per call, "
                     f"{info['achieved_GBps']:.0f} GB/s algorithmic")
+
+    # ---- multi-query verify (width 8) at the same context ----
+    verify = verify_case(torch, kvarn, synth, args.context, 8)
+    verify["vs_decode_call"] = verify["us_per_call"] / head["us_per_step"]
+    log(f"verify width 8 at context {args.context}: {verify['us_per_call']:.2f} us per call "
+        f"({verify['vs_decode_call']:.2f} decode calls)")
 
     # ---- compression throughput (the prompt's 119 x 8 tile-heads in one launch) ----
     K, V, rec0, T, n_w, qs, scale = keep
@@ -284,6 +326,7 @@ def main():
         "hbm_GBps": achieved,
         "decode_contexts": [head] + extra,
         "prefill": prefill,
+        "verify": verify,
         "compress": compress,
         "cpu_baseline": cpu,
     }

@@ -149,6 +149,15 @@ typedef struct kvarn_decode_args {
   const int32_t* n_win;    /* host [batch] window tokens per sequence           */
   int32_t max_win;         /* grid bound: >= n_win[b] for every b               */
   float* out;              /* device [batch][n_q_heads][head_dim]               */
+  int32_t q_len;           /* query rows per sequence, 0 or 1: one decode query;
+                              2..8: multi-query verify (head_dim 128).  Then q,
+                              q_rot and out are [batch][q_len][n_q_heads][head_dim]
+                              and row i of sequence b is the query of window token
+                              n_win[b] - q_len + i: it sees the n_tiles[b] tiles
+                              and window tokens [0, n_win[b] - q_len + i]
+                              (n_win[b] >= q_len).  gmlx PR #116 commit list:
+                              verify widths 2-8 attend the records on the matrix
+                              units at about the cost of one decode step.       */
 } kvarn_decode_args;
 
 /* Workspace bytes kvarn_decode_attention needs for these arguments (0 on
@@ -159,8 +168,10 @@ size_t kvarn_decode_workspace_bytes(const kvarn_decode_args* args);
 
 /* Errors: KVARN_E_INVALID (null pointers, counts out of range, a sequence with
  * no visible key, rec_start[b] + n_tiles[b] > n_record_rows, n_tiles[b] >
- * max_tiles, n_win[b] > max_win, win_start[b] < 0), KVARN_E_UNSUPPORTED (head_dim, GQA ratio,
- * batch > KVARN_MAX_BATCH, group of more than 8 query heads per KV head),
+ * max_tiles, n_win[b] > max_win, win_start[b] < 0, q_len outside 0..8,
+ * n_win[b] < q_len), KVARN_E_UNSUPPORTED (head_dim, GQA ratio, batch >
+ * KVARN_MAX_BATCH, group of more than 8 query heads per KV head, q_len >= 2
+ * with head_dim other than 128),
  * KVARN_E_ALIGN, KVARN_E_WORKSPACE. */
 int kvarn_decode_attention(const kvarn_decode_args* args, void* workspace,
                            size_t workspace_bytes, void* stream);

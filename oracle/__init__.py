@@ -18,6 +18,9 @@ Method sources (cited by page and section):
     deferred inverse WHT).
   * SharpInference issue #433 (follow-ups), item 2: split-tile decode with an
     LSE combine, inverse WHT after combining the rotated tile partials.
+  * gmlx PR #116 "KVarN variance-normalized KV cache", commit list:
+    speculative-verify widths 2-8 attend the compressed records (verify
+    rows are decode queries).
   * colibri PR #399, maintainer's "Ready for review" comment: for an
     orthogonal rotation, q . xhat == rotate(q) . c and the weighted value sum
     is the unrotation of the weighted code sum.
@@ -314,3 +317,17 @@ def prefill_row(q_row: np.ndarray, pos: int, window: int, khat: np.ndarray,
     T = visible_tiles(pos, window)
     lo = TILE * T
     return decode(q_row, khat, vhat, T, K[lo:pos + 1], V[lo:pos + 1], scale)
+
+
+def verify(q: np.ndarray, khat: np.ndarray, vhat: np.ndarray, n_tiles: int,
+           k_win: np.ndarray, v_win: np.ndarray, scale: float) -> np.ndarray:
+    """Multi-query verify (gmlx PR #116 commit list, verify widths 2-8): the
+    w = q.shape[0] newest window tokens are the query rows; row i is the
+    decode query of window token n_w - w + i and sees the n_tiles tiles plus
+    window tokens [0, n_w - w + i].  q: [w][Hq][d]; k_win/v_win: the raw
+    window [n_w][Hkv][d].  Returns out [w][Hq][d] fp64."""
+    w = q.shape[0]
+    n_w = k_win.shape[0]
+    assert n_w >= w
+    return np.stack([decode(q[i], khat, vhat, n_tiles, k_win[:n_w - w + i + 1],
+                            v_win[:n_w - w + i + 1], scale) for i in range(w)])

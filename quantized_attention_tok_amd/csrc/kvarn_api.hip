@@ -55,9 +55,41 @@ DecodePlan plan_fused(int batch, int n_kv, int max_tiles, int max_win) {
   return p;
 }
 
+int q_rows(const kvarn_decode_args* a) { return a->q_len > 1 ? a->q_len : 1; }
+
+// Multi-query verify plan (head_dim 128 prefill workgroups of 8 waves, one per
+// CU): window splits of 64 raw tokens (at most 16 of them), and tiles per
+// split so that all splits of all (sequence, KV head, row block) groups fit
+// on the 256 CUs at once; at most 64 splits in all (the combine's limit).
+DecodePlan plan_verify(int batch, int n_kv, int G, int max_tiles, int max_win) {
+  const int64_t groups = (int64_t)batch * n_kv * ((G + 3) / 4);
+  int wchunk = 64;
+  int nr = (max_win + wchunk - 1) / wchunk;
+  if (nr > 16) {
+    wchunk = ((max_win + 15) / 16 + 31) / 32 * 32;
+    nr = (max_win + wchunk - 1) / wchunk;
+  }
+  if (nr < 1) nr = 1;
+  int64_t per = 256 / groups;
+  int64_t avail = per - nr;
+  if (avail < 1) avail = 1;
+  if (avail > 64 - nr) avail = 64 - nr;
+  int64_t tps = max_tiles > 0 ? (max_tiles + avail - 1) / avail : 1;
+  if (tps < 1) tps = 1;
+  DecodePlan p;
+  p.tps = (int)tps;
+  p.n_tsplit = max_tiles > 0 ? (int)((max_tiles + tps - 1) / tps) : 0;
+  p.n_wsplit = nr;
+  p.wchunk = wchunk;
+  return p;
+}
+
 int validate_decode(const kvarn_decode_args* a, DecodePlan* plan) {
   if (!a) return KVARN_E_INVALID;
   if (!dim_ok(a->head_dim)) return KVARN_E_UNSUPPORTED;
+  if (a->q_len < 0 || a->q_len > 8) return KVARN_E_INVALID;
+  const int w = q_rows(a);
+  if (w > 1 && a->head_dim != 128) return KVARN_E_UNSUPPORTED;
   if (a->batch < 1 || a->n_q_heads < 1 || a->n_kv_heads < 1) return KVARN_E_INVALID;
   if (a->batch > KVARN_MAX_BATCH) return KVARN_E_UNSUPPORTED;
   if (a->n_q_heads % a->n_kv_heads != 0) return KVARN_E_UNSUPPORTED;
@@ -72,6 +104,7 @@ int validate_decode(const kvarn_decode_args* a, DecodePlan* plan) {
     if (nt < 0 || nw < 0 || nt > a->max_tiles || nw > a->max_win) return KVARN_E_INVALID;
     if (a->win_start && a->win_start[b] < 0) return KVARN_E_INVALID;
     if (nt + nw == 0) return KVARN_E_INVALID;
+    if (nw < w && w > 1) return KVARN_E_INVALID;
     if (nt > 0) {
       if (a->rec_start[b] < 0 || a->rec_start[b] + nt > a->n_record_rows) return KVARN_E_INVALID;
       any_tiles = true;
@@ -88,7 +121,8 @@ int validate_decode(const kvarn_decode_args* a, DecodePlan* plan) {
   if (!st16(a->win_seq_stride) || !st16(a->win_tok_stride) || !st16(a->win_head_stride))
     return KVARN_E_ALIGN;
   if (plan) {
-    *plan = fused_decode(a->head_dim)
+    *plan = w > 1 ? plan_verify(a->batch, a->n_kv_heads, G, a->max_tiles, a->max_win)
+          : fused_decode(a->head_dim)
                 ? plan_fused(a->batch, a->n_kv_heads, a->max_tiles, a->max_win)
                 : plan_decode(a->batch, a->n_kv_heads, a->max_tiles, a->max_win, kTargetGroups,
                               kvarn::kWinChunk);
@@ -96,11 +130,11 @@ int validate_decode(const kvarn_decode_args* a, DecodePlan* plan) {
   return KVARN_OK;
 }
 
-size_t decode_part_floats(int batch, int n_q, int d, const DecodePlan& p) {
-  return (size_t)batch * n_q * (size_t)(p.n_tsplit + p.n_wsplit) * (size_t)(d + 4);
+size_t decode_part_floats(int rows, int n_q, int d, const DecodePlan& p) {
+  return (size_t)rows * n_q * (size_t)(p.n_tsplit + p.n_wsplit) * (size_t)(d + 4);
 }
-size_t decode_ws(int batch, int n_q, int d, const DecodePlan& p) {
-  return decode_part_floats(batch, n_q, d, p) * sizeof(float);
+size_t decode_ws(const kvarn_decode_args* a, const DecodePlan& p) {
+  return decode_part_floats(a->batch * q_rows(a), a->n_q_heads, a->head_dim, p) * sizeof(float);
 }
 
 int64_t prefill_tiles_at(int64_t pos, int window) {
@@ -189,7 +223,7 @@ int kvarn_rotate_query(int32_t head_dim, int64_t n_rows, const float* q, float* 
 size_t kvarn_decode_workspace_bytes(const kvarn_decode_args* a) {
   DecodePlan p;
   if (validate_decode(a, &p) != KVARN_OK) return 0;
-  return decode_ws(a->batch, a->n_q_heads, a->head_dim, p);
+  return decode_ws(a, p);
 }
 
 int kvarn_decode_attention(const kvarn_decode_args* a, void* workspace, size_t ws_bytes,
@@ -198,7 +232,8 @@ int kvarn_decode_attention(const kvarn_decode_args* a, void* workspace, size_t w
   int st = validate_decode(a, &p);
   if (st != KVARN_OK) return st;
   const bool fused = fused_decode(a->head_dim);
-  const size_t need = decode_ws(a->batch, a->n_q_heads, a->head_dim, p);
+  const int w = q_rows(a);
+  const size_t need = decode_ws(a, p);
   if (!workspace || ws_bytes < need) return KVARN_E_WORKSPACE;
   if (!al16(workspace)) return KVARN_E_ALIGN;
   kvarn::DecodeParams P;
@@ -228,8 +263,14 @@ int kvarn_decode_attention(const kvarn_decode_args* a, void* workspace, size_t w
     P.n_tiles[b] = a->n_tiles[b];
     P.n_win[b] = a->n_win[b];
   }
-  hipError_t e = fused ? kvarn::launch_decode_fused(P, a->batch, (hipStream_t)stream)
-                       : kvarn::launch_decode(a->head_dim, P, a->batch, (hipStream_t)stream);
+  hipError_t e;
+  if (w > 1) {
+    P.q_len = w;   // without q_rot the workgroups rotate the rows themselves
+    e = kvarn::launch_verify_mfma(P, a->batch, (hipStream_t)stream);
+  } else {
+    e = fused ? kvarn::launch_decode_fused(P, a->batch, (hipStream_t)stream)
+              : kvarn::launch_decode(a->head_dim, P, a->batch, (hipStream_t)stream);
+  }
   return e == hipSuccess ? KVARN_OK : KVARN_E_DEVICE;
 }
 

@@ -30,6 +30,7 @@ struct DecodeParams {
   // sequence; it sees T(p) tiles and raw rows [128 T(p), p] of k_win/v_win,
   // where raw row p lives at (p - raw_base) * win_tok_stride.
   int mode;
+  int q_len;                       // query rows per sequence (multi-query verify)
   int window;
   int64_t pos0, raw_base;
   int64_t rec_start[64];
@@ -85,5 +86,9 @@ hipError_t launch_rotate(int d, int64_t n_rows, const float* q, float* q_rot, hi
 hipError_t launch_decode(int d, const DecodeParams& P, int batch, hipStream_t stream);
 hipError_t launch_decode_fused(const DecodeParams& P, int batch, hipStream_t stream);
 hipError_t launch_prefill_mfma(const PrefillParams& P, hipStream_t stream);
+// Multi-query verify (head_dim 128): P.part holds batch * q_len * n_q *
+// (n_tsplit + n_wsplit) partials of D + 4 floats (n_wsplit window splits of
+// wchunk tokens); with P.q_rot NULL the kernel rotates q itself.
+hipError_t launch_verify_mfma(const DecodeParams& P, int batch, hipStream_t stream);
 
 }  // namespace kvarn

@@ -255,7 +255,30 @@ __device__ __forceinline__ int tiles_at(int64_t p, int window) {
 __device__ __forceinline__ half2v as_h2(uint32_t x) { return __builtin_bit_cast(half2v, x); }
 __device__ __forceinline__ uint32_t as_u(half2v x) { return __builtin_bit_cast(uint32_t, x); }
 
-__global__ void __launch_bounds__(kThreads) prefill_mfma_kernel(PrefillParams P) {
+// What one workgroup computes: the query rows [0, chunk) of one sequence at
+// positions pos0 + r, against its tiles [ja, jb) (clipped to the tiles the
+// rows see) and, if raw, its raw rows; either the final output or, with part
+// set, the unnormalised partial (m, l, o') of each row and head.
+struct Ctx {
+  const float* q;                  // row r, head h at (r * n_q + h) * D
+  const float* q_rot;
+  float* out;
+  const uint8_t* records;          // tile j, KV head h at (j * n_kv + h) * tile bytes
+  const float* k;                  // raw row of position p, KV head h at
+  const float* v;                  //   (p - raw_base) * tok_stride + h * head_stride
+  int64_t tok_stride, head_stride;
+  int64_t pos0, raw_base;
+  float scale;
+  int chunk, window, n_q, n_kv, G;
+  int ja, jb;
+  bool raw;
+  bool rotate;                     // q_rot absent: rotate q in registers
+  int64_t ra, rb;                  // raw positions [ra, rb) of this workgroup
+  float* part;                     // row r, head h at part + r * part_row + h * part_head
+  int64_t part_row, part_head;
+};
+
+__device__ __forceinline__ void prefill_body(const Ctx& P) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
@@ -279,7 +302,9 @@ __global__ void __launch_bounds__(kThreads) prefill_mfma_kernel(PrefillParams P)
   // positions spanned by the workgroup
   const int64_t p_first = P.pos0 + kRows * (blk_first / G);
   const int64_t p_last = P.pos0 + min(kRows * (blk_last / G) + kRows - 1, P.chunk - 1);
-  const int T_wg = tiles_at(p_last, P.window);
+  const int ja = P.ja;
+  const int jend = min(P.jb, tiles_at(p_last, P.window));   // tiles [ja, jend)
+  const bool partial = P.part != nullptr;
 
   __shared__ __attribute__((aligned(16))) uint8_t s_lds[kLdsBytes];
   const float scale_log2 = P.scale * kLog2e;
@@ -289,10 +314,10 @@ __global__ void __launch_bounds__(kThreads) prefill_mfma_kernel(PrefillParams P)
   // ---- tile 0 unpacked, tile 1 in registers; this lane's rotated query:
   // row n, channels 32 k4 + 8 g .. + 7 ----
   TileRegs tr;
-  if (T_wg > 0) load_tile(recs, lane, wv, tr);
+  if (ja < jend) load_tile(recs + (int64_t)ja * rstride, lane, wv, tr);
   float qv[4][8];
   {
-    const float* qp = P.q_rot + ((int64_t)(row_ok ? r0 + n : 0) * P.n_q + hq) * D + 8 * g;
+    const float* qp = (P.rotate ? P.q : P.q_rot) + ((int64_t)(row_ok ? r0 + n : 0) * P.n_q + hq) * D + 8 * g;
 #pragma unroll
     for (int k4 = 0; k4 < 4; ++k4) {
       float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
@@ -304,11 +329,43 @@ __global__ void __launch_bounds__(kThreads) prefill_mfma_kernel(PrefillParams P)
       qv[k4][4] = b.x; qv[k4][5] = b.y; qv[k4][6] = b.z; qv[k4][7] = b.w;
     }
   }
-  if (T_wg > 0) {
+  if (ja < jend) {
     unpack_tile(tr, s_lds + kLdsK, s_lds + kLdsV, s_lds + kLdsC, lane, wv, scale_log2);
-    if (T_wg > 1) load_tile(recs + rstride, lane, wv, tr);
+    if (ja + 1 < jend) load_tile(recs + (int64_t)(ja + 1) * rstride, lane, wv, tr);
   }
   __syncthreads();
+  if (P.rotate) {   // q' = H q in registers: channel 32 k4 + 8 g + jj (g = lane bits 4, 5)
+#pragma unroll
+    for (int k4 = 0; k4 < 4; ++k4)
+#pragma unroll
+      for (int hb = 1; hb < 8; hb <<= 1)   // channel bits 0-2
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj)
+          if (!(jj & hb)) {
+            const float a = qv[k4][jj], b = qv[k4][jj | hb];
+            qv[k4][jj] = a + b;
+            qv[k4][jj | hb] = a - b;
+          }
+#pragma unroll
+    for (int kb = 1; kb < 4; kb <<= 1)     // channel bits 5, 6
+#pragma unroll
+      for (int k4 = 0; k4 < 4; ++k4)
+        if (!(k4 & kb)) {
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) {
+            const float a = qv[k4][jj], b = qv[k4 | kb][jj];
+            qv[k4][jj] = a + b;
+            qv[k4 | kb][jj] = a - b;
+          }
+        }
+#pragma unroll
+    for (int k4 = 0; k4 < 4; ++k4)
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {     // channel bits 3, 4 across the 16-lane rows
+        const float x = bfly_rows<16>(qv[k4][jj], lane);
+        qv[k4][jj] = bfly_rows<32>(x, lane) * wht_scale<D>();
+      }
+  }
   // q' of row n scaled into (-1, 1) by 2^-eq, as fp16 hi + lo pairs
   float qmax = 0.0f;
 #pragma unroll
@@ -348,17 +405,17 @@ __global__ void __launch_bounds__(kThreads) prefill_mfma_kernel(PrefillParams P)
   // other buffer and loading tile j + 2.  The two waves on a SIMD (token
   // halves 0 and 1 of a row group) unpack at opposite ends of the iteration,
   // so the matrix work of one meets the vector work of the other. ----
-  for (int j = 0; j < T_wg; ++j) {
-    const int pb = j & 1;   // buffer of tile j
+  for (int j = ja; j < jend; ++j) {
+    const int pb = (j - ja) & 1;   // buffer of tile j
     const uint8_t* cst = s_lds + kLdsC + pb * kConstBytes;
     const uint4* kop = reinterpret_cast<const uint4*>(s_lds + kLdsK + pb * kOpBytes);
     const uint4* vop = reinterpret_cast<const uint4*>(s_lds + kLdsV + pb * kOpBytes);
-    const bool next = j + 1 < T_wg;
+    const bool next = j + 1 < jend;
     auto unpack_next = [&]() {
       const int nb = pb ^ 1;
       unpack_tile(tr, s_lds + kLdsK + nb * kOpBytes, s_lds + kLdsV + nb * kOpBytes, s_lds + kLdsC + nb * kConstBytes,
                   lane, wv, scale_log2);
-      if (j + 2 < T_wg) load_tile(recs + (int64_t)(j + 2) * rstride, lane, wv, tr);
+      if (j + 2 < jend) load_tile(recs + (int64_t)(j + 2) * rstride, lane, wv, tr);
     };
     if (th == 0 && next) unpack_next();
     if (j < T_wave) {
@@ -520,8 +577,8 @@ __global__ void __launch_bounds__(kThreads) prefill_mfma_kernel(PrefillParams P)
   }
 
   // ---- inverse rotation of the tile part: channel bits kk (0, 1), i (2, 3),
-  // g (4, 5: across 16-lane rows), qb (6) ----
-  if (T_wave > 0) {
+  // g (4, 5: across 16-lane rows), qb (6); partials stay rotated ----
+  if (T_wave > 0 && !partial) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
@@ -578,13 +635,16 @@ __global__ void __launch_bounds__(kThreads) prefill_mfma_kernel(PrefillParams P)
   const int64_t row_lo = (int64_t)kTile * T_row;
   const float* kbase = P.k + (int64_t)kvh * P.head_stride;
   const float* vbase = P.v + (int64_t)kvh * P.head_stride;
-  for (int64_t t0 = raw_lo; t0 <= p_last; t0 += kRawTok) {
+  // raw tokens of this workgroup: [r_lo, r_hi)
+  const int64_t r_lo = raw_lo > P.ra ? raw_lo : P.ra;
+  const int64_t r_hi = p_last + 1 < P.rb ? p_last + 1 : P.rb;
+  for (int64_t t0 = r_lo; P.raw && t0 < r_hi; t0 += kRawTok) {
     __syncthreads();   // previous readers of the staging rows are done
     {
       const int r = tid >> 4, c4 = tid & 15;
       const int64_t t = t0 + r;
       float4 kx[2], vx[2];
-      if (t <= p_last) {
+      if (t < r_hi) {
         const float4* rk = reinterpret_cast<const float4*>(kbase + (t - P.raw_base) * P.tok_stride);
         const float4* rv = reinterpret_cast<const float4*>(vbase + (t - P.raw_base) * P.tok_stride);
 #pragma unroll
@@ -608,7 +668,7 @@ __global__ void __launch_bounds__(kThreads) prefill_mfma_kernel(PrefillParams P)
     __syncthreads();
     const int sb = th;
     const int64_t tb = t0 + 16 * sb;
-    if (!active || tb > p_wlast || tb + 15 < wave_lo) continue;   // wave-uniform
+    if (!active || tb > p_wlast || tb >= r_hi || tb + 15 < wave_lo) continue;   // wave-uniform
     // S^T[t][r]: A = raw keys (row n = token tb + n), B = raw query of row n;
     // MFMA (jj, e) contracts channels 16 jj + 4 g' + e over K slots g'
     floatx4 sacc = {0.f, 0.f, 0.f, 0.f};
@@ -626,7 +686,7 @@ __global__ void __launch_bounds__(kThreads) prefill_mfma_kernel(PrefillParams P)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int64_t t = tb + 4 * g + i;
-      const bool vis = row_ok && t >= row_lo && t <= prow;
+      const bool vis = row_ok && t >= row_lo && t <= prow && t < r_hi;
       sv[i] = vis ? sacc[i] * scale_log2 : -INFINITY;
       tmax = fmaxf(tmax, sv[i]);
     }
@@ -678,12 +738,21 @@ __global__ void __launch_bounds__(kThreads) prefill_mfma_kernel(PrefillParams P)
   __syncthreads();
   if (th == 1 || !row_ok) return;
   const float2 ml2 = mml[rg * 64 + lane];
-  const float M = fmaxf(m_run, ml2.x);   // finite: every row sees its own position
+  const float M = fmaxf(m_run, ml2.x);   // -inf only for a partial that sees nothing
   const float fa = (m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run - M);
   const float fb = (ml2.x == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(ml2.x - M);
-  const float inv = 1.0f / (l_run * fa + ml2.y * fb);
-  const float ca = fa * inv, cb = fb * inv;
-  float* o = P.out + ((int64_t)(r0 + n) * P.n_q + hq) * D;
+  const float lsum = l_run * fa + ml2.y * fb;
+  float ca = fa, cb = fb;
+  float* o;
+  if (partial) {
+    o = P.part + (int64_t)(r0 + n) * P.part_row + (int64_t)hq * P.part_head;
+    if (g == 0) *reinterpret_cast<float2*>(o + D) = make_float2(M, lsum);
+  } else {
+    const float inv = 1.0f / lsum;   // every row of a final output sees its own position
+    ca *= inv;
+    cb *= inv;
+    o = P.out + ((int64_t)(r0 + n) * P.n_q + hq) * D;
+  }
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     float4 ob[4];
@@ -702,12 +771,166 @@ __global__ void __launch_bounds__(kThreads) prefill_mfma_kernel(PrefillParams P)
   }
 }
 
+__global__ void __launch_bounds__(kThreads) prefill_mfma_kernel(PrefillParams P) {
+  Ctx c;
+  c.q = P.q;
+  c.q_rot = P.q_rot;
+  c.out = P.out;
+  c.records = P.records;
+  c.k = P.k;
+  c.v = P.v;
+  c.tok_stride = P.tok_stride;
+  c.head_stride = P.head_stride;
+  c.pos0 = P.pos0;
+  c.raw_base = P.raw_base;
+  c.scale = P.scale;
+  c.chunk = P.chunk;
+  c.window = P.window;
+  c.n_q = P.n_q;
+  c.n_kv = P.n_kv;
+  c.G = P.G;
+  c.ja = 0;
+  c.jb = 0x7fffffff;
+  c.raw = true;
+  c.rotate = false;
+  c.ra = 0;
+  c.rb = INT64_MAX;
+  c.part = nullptr;
+  c.part_row = c.part_head = 0;
+  prefill_body(c);
+}
+
+// Multi-query verify: sequence b's q_len query rows are the q_len newest
+// window tokens; row i sees the n_tiles[b] tiles and window tokens
+// [0, n_win[b] - q_len + i].  That is the chunked-prefill view at positions
+// 128 T + n_win - q_len + i with window parameter n_win - q_len + 1, so the
+// prefill workgroup computes it.  blockIdx.z = b (n_tsplit + n_wsplit) + s:
+// split s < n_tsplit takes tiles [tps s, tps s + tps), split n_tsplit + r the
+// window tokens [wchunk r, wchunk r + wchunk).  Partials: row r = b q_len + i,
+// head h, split s at part + ((r n_q + h) (n_tsplit + n_wsplit) + s) (D + 4).
+__global__ void __launch_bounds__(kThreads) verify_mfma_kernel(DecodeParams P) {
+  const int ns = P.n_tsplit, nsp = P.n_tsplit + P.n_wsplit;
+  const int b = blockIdx.z / nsp, s = blockIdx.z % nsp;
+  const int w = P.q_len;
+  const int T = P.n_tiles[b], nw = P.n_win[b];
+  Ctx c;
+  const int64_t row0 = (int64_t)b * w * P.n_q * D;
+  c.q = P.q + row0;
+  c.rotate = P.q_rot == nullptr;
+  c.q_rot = c.rotate ? c.q : P.q_rot + row0;
+  c.out = P.out;   // unused: partial output
+  c.records = P.records + P.rec_start[b] * (int64_t)P.n_kv * kRecBytes;
+  c.k = P.k_win + (int64_t)b * P.win_seq_stride + P.win_start[b] * P.win_tok_stride;
+  c.v = P.v_win + (int64_t)b * P.win_seq_stride + P.win_start[b] * P.win_tok_stride;
+  c.tok_stride = P.win_tok_stride;
+  c.head_stride = P.win_head_stride;
+  c.raw_base = (int64_t)kTile * T;
+  c.pos0 = c.raw_base + nw - w;
+  c.window = nw - w + 1;
+  c.scale = P.scale;
+  c.chunk = w;
+  c.n_q = P.n_q;
+  c.n_kv = P.n_kv;
+  c.G = P.G;
+  c.ja = s < ns ? P.tps * s : 0;
+  c.jb = s < ns ? P.tps * (s + 1) : 0;
+  c.raw = s >= ns;
+  c.ra = c.raw_base + (int64_t)P.wchunk * (s - ns);
+  c.rb = c.ra + P.wchunk;
+  c.part_head = (int64_t)nsp * (D + 4);
+  c.part_row = (int64_t)P.n_q * c.part_head;
+  c.part = P.part + (int64_t)b * w * c.part_row + (int64_t)s * (D + 4);
+  prefill_body(c);
+}
+
+// Verify combine: one wave per (row, query head), lane l owns channels l and
+// l + 64.  Lane j first reads split j's (m, l); the tile partials merge with
+// log-sum-exp weights, the sum gets one inverse WHT, then the window partials
+// join the same way and the result is divided by L.  Splits: at most 64.
+__global__ void __launch_bounds__(256) verify_combine_kernel(DecodeParams P, int n_rows) {
+  const int lane = threadIdx.x & 63;
+  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);   // (row, head)
+  if (item >= n_rows * P.n_q) return;   // wave-uniform
+  const int ns = P.n_tsplit, nsp = P.n_tsplit + P.n_wsplit;
+  const float* pp = P.part + (int64_t)item * nsp * (D + 4);
+  float2 ml = make_float2(-INFINITY, 0.0f);
+  if (lane < nsp) ml = *reinterpret_cast<const float2*>(pp + (int64_t)lane * (D + 4) + D);
+  // weights of the tile splits and of the window splits, each against its own maximum
+  const bool tile = lane < ns;
+  float mt = tile ? ml.x : -INFINITY, mr = tile ? -INFINITY : ml.x;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    mt = fmaxf(mt, __shfl_xor(mt, m, 64));
+    mr = fmaxf(mr, __shfl_xor(mr, m, 64));
+  }
+  const float mg = tile ? mt : mr;
+  const float wgt = (ml.x == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(ml.x - mg);
+  float lt = tile ? wgt * ml.y : 0.0f, lr = tile ? 0.0f : wgt * ml.y;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    lt += __shfl_xor(lt, m, 64);
+    lr += __shfl_xor(lr, m, 64);
+  }
+  float o0 = 0.0f, o1 = 0.0f, r0 = 0.0f, r1 = 0.0f;
+  for (int j0 = 0; j0 < nsp; j0 += 8) {
+    float x0[8], x1[8], wj[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int j = j0 + k < nsp ? j0 + k : 0;
+      wj[k] = __shfl(wgt, j, 64);
+      x0[k] = pp[(int64_t)j * (D + 4) + lane];
+      x1[k] = pp[(int64_t)j * (D + 4) + lane + 64];
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int j = j0 + k;
+      const float wk = j < nsp ? wj[k] : 0.0f;
+      if (j < ns) {
+        o0 = fmaf(wk, x0[k], o0);
+        o1 = fmaf(wk, x1[k], o1);
+      } else {
+        r0 = fmaf(wk, x0[k], r0);
+        r1 = fmaf(wk, x1[k], r1);
+      }
+    }
+  }
+  // inverse WHT of the rotated tile sum: element lane in o0, lane + 64 in o1
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    const float y0 = __shfl_xor(o0, m, 64), y1 = __shfl_xor(o1, m, 64);
+    const bool up = (lane & m) != 0;
+    o0 = up ? (y0 - o0) : (o0 + y0);
+    o1 = up ? (y1 - o1) : (o1 + y1);
+  }
+  {
+    const float a = o0, c = o1;
+    o0 = (a + c) * wht_scale<D>();
+    o1 = (a - c) * wht_scale<D>();
+  }
+  const float M = fmaxf(mt, mr);   // finite: every row sees window token 0
+  const float a = (mt == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mt - M);
+  const float bw = (mr == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mr - M);
+  const float inv = 1.0f / (lt * a + lr * bw);
+  float* o = P.out + (int64_t)item * D;
+  o[lane] = (o0 * a + r0 * bw) * inv;
+  o[lane + 64] = (o1 * a + r1 * bw) * inv;
+}
+
 }  // namespace
 
 hipError_t launch_prefill_mfma(const PrefillParams& P, hipStream_t stream) {
   const int n_blk = ((P.chunk + kRows - 1) / kRows) * P.G;
   dim3 grid((n_blk + 3) / 4, P.n_kv);
   hipLaunchKernelGGL(prefill_mfma_kernel, grid, dim3(kThreads), 0, stream, P);
+  return hipGetLastError();
+}
+
+hipError_t launch_verify_mfma(const DecodeParams& P, int batch, hipStream_t stream) {
+  const int n_blk = ((P.q_len + kRows - 1) / kRows) * P.G;
+  dim3 grid((n_blk + 3) / 4, P.n_kv, batch * (P.n_tsplit + P.n_wsplit));
+  hipLaunchKernelGGL(verify_mfma_kernel, grid, dim3(kThreads), 0, stream, P);
+  const int items = batch * P.q_len * P.n_q;
+  hipLaunchKernelGGL(verify_combine_kernel, dim3((items + 3) / 4), dim3(256), 0, stream, P, batch * P.q_len);
   return hipGetLastError();
 }
 

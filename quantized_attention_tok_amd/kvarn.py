@@ -40,7 +40,7 @@ class DecodeArgs(ctypes.Structure):
         ("win_head_stride", ctypes.c_int64),
         ("win_start", ctypes.POINTER(ctypes.c_int64)),
         ("n_win", ctypes.POINTER(ctypes.c_int32)), ("max_win", ctypes.c_int32),
-        ("out", ctypes.c_void_p),
+        ("out", ctypes.c_void_p), ("q_len", ctypes.c_int32),
     ]
 
 
@@ -139,7 +139,10 @@ def rotate_query(q: torch.Tensor, out: torch.Tensor | None = None, stream=None) 
 
 def _decode_args(q, q_rot, records, n_record_rows, rec_start, n_tiles, k_win, v_win, n_win,
                  scale, out, max_tiles=None, max_win=None, win_start=None):
-    B, Hq, d = q.shape
+    if q.dim() == 4:   # [B][q_len][Hq][d]: multi-query verify rows
+        B, w, Hq, d = q.shape
+    else:
+        (B, Hq, d), w = q.shape, 1
     n_kv = k_win.shape[2] if k_win is not None else records.shape[1]
     rs = (ctypes.c_int64 * B)(*[int(x) for x in rec_start])
     ws = (ctypes.c_int64 * B)(*[int(x) for x in (win_start if win_start is not None else [0] * B)])
@@ -158,6 +161,7 @@ def _decode_args(q, q_rot, records, n_record_rows, rec_start, n_tiles, k_win, v_
         a.win_seq_stride, a.win_tok_stride, a.win_head_stride = k_win.stride(0), k_win.stride(1), k_win.stride(2)
     a.max_win = int(max(n_win)) if max_win is None else int(max_win)
     a.out = _ptr(out)
+    a.q_len = w
     return a, (rs, nt, nw, ws)
 
 
@@ -167,7 +171,9 @@ def decode_attention(q, q_rot, records, rec_start, n_tiles, k_win, v_win, n_win,
     """Decode attention for a batch.
 
     q, q_rot: [B][Hq][d] fp32 (q_rot may be None for head_dim 128: the kernel
-    rotates q itself).  records: uint8 pool [rows][Hkv][tile_bytes];
+    rotates q itself), or [B][w][Hq][d] for a multi-query verify of width
+    w = 2..8 (head_dim 128): row i is the query of window token n_win - w + i
+    and sees the tiles and window tokens [0, n_win - w + i].  records: uint8 pool [rows][Hkv][tile_bytes];
     sequence b's tile j is row rec_start[b] + j.  k_win, v_win: [B][cap][Hkv][d]
     raw windows (strided views allowed, channels contiguous); n_tiles, n_win:
     per-sequence counts (host sequences); win_start: first window row of each

@@ -109,11 +109,25 @@ def test_decode_validation_and_workspace_query(L):
         (dict(n_record_rows=3), 1),                       # tiles beyond the pool
         (dict(q=FAKE + 4), 3), (dict(win_tok_stride=130), 3),
         (dict(head_dim=256, q_rot=None), 1),             # only head_dim 128 rotates in-kernel
+        (dict(q_len=9), 1), (dict(q_len=-1), 1),          # verify width 0..8
+        (dict(q_len=2, n_win=[1], max_win=1), 1),         # the drafts must be in the window
+        (dict(q_len=2, head_dim=256, n_win=[4], max_win=4), 2),   # verify is head_dim 128
     ]
     for over, want in bad:
         b, k2 = _decode_args(**over)
         assert L.kvarn_decode_attention(ctypes.byref(b), ctypes.c_void_p(FAKE), 1 << 30, None) == want, over
         assert L.kvarn_decode_workspace_bytes(ctypes.byref(b)) == 0
+
+
+def test_verify_workspace_grows_with_width(L):
+    a1, k1 = _decode_args(n_win=[8], max_win=8)
+    a4, k4 = _decode_args(n_win=[8], max_win=8, q_len=4)
+    n1 = L.kvarn_decode_workspace_bytes(ctypes.byref(a1))
+    n4 = L.kvarn_decode_workspace_bytes(ctypes.byref(a4))
+    assert n1 > 0 and n4 > n1
+    # the workgroups rotate the verify rows themselves when q_rot is absent
+    a4r, k4r = _decode_args(n_win=[8], max_win=8, q_len=4, q_rot=None)
+    assert L.kvarn_decode_workspace_bytes(ctypes.byref(a4r)) == n4
 
 
 def test_prefill_validation(L):

@@ -319,6 +319,83 @@ def test_prefill_8b_prompt_sampled_rows_and_rechunk_identity():
     assert err < TOL
 
 
+
+# --------------------------------------------------------------------------
+# multi-query verify: q_len rows per sequence, row i sees window [0, n_w - w + i]
+# --------------------------------------------------------------------------
+
+def _verify_batch(seed, B, Hq, Hkv, tiles, wins, w):
+    d = 128
+    recs_all, rec_start, KV = [], [], []
+    cap = max(wins)
+    kw = np.zeros((B, cap, Hkv, d), np.float32)
+    vw = np.zeros((B, cap, Hkv, d), np.float32)
+    row = 0
+    for b in range(B):
+        K, V = synth.make_kv(seed + 7 * b, 128 * tiles[b] + wins[b], Hkv, d, 2)
+        if tiles[b]:
+            recs_all.append(oracle.compress_tiles(K, V, tiles[b]))
+        rec_start.append(row)
+        row += tiles[b]
+        kw[b, :wins[b]] = K[128 * tiles[b]:]
+        vw[b, :wins[b]] = V[128 * tiles[b]:]
+        KV.append((K, V))
+    recs = np.concatenate(recs_all) if recs_all else np.zeros((0, Hkv, kvarn.tile_bytes(d)), np.uint8)
+    q = synth.make_q(seed, B * w, Hq, d).reshape(B, w, Hq, d)
+    return recs, rec_start, kw, vw, KV, q
+
+
+@pytest.mark.parametrize("Hq,Hkv,w,with_rot", [(16, 8, 2, True), (8, 2, 5, False), (16, 2, 8, True),
+                                                (4, 4, 8, False)])
+def test_decode_multi_query_verify_ragged_batch(Hq, Hkv, w, with_rot):
+    say("verify ragged", Hq, Hkv, w, with_rot)
+    d, B = 128, 3
+    tiles = [3, 0, 1]
+    wins = [40, w, 23]   # the second sequence: no tiles and only the drafts
+    recs, rec_start, kw, vw, KV, q = _verify_batch(900 + w, B, Hq, Hkv, tiles, wins, w)
+    scale = 1 / math.sqrt(d)
+    qd = to_dev(q)
+    qr = kvarn.rotate_query(qd) if with_rot else None
+    rd = to_dev(recs) if recs.size else None
+    out = kvarn.decode_attention(qd, qr, rd, rec_start, tiles, to_dev(kw), to_dev(vw), wins, scale)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    for b in range(B):
+        K, V = KV[b]
+        if tiles[b]:
+            kh, vh = oracle.dequant_records(recs[rec_start[b]:rec_start[b] + tiles[b]], d)
+        else:
+            kh = vh = np.zeros((0, Hkv, d))
+        lo = 128 * tiles[b]
+        ref = oracle.verify(q[b], kh, vh, tiles[b], K[lo:], V[lo:], scale)
+        for i in range(w):
+            err = rel_l2(got[b, i], ref[i])
+            assert err < TOL, (b, i, err)
+
+
+def test_decode_multi_query_verify_8b_shape():
+    say("verify 8b 15488 w8")
+    d, Hq, Hkv, W, ctx, w = 128, 32, 8, 256, 15488, 8
+    T = oracle.visible_tiles(ctx - 1, W)
+    K, V = synth.make_kv(4, ctx, Hkv, d, 2)
+    q = synth.make_q(4, w, Hq, d)[None]
+    recs = gpu_compress(K, V, T)
+    kh, vh = oracle.dequant_records(recs, d)
+    n_w = ctx - 128 * T
+    scale = 1 / math.sqrt(d)
+    out = kvarn.decode_attention(to_dev(q), None, to_dev(recs), [0], [T], to_dev(K[128 * T:][None]),
+                                 to_dev(V[128 * T:][None]), [n_w], scale)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()[0]
+    ref = oracle.verify(q[0], kh, vh, T, K[128 * T:], V[128 * T:], scale)
+    err = max(rel_l2(got[i], ref[i]) for i in range(w))
+    say("rel_l2", err)
+    assert err < TOL
+    # the last verify row is the ordinary decode query of the full window
+    one = run_decode(q[0, w - 1:w], recs, [T], K[128 * T:][None], V[128 * T:][None], scale,
+                     rec_start=[0], n_win=[n_w])
+    assert rel_l2(one[0], got[w - 1]) < 2 * TOL
+
 def test_decode_inkernel_rotation_and_workspace_reuse():
     say("decode q_rot=None, reused workspace")
     d, Hq, Hkv, W = 128, 32, 8, 256

@@ -402,3 +402,30 @@ def test_visible_tile_rule_fits_the_workloads():
     assert oracle.visible_tiles(3072 + 256 + 63, 256) == 24
     assert oracle.visible_tiles(3072 + 256 + 127, 256) == 25
     assert oracle.visible_tiles(254, 256) == 0
+
+
+def test_verify_rows_are_prefill_views_and_last_row_is_decode():
+    """gmlx PR #116 commit list (verify widths 2-8 attend the records): row i of
+    a width-w verify over (T tiles, n_w window tokens) is the chunked-prefill
+    output at position 128 T + n_w - w + i under the window rule with
+    W' = n_w - w + 1 (each such row sees exactly T tiles), computed through
+    visible_tiles and raw-token slicing rather than window prefixes; the last
+    row is the ordinary decode query."""
+    d, Hq, Hkv, T, n_w, w = 128, 4, 2, 2, 11, 5
+    K, V = synth.make_kv(61, 128 * T + n_w, Hkv, d, 2)
+    q = synth.make_q(61, w, Hq, d)
+    recs = oracle.compress_tiles(K, V, T)
+    kh, vh = oracle.dequant_records(recs, d)
+    scale = 1 / np.sqrt(d)
+    got = oracle.verify(q, kh, vh, T, K[128 * T:], V[128 * T:], scale)
+    Wp = n_w - w + 1
+    for i in range(w):
+        pos = 128 * T + n_w - w + i
+        assert oracle.visible_tiles(pos, Wp) == T
+        ref = oracle.prefill_row(q[i], pos, Wp, kh, vh, K, V, scale)
+        assert np.allclose(got[i], ref, rtol=0, atol=1e-13)
+    last = oracle.decode(q[w - 1], kh, vh, T, K[128 * T:], V[128 * T:], scale)
+    assert np.array_equal(got[w - 1], last)
+    # an earlier row differs from the full-window decode (it must not see later drafts)
+    full0 = oracle.decode(q[0], kh, vh, T, K[128 * T:], V[128 * T:], scale)
+    assert np.linalg.norm(got[0] - full0) > 1e-6
