@@ -183,6 +183,43 @@ def verify_case(torch, kvarn, synth, ctx, width, reps=20, seed=2):
             "algorithmic_bytes": decode_bytes(T, n_w, Hq, Hkv, d, tb)}
 
 
+def prefill_case(torch, kvarn, synth, SequenceCache, d, Hq, Hkv, n, chunk, reps, W=256):
+    """Chunked prefill of an n-token prompt in one graph: raw row copies, tile
+    compression, query rotation and prefill attention for every chunk."""
+    dev = "cuda:0"
+    Kp, Vp = synth.make_kv(4, n, Hkv, d, synth.outliers_for(d, 0.01))
+    Qp = synth.make_q(4, n, Hq, d)
+    kp, vp, qp = (torch.from_numpy(x).to(dev) for x in (Kp, Vp, Qp))
+    outp = torch.empty_like(qp)
+    cache = SequenceCache(Hkv, d, W, capacity=n + 128, device=dev)
+    ws = None
+    if d != 128:   # the vector-unit prefill keeps split partials in a workspace
+        big = max(kvarn.prefill_workspace_bytes(qp[p0:p0 + min(chunk, n - p0)], qp[p0:p0 + min(chunk, n - p0)],
+                                                cache.records, n // 128, cache.k, cache.v, 0, p0, W, 1.0)
+                  for p0 in range(0, n, chunk))
+        ws = torch.zeros(max(big, 16), dtype=torch.uint8, device=dev)
+
+    def run_prefill():
+        cache.n_tokens = cache.n_tiles = 0
+        for p0 in range(0, n, chunk):
+            c = min(chunk, n - p0)
+            cache.append(kp[p0:p0 + c], vp[p0:p0 + c])
+            q_c = qp[p0:p0 + c]
+            q_r = kvarn.rotate_query(q_c)
+            rb = 128 * kvarn.visible_tiles(p0, W)
+            kvarn.prefill_attention(q_c, q_r, cache.records, cache.n_tiles, cache.k[rb:],
+                                    cache.v[rb:], rb, p0, W, 1.0 / math.sqrt(d), out=outp[p0:p0 + c],
+                                    workspace=ws)
+
+    ms_p, _ = graph_ms(torch, run_prefill, 1, reps)
+    pairs = n * (n + 1) // 2                            # causal (query, key) pairs per head
+    ops = 2 * 2 * d * pairs * Hq                         # Q.K and P.V multiply-adds as 2 ops each
+    return {"head_dim": d, "n_q_heads": Hq, "n_kv_heads": Hkv, "tokens_per_s": n / (ms_p * 1e-3),
+            "ms": ms_p, "prompt": n, "chunk": chunk, "algorithmic_TOPS": ops / (ms_p * 1e-3) / 1e12,
+            "int8_mfma_frac": ops / (ms_p * 1e-3) / 1e12 / INT8_MFMA_PEAK_TOPS,
+            "includes": "raw row copies, tile compression, query rotation, prefill attention"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -238,33 +275,14 @@ def main():
 
     # ---- chunked prefill of the 15488-token prompt (one graph of all chunks) ----
     prefill = None
+    prefill_wide = []
     if not args.no_prefill:
-        n, chunk = 15488, 512
-        Kp, Vp = synth.make_kv(4, n, Hkv, d, synth.outliers_for(d, 0.01))
-        Qp = synth.make_q(4, n, Hq, d)
-        kp, vp, qp = (torch.from_numpy(x).to(dev) for x in (Kp, Vp, Qp))
-        outp = torch.empty_like(qp)
-        cache = SequenceCache(Hkv, d, W, capacity=n + 128, device=dev)
-
-        def run_prefill():
-            cache.n_tokens = cache.n_tiles = 0
-            for p0 in range(0, n, chunk):
-                c = min(chunk, n - p0)
-                cache.append(kp[p0:p0 + c], vp[p0:p0 + c])
-                q_c = qp[p0:p0 + c]
-                q_r = kvarn.rotate_query(q_c)
-                rb = 128 * kvarn.visible_tiles(p0, W)
-                kvarn.prefill_attention(q_c, q_r, cache.records, cache.n_tiles, cache.k[rb:],
-                                        cache.v[rb:], rb, p0, W, 1.0 / math.sqrt(d), out=outp[p0:p0 + c])
-
-        ms_p, _ = graph_ms(torch, run_prefill, 1, 3)
-        pairs = n * (n + 1) // 2                            # causal (query, key) pairs per head
-        ops = 2 * 2 * d * pairs * Hq                         # Q.K and P.V multiply-adds as 2 ops each
-        prefill = {"tokens_per_s": n / (ms_p * 1e-3), "ms": ms_p, "prompt": n, "chunk": chunk,
-                   "algorithmic_TOPS": ops / (ms_p * 1e-3) / 1e12,
-                   "int8_mfma_frac": ops / (ms_p * 1e-3) / 1e12 / INT8_MFMA_PEAK_TOPS,
-                   "includes": "raw row copies, tile compression, query rotation, prefill attention"}
-        log(f"prefill {n} tokens: {ms_p:.2f} ms")
+        prefill = prefill_case(torch, kvarn, synth, SequenceCache, 128, Hq, Hkv, 15488, 512, 3)
+        log(f"prefill {prefill['prompt']} tokens: {prefill['ms']:.2f} ms")
+        for dw, hq, hkv in ((256, 16, 4), (512, 8, 1)):
+            info = prefill_case(torch, kvarn, synth, SequenceCache, dw, hq, hkv, 4096, 512, 2)
+            prefill_wide.append(info)
+            log(f"prefill head_dim {dw}, {info['prompt']} tokens: {info['ms']:.2f} ms")
 
     if args.calibration_copy:
         src = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
@@ -326,6 +344,7 @@ def main():
         "hbm_GBps": achieved,
         "decode_contexts": [head] + extra,
         "prefill": prefill,
+        "prefill_wide_heads": prefill_wide,
         "verify": verify,
         "compress": compress,
         "cpu_baseline": cpu,

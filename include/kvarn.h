@@ -187,9 +187,13 @@ int kvarn_decode_attention(const kvarn_decode_args* args, void* workspace,
  * [128*T(p), p] (the decode view at p, so the output does not depend on how
  * the prompt is chunked).  The caller compresses every tile the chunk makes
  * due (tiles < T(pos0+C-1)) before this call.
+ *
+ * head_dim 128 runs on the matrix units; head_dim 256 and 512 (issue #433
+ * item 3: prefill at the wider heads) run every chunk row as a vector-unit
+ * split decode query with that view and need a workspace for the partials.
  */
 typedef struct kvarn_prefill_args {
-  int32_t head_dim;        /* 128 (256/512 return KVARN_E_UNSUPPORTED)          */
+  int32_t head_dim;        /* 128, 256 or 512                                   */
   int32_t n_q_heads;
   int32_t n_kv_heads;
   int32_t window;          /* W of the promotion rule, >= 0                     */
@@ -208,12 +212,16 @@ typedef struct kvarn_prefill_args {
   float* out;              /* device [C][n_q_heads][head_dim]                   */
 } kvarn_prefill_args;
 
-/* Workspace bytes kvarn_prefill_attention needs: 0 (every partial result
- * stays in registers and LDS); workspace may be NULL. */
+/* Workspace bytes kvarn_prefill_attention needs (0 on invalid arguments):
+ * 0 at head_dim 128 (every partial result stays in registers and LDS; the
+ * workspace may be NULL), the split partials at 256 and 512.  Device memory
+ * owned by the caller, scratch after the call; calls sharing a workspace
+ * must not overlap in time. */
 size_t kvarn_prefill_workspace_bytes(const kvarn_prefill_args* args);
 
 /* Errors: KVARN_E_INVALID (null pointers, chunk < 1, pos0 < 0, missing tiles
- * or raw rows), KVARN_E_UNSUPPORTED, KVARN_E_ALIGN.  The raw rows
+ * or raw rows), KVARN_E_UNSUPPORTED (head_dim, GQA ratio), KVARN_E_ALIGN,
+ * KVARN_E_WORKSPACE (head_dim 256/512 only).  The raw rows
  * [raw_base, pos0 + C) must be readable. */
 int kvarn_prefill_attention(const kvarn_prefill_args* args, void* workspace,
                             size_t workspace_bytes, void* stream);

@@ -144,7 +144,7 @@ int64_t prefill_tiles_at(int64_t pos, int window) {
 
 int validate_prefill(const kvarn_prefill_args* a, DecodePlan* plan) {
   if (!a) return KVARN_E_INVALID;
-  if (a->head_dim != 128) return dim_ok(a->head_dim) ? KVARN_E_UNSUPPORTED : KVARN_E_UNSUPPORTED;
+  if (!dim_ok(a->head_dim)) return KVARN_E_UNSUPPORTED;
   if (a->n_q_heads < 1 || a->n_kv_heads < 1 || a->chunk < 1 || a->pos0 < 0 || a->window < 0)
     return KVARN_E_INVALID;
   if (a->n_q_heads % a->n_kv_heads != 0) return KVARN_E_UNSUPPORTED;
@@ -274,17 +274,52 @@ int kvarn_decode_attention(const kvarn_decode_args* a, void* workspace, size_t w
   return e == hipSuccess ? KVARN_OK : KVARN_E_DEVICE;
 }
 
+// head_dim 128: the matrix-core prefill keeps its whole state on chip.
+// head_dim 256 / 512: the vector-unit split kernels run every chunk row as a
+// decode query with the prefill view (T(p) tiles, raw rows [128 T(p), p]) and
+// need their partials in the workspace.
 size_t kvarn_prefill_workspace_bytes(const kvarn_prefill_args* a) {
-  (void)a;
-  return 0;   // the matrix-core prefill keeps all of its state on chip
+  DecodePlan p;
+  if (validate_prefill(a, &p) != KVARN_OK) return 0;
+  if (a->head_dim == 128) return 0;
+  return decode_part_floats(a->chunk, a->n_q_heads, a->head_dim, p) * sizeof(float);
 }
 
 int kvarn_prefill_attention(const kvarn_prefill_args* a, void* workspace, size_t ws_bytes,
                             void* stream) {
-  (void)workspace;
-  (void)ws_bytes;
-  int st = validate_prefill(a, nullptr);
+  DecodePlan plan;
+  int st = validate_prefill(a, &plan);
   if (st != KVARN_OK) return st;
+  if (a->head_dim != 128) {
+    const size_t need = decode_part_floats(a->chunk, a->n_q_heads, a->head_dim, plan) * sizeof(float);
+    if (!workspace || ws_bytes < need) return KVARN_E_WORKSPACE;
+    if (!al16(workspace)) return KVARN_E_ALIGN;
+    kvarn::DecodeParams P;
+    memset(&P, 0, sizeof(P));
+    P.q = a->q;
+    P.q_rot = a->q_rot;
+    P.records = static_cast<const uint8_t*>(a->records);
+    P.k_win = a->k;
+    P.v_win = a->v;
+    P.part = static_cast<float*>(workspace);
+    P.out = a->out;
+    P.win_tok_stride = a->tok_stride;
+    P.win_head_stride = a->head_stride;
+    P.scale = a->softmax_scale;
+    P.n_q = a->n_q_heads;
+    P.n_kv = a->n_kv_heads;
+    P.G = a->n_q_heads / a->n_kv_heads;
+    P.tps = plan.tps;
+    P.n_tsplit = plan.n_tsplit;
+    P.n_wsplit = plan.n_wsplit;
+    P.wchunk = plan.wchunk;
+    P.mode = 1;
+    P.window = a->window;
+    P.pos0 = a->pos0;
+    P.raw_base = a->raw_base;
+    hipError_t e = kvarn::launch_decode(a->head_dim, P, a->chunk, (hipStream_t)stream);
+    return e == hipSuccess ? KVARN_OK : KVARN_E_DEVICE;
+  }
   kvarn::PrefillParams P;
   memset(&P, 0, sizeof(P));
   P.q = a->q;

@@ -214,6 +214,13 @@ def _prefill_args(q, q_rot, records, n_record_rows, k, v, raw_base, pos0, window
     return a
 
 
+def prefill_workspace_bytes(q, q_rot, records, n_record_rows, k, v, raw_base, pos0, window,
+                            scale) -> int:
+    """Workspace bytes of a prefill_attention call with these arguments."""
+    a = _prefill_args(q, q_rot, records, n_record_rows, k, v, raw_base, pos0, window, scale, q)
+    return int(lib().kvarn_prefill_workspace_bytes(ctypes.byref(a)))
+
+
 def prefill_attention(q, q_rot, records, n_record_rows, k, v, raw_base, pos0, window, scale,
                       out=None, workspace=None, stream=None):
     """Chunk of C query positions [pos0, pos0+C) of one sequence.

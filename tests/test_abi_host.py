@@ -146,7 +146,13 @@ def test_prefill_validation(L):
     a = args()
     # the matrix-core prefill keeps its whole state on chip
     assert L.kvarn_prefill_workspace_bytes(ctypes.byref(a)) == 0
-    bad = [(dict(head_dim=256), 2), (dict(chunk=0), 1), (dict(pos0=-1), 1),
+    # the vector-unit prefill at head_dim 256 keeps split partials in the workspace
+    a256 = args(head_dim=256, tok_stride=256 * 2, head_stride=256)
+    need = L.kvarn_prefill_workspace_bytes(ctypes.byref(a256))
+    assert need > 0
+    assert L.kvarn_prefill_attention(ctypes.byref(a256), ctypes.c_void_p(FAKE), need - 16, None) == 4
+    assert L.kvarn_prefill_attention(ctypes.byref(a256), None, need, None) == 4
+    bad = [(dict(head_dim=384), 2), (dict(chunk=0), 1), (dict(pos0=-1), 1),
            (dict(n_record_rows=3), 1), (dict(raw_base=384), 1), (dict(k=FAKE + 4), 3),
            (dict(tok_stride=258), 3), (dict(n_q_heads=6), 2)]
     for over, want in bad:

@@ -298,6 +298,25 @@ def test_prefill_small_prompt_every_row():
     assert rel_l2(out, ref) < TOL
 
 
+
+@pytest.mark.parametrize("d,Hq,Hkv", [(256, 16, 4), (512, 8, 1)])
+def test_prefill_wide_heads_every_row_and_rechunk(d, Hq, Hkv):
+    say("prefill wide", d)
+    W, n = 256, 700
+    K, V = synth.make_kv(40 + d, n, Hkv, d, 4)
+    Q = synth.make_q(40 + d, n, Hq, d)
+    out, recs = prefill_run(K, V, Q, W, 256, Hkv, d)
+    assert np.array_equal(recs, oracle.compress_tiles(K, V, recs.shape[0]))
+    kh, vh = oracle.dequant_records(recs, d)
+    ref = np.stack([oracle.prefill_row(Q[p], p, W, kh, vh, K, V, 1 / math.sqrt(d)) for p in range(n)])
+    err = rel_l2(out, ref)
+    say("rel_l2", err)
+    assert err < TOL
+    # another chunking: the same tiles, rows within the split-plan rounding of each other
+    out2, recs2 = prefill_run(K, V, Q, W, 128, Hkv, d)
+    assert np.array_equal(recs2, recs)
+    assert rel_l2(out2, out) < 1e-5
+
 def test_prefill_8b_prompt_sampled_rows_and_rechunk_identity():
     say("prefill 8b")
     d, Hq, Hkv, W = 128, 32, 8, 256
