@@ -51,7 +51,14 @@ def _load():
     u8p = ctypes.POINTER(ctypes.c_uint8)
     lib.oracle_tile_bytes.restype = ctypes.c_longlong
     lib.oracle_tile_bytes.argtypes = [ctypes.c_int]
+    lib.oracle_tile_bytes_fmt.restype = ctypes.c_longlong
+    lib.oracle_tile_bytes_fmt.argtypes = [ctypes.c_int, ctypes.c_int]
     lib.oracle_layout.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_longlong)]
+    lib.oracle_layout_fmt.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_longlong)]
+    lib.oracle_f32_to_f16.restype = ctypes.c_uint16
+    lib.oracle_f32_to_f16.argtypes = [ctypes.c_float]
+    lib.oracle_f16_to_f32.restype = ctypes.c_float
+    lib.oracle_f16_to_f32.argtypes = [ctypes.c_uint16]
     lib.oracle_wht_scale.restype = ctypes.c_float
     lib.oracle_wht_scale.argtypes = [ctypes.c_int]
     lib.oracle_wht_f32.argtypes = [f32p, ctypes.c_int]
@@ -64,8 +71,12 @@ def _load():
     lib.oracle_compress_tile.restype = ctypes.c_int
     lib.oracle_compress_tile.argtypes = [f32p, f32p, ctypes.c_longlong, ctypes.c_int,
                                          ctypes.c_int, u8p]
+    lib.oracle_compress_tile_fmt.restype = ctypes.c_int
+    lib.oracle_compress_tile_fmt.argtypes = [f32p, f32p, ctypes.c_longlong, ctypes.c_int,
+                                             ctypes.c_int, ctypes.c_int, u8p]
     lib.oracle_unpack_codes.argtypes = [u8p, ctypes.c_int, u8p, u8p]
     lib.oracle_dequant_f64.argtypes = [u8p, ctypes.c_int, ctypes.c_int, f64p, f64p]
+    lib.oracle_dequant_f64_fmt.argtypes = [u8p, ctypes.c_int, ctypes.c_int, ctypes.c_int, f64p, f64p]
     lib.oracle_attend_f64.argtypes = [f64p, f64p, f64p, ctypes.c_longlong, ctypes.c_int,
                                       ctypes.c_double, f64p, f64p]
     _lib = lib
@@ -80,17 +91,28 @@ def _p(a, ct):
 # sizes and layout
 # --------------------------------------------------------------------------
 
-def tile_bytes(d: int) -> int:
-    """Bytes of one (tile, kv-head) record: 116*d + 512 (0 if d unsupported)."""
-    return int(_load().oracle_tile_bytes(d))
+def tile_bytes(d: int, f16: bool = False) -> int:
+    """Bytes of one (tile, kv-head) record: 116*d + 512 with fp32 scales, or
+    106*d + 256 with f16 scales (SharpInference issue #433 item 3); 0 if d is
+    unsupported."""
+    return int(_load().oracle_tile_bytes_fmt(d, 1 if f16 else 0))
 
 
-def layout(d: int) -> dict:
+def layout(d: int, f16: bool = False) -> dict:
     """Byte offsets of the record sections."""
     off = (ctypes.c_longlong * 9)()
-    _load().oracle_layout(d, off)
+    _load().oracle_layout_fmt(d, 1 if f16 else 0, off)
     names = ["kcode", "vcode", "ktok", "kscale", "kmin", "vchan", "vscale", "vmin", "end"]
     return dict(zip(names, [int(x) for x in off]))
+
+
+def f32_to_f16_bits(x: float) -> int:
+    """The oracle's binary32 -> binary16 rounding (nearest, ties to even)."""
+    return int(_load().oracle_f32_to_f16(float(np.float32(x))))
+
+
+def f16_bits_to_f32(h: int) -> float:
+    return float(_load().oracle_f16_to_f32(int(h)))
 
 
 def visible_tiles(pos: int, window: int) -> int:
@@ -167,28 +189,33 @@ def rtn_group(x: np.ndarray, bits: int):
 # compression
 # --------------------------------------------------------------------------
 
-def compress_tile(k_tile: np.ndarray, v_tile: np.ndarray, iters: int = 8) -> np.ndarray:
-    """One (tile, kv head): raw fp32 K and V tiles [128][d] -> record bytes."""
+def compress_tile(k_tile: np.ndarray, v_tile: np.ndarray, iters: int = 8,
+                  f16: bool = False) -> np.ndarray:
+    """One (tile, kv head): raw fp32 K and V tiles [128][d] -> record bytes.
+    With f16 the six scale vectors are stored rounded to half precision
+    (nearest, ties to even); the codes are those of the fp32 record."""
     k = np.ascontiguousarray(k_tile, dtype=np.float32)
     v = np.ascontiguousarray(v_tile, dtype=np.float32)
     assert k.shape == v.shape and k.shape[0] == TILE
     d = k.shape[1]
-    rec = np.zeros(tile_bytes(d), np.uint8)
-    rc = _load().oracle_compress_tile(_p(k, ctypes.c_float), _p(v, ctypes.c_float), d, d,
-                                      iters, _p(rec, ctypes.c_uint8))
+    rec = np.zeros(tile_bytes(d, f16), np.uint8)
+    rc = _load().oracle_compress_tile_fmt(_p(k, ctypes.c_float), _p(v, ctypes.c_float), d, d,
+                                          iters, 1 if f16 else 0, _p(rec, ctypes.c_uint8))
     if rc != 0:
         raise ValueError(f"unsupported head_dim {d}")
     return rec
 
 
-def compress_tiles(K: np.ndarray, V: np.ndarray, n_tiles: int, iters: int = 8) -> np.ndarray:
+def compress_tiles(K: np.ndarray, V: np.ndarray, n_tiles: int, iters: int = 8,
+                   f16: bool = False) -> np.ndarray:
     """K, V: [n_tokens][n_kv][d] raw fp32.  Returns records [n_tiles][n_kv][bytes]
     for the first n_tiles whole tiles."""
     n_kv, d = K.shape[1], K.shape[2]
-    out = np.zeros((n_tiles, n_kv, tile_bytes(d)), np.uint8)
+    out = np.zeros((n_tiles, n_kv, tile_bytes(d, f16)), np.uint8)
     for j in range(n_tiles):
         for h in range(n_kv):
-            out[j, h] = compress_tile(K[TILE * j:TILE * (j + 1), h], V[TILE * j:TILE * (j + 1), h], iters)
+            out[j, h] = compress_tile(K[TILE * j:TILE * (j + 1), h], V[TILE * j:TILE * (j + 1), h],
+                                      iters, f16)
     return out
 
 
@@ -201,18 +228,19 @@ def unpack_codes(rec: np.ndarray, d: int):
     return zK, zV
 
 
-def record_scales(rec: np.ndarray, d: int) -> dict:
-    """The six fp32 scale vectors of a record, as numpy views."""
-    off = layout(d)
+def record_scales(rec: np.ndarray, d: int, f16: bool = False) -> dict:
+    """The six scale vectors of a record as fp32 numpy arrays."""
+    off = layout(d, f16)
     rec = np.ascontiguousarray(rec, dtype=np.uint8)
     ng = d // 128
+    w, dt = (2, np.float16) if f16 else (4, np.float32)
 
-    def f32(a, n):
-        return rec[off[a]:off[a] + 4 * n].view(np.float32)
+    def get(a, n):
+        return rec[off[a]:off[a] + w * n].view(dt).astype(np.float32)
     return {
-        "ktok": f32("ktok", TILE), "kscale": f32("kscale", d), "kmin": f32("kmin", d),
-        "vchan": f32("vchan", d), "vscale": f32("vscale", TILE * ng).reshape(TILE, ng),
-        "vmin": f32("vmin", TILE * ng).reshape(TILE, ng),
+        "ktok": get("ktok", TILE), "kscale": get("kscale", d), "kmin": get("kmin", d),
+        "vchan": get("vchan", d), "vscale": get("vscale", TILE * ng).reshape(TILE, ng),
+        "vmin": get("vmin", TILE * ng).reshape(TILE, ng),
     }
 
 
@@ -231,25 +259,25 @@ def hadamard_f64(d: int) -> np.ndarray:
     return np.where(parity == 1, -1.0, 1.0) / np.sqrt(d)
 
 
-def dequant_rotated(rec: np.ndarray, d: int):
+def dequant_rotated(rec: np.ndarray, d: int, f16: bool = False):
     """k'[t][c], v'[t][c] in the rotated domain (fp64), from the stored codes
     and folded scales."""
     rec = np.ascontiguousarray(rec, dtype=np.uint8)
     kd = np.zeros((TILE, d), np.float64)
     vd = np.zeros((TILE, d), np.float64)
-    _load().oracle_dequant_f64(_p(rec, ctypes.c_uint8), d, 1, _p(kd, ctypes.c_double),
-                               _p(vd, ctypes.c_double))
+    _load().oracle_dequant_f64_fmt(_p(rec, ctypes.c_uint8), d, 1 if f16 else 0, 1,
+                                   _p(kd, ctypes.c_double), _p(vd, ctypes.c_double))
     return kd, vd
 
 
-def dequant(rec: np.ndarray, d: int):
+def dequant(rec: np.ndarray, d: int, f16: bool = False):
     """khat = H k', vhat = H v' (fp64, raw domain)."""
-    kd, vd = dequant_rotated(rec, d)
+    kd, vd = dequant_rotated(rec, d, f16)
     H = hadamard_f64(d)
     return kd @ H.T, vd @ H.T
 
 
-def dequant_records(records: np.ndarray, d: int):
+def dequant_records(records: np.ndarray, d: int, f16: bool = False):
     """records [T][n_kv][bytes] -> khat, vhat [T*128][n_kv][d] fp64."""
     T, n_kv = records.shape[0], records.shape[1]
     kh = np.zeros((T * TILE, n_kv, d))
@@ -257,7 +285,7 @@ def dequant_records(records: np.ndarray, d: int):
     H = hadamard_f64(d)
     for j in range(T):
         for h in range(n_kv):
-            kd, vd = dequant_rotated(records[j, h], d)
+            kd, vd = dequant_rotated(records[j, h], d, f16)
             kh[TILE * j:TILE * (j + 1), h] = kd @ H.T
             vh[TILE * j:TILE * (j + 1), h] = vd @ H.T
     return kh, vh

@@ -54,25 +54,70 @@
 
 static int valid_dim(int d) { return d == 128 || d == 256 || d == 512; }
 
-long long oracle_tile_bytes(int d) {
-  if (!valid_dim(d)) return 0;
-  return 116LL * d + 512;
+/* Scale formats of the record: 0 = fp32 scales (116 d + 512 bytes), 1 = f16
+ * scales, each fp32 scale rounded to nearest-even half precision (SharpInference
+ * issue #433 item 3, "f16 scales": 106 d + 256 bytes, 108 B per token per KV
+ * head at d = 128).  The codes are the same in both formats. */
+long long oracle_tile_bytes_fmt(int d, int fmt) {
+  if (!valid_dim(d) || (fmt != 0 && fmt != 1)) return 0;
+  return fmt ? 106LL * d + 256 : 116LL * d + 512;
 }
+long long oracle_tile_bytes(int d) { return oracle_tile_bytes_fmt(d, 0); }
 
 /* offsets: K codes, V codes, ktok, kscale, kmin, vchan, vscale, vmin, end */
-static void layout(int d, long long off[9]) {
+static void layout_fmt(int d, int fmt, long long off[9]) {
+  const long long w = fmt ? 2 : 4;   /* bytes per scale */
   off[0] = 0;                 /* K codes  uint8[d][64]         */
   off[1] = 64LL * d;          /* V codes  uint8[128][d/4]      */
-  off[2] = 96LL * d;          /* ktok     f32[128]             */
-  off[3] = 96LL * d + 512;    /* kscale   f32[d]               */
-  off[4] = 100LL * d + 512;   /* kmin     f32[d]               */
-  off[5] = 104LL * d + 512;   /* vchan    f32[d]               */
-  off[6] = 108LL * d + 512;   /* vscale   f32[128][d/128]      */
-  off[7] = 112LL * d + 512;   /* vmin     f32[128][d/128]      */
-  off[8] = 116LL * d + 512;   /* end                           */
+  off[2] = 96LL * d;          /* ktok     [128]                */
+  off[3] = off[2] + 128 * w;  /* kscale   [d]                  */
+  off[4] = off[3] + d * w;    /* kmin     [d]                  */
+  off[5] = off[4] + d * w;    /* vchan    [d]                  */
+  off[6] = off[5] + d * w;    /* vscale   [128][d/128]         */
+  off[7] = off[6] + d * w;    /* vmin     [128][d/128]         */
+  off[8] = off[7] + d * w;    /* end                           */
 }
+static void layout(int d, long long off[9]) { layout_fmt(d, 0, off); }
 
 void oracle_layout(int d, long long* off) { layout(d, off); }
+void oracle_layout_fmt(int d, int fmt, long long* off) { layout_fmt(d, fmt, off); }
+
+/* IEEE binary32 -> binary16 bits, round to nearest, ties to even (overflow
+ * to infinity, NaN stays NaN), and back (exact). */
+static uint32_t rshift_rne(uint32_t x, int s) {
+  if (s <= 0) return x;
+  if (s >= 32) return 0;
+  const uint32_t q = x >> s, rem = x & ((1u << s) - 1), half = 1u << (s - 1);
+  return q + ((rem > half || (rem == half && (q & 1))) ? 1u : 0u);
+}
+uint16_t oracle_f32_to_f16(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  const uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+  const int e = (int)((u >> 23) & 0xff);
+  const uint32_t m = u & 0x7fffffu;
+  if (e == 255) return (uint16_t)(sign | 0x7c00u | (m ? 0x200u : 0u));
+  const int E = e - 127 + 15;
+  if (E >= 31) return (uint16_t)(sign | 0x7c00u);
+  if (E <= 0) {   /* subnormal half (or zero): value = M 2^-24 */
+    if (e == 0) return sign;   /* fp32 zero or subnormal: far below half's range */
+    const uint32_t M = rshift_rne(m | 0x800000u, 14 - E);
+    return (uint16_t)(sign | M);   /* M = 0x400 is the smallest normal: still correct bits */
+  }
+  uint32_t mh = rshift_rne(m, 13);
+  uint32_t eh = (uint32_t)E;
+  if (mh == 0x400u) { mh = 0; eh += 1; }
+  if (eh >= 31) return (uint16_t)(sign | 0x7c00u);
+  return (uint16_t)(sign | (eh << 10) | mh);
+}
+float oracle_f16_to_f32(uint16_t h) {
+  const int e = (h >> 10) & 31, m = h & 1023;
+  float v;
+  if (e == 0) v = ldexpf((float)m, -24);
+  else if (e == 31) v = m ? NAN : INFINITY;
+  else v = ldexpf((float)(1024 + m), e - 25);
+  return (h & 0x8000) ? -v : v;
+}
 
 /* ------------------------------------------------------------------ */
 /* Walsh-Hadamard transform (fp32, fixed order)                         */
@@ -241,22 +286,28 @@ static void compress_one(const float* src, long long tok_stride, int d, int iter
   free(Xn);
 }
 
-static void put_f32(uint8_t* rec, long long off, int i, float v) {
-  memcpy(rec + off + 4LL * i, &v, 4);
+static void put_scale(uint8_t* rec, long long off, int i, float v, int fmt) {
+  if (fmt) {
+    const uint16_t h = oracle_f32_to_f16(v);
+    memcpy(rec + off + 2LL * i, &h, 2);
+  } else {
+    memcpy(rec + off + 4LL * i, &v, 4);
+  }
 }
 
 /* Compress the K and V tiles of one (tile, kv head).  k and v point at token
- * 0 channel 0; token t starts tok_stride floats later.  Writes 116*d+512
- * bytes to rec.  Returns 0 on success, -1 for an unsupported head_dim. */
-int oracle_compress_tile(const float* k, const float* v, long long tok_stride,
-                         int d, int iters, uint8_t* rec) {
-  if (!valid_dim(d)) return -1;
+ * 0 channel 0; token t starts tok_stride floats later.  Writes
+ * oracle_tile_bytes_fmt(d, fmt) bytes to rec.  Returns 0 on success, -1 for
+ * an unsupported head_dim or format. */
+int oracle_compress_tile_fmt(const float* k, const float* v, long long tok_stride,
+                             int d, int iters, int fmt, uint8_t* rec) {
+  if (!valid_dim(d) || (fmt != 0 && fmt != 1)) return -1;
   tile_parts* P = (tile_parts*)calloc(1, sizeof(tile_parts));
   compress_one(k, tok_stride, d, iters, P->rK, P->sK, P->zK, P->loK, P->dK, 1);
   compress_one(v, tok_stride, d, iters, P->rV, P->sV, P->zV, P->loV, P->dV, 0);
 
   long long off[9];
-  layout(d, off);
+  layout_fmt(d, fmt, off);
   memset(rec, 0, (size_t)off[8]);
   /* K codes, channel-major: byte j of channel c = tokens 2j (low), 2j+1 (high) */
   for (int c = 0; c < d; c++)
@@ -271,20 +322,25 @@ int oracle_compress_tile(const float* k, const float* v, long long tok_stride,
       rec[off[1] + (long long)t * (d / 4) + j] = (uint8_t)b;
     }
   /* folded scales: single fp32 multiplies */
-  for (int t = 0; t < TILE; t++) put_f32(rec, off[2], t, P->rK[t]);
+  for (int t = 0; t < TILE; t++) put_scale(rec, off[2], t, P->rK[t], fmt);
   for (int c = 0; c < d; c++) {
-    put_f32(rec, off[3], c, P->dK[c] * P->sK[c]);
-    put_f32(rec, off[4], c, P->loK[c] * P->sK[c]);
-    put_f32(rec, off[5], c, P->sV[c]);
+    put_scale(rec, off[3], c, P->dK[c] * P->sK[c], fmt);
+    put_scale(rec, off[4], c, P->loK[c] * P->sK[c], fmt);
+    put_scale(rec, off[5], c, P->sV[c], fmt);
   }
   int ng = d / 128;
   for (int t = 0; t < TILE; t++)
     for (int g = 0; g < ng; g++) {
-      put_f32(rec, off[6], t * ng + g, P->dV[t * ng + g] * P->rV[t]);
-      put_f32(rec, off[7], t * ng + g, P->loV[t * ng + g] * P->rV[t]);
+      put_scale(rec, off[6], t * ng + g, P->dV[t * ng + g] * P->rV[t], fmt);
+      put_scale(rec, off[7], t * ng + g, P->loV[t * ng + g] * P->rV[t], fmt);
     }
   free(P);
   return 0;
+}
+
+int oracle_compress_tile(const float* k, const float* v, long long tok_stride,
+                         int d, int iters, uint8_t* rec) {
+  return oracle_compress_tile_fmt(k, v, tok_stride, d, iters, 0, rec);
 }
 
 /* The unpacked codes of a record: zK[t][c] and zV[t][c]. */
@@ -308,11 +364,17 @@ void oracle_unpack_codes(const uint8_t* rec, int d, uint8_t* zK, uint8_t* zV) {
 /* Dequantised cache in fp64                                            */
 /* ------------------------------------------------------------------ */
 
-static double get_f32(const uint8_t* rec, long long off, int i) {
+static double get_scale(const uint8_t* rec, long long off, int i, int fmt) {
+  if (fmt) {
+    uint16_t h;
+    memcpy(&h, rec + off + 2LL * i, 2);
+    return (double)oracle_f16_to_f32(h);
+  }
   float v;
   memcpy(&v, rec + off + 4LL * i, 4);
   return (double)v;
 }
+
 
 /* H[i][j] = (-1)^popcount(i & j) / sqrt(d), applied to one fp64 row. */
 static void hadamard_f64(const double* x, double* y, int d) {
@@ -332,32 +394,36 @@ static void hadamard_f64(const double* x, double* y, int d) {
  *   v'[t][c] = vchan[c] * (zV[t][c] * vscale[t][g] + vmin[t][g])
  *   khat = H k', vhat = H v'  (H is its own inverse)
  * If rotated_only is nonzero the rotation is skipped (k', v' are returned). */
-void oracle_dequant_f64(const uint8_t* rec, int d, int rotated_only,
-                        double* khat, double* vhat) {
+void oracle_dequant_f64_fmt(const uint8_t* rec, int d, int fmt, int rotated_only,
+                            double* khat, double* vhat) {
   long long off[9];
-  layout(d, off);
+  layout_fmt(d, fmt, off);
   uint8_t* zK = (uint8_t*)malloc((size_t)TILE * d);
   uint8_t* zV = (uint8_t*)malloc((size_t)TILE * d);
   double* row = (double*)malloc(sizeof(double) * d);
   oracle_unpack_codes(rec, d, zK, zV);
   int ng = d / 128;
   for (int t = 0; t < TILE; t++) {
-    double ktok = get_f32(rec, off[2], t);
+    double ktok = get_scale(rec, off[2], t, fmt);
     for (int c = 0; c < d; c++)
-      row[c] = ktok * ((double)zK[t * d + c] * get_f32(rec, off[3], c) +
-                       get_f32(rec, off[4], c));
+      row[c] = ktok * ((double)zK[t * d + c] * get_scale(rec, off[3], c, fmt) +
+                       get_scale(rec, off[4], c, fmt));
     if (rotated_only) memcpy(khat + (long long)t * d, row, sizeof(double) * d);
     else hadamard_f64(row, khat + (long long)t * d, d);
     for (int c = 0; c < d; c++) {
       int g = c / 128;
-      row[c] = get_f32(rec, off[5], c) *
-               ((double)zV[t * d + c] * get_f32(rec, off[6], t * ng + g) +
-                get_f32(rec, off[7], t * ng + g));
+      row[c] = get_scale(rec, off[5], c, fmt) *
+               ((double)zV[t * d + c] * get_scale(rec, off[6], t * ng + g, fmt) +
+                get_scale(rec, off[7], t * ng + g, fmt));
     }
     if (rotated_only) memcpy(vhat + (long long)t * d, row, sizeof(double) * d);
     else hadamard_f64(row, vhat + (long long)t * d, d);
   }
   free(zK); free(zV); free(row);
+}
+
+void oracle_dequant_f64(const uint8_t* rec, int d, int rotated_only, double* khat, double* vhat) {
+  oracle_dequant_f64_fmt(rec, d, 0, rotated_only, khat, vhat);
 }
 
 /* ------------------------------------------------------------------ */

@@ -429,3 +429,61 @@ def test_verify_rows_are_prefill_views_and_last_row_is_decode():
     # an earlier row differs from the full-window decode (it must not see later drafts)
     full0 = oracle.decode(q[0], kh, vh, T, K[128 * T:], V[128 * T:], scale)
     assert np.linalg.norm(got[0] - full0) > 1e-6
+
+
+# --------------------------------------------------------------------------
+# f16 scales in the record (SharpInference issue #433 item 3)
+# --------------------------------------------------------------------------
+
+def test_f16_rounding_matches_numpy_half_conversion():
+    """The oracle's binary32 -> binary16 conversion is IEEE round-to-nearest-even:
+    numpy's float16 cast is the library reference, on edge values and on random
+    values from subnormal to overflow range."""
+    edge = [0.0, -0.0, 1.0, -1.0, 65504.0, 65519.99, 65520.0, 1e9, -1e9, 2.0 ** -24, 2.0 ** -25,
+            3 * 2.0 ** -26, 2.0 ** -14, 2.0 ** -14 * (1 - 2.0 ** -11), 6.1e-5, 1.0 + 2.0 ** -11,
+            1.0 + 3 * 2.0 ** -11, 2049.0, 2051.0, 1e-30, float("inf"), -float("inf")]
+    rng = np.random.default_rng(5)
+    rand = (rng.standard_normal(20000) * np.exp2(rng.uniform(-30, 18, 20000))).astype(np.float32)
+    for x in list(np.float32(edge)) + list(rand):
+        want = int(np.array([x], np.float32).astype(np.float16).view(np.uint16)[0])
+        assert oracle.f32_to_f16_bits(x) == want, (x, hex(want))
+        assert oracle.f16_bits_to_f32(want) == float(np.array([want], np.uint16).view(np.float16)[0].astype(np.float32))
+    nan = oracle.f32_to_f16_bits(float("nan"))
+    assert (nan & 0x7c00) == 0x7c00 and (nan & 0x3ff) != 0
+
+
+@pytest.mark.parametrize("d", [128, 256, 512])
+def test_f16_record_same_codes_rounded_scales_and_size(d):
+    K, V = synth.make_kv(77 + d, 128, 1, d, 4)
+    r32 = oracle.compress_tile(K[:, 0], V[:, 0])
+    r16 = oracle.compress_tile(K[:, 0], V[:, 0], f16=True)
+    assert r16.size == oracle.tile_bytes(d, True) == 106 * d + 256
+    z32 = oracle.unpack_codes(r32, d)
+    z16 = oracle.unpack_codes(r16, d)
+    assert np.array_equal(z32[0], z16[0]) and np.array_equal(z32[1], z16[1])
+    s32 = oracle.record_scales(r32, d)
+    s16 = oracle.record_scales(r16, d, f16=True)
+    for name in s32:
+        assert np.array_equal(s32[name].astype(np.float16).astype(np.float32), s16[name]), name
+    if d == 128:   # the pages' saving: 120 -> 108 bytes per token per KV head
+        assert oracle.tile_bytes(128) // 128 == 120 and oracle.tile_bytes(128, True) // 128 == 108
+
+
+def test_f16_record_dequant_within_half_rounding_of_f32_record():
+    """k' = ktok (z kscale + kmin): each of the three stored factors moves by at
+    most 2^-11 relative when rounded to f16, so every dequantised element moves
+    by at most (1 + 2^-11)^2 - 1 relative to the sum of its term magnitudes."""
+    d = 128
+    K, V = synth.make_kv(88, 128, 1, d, 4)
+    r32 = oracle.compress_tile(K[:, 0], V[:, 0])
+    r16 = oracle.compress_tile(K[:, 0], V[:, 0], f16=True)
+    k32, v32 = oracle.dequant_rotated(r32, d)
+    k16, v16 = oracle.dequant_rotated(r16, d, f16=True)
+    s = oracle.record_scales(r32, d)
+    zK, zV = oracle.unpack_codes(r32, d)
+    eps = (1 + 2.0 ** -11) ** 2 - 1 + 1e-12
+    magk = np.abs(s["ktok"])[:, None] * (zK * np.abs(s["kscale"])[None] + np.abs(s["kmin"])[None])
+    magv = np.abs(s["vchan"])[None] * (zV * np.abs(s["vscale"][:, :1]) + np.abs(s["vmin"][:, :1]))
+    assert np.all(np.abs(k16 - k32) <= eps * magk)
+    assert np.all(np.abs(v16 - v32) <= eps * magv)
+    assert np.any(k16 != k32)
