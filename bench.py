@@ -98,12 +98,12 @@ def graph_ms(torch, fn, n_inner, reps):
     return s.elapsed_time(e) / (reps * n_inner), g
 
 
-def decode_case(torch, kvarn, synth, ctx, steps, warmup, seed=2):
+def decode_case(torch, kvarn, synth, ctx, steps, warmup, seed=2, f16=False):
     d, Hq, Hkv, W = 128, 32, 8, 256
     dev = "cuda:0"
     T = kvarn.visible_tiles(ctx - 1, W)
     n_w = ctx - 128 * T
-    tb = kvarn.tile_bytes(d)
+    tb = kvarn.tile_bytes(d, f16)
     scale = 1.0 / math.sqrt(d)
     per_layer = T * Hkv * tb + 2 * n_w * Hkv * d * 4
     L = max(8, int(math.ceil(2 * LLC_BYTES / per_layer)))
@@ -111,13 +111,14 @@ def decode_case(torch, kvarn, synth, ctx, steps, warmup, seed=2):
     kd = torch.from_numpy(K).to(dev)
     vd = torch.from_numpy(V).to(dev)
     rec0 = torch.empty(T, Hkv, tb, dtype=torch.uint8, device=dev)
-    kvarn.compress_tile(kd, vd, rec0, T)
+    kvarn.compress_tile(kd, vd, rec0, T, f16_scales=f16)
     recs = [rec0.clone() for _ in range(L)]
     kw = [kd[128 * T:].clone()[None] for _ in range(L)]
     vw = [vd[128 * T:].clone()[None] for _ in range(L)]
     qs = torch.from_numpy(synth.make_q(seed, L, Hq, d)).to(dev).reshape(L, 1, Hq, d)
     outs = torch.empty_like(qs)
-    ws_bytes = kvarn.decode_workspace_bytes(qs[0], None, recs[0], [0], [T], kw[0], vw[0], [n_w], scale)
+    ws_bytes = kvarn.decode_workspace_bytes(qs[0], None, recs[0], [0], [T], kw[0], vw[0], [n_w], scale,
+                                            f16_scales=f16)
     ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
@@ -125,7 +126,7 @@ def decode_case(torch, kvarn, synth, ctx, steps, warmup, seed=2):
         for l in range(L):
             # q_rot=None: the split kernel rotates q itself
             kvarn.decode_attention(qs[l], None, recs[l], [0], [T], kw[l], vw[l], [n_w], scale,
-                                   out=outs[l], workspace=ws)
+                                   out=outs[l], workspace=ws, f16_scales=f16)
 
     reps = max(1, int(math.ceil(steps / L)))
     warm = max(1, int(math.ceil(warmup / L)))
@@ -141,20 +142,21 @@ def decode_case(torch, kvarn, synth, ctx, steps, warmup, seed=2):
     e.synchronize()
     ms = s.elapsed_time(e) / (reps * L)
     alg = decode_bytes(T, n_w, Hq, Hkv, d, tb)
-    info = {"context": ctx, "tiles": T, "window": n_w, "layers_cycled": L, "us_per_step": ms * 1e3,
+    info = {"context": ctx, "tiles": T, "window": n_w, "scales": "f16" if f16 else "f32",
+            "record_bytes": tb, "layers_cycled": L, "us_per_step": ms * 1e3,
             "kv_tokens_per_s": ctx / (ms * 1e-3), "algorithmic_bytes": alg,
             "achieved_GBps": alg / (ms * 1e-3) / 1e9}
     return info, reps * L, warm * L, (K, V, rec0, T, n_w, qs, scale)
 
 
-def verify_case(torch, kvarn, synth, ctx, width, reps=20, seed=2):
+def verify_case(torch, kvarn, synth, ctx, width, reps=20, seed=2, f16=False):
     """Multi-query verify of `width` draft rows at the 8B decode shape: one call
     reads every record once for all rows (the workload of a decode step)."""
     d, Hq, Hkv, W = 128, 32, 8, 256
     dev = "cuda:0"
     T = kvarn.visible_tiles(ctx - 1, W)
     n_w = ctx - 128 * T
-    tb = kvarn.tile_bytes(d)
+    tb = kvarn.tile_bytes(d, f16)
     scale = 1.0 / math.sqrt(d)
     per_layer = T * Hkv * tb + 2 * n_w * Hkv * d * 4
     L = max(8, int(math.ceil(2 * LLC_BYTES / per_layer)))
@@ -162,20 +164,21 @@ def verify_case(torch, kvarn, synth, ctx, width, reps=20, seed=2):
     kd = torch.from_numpy(K).to(dev)
     vd = torch.from_numpy(V).to(dev)
     rec0 = torch.empty(T, Hkv, tb, dtype=torch.uint8, device=dev)
-    kvarn.compress_tile(kd, vd, rec0, T)
+    kvarn.compress_tile(kd, vd, rec0, T, f16_scales=f16)
     recs = [rec0.clone() for _ in range(L)]
     kw = [kd[128 * T:].clone()[None] for _ in range(L)]
     vw = [vd[128 * T:].clone()[None] for _ in range(L)]
     qs = torch.from_numpy(synth.make_q(seed, L * width, Hq, d)).to(dev).reshape(L, 1, width, Hq, d)
     outs = torch.empty_like(qs)
-    ws_bytes = kvarn.decode_workspace_bytes(qs[0], None, recs[0], [0], [T], kw[0], vw[0], [n_w], scale)
+    ws_bytes = kvarn.decode_workspace_bytes(qs[0], None, recs[0], [0], [T], kw[0], vw[0], [n_w], scale,
+                                            f16_scales=f16)
     ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
     def run():
         for l in range(L):
             kvarn.decode_attention(qs[l], None, recs[l], [0], [T], kw[l], vw[l], [n_w], scale,
-                                   out=outs[l], workspace=ws)
+                                   out=outs[l], workspace=ws, f16_scales=f16)
 
     ms, _ = graph_ms(torch, run, L, reps)
     return {"width": width, "context": ctx, "us_per_call": ms * 1e3,
@@ -256,6 +259,13 @@ def main():
                 log(f"decode context {c}: {info['us_per_step']:.2f} us per call, "
                     f"{info['achieved_GBps']:.0f} GB/s algorithmic")
 
+    # ---- the same decode over records with f16 scales ----
+    dec16 = None
+    if not args.no_extra_contexts:
+        dec16, _, _, _ = decode_case(torch, kvarn, synth, args.context, 320, 32, f16=True)
+        log(f"decode context {args.context}, f16 scales: {dec16['us_per_step']:.2f} us per call, "
+            f"{dec16['achieved_GBps']:.0f} GB/s algorithmic")
+
     # ---- multi-query verify (width 8) at the same context ----
     verify = verify_case(torch, kvarn, synth, args.context, 8)
     verify["vs_decode_call"] = verify["us_per_call"] / head["us_per_step"]
@@ -301,20 +311,24 @@ def main():
             threadpool_limits = None
         import oracle
         recs_np = rec0.cpu().numpy()
-        q_np = qs[0, 0].cpu().numpy()
+        q_all = qs[:, 0].cpu().numpy()
         lim = threadpool_limits(1) if threadpool_limits else None
-        t0 = time.perf_counter()
-        kh, vh = oracle.dequant_records(recs_np, d)
-        oracle.decode(q_np, kh, vh, T, K[128 * T:], V[128 * T:], scale)
+        # whole decode steps (dequantise every record, attend every head), each with
+        # the next layer's query, until about 10 s of one core's work
+        n_steps, t0 = 0, time.perf_counter()
+        while n_steps < 2 or (n_steps < 200 and time.perf_counter() - t0 < 10.0):
+            kh, vh = oracle.dequant_records(recs_np, d)
+            oracle.decode(q_all[n_steps % q_all.shape[0]], kh, vh, T, K[128 * T:], V[128 * T:], scale)
+            n_steps += 1
         sec = time.perf_counter() - t0
         if lim is not None:
             lim.unregister()
         ctx = head["context"]
-        cpu = {"value": ctx / sec, "unit": "KV tokens/s", "cores": 1, "kind": "oracle",
-               "sample": f"one decode step of the 8B-shaped layer at context {ctx}: dequantise "
-                         f"{T * Hkv} records to fp64 and attend 32 heads over {ctx} keys "
-                         f"({sec:.2f} s on one host core)"}
-        log(f"cpu oracle: {sec:.2f} s per decode step")
+        cpu = {"value": n_steps * ctx / sec, "unit": "KV tokens/s", "cores": 1, "kind": "oracle",
+               "sample": f"{n_steps} decode steps of the 8B-shaped layer at context {ctx}, each: "
+                         f"dequantise {T * Hkv} records to fp64 and attend 32 heads over {ctx} keys "
+                         f"({sec:.1f} s on one host core)"}
+        log(f"cpu oracle: {n_steps} decode steps in {sec:.1f} s")
 
     ms_step = head["us_per_step"] * 1e-3
     alg = head["algorithmic_bytes"]
@@ -343,6 +357,7 @@ def main():
                      "algorithmic_bytes_per_launch": alg, "launch_us": ms_step * 1e3},
         "hbm_GBps": achieved,
         "decode_contexts": [head] + extra,
+        "decode_f16_scales": dec16,
         "prefill": prefill,
         "prefill_wide_heads": prefill_wide,
         "verify": verify,

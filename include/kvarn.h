@@ -41,6 +41,14 @@
  *   matrix (its own inverse).  The record size is the one the capacity figure
  *   in PR #434's "Measured" table implies (six fp32 vectors per tile-head).
  *
+ * Record with f16 scales (issue #433 item 3, "f16 scales in the packed tile
+ * layout"): a head_dim argument OR-ed with KVARN_SCALES_F16 selects it in
+ * every call.  Same codes and section order; each scale is the fp32 value
+ * above rounded to the nearest binary16 (ties to even), so the sections are
+ * half as long and the record is 106*d + 256 bytes (108 bytes per token at
+ * d = 128 instead of 120).  The codes are those of the fp32 record: only the
+ * stored scales are rounded.
+ *
  * FP32 window and promotion (PR #434 commit list: "the FP32 window is the
  * staging; whole-tile promotion"): with a window of W tokens, the oldest 128
  * raw tokens are compressed into one tile when the window reaches W+128, so
@@ -59,12 +67,15 @@ extern "C" {
 
 #define KVARN_TILE_TOKENS 128
 #define KVARN_MAX_BATCH 64
+/* OR into any head_dim argument: records carry f16 scales (see above). */
+#define KVARN_SCALES_F16 0x10000
 
 typedef enum kvarn_status {
   KVARN_OK = 0,
   KVARN_E_INVALID = 1,     /* null pointer, negative or inconsistent sizes   */
-  KVARN_E_UNSUPPORTED = 2, /* head_dim not 128/256/512, GQA not integral, or a
-                              size beyond a documented limit                 */
+  KVARN_E_UNSUPPORTED = 2, /* head_dim not 128/256/512 (with or without
+                              KVARN_SCALES_F16), GQA not integral, or a size
+                              beyond a documented limit                      */
   KVARN_E_ALIGN = 3,       /* pointer or stride not 16-byte aligned          */
   KVARN_E_WORKSPACE = 4,   /* workspace missing or smaller than required     */
   KVARN_E_DEVICE = 5       /* HIP reported an error at launch                */
@@ -73,8 +84,9 @@ typedef enum kvarn_status {
 /* Human-readable name of a status code (static string, never NULL). */
 const char* kvarn_status_string(int status);
 
-/* Bytes of one (tile, KV head) record: 116*head_dim + 512, or 0 when
- * head_dim is not 128, 256 or 512. */
+/* Bytes of one (tile, KV head) record: 116*d + 512 (106*d + 256 with
+ * KVARN_SCALES_F16), d = head_dim without the flag; 0 when d is not 128, 256
+ * or 512 or another bit is set. */
 size_t kvarn_tile_bytes(int32_t head_dim);
 
 /*
@@ -104,6 +116,7 @@ int kvarn_compress_tile(int32_t head_dim, int32_t n_tiles, int32_t n_kv_heads,
  * head_dim).  PR #434 commit list (llm_kvarn_rotate_query); issue #180
  * Algorithm step 1 (the rotation preserves attention scores).
  *   q, q_rot    device fp32 [n_rows][head_dim], contiguous; may alias.
+ * KVARN_SCALES_F16 in head_dim is accepted and has no effect here.
  * Errors: KVARN_E_UNSUPPORTED, KVARN_E_INVALID (null, n_rows < 0), KVARN_E_ALIGN.
  */
 int kvarn_rotate_query(int32_t head_dim, int64_t n_rows, const float* q,
@@ -123,7 +136,8 @@ int kvarn_rotate_query(int32_t head_dim, int64_t n_rows, const float* q,
  * in the original domain.
  */
 typedef struct kvarn_decode_args {
-  int32_t head_dim;        /* 128, 256 or 512                                   */
+  int32_t head_dim;        /* 128, 256 or 512, | KVARN_SCALES_F16 for records
+                              with f16 scales                                   */
   int32_t batch;           /* 1..KVARN_MAX_BATCH sequences                      */
   int32_t n_q_heads;       /* multiple of n_kv_heads                            */
   int32_t n_kv_heads;
@@ -193,7 +207,8 @@ int kvarn_decode_attention(const kvarn_decode_args* args, void* workspace,
  * split decode query with that view and need a workspace for the partials.
  */
 typedef struct kvarn_prefill_args {
-  int32_t head_dim;        /* 128, 256 or 512                                   */
+  int32_t head_dim;        /* 128, 256 or 512, | KVARN_SCALES_F16 for records
+                              with f16 scales                                   */
   int32_t n_q_heads;
   int32_t n_kv_heads;
   int32_t window;          /* W of the promotion rule, >= 0                     */

@@ -84,7 +84,7 @@ __device__ __forceinline__ float code_of(float xn, float lo, float inv, float le
   return z;
 }
 
-template <int D>
+template <int D, bool H>
 __global__ void __launch_bounds__(2 * D)
 compress_kernel(const float* __restrict__ kin, const float* __restrict__ vin,
                 int64_t tok_stride, int64_t head_stride, int n_kv,
@@ -92,7 +92,7 @@ compress_kernel(const float* __restrict__ kin, const float* __restrict__ vin,
   constexpr int W = D / 32;        // waves
   constexpr int J = kTile / W;     // channel offsets per LDS exchange round
   constexpr bool kStoreQ = D <= 256;
-  using R = Rec<D>;
+  using R = Rec<D, H>;
 
   __shared__ float smem[16384];    // 64 KB, reused by every phase
 
@@ -294,11 +294,12 @@ compress_kernel(const float* __restrict__ kin, const float* __restrict__ vin,
     if (owner) {
       bc_v[ch_own] = lo;
       bc_x[ch_own] = inv;
-      reinterpret_cast<float*>(rec + R::kscale)[ch_own] = delta * s_own;
-      reinterpret_cast<float*>(rec + R::kmin)[ch_own] = lo * s_own;
+      sc_st<H>(rec + R::kscale, ch_own, delta * s_own);
+      sc_st<H>(rec + R::kmin, ch_own, lo * s_own);
     }
     if (w == 0) {
-      reinterpret_cast<float2*>(rec + R::ktok)[lane] = make_float2(r[0], r[1]);
+      sc_st<H>(rec + R::ktok, 2 * lane, r[0]);
+      sc_st<H>(rec + R::ktok, 2 * lane + 1, r[1]);
     }
     __syncthreads();
     uint8_t* kst = reinterpret_cast<uint8_t*>(smem + 2 * D);  // [D][64] bytes
@@ -326,7 +327,7 @@ compress_kernel(const float* __restrict__ kin, const float* __restrict__ vin,
       mm[(w * kTile + 2 * lane + i) * 2 + 0] = lo;
       mm[(w * kTile + 2 * lane + i) * 2 + 1] = hi;
     }
-    if (owner) reinterpret_cast<float*>(rec + R::vchan)[ch_own] = s_own;
+    if (owner) sc_st<H>(rec + R::vchan, ch_own, s_own);
     __syncthreads();
     const int g = w / 4;  // channel group of this wave
 #pragma unroll
@@ -351,8 +352,8 @@ compress_kernel(const float* __restrict__ kin, const float* __restrict__ vin,
       }
       reinterpret_cast<uint2*>(rec + R::vcode + t * (D / 4) + 8 * w)[0] = make_uint2(packed[0], packed[1]);
       if ((w & 3) == 0) {
-        reinterpret_cast<float*>(rec + R::vscale)[t * R::groups + g] = delta * r[i];
-        reinterpret_cast<float*>(rec + R::vmin)[t * R::groups + g] = lo * r[i];
+        sc_st<H>(rec + R::vscale, t * R::groups + g, delta * r[i]);
+        sc_st<H>(rec + R::vmin, t * R::groups + g, lo * r[i]);
       }
     }
   }
@@ -360,29 +361,38 @@ compress_kernel(const float* __restrict__ kin, const float* __restrict__ vin,
 
 }  // namespace
 
-// Launch the compressor for n_tiles x n_kv tile-heads (keys and values).
-hipError_t launch_compress(int d, int n_tiles, int n_kv, const float* k, const float* v,
-                           int64_t tok_stride, int64_t head_stride, void* records,
-                           hipStream_t stream) {
+// Launch the compressor for n_tiles x n_kv tile-heads (keys and values);
+// h16: store the scales as f16.
+template <bool H>
+hipError_t launch_compress_h(int d, int n_tiles, int n_kv, const float* k, const float* v,
+                             int64_t tok_stride, int64_t head_stride, uint8_t* rec,
+                             hipStream_t stream) {
   dim3 grid(n_tiles, n_kv, 2);
-  uint8_t* rec = static_cast<uint8_t*>(records);
   switch (d) {
     case 128:
-      hipLaunchKernelGGL(compress_kernel<128>, grid, dim3(256), 0, stream, k, v, tok_stride,
+      hipLaunchKernelGGL((compress_kernel<128, H>), grid, dim3(256), 0, stream, k, v, tok_stride,
                          head_stride, n_kv, rec);
       break;
     case 256:
-      hipLaunchKernelGGL(compress_kernel<256>, grid, dim3(512), 0, stream, k, v, tok_stride,
+      hipLaunchKernelGGL((compress_kernel<256, H>), grid, dim3(512), 0, stream, k, v, tok_stride,
                          head_stride, n_kv, rec);
       break;
     case 512:
-      hipLaunchKernelGGL(compress_kernel<512>, grid, dim3(1024), 0, stream, k, v, tok_stride,
+      hipLaunchKernelGGL((compress_kernel<512, H>), grid, dim3(1024), 0, stream, k, v, tok_stride,
                          head_stride, n_kv, rec);
       break;
     default:
       return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_compress(int d, bool h16, int n_tiles, int n_kv, const float* k, const float* v,
+                           int64_t tok_stride, int64_t head_stride, void* records,
+                           hipStream_t stream) {
+  uint8_t* rec = static_cast<uint8_t*>(records);
+  return h16 ? launch_compress_h<true>(d, n_tiles, n_kv, k, v, tok_stride, head_stride, rec, stream)
+             : launch_compress_h<false>(d, n_tiles, n_kv, k, v, tok_stride, head_stride, rec, stream);
 }
 
 }  // namespace kvarn

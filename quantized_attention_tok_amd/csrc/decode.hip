@@ -31,9 +31,9 @@ namespace {
 // ---------------------------------------------------------------------------
 // partial kernel: one (split, kv head, sequence)
 // ---------------------------------------------------------------------------
-template <int D, int G>
+template <int D, int G, bool H>
 __global__ void __launch_bounds__(kDecThreads) decode_partial_kernel(DecodeParams P) {
-  using R = Rec<D>;
+  using R = Rec<D, H>;
   constexpr int NG = D / 128;                 // value channel groups
   constexpr int HH = (G >= 2 && D == 128) ? 2 : 1;   // head halves (K: 128 tokens x HH)
   constexpr int GH = G / HH;                  // heads per thread in the K phase
@@ -110,11 +110,11 @@ __global__ void __launch_bounds__(kDecThreads) decode_partial_kernel(DecodeParam
         const uint4* src = reinterpret_cast<const uint4*>(base + R::kcode);
         uint4* dst = reinterpret_cast<uint4*>(s_code);
         for (int i = tid; i < 4 * D; i += kDecThreads) dst[i] = src[i];
-        const float* ks = reinterpret_cast<const float*>(base + R::kscale);
-        const float* km = reinterpret_cast<const float*>(base + R::kmin);
-        const float* kt = reinterpret_cast<const float*>(base + R::ktok);
-        for (int i = tid; i < D; i += kDecThreads) { s_scale[i] = ks[i]; s_scale[D + i] = km[i]; }
-        if (tid < kTile) s_scale[2 * D + tid] = kt[tid];
+        for (int i = tid; i < D; i += kDecThreads) {
+          s_scale[i] = sc_ld<H>(base + R::kscale, i);
+          s_scale[D + i] = sc_ld<H>(base + R::kmin, i);
+        }
+        if (tid < kTile) s_scale[2 * D + tid] = sc_ld<H>(base + R::ktok, tid);
       }
       __syncthreads();
       // q~ = q' * kscale and bias = q' . kmin
@@ -157,13 +157,10 @@ __global__ void __launch_bounds__(kDecThreads) decode_partial_kernel(DecodeParam
         const uint4* src = reinterpret_cast<const uint4*>(base + R::vcode);
         uint4* dst = reinterpret_cast<uint4*>(s_code);
         for (int i = tid; i < 2 * D; i += kDecThreads) dst[i] = src[i];
-        const float* vch = reinterpret_cast<const float*>(base + R::vchan);
-        const float* vs = reinterpret_cast<const float*>(base + R::vscale);
-        const float* vm = reinterpret_cast<const float*>(base + R::vmin);
-        for (int i = tid; i < D; i += kDecThreads) s_scale[i] = vch[i];
+        for (int i = tid; i < D; i += kDecThreads) s_scale[i] = sc_ld<H>(base + R::vchan, i);
         for (int i = tid; i < kTile * NG; i += kDecThreads) {
-          s_scale[D + i] = vs[i];
-          s_scale[2 * D + i] = vm[i];
+          s_scale[D + i] = sc_ld<H>(base + R::vscale, i);
+          s_scale[2 * D + i] = sc_ld<H>(base + R::vmin, i);
         }
       }
       // ---- online softmax over this tile: one wave per head ----
@@ -353,7 +350,10 @@ __global__ void __launch_bounds__(64) decode_combine_kernel(DecodeParams P) {
 template <int D, int G>
 hipError_t launch_decode_dg(const DecodeParams& P, int batch, hipStream_t stream) {
   dim3 grid(P.n_tsplit + P.n_wsplit, P.n_kv, batch);
-  hipLaunchKernelGGL((decode_partial_kernel<D, G>), grid, dim3(kDecThreads), 0, stream, P);
+  if (P.h16)
+    hipLaunchKernelGGL((decode_partial_kernel<D, G, true>), grid, dim3(kDecThreads), 0, stream, P);
+  else
+    hipLaunchKernelGGL((decode_partial_kernel<D, G, false>), grid, dim3(kDecThreads), 0, stream, P);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(P.n_q, batch), dim3(64), 0, stream, P);

@@ -170,9 +170,10 @@ __device__ __forceinline__ float wsum(float v) {
   return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
 }
 
-template <int G, int TPW>
+template <int G, int TPW, bool H>
 __global__ void __launch_bounds__(256 * TPW) decode_split_kernel(DecodeParams P) {
   using L = Lds<G, TPW>;
+  using R = Rec<D, H>;
   constexpr int NW = L::kNW;
   constexpr int NT = 64 * NW;
   constexpr int HPL = L::HPL, RPH = L::RPH;
@@ -212,8 +213,8 @@ __global__ void __launch_bounds__(256 * TPW) decode_split_kernel(DecodeParams P)
   const float c_log2 = P.scale * kLog2e;
   const int tau = wv >> 2, wq = wv & 3;
   const bool has_tile = tau < ntl;
-  const int64_t rstride = (int64_t)P.n_kv * kRecBytes;
-  const uint8_t* recs = P.records + ((sv.rec_row0 + j0) * (int64_t)P.n_kv + kvh) * kRecBytes;
+  const int64_t rstride = (int64_t)P.n_kv * R::bytes;
+  const uint8_t* recs = P.records + ((sv.rec_row0 + j0) * (int64_t)P.n_kv + kvh) * R::bytes;
   const float* qsrc = (P.q_rot ? P.q_rot : P.q) + ((int64_t)b * P.n_q + (int64_t)kvh * G) * D;
   const float* qraw = P.q + ((int64_t)b * P.n_q + (int64_t)kvh * G) * D;
 
@@ -255,15 +256,13 @@ __global__ void __launch_bounds__(256 * TPW) decode_split_kernel(DecodeParams P)
       const bool ok = pr < TPW * G && pr / G < ntl;
       const int tt = ok ? pr / G : 0, h = ok ? pr % G : 0;
       const uint8_t* rp = recs + tt * rstride;
-      const float* ks = reinterpret_cast<const float*>(rp + kOffKscale);
-      const float* km = reinterpret_cast<const float*>(rp + kOffKmin);
       pq0[k] = qsrc[h * D + lane];
       pq1[k] = qsrc[h * D + lane + 64];
-      pks0[k] = ks[lane];
-      pks1[k] = ks[lane + 64];
-      pkm0[k] = km[lane];
-      pkm1[k] = km[lane + 64];
-      pvs[k] = *reinterpret_cast<const float2*>(rp + kOffVscale + 8 * lane);
+      pks0[k] = sc_ld<H>(rp + R::kscale, lane);
+      pks1[k] = sc_ld<H>(rp + R::kscale, lane + 64);
+      pkm0[k] = sc_ld<H>(rp + R::kmin, lane);
+      pkm1[k] = sc_ld<H>(rp + R::kmin, lane + 64);
+      pvs[k] = sc_ld2<H>(rp + R::vscale, 2 * lane);
     }
     // keep the prep loads ahead of the tile loads in the memory queue
     asm volatile("" ::: "memory");
@@ -273,14 +272,14 @@ __global__ void __launch_bounds__(256 * TPW) decode_split_kernel(DecodeParams P)
       const uint8_t* rg = recs + (has_tile ? tau : 0) * rstride;
       kc0 = *reinterpret_cast<const uint4*>(rg + lane * 64 + 16 * wq);
       kc1 = *reinterpret_cast<const uint4*>(rg + (lane + 64) * 64 + 16 * wq);
-      vcd = *reinterpret_cast<const uint4*>(rg + kOffV + 32 * 32 * wq + 16 * lane);
+      vcd = *reinterpret_cast<const uint4*>(rg + R::vcode + 32 * 32 * wq + 16 * lane);
       const int tok = 32 * wq + 2 * n;
-      kt = *reinterpret_cast<const float2*>(rg + kOffKtok + 4 * tok);
-      vsc = *reinterpret_cast<const float2*>(rg + kOffVscale + 4 * tok);
-      vmn = *reinterpret_cast<const float2*>(rg + kOffVmin + 4 * tok);
-      const float* vch = reinterpret_cast<const float*>(rg + kOffVchan) + 16 * (n & 7) + 8 * (n >> 3);
-      vca = *reinterpret_cast<const float4*>(vch);
-      vcb = *reinterpret_cast<const float4*>(vch + 4);
+      kt = sc_ld2<H>(rg + R::ktok, tok);
+      vsc = sc_ld2<H>(rg + R::vscale, tok);
+      vmn = sc_ld2<H>(rg + R::vmin, tok);
+      const int vci = 16 * (n & 7) + 8 * (n >> 3);
+      vca = sc_ld4<H>(rg + R::vchan, vci);
+      vcb = sc_ld4<H>(rg + R::vchan, vci + 4);
     }
 
     // ---- 2. prep: rotated query, q~ hi/lo operand rows, unscale, bias, w scale ----
@@ -589,16 +588,21 @@ __global__ void __launch_bounds__(256) decode_combine_kernel(DecodeParams P) {
   }
 }
 
-template <int G>
-hipError_t launch_split_g(const DecodeParams& P, int batch, hipStream_t stream) {
+template <int G, bool H>
+hipError_t launch_split_gh(const DecodeParams& P, int batch, hipStream_t stream) {
   dim3 grid(P.n_tsplit, P.n_kv, batch);
   switch (P.tps) {
-    case 1: hipLaunchKernelGGL((decode_split_kernel<G, 1>), grid, dim3(256), 0, stream, P); break;
-    case 2: hipLaunchKernelGGL((decode_split_kernel<G, 2>), grid, dim3(512), 0, stream, P); break;
-    case 4: hipLaunchKernelGGL((decode_split_kernel<G, 4>), grid, dim3(1024), 0, stream, P); break;
+    case 1: hipLaunchKernelGGL((decode_split_kernel<G, 1, H>), grid, dim3(256), 0, stream, P); break;
+    case 2: hipLaunchKernelGGL((decode_split_kernel<G, 2, H>), grid, dim3(512), 0, stream, P); break;
+    case 4: hipLaunchKernelGGL((decode_split_kernel<G, 4, H>), grid, dim3(1024), 0, stream, P); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <int G>
+hipError_t launch_split_g(const DecodeParams& P, int batch, hipStream_t stream) {
+  return P.h16 ? launch_split_gh<G, true>(P, batch, stream) : launch_split_gh<G, false>(P, batch, stream);
 }
 
 }  // namespace

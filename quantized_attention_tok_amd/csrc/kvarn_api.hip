@@ -10,7 +10,14 @@
 
 namespace {
 
-bool dim_ok(int32_t d) { return d == 128 || d == 256 || d == 512; }
+// A head_dim argument holds the head dimension in its low 16 bits, optionally
+// OR-ed with KVARN_SCALES_F16 (records with f16 scales); no other bits.
+int dim_of(int32_t hd) { return hd & 0xFFFF; }
+bool f16_of(int32_t hd) { return (hd & KVARN_SCALES_F16) != 0; }
+bool dim_ok(int32_t hd) {
+  const int d = dim_of(hd);
+  return (hd & ~(0xFFFF | KVARN_SCALES_F16)) == 0 && (d == 128 || d == 256 || d == 512);
+}
 bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool st16(int64_t floats) { return (floats % 4) == 0; }
 
@@ -89,7 +96,7 @@ int validate_decode(const kvarn_decode_args* a, DecodePlan* plan) {
   if (!dim_ok(a->head_dim)) return KVARN_E_UNSUPPORTED;
   if (a->q_len < 0 || a->q_len > 8) return KVARN_E_INVALID;
   const int w = q_rows(a);
-  if (w > 1 && a->head_dim != 128) return KVARN_E_UNSUPPORTED;
+  if (w > 1 && dim_of(a->head_dim) != 128) return KVARN_E_UNSUPPORTED;
   if (a->batch < 1 || a->n_q_heads < 1 || a->n_kv_heads < 1) return KVARN_E_INVALID;
   if (a->batch > KVARN_MAX_BATCH) return KVARN_E_UNSUPPORTED;
   if (a->n_q_heads % a->n_kv_heads != 0) return KVARN_E_UNSUPPORTED;
@@ -97,7 +104,7 @@ int validate_decode(const kvarn_decode_args* a, DecodePlan* plan) {
   if (!(G == 1 || G == 2 || G == 4 || G == 8)) return KVARN_E_UNSUPPORTED;
   if (a->max_tiles < 0 || a->max_win < 0 || a->n_record_rows < 0) return KVARN_E_INVALID;
   if (!a->q || !a->out || !a->n_tiles || !a->n_win || !a->rec_start) return KVARN_E_INVALID;
-  if (!a->q_rot && !fused_decode(a->head_dim)) return KVARN_E_INVALID;
+  if (!a->q_rot && !fused_decode(dim_of(a->head_dim))) return KVARN_E_INVALID;
   bool any_tiles = false, any_win = false;
   for (int b = 0; b < a->batch; ++b) {
     const int nt = a->n_tiles[b], nw = a->n_win[b];
@@ -113,7 +120,8 @@ int validate_decode(const kvarn_decode_args* a, DecodePlan* plan) {
   }
   if (any_tiles && !a->records) return KVARN_E_INVALID;
   if (any_win && (!a->k_win || !a->v_win)) return KVARN_E_INVALID;
-  if (any_win && (a->win_tok_stride < a->head_dim || a->win_head_stride < 0 || a->win_seq_stride < 0))
+  if (any_win && (a->win_tok_stride < dim_of(a->head_dim) || a->win_head_stride < 0 ||
+                  a->win_seq_stride < 0))
     return KVARN_E_INVALID;
   if (!al16(a->q) || !al16(a->q_rot) || !al16(a->out) || !al16(a->records) ||
       !al16(a->k_win) || !al16(a->v_win))
@@ -122,7 +130,7 @@ int validate_decode(const kvarn_decode_args* a, DecodePlan* plan) {
     return KVARN_E_ALIGN;
   if (plan) {
     *plan = w > 1 ? plan_verify(a->batch, a->n_kv_heads, G, a->max_tiles, a->max_win)
-          : fused_decode(a->head_dim)
+          : fused_decode(dim_of(a->head_dim))
                 ? plan_fused(a->batch, a->n_kv_heads, a->max_tiles, a->max_win)
                 : plan_decode(a->batch, a->n_kv_heads, a->max_tiles, a->max_win, kTargetGroups,
                               kvarn::kWinChunk);
@@ -134,7 +142,7 @@ size_t decode_part_floats(int rows, int n_q, int d, const DecodePlan& p) {
   return (size_t)rows * n_q * (size_t)(p.n_tsplit + p.n_wsplit) * (size_t)(d + 4);
 }
 size_t decode_ws(const kvarn_decode_args* a, const DecodePlan& p) {
-  return decode_part_floats(a->batch * q_rows(a), a->n_q_heads, a->head_dim, p) * sizeof(float);
+  return decode_part_floats(a->batch * q_rows(a), a->n_q_heads, dim_of(a->head_dim), p) * sizeof(float);
 }
 
 int64_t prefill_tiles_at(int64_t pos, int window) {
@@ -157,7 +165,7 @@ int validate_prefill(const kvarn_prefill_args* a, DecodePlan* plan) {
   if (t_last > 0 && !a->records) return KVARN_E_INVALID;
   if (a->n_record_rows < t_last) return KVARN_E_INVALID;
   if (a->raw_base < 0 || a->raw_base > KVARN_TILE_TOKENS * t_first) return KVARN_E_INVALID;
-  if (a->tok_stride < a->head_dim || a->head_stride < 0) return KVARN_E_INVALID;
+  if (a->tok_stride < dim_of(a->head_dim) || a->head_stride < 0) return KVARN_E_INVALID;
   if (!al16(a->q) || !al16(a->q_rot) || !al16(a->out) || !al16(a->records) || !al16(a->k) ||
       !al16(a->v))
     return KVARN_E_ALIGN;
@@ -189,7 +197,7 @@ const char* kvarn_status_string(int status) {
 }
 
 size_t kvarn_tile_bytes(int32_t head_dim) {
-  return dim_ok(head_dim) ? (size_t)(116 * head_dim + 512) : 0;
+  return dim_ok(head_dim) ? (size_t)kvarn::tile_bytes_rt(dim_of(head_dim), f16_of(head_dim)) : 0;
 }
 
 int kvarn_compress_tile(int32_t head_dim, int32_t n_tiles, int32_t n_kv_heads, const float* k,
@@ -199,12 +207,12 @@ int kvarn_compress_tile(int32_t head_dim, int32_t n_tiles, int32_t n_kv_heads, c
   if (n_tiles < 0 || n_kv_heads < 1) return KVARN_E_INVALID;
   if (n_tiles == 0) return KVARN_OK;
   if (!k || !v || !records) return KVARN_E_INVALID;
-  if (tok_stride < head_dim || head_stride < 0) return KVARN_E_INVALID;
+  if (tok_stride < dim_of(head_dim) || head_stride < 0) return KVARN_E_INVALID;
   if (n_kv_heads > 65535) return KVARN_E_UNSUPPORTED;
   if (!al16(k) || !al16(v) || !al16(records) || !st16(tok_stride) || !st16(head_stride))
     return KVARN_E_ALIGN;
-  hipError_t e = kvarn::launch_compress(head_dim, n_tiles, n_kv_heads, k, v, tok_stride,
-                                        head_stride, records, (hipStream_t)stream);
+  hipError_t e = kvarn::launch_compress(dim_of(head_dim), f16_of(head_dim), n_tiles, n_kv_heads, k,
+                                        v, tok_stride, head_stride, records, (hipStream_t)stream);
   return e == hipSuccess ? KVARN_OK : KVARN_E_DEVICE;
 }
 
@@ -216,7 +224,7 @@ int kvarn_rotate_query(int32_t head_dim, int64_t n_rows, const float* q, float* 
   if (!q || !q_rot) return KVARN_E_INVALID;
   if (!al16(q) || !al16(q_rot)) return KVARN_E_ALIGN;
   if ((n_rows + 3) / 4 > 0x7fffffffLL) return KVARN_E_UNSUPPORTED;
-  hipError_t e = kvarn::launch_rotate(head_dim, n_rows, q, q_rot, (hipStream_t)stream);
+  hipError_t e = kvarn::launch_rotate(dim_of(head_dim), n_rows, q, q_rot, (hipStream_t)stream);
   return e == hipSuccess ? KVARN_OK : KVARN_E_DEVICE;
 }
 
@@ -231,7 +239,7 @@ int kvarn_decode_attention(const kvarn_decode_args* a, void* workspace, size_t w
   DecodePlan p;
   int st = validate_decode(a, &p);
   if (st != KVARN_OK) return st;
-  const bool fused = fused_decode(a->head_dim);
+  const bool fused = fused_decode(dim_of(a->head_dim));
   const int w = q_rows(a);
   const size_t need = decode_ws(a, p);
   if (!workspace || ws_bytes < need) return KVARN_E_WORKSPACE;
@@ -257,6 +265,7 @@ int kvarn_decode_attention(const kvarn_decode_args* a, void* workspace, size_t w
   P.n_wsplit = p.n_wsplit;
   P.wchunk = p.wchunk;
   P.mode = 0;
+  P.h16 = f16_of(a->head_dim);
   for (int b = 0; b < a->batch; ++b) {
     P.rec_start[b] = a->rec_start[b];
     P.win_start[b] = a->win_start ? a->win_start[b] : 0;
@@ -269,7 +278,7 @@ int kvarn_decode_attention(const kvarn_decode_args* a, void* workspace, size_t w
     e = kvarn::launch_verify_mfma(P, a->batch, (hipStream_t)stream);
   } else {
     e = fused ? kvarn::launch_decode_fused(P, a->batch, (hipStream_t)stream)
-              : kvarn::launch_decode(a->head_dim, P, a->batch, (hipStream_t)stream);
+              : kvarn::launch_decode(dim_of(a->head_dim), P, a->batch, (hipStream_t)stream);
   }
   return e == hipSuccess ? KVARN_OK : KVARN_E_DEVICE;
 }
@@ -281,8 +290,8 @@ int kvarn_decode_attention(const kvarn_decode_args* a, void* workspace, size_t w
 size_t kvarn_prefill_workspace_bytes(const kvarn_prefill_args* a) {
   DecodePlan p;
   if (validate_prefill(a, &p) != KVARN_OK) return 0;
-  if (a->head_dim == 128) return 0;
-  return decode_part_floats(a->chunk, a->n_q_heads, a->head_dim, p) * sizeof(float);
+  if (dim_of(a->head_dim) == 128) return 0;
+  return decode_part_floats(a->chunk, a->n_q_heads, dim_of(a->head_dim), p) * sizeof(float);
 }
 
 int kvarn_prefill_attention(const kvarn_prefill_args* a, void* workspace, size_t ws_bytes,
@@ -290,8 +299,9 @@ int kvarn_prefill_attention(const kvarn_prefill_args* a, void* workspace, size_t
   DecodePlan plan;
   int st = validate_prefill(a, &plan);
   if (st != KVARN_OK) return st;
-  if (a->head_dim != 128) {
-    const size_t need = decode_part_floats(a->chunk, a->n_q_heads, a->head_dim, plan) * sizeof(float);
+  if (dim_of(a->head_dim) != 128) {
+    const size_t need =
+        decode_part_floats(a->chunk, a->n_q_heads, dim_of(a->head_dim), plan) * sizeof(float);
     if (!workspace || ws_bytes < need) return KVARN_E_WORKSPACE;
     if (!al16(workspace)) return KVARN_E_ALIGN;
     kvarn::DecodeParams P;
@@ -314,10 +324,11 @@ int kvarn_prefill_attention(const kvarn_prefill_args* a, void* workspace, size_t
     P.n_wsplit = plan.n_wsplit;
     P.wchunk = plan.wchunk;
     P.mode = 1;
+    P.h16 = f16_of(a->head_dim);
     P.window = a->window;
     P.pos0 = a->pos0;
     P.raw_base = a->raw_base;
-    hipError_t e = kvarn::launch_decode(a->head_dim, P, a->chunk, (hipStream_t)stream);
+    hipError_t e = kvarn::launch_decode(dim_of(a->head_dim), P, a->chunk, (hipStream_t)stream);
     return e == hipSuccess ? KVARN_OK : KVARN_E_DEVICE;
   }
   kvarn::PrefillParams P;
@@ -338,6 +349,7 @@ int kvarn_prefill_attention(const kvarn_prefill_args* a, void* workspace, size_t
   P.n_q = a->n_q_heads;
   P.n_kv = a->n_kv_heads;
   P.G = a->n_q_heads / a->n_kv_heads;
+  P.h16 = f16_of(a->head_dim);
   hipError_t e = kvarn::launch_prefill_mfma(P, (hipStream_t)stream);
   return e == hipSuccess ? KVARN_OK : KVARN_E_DEVICE;
 }

@@ -11,22 +11,71 @@ namespace kvarn {
 constexpr int kTile = 128;   // tokens per tile
 constexpr int kWave = 64;    // CDNA wavefront width
 
-// Byte offsets of the record sections for head_dim D.
-template <int D>
+// Byte offsets of the record sections for head_dim D: codes, then the six
+// scale vectors as fp32 (H = false, 116 D + 512 bytes) or as f16 rounded to
+// nearest-even (H = true, 106 D + 256 bytes; SharpInference issue #433
+// item 3, "f16 scales").
+template <int D, bool H = false>
 struct Rec {
+  static constexpr int sb = H ? 2 : 4;   // bytes per stored scale
   static constexpr int kcode = 0;
   static constexpr int vcode = 64 * D;
   static constexpr int ktok = 96 * D;
-  static constexpr int kscale = 96 * D + 512;
-  static constexpr int kmin = 100 * D + 512;
-  static constexpr int vchan = 104 * D + 512;
-  static constexpr int vscale = 108 * D + 512;
-  static constexpr int vmin = 112 * D + 512;
-  static constexpr int bytes = 116 * D + 512;
+  static constexpr int kscale = ktok + 128 * sb;
+  static constexpr int kmin = kscale + D * sb;
+  static constexpr int vchan = kmin + D * sb;
+  static constexpr int vscale = vchan + D * sb;
+  static constexpr int vmin = vscale + D * sb;
+  static constexpr int bytes = vmin + D * sb;
   static constexpr int groups = D / 128;
 };
+static_assert(Rec<128>::bytes == 116 * 128 + 512 && Rec<128, true>::bytes == 106 * 128 + 256, "layout");
 
-__host__ __device__ inline int64_t tile_bytes_rt(int d) { return 116LL * d + 512; }
+__host__ __device__ inline int64_t tile_bytes_rt(int d, bool h = false) {
+  return h ? 106LL * d + 256 : 116LL * d + 512;
+}
+
+// Scale element i of a section at p (fp32 or f16 storage), as fp32.
+template <bool H>
+__device__ __forceinline__ float sc_ld(const uint8_t* p, int i) {
+  if constexpr (H) return (float)reinterpret_cast<const _Float16*>(p)[i];
+  else return reinterpret_cast<const float*>(p)[i];
+}
+// elements i, i + 1 (i even)
+template <bool H>
+__device__ __forceinline__ float2 sc_ld2(const uint8_t* p, int i) {
+  if constexpr (H) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    const h2 x = *reinterpret_cast<const h2*>(p + 2 * i);
+    return make_float2((float)x[0], (float)x[1]);
+  } else {
+    return *reinterpret_cast<const float2*>(p + 4 * i);
+  }
+}
+// elements i .. i + 3 (i a multiple of 4)
+template <bool H>
+__device__ __forceinline__ float4 sc_ld4(const uint8_t* p, int i) {
+  if constexpr (H) {
+    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+    const h4 x = *reinterpret_cast<const h4*>(p + 2 * i);
+    return make_float4((float)x[0], (float)x[1], (float)x[2], (float)x[3]);
+  } else {
+    return *reinterpret_cast<const float4*>(p + 4 * i);
+  }
+}
+// store element i.  f16: the fp32 value v is rounded to nearest-even half.
+// The empty asm pins v as an fp32 register value: without it the compiler
+// folds a producing multiply into v_fma_mixlo_f16, which rounds the exact
+// product to half once instead of rounding the fp32 scale.
+template <bool H>
+__device__ __forceinline__ void sc_st(uint8_t* p, int i, float v) {
+  if constexpr (H) {
+    asm("" : "+v"(v));
+    reinterpret_cast<_Float16*>(p)[i] = (_Float16)v;
+  } else {
+    reinterpret_cast<float*>(p)[i] = v;
+  }
+}
 
 // fp32(1/sqrt(D)): 2^-k/2 for even log2(D); otherwise the rounded sqrt(2)
 // scaled by a power of two (exact scaling, so still correctly rounded).

@@ -31,6 +31,7 @@ struct DecodeParams {
   // where raw row p lives at (p - raw_base) * win_tok_stride.
   int mode;
   int q_len;                       // query rows per sequence (multi-query verify)
+  int h16;                         // records carry f16 scales
   int window;
   int64_t pos0, raw_base;
   int64_t rec_start[64];
@@ -51,6 +52,7 @@ struct PrefillParams {
   int64_t pos0, raw_base;
   float scale;
   int chunk, window, n_q, n_kv, G;
+  int h16;                         // records carry f16 scales
 };
 
 // Tiles, window tokens, first record row and window base of sequence b.
@@ -79,7 +81,7 @@ __device__ __forceinline__ SeqView seq_view(const DecodeParams& P, int b) {
   return v;
 }
 
-hipError_t launch_compress(int d, int n_tiles, int n_kv, const float* k, const float* v,
+hipError_t launch_compress(int d, bool h16, int n_tiles, int n_kv, const float* k, const float* v,
                            int64_t tok_stride, int64_t head_stride, void* records,
                            hipStream_t stream);
 hipError_t launch_rotate(int d, int64_t n_rows, const float* q, float* q_rot, hipStream_t stream);

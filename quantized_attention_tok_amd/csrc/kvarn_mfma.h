@@ -23,14 +23,6 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 constexpr int D = 128;
-constexpr int kRecBytes = Rec<D>::bytes;     // 15360
-constexpr int kOffV = Rec<D>::vcode;
-constexpr int kOffKtok = Rec<D>::ktok;
-constexpr int kOffKscale = Rec<D>::kscale;
-constexpr int kOffKmin = Rec<D>::kmin;
-constexpr int kOffVchan = Rec<D>::vchan;
-constexpr int kOffVscale = Rec<D>::vscale;
-constexpr int kOffVmin = Rec<D>::vmin;
 constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ half8 as_half8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {

@@ -137,27 +137,28 @@ struct TileRegs {
   float c0, c1, c2;
 };
 
+template <bool H>
 __device__ __forceinline__ void load_tile(const uint8_t* rec, int lane, int wv, TileRegs& r) {
+  using R = Rec<D, H>;
   const int hi4 = lane >> 4, lo4 = lane & 15;
   if (wv < 4) {
     const uint32_t* src = reinterpret_cast<const uint32_t*>(rec + (8 * (4 * wv + hi4)) * 64) + lo4;
 #pragma unroll
     for (int e = 0; e < 8; ++e) r.c[e] = src[16 * e];
   } else {
-    const uint8_t* vcode = rec + kOffV;
+    const uint8_t* vcode = rec + R::vcode;
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         r.c[4 * h + i] = *reinterpret_cast<const uint16_t*>(vcode + (32 * (wv - 4) + 16 * h + 4 * hi4 + i) * (D / 4) + 2 * lo4);
   }
-  const float* f = reinterpret_cast<const float*>(rec);
   const int idx = 64 * (wv & 1) + lane;
   const int role = wv >> 1;
-  r.xa = *reinterpret_cast<const float2*>(f + (role < 2 ? kOffKscale : kOffVscale) / 4 + 2 * lane);
-  r.xb = *reinterpret_cast<const float2*>(f + kOffKmin / 4 + 2 * lane);
-  r.c0 = f[(role == 0 ? kOffKtok : role == 1 ? kOffKscale : role == 2 ? kOffVscale : kOffVchan) / 4 + idx];
-  r.c1 = f[(role == 2 ? kOffVmin : kOffKmin) / 4 + idx];
+  r.xa = sc_ld2<H>(rec + (role < 2 ? R::kscale : R::vscale), 2 * lane);
+  r.xb = sc_ld2<H>(rec + R::kmin, 2 * lane);
+  r.c0 = sc_ld<H>(rec + (role == 0 ? R::ktok : role == 1 ? R::kscale : role == 2 ? R::vscale : R::vchan), idx);
+  r.c1 = sc_ld<H>(rec + (role == 2 ? R::vmin : R::kmin), idx);
   r.c2 = 0.0f;
 }
 
@@ -278,6 +279,7 @@ struct Ctx {
   int64_t part_row, part_head;
 };
 
+template <bool H>
 __device__ __forceinline__ void prefill_body(const Ctx& P) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -308,13 +310,13 @@ __device__ __forceinline__ void prefill_body(const Ctx& P) {
 
   __shared__ __attribute__((aligned(16))) uint8_t s_lds[kLdsBytes];
   const float scale_log2 = P.scale * kLog2e;
-  const uint8_t* recs = P.records + (int64_t)kvh * kRecBytes;
-  const int64_t rstride = (int64_t)P.n_kv * kRecBytes;
+  const uint8_t* recs = P.records + (int64_t)kvh * Rec<D, H>::bytes;
+  const int64_t rstride = (int64_t)P.n_kv * Rec<D, H>::bytes;
 
   // ---- tile 0 unpacked, tile 1 in registers; this lane's rotated query:
   // row n, channels 32 k4 + 8 g .. + 7 ----
   TileRegs tr;
-  if (ja < jend) load_tile(recs + (int64_t)ja * rstride, lane, wv, tr);
+  if (ja < jend) load_tile<H>(recs + (int64_t)ja * rstride, lane, wv, tr);
   float qv[4][8];
   {
     const float* qp = (P.rotate ? P.q : P.q_rot) + ((int64_t)(row_ok ? r0 + n : 0) * P.n_q + hq) * D + 8 * g;
@@ -331,7 +333,7 @@ __device__ __forceinline__ void prefill_body(const Ctx& P) {
   }
   if (ja < jend) {
     unpack_tile(tr, s_lds + kLdsK, s_lds + kLdsV, s_lds + kLdsC, lane, wv, scale_log2);
-    if (ja + 1 < jend) load_tile(recs + (int64_t)(ja + 1) * rstride, lane, wv, tr);
+    if (ja + 1 < jend) load_tile<H>(recs + (int64_t)(ja + 1) * rstride, lane, wv, tr);
   }
   __syncthreads();
   if (P.rotate) {   // q' = H q in registers: channel 32 k4 + 8 g + jj (g = lane bits 4, 5)
@@ -415,7 +417,7 @@ __device__ __forceinline__ void prefill_body(const Ctx& P) {
       const int nb = pb ^ 1;
       unpack_tile(tr, s_lds + kLdsK + nb * kOpBytes, s_lds + kLdsV + nb * kOpBytes, s_lds + kLdsC + nb * kConstBytes,
                   lane, wv, scale_log2);
-      if (j + 2 < jend) load_tile(recs + (int64_t)(j + 2) * rstride, lane, wv, tr);
+      if (j + 2 < jend) load_tile<H>(recs + (int64_t)(j + 2) * rstride, lane, wv, tr);
     };
     if (th == 0 && next) unpack_next();
     if (j < T_wave) {
@@ -771,6 +773,7 @@ __device__ __forceinline__ void prefill_body(const Ctx& P) {
   }
 }
 
+template <bool H>
 __global__ void __launch_bounds__(kThreads) prefill_mfma_kernel(PrefillParams P) {
   Ctx c;
   c.q = P.q;
@@ -797,7 +800,7 @@ __global__ void __launch_bounds__(kThreads) prefill_mfma_kernel(PrefillParams P)
   c.rb = INT64_MAX;
   c.part = nullptr;
   c.part_row = c.part_head = 0;
-  prefill_body(c);
+  prefill_body<H>(c);
 }
 
 // Multi-query verify: sequence b's q_len query rows are the q_len newest
@@ -808,6 +811,7 @@ __global__ void __launch_bounds__(kThreads) prefill_mfma_kernel(PrefillParams P)
 // split s < n_tsplit takes tiles [tps s, tps s + tps), split n_tsplit + r the
 // window tokens [wchunk r, wchunk r + wchunk).  Partials: row r = b q_len + i,
 // head h, split s at part + ((r n_q + h) (n_tsplit + n_wsplit) + s) (D + 4).
+template <bool H>
 __global__ void __launch_bounds__(kThreads) verify_mfma_kernel(DecodeParams P) {
   const int ns = P.n_tsplit, nsp = P.n_tsplit + P.n_wsplit;
   const int b = blockIdx.z / nsp, s = blockIdx.z % nsp;
@@ -819,7 +823,7 @@ __global__ void __launch_bounds__(kThreads) verify_mfma_kernel(DecodeParams P) {
   c.rotate = P.q_rot == nullptr;
   c.q_rot = c.rotate ? c.q : P.q_rot + row0;
   c.out = P.out;   // unused: partial output
-  c.records = P.records + P.rec_start[b] * (int64_t)P.n_kv * kRecBytes;
+  c.records = P.records + P.rec_start[b] * (int64_t)P.n_kv * Rec<D, H>::bytes;
   c.k = P.k_win + (int64_t)b * P.win_seq_stride + P.win_start[b] * P.win_tok_stride;
   c.v = P.v_win + (int64_t)b * P.win_seq_stride + P.win_start[b] * P.win_tok_stride;
   c.tok_stride = P.win_tok_stride;
@@ -840,7 +844,7 @@ __global__ void __launch_bounds__(kThreads) verify_mfma_kernel(DecodeParams P) {
   c.part_head = (int64_t)nsp * (D + 4);
   c.part_row = (int64_t)P.n_q * c.part_head;
   c.part = P.part + (int64_t)b * w * c.part_row + (int64_t)s * (D + 4);
-  prefill_body(c);
+  prefill_body<H>(c);
 }
 
 // Verify combine: one wave per (row, query head), lane l owns channels l and
@@ -921,14 +925,20 @@ __global__ void __launch_bounds__(256) verify_combine_kernel(DecodeParams P, int
 hipError_t launch_prefill_mfma(const PrefillParams& P, hipStream_t stream) {
   const int n_blk = ((P.chunk + kRows - 1) / kRows) * P.G;
   dim3 grid((n_blk + 3) / 4, P.n_kv);
-  hipLaunchKernelGGL(prefill_mfma_kernel, grid, dim3(kThreads), 0, stream, P);
+  if (P.h16)
+    hipLaunchKernelGGL(prefill_mfma_kernel<true>, grid, dim3(kThreads), 0, stream, P);
+  else
+    hipLaunchKernelGGL(prefill_mfma_kernel<false>, grid, dim3(kThreads), 0, stream, P);
   return hipGetLastError();
 }
 
 hipError_t launch_verify_mfma(const DecodeParams& P, int batch, hipStream_t stream) {
   const int n_blk = ((P.q_len + kRows - 1) / kRows) * P.G;
   dim3 grid((n_blk + 3) / 4, P.n_kv, batch * (P.n_tsplit + P.n_wsplit));
-  hipLaunchKernelGGL(verify_mfma_kernel, grid, dim3(kThreads), 0, stream, P);
+  if (P.h16)
+    hipLaunchKernelGGL(verify_mfma_kernel<true>, grid, dim3(kThreads), 0, stream, P);
+  else
+    hipLaunchKernelGGL(verify_mfma_kernel<false>, grid, dim3(kThreads), 0, stream, P);
   const int items = batch * P.q_len * P.n_q;
   hipLaunchKernelGGL(verify_combine_kernel, dim3((items + 3) / 4), dim3(256), 0, stream, P, batch * P.q_len);
   return hipGetLastError();

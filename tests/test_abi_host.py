@@ -40,6 +40,19 @@ def test_tile_bytes_and_status_strings(L):
     assert L.kvarn_status_string(99) == b"KVARN_E_UNKNOWN"
 
 
+def test_f16_scale_flag_sizes_match_the_oracle_record(L):
+    import oracle
+    from quantized_attention_tok_amd import kvarn
+    m = re.search(r"#define\s+KVARN_SCALES_F16\s+(0x[0-9a-fA-F]+)", open(HEADER).read())
+    assert m and int(m.group(1), 16) == kvarn.SCALES_F16
+    F = kvarn.SCALES_F16
+    for d in (128, 256, 512):
+        assert L.kvarn_tile_bytes(d | F) == oracle.tile_bytes(d, f16=True)
+        assert L.kvarn_tile_bytes(d) == oracle.tile_bytes(d)
+    assert L.kvarn_tile_bytes(128 | F) == 13824   # 108 bytes per token at d = 128
+    assert L.kvarn_tile_bytes(128 | 0x20000) == 0 and L.kvarn_tile_bytes(96 | F) == 0
+
+
 # These calls pass fake device pointers that every case must reject before a
 # launch; on a machine with a GPU a wrongly accepted case would launch a kernel
 # on them, so the module only runs where no GPU is visible.
@@ -62,6 +75,11 @@ def test_compress_validation(L):
     assert f(128, 1, 1, vp(FAKE + 4), vp(FAKE), 128, 128, vp(FAKE), None) == 3
     assert f(128, 1, 1, vp(FAKE), vp(FAKE), 130, 128, vp(FAKE), None) == 3
     assert f(128, 0, 1, None, None, 0, 0, None, None) == 0   # empty is a no-op
+    F = 0x10000   # KVARN_SCALES_F16
+    assert f(100 | F, 1, 1, vp(FAKE), vp(FAKE), 128, 128, vp(FAKE), None) == 2
+    assert f(128 | 0x40000, 1, 1, vp(FAKE), vp(FAKE), 128, 128, vp(FAKE), None) == 2
+    assert f(256 | F, 1, 1, vp(FAKE), vp(FAKE), 128, 256, vp(FAKE), None) == 1   # stride < 256
+    assert f(128 | F, 1, 1, vp(FAKE), vp(FAKE), 128, 128, vp(FAKE + 8), None) == 3
 
 
 def test_rotate_validation(L):
@@ -112,6 +130,8 @@ def test_decode_validation_and_workspace_query(L):
         (dict(q_len=9), 1), (dict(q_len=-1), 1),          # verify width 0..8
         (dict(q_len=2, n_win=[1], max_win=1), 1),         # the drafts must be in the window
         (dict(q_len=2, head_dim=256, n_win=[4], max_win=4), 2),   # verify is head_dim 128
+        (dict(head_dim=128 | 0x80000), 2),                # unknown format bit
+        (dict(head_dim=128 | 0x10000, n_record_rows=3), 1),   # f16-scale records, same checks
     ]
     for over, want in bad:
         b, k2 = _decode_args(**over)
@@ -152,7 +172,11 @@ def test_prefill_validation(L):
     assert need > 0
     assert L.kvarn_prefill_attention(ctypes.byref(a256), ctypes.c_void_p(FAKE), need - 16, None) == 4
     assert L.kvarn_prefill_attention(ctypes.byref(a256), None, need, None) == 4
-    bad = [(dict(head_dim=384), 2), (dict(chunk=0), 1), (dict(pos0=-1), 1),
+    # the f16-scale format does not change the workspace
+    a256h = args(head_dim=256 | 0x10000, tok_stride=256 * 2, head_stride=256)
+    assert L.kvarn_prefill_workspace_bytes(ctypes.byref(a256h)) == need
+    bad = [(dict(head_dim=384), 2), (dict(head_dim=128 | 0x20000), 2), (dict(chunk=0), 1),
+           (dict(pos0=-1), 1),
            (dict(n_record_rows=3), 1), (dict(raw_base=384), 1), (dict(k=FAKE + 4), 3),
            (dict(tok_stride=258), 3), (dict(n_q_heads=6), 2)]
     for over, want in bad:
