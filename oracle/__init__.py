@@ -21,6 +21,10 @@ Method sources (cited by page and section):
   * gmlx PR #116 "KVarN variance-normalized KV cache", commit list:
     speculative-verify widths 2-8 attend the compressed records (verify
     rows are decode queries).
+  * gmlx PR #116 commit list: mixed-width "k6v5"-style arms and key/value
+    widths chosen on their own (RTN with 2^b - 1 levels; the codes of every
+    width are an LSB-first bit stream, which for 4/2 bits is the nibble and
+    crumb order of the K4V2 record).
   * colibri PR #399, maintainer's "Ready for review" comment: for an
     orthogonal rotation, q . xhat == rotate(q) . c and the weighted value sum
     is the unrotation of the weighted code sum.
@@ -75,6 +79,14 @@ def _load():
     lib.oracle_compress_tile_fmt.argtypes = [f32p, f32p, ctypes.c_longlong, ctypes.c_int,
                                              ctypes.c_int, ctypes.c_int, u8p]
     lib.oracle_unpack_codes.argtypes = [u8p, ctypes.c_int, u8p, u8p]
+    i = ctypes.c_int
+    lib.oracle_tile_bytes_w.restype = ctypes.c_longlong
+    lib.oracle_tile_bytes_w.argtypes = [i, i, i, i]
+    lib.oracle_layout_w.argtypes = [i, i, i, i, ctypes.POINTER(ctypes.c_longlong)]
+    lib.oracle_compress_tile_w.restype = ctypes.c_int
+    lib.oracle_compress_tile_w.argtypes = [f32p, f32p, ctypes.c_longlong, i, i, i, i, i, u8p]
+    lib.oracle_unpack_codes_w.argtypes = [u8p, i, i, i, u8p, u8p]
+    lib.oracle_dequant_f64_w.argtypes = [u8p, i, i, i, i, i, f64p, f64p]
     lib.oracle_dequant_f64.argtypes = [u8p, ctypes.c_int, ctypes.c_int, f64p, f64p]
     lib.oracle_dequant_f64_fmt.argtypes = [u8p, ctypes.c_int, ctypes.c_int, ctypes.c_int, f64p, f64p]
     lib.oracle_attend_f64.argtypes = [f64p, f64p, f64p, ctypes.c_longlong, ctypes.c_int,
@@ -91,17 +103,27 @@ def _p(a, ct):
 # sizes and layout
 # --------------------------------------------------------------------------
 
-def tile_bytes(d: int, f16: bool = False) -> int:
+def _k4v2(kbits, vbits):
+    return kbits == 4 and vbits == 2
+
+
+def tile_bytes(d: int, f16: bool = False, kbits: int = 4, vbits: int = 2) -> int:
     """Bytes of one (tile, kv-head) record: 116*d + 512 with fp32 scales, or
-    106*d + 256 with f16 scales (SharpInference issue #433 item 3); 0 if d is
-    unsupported."""
-    return int(_load().oracle_tile_bytes_fmt(d, 1 if f16 else 0))
+    106*d + 256 with f16 scales (SharpInference issue #433 item 3), for 4-bit
+    keys and 2-bit values; 16*d*(kbits + vbits) code bytes in general.  0 if
+    d or a width is unsupported."""
+    if _k4v2(kbits, vbits):
+        return int(_load().oracle_tile_bytes_fmt(d, 1 if f16 else 0))
+    return int(_load().oracle_tile_bytes_w(d, 1 if f16 else 0, kbits, vbits))
 
 
-def layout(d: int, f16: bool = False) -> dict:
+def layout(d: int, f16: bool = False, kbits: int = 4, vbits: int = 2) -> dict:
     """Byte offsets of the record sections."""
     off = (ctypes.c_longlong * 9)()
-    _load().oracle_layout_fmt(d, 1 if f16 else 0, off)
+    if _k4v2(kbits, vbits):
+        _load().oracle_layout_fmt(d, 1 if f16 else 0, off)
+    else:
+        _load().oracle_layout_w(d, 1 if f16 else 0, kbits, vbits, off)
     names = ["kcode", "vcode", "ktok", "kscale", "kmin", "vchan", "vscale", "vmin", "end"]
     return dict(zip(names, [int(x) for x in off]))
 
@@ -189,15 +211,35 @@ def rtn_group(x: np.ndarray, bits: int):
 # compression
 # --------------------------------------------------------------------------
 
-def compress_tile(k_tile: np.ndarray, v_tile: np.ndarray, iters: int = 8,
-                  f16: bool = False) -> np.ndarray:
-    """One (tile, kv head): raw fp32 K and V tiles [128][d] -> record bytes.
-    With f16 the six scale vectors are stored rounded to half precision
-    (nearest, ties to even); the codes are those of the fp32 record."""
+def _tiles_in(k_tile, v_tile):
     k = np.ascontiguousarray(k_tile, dtype=np.float32)
     v = np.ascontiguousarray(v_tile, dtype=np.float32)
     assert k.shape == v.shape and k.shape[0] == TILE
-    d = k.shape[1]
+    return k, v, k.shape[1]
+
+
+def compress_tile_bits(k_tile: np.ndarray, v_tile: np.ndarray, iters: int = 8, f16: bool = False,
+                       kbits: int = 4, vbits: int = 2) -> np.ndarray:
+    """compress_tile packed by the bit-stream writer (any widths, 4/2 included)."""
+    k, v, d = _tiles_in(k_tile, v_tile)
+    rec = np.zeros(int(_load().oracle_tile_bytes_w(d, 1 if f16 else 0, kbits, vbits)), np.uint8)
+    rc = _load().oracle_compress_tile_w(_p(k, ctypes.c_float), _p(v, ctypes.c_float), d, d, iters,
+                                        1 if f16 else 0, kbits, vbits, _p(rec, ctypes.c_uint8))
+    if rc != 0:
+        raise ValueError(f"unsupported head_dim {d} or widths {kbits}/{vbits}")
+    return rec
+
+
+def compress_tile(k_tile: np.ndarray, v_tile: np.ndarray, iters: int = 8,
+                  f16: bool = False, kbits: int = 4, vbits: int = 2) -> np.ndarray:
+    """One (tile, kv head): raw fp32 K and V tiles [128][d] -> record bytes.
+    With f16 the six scale vectors are stored rounded to half precision
+    (nearest, ties to even); the codes are those of the fp32 record.  Keys
+    take kbits-bit codes, values vbits-bit codes (K4V2 by default, packed
+    nibble by nibble; other widths by the bit-stream writer)."""
+    if not _k4v2(kbits, vbits):
+        return compress_tile_bits(k_tile, v_tile, iters, f16, kbits, vbits)
+    k, v, d = _tiles_in(k_tile, v_tile)
     rec = np.zeros(tile_bytes(d, f16), np.uint8)
     rc = _load().oracle_compress_tile_fmt(_p(k, ctypes.c_float), _p(v, ctypes.c_float), d, d,
                                           iters, 1 if f16 else 0, _p(rec, ctypes.c_uint8))
@@ -207,19 +249,31 @@ def compress_tile(k_tile: np.ndarray, v_tile: np.ndarray, iters: int = 8,
 
 
 def compress_tiles(K: np.ndarray, V: np.ndarray, n_tiles: int, iters: int = 8,
-                   f16: bool = False) -> np.ndarray:
+                   f16: bool = False, kbits: int = 4, vbits: int = 2) -> np.ndarray:
     """K, V: [n_tokens][n_kv][d] raw fp32.  Returns records [n_tiles][n_kv][bytes]
     for the first n_tiles whole tiles."""
     n_kv, d = K.shape[1], K.shape[2]
-    out = np.zeros((n_tiles, n_kv, tile_bytes(d, f16)), np.uint8)
+    out = np.zeros((n_tiles, n_kv, tile_bytes(d, f16, kbits, vbits)), np.uint8)
     for j in range(n_tiles):
         for h in range(n_kv):
             out[j, h] = compress_tile(K[TILE * j:TILE * (j + 1), h], V[TILE * j:TILE * (j + 1), h],
-                                      iters, f16)
+                                      iters, f16, kbits, vbits)
     return out
 
 
-def unpack_codes(rec: np.ndarray, d: int):
+def unpack_codes_bits(rec: np.ndarray, d: int, kbits: int = 4, vbits: int = 2):
+    """zK[t][c], zV[t][c] read by the bit-stream reader (any widths)."""
+    rec = np.ascontiguousarray(rec, dtype=np.uint8)
+    zK = np.zeros((TILE, d), np.uint8)
+    zV = np.zeros((TILE, d), np.uint8)
+    _load().oracle_unpack_codes_w(_p(rec, ctypes.c_uint8), d, kbits, vbits, _p(zK, ctypes.c_uint8),
+                                  _p(zV, ctypes.c_uint8))
+    return zK, zV
+
+
+def unpack_codes(rec: np.ndarray, d: int, kbits: int = 4, vbits: int = 2):
+    if not _k4v2(kbits, vbits):
+        return unpack_codes_bits(rec, d, kbits, vbits)
     rec = np.ascontiguousarray(rec, dtype=np.uint8)
     zK = np.zeros((TILE, d), np.uint8)
     zV = np.zeros((TILE, d), np.uint8)
@@ -228,9 +282,10 @@ def unpack_codes(rec: np.ndarray, d: int):
     return zK, zV
 
 
-def record_scales(rec: np.ndarray, d: int, f16: bool = False) -> dict:
+def record_scales(rec: np.ndarray, d: int, f16: bool = False, kbits: int = 4,
+                  vbits: int = 2) -> dict:
     """The six scale vectors of a record as fp32 numpy arrays."""
-    off = layout(d, f16)
+    off = layout(d, f16, kbits, vbits)
     rec = np.ascontiguousarray(rec, dtype=np.uint8)
     ng = d // 128
     w, dt = (2, np.float16) if f16 else (4, np.float32)
@@ -259,25 +314,30 @@ def hadamard_f64(d: int) -> np.ndarray:
     return np.where(parity == 1, -1.0, 1.0) / np.sqrt(d)
 
 
-def dequant_rotated(rec: np.ndarray, d: int, f16: bool = False):
+def dequant_rotated(rec: np.ndarray, d: int, f16: bool = False, kbits: int = 4, vbits: int = 2):
     """k'[t][c], v'[t][c] in the rotated domain (fp64), from the stored codes
     and folded scales."""
     rec = np.ascontiguousarray(rec, dtype=np.uint8)
     kd = np.zeros((TILE, d), np.float64)
     vd = np.zeros((TILE, d), np.float64)
-    _load().oracle_dequant_f64_fmt(_p(rec, ctypes.c_uint8), d, 1 if f16 else 0, 1,
-                                   _p(kd, ctypes.c_double), _p(vd, ctypes.c_double))
+    if _k4v2(kbits, vbits):
+        _load().oracle_dequant_f64_fmt(_p(rec, ctypes.c_uint8), d, 1 if f16 else 0, 1,
+                                       _p(kd, ctypes.c_double), _p(vd, ctypes.c_double))
+    else:
+        _load().oracle_dequant_f64_w(_p(rec, ctypes.c_uint8), d, 1 if f16 else 0, kbits, vbits, 1,
+                                     _p(kd, ctypes.c_double), _p(vd, ctypes.c_double))
     return kd, vd
 
 
-def dequant(rec: np.ndarray, d: int, f16: bool = False):
+def dequant(rec: np.ndarray, d: int, f16: bool = False, kbits: int = 4, vbits: int = 2):
     """khat = H k', vhat = H v' (fp64, raw domain)."""
-    kd, vd = dequant_rotated(rec, d, f16)
+    kd, vd = dequant_rotated(rec, d, f16, kbits, vbits)
     H = hadamard_f64(d)
     return kd @ H.T, vd @ H.T
 
 
-def dequant_records(records: np.ndarray, d: int, f16: bool = False):
+def dequant_records(records: np.ndarray, d: int, f16: bool = False, kbits: int = 4,
+                    vbits: int = 2):
     """records [T][n_kv][bytes] -> khat, vhat [T*128][n_kv][d] fp64."""
     T, n_kv = records.shape[0], records.shape[1]
     kh = np.zeros((T * TILE, n_kv, d))
@@ -285,7 +345,7 @@ def dequant_records(records: np.ndarray, d: int, f16: bool = False):
     H = hadamard_f64(d)
     for j in range(T):
         for h in range(n_kv):
-            kd, vd = dequant_rotated(records[j, h], d, f16)
+            kd, vd = dequant_rotated(records[j, h], d, f16, kbits, vbits)
             kh[TILE * j:TILE * (j + 1), h] = kd @ H.T
             vh[TILE * j:TILE * (j + 1), h] = vd @ H.T
     return kh, vh

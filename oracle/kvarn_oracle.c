@@ -18,6 +18,10 @@
  *     CPU + CUDA (#180)", commit list: channel-major K / token-major V packing
  *     in 128-token tiles, 2-bit bit packing; "Measured" table: the capacity
  *     figure that fixes the record size.
+ *   - gmlx PR #116 "KVarN variance-normalized KV cache", commit list: mixed
+ *     key / value widths ("k6v5"-style arms, widths set per side): the
+ *     *_w functions take kb-bit keys and vb-bit values (1..8 bits each),
+ *     packed as LSB-first bit streams.
  *
  * Precision.  Compression is an encoding: the packed codes are decided in
  * fp32, and both this oracle and the GPU path must make every decision in the
@@ -64,12 +68,26 @@ long long oracle_tile_bytes_fmt(int d, int fmt) {
 }
 long long oracle_tile_bytes(int d) { return oracle_tile_bytes_fmt(d, 0); }
 
+/* Code widths (SharpInference gmlx PR #116 commit list: mixed-width "k6v5"
+ * arms, key and value widths set on their own): kb-bit keys and vb-bit values,
+ * 1 <= kb, vb <= 8, levels 2^b - 1.  Codes are an LSB-first bit stream: the
+ * code of token t in channel c's key stream starts at bit kb*t, the code of
+ * channel c in token t's value stream at bit vb*c.  K4V2 is kb = 4, vb = 2:
+ * 64 bytes per channel, d/4 bytes per token. */
+static int valid_bits(int b) { return b >= 1 && b <= 8; }
+
+long long oracle_tile_bytes_w(int d, int fmt, int kb, int vb) {
+  if (!valid_dim(d) || (fmt != 0 && fmt != 1) || !valid_bits(kb) || !valid_bits(vb)) return 0;
+  const long long w = fmt ? 2 : 4;
+  return 16LL * d * (kb + vb) + w * (128 + 5LL * d);
+}
+
 /* offsets: K codes, V codes, ktok, kscale, kmin, vchan, vscale, vmin, end */
-static void layout_fmt(int d, int fmt, long long off[9]) {
+static void layout_w(int d, int fmt, int kb, int vb, long long off[9]) {
   const long long w = fmt ? 2 : 4;   /* bytes per scale */
-  off[0] = 0;                 /* K codes  uint8[d][64]         */
-  off[1] = 64LL * d;          /* V codes  uint8[128][d/4]      */
-  off[2] = 96LL * d;          /* ktok     [128]                */
+  off[0] = 0;                 /* K codes  [d][16 kb] bytes     */
+  off[1] = 16LL * kb * d;     /* V codes  [128][d vb / 8]      */
+  off[2] = off[1] + 16LL * vb * d;   /* ktok [128]             */
   off[3] = off[2] + 128 * w;  /* kscale   [d]                  */
   off[4] = off[3] + d * w;    /* kmin     [d]                  */
   off[5] = off[4] + d * w;    /* vchan    [d]                  */
@@ -77,10 +95,12 @@ static void layout_fmt(int d, int fmt, long long off[9]) {
   off[7] = off[6] + d * w;    /* vmin     [128][d/128]         */
   off[8] = off[7] + d * w;    /* end                           */
 }
+static void layout_fmt(int d, int fmt, long long off[9]) { layout_w(d, fmt, 4, 2, off); }
 static void layout(int d, long long off[9]) { layout_fmt(d, 0, off); }
 
 void oracle_layout(int d, long long* off) { layout(d, off); }
 void oracle_layout_fmt(int d, int fmt, long long* off) { layout_fmt(d, fmt, off); }
+void oracle_layout_w(int d, int fmt, int kb, int vb, long long* off) { layout_w(d, fmt, kb, vb, off); }
 
 /* IEEE binary32 -> binary16 bits, round to nearest, ties to even (overflow
  * to infinity, NaN stays NaN), and back (exact). */
@@ -261,7 +281,7 @@ typedef struct {
 
 static void compress_one(const float* src, long long tok_stride, int d, int iters,
                          float* r, float* s, uint8_t* z, float* lo, float* dl,
-                         int is_key) {
+                         int is_key, int levels) {
   float* X = (float*)malloc(sizeof(float) * TILE * d);
   float* Xn = (float*)malloc(sizeof(float) * TILE * d);
   for (int t = 0; t < TILE; t++) {
@@ -271,15 +291,15 @@ static void compress_one(const float* src, long long tok_stride, int d, int iter
   oracle_sinkhorn_f32(X, d, iters, r, s);
   oracle_normalise_f32(X, d, r, s, Xn);
   if (is_key) {
-    /* per channel over the tile's 128 tokens, 4 bits */
+    /* per channel over the tile's 128 tokens */
     for (int c = 0; c < d; c++)
-      oracle_rtn_group(Xn + c, TILE, d, 15, &lo[c], &dl[c], z + c, d);
+      oracle_rtn_group(Xn + c, TILE, d, levels, &lo[c], &dl[c], z + c, d);
   } else {
-    /* per token over each group of 128 channels, 2 bits */
+    /* per token over each group of 128 channels */
     int ng = d / 128;
     for (int t = 0; t < TILE; t++)
       for (int g = 0; g < ng; g++)
-        oracle_rtn_group(Xn + t * d + 128 * g, 128, 1, 3, &lo[t * ng + g],
+        oracle_rtn_group(Xn + t * d + 128 * g, 128, 1, levels, &lo[t * ng + g],
                          &dl[t * ng + g], z + t * d + 128 * g, 1);
   }
   free(X);
@@ -295,33 +315,18 @@ static void put_scale(uint8_t* rec, long long off, int i, float v, int fmt) {
   }
 }
 
-/* Compress the K and V tiles of one (tile, kv head).  k and v point at token
- * 0 channel 0; token t starts tok_stride floats later.  Writes
- * oracle_tile_bytes_fmt(d, fmt) bytes to rec.  Returns 0 on success, -1 for
- * an unsupported head_dim or format. */
-int oracle_compress_tile_fmt(const float* k, const float* v, long long tok_stride,
-                             int d, int iters, int fmt, uint8_t* rec) {
-  if (!valid_dim(d) || (fmt != 0 && fmt != 1)) return -1;
+/* Everything the compressor decides for one tile-head: RTN with 2^kb - 1
+ * levels for the keys and 2^vb - 1 for the values.  Caller frees. */
+static tile_parts* tile_decide(const float* k, const float* v, long long tok_stride, int d,
+                               int iters, int kb, int vb) {
   tile_parts* P = (tile_parts*)calloc(1, sizeof(tile_parts));
-  compress_one(k, tok_stride, d, iters, P->rK, P->sK, P->zK, P->loK, P->dK, 1);
-  compress_one(v, tok_stride, d, iters, P->rV, P->sV, P->zV, P->loV, P->dV, 0);
+  compress_one(k, tok_stride, d, iters, P->rK, P->sK, P->zK, P->loK, P->dK, 1, (1 << kb) - 1);
+  compress_one(v, tok_stride, d, iters, P->rV, P->sV, P->zV, P->loV, P->dV, 0, (1 << vb) - 1);
+  return P;
+}
 
-  long long off[9];
-  layout_fmt(d, fmt, off);
-  memset(rec, 0, (size_t)off[8]);
-  /* K codes, channel-major: byte j of channel c = tokens 2j (low), 2j+1 (high) */
-  for (int c = 0; c < d; c++)
-    for (int j = 0; j < TILE / 2; j++)
-      rec[off[0] + 64LL * c + j] =
-          (uint8_t)(P->zK[(2 * j) * d + c] | (P->zK[(2 * j + 1) * d + c] << 4));
-  /* V codes, token-major: byte j of token t = channels 4j+i at bits 2i */
-  for (int t = 0; t < TILE; t++)
-    for (int j = 0; j < d / 4; j++) {
-      int b = 0;
-      for (int i = 0; i < 4; i++) b |= P->zV[t * d + 4 * j + i] << (2 * i);
-      rec[off[1] + (long long)t * (d / 4) + j] = (uint8_t)b;
-    }
-  /* folded scales: single fp32 multiplies */
+/* folded scales: single fp32 multiplies */
+static void put_scales(uint8_t* rec, const long long off[9], const tile_parts* P, int d, int fmt) {
   for (int t = 0; t < TILE; t++) put_scale(rec, off[2], t, P->rK[t], fmt);
   for (int c = 0; c < d; c++) {
     put_scale(rec, off[3], c, P->dK[c] * P->sK[c], fmt);
@@ -334,6 +339,60 @@ int oracle_compress_tile_fmt(const float* k, const float* v, long long tok_strid
       put_scale(rec, off[6], t * ng + g, P->dV[t * ng + g] * P->rV[t], fmt);
       put_scale(rec, off[7], t * ng + g, P->loV[t * ng + g] * P->rV[t], fmt);
     }
+}
+
+/* K4V2 packing, nibble by nibble and crumb by crumb. */
+static void pack_k4v2(uint8_t* rec, const long long off[9], const tile_parts* P, int d) {
+  /* K codes, channel-major: byte j of channel c = tokens 2j (low), 2j+1 (high) */
+  for (int c = 0; c < d; c++)
+    for (int j = 0; j < TILE / 2; j++)
+      rec[off[0] + 64LL * c + j] =
+          (uint8_t)(P->zK[(2 * j) * d + c] | (P->zK[(2 * j + 1) * d + c] << 4));
+  /* V codes, token-major: byte j of token t = channels 4j+i at bits 2i */
+  for (int t = 0; t < TILE; t++)
+    for (int j = 0; j < d / 4; j++) {
+      int b = 0;
+      for (int i = 0; i < 4; i++) b |= P->zV[t * d + 4 * j + i] << (2 * i);
+      rec[off[1] + (long long)t * (d / 4) + j] = (uint8_t)b;
+    }
+}
+
+/* Any widths: a b-bit code goes one bit at a time into an LSB-first stream
+ * (bit i of the stream is bit i % 8 of byte i / 8). */
+static void put_code(uint8_t* stream, long long bit0, int b, unsigned code) {
+  for (int i = 0; i < b; i++)
+    if ((code >> i) & 1u) stream[(bit0 + i) >> 3] |= (uint8_t)(1u << ((bit0 + i) & 7));
+}
+static unsigned get_code(const uint8_t* stream, long long bit0, int b) {
+  unsigned code = 0;
+  for (int i = 0; i < b; i++) code |= (unsigned)((stream[(bit0 + i) >> 3] >> ((bit0 + i) & 7)) & 1u) << i;
+  return code;
+}
+static void pack_bits(uint8_t* rec, const long long off[9], const tile_parts* P, int d, int kb,
+                      int vb) {
+  /* K: channel c's stream of 16 kb bytes, token t at bit kb t */
+  for (int c = 0; c < d; c++)
+    for (int t = 0; t < TILE; t++)
+      put_code(rec + off[0] + 16LL * kb * c, (long long)kb * t, kb, P->zK[t * d + c]);
+  /* V: token t's stream of d vb / 8 bytes, channel c at bit vb c */
+  for (int t = 0; t < TILE; t++)
+    for (int c = 0; c < d; c++)
+      put_code(rec + off[1] + (long long)t * d * vb / 8, (long long)vb * c, vb, P->zV[t * d + c]);
+}
+
+/* Compress the K and V tiles of one (tile, kv head).  k and v point at token
+ * 0 channel 0; token t starts tok_stride floats later.  Writes
+ * oracle_tile_bytes_fmt(d, fmt) bytes to rec.  Returns 0 on success, -1 for
+ * an unsupported head_dim or format. */
+int oracle_compress_tile_fmt(const float* k, const float* v, long long tok_stride,
+                             int d, int iters, int fmt, uint8_t* rec) {
+  if (!valid_dim(d) || (fmt != 0 && fmt != 1)) return -1;
+  tile_parts* P = tile_decide(k, v, tok_stride, d, iters, 4, 2);
+  long long off[9];
+  layout_fmt(d, fmt, off);
+  memset(rec, 0, (size_t)off[8]);
+  pack_k4v2(rec, off, P, d);
+  put_scales(rec, off, P, d, fmt);
   free(P);
   return 0;
 }
@@ -343,7 +402,22 @@ int oracle_compress_tile(const float* k, const float* v, long long tok_stride,
   return oracle_compress_tile_fmt(k, v, tok_stride, d, iters, 0, rec);
 }
 
-/* The unpacked codes of a record: zK[t][c] and zV[t][c]. */
+/* The same with kb-bit keys and vb-bit values, packed by the bit-stream
+ * writer.  Writes oracle_tile_bytes_w(d, fmt, kb, vb) bytes. */
+int oracle_compress_tile_w(const float* k, const float* v, long long tok_stride, int d,
+                           int iters, int fmt, int kb, int vb, uint8_t* rec) {
+  if (!oracle_tile_bytes_w(d, fmt, kb, vb)) return -1;
+  tile_parts* P = tile_decide(k, v, tok_stride, d, iters, kb, vb);
+  long long off[9];
+  layout_w(d, fmt, kb, vb, off);
+  memset(rec, 0, (size_t)off[8]);
+  pack_bits(rec, off, P, d, kb, vb);
+  put_scales(rec, off, P, d, fmt);
+  free(P);
+  return 0;
+}
+
+/* The unpacked codes of a K4V2 record: zK[t][c] and zV[t][c]. */
 void oracle_unpack_codes(const uint8_t* rec, int d, uint8_t* zK, uint8_t* zV) {
   long long off[9];
   layout(d, off);
@@ -358,6 +432,18 @@ void oracle_unpack_codes(const uint8_t* rec, int d, uint8_t* zK, uint8_t* zV) {
       uint8_t b = rec[off[1] + (long long)t * (d / 4) + c / 4];
       zV[t * d + c] = (b >> (2 * (c % 4))) & 3;
     }
+}
+
+/* The unpacked codes of a record with kb-bit keys and vb-bit values. */
+void oracle_unpack_codes_w(const uint8_t* rec, int d, int kb, int vb, uint8_t* zK, uint8_t* zV) {
+  long long off[9];
+  layout_w(d, 0, kb, vb, off);   /* code sections do not depend on the scale format */
+  for (int c = 0; c < d; c++)
+    for (int t = 0; t < TILE; t++)
+      zK[t * d + c] = (uint8_t)get_code(rec + off[0] + 16LL * kb * c, (long long)kb * t, kb);
+  for (int t = 0; t < TILE; t++)
+    for (int c = 0; c < d; c++)
+      zV[t * d + c] = (uint8_t)get_code(rec + off[1] + (long long)t * d * vb / 8, (long long)vb * c, vb);
 }
 
 /* ------------------------------------------------------------------ */
@@ -389,19 +475,15 @@ static void hadamard_f64(const double* x, double* y, int d) {
   }
 }
 
-/* Dequantise one record to the raw (unrotated) domain:
+/* Dequantise one record to the raw (unrotated) domain from its codes:
  *   k'[t][c] = ktok[t] * (zK[t][c] * kscale[c] + kmin[c])
  *   v'[t][c] = vchan[c] * (zV[t][c] * vscale[t][g] + vmin[t][g])
  *   khat = H k', vhat = H v'  (H is its own inverse)
  * If rotated_only is nonzero the rotation is skipped (k', v' are returned). */
-void oracle_dequant_f64_fmt(const uint8_t* rec, int d, int fmt, int rotated_only,
-                            double* khat, double* vhat) {
-  long long off[9];
-  layout_fmt(d, fmt, off);
-  uint8_t* zK = (uint8_t*)malloc((size_t)TILE * d);
-  uint8_t* zV = (uint8_t*)malloc((size_t)TILE * d);
+static void dequant_codes(const uint8_t* rec, const long long off[9], int d, int fmt,
+                          const uint8_t* zK, const uint8_t* zV, int rotated_only,
+                          double* khat, double* vhat) {
   double* row = (double*)malloc(sizeof(double) * d);
-  oracle_unpack_codes(rec, d, zK, zV);
   int ng = d / 128;
   for (int t = 0; t < TILE; t++) {
     double ktok = get_scale(rec, off[2], t, fmt);
@@ -419,11 +501,33 @@ void oracle_dequant_f64_fmt(const uint8_t* rec, int d, int fmt, int rotated_only
     if (rotated_only) memcpy(vhat + (long long)t * d, row, sizeof(double) * d);
     else hadamard_f64(row, vhat + (long long)t * d, d);
   }
-  free(zK); free(zV); free(row);
+  free(row);
+}
+
+void oracle_dequant_f64_fmt(const uint8_t* rec, int d, int fmt, int rotated_only,
+                            double* khat, double* vhat) {
+  long long off[9];
+  layout_fmt(d, fmt, off);
+  uint8_t* zK = (uint8_t*)malloc((size_t)TILE * d);
+  uint8_t* zV = (uint8_t*)malloc((size_t)TILE * d);
+  oracle_unpack_codes(rec, d, zK, zV);
+  dequant_codes(rec, off, d, fmt, zK, zV, rotated_only, khat, vhat);
+  free(zK); free(zV);
 }
 
 void oracle_dequant_f64(const uint8_t* rec, int d, int rotated_only, double* khat, double* vhat) {
   oracle_dequant_f64_fmt(rec, d, 0, rotated_only, khat, vhat);
+}
+
+void oracle_dequant_f64_w(const uint8_t* rec, int d, int fmt, int kb, int vb, int rotated_only,
+                          double* khat, double* vhat) {
+  long long off[9];
+  layout_w(d, fmt, kb, vb, off);
+  uint8_t* zK = (uint8_t*)malloc((size_t)TILE * d);
+  uint8_t* zV = (uint8_t*)malloc((size_t)TILE * d);
+  oracle_unpack_codes_w(rec, d, kb, vb, zK, zV);
+  dequant_codes(rec, off, d, fmt, zK, zV, rotated_only, khat, vhat);
+  free(zK); free(zV);
 }
 
 /* ------------------------------------------------------------------ */

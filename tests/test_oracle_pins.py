@@ -488,3 +488,93 @@ def test_f16_record_dequant_within_half_rounding_of_f32_record():
     assert np.all(np.abs(k16 - k32) <= eps * magk)
     assert np.all(np.abs(v16 - v32) <= eps * magv)
     assert np.any(k16 != k32)
+
+
+# --------------------------------------------------------------------------
+# configurable key / value widths (gmlx PR #116 commit list: k6v5-style arms)
+# --------------------------------------------------------------------------
+
+WIDTHS = [(6, 5), (3, 1), (8, 8), (2, 3), (5, 4), (1, 7)]
+
+
+@pytest.mark.parametrize("d", [128, 256, 512])
+@pytest.mark.parametrize("f16", [False, True])
+def test_bit_stream_packer_and_reader_agree_with_the_k4v2_nibble_code(d, f16):
+    """At 4/2 bits the LSB-first bit stream is the nibble / crumb record: the
+    bit-level writer and reader reproduce the hand-packed bytes and codes."""
+    K, V = synth.make_kv(90 + d, 128, 1, d, 4)
+    r = oracle.compress_tile(K[:, 0], V[:, 0], f16=f16)
+    assert np.array_equal(oracle.compress_tile_bits(K[:, 0], V[:, 0], f16=f16), r)
+    a, b = oracle.unpack_codes(r, d), oracle.unpack_codes_bits(r, d)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_width_record_sizes_closed_form():
+    for d in (128, 256, 512):
+        for kb in range(1, 9):
+            for vb in range(1, 9):
+                codes = 128 * d * (kb + vb) // 8
+                assert oracle.tile_bytes(d, False, kb, vb) == codes + 4 * (128 + 5 * d)
+                assert oracle.tile_bytes(d, True, kb, vb) == codes + 2 * (128 + 5 * d)
+        assert oracle.tile_bytes(d, False, 0, 2) == 0 and oracle.tile_bytes(d, False, 4, 9) == 0
+    assert oracle.tile_bytes(128, False, 4, 2) == 116 * 128 + 512
+
+
+@pytest.mark.parametrize("kb,vb", WIDTHS)
+def test_width_codes_are_little_endian_bit_streams(kb, vb):
+    """Rebuild both code sections from the codes with Python integers: key
+    channel c is sum_t zK[t][c] 2^(kb t), value token t is sum_c zV[t][c]
+    2^(vb c), each stored little-endian."""
+    d = 256
+    K, V = synth.make_kv(7 * kb + vb, 128, 1, d, 4)
+    rec = oracle.compress_tile(K[:, 0], V[:, 0], kbits=kb, vbits=vb)
+    off = oracle.layout(d, False, kb, vb)
+    zK, zV = oracle.unpack_codes(rec, d, kb, vb)
+    for c in (0, 1, 77, d - 1):
+        n = sum(int(zK[t, c]) << (kb * t) for t in range(128))
+        want = n.to_bytes(16 * kb, "little")
+        assert bytes(rec[off["kcode"] + 16 * kb * c: off["kcode"] + 16 * kb * (c + 1)]) == want
+    for t in (0, 5, 127):
+        n = sum(int(zV[t, c]) << (vb * c) for c in range(d))
+        lo = off["vcode"] + t * d * vb // 8
+        assert bytes(rec[lo: lo + d * vb // 8]) == n.to_bytes(d * vb // 8, "little")
+    assert off["ktok"] == 16 * d * (kb + vb)
+
+
+@pytest.mark.parametrize("kb,vb", WIDTHS)
+def test_width_rtn_uses_every_level_and_stays_within_half_a_step(kb, vb):
+    """RTN with 2^b - 1 levels: every key channel and value token group holds
+    code 0 (its minimum) and code 2^b - 1 (its maximum); every dequantised
+    element of the rotated tile is within half a step (r s delta / 2) of the
+    rotated input."""
+    d = 128
+    K, V = synth.make_kv(11 * kb + vb, 128, 1, d, 4)
+    rec = oracle.compress_tile(K[:, 0], V[:, 0], kbits=kb, vbits=vb)
+    zK, zV = oracle.unpack_codes(rec, d, kb, vb)
+    assert np.all(zK.min(axis=0) == 0) and np.all(zK.max(axis=0) == 2 ** kb - 1)
+    assert np.all(zV.min(axis=1) == 0) and np.all(zV.max(axis=1) == 2 ** vb - 1)
+    s = oracle.record_scales(rec, d, False, kb, vb)
+    kd, vd = oracle.dequant_rotated(rec, d, False, kb, vb)
+    Xk = oracle.wht_f32(K[:, 0]).astype(np.float64)
+    Xv = oracle.wht_f32(V[:, 0]).astype(np.float64)
+    stepk = s["ktok"][:, None].astype(np.float64) * s["kscale"][None].astype(np.float64)
+    stepv = s["vchan"][None].astype(np.float64) * s["vscale"][:, :1].astype(np.float64)
+    assert np.all(np.abs(kd - Xk) <= 0.5 * stepk * (1 + 1e-4) + 1e-6 * np.abs(Xk))
+    assert np.all(np.abs(vd - Xv) <= 0.5 * stepv * (1 + 1e-4) + 1e-6 * np.abs(Xv))
+
+
+def test_width_error_falls_with_every_added_bit():
+    """Each extra bit roughly halves the step: the relative L2 error of the
+    dequantised keys and values falls by more than 1.5x per bit."""
+    d = 128
+    K, V = synth.make_kv(123, 128, 1, d, 4)
+    Xk = oracle.wht_f32(K[:, 0]).astype(np.float64)
+    Xv = oracle.wht_f32(V[:, 0]).astype(np.float64)
+    ek, ev = [], []
+    for b in range(1, 9):
+        rec = oracle.compress_tile(K[:, 0], V[:, 0], kbits=b, vbits=b)
+        kd, vd = oracle.dequant_rotated(rec, d, False, b, b)
+        ek.append(np.linalg.norm(kd - Xk) / np.linalg.norm(Xk))
+        ev.append(np.linalg.norm(vd - Xv) / np.linalg.norm(Xv))
+    for i in range(1, 8):
+        assert ek[i] < ek[i - 1] / 1.5 and ev[i] < ev[i - 1] / 1.5, (i, ek, ev)
