@@ -98,12 +98,13 @@ def graph_ms(torch, fn, n_inner, reps):
     return s.elapsed_time(e) / (reps * n_inner), g
 
 
-def decode_case(torch, kvarn, synth, ctx, steps, warmup, seed=2, f16=False):
+def decode_case(torch, kvarn, synth, ctx, steps, warmup, seed=2, f16=False, kbits=4, vbits=2):
     d, Hq, Hkv, W = 128, 32, 8, 256
     dev = "cuda:0"
     T = kvarn.visible_tiles(ctx - 1, W)
     n_w = ctx - 128 * T
-    tb = kvarn.tile_bytes(d, f16)
+    tb = kvarn.tile_bytes(d, f16, kbits, vbits)
+    k4v2 = (kbits, vbits) == (4, 2)
     scale = 1.0 / math.sqrt(d)
     per_layer = T * Hkv * tb + 2 * n_w * Hkv * d * 4
     L = max(8, int(math.ceil(2 * LLC_BYTES / per_layer)))
@@ -111,22 +112,28 @@ def decode_case(torch, kvarn, synth, ctx, steps, warmup, seed=2, f16=False):
     kd = torch.from_numpy(K).to(dev)
     vd = torch.from_numpy(V).to(dev)
     rec0 = torch.empty(T, Hkv, tb, dtype=torch.uint8, device=dev)
-    kvarn.compress_tile(kd, vd, rec0, T, f16_scales=f16)
+    kvarn.compress_tile(kd, vd, rec0, T, f16_scales=f16, kbits=kbits, vbits=vbits)
     recs = [rec0.clone() for _ in range(L)]
     kw = [kd[128 * T:].clone()[None] for _ in range(L)]
     vw = [vd[128 * T:].clone()[None] for _ in range(L)]
     qs = torch.from_numpy(synth.make_q(seed, L, Hq, d)).to(dev).reshape(L, 1, Hq, d)
     outs = torch.empty_like(qs)
-    ws_bytes = kvarn.decode_workspace_bytes(qs[0], None, recs[0], [0], [T], kw[0], vw[0], [n_w], scale,
-                                            f16_scales=f16)
+    qr = torch.empty_like(qs[0])
+    ws_bytes = kvarn.decode_workspace_bytes(qs[0], None if k4v2 else qr, recs[0], [0], [T], kw[0], vw[0],
+                                            [n_w], scale, f16_scales=f16, kbits=kbits, vbits=vbits)
     ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
     def run():
         for l in range(L):
-            # q_rot=None: the split kernel rotates q itself
-            kvarn.decode_attention(qs[l], None, recs[l], [0], [T], kw[l], vw[l], [n_w], scale,
-                                   out=outs[l], workspace=ws, f16_scales=f16)
+            if k4v2:   # q_rot=None: the split kernel rotates q itself
+                kvarn.decode_attention(qs[l], None, recs[l], [0], [T], kw[l], vw[l], [n_w], scale,
+                                       out=outs[l], workspace=ws, f16_scales=f16)
+            else:      # the vector-unit kernels take a rotated query
+                kvarn.rotate_query(qs[l], out=qr)
+                kvarn.decode_attention(qs[l], qr, recs[l], [0], [T], kw[l], vw[l], [n_w], scale,
+                                       out=outs[l], workspace=ws, f16_scales=f16, kbits=kbits,
+                                       vbits=vbits)
 
     reps = max(1, int(math.ceil(steps / L)))
     warm = max(1, int(math.ceil(warmup / L)))
@@ -143,7 +150,8 @@ def decode_case(torch, kvarn, synth, ctx, steps, warmup, seed=2, f16=False):
     ms = s.elapsed_time(e) / (reps * L)
     alg = decode_bytes(T, n_w, Hq, Hkv, d, tb)
     info = {"context": ctx, "tiles": T, "window": n_w, "scales": "f16" if f16 else "f32",
-            "record_bytes": tb, "layers_cycled": L, "us_per_step": ms * 1e3,
+            "key_bits": kbits, "value_bits": vbits, "record_bytes": tb, "layers_cycled": L,
+            "us_per_step": ms * 1e3,
             "kv_tokens_per_s": ctx / (ms * 1e-3), "algorithmic_bytes": alg,
             "achieved_GBps": alg / (ms * 1e-3) / 1e9}
     return info, reps * L, warm * L, (K, V, rec0, T, n_w, qs, scale)
@@ -265,6 +273,12 @@ def main():
         dec16, _, _, _ = decode_case(torch, kvarn, synth, args.context, 320, 32, f16=True)
         log(f"decode context {args.context}, f16 scales: {dec16['us_per_step']:.2f} us per call, "
             f"{dec16['achieved_GBps']:.0f} GB/s algorithmic")
+    # ---- and over K6V5 records (vector-unit kernels, query rotation in the step) ----
+    dec65 = None
+    if not args.no_extra_contexts:
+        dec65, _, _, _ = decode_case(torch, kvarn, synth, args.context, 160, 16, kbits=6, vbits=5)
+        log(f"decode context {args.context}, 6-bit keys / 5-bit values: {dec65['us_per_step']:.2f} us "
+            f"per call, {dec65['achieved_GBps']:.0f} GB/s algorithmic")
 
     # ---- multi-query verify (width 8) at the same context ----
     verify = verify_case(torch, kvarn, synth, args.context, 8)
@@ -358,6 +372,7 @@ def main():
         "hbm_GBps": achieved,
         "decode_contexts": [head] + extra,
         "decode_f16_scales": dec16,
+        "decode_k6v5": dec65,
         "prefill": prefill,
         "prefill_wide_heads": prefill_wide,
         "verify": verify,

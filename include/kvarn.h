@@ -49,6 +49,19 @@
  * d = 128 instead of 120).  The codes are those of the fp32 record: only the
  * stored scales are rounded.
  *
+ * Code widths (gmlx PR #116 commit list: mixed-width "k6v5"-style arms, key
+ * and value widths set on their own): a head_dim argument OR-ed with
+ * KVARN_KEY_BITS(kb) and KVARN_VALUE_BITS(vb), 1 <= kb, vb <= 8, selects RTN
+ * with 2^kb - 1 key levels and 2^vb - 1 value levels.  The code sections become
+ * LSB-first bit streams: key channel c's stream is 16*kb bytes at 16*kb*c with
+ * token t at bit kb*t; value token t's stream is d*vb/8 bytes at 16*kb*d +
+ * t*d*vb/8 with channel c at bit vb*c (for kb = 4, vb = 2: the layout above).
+ * The six scale sections follow at 16*d*(kb+vb) in the same order, so the
+ * record is 16*d*(kb+vb) + 20*d + 512 bytes (10*d + 256 with f16 scales).
+ * Only K4V2 records at head_dim 128 run on the matrix units; other widths run
+ * decode and prefill on the vector-unit kernels (a q_rot is then required,
+ * prefill needs a workspace, and multi-query verify is unsupported).
+ *
  * FP32 window and promotion (PR #434 commit list: "the FP32 window is the
  * staging; whole-tile promotion"): with a window of W tokens, the oldest 128
  * raw tokens are compressed into one tile when the window reaches W+128, so
@@ -69,13 +82,17 @@ extern "C" {
 #define KVARN_MAX_BATCH 64
 /* OR into any head_dim argument: records carry f16 scales (see above). */
 #define KVARN_SCALES_F16 0x10000
+/* OR into any head_dim argument: key / value code widths 1..8 (see above);
+ * a zero field means the default (4-bit keys, 2-bit values). */
+#define KVARN_KEY_BITS(b) (((b) & 0xF) << 20)
+#define KVARN_VALUE_BITS(b) (((b) & 0xF) << 24)
 
 typedef enum kvarn_status {
   KVARN_OK = 0,
   KVARN_E_INVALID = 1,     /* null pointer, negative or inconsistent sizes   */
-  KVARN_E_UNSUPPORTED = 2, /* head_dim not 128/256/512 (with or without
-                              KVARN_SCALES_F16), GQA not integral, or a size
-                              beyond a documented limit                      */
+  KVARN_E_UNSUPPORTED = 2, /* head_dim not 128/256/512 (with or without the
+                              format flags), a code width above 8, GQA not
+                              integral, or a size beyond a documented limit  */
   KVARN_E_ALIGN = 3,       /* pointer or stride not 16-byte aligned          */
   KVARN_E_WORKSPACE = 4,   /* workspace missing or smaller than required     */
   KVARN_E_DEVICE = 5       /* HIP reported an error at launch                */
@@ -85,8 +102,9 @@ typedef enum kvarn_status {
 const char* kvarn_status_string(int status);
 
 /* Bytes of one (tile, KV head) record: 116*d + 512 (106*d + 256 with
- * KVARN_SCALES_F16), d = head_dim without the flag; 0 when d is not 128, 256
- * or 512 or another bit is set. */
+ * KVARN_SCALES_F16), d = head_dim without the flags; 16*d*(kb+vb) + 20*d + 512
+ * (+ 10*d + 256 with f16 scales) for other code widths; 0 when d is not 128,
+ * 256 or 512, a width is above 8, or an unknown bit is set. */
 size_t kvarn_tile_bytes(int32_t head_dim);
 
 /*
@@ -136,8 +154,8 @@ int kvarn_rotate_query(int32_t head_dim, int64_t n_rows, const float* q,
  * in the original domain.
  */
 typedef struct kvarn_decode_args {
-  int32_t head_dim;        /* 128, 256 or 512, | KVARN_SCALES_F16 for records
-                              with f16 scales                                   */
+  int32_t head_dim;        /* 128, 256 or 512, | KVARN_SCALES_F16 (f16 scales),
+                              | KVARN_KEY_BITS / KVARN_VALUE_BITS (widths)      */
   int32_t batch;           /* 1..KVARN_MAX_BATCH sequences                      */
   int32_t n_q_heads;       /* multiple of n_kv_heads                            */
   int32_t n_kv_heads;
@@ -145,8 +163,8 @@ typedef struct kvarn_decode_args {
   int32_t max_tiles;       /* grid bound: >= n_tiles[b] for every b             */
   const float* q;          /* device [batch][n_q_heads][head_dim] raw query     */
   const float* q_rot;      /* device [batch][n_q_heads][head_dim] rotated query;
-                              may be NULL when head_dim is 128: the kernel then
-                              rotates q itself                                  */
+                              may be NULL at head_dim 128 with K4V2 records:
+                              the kernel then rotates q itself                  */
   const void* records;     /* device record pool; record (b, j, h) at
                               ((rec_start[b] + j)*n_kv_heads + h)*tile_bytes    */
   int64_t n_record_rows;   /* rows in the pool (a row = n_kv_heads records)     */
@@ -164,7 +182,8 @@ typedef struct kvarn_decode_args {
   int32_t max_win;         /* grid bound: >= n_win[b] for every b               */
   float* out;              /* device [batch][n_q_heads][head_dim]               */
   int32_t q_len;           /* query rows per sequence, 0 or 1: one decode query;
-                              2..8: multi-query verify (head_dim 128).  Then q,
+                              2..8: multi-query verify (head_dim 128, K4V2
+                              records).  Then q,
                               q_rot and out are [batch][q_len][n_q_heads][head_dim]
                               and row i of sequence b is the query of window token
                               n_win[b] - q_len + i: it sees the n_tiles[b] tiles
@@ -185,7 +204,7 @@ size_t kvarn_decode_workspace_bytes(const kvarn_decode_args* args);
  * max_tiles, n_win[b] > max_win, win_start[b] < 0, q_len outside 0..8,
  * n_win[b] < q_len), KVARN_E_UNSUPPORTED (head_dim, GQA ratio, batch >
  * KVARN_MAX_BATCH, group of more than 8 query heads per KV head, q_len >= 2
- * with head_dim other than 128),
+ * with head_dim other than 128 or with other code widths),
  * KVARN_E_ALIGN, KVARN_E_WORKSPACE. */
 int kvarn_decode_attention(const kvarn_decode_args* args, void* workspace,
                            size_t workspace_bytes, void* stream);
@@ -202,13 +221,14 @@ int kvarn_decode_attention(const kvarn_decode_args* args, void* workspace,
  * the prompt is chunked).  The caller compresses every tile the chunk makes
  * due (tiles < T(pos0+C-1)) before this call.
  *
- * head_dim 128 runs on the matrix units; head_dim 256 and 512 (issue #433
- * item 3: prefill at the wider heads) run every chunk row as a vector-unit
- * split decode query with that view and need a workspace for the partials.
+ * head_dim 128 over K4V2 records runs on the matrix units; head_dim 256 and
+ * 512 (issue #433 item 3: prefill at the wider heads) and records with other
+ * code widths run every chunk row as a vector-unit split decode query with
+ * that view and need a workspace for the partials.
  */
 typedef struct kvarn_prefill_args {
-  int32_t head_dim;        /* 128, 256 or 512, | KVARN_SCALES_F16 for records
-                              with f16 scales                                   */
+  int32_t head_dim;        /* 128, 256 or 512, | KVARN_SCALES_F16 (f16 scales),
+                              | KVARN_KEY_BITS / KVARN_VALUE_BITS (widths)      */
   int32_t n_q_heads;
   int32_t n_kv_heads;
   int32_t window;          /* W of the promotion rule, >= 0                     */

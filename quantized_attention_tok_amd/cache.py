@@ -17,12 +17,13 @@ TILE = 128
 
 class SequenceCache:
     def __init__(self, n_kv: int, head_dim: int, window: int, capacity: int,
-                 device: str | torch.device = "cuda", f16_scales: bool = False):
+                 device: str | torch.device = "cuda", f16_scales: bool = False,
+                 kbits: int = 4, vbits: int = 2):
         self.n_kv, self.d, self.window = n_kv, head_dim, window
-        self.f16_scales = f16_scales
+        self.f16_scales, self.kbits, self.vbits = f16_scales, kbits, vbits
         self.k = torch.empty(capacity, n_kv, head_dim, dtype=torch.float32, device=device)
         self.v = torch.empty_like(self.k)
-        self.records = torch.empty(capacity // TILE + 1, n_kv, kvarn.tile_bytes(head_dim, f16_scales),
+        self.records = torch.empty(capacity // TILE + 1, n_kv, kvarn.tile_bytes(head_dim, f16_scales, kbits, vbits),
                                    dtype=torch.uint8, device=device)
         self.n_tokens = 0
         self.n_tiles = 0
@@ -50,6 +51,7 @@ class SequenceCache:
         if new > 0:
             lo = TILE * self.n_tiles
             kvarn.compress_tile(self.k[lo:], self.v[lo:], self.records[self.n_tiles:], new,
-                                stream=stream, f16_scales=self.f16_scales)
+                                stream=stream, f16_scales=self.f16_scales, kbits=self.kbits,
+                                vbits=self.vbits)
             self.n_tiles = due
         return max(new, 0)

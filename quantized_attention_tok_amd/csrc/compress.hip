@@ -84,17 +84,24 @@ __device__ __forceinline__ float code_of(float xn, float lo, float inv, float le
   return z;
 }
 
-template <int D, bool H>
+// GEN: kb-bit keys and vb-bit values (runtime widths, LSB-first bit streams);
+// otherwise the K4V2 record (kb, vb ignored).
+template <int D, bool H, bool GEN>
 __global__ void __launch_bounds__(2 * D)
 compress_kernel(const float* __restrict__ kin, const float* __restrict__ vin,
                 int64_t tok_stride, int64_t head_stride, int n_kv,
-                uint8_t* __restrict__ records) {
+                uint8_t* __restrict__ records, int kb, int vb) {
   constexpr int W = D / 32;        // waves
   constexpr int J = kTile / W;     // channel offsets per LDS exchange round
   constexpr bool kStoreQ = D <= 256;
   using R = Rec<D, H>;
+  if constexpr (!GEN) { kb = 4; vb = 2; }
+  const RecRT o = rec_rt(D, H, kb, vb);
 
-  __shared__ float smem[16384];    // 64 KB, reused by every phase
+  // 64 KB, reused by every phase; the generic key packing stages one byte per
+  // code after two per-channel vectors (34 D floats)
+  constexpr int kSmem = (GEN && 34 * D > 16384) ? 34 * D : 16384;
+  __shared__ float smem[kSmem];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -105,7 +112,7 @@ compress_kernel(const float* __restrict__ kin, const float* __restrict__ vin,
 
   const float* src = (is_key ? kin : vin) + (int64_t)job * kTile * tok_stride +
                      (int64_t)head * head_stride;
-  uint8_t* rec = records + ((int64_t)job * n_kv + head) * R::bytes;
+  uint8_t* rec = records + ((int64_t)job * n_kv + head) * o.bytes;
 
   // ---- load rows 2l, 2l+1, channels [32w, 32w+32) ----
   float x[2][32];
@@ -289,33 +296,60 @@ compress_kernel(const float* __restrict__ kin, const float* __restrict__ vin,
     }
     float lo = halve32(lo_a, lane, OpMin{}) + 0.0f;
     float hi = halve32(hi_a, lane, OpMax{}) + 0.0f;
-    float delta = (hi - lo) / 15.0f;
+    const float klev = GEN ? (float)((1 << kb) - 1) : 15.0f;
+    float delta = (hi - lo) / klev;
     float inv = (delta >= FLT_MIN) ? 1.0f / delta : 0.0f;
     if (owner) {
       bc_v[ch_own] = lo;
       bc_x[ch_own] = inv;
-      sc_st<H>(rec + R::kscale, ch_own, delta * s_own);
-      sc_st<H>(rec + R::kmin, ch_own, lo * s_own);
+      sc_st<H>(rec + o.kscale, ch_own, delta * s_own);
+      sc_st<H>(rec + o.kmin, ch_own, lo * s_own);
     }
     if (w == 0) {
-      sc_st<H>(rec + R::ktok, 2 * lane, r[0]);
-      sc_st<H>(rec + R::ktok, 2 * lane + 1, r[1]);
+      sc_st<H>(rec + o.ktok, 2 * lane, r[0]);
+      sc_st<H>(rec + o.ktok, 2 * lane + 1, r[1]);
     }
     __syncthreads();
-    uint8_t* kst = reinterpret_cast<uint8_t*>(smem + 2 * D);  // [D][64] bytes
+    if constexpr (GEN) {
+      uint8_t* kst = reinterpret_cast<uint8_t*>(smem + 2 * D);  // [D][128] one byte per code
 #pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      const float lj = bc_v[32 * w + j], ij = bc_x[32 * w + j];
-      int z0 = (int)code_of(x[0][j], lj, ij, 15.0f);
-      int z1 = (int)code_of(x[1][j], lj, ij, 15.0f);
-      kst[(32 * w + j) * 64 + lane] = (uint8_t)(z0 | (z1 << 4));
+      for (int j = 0; j < 32; ++j) {
+        const float lj = bc_v[32 * w + j], ij = bc_x[32 * w + j];
+        const int z0 = (int)code_of(x[0][j], lj, ij, klev);
+        const int z1 = (int)code_of(x[1][j], lj, ij, klev);
+        *reinterpret_cast<uint16_t*>(kst + (32 * w + j) * kTile + 2 * lane) = (uint16_t)(z0 | (z1 << 8));
+      }
+      __syncthreads();
+      // dword q of channel c's stream holds the codes whose bits meet [32 q, 32 q + 32)
+      const int per = 4 * kb;   // dwords per channel
+      uint32_t* dst = reinterpret_cast<uint32_t*>(rec + o.kcode);
+      for (int i = tid; i < D * per; i += 2 * D) {
+        const int c = i / per, q = i - c * per;
+        const int t0 = (32 * q) / kb, t1 = (32 * q + 31) / kb;
+        uint32_t acc = 0;
+        for (int t = t0; t <= t1; ++t) {
+          const int pos = kb * t - 32 * q;   // in (-kb, 32)
+          const uint32_t z = kst[c * kTile + t];
+          acc |= pos >= 0 ? (z << pos) : (z >> -pos);
+        }
+        dst[i] = acc;
+      }
+    } else {
+      uint8_t* kst = reinterpret_cast<uint8_t*>(smem + 2 * D);  // [D][64] bytes
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        const float lj = bc_v[32 * w + j], ij = bc_x[32 * w + j];
+        int z0 = (int)code_of(x[0][j], lj, ij, 15.0f);
+        int z1 = (int)code_of(x[1][j], lj, ij, 15.0f);
+        kst[(32 * w + j) * 64 + lane] = (uint8_t)(z0 | (z1 << 4));
+      }
+      __syncthreads();
+      // coalesced copy of the D*64 code bytes: 32 bytes per thread
+      const uint4* s4 = reinterpret_cast<const uint4*>(kst);
+      uint4* d4 = reinterpret_cast<uint4*>(rec + R::kcode);
+#pragma unroll
+      for (int q = 0; q < 2; ++q) d4[tid * 2 + q] = s4[tid * 2 + q];
     }
-    __syncthreads();
-    // coalesced copy of the D*64 code bytes: 32 bytes per thread
-    const uint4* s4 = reinterpret_cast<const uint4*>(kst);
-    uint4* d4 = reinterpret_cast<uint4*>(rec + R::kcode);
-#pragma unroll
-    for (int q = 0; q < 2; ++q) d4[tid * 2 + q] = s4[tid * 2 + q];
   } else {
     // ---- values: per token over each 128-channel group, 2 bits ----
     float* mm = smem + 2 * D;  // [W][128][2]
@@ -327,7 +361,7 @@ compress_kernel(const float* __restrict__ kin, const float* __restrict__ vin,
       mm[(w * kTile + 2 * lane + i) * 2 + 0] = lo;
       mm[(w * kTile + 2 * lane + i) * 2 + 1] = hi;
     }
-    if (owner) sc_st<H>(rec + R::vchan, ch_own, s_own);
+    if (owner) sc_st<H>(rec + o.vchan, ch_own, s_own);
     __syncthreads();
     const int g = w / 4;  // channel group of this wave
 #pragma unroll
@@ -342,18 +376,37 @@ compress_kernel(const float* __restrict__ kin, const float* __restrict__ vin,
       }
       lo = lo + 0.0f;
       hi = hi + 0.0f;
-      float delta = (hi - lo) / 3.0f;
+      const float vlev = GEN ? (float)((1 << vb) - 1) : 3.0f;
+      float delta = (hi - lo) / vlev;
       float inv = (delta >= FLT_MIN) ? 1.0f / delta : 0.0f;
-      uint32_t packed[2] = {0u, 0u};
+      if constexpr (GEN) {
+        // the wave's 32 channels fill dwords [w vb, w vb + vb) of token t's stream
+        uint32_t* dst = reinterpret_cast<uint32_t*>(rec + o.vcode + t * (D * vb / 8)) + w * vb;
+        uint64_t acc = 0;
+        int nb = 0, q = 0;
 #pragma unroll
-      for (int j = 0; j < 32; ++j) {
-        uint32_t z = (uint32_t)code_of(x[i][j], lo, inv, 3.0f);
-        packed[j / 16] |= z << (2 * (j % 16));
+        for (int j = 0; j < 32; ++j) {
+          const uint64_t z = (uint64_t)code_of(x[i][j], lo, inv, vlev);
+          acc |= z << nb;
+          nb += vb;
+          if (nb >= 32) {
+            dst[q++] = (uint32_t)acc;
+            acc >>= 32;
+            nb -= 32;
+          }
+        }
+      } else {
+        uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+          uint32_t z = (uint32_t)code_of(x[i][j], lo, inv, 3.0f);
+          packed[j / 16] |= z << (2 * (j % 16));
+        }
+        reinterpret_cast<uint2*>(rec + R::vcode + t * (D / 4) + 8 * w)[0] = make_uint2(packed[0], packed[1]);
       }
-      reinterpret_cast<uint2*>(rec + R::vcode + t * (D / 4) + 8 * w)[0] = make_uint2(packed[0], packed[1]);
       if ((w & 3) == 0) {
-        sc_st<H>(rec + R::vscale, t * R::groups + g, delta * r[i]);
-        sc_st<H>(rec + R::vmin, t * R::groups + g, lo * r[i]);
+        sc_st<H>(rec + o.vscale, t * R::groups + g, delta * r[i]);
+        sc_st<H>(rec + o.vmin, t * R::groups + g, lo * r[i]);
       }
     }
   }
@@ -362,24 +415,24 @@ compress_kernel(const float* __restrict__ kin, const float* __restrict__ vin,
 }  // namespace
 
 // Launch the compressor for n_tiles x n_kv tile-heads (keys and values);
-// h16: store the scales as f16.
-template <bool H>
-hipError_t launch_compress_h(int d, int n_tiles, int n_kv, const float* k, const float* v,
-                             int64_t tok_stride, int64_t head_stride, uint8_t* rec,
-                             hipStream_t stream) {
+// h16: store the scales as f16; kb / vb: key / value code widths.
+template <bool H, bool GEN>
+hipError_t launch_compress_hg(int d, int n_tiles, int n_kv, const float* k, const float* v,
+                              int64_t tok_stride, int64_t head_stride, uint8_t* rec, int kb,
+                              int vb, hipStream_t stream) {
   dim3 grid(n_tiles, n_kv, 2);
   switch (d) {
     case 128:
-      hipLaunchKernelGGL((compress_kernel<128, H>), grid, dim3(256), 0, stream, k, v, tok_stride,
-                         head_stride, n_kv, rec);
+      hipLaunchKernelGGL((compress_kernel<128, H, GEN>), grid, dim3(256), 0, stream, k, v,
+                         tok_stride, head_stride, n_kv, rec, kb, vb);
       break;
     case 256:
-      hipLaunchKernelGGL((compress_kernel<256, H>), grid, dim3(512), 0, stream, k, v, tok_stride,
-                         head_stride, n_kv, rec);
+      hipLaunchKernelGGL((compress_kernel<256, H, GEN>), grid, dim3(512), 0, stream, k, v,
+                         tok_stride, head_stride, n_kv, rec, kb, vb);
       break;
     case 512:
-      hipLaunchKernelGGL((compress_kernel<512, H>), grid, dim3(1024), 0, stream, k, v, tok_stride,
-                         head_stride, n_kv, rec);
+      hipLaunchKernelGGL((compress_kernel<512, H, GEN>), grid, dim3(1024), 0, stream, k, v,
+                         tok_stride, head_stride, n_kv, rec, kb, vb);
       break;
     default:
       return hipErrorInvalidValue;
@@ -387,12 +440,16 @@ hipError_t launch_compress_h(int d, int n_tiles, int n_kv, const float* k, const
   return hipGetLastError();
 }
 
-hipError_t launch_compress(int d, bool h16, int n_tiles, int n_kv, const float* k, const float* v,
-                           int64_t tok_stride, int64_t head_stride, void* records,
+hipError_t launch_compress(int d, bool h16, int kb, int vb, int n_tiles, int n_kv, const float* k,
+                           const float* v, int64_t tok_stride, int64_t head_stride, void* records,
                            hipStream_t stream) {
   uint8_t* rec = static_cast<uint8_t*>(records);
-  return h16 ? launch_compress_h<true>(d, n_tiles, n_kv, k, v, tok_stride, head_stride, rec, stream)
-             : launch_compress_h<false>(d, n_tiles, n_kv, k, v, tok_stride, head_stride, rec, stream);
+  const bool gen = !(kb == 4 && vb == 2);
+  if (h16)
+    return gen ? launch_compress_hg<true, true>(d, n_tiles, n_kv, k, v, tok_stride, head_stride, rec, kb, vb, stream)
+               : launch_compress_hg<true, false>(d, n_tiles, n_kv, k, v, tok_stride, head_stride, rec, kb, vb, stream);
+  return gen ? launch_compress_hg<false, true>(d, n_tiles, n_kv, k, v, tok_stride, head_stride, rec, kb, vb, stream)
+             : launch_compress_hg<false, false>(d, n_tiles, n_kv, k, v, tok_stride, head_stride, rec, kb, vb, stream);
 }
 
 }  // namespace kvarn

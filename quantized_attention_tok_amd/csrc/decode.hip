@@ -31,9 +31,13 @@ namespace {
 // ---------------------------------------------------------------------------
 // partial kernel: one (split, kv head, sequence)
 // ---------------------------------------------------------------------------
-template <int D, int G, bool H>
+// GEN: records with P.kb-bit keys and P.vb-bit values (LSB-first bit
+// streams); otherwise the K4V2 record.
+template <int D, int G, bool H, bool GEN>
 __global__ void __launch_bounds__(kDecThreads) decode_partial_kernel(DecodeParams P) {
-  using R = Rec<D, H>;
+  const int kb = GEN ? P.kb : 4, vb = GEN ? P.vb : 2;
+  const RecRT R = rec_rt(D, H, kb, vb);
+  const uint32_t kmask = (1u << kb) - 1u, vmask = (1u << vb) - 1u;
   constexpr int NG = D / 128;                 // value channel groups
   constexpr int HH = (G >= 2 && D == 128) ? 2 : 1;   // head halves (K: 128 tokens x HH)
   constexpr int GH = G / HH;                  // heads per thread in the K phase
@@ -57,7 +61,8 @@ __global__ void __launch_bounds__(kDecThreads) decode_partial_kernel(DecodeParam
   __shared__ float s_u[G][NG];                // sum p * vmin
   __shared__ float s_bias[G];
   __shared__ float s_m[G], s_l[G], s_alpha[G];
-  __shared__ __attribute__((aligned(16))) uint8_t s_code[64 * D];  // K codes, then V codes
+  // K codes, then V codes (+ 16 bytes: a code's second byte may be read past the end)
+  __shared__ __attribute__((aligned(16))) uint8_t s_code[(GEN ? 128 : 64) * D + 16];
   __shared__ float s_scale[3 * D + 128];      // kscale, kmin, ktok  |  vchan, vscale, vmin
 
   const SeqView sv = seq_view(P, b);
@@ -103,18 +108,18 @@ __global__ void __launch_bounds__(kDecThreads) decode_partial_kernel(DecodeParam
   __syncthreads();
 
   if (is_tile) {
-    const uint8_t* base = P.records + ((sv.rec_row0 + t_begin) * (int64_t)P.n_kv + kvh) * R::bytes;
-    for (int tile = t_begin; tile < t_end; ++tile, base += (int64_t)P.n_kv * R::bytes) {
+    const uint8_t* base = P.records + ((sv.rec_row0 + t_begin) * (int64_t)P.n_kv + kvh) * R.bytes;
+    for (int tile = t_begin; tile < t_end; ++tile, base += (int64_t)P.n_kv * R.bytes) {
       // ---- stage K codes and key scales ----
       {
-        const uint4* src = reinterpret_cast<const uint4*>(base + R::kcode);
+        const uint4* src = reinterpret_cast<const uint4*>(base + R.kcode);
         uint4* dst = reinterpret_cast<uint4*>(s_code);
-        for (int i = tid; i < 4 * D; i += kDecThreads) dst[i] = src[i];
+        for (int i = tid; i < kb * D; i += kDecThreads) dst[i] = src[i];
         for (int i = tid; i < D; i += kDecThreads) {
-          s_scale[i] = sc_ld<H>(base + R::kscale, i);
-          s_scale[D + i] = sc_ld<H>(base + R::kmin, i);
+          s_scale[i] = sc_ld<H>(base + R.kscale, i);
+          s_scale[D + i] = sc_ld<H>(base + R.kmin, i);
         }
-        if (tid < kTile) s_scale[2 * D + tid] = sc_ld<H>(base + R::ktok, tid);
+        if (tid < kTile) s_scale[2 * D + tid] = sc_ld<H>(base + R.ktok, tid);
       }
       __syncthreads();
       // q~ = q' * kscale and bias = q' . kmin
@@ -138,8 +143,15 @@ __global__ void __launch_bounds__(kDecThreads) decode_partial_kernel(DecodeParam
 #pragma unroll
           for (int h = 0; h < GH; ++h) sacc[h] = 0.0f;
           for (int c = 0; c < D; ++c) {
-            const uint32_t byte = s_code[c * 64 + (t >> 1)];
-            const float z = (float)((byte >> ((t & 1) * 4)) & 15u);
+            float z;
+            if constexpr (GEN) {   // token t of channel c's stream: bits [kb t, kb t + kb)
+              const int bit = kb * t;
+              const uint8_t* p = s_code + c * 16 * kb + (bit >> 3);
+              z = (float)((((uint32_t)p[0] | ((uint32_t)p[1] << 8)) >> (bit & 7)) & kmask);
+            } else {
+              const uint32_t byte = s_code[c * 64 + (t >> 1)];
+              z = (float)((byte >> ((t & 1) * 4)) & 15u);
+            }
 #pragma unroll
             for (int h = 0; h < GH; ++h) sacc[h] += s_qt[c][hh * GH + h] * z;
           }
@@ -154,13 +166,13 @@ __global__ void __launch_bounds__(kDecThreads) decode_partial_kernel(DecodeParam
       __syncthreads();
       // ---- stage V codes and value scales (K buffers are free) ----
       {
-        const uint4* src = reinterpret_cast<const uint4*>(base + R::vcode);
+        const uint4* src = reinterpret_cast<const uint4*>(base + R.vcode);
         uint4* dst = reinterpret_cast<uint4*>(s_code);
-        for (int i = tid; i < 2 * D; i += kDecThreads) dst[i] = src[i];
-        for (int i = tid; i < D; i += kDecThreads) s_scale[i] = sc_ld<H>(base + R::vchan, i);
+        for (int i = tid; i < vb * D; i += kDecThreads) dst[i] = src[i];
+        for (int i = tid; i < D; i += kDecThreads) s_scale[i] = sc_ld<H>(base + R.vchan, i);
         for (int i = tid; i < kTile * NG; i += kDecThreads) {
-          s_scale[D + i] = sc_ld<H>(base + R::vscale, i);
-          s_scale[2 * D + i] = sc_ld<H>(base + R::vmin, i);
+          s_scale[D + i] = sc_ld<H>(base + R.vscale, i);
+          s_scale[2 * D + i] = sc_ld<H>(base + R.vmin, i);
         }
       }
       // ---- online softmax over this tile: one wave per head ----
@@ -205,7 +217,14 @@ __global__ void __launch_bounds__(kDecThreads) decode_partial_kernel(DecodeParam
 #pragma unroll
           for (int h = 0; h < GV; ++h) pacc[h] = 0.0f;
           for (int t = 0; t < kTile; ++t) {
-            const float z = (float)((s_code[t * (D / 4) + (c >> 2)] >> sh) & 3u);
+            float z;
+            if constexpr (GEN) {   // channel c of token t's stream: bits [vb c, vb c + vb)
+              const int bit = vb * c;
+              const uint8_t* p = s_code + t * (D * vb / 8) + (bit >> 3);
+              z = (float)((((uint32_t)p[0] | ((uint32_t)p[1] << 8)) >> (bit & 7)) & vmask);
+            } else {
+              z = (float)((s_code[t * (D / 4) + (c >> 2)] >> sh) & 3u);
+            }
 #pragma unroll
             for (int h = 0; h < GV; ++h) pacc[h] += s_w[hv * GV + h][g][t] * z;
           }
@@ -350,10 +369,18 @@ __global__ void __launch_bounds__(64) decode_combine_kernel(DecodeParams P) {
 template <int D, int G>
 hipError_t launch_decode_dg(const DecodeParams& P, int batch, hipStream_t stream) {
   dim3 grid(P.n_tsplit + P.n_wsplit, P.n_kv, batch);
-  if (P.h16)
-    hipLaunchKernelGGL((decode_partial_kernel<D, G, true>), grid, dim3(kDecThreads), 0, stream, P);
-  else
-    hipLaunchKernelGGL((decode_partial_kernel<D, G, false>), grid, dim3(kDecThreads), 0, stream, P);
+  const bool gen = !(P.kb == 4 && P.vb == 2);
+  if (P.h16) {
+    if (gen)
+      hipLaunchKernelGGL((decode_partial_kernel<D, G, true, true>), grid, dim3(kDecThreads), 0, stream, P);
+    else
+      hipLaunchKernelGGL((decode_partial_kernel<D, G, true, false>), grid, dim3(kDecThreads), 0, stream, P);
+  } else {
+    if (gen)
+      hipLaunchKernelGGL((decode_partial_kernel<D, G, false, true>), grid, dim3(kDecThreads), 0, stream, P);
+    else
+      hipLaunchKernelGGL((decode_partial_kernel<D, G, false, false>), grid, dim3(kDecThreads), 0, stream, P);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(P.n_q, batch), dim3(64), 0, stream, P);

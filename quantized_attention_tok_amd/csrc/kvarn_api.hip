@@ -10,13 +10,20 @@
 
 namespace {
 
-// A head_dim argument holds the head dimension in its low 16 bits, optionally
-// OR-ed with KVARN_SCALES_F16 (records with f16 scales); no other bits.
+// A head_dim argument is a format word: the head dimension in bits 0-15,
+// KVARN_SCALES_F16 (records with f16 scales), the key code width in bits
+// 20-23 and the value code width in bits 24-27 (0 = the K4V2 default); no
+// other bits.
+constexpr int32_t kFieldMask = 0xFFFF | KVARN_SCALES_F16 | (0xF << 20) | (0xF << 24);
 int dim_of(int32_t hd) { return hd & 0xFFFF; }
 bool f16_of(int32_t hd) { return (hd & KVARN_SCALES_F16) != 0; }
+int kbits_of(int32_t hd) { const int b = (hd >> 20) & 0xF; return b ? b : 4; }
+int vbits_of(int32_t hd) { const int b = (hd >> 24) & 0xF; return b ? b : 2; }
+bool k4v2(int32_t hd) { return kbits_of(hd) == 4 && vbits_of(hd) == 2; }
 bool dim_ok(int32_t hd) {
   const int d = dim_of(hd);
-  return (hd & ~(0xFFFF | KVARN_SCALES_F16)) == 0 && (d == 128 || d == 256 || d == 512);
+  return (hd & ~kFieldMask) == 0 && (d == 128 || d == 256 || d == 512) && kbits_of(hd) <= 8 &&
+         vbits_of(hd) <= 8;
 }
 bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool st16(int64_t floats) { return (floats % 4) == 0; }
@@ -42,8 +49,9 @@ DecodePlan plan_decode(int batch, int n_kv, int max_tiles, int max_win, int64_t 
   return p;
 }
 
-// head_dim 128 decode runs the matrix-core split kernel plus its combine.
-bool fused_decode(int d) { return d == 128; }
+// head_dim 128 decode over K4V2 records runs the matrix-core split kernel
+// plus its combine; other widths and head dims run the vector-unit kernels.
+bool fused_decode(int32_t hd) { return dim_of(hd) == 128 && k4v2(hd); }
 
 // Matrix-core split plan: TPW tiles per workgroup (4 waves per tile): 2 once
 // the batch has enough tiles for 256 such workgroups (measured fastest at the
@@ -96,7 +104,7 @@ int validate_decode(const kvarn_decode_args* a, DecodePlan* plan) {
   if (!dim_ok(a->head_dim)) return KVARN_E_UNSUPPORTED;
   if (a->q_len < 0 || a->q_len > 8) return KVARN_E_INVALID;
   const int w = q_rows(a);
-  if (w > 1 && dim_of(a->head_dim) != 128) return KVARN_E_UNSUPPORTED;
+  if (w > 1 && !fused_decode(a->head_dim)) return KVARN_E_UNSUPPORTED;
   if (a->batch < 1 || a->n_q_heads < 1 || a->n_kv_heads < 1) return KVARN_E_INVALID;
   if (a->batch > KVARN_MAX_BATCH) return KVARN_E_UNSUPPORTED;
   if (a->n_q_heads % a->n_kv_heads != 0) return KVARN_E_UNSUPPORTED;
@@ -104,7 +112,7 @@ int validate_decode(const kvarn_decode_args* a, DecodePlan* plan) {
   if (!(G == 1 || G == 2 || G == 4 || G == 8)) return KVARN_E_UNSUPPORTED;
   if (a->max_tiles < 0 || a->max_win < 0 || a->n_record_rows < 0) return KVARN_E_INVALID;
   if (!a->q || !a->out || !a->n_tiles || !a->n_win || !a->rec_start) return KVARN_E_INVALID;
-  if (!a->q_rot && !fused_decode(dim_of(a->head_dim))) return KVARN_E_INVALID;
+  if (!a->q_rot && !fused_decode(a->head_dim)) return KVARN_E_INVALID;
   bool any_tiles = false, any_win = false;
   for (int b = 0; b < a->batch; ++b) {
     const int nt = a->n_tiles[b], nw = a->n_win[b];
@@ -130,7 +138,7 @@ int validate_decode(const kvarn_decode_args* a, DecodePlan* plan) {
     return KVARN_E_ALIGN;
   if (plan) {
     *plan = w > 1 ? plan_verify(a->batch, a->n_kv_heads, G, a->max_tiles, a->max_win)
-          : fused_decode(dim_of(a->head_dim))
+          : fused_decode(a->head_dim)
                 ? plan_fused(a->batch, a->n_kv_heads, a->max_tiles, a->max_win)
                 : plan_decode(a->batch, a->n_kv_heads, a->max_tiles, a->max_win, kTargetGroups,
                               kvarn::kWinChunk);
@@ -197,7 +205,9 @@ const char* kvarn_status_string(int status) {
 }
 
 size_t kvarn_tile_bytes(int32_t head_dim) {
-  return dim_ok(head_dim) ? (size_t)kvarn::tile_bytes_rt(dim_of(head_dim), f16_of(head_dim)) : 0;
+  return dim_ok(head_dim) ? (size_t)kvarn::rec_rt(dim_of(head_dim), f16_of(head_dim),
+                                                  kbits_of(head_dim), vbits_of(head_dim)).bytes
+                          : 0;
 }
 
 int kvarn_compress_tile(int32_t head_dim, int32_t n_tiles, int32_t n_kv_heads, const float* k,
@@ -211,8 +221,9 @@ int kvarn_compress_tile(int32_t head_dim, int32_t n_tiles, int32_t n_kv_heads, c
   if (n_kv_heads > 65535) return KVARN_E_UNSUPPORTED;
   if (!al16(k) || !al16(v) || !al16(records) || !st16(tok_stride) || !st16(head_stride))
     return KVARN_E_ALIGN;
-  hipError_t e = kvarn::launch_compress(dim_of(head_dim), f16_of(head_dim), n_tiles, n_kv_heads, k,
-                                        v, tok_stride, head_stride, records, (hipStream_t)stream);
+  hipError_t e = kvarn::launch_compress(dim_of(head_dim), f16_of(head_dim), kbits_of(head_dim),
+                                        vbits_of(head_dim), n_tiles, n_kv_heads, k, v, tok_stride,
+                                        head_stride, records, (hipStream_t)stream);
   return e == hipSuccess ? KVARN_OK : KVARN_E_DEVICE;
 }
 
@@ -239,7 +250,7 @@ int kvarn_decode_attention(const kvarn_decode_args* a, void* workspace, size_t w
   DecodePlan p;
   int st = validate_decode(a, &p);
   if (st != KVARN_OK) return st;
-  const bool fused = fused_decode(dim_of(a->head_dim));
+  const bool fused = fused_decode(a->head_dim);
   const int w = q_rows(a);
   const size_t need = decode_ws(a, p);
   if (!workspace || ws_bytes < need) return KVARN_E_WORKSPACE;
@@ -266,6 +277,8 @@ int kvarn_decode_attention(const kvarn_decode_args* a, void* workspace, size_t w
   P.wchunk = p.wchunk;
   P.mode = 0;
   P.h16 = f16_of(a->head_dim);
+  P.kb = kbits_of(a->head_dim);
+  P.vb = vbits_of(a->head_dim);
   for (int b = 0; b < a->batch; ++b) {
     P.rec_start[b] = a->rec_start[b];
     P.win_start[b] = a->win_start ? a->win_start[b] : 0;
@@ -283,14 +296,14 @@ int kvarn_decode_attention(const kvarn_decode_args* a, void* workspace, size_t w
   return e == hipSuccess ? KVARN_OK : KVARN_E_DEVICE;
 }
 
-// head_dim 128: the matrix-core prefill keeps its whole state on chip.
-// head_dim 256 / 512: the vector-unit split kernels run every chunk row as a
-// decode query with the prefill view (T(p) tiles, raw rows [128 T(p), p]) and
-// need their partials in the workspace.
+// head_dim 128 over K4V2 records: the matrix-core prefill keeps its whole
+// state on chip.  head_dim 256 / 512 and other code widths: the vector-unit
+// split kernels run every chunk row as a decode query with the prefill view
+// (T(p) tiles, raw rows [128 T(p), p]) and need their partials in the workspace.
 size_t kvarn_prefill_workspace_bytes(const kvarn_prefill_args* a) {
   DecodePlan p;
   if (validate_prefill(a, &p) != KVARN_OK) return 0;
-  if (dim_of(a->head_dim) == 128) return 0;
+  if (fused_decode(a->head_dim)) return 0;
   return decode_part_floats(a->chunk, a->n_q_heads, dim_of(a->head_dim), p) * sizeof(float);
 }
 
@@ -299,7 +312,7 @@ int kvarn_prefill_attention(const kvarn_prefill_args* a, void* workspace, size_t
   DecodePlan plan;
   int st = validate_prefill(a, &plan);
   if (st != KVARN_OK) return st;
-  if (dim_of(a->head_dim) != 128) {
+  if (!fused_decode(a->head_dim)) {
     const size_t need =
         decode_part_floats(a->chunk, a->n_q_heads, dim_of(a->head_dim), plan) * sizeof(float);
     if (!workspace || ws_bytes < need) return KVARN_E_WORKSPACE;
@@ -325,6 +338,8 @@ int kvarn_prefill_attention(const kvarn_prefill_args* a, void* workspace, size_t
     P.wchunk = plan.wchunk;
     P.mode = 1;
     P.h16 = f16_of(a->head_dim);
+    P.kb = kbits_of(a->head_dim);
+    P.vb = vbits_of(a->head_dim);
     P.window = a->window;
     P.pos0 = a->pos0;
     P.raw_base = a->raw_base;

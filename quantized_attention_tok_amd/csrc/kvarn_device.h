@@ -35,6 +35,29 @@ __host__ __device__ inline int64_t tile_bytes_rt(int d, bool h = false) {
   return h ? 106LL * d + 256 : 116LL * d + 512;
 }
 
+// Record layout for kb-bit keys and vb-bit values (gmlx PR #116 commit list:
+// key and value widths chosen on their own, 1..8 bits).  The codes are LSB-
+// first bit streams: key channel c's stream is 16 kb bytes with token t at bit
+// kb t; value token t's stream is d vb / 8 bytes with channel c at bit vb c.
+// For kb = 4, vb = 2 this is Rec<D, H> (nibbles and crumbs).
+struct RecRT {
+  int kcode, vcode, ktok, kscale, kmin, vchan, vscale, vmin, bytes;
+};
+__host__ __device__ inline RecRT rec_rt(int d, bool h, int kb, int vb) {
+  const int sb = h ? 2 : 4;
+  RecRT r;
+  r.kcode = 0;
+  r.vcode = 16 * kb * d;
+  r.ktok = r.vcode + 16 * vb * d;
+  r.kscale = r.ktok + 128 * sb;
+  r.kmin = r.kscale + d * sb;
+  r.vchan = r.kmin + d * sb;
+  r.vscale = r.vchan + d * sb;
+  r.vmin = r.vscale + d * sb;
+  r.bytes = r.vmin + d * sb;
+  return r;
+}
+
 // Scale element i of a section at p (fp32 or f16 storage), as fp32.
 template <bool H>
 __device__ __forceinline__ float sc_ld(const uint8_t* p, int i) {

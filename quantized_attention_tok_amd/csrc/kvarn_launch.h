@@ -32,6 +32,7 @@ struct DecodeParams {
   int mode;
   int q_len;                       // query rows per sequence (multi-query verify)
   int h16;                         // records carry f16 scales
+  int kb, vb;                      // key / value code widths (4 / 2: the K4V2 record)
   int window;
   int64_t pos0, raw_base;
   int64_t rec_start[64];
@@ -81,8 +82,8 @@ __device__ __forceinline__ SeqView seq_view(const DecodeParams& P, int b) {
   return v;
 }
 
-hipError_t launch_compress(int d, bool h16, int n_tiles, int n_kv, const float* k, const float* v,
-                           int64_t tok_stride, int64_t head_stride, void* records,
+hipError_t launch_compress(int d, bool h16, int kb, int vb, int n_tiles, int n_kv, const float* k,
+                           const float* v, int64_t tok_stride, int64_t head_stride, void* records,
                            hipStream_t stream);
 hipError_t launch_rotate(int d, int64_t n_rows, const float* q, float* q_rot, hipStream_t stream);
 hipError_t launch_decode(int d, const DecodeParams& P, int batch, hipStream_t stream);

@@ -17,6 +17,14 @@ TILE = 128
 
 KVARN_OK = 0
 SCALES_F16 = 0x10000   # head_dim flag: records with f16 scales
+
+
+def KEY_BITS(b: int) -> int:     # head_dim field: key code width 1..8
+    return (b & 0xF) << 20
+
+
+def VALUE_BITS(b: int) -> int:   # head_dim field: value code width 1..8
+    return (b & 0xF) << 24
 STATUS = {0: "KVARN_OK", 1: "KVARN_E_INVALID", 2: "KVARN_E_UNSUPPORTED", 3: "KVARN_E_ALIGN",
           4: "KVARN_E_WORKSPACE", 5: "KVARN_E_DEVICE"}
 
@@ -110,34 +118,40 @@ def _stream(stream=None):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def _hd(d: int, f16_scales: bool) -> int:
-    return d | SCALES_F16 if f16_scales else d
+def _hd(d: int, f16_scales: bool = False, kbits: int = 4, vbits: int = 2) -> int:
+    """The head_dim format word: d, the f16-scale flag and the code widths."""
+    hd = d | SCALES_F16 if f16_scales else d
+    if (kbits, vbits) != (4, 2):
+        hd |= KEY_BITS(kbits) | VALUE_BITS(vbits)
+    return hd
 
 
-def tile_bytes(head_dim: int, f16_scales: bool = False) -> int:
-    return int(lib().kvarn_tile_bytes(_hd(head_dim, f16_scales)))
+def tile_bytes(head_dim: int, f16_scales: bool = False, kbits: int = 4, vbits: int = 2) -> int:
+    return int(lib().kvarn_tile_bytes(_hd(head_dim, f16_scales, kbits, vbits)))
 
 
-def _check_records(records, d, f16_scales):
+def _check_records(records, d, f16_scales, kbits=4, vbits=2):
     if records is not None and records.dim() == 3:
-        assert records.shape[-1] == tile_bytes(d, f16_scales), "record size does not match the format"
+        assert records.shape[-1] == tile_bytes(d, f16_scales, kbits, vbits), \
+            "record size does not match the format"
 
 
 def compress_tile(k: torch.Tensor, v: torch.Tensor, records: torch.Tensor, n_tiles: int,
-                  stream=None, f16_scales: bool = False) -> None:
+                  stream=None, f16_scales: bool = False, kbits: int = 4, vbits: int = 2) -> None:
     """Compress tiles [0, n_tiles) of raw k/v ([tokens][kv_heads][d] views with
     contiguous channels) into records ([n_tiles][kv_heads][tile_bytes] uint8);
-    f16_scales selects the record with f16 scales."""
+    f16_scales selects the record with f16 scales, kbits / vbits the code
+    widths (1..8; K4V2 by default)."""
     assert k.shape == v.shape and k.stride() == v.stride() and k.stride(2) == 1
     d, n_kv = k.shape[2], k.shape[1]
     if n_tiles > 0:
         assert k.shape[0] >= TILE * n_tiles
-        assert records.numel() >= n_tiles * n_kv * tile_bytes(d, f16_scales)
+        assert records.numel() >= n_tiles * n_kv * tile_bytes(d, f16_scales, kbits, vbits)
         assert records.dtype == torch.uint8
-        _check_records(records, d, f16_scales)
+        _check_records(records, d, f16_scales, kbits, vbits)
     _check("kvarn_compress_tile", lib().kvarn_compress_tile(
-        _hd(d, f16_scales), n_tiles, n_kv, _ptr(k), _ptr(v), k.stride(0), k.stride(1),
-        _ptr(records), _stream(stream)))
+        _hd(d, f16_scales, kbits, vbits), n_tiles, n_kv, _ptr(k), _ptr(v), k.stride(0),
+        k.stride(1), _ptr(records), _stream(stream)))
 
 
 def rotate_query(q: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
@@ -152,7 +166,8 @@ def rotate_query(q: torch.Tensor, out: torch.Tensor | None = None, stream=None) 
 
 
 def _decode_args(q, q_rot, records, n_record_rows, rec_start, n_tiles, k_win, v_win, n_win,
-                 scale, out, max_tiles=None, max_win=None, win_start=None, f16_scales=False):
+                 scale, out, max_tiles=None, max_win=None, win_start=None, f16_scales=False,
+                 kbits=4, vbits=2):
     if q.dim() == 4:   # [B][q_len][Hq][d]: multi-query verify rows
         B, w, Hq, d = q.shape
     else:
@@ -163,8 +178,8 @@ def _decode_args(q, q_rot, records, n_record_rows, rec_start, n_tiles, k_win, v_
     nt = (ctypes.c_int32 * B)(*[int(x) for x in n_tiles])
     nw = (ctypes.c_int32 * B)(*[int(x) for x in n_win])
     a = DecodeArgs()
-    _check_records(records, d, f16_scales)
-    a.head_dim, a.batch, a.n_q_heads, a.n_kv_heads = _hd(d, f16_scales), B, Hq, n_kv
+    _check_records(records, d, f16_scales, kbits, vbits)
+    a.head_dim, a.batch, a.n_q_heads, a.n_kv_heads = _hd(d, f16_scales, kbits, vbits), B, Hq, n_kv
     a.softmax_scale = scale
     a.max_tiles = int(max(n_tiles)) if max_tiles is None else int(max_tiles)
     a.q, a.q_rot = _ptr(q), (_ptr(q_rot) if q_rot is not None else None)
@@ -182,7 +197,7 @@ def _decode_args(q, q_rot, records, n_record_rows, rec_start, n_tiles, k_win, v_
 
 def decode_attention(q, q_rot, records, rec_start, n_tiles, k_win, v_win, n_win, scale,
                      out=None, workspace=None, max_tiles=None, max_win=None, stream=None,
-                     win_start=None, f16_scales=False):
+                     win_start=None, f16_scales=False, kbits=4, vbits=2):
     """Decode attention for a batch.
 
     q, q_rot: [B][Hq][d] fp32 (q_rot may be None for head_dim 128: the kernel
@@ -192,13 +207,13 @@ def decode_attention(q, q_rot, records, rec_start, n_tiles, k_win, v_win, n_win,
     sequence b's tile j is row rec_start[b] + j.  k_win, v_win: [B][cap][Hkv][d]
     raw windows (strided views allowed, channels contiguous); n_tiles, n_win:
     per-sequence counts (host sequences); win_start: first window row of each
-    sequence (default 0); f16_scales: the records carry f16 scales.  Returns
-    out [B][Hq][d]."""
+    sequence (default 0); f16_scales: the records carry f16 scales; kbits /
+    vbits: their code widths.  Returns out [B][Hq][d]."""
     if out is None:
         out = torch.empty_like(q)
     rows = records.shape[0] if records is not None else 0
     a, keep = _decode_args(q, q_rot, records, rows, rec_start, n_tiles, k_win, v_win, n_win,
-                           scale, out, max_tiles, max_win, win_start, f16_scales)
+                           scale, out, max_tiles, max_win, win_start, f16_scales, kbits, vbits)
     need = int(lib().kvarn_decode_workspace_bytes(ctypes.byref(a)))
     if workspace is None:
         workspace = torch.zeros(max(need, 16), dtype=torch.uint8, device=q.device)
@@ -208,19 +223,22 @@ def decode_attention(q, q_rot, records, rec_start, n_tiles, k_win, v_win, n_win,
 
 
 def decode_workspace_bytes(q, q_rot, records, rec_start, n_tiles, k_win, v_win, n_win, scale,
-                           max_tiles=None, max_win=None, f16_scales=False) -> int:
+                           max_tiles=None, max_win=None, f16_scales=False, kbits=4,
+                           vbits=2) -> int:
     rows = records.shape[0] if records is not None else 0
     a, keep = _decode_args(q, q_rot, records, rows, rec_start, n_tiles, k_win, v_win, n_win,
-                           scale, q, max_tiles, max_win, f16_scales=f16_scales)
+                           scale, q, max_tiles, max_win, f16_scales=f16_scales, kbits=kbits,
+                           vbits=vbits)
     return int(lib().kvarn_decode_workspace_bytes(ctypes.byref(a)))
 
 
 def _prefill_args(q, q_rot, records, n_record_rows, k, v, raw_base, pos0, window, scale, out,
-                  f16_scales=False):
+                  f16_scales=False, kbits=4, vbits=2):
     C, Hq, d = q.shape
-    _check_records(records, d, f16_scales)
+    _check_records(records, d, f16_scales, kbits, vbits)
     a = PrefillArgs()
-    a.head_dim, a.n_q_heads, a.n_kv_heads, a.window = _hd(d, f16_scales), Hq, k.shape[1], window
+    a.head_dim, a.n_q_heads, a.n_kv_heads, a.window = (_hd(d, f16_scales, kbits, vbits), Hq,
+                                                       k.shape[1], window)
     a.pos0, a.chunk, a.softmax_scale = pos0, C, scale
     a.q, a.q_rot = _ptr(q), _ptr(q_rot)
     a.records = _ptr(records) if records is not None else None
@@ -233,25 +251,25 @@ def _prefill_args(q, q_rot, records, n_record_rows, k, v, raw_base, pos0, window
 
 
 def prefill_workspace_bytes(q, q_rot, records, n_record_rows, k, v, raw_base, pos0, window,
-                            scale, f16_scales=False) -> int:
+                            scale, f16_scales=False, kbits=4, vbits=2) -> int:
     """Workspace bytes of a prefill_attention call with these arguments."""
     a = _prefill_args(q, q_rot, records, n_record_rows, k, v, raw_base, pos0, window, scale, q,
-                      f16_scales)
+                      f16_scales, kbits, vbits)
     return int(lib().kvarn_prefill_workspace_bytes(ctypes.byref(a)))
 
 
 def prefill_attention(q, q_rot, records, n_record_rows, k, v, raw_base, pos0, window, scale,
-                      out=None, workspace=None, stream=None, f16_scales=False):
+                      out=None, workspace=None, stream=None, f16_scales=False, kbits=4, vbits=2):
     """Chunk of C query positions [pos0, pos0+C) of one sequence.
 
     q, q_rot: [C][Hq][d].  records: [rows][Hkv][tile_bytes] (tile j = row j).
     k, v: raw [n][Hkv][d] views whose row i is absolute position raw_base + i;
-    f16_scales: the records carry f16 scales."""
+    f16_scales: the records carry f16 scales; kbits / vbits: their code widths."""
     assert k.stride(2) == 1 and k.stride() == v.stride()
     if out is None:
         out = torch.empty_like(q)
     a = _prefill_args(q, q_rot, records, n_record_rows, k, v, raw_base, pos0, window, scale, out,
-                      f16_scales)
+                      f16_scales, kbits, vbits)
     need = int(lib().kvarn_prefill_workspace_bytes(ctypes.byref(a)))
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)

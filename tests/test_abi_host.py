@@ -53,6 +53,24 @@ def test_f16_scale_flag_sizes_match_the_oracle_record(L):
     assert L.kvarn_tile_bytes(128 | 0x20000) == 0 and L.kvarn_tile_bytes(96 | F) == 0
 
 
+def test_code_width_fields_and_sizes_match_the_oracle_record(L):
+    import oracle
+    from quantized_attention_tok_amd import kvarn
+    text = open(HEADER).read()
+    assert re.search(r"#define\s+KVARN_KEY_BITS\(b\)\s+\(\(\(b\) & 0xF\) << 20\)", text)
+    assert re.search(r"#define\s+KVARN_VALUE_BITS\(b\)\s+\(\(\(b\) & 0xF\) << 24\)", text)
+    for d in (128, 256, 512):
+        for kb in range(1, 9):
+            for vb in range(1, 9):
+                for f16 in (False, True):
+                    hd = kvarn._hd(d, f16, kb, vb)
+                    assert L.kvarn_tile_bytes(hd) == oracle.tile_bytes(d, f16, kb, vb), (d, kb, vb, f16)
+    # a zero field is the K4V2 default; widths above 8 are unsupported
+    assert L.kvarn_tile_bytes(128 | (4 << 20) | (2 << 24)) == L.kvarn_tile_bytes(128)
+    assert L.kvarn_tile_bytes(128 | (9 << 20)) == 0 and L.kvarn_tile_bytes(128 | (15 << 24)) == 0
+    assert L.kvarn_tile_bytes(128 | (1 << 28)) == 0
+
+
 # These calls pass fake device pointers that every case must reject before a
 # launch; on a machine with a GPU a wrongly accepted case would launch a kernel
 # on them, so the module only runs where no GPU is visible.
@@ -132,6 +150,9 @@ def test_decode_validation_and_workspace_query(L):
         (dict(q_len=2, head_dim=256, n_win=[4], max_win=4), 2),   # verify is head_dim 128
         (dict(head_dim=128 | 0x80000), 2),                # unknown format bit
         (dict(head_dim=128 | 0x10000, n_record_rows=3), 1),   # f16-scale records, same checks
+        (dict(head_dim=128 | (6 << 20) | (5 << 24), q_rot=None), 1),   # vector path needs q_rot
+        (dict(head_dim=128 | (6 << 20), q_len=2, n_win=[4], max_win=4), 2),   # verify is K4V2 only
+        (dict(head_dim=128 | (9 << 20)), 2),             # key width above 8
     ]
     for over, want in bad:
         b, k2 = _decode_args(**over)
@@ -175,6 +196,10 @@ def test_prefill_validation(L):
     # the f16-scale format does not change the workspace
     a256h = args(head_dim=256 | 0x10000, tok_stride=256 * 2, head_stride=256)
     assert L.kvarn_prefill_workspace_bytes(ctypes.byref(a256h)) == need
+    # other code widths at head_dim 128 take the vector-unit path and its workspace
+    aw = args(head_dim=128 | (6 << 20) | (5 << 24))
+    assert L.kvarn_prefill_workspace_bytes(ctypes.byref(aw)) > 0
+    assert L.kvarn_prefill_attention(ctypes.byref(aw), None, 1 << 30, None) == 4
     bad = [(dict(head_dim=384), 2), (dict(head_dim=128 | 0x20000), 2), (dict(chunk=0), 1),
            (dict(pos0=-1), 1),
            (dict(n_record_rows=3), 1), (dict(raw_base=384), 1), (dict(k=FAKE + 4), 3),
