@@ -105,22 +105,28 @@ template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
-// value of lane (lane ^ M)
+// value of lane (lane ^ M), M < 16, on the DPP paths (no LDS round trip):
+// lane ^ 4 is the half-row mirror (lane ^ 7) followed by quad_perm [3,2,1,0]
 template <int M>
 __device__ __forceinline__ float xshfl(float v) {
   if constexpr (M == 1) return dpp_f<0xB1>(v);        // quad_perm [1,0,3,2]
   else if constexpr (M == 2) return dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]
   else if constexpr (M == 8) return dpp_f<0x128>(v);  // row_ror:8
-  else if constexpr (M == 4 || M == 16)
-    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), (M << 10) | 0x1F));
-  else return __shfl_xor(v, 32, 64);
+  else return dpp_f<0x1B>(dpp_f<0x141>(v));           // M == 4: row_half_mirror, quad_perm [3,2,1,0]
 }
-// Walsh-Hadamard butterfly on lane bit M: lower lane a + b, upper lane a - b
-// (partner + sign * own, the sign +1 / -1 from the lane's bit M).
+// Walsh-Hadamard butterfly on lane bit M: lower lane a + b, upper lane a - b.
+// Bits 16 and 32 use the gfx950 permlane swaps: a swap of x with itself gives
+// the lower lane (own, partner) and the upper lane (partner, own).
 template <int M>
 __device__ __forceinline__ float bfly(float x, int lane) {
   const float sg = __int_as_float(0x3F800000 | ((lane & M) ? 0x80000000 : 0));
-  return xshfl<M>(x) + x * sg;
+  if constexpr (M >= 16) {
+    const auto r = (M == 32) ? __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false)
+                             : __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaf(sg, __uint_as_float(r[1]), __uint_as_float(r[0]));
+  } else {
+    return xshfl<M>(x) + x * sg;
+  }
 }
 // x holds element lane, y element lane + 64 of a 128-vector: y <- H_128 x / sqrt(128)
 __device__ __forceinline__ void wht128(float& x, float& y, int lane) {
@@ -160,14 +166,21 @@ __device__ __forceinline__ float row_sum16(float v) {
 __device__ __forceinline__ float lane_f(float v, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
-// whole-wave reductions, uniform result
+// whole-wave reductions (every lane gets the result): within the 16-lane rows
+// by DPP, across the rows by permlane swaps
 __device__ __forceinline__ float wmax(float v) {
   v = row_max16(v);
-  return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float wsum(float v) {
   v = row_sum16(v);
-  return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 template <int G, int TPW, bool H>
@@ -186,7 +199,18 @@ __global__ void __launch_bounds__(256 * TPW) decode_split_kernel(DecodeParams P)
   const int split = blockIdx.x;
   const int kvh = blockIdx.y;
   const int b = blockIdx.z;
-  const int n_split = P.n_tsplit;
+  // Every kernel argument the workgroup needs, read before any branch and
+  // pinned in registers together: one round of scalar loads, not a chain.
+  const SeqView sv = seq_view_decode(P, b);
+  const int n_split = P.n_tsplit, n_q = P.n_q, n_kv = P.n_kv;
+  const float p_scale = P.scale;
+  const float *p_q = P.q, *p_qrot = P.q_rot, *p_kwin = P.k_win, *p_vwin = P.v_win;
+  const uint8_t* p_rec = P.records;
+  float* p_part = P.part;
+  const int64_t p_hst = P.win_head_stride, p_tok = P.win_tok_stride;
+  asm volatile("" ::"s"(sv.nt), "s"(sv.nw), "s"(sv.rec_row0), "s"(sv.win_off), "s"(n_split),
+               "s"(n_q), "s"(n_kv), "s"(p_scale), "s"(p_q), "s"(p_qrot), "s"(p_kwin), "s"(p_vwin),
+               "s"(p_rec), "s"(p_part), "s"(p_hst), "s"(p_tok));
 
   __shared__ __attribute__((aligned(16))) uint8_t lds[L::bytes];
   float2* s_ml = reinterpret_cast<float2*>(lds + L::ml);
@@ -197,8 +221,7 @@ __global__ void __launch_bounds__(256 * TPW) decode_split_kernel(DecodeParams P)
   float* s_winv = reinterpret_cast<float*>(lds + L::winv);
   float* s_winp = reinterpret_cast<float*>(lds + L::winp);
 
-  const SeqView sv = seq_view(P, b);
-  float* part = P.part + (((int64_t)b * P.n_q + (int64_t)kvh * G) * n_split + split) * (D + 4);
+  float* part = p_part + (((int64_t)b * n_q + (int64_t)kvh * G) * n_split + split) * (D + 4);
   const int64_t hs = (int64_t)n_split * (D + 4);   // partial of head h at part + h * hs
   const int j0 = split * TPW;
   const int ntl = max(0, min(TPW, sv.nt - j0));                     // tiles of this split
@@ -210,13 +233,13 @@ __global__ void __launch_bounds__(256 * TPW) decode_split_kernel(DecodeParams P)
     }
     return;
   }
-  const float c_log2 = P.scale * kLog2e;
+  const float c_log2 = p_scale * kLog2e;
   const int tau = wv >> 2, wq = wv & 3;
   const bool has_tile = tau < ntl;
-  const int64_t rstride = (int64_t)P.n_kv * R::bytes;
-  const uint8_t* recs = P.records + ((sv.rec_row0 + j0) * (int64_t)P.n_kv + kvh) * R::bytes;
-  const float* qsrc = (P.q_rot ? P.q_rot : P.q) + ((int64_t)b * P.n_q + (int64_t)kvh * G) * D;
-  const float* qraw = P.q + ((int64_t)b * P.n_q + (int64_t)kvh * G) * D;
+  const int64_t rstride = (int64_t)n_kv * R::bytes;
+  const uint8_t* recs = p_rec + ((sv.rec_row0 + j0) * (int64_t)n_kv + kvh) * R::bytes;
+  const float* qsrc = (p_qrot ? p_qrot : p_q) + ((int64_t)b * n_q + (int64_t)kvh * G) * D;
+  const float* qraw = p_q + ((int64_t)b * n_q + (int64_t)kvh * G) * D;
 
   // ---- 1. loads.  Window rows first: the waits for the tile loads below then
   //      never include them.  Inside a split with tiles every wave issues the
@@ -230,13 +253,13 @@ __global__ void __launch_bounds__(256 * TPW) decode_split_kernel(DecodeParams P)
       qw1[h] = qraw[h * D + lane + 64];
     }
   }
-  const float* kwin = P.k_win + sv.win_off + (int64_t)kvh * P.win_head_stride;
-  const float* vwin = P.v_win + sv.win_off + (int64_t)kvh * P.win_head_stride;
+  const float* kwin = p_kwin + sv.win_off + (int64_t)kvh * p_hst;
+  const float* vwin = p_vwin + sv.win_off + (int64_t)kvh * p_hst;
 #pragma unroll
   for (int k = 0; k < KW; ++k) {
     const int tr = wv + NW * k;
     if (tr < nwt) {
-      const int64_t row = (int64_t)(kWinPerSplit * split + tr) * P.win_tok_stride;
+      const int64_t row = (int64_t)(kWinPerSplit * split + tr) * p_tok;
       wk0[k] = kwin[row + lane];
       wk1[k] = kwin[row + lane + 64];
       wv0[k] = vwin[row + lane];
@@ -289,7 +312,7 @@ __global__ void __launch_bounds__(256 * TPW) decode_split_kernel(DecodeParams P)
       const bool ok = pr < TPW * G && tt < ntl;   // wave-uniform; the math runs either way
       {
         float x0 = pq0[k], x1 = pq1[k];
-        if (!P.q_rot) wht128(x0, x1, lane);
+        if (!p_qrot) wht128(x0, x1, lane);
         const float y0 = x0 * pks0[k], y1 = x1 * pks1[k];
         const float amax = wmax(fmaxf(fabsf(y0), fabsf(y1)));
         const float bias = wsum(x0 * pkm0[k] + x1 * pkm1[k]);

@@ -82,6 +82,17 @@ __device__ __forceinline__ SeqView seq_view(const DecodeParams& P, int b) {
   return v;
 }
 
+// The decode view (mode 0) alone: no branch on the mode, so the compiler can
+// issue every kernel-argument load at once.
+__device__ __forceinline__ SeqView seq_view_decode(const DecodeParams& P, int b) {
+  SeqView v;
+  v.nt = P.n_tiles[b];
+  v.nw = P.n_win[b];
+  v.rec_row0 = P.rec_start[b];
+  v.win_off = (int64_t)b * P.win_seq_stride + P.win_start[b] * P.win_tok_stride;
+  return v;
+}
+
 hipError_t launch_compress(int d, bool h16, int kb, int vb, int n_tiles, int n_kv, const float* k,
                            const float* v, int64_t tok_stride, int64_t head_stride, void* records,
                            hipStream_t stream);
