@@ -78,18 +78,17 @@ struct Lds {
   static constexpr int wop_wave = kMRows * kWRow * 4;
   static constexpr int qt = wop + kNW * wop_wave;           // [TPW][k4][16 rows][4] uint4: q~ hi/lo
   static constexpr int qt_tile = 4 * kMRows * 64;
-  static constexpr int wins = qt + TPW * qt_tile;           // [G][16] f32: window scores (log2)
-  static constexpr int winw = wins + G * kWinPerSplit * 4;  // [G][16] f32: window weights
+  static constexpr int winw = qt + TPW * qt_tile;           // [G][16] f32: window weights
   static constexpr int winv = winw + G * kWinPerSplit * 4;  // [16][D] f32: rotated window values
   static constexpr int winp = winv + kWinPerSplit * D * 4;  // [G][16][4] f32: window q . k row sums
   static constexpr int us = winp + G * kWinPerSplit * 16;   // [TPW][G] f32: score unscale
   static constexpr int bias = us + TPW * G * 4;             // [TPW][G] f32: sum_c q'_c kmin_c
   static constexpr int fv = bias + TPW * G * 4;             // [TPW] int: w fp16 scale exponent
   static constexpr int ml = align16(fv + TPW * 4);          // [G][wave] float2: m, l
-  static constexpr int mx = ml + kNW * G * 8;               // [G] f32: workgroup max
-  static constexpr int bytes = mx + G * 4;
+  static constexpr int bytes = ml + kNW * G * 8;
   static constexpr int mo = 0;                              // merge: [wave][G][D] f32 (over codes, w, q~)
-  static_assert(kNW * G * D * 4 <= wins, "merge area fits below the window entries");
+  static_assert(kNW * G * D * 4 <= winw, "merge area fits below the window entries");
+  static_assert(kNW <= 16, "the merge gives each wave's state one lane of a 16-lane row");
   static_assert((wop % 16) == 0 && (qt % 16) == 0 && (winv % 16) == 0, "aligned sections");
 };
 
@@ -214,9 +213,7 @@ __global__ void __launch_bounds__(256 * TPW) decode_split_kernel(DecodeParams P)
 
   __shared__ __attribute__((aligned(16))) uint8_t lds[L::bytes];
   float2* s_ml = reinterpret_cast<float2*>(lds + L::ml);
-  float* s_mx = reinterpret_cast<float*>(lds + L::mx);
   float* s_mo = reinterpret_cast<float*>(lds + L::mo);
-  float* s_wins = reinterpret_cast<float*>(lds + L::wins);
   float* s_winw = reinterpret_cast<float*>(lds + L::winw);
   float* s_winv = reinterpret_cast<float*>(lds + L::winv);
   float* s_winp = reinterpret_cast<float*>(lds + L::winp);
@@ -470,24 +467,38 @@ __global__ void __launch_bounds__(256 * TPW) decode_split_kernel(DecodeParams P)
     }
   }
   __syncthreads();   // every wave is done with its codes and w rows: the merge area may be written
-  if (tid < G) {   // head max; window scores (log2 domain) from their row sums
-    float M = -INFINITY;
-    for (int w = 0; w < n_act; ++w) M = fmaxf(M, s_ml[tid * NW + w].x);
-    for (int t = 0; t < nwt; ++t) {
-      const float4 r = *reinterpret_cast<const float4*>(s_winp + 4 * (tid * kWinPerSplit + t));
-      const float sc = ((r.x + r.y) + (r.z + r.w)) * c_log2;
-      s_wins[tid * kWinPerSplit + t] = sc;
-      M = fmaxf(M, sc);
+  // Head maxima and sums, lane-parallel in every wave: lane (g, n) of head
+  // HPL g + jj takes wave n's state (n < n_act) and window token n (n < nwt).
+  float Mh[HPL];
+#pragma unroll
+  for (int jj = 0; jj < HPL; ++jj) {
+    const int hr = HPL * g + jj;
+    const int h = hr < G ? hr : G - 1;
+    const float2 ml = (n < n_act) ? s_ml[h * NW + n] : make_float2(-INFINITY, 0.0f);
+    float sc = -INFINITY;
+    if (n < nwt) {
+      const float4 r = *reinterpret_cast<const float4*>(s_winp + 4 * (h * kWinPerSplit + n));
+      sc = ((r.x + r.y) + (r.z + r.w)) * c_log2;
     }
-    s_mx[tid] = M;
+    const float M = row_max16(fmaxf(ml.x, sc));
+    const float ww = (n < nwt) ? __builtin_amdgcn_exp2f(sc - M) : 0.0f;
+    const float ls = (n < n_act) ? __builtin_amdgcn_exp2f(ml.x - M) * ml.y : 0.0f;
+    const float L = row_sum16(ls + ww);
+    Mh[jj] = M;
+    if (wv == 0 && hr < G) {
+      if (n < nwt) s_winw[h * kWinPerSplit + n] = ww;
+      if (n == 0) {
+        part[h * hs + D] = M;   // log2 domain
+        part[h * hs + D + 1] = L;
+      }
+    }
   }
-  __syncthreads();
   if (wv < n_act) {
 #pragma unroll
     for (int jj = 0; jj < HPL; ++jj) {
       const int h = HPL * g + jj;
       if (h < G) {
-        const float sc = __builtin_amdgcn_exp2f(m_w[jj] - s_mx[h]);
+        const float sc = __builtin_amdgcn_exp2f(m_w[jj] - Mh[jj]);
         float* dst = s_mo + (wv * G + h) * D + 16 * (n & 7) + 8 * (n >> 3);
         *reinterpret_cast<float4*>(dst) =
             make_float4(o_w[jj][0] * sc, o_w[jj][1] * sc, o_w[jj][2] * sc, o_w[jj][3] * sc);
@@ -495,22 +506,6 @@ __global__ void __launch_bounds__(256 * TPW) decode_split_kernel(DecodeParams P)
             make_float4(o_w[jj][4] * sc, o_w[jj][5] * sc, o_w[jj][6] * sc, o_w[jj][7] * sc);
       }
     }
-  }
-  if (tid < G * kWinPerSplit) {
-    const int h = tid / kWinPerSplit, t = tid % kWinPerSplit;
-    if (t < nwt) s_winw[h * kWinPerSplit + t] = __builtin_amdgcn_exp2f(s_wins[h * kWinPerSplit + t] - s_mx[h]);
-  }
-  if (tid >= NT - G) {   // L of head h (any lane of the last wave)
-    const int h = tid - (NT - G);
-    const float M = s_mx[h];
-    float l = 0.0f;
-    for (int w = 0; w < n_act; ++w) {
-      const float2 ml = s_ml[h * NW + w];
-      l += __builtin_amdgcn_exp2f(ml.x - M) * ml.y;
-    }
-    for (int t = 0; t < nwt; ++t) l += __builtin_amdgcn_exp2f(s_wins[h * kWinPerSplit + t] - M);
-    part[h * hs + D] = M;   // log2 domain
-    part[h * hs + D + 1] = l;
   }
   __syncthreads();
   for (int i = tid; i < G * D; i += NT) {
