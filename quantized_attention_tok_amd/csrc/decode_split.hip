@@ -519,11 +519,12 @@ __global__ void __launch_bounds__(256 * TPW) decode_split_kernel(DecodeParams P)
 
 // ---------------------------------------------------------------------------
 // Combine: one workgroup of 4 waves per (query head, sequence); lane l owns
-// channels 2l, 2l+1.  Wave w folds splits [32 w + 128 k, +32) with an online
-// log-sum-exp (all loads of a pass in flight, the pass's weights through
-// LDS); the four wave states merge in LDS, wave 0 applies the inverse WHT
-// and divides by L.
+// channels 2l, 2l+1.  Wave w folds splits [PW w + 4 PW k, +PW) with an online
+// log-sum-exp (all loads of a pass in flight, split j's weight read from lane
+// j); the four wave states merge in LDS, wave 0 applies the inverse WHT and
+// divides by L.
 // ---------------------------------------------------------------------------
+template <int PW>
 __global__ void __launch_bounds__(256) decode_combine_kernel(DecodeParams P) {
   const int hq = blockIdx.x;
   const int b = blockIdx.y;
@@ -531,18 +532,17 @@ __global__ void __launch_bounds__(256) decode_combine_kernel(DecodeParams P) {
   const int lane = tid & 63, w = tid >> 6;
   const int ns = P.n_tsplit;
   const float* ph = P.part + ((int64_t)b * P.n_q + hq) * (int64_t)ns * (D + 4);
-  __shared__ float s_w[4][32];
   __shared__ float s_st[4][2];
   __shared__ __attribute__((aligned(16))) float s_o[4][D];
   float M = -INFINITY, Lt = 0.0f, t0 = 0.f, t1 = 0.f;
-  for (int base = 32 * w; base < ns; base += 128) {
-    float2 v[32];
+  for (int base = PW * w; base < ns; base += 4 * PW) {
+    float2 v[PW];
 #pragma unroll
-    for (int j = 0; j < 32; ++j)
+    for (int j = 0; j < PW; ++j)
       v[j] = (base + j < ns) ? *reinterpret_cast<const float2*>(ph + (int64_t)(base + j) * (D + 4) + 2 * lane)
                              : make_float2(0.f, 0.f);
     float m = -INFINITY, l = 0.0f;
-    if (lane < 32 && base + lane < ns) {
+    if (lane < PW && base + lane < ns) {
       const float2 ml = *reinterpret_cast<const float2*>(ph + (int64_t)(base + lane) * (D + 4) + D);
       m = ml.x;
       l = ml.y;
@@ -555,11 +555,10 @@ __global__ void __launch_bounds__(256) decode_combine_kernel(DecodeParams P) {
     }
     const float wgt = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - M);
     Lt += wsum(wgt * l);
-    if (lane < 32) s_w[w][lane] = wgt;   // read back by this wave only
     float a0 = 0.f, a1 = 0.f;
 #pragma unroll
-    for (int j = 0; j < 32; j += 2) {
-      const float w0 = s_w[w][j], w1 = s_w[w][j + 1];
+    for (int j = 0; j < PW; j += 2) {   // split j's weight is lane j's
+      const float w0 = lane_f(wgt, j), w1 = lane_f(wgt, j + 1);
       t0 += w0 * v[j].x;
       t1 += w0 * v[j].y;
       a0 += w1 * v[j + 1].x;
@@ -635,7 +634,12 @@ hipError_t launch_decode_fused(const DecodeParams& P, int batch, hipStream_t str
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_combine_kernel, dim3(P.n_q, batch), dim3(256), 0, stream, P);
+  // passes of 16 splits per wave while one pass of the four waves covers every
+  // split, else 32 (fewer, longer passes)
+  if (P.n_tsplit <= 64)
+    hipLaunchKernelGGL(decode_combine_kernel<16>, dim3(P.n_q, batch), dim3(256), 0, stream, P);
+  else
+    hipLaunchKernelGGL(decode_combine_kernel<32>, dim3(P.n_q, batch), dim3(256), 0, stream, P);
   return hipGetLastError();
 }
 
