@@ -92,6 +92,16 @@ struct Lds {
   static_assert((wop % 16) == 0 && (qt % 16) == 0 && (winv % 16) == 0, "aligned sections");
 };
 
+// Bytes p[0] and p[off] in bits 0-7 and 16-23 (built as two 16-bit lanes, so
+// the compiler joins the two LDS byte loads with one v_perm_b32).
+typedef unsigned short ushort2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t byte_pair(const uint8_t* p, int off) {
+  ushort2v t;
+  t.x = p[0];
+  t.y = p[off];
+  return __builtin_bit_cast(uint32_t, t);
+}
+
 // fp16 hi + lo parts of (a, b): hi rounds toward zero, lo holds the rest.
 __device__ __forceinline__ void split_pair(float a, float b, uint32_t& hi, uint32_t& lo) {
   const half2v h = __builtin_amdgcn_cvt_pkrtz(a, b);
@@ -368,7 +378,7 @@ __global__ void __launch_bounds__(256 * TPW) decode_split_kernel(DecodeParams P)
       uint32_t e[4], o[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint32_t x = (uint32_t)kg[576 * k4 + 32 * i] | ((uint32_t)kg[576 * k4 + 32 * i + 16] << 16);
+        const uint32_t x = byte_pair(kg + 576 * k4 + 32 * i, 16);
         e[i] = (x << 4) & 0x00F000F0u;   // token 2 n
         o[i] = x & 0x00F000F0u;          // token 2 n + 1
       }
@@ -418,7 +428,7 @@ __global__ void __launch_bounds__(256 * TPW) decode_split_kernel(DecodeParams P)
 #pragma unroll
     for (int pq = 0; pq < 4; ++pq) {
 #pragma unroll
-      for (int e = 0; e < 2; ++e) x[e][pq] = (uint32_t)vg[64 * pq + e] | ((uint32_t)vg[64 * pq + 32 + e] << 16);
+      for (int e = 0; e < 2; ++e) x[e][pq] = byte_pair(vg + 64 * pq + e, 32);
     }
     const float vch[8] = {vca.x, vca.y, vca.z, vca.w, vcb.x, vcb.y, vcb.z, vcb.w};
     const float un_lo = pow2i(24 - vexp - 4), un_hi = pow2i(24 - vexp - 6);
