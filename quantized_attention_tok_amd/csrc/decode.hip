@@ -308,35 +308,85 @@ __global__ void __launch_bounds__(kDecThreads) decode_partial_kernel(DecodeParam
 }
 
 // ---------------------------------------------------------------------------
-// combine kernel: one wave per (query head, sequence)
+// combine kernel: one workgroup of 4 waves per (query head, sequence); lane l
+// owns channels l + 64 k.  Wave w folds splits [16 w + 64 i, +16) with an
+// online log-sum-exp (split j's (m, l) in lane j, its weight read from lane
+// j; the tile partials (rotated domain) and the window partials (raw domain)
+// summed apart); the four wave states merge in LDS, wave 0 applies the
+// inverse WHT to the tile sum, adds the window sum and divides by L.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ void __launch_bounds__(64) decode_combine_kernel(DecodeParams P) {
+__global__ void __launch_bounds__(256) decode_combine_kernel(DecodeParams P) {
   constexpr int K = D / 64;
+  constexpr int PW = 16;
   const int hq = blockIdx.x;
   const int b = blockIdx.y;
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  const int nts = P.n_tsplit;
   const int n_split = P.n_tsplit + P.n_wsplit;
   const float* part = P.part + ((int64_t)b * P.n_q + hq) * n_split * (D + 4);
+  __shared__ float s_st[4][2];
+  __shared__ float s_o[4][2][D];
 
-  float M = -INFINITY;
-  for (int s = 0; s < n_split; ++s) M = fmaxf(M, part[(int64_t)s * (D + 4) + D]);
-  float L = 0.0f;
+  float M = -INFINITY, L = 0.0f;
   float orot[K], oraw[K];
 #pragma unroll
   for (int k = 0; k < K; ++k) { orot[k] = 0.0f; oraw[k] = 0.0f; }
-  for (int s = 0; s < n_split; ++s) {
-    const float* ps = part + (int64_t)s * (D + 4);
-    const float m = ps[D];
-    const float wgt = (m == -INFINITY) ? 0.0f : __expf(m - M);
-    L += wgt * ps[D + 1];
-    if (s < P.n_tsplit) {
-#pragma unroll
-      for (int k = 0; k < K; ++k) orot[k] += wgt * ps[lane + 64 * k];
-    } else {
-#pragma unroll
-      for (int k = 0; k < K; ++k) oraw[k] += wgt * ps[lane + 64 * k];
+  for (int base = PW * w; base < n_split; base += 4 * PW) {
+    float m = -INFINITY, l = 0.0f;
+    if (lane < PW && base + lane < n_split) {
+      m = part[(int64_t)(base + lane) * (D + 4) + D];
+      l = part[(int64_t)(base + lane) * (D + 4) + D + 1];
     }
+    const float mc = wave_max(m);
+    if (mc > M) {
+      const float r = __expf(M - mc);   // 0 while M = -inf
+      L *= r;
+#pragma unroll
+      for (int k = 0; k < K; ++k) { orot[k] *= r; oraw[k] *= r; }
+      M = mc;
+    }
+    const float wgt = (m == -INFINITY) ? 0.0f : __expf(m - M);
+    L += wave_sum(wgt * l);
+#pragma unroll
+    for (int j = 0; j < PW; ++j) {
+      const int s = base + j;
+      if (s < n_split) {   // uniform
+        const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), j));
+        const float* ps = part + (int64_t)s * (D + 4);
+        if (s < nts) {
+#pragma unroll
+          for (int k = 0; k < K; ++k) orot[k] = fmaf(wj, ps[lane + 64 * k], orot[k]);
+        } else {
+#pragma unroll
+          for (int k = 0; k < K; ++k) oraw[k] = fmaf(wj, ps[lane + 64 * k], oraw[k]);
+        }
+      }
+    }
+  }
+  if (lane == 0) { s_st[w][0] = M; s_st[w][1] = L; }
+  __syncthreads();
+  const float Mall = fmaxf(fmaxf(s_st[0][0], s_st[1][0]), fmaxf(s_st[2][0], s_st[3][0]));
+  const float sc = (M == -INFINITY) ? 0.0f : __expf(M - Mall);
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    s_o[w][0][lane + 64 * k] = orot[k] * sc;
+    s_o[w][1][lane + 64 * k] = oraw[k] * sc;
+  }
+  __syncthreads();
+  if (w != 0) return;
+  float Lall = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float mi = s_st[i][0];
+    Lall += (mi == -INFINITY) ? 0.0f : __expf(mi - Mall) * s_st[i][1];
+  }
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const int c = lane + 64 * k;
+    orot[k] = (s_o[0][0][c] + s_o[1][0][c]) + (s_o[2][0][c] + s_o[3][0][c]);
+    oraw[k] = (s_o[0][1][c] + s_o[1][1][c]) + (s_o[2][1][c] + s_o[3][1][c]);
   }
   // inverse WHT (the WHT itself) of the merged rotated-domain part
 #pragma unroll
@@ -360,7 +410,7 @@ __global__ void __launch_bounds__(64) decode_combine_kernel(DecodeParams P) {
     }
   }
   const float c = wht_scale<D>();
-  const float invL = 1.0f / L;
+  const float invL = 1.0f / Lall;
   float* o = P.out + ((int64_t)b * P.n_q + hq) * D;
 #pragma unroll
   for (int k = 0; k < K; ++k) o[lane + 64 * k] = (orot[k] * c + oraw[k]) * invL;
@@ -383,7 +433,7 @@ hipError_t launch_decode_dg(const DecodeParams& P, int batch, hipStream_t stream
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(P.n_q, batch), dim3(64), 0, stream, P);
+  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(P.n_q, batch), dim3(256), 0, stream, P);
   return hipGetLastError();
 }
 
