@@ -308,15 +308,15 @@ __global__ void __launch_bounds__(kDecThreads) decode_partial_kernel(DecodeParam
 }
 
 // ---------------------------------------------------------------------------
-// combine kernel: one workgroup of 4 waves per (query head, sequence); lane l
-// owns channels l + 64 k.  Wave w folds splits [16 w + 64 i, +16) with an
+// combine kernel: one workgroup of NWV waves per (query head, sequence); lane
+// l owns channels l + 64 k.  Wave w folds splits [16 w + 16 NWV i, +16) with an
 // online log-sum-exp (split j's (m, l) in lane j, its weight read from lane
 // j; the tile partials (rotated domain) and the window partials (raw domain)
-// summed apart); the four wave states merge in LDS, wave 0 applies the
+// summed apart); the wave states merge in LDS, wave 0 applies the
 // inverse WHT to the tile sum, adds the window sum and divides by L.
 // ---------------------------------------------------------------------------
-template <int D>
-__global__ void __launch_bounds__(256) decode_combine_kernel(DecodeParams P) {
+template <int D, int NWV>
+__global__ void __launch_bounds__(64 * NWV) decode_combine_kernel(DecodeParams P) {
   constexpr int K = D / 64;
   constexpr int PW = 16;
   const int hq = blockIdx.x;
@@ -326,14 +326,14 @@ __global__ void __launch_bounds__(256) decode_combine_kernel(DecodeParams P) {
   const int nts = P.n_tsplit;
   const int n_split = P.n_tsplit + P.n_wsplit;
   const float* part = P.part + ((int64_t)b * P.n_q + hq) * n_split * (D + 4);
-  __shared__ float s_st[4][2];
-  __shared__ float s_o[4][2][D];
+  __shared__ float s_st[NWV][2];
+  __shared__ float s_o[NWV][2][D];
 
   float M = -INFINITY, L = 0.0f;
   float orot[K], oraw[K];
 #pragma unroll
   for (int k = 0; k < K; ++k) { orot[k] = 0.0f; oraw[k] = 0.0f; }
-  for (int base = PW * w; base < n_split; base += 4 * PW) {
+  for (int base = PW * w; base < n_split; base += NWV * PW) {
     float m = -INFINITY, l = 0.0f;
     if (lane < PW && base + lane < n_split) {
       m = part[(int64_t)(base + lane) * (D + 4) + D];
@@ -365,28 +365,36 @@ __global__ void __launch_bounds__(256) decode_combine_kernel(DecodeParams P) {
       }
     }
   }
-  if (lane == 0) { s_st[w][0] = M; s_st[w][1] = L; }
-  __syncthreads();
-  const float Mall = fmaxf(fmaxf(s_st[0][0], s_st[1][0]), fmaxf(s_st[2][0], s_st[3][0]));
-  const float sc = (M == -INFINITY) ? 0.0f : __expf(M - Mall);
+  float Lall = L;
+  if constexpr (NWV > 1) {
+    if (lane == 0) { s_st[w][0] = M; s_st[w][1] = L; }
+    __syncthreads();
+    float Mall = s_st[0][0];
 #pragma unroll
-  for (int k = 0; k < K; ++k) {
-    s_o[w][0][lane + 64 * k] = orot[k] * sc;
-    s_o[w][1][lane + 64 * k] = oraw[k] * sc;
-  }
-  __syncthreads();
-  if (w != 0) return;
-  float Lall = 0.0f;
+    for (int i = 1; i < NWV; ++i) Mall = fmaxf(Mall, s_st[i][0]);
+    const float sc = (M == -INFINITY) ? 0.0f : __expf(M - Mall);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float mi = s_st[i][0];
-    Lall += (mi == -INFINITY) ? 0.0f : __expf(mi - Mall) * s_st[i][1];
-  }
+    for (int k = 0; k < K; ++k) {
+      s_o[w][0][lane + 64 * k] = orot[k] * sc;
+      s_o[w][1][lane + 64 * k] = oraw[k] * sc;
+    }
+    __syncthreads();
+    if (w != 0) return;
+    Lall = 0.0f;
 #pragma unroll
-  for (int k = 0; k < K; ++k) {
-    const int c = lane + 64 * k;
-    orot[k] = (s_o[0][0][c] + s_o[1][0][c]) + (s_o[2][0][c] + s_o[3][0][c]);
-    oraw[k] = (s_o[0][1][c] + s_o[1][1][c]) + (s_o[2][1][c] + s_o[3][1][c]);
+    for (int i = 0; i < NWV; ++i) {
+      const float mi = s_st[i][0];
+      Lall += (mi == -INFINITY) ? 0.0f : __expf(mi - Mall) * s_st[i][1];
+    }
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int c = lane + 64 * k;
+      float a = 0.0f, r = 0.0f;
+#pragma unroll
+      for (int i = 0; i < NWV; ++i) { a += s_o[i][0][c]; r += s_o[i][1][c]; }
+      orot[k] = a;
+      oraw[k] = r;
+    }
   }
   // inverse WHT (the WHT itself) of the merged rotated-domain part
 #pragma unroll
@@ -433,7 +441,11 @@ hipError_t launch_decode_dg(const DecodeParams& P, int batch, hipStream_t stream
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(P.n_q, batch), dim3(256), 0, stream, P);
+  // four waves when there are more splits than one 16-split pass, else one
+  if (P.n_tsplit + P.n_wsplit > 16)
+    hipLaunchKernelGGL((decode_combine_kernel<D, 4>), dim3(P.n_q, batch), dim3(256), 0, stream, P);
+  else
+    hipLaunchKernelGGL((decode_combine_kernel<D, 1>), dim3(P.n_q, batch), dim3(64), 0, stream, P);
   return hipGetLastError();
 }
 
