@@ -817,16 +817,24 @@ __global__ void __launch_bounds__(kThreads) verify_mfma_kernel(DecodeParams P) {
   const int b = blockIdx.z / nsp, s = blockIdx.z % nsp;
   const int w = P.q_len;
   const int T = P.n_tiles[b], nw = P.n_win[b];
+  // the arguments this workgroup reads, pinned together: one round of scalar
+  // loads instead of a chain
+  const int64_t rs0 = P.rec_start[b], ws0 = P.win_start[b];
+  const int64_t seq_st = P.win_seq_stride, tok_st = P.win_tok_stride;
+  const float* p_q = P.q;
+  const float* p_qrot = P.q_rot;
+  asm volatile("" ::"s"(ns), "s"(nsp), "s"(w), "s"(T), "s"(nw), "s"(rs0), "s"(ws0), "s"(seq_st),
+               "s"(tok_st), "s"(p_q), "s"(p_qrot));
   Ctx c;
   const int64_t row0 = (int64_t)b * w * P.n_q * D;
-  c.q = P.q + row0;
-  c.rotate = P.q_rot == nullptr;
-  c.q_rot = c.rotate ? c.q : P.q_rot + row0;
+  c.q = p_q + row0;
+  c.rotate = p_qrot == nullptr;
+  c.q_rot = c.rotate ? c.q : p_qrot + row0;
   c.out = P.out;   // unused: partial output
-  c.records = P.records + P.rec_start[b] * (int64_t)P.n_kv * Rec<D, H>::bytes;
-  c.k = P.k_win + (int64_t)b * P.win_seq_stride + P.win_start[b] * P.win_tok_stride;
-  c.v = P.v_win + (int64_t)b * P.win_seq_stride + P.win_start[b] * P.win_tok_stride;
-  c.tok_stride = P.win_tok_stride;
+  c.records = P.records + rs0 * (int64_t)P.n_kv * Rec<D, H>::bytes;
+  c.k = P.k_win + (int64_t)b * seq_st + ws0 * tok_st;
+  c.v = P.v_win + (int64_t)b * seq_st + ws0 * tok_st;
+  c.tok_stride = tok_st;
   c.head_stride = P.win_head_stride;
   c.raw_base = (int64_t)kTile * T;
   c.pos0 = c.raw_base + nw - w;
