@@ -450,6 +450,9 @@ __device__ __forceinline__ void prefill_body(const Ctx& P) {
       }
       // bias b = sum_c q'_c kmin_c: every row of A is kmin 2^(13 - em) (hi, lo),
       // B is q' 2^-eq (hi, lo); rescaled to the score accumulator's 2^(-7 - ek - eq)
+      // matrix-core blocks run at raised wave priority, so the arbiter issues them
+      // while the other wave of the SIMD works through its vector blocks
+      __builtin_amdgcn_s_setprio(1);
       floatx4 bacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int k4 = 0; k4 < 4; ++k4) {
@@ -489,6 +492,7 @@ __device__ __forceinline__ void prefill_body(const Ctx& P) {
         ymax = fmaxf(fmaxf(ymax, y[bb][0]), y[bb][1]);
         ymax = fmaxf(fmaxf(ymax, y[bb][2]), y[bb][3]);
       }
+      __builtin_amdgcn_s_setprio(0);
       // lazy running maximum: raised only when the tile exceeds it by > tau
       const bool vis = j < T_row;
       const float tmax = rows_max(ymax) * beta;
@@ -547,6 +551,7 @@ __device__ __forceinline__ void prefill_body(const Ctx& P) {
         Wl[tt] = as_half8(wl[2 * tt][0], wl[2 * tt][1], wl[2 * tt + 1][0], wl[2 * tt + 1][1]);
       }
       const float* vcu = reinterpret_cast<const float*>(cst + kCVcu);
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         float4 vc[4];   // channels 64 qb + 16 g + 4 i .. + 3
@@ -573,6 +578,7 @@ __device__ __forceinline__ void prefill_body(const Ctx& P) {
         }
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     if (th == 1 && next) unpack_next();
     // tile j + 1 is in place and every wave is done with tile j's buffer
     __syncthreads();
