@@ -46,6 +46,27 @@ struct OpAdd { __device__ float operator()(float a, float b) const { return a + 
 struct OpMin { __device__ float operator()(float a, float b) const { return b < a ? b : a; } };
 struct OpMax { __device__ float operator()(float a, float b) const { return b > a ? b : a; } };
 
+// Value of lane l ^ M, by data-parallel moves and the gfx950 permlane swaps
+// (no LDS round trip): l ^ 4 is the half-row mirror (l ^ 7) followed by
+// quad_perm [3,2,1,0]; a swap of v with itself gives the lower lane of a pair
+// (own, partner) and the upper lane (partner, own).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int M>
+__device__ __forceinline__ float xor_lane(float v, int lane) {
+  if constexpr (M == 1) return dpp_mov<0xB1>(v);        // quad_perm [1,0,3,2]
+  else if constexpr (M == 2) return dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]
+  else if constexpr (M == 4) return dpp_mov<0x1B>(dpp_mov<0x141>(v));
+  else if constexpr (M == 8) return dpp_mov<0x128>(v);  // row_ror:8
+  else {
+    const auto r = (M == 32) ? __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false)
+                             : __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float((lane & M) ? r[0] : r[1]);
+  }
+}
+
 // One halving stage across lanes l and l^M for the first N live values.
 template <int N, int M, typename Op>
 __device__ __forceinline__ void halve_stage(float (&a)[32], int lane, Op op) {
@@ -54,7 +75,7 @@ __device__ __forceinline__ void halve_stage(float (&a)[32], int lane, Op op) {
   for (int i = 0; i < N / 2; ++i) {
     float send = up ? a[i] : a[i + N / 2];
     float keep = up ? a[i + N / 2] : a[i];
-    float recv = shfl_xor(send, M);
+    float recv = xor_lane<M>(send, lane);
     a[i] = op(keep, recv);
   }
 }
@@ -70,7 +91,7 @@ __device__ __forceinline__ float halve32(float (&a)[32], int lane, Op op) {
   halve_stage<8, 4>(a, lane, op);
   halve_stage<4, 8>(a, lane, op);
   halve_stage<2, 16>(a, lane, op);
-  return op(a[0], shfl_xor(a[0], 32));
+  return op(a[0], xor_lane<32>(a[0], lane));
 }
 
 __device__ __forceinline__ int brev5(int l) {
