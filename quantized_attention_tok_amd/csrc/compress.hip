@@ -119,9 +119,12 @@ compress_kernel(const float* __restrict__ kin, const float* __restrict__ vin,
   if constexpr (!GEN) { kb = 4; vb = 2; }
   const RecRT o = rec_rt(D, H, kb, vb);
 
-  // 64 KB, reused by every phase; the generic key packing stages one byte per
-  // code after two per-channel vectors (34 D floats)
-  constexpr int kSmem = (GEN && 34 * D > 16384) ? 34 * D : 16384;
+  // Reused by every phase: 64 KB, more for the padded WHT exchange (W x 128
+  // rows of J + 1 floats) and for the generic key packing (one byte per code
+  // after two per-channel vectors: 34 D floats).
+  constexpr int kXS = J + 1;   // exchange row stride: 2-way instead of 64-way bank conflicts
+  constexpr int kSmem0 = W * kTile * kXS > 16384 ? W * kTile * kXS : 16384;
+  constexpr int kSmem = (GEN && 34 * D > kSmem0) ? 34 * D : kSmem0;
   __shared__ float smem[kSmem];
 
   const int tid = threadIdx.x;
@@ -164,7 +167,7 @@ compress_kernel(const float* __restrict__ kin, const float* __restrict__ vin,
   }
   // ---- WHT: strides 32..D/2 across waves, J channel offsets per round ----
   if constexpr (W > 1) {
-    float* xch = smem;  // [W][128][J]
+    float* xch = smem;  // [W][128][kXS]
     constexpr int kPer = 2 * J / W;  // (token, offset) columns per thread
 #pragma unroll
     for (int r = 0; r < 32 / J; ++r) {
@@ -172,7 +175,7 @@ compress_kernel(const float* __restrict__ kin, const float* __restrict__ vin,
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int jj = 0; jj < J; ++jj)
-          xch[(w * kTile + 2 * lane + i) * J + jj] = x[i][r * J + jj];
+          xch[(w * kTile + 2 * lane + i) * kXS + jj] = x[i][r * J + jj];
       __syncthreads();
 #pragma unroll
       for (int k = 0; k < kPer; ++k) {
@@ -180,7 +183,7 @@ compress_kernel(const float* __restrict__ kin, const float* __restrict__ vin,
         const int t = idx / J, jj = idx % J;
         float y[W];
 #pragma unroll
-        for (int u = 0; u < W; ++u) y[u] = xch[(u * kTile + t) * J + jj];
+        for (int u = 0; u < W; ++u) y[u] = xch[(u * kTile + t) * kXS + jj];
 #pragma unroll
         for (int hs = 1; hs < W; hs <<= 1) {
 #pragma unroll
@@ -193,14 +196,14 @@ compress_kernel(const float* __restrict__ kin, const float* __restrict__ vin,
           }
         }
 #pragma unroll
-        for (int u = 0; u < W; ++u) xch[(u * kTile + t) * J + jj] = y[u];
+        for (int u = 0; u < W; ++u) xch[(u * kTile + t) * kXS + jj] = y[u];
       }
       __syncthreads();
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int jj = 0; jj < J; ++jj)
-          x[i][r * J + jj] = xch[(w * kTile + 2 * lane + i) * J + jj];
+          x[i][r * J + jj] = xch[(w * kTile + 2 * lane + i) * kXS + jj];
       __syncthreads();
     }
   }
