@@ -442,3 +442,59 @@ def test_decode_inkernel_rotation_and_workspace_reuse():
                                 workspace=ws)
     torch.cuda.synchronize()
     assert rel_l2(o2[0].cpu().numpy(), outs[0][0].cpu().numpy()) < 1e-6
+
+
+@pytest.mark.parametrize("with_rot", [True, False])
+def test_decode_batch_at_the_limit_mixed_views(with_rot):
+    """KVARN_MAX_BATCH = 64 sequences in one call (the per-sequence argument
+    arrays at their size): tile-only, window-only and mixed sequences, records
+    from a shared pool at scattered rows, windows at per-sequence offsets."""
+    say("decode batch 64", with_rot)
+    d, Hq, Hkv, B = 128, 8, 2, 64
+    rng = np.random.default_rng(64)
+    tiles = [int(x) for x in rng.integers(0, 4, size=B)]
+    wins = [int(x) for x in rng.integers(0, 41, size=B)]
+    for b in range(B):
+        if tiles[b] + wins[b] == 0:
+            wins[b] = 1
+    tiles[0], wins[0] = 3, 0      # tiles only
+    tiles[1], wins[1] = 0, 33     # window only
+    recs_all, rec_start, KV = [], [], []
+    row = 5                        # the pool starts with unused rows
+    pool = [np.zeros((5, Hkv, kvarn.tile_bytes(d)), np.uint8)]
+    cap = max(wins) + 7
+    kw = np.zeros((B, cap, Hkv, d), np.float32)
+    vw = np.zeros_like(kw)
+    win_start = []
+    for b in range(B):
+        K, V = synth.make_kv(5000 + b, 128 * tiles[b] + wins[b], Hkv, d, 2)
+        if tiles[b]:
+            pool.append(oracle.compress_tiles(K, V, tiles[b]))
+        rec_start.append(row)
+        row += tiles[b]
+        ws = b % 7                 # window rows start at a per-sequence offset
+        kw[b, ws:ws + wins[b]] = K[128 * tiles[b]:]
+        vw[b, ws:ws + wins[b]] = V[128 * tiles[b]:]
+        win_start.append(ws)
+        KV.append((K, V))
+    recs = np.concatenate(pool)
+    q = synth.make_q(6000, B, Hq, d)
+    scale = 1 / math.sqrt(d)
+    qd = to_dev(q)
+    qr = kvarn.rotate_query(qd) if with_rot else None
+    out = kvarn.decode_attention(qd, qr, to_dev(recs), rec_start, tiles, to_dev(kw), to_dev(vw),
+                                 wins, scale, win_start=win_start)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    worst = 0.0
+    for b in range(B):
+        K, V = KV[b]
+        if tiles[b]:
+            kh, vh = oracle.dequant_records(recs[rec_start[b]:rec_start[b] + tiles[b]], d)
+        else:
+            kh = vh = np.zeros((0, Hkv, d))
+        lo = 128 * tiles[b]
+        ref = oracle.decode(q[b], kh, vh, tiles[b], K[lo:], V[lo:], scale)
+        worst = max(worst, rel_l2(got[b], ref))
+    say("worst rel_l2", worst)
+    assert worst < TOL
