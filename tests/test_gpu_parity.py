@@ -298,6 +298,31 @@ def test_prefill_small_prompt_every_row():
     assert rel_l2(out, ref) < TOL
 
 
+def test_prefill_raw_magnitude_jumps_every_row():
+    """Raw window rows whose magnitude jumps by orders of magnitude between and
+    inside 64-token staging steps, a query block far from unit scale, and the
+    same rows later inside compressed tiles: every row within the bar on its own."""
+    say("prefill raw magnitudes")
+    d, Hq, Hkv, W = 128, 8, 2, 256
+    n = 900
+    K, V = synth.make_kv(23, n, Hkv, d, 2)
+    Q = synth.make_q(23, n, Hq, d)
+    V[520:584] *= np.float32(1e4)
+    V[600:630, 1] *= np.float32(1e-3)
+    K[650:700] *= np.float32(1e-3)
+    K[700:740, 0] *= np.float32(6.0)
+    V[760:800] *= np.float32(3e5)
+    Q[820:880] *= np.float32(40.0)
+    out, recs = prefill_run(K, V, Q, W, 256, Hkv, d)
+    assert np.array_equal(recs, oracle.compress_tiles(K, V, recs.shape[0]))
+    kh, vh = oracle.dequant_records(recs, d)
+    ref = np.stack([oracle.prefill_row(Q[p], p, W, kh, vh, K, V, 1 / math.sqrt(d)) for p in range(n)])
+    num = np.linalg.norm((out.astype(np.float64) - ref).reshape(n, -1), axis=1)
+    rel = num / np.linalg.norm(ref.reshape(n, -1), axis=1)
+    say("per-row rel rms", float(np.sqrt(np.mean(rel ** 2))), "max", float(rel.max()))
+    assert np.sqrt(np.mean(rel ** 2)) < TOL and rel.max() < 10 * TOL
+
+
 
 @pytest.mark.parametrize("d,Hq,Hkv", [(256, 16, 4), (512, 8, 1)])
 def test_prefill_wide_heads_every_row_and_rechunk(d, Hq, Hkv):
