@@ -31,9 +31,9 @@
 // lane r again, so the softmax state of a row never moves between lanes.
 // After the last tile each row's O' is rotated back with the WHT butterflies
 // (in-lane, and across the four 16-lane rows with the gfx950 permlane swaps),
-// then the raw tokens are added 64 at a time: staged in LDS as fp16 hi + lo
-// operands, scored against the raw query and aggregated straight into the same
-// accumulator on the same fp16 MFMAs.
+// then the raw tokens are added with fp32 MFMAs (v_mfma_f32_16x16x4_f32):
+// scores from the raw query and raw keys, and the aggregate of raw values
+// straight into the same accumulator.
 #include <float.h>
 
 #include "kvarn_launch.h"
@@ -49,6 +49,8 @@ typedef __fp16 fp16x2 __attribute__((ext_vector_type(2)));   // cvt_pkrtz result
 
 constexpr int kRows = 16;                          // query rows per wave
 constexpr int kThreads = 512;                      // 8 waves
+constexpr int kRawTok = 32;                        // raw tokens staged per step
+constexpr int kRawRow = D + 4;                     // padded LDS row of raw K / V (floats)
 constexpr int kOpBytes = 32768;                    // one tile's K or V operands (fp16)
 // LDS: K operands of buffers 0 and 1, V operands of buffers 0 and 1, then the
 // two constant areas, so that every read of a tile is a lane offset plus an
@@ -59,18 +61,9 @@ constexpr int kCExp = 3072;                        // int ek, ev, em
 constexpr int kConstBytes = 3088;
 constexpr int kLdsK = 0, kLdsV = 2 * kOpBytes, kLdsC = 4 * kOpBytes;
 constexpr int kLdsBytes = kLdsC + 2 * kConstBytes;
-// Raw tokens (over the tile buffers): a step of 64 tokens as fp16 hi and lo
-// operands; keys token-major (row = token, 16-byte padded so that 16
-// consecutive rows fall in 16 distinct bank groups), values channel-major
-// (row = value row, see raw_stage); then 16 floats of step maxima.
-constexpr int kRStep = 64;
-constexpr int kRKRow = 2 * D + 16;
-constexpr int kRVRow = 2 * kRStep + 16;
-constexpr int kRKH = 0, kRKL = kRStep * kRKRow;
-constexpr int kRVH = 2 * kRStep * kRKRow, kRVL = kRVH + D * kRVRow;
-constexpr int kRMax = kRVL + D * kRVRow;
+constexpr int kLdsRaw = 2 * kRawTok * kRawRow * 4; // raw K and V rows (over the tiles)
 constexpr int kMergeO = 4 * 8 * 64 * 16;           // merge: O of the h = 1 waves, then (m, l)
-static_assert(kRMax + 64 <= kLdsBytes && kMergeO + 4 * 64 * 8 <= kLdsBytes, "staging fits");
+static_assert(kLdsRaw <= kLdsBytes && kMergeO + 4 * 64 * 8 <= kLdsBytes, "staging fits");
 // Lazy softmax rescaling: a row's running maximum is raised only when a tile's
 // maximum exceeds it by more than kTau (log2 units), so probabilities stay
 // below 2^kTau and the output is rescaled only on those tiles.
@@ -261,91 +254,6 @@ __device__ __forceinline__ int tiles_at(int64_t p, int window) {
 }
 
 __device__ __forceinline__ half2v as_h2(uint32_t x) { return __builtin_bit_cast(half2v, x); }
-
-// fp16 hi (rounded toward zero, so never to infinity below 2^16) and lo parts
-// of a pair, packed: x = hi + lo to about 2^-22 relative
-__device__ __forceinline__ void split_pair(float a, float b, uint32_t& hi, uint32_t& lo) {
-  const fp16x2 h = __builtin_amdgcn_cvt_pkrtz(a, b);
-  const fp16x2 l = __builtin_amdgcn_cvt_pkrtz(a - (float)h.x, b - (float)h.y);
-  hi = __builtin_bit_cast(uint32_t, h);
-  lo = __builtin_bit_cast(uint32_t, l);
-}
-
-// What one thread stages of a raw step [t0, t0 + 64): keys of token
-// (tid + 512 e) / 16, channels 8 ((tid + 512 e) % 16) .. + 7 (e = 0, 1, in k[2 e],
-// k[2 e + 1]); values of channels c1 = 4 (lane % 16) + lane / 16 and c1 + 64
-// (v[j], v[8 + j]) of the eight tokens 32 h + 16 (j / 4) + 4 g + j % 4 with
-// (h, g) = (wave / 4, wave % 4).  Tokens at or past the step's n_left read as
-// zero.
-struct RawRegs {
-  float4 k[4];
-  float v[16];
-};
-
-// kbase / vbase point at the key / value row of token t0 (head offset
-// included); koff is this thread's key offset (token (tid / 16) of the step,
-// channel 8 (tid % 16)), c1 its value channel.  The value tokens of a wave are
-// wave-uniform, so their loads take one scalar address each.
-__device__ __forceinline__ void raw_load(const float* kbase, const float* vbase, int64_t tok_stride, int64_t koff,
-                                         int c1, int tk0, int wvu, int64_t n_left, RawRegs& rr) {
-#pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
-    if (tk0 + 32 * e < n_left) {
-      const float4* src = reinterpret_cast<const float4*>(kbase + koff + 32 * e * tok_stride);
-      a = src[0];
-      b = src[1];
-    }
-    rr.k[2 * e] = a;
-    rr.k[2 * e + 1] = b;
-  }
-  const int h = wvu >> 2, g = wvu & 3;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int tt = 32 * h + 16 * (j >> 2) + 4 * g + (j & 3);   // wave-uniform
-    float x0 = 0.0f, x1 = 0.0f;
-    if (tt < n_left) {
-      const float* src = vbase + tt * tok_stride;
-      x0 = src[c1];
-      x1 = src[c1 + 64];
-    }
-    rr.v[j] = x0;
-    rr.v[8 + j] = x1;
-  }
-}
-
-// Writes a staged step as fp16 hi / lo operands, keys times ks, values times vs.
-// Key row = token, channels in order.  Value row l (< 64) holds channel
-// 4 (l % 16) + l / 16, row 64 + l that channel + 64, so that rows 16 m .. 16 m + 15
-// are the A rows of aggregate block m (channels 64 (m / 4) + 4 n' + m % 4); in a
-// row, the 16 bytes 16 (4 h + g) hold the eight tokens of wave (h, g) in the
-// order of the score layout: K slot 8 g + 4 b + i is token 32 h + 16 b + 4 g + i.
-__device__ __forceinline__ void raw_stage(const RawRegs& rr, uint8_t* lds, int tid, float ks, float vs) {
-  const int wv = tid >> 6, lane = tid & 63;
-#pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    const int it = tid + 512 * e;
-    const float4 a = rr.k[2 * e], b = rr.k[2 * e + 1];
-    uint32_t hi[4], lo[4];
-    split_pair(a.x * ks, a.y * ks, hi[0], lo[0]);
-    split_pair(a.z * ks, a.w * ks, hi[1], lo[1]);
-    split_pair(b.x * ks, b.y * ks, hi[2], lo[2]);
-    split_pair(b.z * ks, b.w * ks, hi[3], lo[3]);
-    uint8_t* dst = lds + (it >> 4) * kRKRow + 16 * (it & 15);
-    *reinterpret_cast<uint4*>(dst + kRKH) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-    *reinterpret_cast<uint4*>(dst + kRKL) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-  }
-  const int h = wv >> 2, g = wv & 3;
-#pragma unroll
-  for (int cc = 0; cc < 2; ++cc) {
-    uint32_t hi[4], lo[4];
-#pragma unroll
-    for (int pr = 0; pr < 4; ++pr) split_pair(rr.v[8 * cc + 2 * pr] * vs, rr.v[8 * cc + 2 * pr + 1] * vs, hi[pr], lo[pr]);
-    uint8_t* dst = lds + (lane + 64 * cc) * kRVRow + 16 * (4 * h + g);
-    *reinterpret_cast<uint4*>(dst + kRVH) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-    *reinterpret_cast<uint4*>(dst + kRVL) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-  }
-}
 __device__ __forceinline__ uint32_t as_u(half2v x) { return __builtin_bit_cast(uint32_t, x); }
 
 // What one workgroup computes: the query rows [0, chunk) of one sequence at
@@ -720,40 +628,16 @@ __device__ __forceinline__ void prefill_body(const Ctx& P) {
         }
   }
 
-  // ---- raw tokens [128 T(p), p] in steps of 64, 32 per wave (tokens 32 th ..
-  // + 31 of the step), on v_mfma_f32_16x16x32_f16 with fp16 hi + lo operands
-  // (hi hi + hi lo + lo hi, about 2^-22 relative).  Keys of a step are scaled by
-  // one power of two that puts their maximum into [2^13, 2^14); values by 2^sv,
-  // where sv changes only when a step's values would overflow fp16 or drop into
-  // its subnormal range, and the accumulator is kept in units of 2^sv so that
-  // the aggregate adds into it directly. ----
-  // raw query of row n as B operands: channels 32 k4 + 8 g .. + 7, times 2^rho
-  uint32_t rqh[4][4], rql[4][4];
-  float rf;   // log2-domain score factor before the keys' step exponent
-  {
-    const float* qp = P.q + ((int64_t)(row_ok ? r0 + n : 0) * P.n_q + hq) * D + 8 * g;
-    float x[4][8];
-    float qm = 0.0f;
+  // ---- raw tokens [128 T(p), p] on fp32 MFMA, 16-token blocks of parity th ----
+  float4 qr[8];   // raw query of row n, channels 16 jj + 4 g .. + 3
 #pragma unroll
-    for (int k4 = 0; k4 < 4; ++k4) {
-      float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
-      if (row_ok) {
-        a = *reinterpret_cast<const float4*>(qp + 32 * k4);
-        b = *reinterpret_cast<const float4*>(qp + 32 * k4 + 4);
-      }
-      x[k4][0] = a.x; x[k4][1] = a.y; x[k4][2] = a.z; x[k4][3] = a.w;
-      x[k4][4] = b.x; x[k4][5] = b.y; x[k4][6] = b.z; x[k4][7] = b.w;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) qm = fmaxf(qm, fabsf(x[k4][j]));
-    }
-    const int rho = fp16_scale_exp(rows_max(qm));
-    const float qs = pow2i(rho);
-    rf = scale_log2 * pow2i(-rho);
-#pragma unroll
-    for (int k4 = 0; k4 < 4; ++k4)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) split_pair(x[k4][2 * i] * qs, x[k4][2 * i + 1] * qs, rqh[k4][i], rql[k4][i]);
+  for (int jj = 0; jj < 8; ++jj) {
+    qr[jj] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (row_ok)
+      qr[jj] = *reinterpret_cast<const float4*>(P.q + ((int64_t)(r0 + n) * P.n_q + hq) * D + 16 * jj + 4 * g);
   }
+  float* s_k = reinterpret_cast<float*>(s_lds);   // over the tile buffers
+  float* s_v = s_k + kRawTok * kRawRow;
   const int64_t raw_lo = (int64_t)kTile * tiles_at(p_first, P.window);
   const int64_t wave_lo = (int64_t)kTile * tiles_at(P.pos0 + r0, P.window);
   const int64_t row_lo = (int64_t)kTile * T_row;
@@ -762,139 +646,89 @@ __device__ __forceinline__ void prefill_body(const Ctx& P) {
   // raw tokens of this workgroup: [r_lo, r_hi)
   const int64_t r_lo = raw_lo > P.ra ? raw_lo : P.ra;
   const int64_t r_hi = p_last + 1 < P.rb ? p_last + 1 : P.rb;
-  const bool any_raw = P.raw && r_lo < r_hi;   // workgroup-uniform
-  float* s_max = reinterpret_cast<float*>(s_lds + kRMax);
-  int sv = 0;
-  // per-thread staging offsets (loop-invariant) and the wave index as a scalar
-  const int wvu = __builtin_amdgcn_readfirstlane(wv);
-  const int tk0 = tid >> 4;
-  const int64_t koff = (int64_t)tk0 * P.tok_stride + 8 * (tid & 15);
-  const int c1 = 4 * (lane & 15) + (lane >> 4);
-  RawRegs rr;
-  if (any_raw)
-    raw_load(kbase + (r_lo - P.raw_base) * P.tok_stride, vbase + (r_lo - P.raw_base) * P.tok_stride, P.tok_stride,
-             koff, c1, tk0, wvu, r_hi - r_lo, rr);
-  for (int64_t t0 = r_lo; any_raw && t0 < r_hi; t0 += kRStep) {
-    {   // step maxima of |k| and |v|, one per wave
-      float km = 0.0f, vm = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        km = fmaxf(km, fmaxf(fmaxf(fabsf(rr.k[e].x), fabsf(rr.k[e].y)), fmaxf(fabsf(rr.k[e].z), fabsf(rr.k[e].w))));
-#pragma unroll
-      for (int j = 0; j < 16; ++j) vm = fmaxf(vm, fabsf(rr.v[j]));
-      km = wave_max_nn(km);
-      vm = wave_max_nn(vm);
-      if (lane == 0) {
-        s_max[wv] = km;
-        s_max[8 + wv] = vm;
-      }
-    }
-    __syncthreads();   // the maxima are in; every wave is done with the previous step's operands
-    float kmax, vmax;
+  for (int64_t t0 = r_lo; P.raw && t0 < r_hi; t0 += kRawTok) {
+    __syncthreads();   // previous readers of the staging rows are done
     {
-      const float4 a = *reinterpret_cast<const float4*>(s_max);
-      const float4 b = *reinterpret_cast<const float4*>(s_max + 4);
-      const float4 c = *reinterpret_cast<const float4*>(s_max + 8);
-      const float4 d = *reinterpret_cast<const float4*>(s_max + 12);
-      kmax = fmaxf(fmaxf(fmaxf(a.x, a.y), fmaxf(a.z, a.w)), fmaxf(fmaxf(b.x, b.y), fmaxf(b.z, b.w)));
-      vmax = fmaxf(fmaxf(fmaxf(c.x, c.y), fmaxf(c.z, c.w)), fmaxf(fmaxf(d.x, d.y), fmaxf(d.z, d.w)));
-    }
-    const int ek = fp16_scale_exp(kmax);
-    if (vmax > 0.0f) {
-      const int es = fp16_scale_exp(vmax);   // vmax 2^es in [2^13, 2^14)
-      if (sv > es + 1 || sv < es - 9) {      // 2^sv would overflow or lose bits: change units
-        const int dd = es - sv;
-        const float c = pow2i(dd < -126 ? -126 : (dd > 127 ? 127 : dd));
+      const int r = tid >> 4, c4 = tid & 15;
+      const int64_t t = t0 + r;
+      float4 kx[2], vx[2];
+      if (t < r_hi) {
+        const float4* rk = reinterpret_cast<const float4*>(kbase + (t - P.raw_base) * P.tok_stride);
+        const float4* rv = reinterpret_cast<const float4*>(vbase + (t - P.raw_base) * P.tok_stride);
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
+        for (int e = 0; e < 2; ++e) {
+          kx[e] = rk[c4 + 16 * e];
+          vx[e] = rv[c4 + 16 * e];
+        }
+      } else {
 #pragma unroll
-          for (int kk = 0; kk < 4; ++kk)
+        for (int e = 0; e < 2; ++e) {
+          kx[e] = make_float4(0.f, 0.f, 0.f, 0.f);
+          vx[e] = kx[e];
+        }
+      }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) O[qb][kk][i] *= c;
-        sv = es;
+      for (int e = 0; e < 2; ++e) {
+        *reinterpret_cast<float4*>(s_k + r * kRawRow + 4 * (c4 + 16 * e)) = kx[e];
+        *reinterpret_cast<float4*>(s_v + r * kRawRow + 4 * (c4 + 16 * e)) = vx[e];
       }
     }
-    raw_stage(rr, s_lds, tid, pow2i(ek), pow2i(sv));
-    if (t0 + kRStep < r_hi)
-      raw_load(kbase + (t0 + kRStep - P.raw_base) * P.tok_stride, vbase + (t0 + kRStep - P.raw_base) * P.tok_stride,
-               P.tok_stride, koff, c1, tk0, wvu, r_hi - t0 - kRStep, rr);
-    __syncthreads();   // the step's operands are in
-    const int64_t tb = t0 + 32 * th;
-    if (!active || tb > p_wlast || tb >= r_hi || tb + 31 < wave_lo) continue;   // wave-uniform
-    // S^T[t][r]: block b = tokens tb + 16 b + (A row), lane (g, n): tokens tb + 16 b + 4 g + i of row n
-    floatx4 acc[2];
+    __syncthreads();
+    const int sb = th;
+    const int64_t tb = t0 + 16 * sb;
+    if (!active || tb > p_wlast || tb >= r_hi || tb + 15 < wave_lo) continue;   // wave-uniform
+    // S^T[t][r]: A = raw keys (row n = token tb + n), B = raw query of row n;
+    // MFMA (jj, e) contracts channels 16 jj + 4 g' + e over K slots g'
+    floatx4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      acc[b] = (floatx4){0.f, 0.f, 0.f, 0.f};
-      const uint8_t* kr = s_lds + (32 * th + 16 * b + n) * kRKRow + 16 * g;
-#pragma unroll
-      for (int k4 = 0; k4 < 4; ++k4) {
-        const uint4 ah = *reinterpret_cast<const uint4*>(kr + kRKH + 64 * k4);
-        const uint4 al = *reinterpret_cast<const uint4*>(kr + kRKL + 64 * k4);
-        const half8 Ah = as_half8(ah.x, ah.y, ah.z, ah.w), Al = as_half8(al.x, al.y, al.z, al.w);
-        const half8 Qh = as_half8(rqh[k4][0], rqh[k4][1], rqh[k4][2], rqh[k4][3]);
-        const half8 Ql = as_half8(rql[k4][0], rql[k4][1], rql[k4][2], rql[k4][3]);
-        acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, Qh, acc[b], 0, 0, 0);
-        acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, Ql, acc[b], 0, 0, 0);
-        acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Al, Qh, acc[b], 0, 0, 0);
-      }
+    for (int jj = 0; jj < 8; ++jj) {
+      const float4 ka = *reinterpret_cast<const float4*>(s_k + (16 * sb + n) * kRawRow + 16 * jj + 4 * g);
+      sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(ka.x, qr[jj].x, sacc, 0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(ka.y, qr[jj].y, sacc, 0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(ka.z, qr[jj].z, sacc, 0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(ka.w, qr[jj].w, sacc, 0, 0, 0);
     }
-    const float f = rf * pow2i(-ek);
-    float y[2][4];
-    float ymax = -INFINITY;
+    // lane (g, n): tokens tb + 4 g + i of row n
+    float sv[4];
+    float tmax = -INFINITY;
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int i = 0; i < 4; ++i) {
+      const int64_t t = tb + 4 * g + i;
+      const bool vis = row_ok && t >= row_lo && t <= prow && t < r_hi;
+      sv[i] = vis ? sacc[i] * scale_log2 : -INFINITY;
+      tmax = fmaxf(tmax, sv[i]);
+    }
+    tmax = rows_max(tmax);
+    const float m_new = fmaxf(m_run, tmax);
+    const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    float pv[4], psum = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t t = tb + 16 * b + 4 * g + i;
-        const bool vis = row_ok && t >= row_lo && t <= prow && t < r_hi;
-        y[b][i] = vis ? acc[b][i] * f : -INFINITY;
-        ymax = fmaxf(ymax, y[b][i]);
-      }
-    // lazy running maximum as over the tiles (probabilities stay below 2^tau)
-    const float tmax = rows_max(ymax);
-    const bool raise = !(tmax <= m_run + kTau);   // never for a row that sees nothing here
-    const float m_new = raise ? tmax : m_run;
-    const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;   // 0 from -inf
+    for (int i = 0; i < 4; ++i) {
+      pv[i] = __builtin_amdgcn_exp2f(sv[i] - m_use);
+      psum += pv[i];
+    }
+    l_run = l_run * alpha + rows_sum(psum);
     m_run = m_new;
-    l_run *= alpha;
-    if (__builtin_amdgcn_ballot_w64(raise) != 0) {
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) O[qb][kk][i] *= alpha;
-    }
-    const float mu = (m_run == -INFINITY) ? 0.0f : m_run;
-    float pv[2][4], psum = 0.0f;
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pv[b][i] = __builtin_amdgcn_exp2f(y[b][i] - mu);
-        psum += pv[b][i];
-      }
-    l_run += rows_sum(psum);
-    // O^T[c][n] += sum_t v[t][c] p[n][t]: K slot 8 g + 4 b + i is token tb + 16 b + 4 g + i;
-    // block 4 qb + kk holds channels 64 qb + 4 n' + kk in its A rows n'
-    uint32_t wh[4], wl[4];
-#pragma unroll
-    for (int pr = 0; pr < 4; ++pr) split_pair(pv[pr >> 1][2 * (pr & 1)], pv[pr >> 1][2 * (pr & 1) + 1], wh[pr], wl[pr]);
-    const half8 Wh = as_half8(wh[0], wh[1], wh[2], wh[3]), Wl = as_half8(wl[0], wl[1], wl[2], wl[3]);
-    const uint8_t* vr = s_lds + n * kRVRow + 16 * (4 * th + g);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int blk = 4 * qb + kk;
-        const uint4 ah = *reinterpret_cast<const uint4*>(vr + kRVH + 16 * blk * kRVRow);
-        const uint4 al = *reinterpret_cast<const uint4*>(vr + kRVL + 16 * blk * kRVRow);
-        const half8 Ah = as_half8(ah.x, ah.y, ah.z, ah.w), Al = as_half8(al.x, al.y, al.z, al.w);
-        O[qb][kk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, Wh, O[qb][kk], 0, 0, 0);
-        O[qb][kk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, Wl, O[qb][kk], 0, 0, 0);
-        O[qb][kk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Al, Wh, O[qb][kk], 0, 0, 0);
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) O[qb][kk][i] *= alpha;
+    // O^T[c][n] += sum_t v[t][c] p[n][t]; step i: K slot g is token tb + 4 g + i,
+    // A row n' is channel 64 qb + 4 n' + kk
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const float4 vv = *reinterpret_cast<const float4*>(s_v + (16 * sb + 4 * g + i) * kRawRow + 64 * qb + 4 * n);
+        O[qb][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(vv.x, pv[i], O[qb][0], 0, 0, 0);
+        O[qb][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(vv.y, pv[i], O[qb][1], 0, 0, 0);
+        O[qb][2] = __builtin_amdgcn_mfma_f32_16x16x4f32(vv.z, pv[i], O[qb][2], 0, 0, 0);
+        O[qb][3] = __builtin_amdgcn_mfma_f32_16x16x4f32(vv.w, pv[i], O[qb][3], 0, 0, 0);
       }
+    }
   }
 
   // ---- merge the two token halves of each row group, normalise, store ----
@@ -916,7 +750,7 @@ __device__ __forceinline__ void prefill_body(const Ctx& P) {
   const float fa = (m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run - M);
   const float fb = (ml2.x == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(ml2.x - M);
   const float lsum = l_run * fa + ml2.y * fb;
-  float ca = fa * pow2i(-sv), cb = fb * pow2i(-sv);   // back from units of 2^sv
+  float ca = fa, cb = fb;
   float* o;
   if (partial) {
     o = P.part + (int64_t)(r0 + n) * P.part_row + (int64_t)hq * P.part_head;
