@@ -256,6 +256,33 @@ __device__ __forceinline__ int tiles_at(int64_t p, int window) {
 __device__ __forceinline__ half2v as_h2(uint32_t x) { return __builtin_bit_cast(half2v, x); }
 __device__ __forceinline__ uint32_t as_u(half2v x) { return __builtin_bit_cast(uint32_t, x); }
 
+// One thread's share of a raw staging step: floats 4 c4 .. + 3 and 4 c4 + 64 .. + 67
+// of the key and value rows of token t.  The load always reads a row of the
+// range (t clamped below r_hi) and ok marks whether t itself is in it, so that
+// no branch has to wait on the load.
+struct RawShare {
+  float4 k0, k1, v0, v1;
+  bool ok;
+};
+
+__device__ __forceinline__ float4 keep4(bool ok, float4 x) {
+  return make_float4(ok ? x.x : 0.0f, ok ? x.y : 0.0f, ok ? x.z : 0.0f, ok ? x.w : 0.0f);
+}
+
+__device__ __forceinline__ RawShare raw_fetch(const float* kbase, const float* vbase, int64_t tok_stride,
+                                              int64_t raw_base, int64_t t, int64_t r_hi, int c4) {
+  RawShare x;
+  x.ok = t < r_hi;
+  const int64_t tc = x.ok ? t : r_hi - 1;
+  const float4* rk = reinterpret_cast<const float4*>(kbase + (tc - raw_base) * tok_stride);
+  const float4* rv = reinterpret_cast<const float4*>(vbase + (tc - raw_base) * tok_stride);
+  x.k0 = rk[c4];
+  x.k1 = rk[c4 + 16];
+  x.v0 = rv[c4];
+  x.v1 = rv[c4 + 16];
+  return x;
+}
+
 // What one workgroup computes: the query rows [0, chunk) of one sequence at
 // positions pos0 + r, against its tiles [ja, jb) (clipped to the tiles the
 // rows see) and, if raw, its raw rows; either the final output or, with part
@@ -646,33 +673,19 @@ __device__ __forceinline__ void prefill_body(const Ctx& P) {
   // raw tokens of this workgroup: [r_lo, r_hi)
   const int64_t r_lo = raw_lo > P.ra ? raw_lo : P.ra;
   const int64_t r_hi = p_last + 1 < P.rb ? p_last + 1 : P.rb;
+  // this thread's staging share of a step: token t0 + tid / 16, floats 4 (tid % 16) and
+  // 4 (tid % 16) + 64 of its key and value rows; the next step's share is loaded
+  // into registers while the current step is computed
+  const int sr = tid >> 4, sc4 = tid & 15;
+  RawShare xs;
+  if (P.raw && r_lo < r_hi) xs = raw_fetch(kbase, vbase, P.tok_stride, P.raw_base, r_lo + sr, r_hi, sc4);
   for (int64_t t0 = r_lo; P.raw && t0 < r_hi; t0 += kRawTok) {
     __syncthreads();   // previous readers of the staging rows are done
-    {
-      const int r = tid >> 4, c4 = tid & 15;
-      const int64_t t = t0 + r;
-      float4 kx[2], vx[2];
-      if (t < r_hi) {
-        const float4* rk = reinterpret_cast<const float4*>(kbase + (t - P.raw_base) * P.tok_stride);
-        const float4* rv = reinterpret_cast<const float4*>(vbase + (t - P.raw_base) * P.tok_stride);
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          kx[e] = rk[c4 + 16 * e];
-          vx[e] = rv[c4 + 16 * e];
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          kx[e] = make_float4(0.f, 0.f, 0.f, 0.f);
-          vx[e] = kx[e];
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        *reinterpret_cast<float4*>(s_k + r * kRawRow + 4 * (c4 + 16 * e)) = kx[e];
-        *reinterpret_cast<float4*>(s_v + r * kRawRow + 4 * (c4 + 16 * e)) = vx[e];
-      }
-    }
+    *reinterpret_cast<float4*>(s_k + sr * kRawRow + 4 * sc4) = keep4(xs.ok, xs.k0);
+    *reinterpret_cast<float4*>(s_k + sr * kRawRow + 4 * (sc4 + 16)) = keep4(xs.ok, xs.k1);
+    *reinterpret_cast<float4*>(s_v + sr * kRawRow + 4 * sc4) = keep4(xs.ok, xs.v0);
+    *reinterpret_cast<float4*>(s_v + sr * kRawRow + 4 * (sc4 + 16)) = keep4(xs.ok, xs.v1);
+    if (t0 + kRawTok < r_hi) xs = raw_fetch(kbase, vbase, P.tok_stride, P.raw_base, t0 + kRawTok + sr, r_hi, sc4);
     __syncthreads();
     const int sb = th;
     const int64_t tb = t0 + 16 * sb;
