@@ -298,6 +298,26 @@ def test_prefill_small_prompt_every_row():
     assert rel_l2(out, ref) < TOL
 
 
+@pytest.mark.parametrize("W,chunk,Hq,Hkv,n", [(0, 100, 8, 8, 620), (1, 17, 4, 2, 300), (100, 333, 16, 2, 800),
+                                              (384, 1, 8, 1, 410), (128, 1000, 8, 4, 700)])
+def test_prefill_windows_ragged_chunks_and_gqa_every_row(W, chunk, Hq, Hkv, n):
+    """Windows 0, 1 and not a multiple of 128, chunks that cut 16-row column
+    blocks and tiles anywhere (down to one row, up to the whole prompt), and
+    query/KV head ratios 1, 2 and 8 on the head_dim-128 matrix-core kernel."""
+    say("prefill window/chunk/gqa", W, chunk, Hq, Hkv, n)
+    d = 128
+    K, V = synth.make_kv(60 + W + chunk, n, Hkv, d, 2)
+    Q = synth.make_q(60 + W + chunk, n, Hq, d)
+    out, recs = prefill_run(K, V, Q, W, chunk, Hkv, d)
+    assert recs.shape[0] == oracle.visible_tiles(n - 1, W)
+    assert np.array_equal(recs, oracle.compress_tiles(K, V, recs.shape[0]))
+    kh, vh = oracle.dequant_records(recs, d)
+    ref = np.stack([oracle.prefill_row(Q[p], p, W, kh, vh, K, V, 1 / math.sqrt(d)) for p in range(n)])
+    err = rel_l2(out, ref)
+    say("rel_l2", err)
+    assert err < TOL
+
+
 def test_prefill_raw_magnitude_jumps_every_row():
     """Raw window rows whose magnitude jumps by orders of magnitude between and
     inside 64-token staging steps, a query block far from unit scale, and the
