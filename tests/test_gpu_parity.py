@@ -543,3 +543,48 @@ def test_decode_batch_at_the_limit_mixed_views(with_rot):
         worst = max(worst, rel_l2(got[b], ref))
     say("worst rel_l2", worst)
     assert worst < TOL
+
+
+@pytest.mark.parametrize("Hq,Hkv,with_rot", [(16, 2, True), (32, 4, False), (8, 8, True), (4, 4, False)])
+def test_decode_gqa_8_and_1_ragged_batch(Hq, Hkv, with_rot):
+    """The head_dim-128 matrix-core decode with 8 query heads per KV head (all
+    eight in one MFMA column block) and with one, over a ragged batch: long and
+    short tile runs, windows from 1 token to past a 16-token split, a sequence
+    with tiles only; both query paths."""
+    say("decode gqa", Hq, Hkv, with_rot)
+    d = 128
+    tiles, wins = [40, 1, 7, 0], [300, 1, 0, 17]
+    B = len(tiles)
+    recs_all, rec_start, KV, row = [], [], [], 0
+    cap = max(wins)
+    kw = np.zeros((B, cap, Hkv, d), np.float32)
+    vw = np.zeros_like(kw)
+    for b in range(B):
+        K, V = synth.make_kv(7000 + 11 * b + Hq, 128 * tiles[b] + wins[b], Hkv, d, 2)
+        if tiles[b]:
+            recs_all.append(gpu_compress(K, V, tiles[b]))
+        rec_start.append(row)
+        row += tiles[b]
+        kw[b, :wins[b]] = K[128 * tiles[b]:]
+        vw[b, :wins[b]] = V[128 * tiles[b]:]
+        KV.append((K, V))
+    recs = np.concatenate(recs_all)
+    q = synth.make_q(7100 + Hq, B, Hq, d)
+    scale = 1 / math.sqrt(d)
+    qd = to_dev(q)
+    out = kvarn.decode_attention(qd, kvarn.rotate_query(qd) if with_rot else None, to_dev(recs), rec_start,
+                                 tiles, to_dev(kw), to_dev(vw), wins, scale)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    for b in range(B):
+        K, V = KV[b]
+        if tiles[b]:
+            mine = recs[rec_start[b]:rec_start[b] + tiles[b]]
+            assert np.array_equal(mine, oracle.compress_tiles(K, V, tiles[b]))
+            kh, vh = oracle.dequant_records(mine, d)
+        else:
+            kh = vh = np.zeros((0, Hkv, d))
+        lo = 128 * tiles[b]
+        ref = oracle.decode(q[b], kh, vh, tiles[b], K[lo:], V[lo:], scale)
+        err = rel_l2(got[b], ref)
+        assert err < TOL, (b, err)
