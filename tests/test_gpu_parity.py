@@ -142,7 +142,9 @@ def test_decode_8b_shape(ctx):
     K, V = synth.make_kv(2, ctx, Hkv, d, 2)
     q = synth.make_q(2, 1, Hq, d)
     recs = gpu_compress(K, V, T)
-    kh, vh = oracle.dequant_records(recs, d)
+    want = oracle.compress_tiles(K, V, T)
+    assert np.array_equal(recs, want)          # every record byte-identical to the oracle's
+    kh, vh = oracle.dequant_records(want, d)
     kw = K[128 * T:][None]
     vw = V[128 * T:][None]
     scale = 1 / math.sqrt(d)
@@ -151,10 +153,6 @@ def test_decode_8b_shape(ctx):
     err = rel_l2(got[0], ref)
     say("rel_l2", err)
     assert err < TOL
-    # spot-check byte parity of a few records against the oracle compressor
-    for j in (0, T // 2, T - 1):
-        want = oracle.compress_tiles(K[128 * j:128 * (j + 1)], V[128 * j:128 * (j + 1)], 1)
-        assert np.array_equal(recs[j:j + 1], want)
 
 
 def test_decode_qwen06b_64_steps_with_appends():
@@ -374,7 +372,9 @@ def test_prefill_8b_prompt_sampled_rows_and_rechunk_identity():
         out_c, recs_c = prefill_run(K, V, Q, W, chunk, Hkv, d)
         assert np.array_equal(recs_c, recs512)          # tiles are schedule-independent
         assert rel_l2(out_c, out512) < 1e-6
-    kh, vh = oracle.dequant_records(recs512, d)
+    want = oracle.compress_tiles(K, V, 119)
+    assert np.array_equal(recs512, want)       # every record byte-identical to the oracle's
+    kh, vh = oracle.dequant_records(want, d)
     rows = sorted(set(list(range(0, 1024, 37)) + [383, 384, 511, 512, 639, 640, 8191, 8192, n - 1]
                       + list(range(0, n, 61))[:60]))
     ref = np.stack([oracle.prefill_row(Q[p], p, W, kh, vh, K, V, 1 / math.sqrt(d)) for p in rows])
@@ -444,7 +444,9 @@ def test_decode_multi_query_verify_8b_shape():
     K, V = synth.make_kv(4, ctx, Hkv, d, 2)
     q = synth.make_q(4, w, Hq, d)[None]
     recs = gpu_compress(K, V, T)
-    kh, vh = oracle.dequant_records(recs, d)
+    want = oracle.compress_tiles(K, V, T)
+    assert np.array_equal(recs, want)
+    kh, vh = oracle.dequant_records(want, d)
     n_w = ctx - 128 * T
     scale = 1 / math.sqrt(d)
     out = kvarn.decode_attention(to_dev(q), None, to_dev(recs), [0], [T], to_dev(K[128 * T:][None]),
@@ -467,7 +469,9 @@ def test_decode_inkernel_rotation_and_workspace_reuse():
     T = oracle.visible_tiles(ctx - 1, W)
     K, V = synth.make_kv(31, ctx, Hkv, d, 2)
     recs = gpu_compress(K, V, T)
-    kh, vh = oracle.dequant_records(recs, d)
+    want = oracle.compress_tiles(K, V, T)
+    assert np.array_equal(recs, want)
+    kh, vh = oracle.dequant_records(want, d)
     qd_all = synth.make_q(31, 3, Hq, d)
     kw = to_dev(K[128 * T:][None]); vw = to_dev(V[128 * T:][None]); rd = to_dev(recs)
     nb = kvarn.decode_workspace_bytes(to_dev(qd_all[:1]), None, rd, [0], [T], kw, vw, [ctx - 128 * T], 0.1)
