@@ -196,7 +196,8 @@ def verify_case(torch, kvarn, synth, ctx, width, reps=20, seed=2, f16=False):
 
 def prefill_case(torch, kvarn, synth, SequenceCache, d, Hq, Hkv, n, chunk, reps, W=256):
     """Chunked prefill of an n-token prompt in one graph: raw row copies, tile
-    compression, query rotation and prefill attention for every chunk."""
+    compression, query rotation (inside the prefill kernel at head_dim 128)
+    and prefill attention for every chunk."""
     dev = "cuda:0"
     Kp, Vp = synth.make_kv(4, n, Hkv, d, synth.outliers_for(d, 0.01))
     Qp = synth.make_q(4, n, Hq, d)
@@ -216,7 +217,7 @@ def prefill_case(torch, kvarn, synth, SequenceCache, d, Hq, Hkv, n, chunk, reps,
             c = min(chunk, n - p0)
             cache.append(kp[p0:p0 + c], vp[p0:p0 + c])
             q_c = qp[p0:p0 + c]
-            q_r = kvarn.rotate_query(q_c)
+            q_r = kvarn.rotate_query(q_c) if d != 128 else None   # head_dim 128: rotated in-kernel
             rb = 128 * kvarn.visible_tiles(p0, W)
             kvarn.prefill_attention(q_c, q_r, cache.records, cache.n_tiles, cache.k[rb:],
                                     cache.v[rb:], rb, p0, W, 1.0 / math.sqrt(d), out=outp[p0:p0 + c],

@@ -236,7 +236,10 @@ typedef struct kvarn_prefill_args {
   int32_t chunk;           /* C >= 1 query positions                            */
   float softmax_scale;
   const float* q;          /* device [C][n_q_heads][head_dim] raw               */
-  const float* q_rot;      /* device [C][n_q_heads][head_dim] rotated           */
+  const float* q_rot;      /* device [C][n_q_heads][head_dim] rotated; NULL at
+                              head_dim 128 over K4V2 records: the kernel then
+                              rotates each row itself (the vector-unit paths
+                              require it)                                      */
   const void* records;     /* device: record (j, h) at (j*n_kv_heads+h)*tile_bytes */
   int64_t n_record_rows;   /* tiles available; must be >= T(pos0 + C - 1)       */
   const float* k;          /* device raw keys: absolute position p, KV head h at

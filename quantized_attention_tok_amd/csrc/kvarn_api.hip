@@ -167,7 +167,8 @@ int validate_prefill(const kvarn_prefill_args* a, DecodePlan* plan) {
   if (a->n_q_heads % a->n_kv_heads != 0) return KVARN_E_UNSUPPORTED;
   const int G = a->n_q_heads / a->n_kv_heads;
   if (!(G == 1 || G == 2 || G == 4 || G == 8)) return KVARN_E_UNSUPPORTED;
-  if (!a->q || !a->q_rot || !a->out || !a->k || !a->v) return KVARN_E_INVALID;
+  if (!a->q || !a->out || !a->k || !a->v) return KVARN_E_INVALID;
+  if (!a->q_rot && !fused_decode(a->head_dim)) return KVARN_E_INVALID;
   const int64_t last = a->pos0 + a->chunk - 1;
   const int64_t t_first = prefill_tiles_at(a->pos0, a->window);
   const int64_t t_last = prefill_tiles_at(last, a->window);

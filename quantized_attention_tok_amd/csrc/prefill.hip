@@ -363,11 +363,13 @@ __device__ __forceinline__ void prefill_body(const Ctx& P) {
     if (ja + 1 < jend) load_tile<H>(recs + (int64_t)(ja + 1) * rstride, lane, wv, tr);
   }
   __syncthreads();
-  if (P.rotate) {   // q' = H q in registers: channel 32 k4 + 8 g + jj (g = lane bits 4, 5)
+  if (P.rotate) {   // q' = H q in registers: channel 32 k4 + 8 g + jj (g = lane bits 4, 5),
+                    // butterfly strides in ascending order, then one scale: the rounding of
+                    // the separate rotation (and of the oracle's fp32 transform), bit for bit
 #pragma unroll
     for (int k4 = 0; k4 < 4; ++k4)
 #pragma unroll
-      for (int hb = 1; hb < 8; hb <<= 1)   // channel bits 0-2
+      for (int hb = 1; hb < 8; hb <<= 1)   // strides 1, 2, 4: channel bits 0-2
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj)
           if (!(jj & hb)) {
@@ -376,7 +378,12 @@ __device__ __forceinline__ void prefill_body(const Ctx& P) {
             qv[k4][jj | hb] = a - b;
           }
 #pragma unroll
-    for (int kb = 1; kb < 4; kb <<= 1)     // channel bits 5, 6
+    for (int k4 = 0; k4 < 4; ++k4)
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj)       // strides 8, 16: channel bits 3, 4 across the 16-lane rows
+        qv[k4][jj] = bfly_rows<32>(bfly_rows<16>(qv[k4][jj], lane), lane);
+#pragma unroll
+    for (int kb = 1; kb < 4; kb <<= 1)     // strides 32, 64: channel bits 5, 6
 #pragma unroll
       for (int k4 = 0; k4 < 4; ++k4)
         if (!(k4 & kb)) {
@@ -390,10 +397,7 @@ __device__ __forceinline__ void prefill_body(const Ctx& P) {
 #pragma unroll
     for (int k4 = 0; k4 < 4; ++k4)
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {     // channel bits 3, 4 across the 16-lane rows
-        const float x = bfly_rows<16>(qv[k4][jj], lane);
-        qv[k4][jj] = bfly_rows<32>(x, lane) * wht_scale<D>();
-      }
+      for (int jj = 0; jj < 8; ++jj) qv[k4][jj] *= wht_scale<D>();
   }
   // q' of row n scaled into (-1, 1) by 2^-eq, as fp16 hi + lo pairs
   float qmax = 0.0f;
@@ -814,7 +818,8 @@ __global__ void __launch_bounds__(kThreads) prefill_mfma_kernel(PrefillParams P)
   c.ja = 0;
   c.jb = 0x7fffffff;
   c.raw = true;
-  c.rotate = false;
+  c.rotate = P.q_rot == nullptr;   // no rotated query given: rows rotate q in registers
+  if (c.rotate) c.q_rot = P.q;
   c.ra = 0;
   c.rb = INT64_MAX;
   c.part = nullptr;

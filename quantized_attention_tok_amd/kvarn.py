@@ -262,7 +262,8 @@ def prefill_attention(q, q_rot, records, n_record_rows, k, v, raw_base, pos0, wi
                       out=None, workspace=None, stream=None, f16_scales=False, kbits=4, vbits=2):
     """Chunk of C query positions [pos0, pos0+C) of one sequence.
 
-    q, q_rot: [C][Hq][d].  records: [rows][Hkv][tile_bytes] (tile j = row j).
+    q, q_rot: [C][Hq][d] (q_rot may be None at head_dim 128 over K4V2 records:
+    the kernel rotates the rows itself).  records: [rows][Hkv][tile_bytes] (tile j = row j).
     k, v: raw [n][Hkv][d] views whose row i is absolute position raw_base + i;
     f16_scales: the records carry f16 scales; kbits / vbits: their code widths."""
     assert k.stride(2) == 1 and k.stride() == v.stride()

@@ -187,6 +187,10 @@ def test_prefill_validation(L):
     a = args()
     # the matrix-core prefill keeps its whole state on chip
     assert L.kvarn_prefill_workspace_bytes(ctypes.byref(a)) == 0
+    # it rotates the rows itself when no rotated query is given; the vector paths need one
+    assert L.kvarn_prefill_workspace_bytes(ctypes.byref(args(q_rot=None))) == 0
+    assert L.kvarn_prefill_attention(ctypes.byref(args(head_dim=256, q_rot=None, tok_stride=512, head_stride=256)),
+                                     ctypes.c_void_p(FAKE), 1 << 30, None) == 1
     # the vector-unit prefill at head_dim 256 keeps split partials in the workspace
     a256 = args(head_dim=256, tok_stride=256 * 2, head_stride=256)
     need = L.kvarn_prefill_workspace_bytes(ctypes.byref(a256))
