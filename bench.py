@@ -157,6 +157,51 @@ def decode_case(torch, kvarn, synth, ctx, steps, warmup, seed=2, f16=False, kbit
     return info, reps * L, warm * L, (K, V, rec0, T, n_w, qs, scale)
 
 
+def wide_batch_case(torch, kvarn, synth, name, reps=10):
+    """The batched wide-head decode workload: 16 sequences whose contexts are
+    uniform in 1k-32k tokens in whole compressed tiles, each with a 256-token
+    FP32 window; one step = the query rotation and one decode call for the
+    batch, the records alternating between two copies (more than the LLC)."""
+    w = synth.WORKLOADS[name]
+    d, Hq, Hkv, W, B = w.head_dim, w.n_q_heads, w.n_kv_heads, w.window, w.batch
+    dev = "cuda:0"
+    tiles = [int(t) for t in synth.ragged_contexts(w.seed, B, w.extra["ctx_lo"], w.extra["ctx_hi"], W)]
+    tb = kvarn.tile_bytes(d)
+    rec_start = [int(x) for x in np.cumsum([0] + tiles[:-1])]
+    pool = torch.empty(sum(tiles), Hkv, tb, dtype=torch.uint8, device=dev)
+    kw = torch.empty(B, W, Hkv, d, device=dev)
+    vw = torch.empty_like(kw)
+    for b in range(B):
+        K, V = synth.batch_sequence_kv(w, b, 128 * tiles[b] + W)
+        kd = torch.from_numpy(K).to(dev)
+        vd = torch.from_numpy(V).to(dev)
+        kvarn.compress_tile(kd, vd, pool[rec_start[b]:rec_start[b] + tiles[b]], tiles[b])
+        kw[b] = kd[128 * tiles[b]:]
+        vw[b] = vd[128 * tiles[b]:]
+        del K, V, kd, vd
+    pools = [pool, pool.clone()]
+    q = torch.from_numpy(synth.make_q(w.seed, B, Hq, d)).to(dev)
+    qr = torch.empty_like(q)
+    out = torch.empty_like(q)
+    scale = 1.0 / math.sqrt(d)
+    wins = [W] * B
+    ws = torch.zeros(max(16, kvarn.decode_workspace_bytes(q, qr, pool, rec_start, tiles, kw, vw, wins, scale)),
+                     dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def run():
+        for p in pools:
+            kvarn.rotate_query(q, out=qr)
+            kvarn.decode_attention(q, qr, p, rec_start, tiles, kw, vw, wins, scale, out=out, workspace=ws)
+
+    ms, _ = graph_ms(torch, run, len(pools), reps)
+    alg = sum(decode_bytes(t, W, Hq, Hkv, d, tb) for t in tiles)
+    kv_tokens = sum(128 * t + W for t in tiles)
+    return {"head_dim": d, "n_q_heads": Hq, "n_kv_heads": Hkv, "batch": B, "tiles": tiles, "window": W,
+            "us_per_step": ms * 1e3, "kv_tokens_per_s": kv_tokens / (ms * 1e-3), "algorithmic_bytes": alg,
+            "achieved_GBps": alg / (ms * 1e-3) / 1e9, "includes": "query rotation, decode attention"}
+
+
 def verify_case(torch, kvarn, synth, ctx, width, reps=20, seed=2, f16=False):
     """Multi-query verify of `width` draft rows at the 8B decode shape: one call
     reads every record once for all rows (the workload of a decode step)."""
@@ -287,6 +332,16 @@ def main():
     log(f"verify width 8 at context {args.context}: {verify['us_per_call']:.2f} us per call "
         f"({verify['vs_decode_call']:.2f} decode calls)")
 
+    # ---- batched decode at the wide heads: 16 sequences, contexts 1k-32k ----
+    wide_batch = []
+    if not args.no_extra_contexts:
+        for name in ("wide_d256", "wide_d512"):
+            info = wide_batch_case(torch, kvarn, synth, name)
+            wide_batch.append(info)
+            log(f"batched decode head_dim {info['head_dim']} ({info['batch']} sequences, "
+                f"{sum(info['tiles'])} tiles): {info['us_per_step']:.1f} us per step, "
+                f"{info['achieved_GBps']:.0f} GB/s algorithmic")
+
     # ---- compression throughput (the prompt's 119 x 8 tile-heads in one launch) ----
     K, V, rec0, T, n_w, qs, scale = keep
     kd = torch.from_numpy(K).to(dev)
@@ -377,6 +432,7 @@ def main():
         "prefill": prefill,
         "prefill_wide_heads": prefill_wide,
         "verify": verify,
+        "decode_wide_heads_batch16": wide_batch,
         "compress": compress,
         "cpu_baseline": cpu,
     }

@@ -94,6 +94,11 @@ def make_q(seed: int, n_rows: int, n_q: int, d: int):
     return rq.standard_normal((n_rows, n_q, d), dtype=np.float32)
 
 
+def batch_sequence_kv(w: Workload, b: int, n_tokens: int):
+    """K, V of sequence b of a batched workload, from streams of its own."""
+    return make_kv(w.seed * 1000 + b, n_tokens, w.n_kv_heads, w.head_dim, w.n_outliers)
+
+
 def ragged_contexts(seed: int, batch: int, lo: int, hi: int, window: int):
     """Per-sequence compressed-tile counts for a ragged batch: a context drawn
     uniformly in [lo, hi] tokens and rounded to whole tiles, plus the window."""

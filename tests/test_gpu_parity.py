@@ -599,3 +599,66 @@ def test_decode_gqa_8_and_1_ragged_batch(Hq, Hkv, with_rot):
         ref = oracle.decode(q[b], kh, vh, tiles[b], K[lo:], V[lo:], scale)
         err = rel_l2(got[b], ref)
         assert err < TOL, (b, err)
+
+
+@pytest.mark.parametrize("name", ["wide_d256", "wide_d512"])
+def test_decode_wide_batch16_full_size_sampled(name):
+    """The batched wide-head workload at its full size (16 sequences, contexts
+    uniform in 1k-32k tokens in whole tiles, a 256-token window each), in the
+    one call the benchmark times: a sampled record of every sequence byte for
+    byte against the oracle; the two shortest sequences (which the oracle can
+    compress whole in seconds) every record and the output against the fp64
+    oracle; the three longest against one-sequence calls of their own (the
+    batch changes only the split plan, so they agree to rounding)."""
+    w = synth.WORKLOADS[name]
+    d, Hq, Hkv, W, B = w.head_dim, w.n_q_heads, w.n_kv_heads, w.window, w.batch
+    say("wide batch", name)
+    tiles = [int(t) for t in synth.ragged_contexts(w.seed, B, w.extra["ctx_lo"], w.extra["ctx_hi"], W)]
+    tb = kvarn.tile_bytes(d)
+    rec_start = [int(x) for x in np.cumsum([0] + tiles[:-1])]
+    pool = torch.empty(sum(tiles), Hkv, tb, dtype=torch.uint8, device=DEV)
+    kw = torch.empty(B, W, Hkv, d, device=DEV)
+    vw = torch.empty_like(kw)
+    order = sorted(range(B), key=lambda b: tiles[b])
+    short, long_ = order[:2], order[-3:]
+    keep = {}
+    pick = np.random.default_rng(w.seed)
+    for b in range(B):
+        K, V = synth.batch_sequence_kv(w, b, 128 * tiles[b] + W)
+        kd, vd = to_dev(K), to_dev(V)
+        kvarn.compress_tile(kd, vd, pool[rec_start[b]:rec_start[b] + tiles[b]], tiles[b])
+        kw[b] = kd[128 * tiles[b]:]
+        vw[b] = vd[128 * tiles[b]:]
+        torch.cuda.synchronize()
+        j = int(pick.integers(0, tiles[b]))
+        got_rec = pool[rec_start[b] + j:rec_start[b] + j + 1].cpu().numpy()
+        want_rec = oracle.compress_tiles(K[128 * j:128 * (j + 1)], V[128 * j:128 * (j + 1)], 1)
+        assert np.array_equal(got_rec, want_rec), (b, j)
+        if b in short:
+            keep[b] = (K, V)
+        del K, V, kd, vd
+    say("tiles", tiles)
+    q = synth.make_q(w.seed, B, Hq, d)
+    qd = to_dev(q)
+    scale = 1 / math.sqrt(d)
+    out = kvarn.decode_attention(qd, kvarn.rotate_query(qd), pool, rec_start, tiles, kw, vw, [W] * B, scale)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    for b in short:
+        K, V = keep[b]
+        want = oracle.compress_tiles(K, V, tiles[b])
+        assert np.array_equal(pool[rec_start[b]:rec_start[b] + tiles[b]].cpu().numpy(), want), b
+        kh, vh = oracle.dequant_records(want, d)
+        lo = 128 * tiles[b]
+        ref = oracle.decode(q[b], kh, vh, tiles[b], K[lo:], V[lo:], scale)
+        err = rel_l2(got[b], ref)
+        say("sequence", b, "tiles", tiles[b], "rel_l2", err)
+        assert err < TOL, (b, err)
+    for b in long_:
+        qb = qd[b:b + 1].contiguous()
+        one = kvarn.decode_attention(qb, kvarn.rotate_query(qb), pool, [rec_start[b]], [tiles[b]], kw[b:b + 1],
+                                     vw[b:b + 1], [W], scale)
+        torch.cuda.synchronize()
+        diff = rel_l2(one.cpu().numpy()[0], got[b])
+        say("sequence", b, "tiles", tiles[b], "batch vs alone", diff)
+        assert diff < 1e-5, (b, diff)
