@@ -57,7 +57,14 @@ __global__ void __launch_bounds__(kDecThreads) decode_partial_kernel(DecodeParam
   __shared__ float s_q[G][D];                 // rotated (tiles) or raw (window) query
   __shared__ float s_qt[D][G];                // q~ for the current tile, [channel][head]
   __shared__ float s_sc[G][kTile];            // scores, then probabilities
-  __shared__ float s_w[G][NG][kTile];         // p * vscale
+  __shared__ float s_w[NG][kTile][G];         // p * vscale, a token's heads contiguous
+  // D = 512: the two halves of the workgroup sum a token's scores over the two
+  // channel halves (otherwise only 128 threads would work on the keys); the
+  // softmax waves add them (ktok kept apart from the value scales that
+  // overwrite it)
+  constexpr int KP = D >= 512 ? 2 : 1;
+  __shared__ float s_kp[KP][G][kTile];
+  __shared__ float s_ktok[kTile];
   __shared__ float s_u[G][NG];                // sum p * vmin
   __shared__ float s_bias[G];
   __shared__ float s_m[G], s_l[G], s_alpha[G];
@@ -134,8 +141,30 @@ __global__ void __launch_bounds__(kDecThreads) decode_partial_kernel(DecodeParam
         if (lane == 0) s_bias[h] = a;
       }
       __syncthreads();
-      // ---- K scores: thread = (token, head half) ----
-      {
+      // ---- K scores: thread = (token, head half), or (token, channel half) at D = 512 ----
+      if constexpr (KP == 2) {
+        const int t = tid % kTile;
+        const int cp = tid / kTile;
+        float sacc[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) sacc[h] = 0.0f;
+        for (int c = cp * (D / 2); c < (cp + 1) * (D / 2); ++c) {
+          float z;
+          if constexpr (GEN) {
+            const int bit = kb * t;
+            const uint8_t* p = s_code + c * 16 * kb + (bit >> 3);
+            z = (float)((((uint32_t)p[0] | ((uint32_t)p[1] << 8)) >> (bit & 7)) & kmask);
+          } else {
+            const uint32_t byte = s_code[c * 64 + (t >> 1)];
+            z = (float)((byte >> ((t & 1) * 4)) & 15u);
+          }
+#pragma unroll
+          for (int h = 0; h < G; ++h) sacc[h] += s_qt[c][h] * z;
+        }
+#pragma unroll
+        for (int h = 0; h < G; ++h) s_kp[cp][h][t] = sacc[h];
+        if (cp == 0) s_ktok[t] = s_scale[2 * D + t];
+      } else {
         const int t = tid % kTile;
         const int hh = tid / kTile;
         if (hh < HH) {
@@ -177,7 +206,14 @@ __global__ void __launch_bounds__(kDecThreads) decode_partial_kernel(DecodeParam
       }
       // ---- online softmax over this tile: one wave per head ----
       for (int h = wv; h < G; h += kDecThreads / 64) {
-        const float s0 = s_sc[h][lane], s1 = s_sc[h][lane + 64];
+        float s0, s1;
+        if constexpr (KP == 2) {
+          s0 = P.scale * s_ktok[lane] * ((s_kp[0][h][lane] + s_kp[1][h][lane]) + s_bias[h]);
+          s1 = P.scale * s_ktok[lane + 64] * ((s_kp[0][h][lane + 64] + s_kp[1][h][lane + 64]) + s_bias[h]);
+        } else {
+          s0 = s_sc[h][lane];
+          s1 = s_sc[h][lane + 64];
+        }
         const float mt = wave_max(fmaxf(s0, s1));
         const float m_old = s_m[h];
         const float m_new = fmaxf(m_old, mt);
@@ -195,8 +231,8 @@ __global__ void __launch_bounds__(kDecThreads) decode_partial_kernel(DecodeParam
       __syncthreads();
       // w = p * vscale, u = sum p * vmin  (value scales are staged now)
       for (int i = tid; i < G * NG * kTile; i += kDecThreads) {
-        const int h = i / (NG * kTile), r = i % (NG * kTile), g = r / kTile, t = r % kTile;
-        s_w[h][g][t] = s_sc[h][t] * s_scale[D + t * NG + g];
+        const int g = i / (kTile * G), r = i % (kTile * G), t = r / G, h = r % G;
+        s_w[g][t][h] = s_sc[h][t] * s_scale[D + t * NG + g];
       }
       for (int i = wv; i < G * NG; i += kDecThreads / 64) {
         const int h = i / NG, g = i % NG;
@@ -226,7 +262,7 @@ __global__ void __launch_bounds__(kDecThreads) decode_partial_kernel(DecodeParam
               z = (float)((s_code[t * (D / 4) + (c >> 2)] >> sh) & 3u);
             }
 #pragma unroll
-            for (int h = 0; h < GV; ++h) pacc[h] += s_w[hv * GV + h][g][t] * z;
+            for (int h = 0; h < GV; ++h) pacc[h] += s_w[g][t][hv * GV + h] * z;
           }
           const float vch = s_scale[c];
 #pragma unroll
