@@ -55,16 +55,23 @@ __global__ void __launch_bounds__(kDecThreads) decode_partial_kernel(DecodeParam
   const int n_split = P.n_tsplit + P.n_wsplit;
 
   __shared__ float s_q[G][D];                 // rotated (tiles) or raw (window) query
-  __shared__ float s_qt[D][G];                // q~ for the current tile, [channel][head]
-  __shared__ float s_sc[G][kTile];            // scores, then probabilities
-  __shared__ float s_w[NG][kTile][G];         // p * vscale, a token's heads contiguous
+  // q~ of the current tile [channel][head] in the key phase, then w = p * vscale
+  // [group][token][head] (a token's heads contiguous) in the value phase: the
+  // same D * G floats
+  __shared__ __attribute__((aligned(16))) float s_qw[D * G];
+  float(*s_qt)[G] = reinterpret_cast<float(*)[G]>(s_qw);
+  float(*s_w)[kTile][G] = reinterpret_cast<float(*)[kTile][G]>(s_qw);
   // D = 512: the two halves of the workgroup sum a token's scores over the two
   // channel halves (otherwise only 128 threads would work on the keys); the
   // softmax waves add them (ktok kept apart from the value scales that
-  // overwrite it)
+  // overwrite it).  The scores, then probabilities, of head h then sit on
+  // the first half's sums of head h, which the same lanes read just before.
+  // With both overlays the head_dim-512 workgroup fits twice in a CU's LDS.
   constexpr int KP = D >= 512 ? 2 : 1;
   __shared__ float s_kp[KP][G][kTile];
   __shared__ float s_ktok[kTile];
+  __shared__ float s_sco[KP == 2 ? 1 : G * kTile];
+  float(*s_sc)[kTile] = reinterpret_cast<float(*)[kTile]>(KP == 2 ? &s_kp[0][0][0] : s_sco);
   __shared__ float s_u[G][NG];                // sum p * vmin
   __shared__ float s_bias[G];
   __shared__ float s_m[G], s_l[G], s_alpha[G];
