@@ -17,7 +17,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkvarn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["kvarn_api.hip", "compress.hip", "rotate.hip", "decode.hip", "decode_split.hip", "prefill.hip"]
+SOURCES = ["kvarn_api.hip", "compress.hip", "rotate.hip", "decode.hip", "decode_split.hip", "decode_wide.hip", "prefill.hip"]
 
 COMMON = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -49,7 +49,7 @@ __global__ void __launch_bounds__(kDecThreads) decode_partial_kernel(DecodeParam
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
-  const int split = blockIdx.x;
+  const int split = blockIdx.x + P.split0;
   const int kvh = blockIdx.y;
   const int b = blockIdx.z;
   const int n_split = P.n_tsplit + P.n_wsplit;
@@ -469,8 +469,24 @@ __global__ void __launch_bounds__(64 * NWV) decode_combine_kernel(DecodeParams P
 
 template <int D, int G>
 hipError_t launch_decode_dg(const DecodeParams& P, int batch, hipStream_t stream) {
-  dim3 grid(P.n_tsplit + P.n_wsplit, P.n_kv, batch);
   const bool gen = !(P.kb == 4 && P.vb == 2);
+  if (D >= 256 && !gen) {
+    // K4V2 at head_dim 256 / 512: tile splits on the matrix cores, the window
+    // splits on this kernel, launched over them alone
+    hipError_t e = hipSuccess;
+    if (P.n_tsplit > 0) e = launch_decode_wide_tiles(D, P, batch, stream);
+    if (e != hipSuccess) return e;
+    if (P.n_wsplit > 0) {
+      DecodeParams W = P;
+      W.split0 = P.n_tsplit;
+      const dim3 wgrid(P.n_wsplit, P.n_kv, batch);
+      if (P.h16)
+        hipLaunchKernelGGL((decode_partial_kernel<D, G, true, false>), wgrid, dim3(kDecThreads), 0, stream, W);
+      else
+        hipLaunchKernelGGL((decode_partial_kernel<D, G, false, false>), wgrid, dim3(kDecThreads), 0, stream, W);
+    }
+  } else {
+  dim3 grid(P.n_tsplit + P.n_wsplit, P.n_kv, batch);
   if (P.h16) {
     if (gen)
       hipLaunchKernelGGL((decode_partial_kernel<D, G, true, true>), grid, dim3(kDecThreads), 0, stream, P);
@@ -481,6 +497,7 @@ hipError_t launch_decode_dg(const DecodeParams& P, int batch, hipStream_t stream
       hipLaunchKernelGGL((decode_partial_kernel<D, G, false, true>), grid, dim3(kDecThreads), 0, stream, P);
     else
       hipLaunchKernelGGL((decode_partial_kernel<D, G, false, false>), grid, dim3(kDecThreads), 0, stream, P);
+  }
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -1,0 +1,417 @@
+// decode_wide.hip -- matrix-core tile splits of the split-tile decode for
+// head_dim 256 and 512 over K4V2 records on gfx950.
+//
+// The same two contractions as the head_dim-128 decode (SharpInference issue
+// #433 item 2: split tiles merged by a log-sum-exp combine; issue #180
+// Algorithm step 4: scales folded in at read time, the cache never
+// reconstructed):
+//   S[(h,part)][t] = sum_c q~[(h,part)][c] zK[t][c]        q~ = q' kscale
+//   O[(h,part)][c] = sum_t w_g[(h,part)][t] zV[t][c]       w_g = p vscale_{t,g}
+// on v_mfma_f32_16x16x32_f16 with fp32 operands split into fp16 hi/lo rows and
+// codes as fp16 subnormals (code in bits 4-7), over D / 32 channel steps for
+// the scores and D / 128 value groups of eight 16-channel blocks for the
+// aggregate; each value group has its own per-token scale, so its w operand
+// rows are written afresh.
+//
+// Workgroup = (tile split, KV head, sequence), 4 waves.  The split's tiles
+// run one after the other; wave w owns the 32-token quarter w of every tile
+// and keeps its own online softmax state (running max, sum, rescaled output
+// columns) across them, so the waves meet once per tile (the q~ operands of
+// the tile, double-buffered) and once at the end, where their states merge
+// into one partial per query head.  The partial holds the rotated-domain
+// output sum, the running max in natural-log units and the sum of weights,
+// as the vector-unit window splits and the combine kernel expect.
+//
+// Each wave stages its own codes in a private LDS area: the K codes (channel
+// row c of 16 bytes at 16 c + 16 (c / 8)), then, once the scores are taken,
+// the V codes over them (token row t of D / 4 bytes at (D / 4) t + 32 (t / 8)).
+// The padding puts the rows one MFMA operand gathers in distinct banks.
+//
+// Lanes of one wave hand data to each other through LDS (codes, w rows)
+// with no barrier: a wave's LDS accesses complete in program order, but the
+// compiler reasons per lane and may keep a value loaded earlier when the lane
+// itself stored nothing at that address (it did so for the w rows, which only
+// the lanes of present heads write).  lds_sync() marks each hand-off.
+#include <float.h>
+
+#include "kvarn_launch.h"
+#include "kvarn_mfma.h"
+
+namespace kvarn {
+namespace {
+
+using mfma::as_half8;
+using mfma::byte_pair;
+using mfma::floatx4;
+using mfma::fp16_scale_exp;
+using mfma::half8;
+using mfma::pow2i;
+using mfma::row_max16;
+using mfma::row_sum16;
+using mfma::split_pair;
+using mfma::wmax;
+using mfma::wsum;
+
+constexpr float kLog2eW = 1.4426950408889634f;
+constexpr float kLn2W = 0.6931471805599453f;
+constexpr int kWRowW = 20;   // dwords per w operand row (80 bytes)
+constexpr int kRowsW = 16;   // MFMA operand rows; rows that hold no head part stay zero
+
+constexpr int align16w(int x) { return (x + 15) / 16 * 16; }
+
+// compiler memory barrier: LDS loads after it are issued afresh, and no LDS
+// access moves across it
+__device__ __forceinline__ void lds_sync() { asm volatile("" ::: "memory"); }
+
+// native 16-byte vector (arrays of it stay in registers)
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <int D, int G>
+struct WideLds {
+  // head h's fp16 hi and lo parts sit in operand rows RPH h and RPH h + 1, so
+  // lane group g of an MFMA result holds heads HPL g .. HPL g + HPL - 1
+  static constexpr int HPL = G > 4 ? 2 : 1;
+  static constexpr int RPH = 4 / HPL;
+  static constexpr int code_wave = 18 * D;                   // K codes, then V codes
+  static constexpr int code = 0;                             // [wave]
+  static constexpr int wop = 4 * code_wave;                  // [wave][16 rows][kWRowW] dwords
+  static constexpr int wop_wave = kRowsW * kWRowW * 4;
+  static constexpr int qt = wop + 4 * wop_wave;              // [2][D/32][16 rows][4] uint4
+  static constexpr int qt_tile = (D / 32) * kRowsW * 64;
+  static constexpr int us = qt + 2 * qt_tile;                // [2][G] f32: score unscale
+  static constexpr int bias = us + 2 * G * 4;                // [2][G] f32: sum_c q'_c kmin_c
+  static constexpr int fv = bias + 2 * G * 4;                // [2] int: w fp16 scale exponent
+  static constexpr int ml = align16w(fv + 8);                // [G][4] float2: m, l per wave
+  static constexpr int bytes = ml + G * 4 * 8;
+  static constexpr int mo = 0;                               // merge: [wave][G][D] f32
+  static_assert(8 * D + 128 <= code_wave, "a wave's V codes fit its K-code area");
+  static_assert(4 * G * D * 4 <= us, "the merge area lies below the per-tile scalars");
+  static_assert((wop % 16) == 0 && (qt % 16) == 0, "aligned sections");
+};
+
+template <int D, int G, bool H>
+__global__ void __launch_bounds__(256) decode_wide_kernel(DecodeParams P) {
+  using L = WideLds<D, G>;
+  using R = Rec<D, H>;
+  constexpr int NB = D / 128;            // value groups
+  constexpr int HPL = L::HPL, RPH = L::RPH;
+  constexpr int K4 = D / 32;             // channel steps of the score products
+  constexpr int CPL = D / 64;            // channels per lane in the query prep / K-code slice
+  constexpr int VPL = D / 128;           // 16-byte pieces of the wave's V codes per lane
+  constexpr int PPW = (G + 3) / 4;       // query heads prepared per wave
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int split = blockIdx.x;
+  const int kvh = blockIdx.y;
+  const int b = blockIdx.z;
+  const SeqView sv = seq_view(P, b);
+  const int n_split = P.n_tsplit + P.n_wsplit;
+
+  __shared__ __attribute__((aligned(16))) uint8_t lds[L::bytes];
+
+  float* part = P.part + (((int64_t)b * P.n_q + (int64_t)kvh * G) * n_split + split) * (D + 4);
+  const int64_t hs = (int64_t)n_split * (D + 4);   // partial of head h at part + h * hs
+  const int t_begin = split * P.tps;
+  const int t_end = min(sv.nt, t_begin + P.tps);
+  if (t_begin >= t_end) {   // empty partial: m = -inf, l = 0, o = 0
+    for (int i = tid; i < G * (D + 2); i += 256) {
+      const int h = i / (D + 2), c = i % (D + 2);
+      part[h * hs + c] = (c == D) ? -INFINITY : 0.0f;
+    }
+    return;
+  }
+
+  // rotated query rows of the heads this wave prepares (clamped rows are read, never used)
+  const float* qsrc = P.q_rot + ((int64_t)b * P.n_q + (int64_t)kvh * G) * D;
+  float qp[PPW][CPL];
+#pragma unroll
+  for (int k = 0; k < PPW; ++k) {
+    const int h = wv + 4 * k;
+    const int hc = h < G ? h : 0;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) qp[k][i] = qsrc[hc * D + lane + 64 * i];
+  }
+  // operand rows that hold no head part stay zero (both q~ buffers, every w area)
+  if constexpr (RPH > 2 || G < 8) {
+    for (int i = tid; i < 2 * K4 * kRowsW * 4; i += 256) {
+      const int r = (i >> 2) & (kRowsW - 1);
+      if ((r % RPH) >= 2 || r / RPH >= G) reinterpret_cast<uint4*>(lds + L::qt)[i] = make_uint4(0, 0, 0, 0);
+    }
+    for (int i = tid; i < 4 * kRowsW * (kWRowW / 4); i += 256) {
+      const int r = (i / (kWRowW / 4)) % kRowsW;
+      if ((r % RPH) >= 2 || r / RPH >= G) reinterpret_cast<uint4*>(lds + L::wop)[i] = make_uint4(0, 0, 0, 0);
+    }
+  }
+
+  float m_w[HPL], l_w[HPL], o_w[HPL][8 * NB];
+#pragma unroll
+  for (int jj = 0; jj < HPL; ++jj) {
+    m_w[jj] = -INFINITY;
+    l_w[jj] = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 8 * NB; ++q) o_w[jj][q] = 0.0f;
+  }
+  const float c_log2 = P.scale * kLog2eW;
+  const int64_t rstride = (int64_t)P.n_kv * R::bytes;
+  const uint8_t* rec = P.records + ((sv.rec_row0 + t_begin) * (int64_t)P.n_kv + kvh) * R::bytes;
+  uint8_t* cs = lds + L::code + wv * L::code_wave;
+  uint32_t* wrow = reinterpret_cast<uint32_t*>(lds + L::wop + wv * L::wop_wave);
+  const int tok = 32 * wv + 2 * n;                      // the lane's two tokens of the quarter
+  const int vci = 16 * (n & 7) + 8 * (n >> 3);          // its first output channel of a value group
+
+  for (int j = t_begin; j < t_end; ++j, rec += rstride) {
+    const int buf = (j - t_begin) & 1;
+    // ---- loads: prep scales first, then the wave's own slice ----
+    float ks[CPL], km[CPL];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      ks[i] = sc_ld<H>(rec + R::kscale, lane + 64 * i);
+      km[i] = sc_ld<H>(rec + R::kmin, lane + 64 * i);
+    }
+    float vmx = 0.0f;   // wave 0: the tile's largest value scale (tokens 2 lane, 2 lane + 1)
+    if (wv == 0) {
+#pragma unroll
+      for (int i = 0; i < NB / 2; ++i) {
+        const float4 x = sc_ld4<H>(rec + R::vscale, 2 * NB * lane + 4 * i);
+        vmx = fmaxf(vmx, fmaxf(fmaxf(x.x, x.y), fmaxf(x.z, x.w)));
+      }
+    }
+    u32x4 kc[CPL], vc[VPL];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) kc[i] = *reinterpret_cast<const u32x4*>(rec + (lane + 64 * i) * 64 + 16 * wv);
+#pragma unroll
+    for (int i = 0; i < VPL; ++i)
+      vc[i] = *reinterpret_cast<const u32x4*>(rec + R::vcode + 8 * D * wv + 16 * (lane + 64 * i));
+    const float2 kt = sc_ld2<H>(rec + R::ktok, tok);
+    float vs[2 * NB], vm[2 * NB];   // token tok + e, group cb at e NB + cb
+#pragma unroll
+    for (int i = 0; i < NB / 2; ++i) {
+      const float4 x = sc_ld4<H>(rec + R::vscale, tok * NB + 4 * i);
+      const float4 y = sc_ld4<H>(rec + R::vmin, tok * NB + 4 * i);
+      vs[4 * i] = x.x; vs[4 * i + 1] = x.y; vs[4 * i + 2] = x.z; vs[4 * i + 3] = x.w;
+      vm[4 * i] = y.x; vm[4 * i + 1] = y.y; vm[4 * i + 2] = y.z; vm[4 * i + 3] = y.w;
+    }
+
+    // ---- prep: q~ hi/lo operand rows, score unscale, bias, w scale ----
+#pragma unroll
+    for (int k = 0; k < PPW; ++k) {
+      const int h = wv + 4 * k;
+      if (h < G) {   // wave-uniform
+        float y[CPL];
+        float am = 0.0f, bs = 0.0f;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+          y[i] = qp[k][i] * ks[i];
+          am = fmaxf(am, fabsf(y[i]));
+          bs = fmaf(qp[k][i], km[i], bs);
+        }
+        const float amax = wmax(am);
+        const float bias = wsum(bs);
+        const int fe = fp16_scale_exp(amax);   // amax 2^fe in [2^13, 2^14)
+        const float f = pow2i(fe - 4);
+        // channel c -> uint4 [k4 = c / 32][row][(c / 8) % 4], half c % 8; channel
+        // lane + 64 i has k4 = 2 i + lane / 32
+        uint16_t* qt = reinterpret_cast<uint16_t*>(lds + L::qt + buf * L::qt_tile);
+        const int i0 = (((lane >> 5) * kRowsW + RPH * h) * 4 + ((lane >> 3) & 3)) * 8 + (lane & 7);
+#pragma unroll
+        for (int i = 0; i < CPL; i += 2) {
+          uint32_t hi, lo;
+          split_pair(y[i] * f, y[i + 1] * f, hi, lo);
+          const int ia = i0 + i * 2 * kRowsW * 32;
+          const int ib = ia + 2 * kRowsW * 32;
+          qt[ia] = (uint16_t)(hi & 0xFFFFu);
+          qt[ia + 32] = (uint16_t)(lo & 0xFFFFu);   // row RPH h + 1
+          qt[ib] = (uint16_t)(hi >> 16);
+          qt[ib + 32] = (uint16_t)(lo >> 16);
+        }
+        if (lane == 0) {
+          reinterpret_cast<float*>(lds + L::us)[buf * G + h] = pow2i(24 - fe);
+          reinterpret_cast<float*>(lds + L::bias)[buf * G + h] = bias;
+        }
+      }
+    }
+    if (wv == 0) {
+      const float vmax = wmax(vmx);   // p <= 1, so w <= the largest value scale
+      if (lane == 0) reinterpret_cast<int*>(lds + L::fv)[buf] = fp16_scale_exp(vmax);
+    }
+    // ---- the wave's K codes into its own area ----
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const int c = lane + 64 * i;
+      *reinterpret_cast<u32x4*>(cs + 16 * c + 16 * (c >> 3)) = kc[i];
+    }
+    __syncthreads();   // q~ operands and the tile's scalars are ready
+
+    // ---- scores: A = q~ rows, B = code nibbles of tokens 2 n, 2 n + 1 of the quarter ----
+    const uint4* qtu = reinterpret_cast<const uint4*>(lds + L::qt + buf * L::qt_tile);
+    floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    const uint8_t* kg = cs + 144 * g + n;   // channel 32 k4 + 8 g + j at kg[576 k4 + 16 j]
+#pragma unroll
+    for (int k4 = 0; k4 < K4; ++k4) {
+      const uint4 a = qtu[(k4 * kRowsW + n) * 4 + g];
+      const half8 A = as_half8(a.x, a.y, a.z, a.w);
+      uint32_t e[4], o[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t x = byte_pair(kg + 576 * k4 + 32 * i, 16);
+        e[i] = (x << 4) & 0x00F000F0u;   // token 2 n
+        o[i] = x & 0x00F000F0u;          // token 2 n + 1
+      }
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, as_half8(e[0], e[1], e[2], e[3]), acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, as_half8(o[0], o[1], o[2], o[3]), acc1, 0, 0, 0);
+    }
+
+    // ---- online softmax of the quarter (lane (g, n): rows 4 g + i = head HPL g + i / RPH, part i % RPH) ----
+    const int vexp = reinterpret_cast<const int*>(lds + L::fv)[buf];
+    const float fv = pow2i(vexp);
+    const float k0 = kt.x * c_log2, k1 = kt.y * c_log2;
+    float p0[HPL], p1[HPL];
+#pragma unroll
+    for (int jj = 0; jj < HPL; ++jj) {
+      const int h = HPL * g + jj;
+      const int hc = h < G ? h : G - 1;
+      const float us = reinterpret_cast<const float*>(lds + L::us)[buf * G + hc];
+      const float bi = reinterpret_cast<const float*>(lds + L::bias)[buf * G + hc];
+      const float s0 = k0 * fmaf(acc0[RPH * jj] + acc0[RPH * jj + 1], us, bi);
+      const float s1 = k1 * fmaf(acc1[RPH * jj] + acc1[RPH * jj + 1], us, bi);
+      const float m_new = fmaxf(m_w[jj], row_max16(fmaxf(s0, s1)));
+      const float alpha = __builtin_amdgcn_exp2f(m_w[jj] - m_new);   // 0 on the first tile
+      p0[jj] = __builtin_amdgcn_exp2f(s0 - m_new);
+      p1[jj] = __builtin_amdgcn_exp2f(s1 - m_new);
+      m_w[jj] = m_new;
+      l_w[jj] = fmaf(l_w[jj], alpha, p0[jj] + p1[jj]);   // summed over the row in the merge
+#pragma unroll
+      for (int q = 0; q < 8 * NB; ++q) o_w[jj][q] *= alpha;
+    }
+
+    // ---- the wave's V codes over its K codes ----
+    lds_sync();
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const int off = 16 * (lane + 64 * i);
+      const int t = off / (D / 4);
+      *reinterpret_cast<u32x4*>(cs + (D / 4) * t + 32 * (t >> 3) + off % (D / 4)) = vc[i];
+    }
+    lds_sync();
+
+    // ---- value aggregate per group: A = w rows, B = crumbs of tokens 8 g + j,
+    //      channels 128 cb + 16 (n % 8) + 8 (n / 8) + qb ----
+    const float un_lo = pow2i(24 - vexp - 4), un_hi = pow2i(24 - vexp - 6);
+    const uint8_t* vg = cs + 8 * (D / 4) * g + 32 * g + 4 * (n & 7) + 2 * (n >> 3);
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb) {
+      lds_sync();   // the previous group's w rows are read before they are overwritten
+      float u[HPL];
+#pragma unroll
+      for (int jj = 0; jj < HPL; ++jj) {
+        const int h = HPL * g + jj;
+        uint32_t hi, lo;
+        split_pair(p0[jj] * (vs[cb] * fv), p1[jj] * (vs[NB + cb] * fv), hi, lo);
+        if (h < G) {
+          wrow[(RPH * h) * kWRowW + n] = hi;
+          wrow[(RPH * h + 1) * kWRowW + n] = lo;
+        }
+        u[jj] = row_sum16(p0[jj] * vm[cb] + p1[jj] * vm[NB + cb]);   // sum_t p vmin over the quarter
+      }
+      lds_sync();   // every lane's w rows of this group are read afresh
+      const uint4 wa = *reinterpret_cast<const uint4*>(wrow + n * kWRowW + 4 * g);
+      const half8 A = as_half8(wa.x, wa.y, wa.z, wa.w);
+      uint32_t x[2][4];
+#pragma unroll
+      for (int pq = 0; pq < 4; ++pq) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e) x[e][pq] = byte_pair(vg + 32 * cb + (D / 2) * pq + e, D / 4);
+      }
+      const float4 vca = sc_ld4<H>(rec + R::vchan, 128 * cb + vci);
+      const float4 vcb = sc_ld4<H>(rec + R::vchan, 128 * cb + vci + 4);
+      const float vch[8] = {vca.x, vca.y, vca.z, vca.w, vcb.x, vcb.y, vcb.z, vcb.w};
+#pragma unroll
+      for (int qb = 0; qb < 8; ++qb) {
+        const int e = qb >> 2, cr = qb & 3;
+        const uint32_t mask = (cr & 1) ? 0x00C000C0u : 0x00300030u;
+        uint32_t bv[4];
+#pragma unroll
+        for (int pq = 0; pq < 4; ++pq) bv[pq] = ((cr < 2) ? (x[e][pq] << 4) : x[e][pq]) & mask;
+        const floatx4 z = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, as_half8(bv[0], bv[1], bv[2], bv[3]),
+                                                               (floatx4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        const float un = (cr & 1) ? un_hi : un_lo;
+#pragma unroll
+        for (int jj = 0; jj < HPL; ++jj)
+          o_w[jj][8 * cb + qb] = fmaf(vch[qb], fmaf(z[RPH * jj] + z[RPH * jj + 1], un, u[jj]), o_w[jj][8 * cb + qb]);
+      }
+    }
+  }
+
+  // ---- merge the four wave states into one partial per query head ----
+  __syncthreads();   // every wave is done with the areas the merge overwrites
+  float* s_mo = reinterpret_cast<float*>(lds + L::mo);
+  float2* s_ml = reinterpret_cast<float2*>(lds + L::ml);
+#pragma unroll
+  for (int jj = 0; jj < HPL; ++jj) {
+    const int h = HPL * g + jj;
+    const float lsum = row_sum16(l_w[jj]);
+    if (h < G) {
+#pragma unroll
+      for (int cb = 0; cb < NB; ++cb) {
+#pragma unroll
+        for (int qb = 0; qb < 8; ++qb) s_mo[(wv * G + h) * D + 128 * cb + vci + qb] = o_w[jj][8 * cb + qb];
+      }
+      if (n == 0) s_ml[h * 4 + wv] = make_float2(m_w[jj], lsum);
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < G * D; i += 256) {
+    const int h = i / D, c = i % D;
+    float M = s_ml[h * 4].x;
+#pragma unroll
+    for (int w = 1; w < 4; ++w) M = fmaxf(M, s_ml[h * 4 + w].x);
+    float o = 0.0f, l = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float2 ml = s_ml[h * 4 + w];
+      const float sc = __builtin_amdgcn_exp2f(ml.x - M);
+      o = fmaf(sc, s_mo[(w * G + h) * D + c], o);
+      l = fmaf(sc, ml.y, l);
+    }
+    part[h * hs + c] = o;
+    if (c == 0) {
+      part[h * hs + D] = M * kLn2W;   // natural-log units, as the combine expects
+      part[h * hs + D + 1] = l;
+    }
+  }
+}
+
+template <int D, int G>
+hipError_t launch_wide_dg(const DecodeParams& P, int batch, hipStream_t stream) {
+  const dim3 grid(P.n_tsplit, P.n_kv, batch);
+  if (P.h16)
+    hipLaunchKernelGGL((decode_wide_kernel<D, G, true>), grid, dim3(256), 0, stream, P);
+  else
+    hipLaunchKernelGGL((decode_wide_kernel<D, G, false>), grid, dim3(256), 0, stream, P);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_wide_d(const DecodeParams& P, int batch, hipStream_t stream) {
+  switch (P.G) {
+    case 1: return launch_wide_dg<D, 1>(P, batch, stream);
+    case 2: return launch_wide_dg<D, 2>(P, batch, stream);
+    case 4: return launch_wide_dg<D, 4>(P, batch, stream);
+    case 8: return launch_wide_dg<D, 8>(P, batch, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode_wide_tiles(int d, const DecodeParams& P, int batch, hipStream_t stream) {
+  switch (d) {
+    case 256: return launch_wide_d<256>(P, batch, stream);
+    case 512: return launch_wide_d<512>(P, batch, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace kvarn

@@ -26,6 +26,7 @@ struct DecodeParams {
   int n_q, n_kv, G;
   int tps, n_tsplit, n_wsplit;
   int wchunk;                      // window tokens per window split
+  int split0;                      // split index of blockIdx.x 0 (a launch over the window splits alone)
   // prefill view (mode 1): "sequence" b is query position pos0 + b of one
   // sequence; it sees T(p) tiles and raw rows [128 T(p), p] of k_win/v_win,
   // where raw row p lives at (p - raw_base) * win_tok_stride.
@@ -99,6 +100,9 @@ hipError_t launch_compress(int d, bool h16, int kb, int vb, int n_tiles, int n_k
 hipError_t launch_rotate(int d, int64_t n_rows, const float* q, float* q_rot, hipStream_t stream);
 hipError_t launch_decode(int d, const DecodeParams& P, int batch, hipStream_t stream);
 hipError_t launch_decode_fused(const DecodeParams& P, int batch, hipStream_t stream);
+// Tile splits alone (grid n_tsplit x n_kv x batch) for head_dim 256 / 512 over
+// K4V2 records, on the matrix cores; P.q_rot must hold the rotated queries.
+hipError_t launch_decode_wide_tiles(int d, const DecodeParams& P, int batch, hipStream_t stream);
 hipError_t launch_prefill_mfma(const PrefillParams& P, hipStream_t stream);
 // Multi-query verify (head_dim 128): P.part holds batch * q_len * n_q *
 // (n_tsplit + n_wsplit) partials of D + 4 floats (n_wsplit window splits of

@@ -68,5 +68,81 @@ __device__ __forceinline__ float wave_sum16(float v) {
 __device__ __forceinline__ uint32_t nib_lo(uint32_t x) { return (x << 4) & 0x00F000F0u; }
 __device__ __forceinline__ uint32_t nib_hi(uint32_t x) { return x & 0x00F000F0u; }
 
+
+typedef __fp16 half2v __attribute__((ext_vector_type(2)));
+
+// Bytes p[0] and p[off] in bits 0-7 and 16-23 (built as two 16-bit lanes, so
+// the compiler joins the two LDS byte loads with one v_perm_b32).
+typedef unsigned short ushort2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t byte_pair(const uint8_t* p, int off) {
+  ushort2v t;
+  t.x = p[0];
+  t.y = p[off];
+  return __builtin_bit_cast(uint32_t, t);
+}
+
+// fp16 hi + lo parts of (a, b): hi rounds toward zero, lo holds the rest.
+__device__ __forceinline__ void split_pair(float a, float b, uint32_t& hi, uint32_t& lo) {
+  const half2v h = __builtin_amdgcn_cvt_pkrtz(a, b);
+  const half2v l = __builtin_amdgcn_cvt_pkrtz(a - (float)h.x, b - (float)h.y);
+  hi = __builtin_bit_cast(uint32_t, h);
+  lo = __builtin_bit_cast(uint32_t, l);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// value of lane (lane ^ M), M < 16, on the DPP paths (no LDS round trip):
+// lane ^ 4 is the half-row mirror (lane ^ 7) followed by quad_perm [3,2,1,0]
+template <int M>
+__device__ __forceinline__ float xshfl(float v) {
+  if constexpr (M == 1) return dpp_f<0xB1>(v);        // quad_perm [1,0,3,2]
+  else if constexpr (M == 2) return dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]
+  else if constexpr (M == 8) return dpp_f<0x128>(v);  // row_ror:8
+  else return dpp_f<0x1B>(dpp_f<0x141>(v));           // M == 4: row_half_mirror, quad_perm [3,2,1,0]
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+// Reductions over the 16 lanes of a DPP row (every lane of the row gets it).
+// The max runs on an integer key with the order of the floats (negative
+// values have their magnitude bits flipped), which needs no NaN handling.
+__device__ __forceinline__ float row_max16(float v) {
+  int k = __float_as_int(v);
+  k ^= (k >> 31) & 0x7FFFFFFF;
+  k = max(k, dpp_i<0x128>(k));   // row_ror:8
+  k = max(k, dpp_i<0x124>(k));   // row_ror:4
+  k = max(k, dpp_i<0x122>(k));   // row_ror:2
+  k = max(k, dpp_i<0x121>(k));   // row_ror:1
+  return __int_as_float(k ^ ((k >> 31) & 0x7FFFFFFF));
+}
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dpp_f<0x128>(v);
+  v += dpp_f<0x124>(v);
+  v += dpp_f<0x122>(v);
+  return v + dpp_f<0x121>(v);
+}
+__device__ __forceinline__ float lane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+// whole-wave reductions (every lane gets the result): within the 16-lane rows
+// by DPP, across the rows by permlane swaps
+__device__ __forceinline__ float wmax(float v) {
+  v = row_max16(v);
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float wsum(float v) {
+  v = row_sum16(v);
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 }  // namespace mfma
 }  // namespace kvarn

@@ -601,6 +601,69 @@ def test_decode_gqa_8_and_1_ragged_batch(Hq, Hkv, with_rot):
         assert err < TOL, (b, err)
 
 
+@pytest.mark.parametrize("d,Hq,Hkv,f16", [(256, 4, 4, False), (256, 8, 4, True), (256, 16, 2, False),
+                                          (512, 4, 4, True), (512, 4, 2, False), (512, 8, 2, False)])
+def test_decode_wide_every_group_size_ragged(d, Hq, Hkv, f16):
+    """Head_dim 256 / 512 over K4V2 records for each query group size G = Hq / Hkv
+    (1, 2, 4, 8 heads in the matrix-core operand rows), in a ragged batch with a
+    window-only sequence and one without window tokens; then the same records
+    with every window empty (no window splits at all)."""
+    say("decode wide group sizes", d, Hq, Hkv, f16)
+    tiles, wins = [9, 0, 4, 1], [200, 37, 0, 256]
+    B = len(tiles)
+    kw = np.zeros((B, max(wins), Hkv, d), np.float32)
+    vw = np.zeros_like(kw)
+    recs_all, rec_start, KV, row = [], [], [], 0
+    for b in range(B):
+        K, V = synth.make_kv(900 + 7 * b + d + Hq, 128 * tiles[b] + wins[b], Hkv, d, 4)
+        if tiles[b]:
+            rec = torch.zeros(tiles[b], Hkv, kvarn.tile_bytes(d, f16), dtype=torch.uint8, device=DEV)
+            kvarn.compress_tile(to_dev(K), to_dev(V), rec, tiles[b], f16_scales=f16)
+            torch.cuda.synchronize()
+            recs_all.append(rec.cpu().numpy())
+        rec_start.append(row)
+        row += tiles[b]
+        kw[b, :wins[b]] = K[128 * tiles[b]:]
+        vw[b, :wins[b]] = V[128 * tiles[b]:]
+        KV.append((K, V))
+    recs = np.concatenate(recs_all)
+    q = synth.make_q(950 + d + Hq, B, Hq, d)
+    qd = to_dev(q)
+    scale = 1 / math.sqrt(d)
+    deq = {}
+    for b in range(B):
+        K, V = KV[b]
+        if tiles[b]:
+            mine = recs[rec_start[b]:rec_start[b] + tiles[b]]
+            assert np.array_equal(mine, oracle.compress_tiles(K, V, tiles[b], f16=f16))
+            deq[b] = oracle.dequant_records(mine, d, f16=f16)
+        else:
+            deq[b] = (np.zeros((0, Hkv, d)), np.zeros((0, Hkv, d)))
+    out = kvarn.decode_attention(qd, kvarn.rotate_query(qd), to_dev(recs), rec_start, tiles, to_dev(kw),
+                                 to_dev(vw), wins, scale, f16_scales=f16)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    for b in range(B):
+        K, V = KV[b]
+        lo = 128 * tiles[b]
+        ref = oracle.decode(q[b], deq[b][0], deq[b][1], tiles[b], K[lo:], V[lo:], scale)
+        err = rel_l2(got[b], ref)
+        assert err < TOL, (b, err)
+    # tiles only: every window empty
+    keep = [b for b in range(B) if tiles[b]]
+    out = kvarn.decode_attention(qd[keep], kvarn.rotate_query(qd[keep]), to_dev(recs),
+                                 [rec_start[b] for b in keep], [tiles[b] for b in keep], to_dev(kw[keep]),
+                                 to_dev(vw[keep]), [0] * len(keep), scale, f16_scales=f16)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    for i, b in enumerate(keep):
+        K, V = KV[b]
+        empty = K[:0]
+        ref = oracle.decode(q[b], deq[b][0], deq[b][1], tiles[b], empty, V[:0], scale)
+        err = rel_l2(got[i], ref)
+        assert err < TOL, (b, err)
+
+
 @pytest.mark.parametrize("name", ["wide_d256", "wide_d512"])
 def test_decode_wide_batch16_full_size_sampled(name):
     """The batched wide-head workload at its full size (16 sequences, contexts
