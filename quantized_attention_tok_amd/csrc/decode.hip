@@ -291,15 +291,25 @@ __global__ void __launch_bounds__(kDecThreads) decode_partial_kernel(DecodeParam
       const int t = tid % kWinChunk;
       const int hg0 = tid / kWinChunk;
       if (t < n) {
+        // each key chunk is loaded once for every head of the thread
+        constexpr int NH = (G + 3) / 4;   // heads hg0, hg0 + 4
         const float* krow = kb + (int64_t)(w_begin + t) * P.win_tok_stride;
-        for (int h = hg0; h < G; h += kDecThreads / kWinChunk) {
-          float a = 0.0f;
-          for (int c = 0; c < D; c += 4) {
-            const float4 kk = *reinterpret_cast<const float4*>(krow + c);
-            a += s_q[h][c] * kk.x + s_q[h][c + 1] * kk.y + s_q[h][c + 2] * kk.z + s_q[h][c + 3] * kk.w;
+        float a[NH];
+#pragma unroll
+        for (int i = 0; i < NH; ++i) a[i] = 0.0f;
+#pragma unroll 8
+        for (int c = 0; c < D; c += 4) {
+          const float4 kk = *reinterpret_cast<const float4*>(krow + c);
+#pragma unroll
+          for (int i = 0; i < NH; ++i) {
+            const int h = hg0 + 4 * i;
+            if (h < G)
+              a[i] += s_q[h][c] * kk.x + s_q[h][c + 1] * kk.y + s_q[h][c + 2] * kk.z + s_q[h][c + 3] * kk.w;
           }
-          s_sc[h][t] = P.scale * a;
         }
+#pragma unroll
+        for (int i = 0; i < NH; ++i)
+          if (hg0 + 4 * i < G) s_sc[hg0 + 4 * i][t] = P.scale * a[i];
       } else {
         for (int h = hg0; h < G; h += kDecThreads / kWinChunk) s_sc[h][t] = -INFINITY;
       }
@@ -314,20 +324,33 @@ __global__ void __launch_bounds__(kDecThreads) decode_partial_kernel(DecodeParam
       if (lane == 0) { s_m[h] = m; s_l[h] = l; s_alpha[h] = 0.0f; }
     }
     __syncthreads();
+    // all of the thread's channels at once, tokens eight at a time, so the
+    // value loads are in flight together rather than one per token
+    if (vc0 < D) {
+      const float* vcol = vb + (int64_t)w_begin * P.win_tok_stride + vc0;
+      int t = 0;
+      for (; t + 8 <= n; t += 8) {
+        float v[8][VC];
 #pragma unroll
-    for (int k = 0; k < VC; ++k) {
-      const int c = vc0 + k * VSTRIDE;
-      if (c < D) {
-        float pacc[GV];
+        for (int u = 0; u < 8; ++u)
 #pragma unroll
-        for (int h = 0; h < GV; ++h) pacc[h] = 0.0f;
-        for (int t = 0; t < n; ++t) {
-          const float v = vb[(int64_t)(w_begin + t) * P.win_tok_stride + c];
+          for (int k = 0; k < VC; ++k) v[u][k] = vcol[(int64_t)(t + u) * P.win_tok_stride + k * VSTRIDE];
 #pragma unroll
-          for (int h = 0; h < GV; ++h) pacc[h] += s_sc[hv * GV + h][t] * v;
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+          for (int h = 0; h < GV; ++h) {
+            const float p = s_sc[hv * GV + h][t + u];
+#pragma unroll
+            for (int k = 0; k < VC; ++k) acc[h][k] += p * v[u][k];
+          }
+      }
+      for (; t < n; ++t) {
+#pragma unroll
+        for (int h = 0; h < GV; ++h) {
+          const float p = s_sc[hv * GV + h][t];
+#pragma unroll
+          for (int k = 0; k < VC; ++k) acc[h][k] += p * vcol[(int64_t)t * P.win_tok_stride + k * VSTRIDE];
         }
-#pragma unroll
-        for (int h = 0; h < GV; ++h) acc[h][k] = pacc[h];
       }
     }
   }
