@@ -23,6 +23,7 @@
 #include <float.h>
 
 #include "kvarn_launch.h"
+#include "kvarn_mfma.h"
 
 namespace kvarn {
 
@@ -54,7 +55,7 @@ __global__ void __launch_bounds__(kDecThreads) decode_partial_kernel(DecodeParam
   const int b = blockIdx.z;
   const int n_split = P.n_tsplit + P.n_wsplit;
 
-  __shared__ float s_q[G][D];                 // rotated (tiles) or raw (window) query
+  __shared__ __attribute__((aligned(16))) float s_q[G][D];   // rotated (tiles) or raw (window) query
   // q~ of the current tile [channel][head] in the key phase, then w = p * vscale
   // [group][token][head] (a token's heads contiguous) in the value phase: the
   // same D * G floats
@@ -286,32 +287,32 @@ __global__ void __launch_bounds__(kDecThreads) decode_partial_kernel(DecodeParam
     const float* kb = P.k_win + sv.win_off + (int64_t)kvh * P.win_head_stride;
     const float* vb = P.v_win + sv.win_off + (int64_t)kvh * P.win_head_stride;
     const int n = w_end - w_begin;
-    // scores: thread = (token in chunk, head group of 4)
+    // scores: each wave takes four tokens per step, 16 lanes per token; a lane
+    // reads 16-byte pieces 64 channels apart of its token's key row (the 16
+    // lanes of a token read whole 256-byte runs) and the 16 partial dot
+    // products are summed across the lanes' DPP row
     {
-      const int t = tid % kWinChunk;
-      const int hg0 = tid / kWinChunk;
-      if (t < n) {
-        // each key chunk is loaded once for every head of the thread
-        constexpr int NH = (G + 3) / 4;   // heads hg0, hg0 + 4
-        const float* krow = kb + (int64_t)(w_begin + t) * P.win_tok_stride;
-        float a[NH];
+      const int piece = lane & 15;
+      for (int tb = 4 * wv; tb < kWinChunk; tb += 16) {   // wave-uniform
+        // the query pieces are read from LDS in every step, not held in registers
+        asm volatile("" ::: "memory");
+        const int t = tb + (lane >> 4);
+        const bool ok = t < n;
+        const float* krow = kb + (int64_t)(w_begin + (ok ? t : 0)) * P.win_tok_stride + 4 * piece;
+        float4 kk[D / 64];
 #pragma unroll
-        for (int i = 0; i < NH; ++i) a[i] = 0.0f;
-#pragma unroll 8
-        for (int c = 0; c < D; c += 4) {
-          const float4 kk = *reinterpret_cast<const float4*>(krow + c);
+        for (int i = 0; i < D / 64; ++i) kk[i] = *reinterpret_cast<const float4*>(krow + 64 * i);
 #pragma unroll
-          for (int i = 0; i < NH; ++i) {
-            const int h = hg0 + 4 * i;
-            if (h < G)
-              a[i] += s_q[h][c] * kk.x + s_q[h][c + 1] * kk.y + s_q[h][c + 2] * kk.z + s_q[h][c + 3] * kk.w;
+        for (int h = 0; h < G; ++h) {
+          float a = 0.0f;
+#pragma unroll
+          for (int i = 0; i < D / 64; ++i) {
+            const float4 qq = *reinterpret_cast<const float4*>(&s_q[h][4 * piece + 64 * i]);
+            a += qq.x * kk[i].x + qq.y * kk[i].y + qq.z * kk[i].z + qq.w * kk[i].w;
           }
+          a = mfma::row_sum16(a);
+          if (piece == 0) s_sc[h][t] = ok ? P.scale * a : -INFINITY;
         }
-#pragma unroll
-        for (int i = 0; i < NH; ++i)
-          if (hg0 + 4 * i < G) s_sc[hg0 + 4 * i][t] = P.scale * a[i];
-      } else {
-        for (int h = hg0; h < G; h += kDecThreads / kWinChunk) s_sc[h][t] = -INFINITY;
       }
     }
     __syncthreads();
