@@ -664,6 +664,57 @@ def test_decode_wide_every_group_size_ragged(d, Hq, Hkv, f16):
         assert err < TOL, (b, err)
 
 
+@pytest.mark.parametrize("d,Hq,Hkv", [(256, 4, 4), (512, 4, 2)])
+def test_decode_wide_multi_tile_splits_small_groups(d, Hq, Hkv):
+    """Head_dim 256 / 512 with query group sizes 1 and 2 in a batch large enough
+    that the split plan puts two or more tiles in a split (each wave's softmax
+    state then runs over several tiles): every sequence agrees with its own
+    single-sequence call (one tile per split) to 1e-5, and the two shortest
+    sequences with the oracle."""
+    say("decode wide multi-tile splits", d, Hq, Hkv)
+    B = 8
+    tiles = [70, 3, 66, 5, 80, 71, 69, 75] if Hkv == 4 else [140, 3, 131, 5, 150, 142, 139, 145]
+    wins = [256, 40, 130, 255, 1, 200, 64, 99]
+    assert B * Hkv * max(tiles) > 2048          # over the decode plan's workgroup target: 2+ tiles per split
+    recs_all, rec_start, KV, row = [], [], [], 0
+    kw = np.zeros((B, max(wins), Hkv, d), np.float32)
+    vw = np.zeros_like(kw)
+    for b in range(B):
+        K, V = synth.make_kv(1500 + 11 * b + d, 128 * tiles[b] + wins[b], Hkv, d, 4)
+        rec = torch.zeros(tiles[b], Hkv, kvarn.tile_bytes(d), dtype=torch.uint8, device=DEV)
+        kvarn.compress_tile(to_dev(K), to_dev(V), rec, tiles[b])
+        recs_all.append(rec)
+        rec_start.append(row)
+        row += tiles[b]
+        kw[b, :wins[b]] = K[128 * tiles[b]:]
+        vw[b, :wins[b]] = V[128 * tiles[b]:]
+        KV.append((K, V))
+    pool = torch.cat(recs_all)
+    q = synth.make_q(1600 + d, B, Hq, d)
+    qd = to_dev(q)
+    qr = kvarn.rotate_query(qd)
+    scale = 1 / math.sqrt(d)
+    kwd, vwd = to_dev(kw), to_dev(vw)
+    out = kvarn.decode_attention(qd, qr, pool, rec_start, tiles, kwd, vwd, wins, scale)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    for b in range(B):
+        one = kvarn.decode_attention(qd[b:b + 1], qr[b:b + 1], recs_all[b], [0], [tiles[b]], kwd[b:b + 1],
+                                     vwd[b:b + 1], [wins[b]], scale)
+        torch.cuda.synchronize()
+        err = rel_l2(got[b], one.cpu().numpy()[0])
+        assert err < 1e-5, (b, err)
+    for b in (1, 3):
+        K, V = KV[b]
+        recs = recs_all[b].cpu().numpy()
+        assert np.array_equal(recs, oracle.compress_tiles(K, V, tiles[b]))
+        kh, vh = oracle.dequant_records(recs, d)
+        lo = 128 * tiles[b]
+        ref = oracle.decode(q[b], kh, vh, tiles[b], K[lo:], V[lo:], scale)
+        err = rel_l2(got[b], ref)
+        assert err < TOL, (b, err)
+
+
 @pytest.mark.parametrize("name", ["wide_d256", "wide_d512"])
 def test_decode_wide_batch16_full_size_sampled(name):
     """The batched wide-head workload at its full size (16 sequences, contexts
