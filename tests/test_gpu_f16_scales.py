@@ -187,7 +187,7 @@ def _prefill16(K, V, Q, W, chunk, Hkv, d):
     return torch.cat(outs).cpu().numpy(), cache.records[:cache.n_tiles].cpu().numpy()
 
 
-@pytest.mark.parametrize("d,Hq,Hkv,n", [(128, 8, 2, 1100), (256, 16, 4, 700)])
+@pytest.mark.parametrize("d,Hq,Hkv,n", [(128, 8, 2, 1100), (256, 16, 4, 700), (512, 8, 1, 500)])
 def test_prefill_f16_every_row(d, Hq, Hkv, n):
     say("prefill f16", d, n)
     W = 256
