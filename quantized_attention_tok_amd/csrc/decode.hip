@@ -525,8 +525,11 @@ hipError_t launch_decode_dg(const DecodeParams& P, int batch, hipStream_t stream
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // four waves when there are more splits than one 16-split pass, else one
-  if (P.n_tsplit + P.n_wsplit > 16)
+  // sixteen waves past four 16-split passes (every pass in flight at once),
+  // four waves past one pass, else one
+  if (P.n_tsplit + P.n_wsplit > 64)
+    hipLaunchKernelGGL((decode_combine_kernel<D, 16>), dim3(P.n_q, batch), dim3(1024), 0, stream, P);
+  else if (P.n_tsplit + P.n_wsplit > 16)
     hipLaunchKernelGGL((decode_combine_kernel<D, 4>), dim3(P.n_q, batch), dim3(256), 0, stream, P);
   else
     hipLaunchKernelGGL((decode_combine_kernel<D, 1>), dim3(P.n_q, batch), dim3(64), 0, stream, P);
