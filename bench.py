@@ -181,18 +181,16 @@ def wide_batch_case(torch, kvarn, synth, name, reps=10):
         del K, V, kd, vd
     pools = [pool, pool.clone()]
     q = torch.from_numpy(synth.make_q(w.seed, B, Hq, d)).to(dev)
-    qr = torch.empty_like(q)
     out = torch.empty_like(q)
     scale = 1.0 / math.sqrt(d)
     wins = [W] * B
-    ws = torch.zeros(max(16, kvarn.decode_workspace_bytes(q, qr, pool, rec_start, tiles, kw, vw, wins, scale)),
+    ws = torch.zeros(max(16, kvarn.decode_workspace_bytes(q, None, pool, rec_start, tiles, kw, vw, wins, scale)),
                      dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
     def run():
-        for p in pools:
-            kvarn.rotate_query(q, out=qr)
-            kvarn.decode_attention(q, qr, p, rec_start, tiles, kw, vw, wins, scale, out=out, workspace=ws)
+        for p in pools:   # q_rot=None: the tile kernel rotates the queries itself
+            kvarn.decode_attention(q, None, p, rec_start, tiles, kw, vw, wins, scale, out=out, workspace=ws)
 
     ms, _ = graph_ms(torch, run, len(pools), reps)
     alg = sum(decode_bytes(t, W, Hq, Hkv, d, tb) for t in tiles)
@@ -262,7 +260,7 @@ def prefill_case(torch, kvarn, synth, SequenceCache, d, Hq, Hkv, n, chunk, reps,
             c = min(chunk, n - p0)
             cache.append(kp[p0:p0 + c], vp[p0:p0 + c])
             q_c = qp[p0:p0 + c]
-            q_r = kvarn.rotate_query(q_c) if d != 128 else None   # head_dim 128: rotated in-kernel
+            q_r = None   # K4V2 records: the kernels rotate the rows themselves
             rb = 128 * kvarn.visible_tiles(p0, W)
             kvarn.prefill_attention(q_c, q_r, cache.records, cache.n_tiles, cache.k[rb:],
                                     cache.v[rb:], rb, p0, W, 1.0 / math.sqrt(d), out=outp[p0:p0 + c],

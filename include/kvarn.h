@@ -58,9 +58,11 @@
  * t*d*vb/8 with channel c at bit vb*c (for kb = 4, vb = 2: the layout above).
  * The six scale sections follow at 16*d*(kb+vb) in the same order, so the
  * record is 16*d*(kb+vb) + 20*d + 512 bytes (10*d + 256 with f16 scales).
- * Only K4V2 records at head_dim 128 run on the matrix units; other widths run
- * decode and prefill on the vector-unit kernels (a q_rot is then required,
- * prefill needs a workspace, and multi-query verify is unsupported).
+ * K4V2 records run on the matrix units (at head_dim 256 and 512 the raw
+ * window part of decode and prefill runs on the vector units, and prefill
+ * needs a workspace); other widths run decode and prefill on the vector-unit
+ * kernels (a q_rot is then required, prefill needs a workspace, and
+ * multi-query verify is unsupported).
  *
  * FP32 window and promotion (PR #434 commit list: "the FP32 window is the
  * staging; whole-tile promotion"): with a window of W tokens, the oldest 128
@@ -163,8 +165,8 @@ typedef struct kvarn_decode_args {
   int32_t max_tiles;       /* grid bound: >= n_tiles[b] for every b             */
   const float* q;          /* device [batch][n_q_heads][head_dim] raw query     */
   const float* q_rot;      /* device [batch][n_q_heads][head_dim] rotated query;
-                              may be NULL at head_dim 128 with K4V2 records:
-                              the kernel then rotates q itself                  */
+                              may be NULL with K4V2 records (any head_dim):
+                              the kernels then rotate q themselves              */
   const void* records;     /* device record pool; record (b, j, h) at
                               ((rec_start[b] + j)*n_kv_heads + h)*tile_bytes    */
   int64_t n_record_rows;   /* rows in the pool (a row = n_kv_heads records)     */
@@ -236,10 +238,10 @@ typedef struct kvarn_prefill_args {
   int32_t chunk;           /* C >= 1 query positions                            */
   float softmax_scale;
   const float* q;          /* device [C][n_q_heads][head_dim] raw               */
-  const float* q_rot;      /* device [C][n_q_heads][head_dim] rotated; NULL at
-                              head_dim 128 over K4V2 records: the kernel then
-                              rotates each row itself (the vector-unit paths
-                              require it)                                      */
+  const float* q_rot;      /* device [C][n_q_heads][head_dim] rotated; NULL
+                              over K4V2 records (any head_dim): the kernels
+                              then rotate each row themselves (the vector-unit
+                              paths of other code widths require it)           */
   const void* records;     /* device: record (j, h) at (j*n_kv_heads+h)*tile_bytes */
   int64_t n_record_rows;   /* tiles available; must be >= T(pos0 + C - 1)       */
   const float* k;          /* device raw keys: absolute position p, KV head h at

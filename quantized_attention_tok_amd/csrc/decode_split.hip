@@ -90,20 +90,6 @@ struct Lds {
   static_assert((wop % 16) == 0 && (qt % 16) == 0 && (winv % 16) == 0, "aligned sections");
 };
 
-// Walsh-Hadamard butterfly on lane bit M: lower lane a + b, upper lane a - b.
-// Bits 16 and 32 use the gfx950 permlane swaps: a swap of x with itself gives
-// the lower lane (own, partner) and the upper lane (partner, own).
-template <int M>
-__device__ __forceinline__ float bfly(float x, int lane) {
-  const float sg = __int_as_float(0x3F800000 | ((lane & M) ? 0x80000000 : 0));
-  if constexpr (M >= 16) {
-    const auto r = (M == 32) ? __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false)
-                             : __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaf(sg, __uint_as_float(r[1]), __uint_as_float(r[0]));
-  } else {
-    return xshfl<M>(x) + x * sg;
-  }
-}
 // x holds element lane, y element lane + 64 of a 128-vector: y <- H_128 x / sqrt(128)
 __device__ __forceinline__ void wht128(float& x, float& y, int lane) {
   x = bfly<1>(x, lane); y = bfly<1>(y, lane);

@@ -41,6 +41,7 @@ namespace kvarn {
 namespace {
 
 using mfma::as_half8;
+using mfma::bfly;
 using mfma::byte_pair;
 using mfma::floatx4;
 using mfma::fp16_scale_exp;
@@ -123,8 +124,13 @@ __global__ void __launch_bounds__(256) decode_wide_kernel(DecodeParams P) {
     return;
   }
 
-  // rotated query rows of the heads this wave prepares (clamped rows are read, never used)
-  const float* qsrc = P.q_rot + ((int64_t)b * P.n_q + (int64_t)kvh * G) * D;
+  // rotated query rows of the heads this wave prepares (clamped rows are read,
+  // never used); with q_rot NULL the wave rotates the raw rows itself: the
+  // Walsh-Hadamard butterflies on channel bits 0-5 across lanes (DPP and
+  // permlane swaps), bits 6 and up between a lane's registers (channel
+  // lane + 64 i), ascending, then the 1/sqrt(D) scale
+  const bool rot = P.q_rot == nullptr;
+  const float* qsrc = (rot ? P.q : P.q_rot) + ((int64_t)b * P.n_q + (int64_t)kvh * G) * D;
   float qp[PPW][CPL];
 #pragma unroll
   for (int k = 0; k < PPW; ++k) {
@@ -132,6 +138,31 @@ __global__ void __launch_bounds__(256) decode_wide_kernel(DecodeParams P) {
     const int hc = h < G ? h : 0;
 #pragma unroll
     for (int i = 0; i < CPL; ++i) qp[k][i] = qsrc[hc * D + lane + 64 * i];
+    if (rot) {   // uniform
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) {
+        float x = qp[k][i];
+        x = bfly<1>(x, lane);
+        x = bfly<2>(x, lane);
+        x = bfly<4>(x, lane);
+        x = bfly<8>(x, lane);
+        x = bfly<16>(x, lane);
+        qp[k][i] = bfly<32>(x, lane);
+      }
+#pragma unroll
+      for (int s = 1; s < CPL; s <<= 1) {
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+          if ((i & s) == 0) {
+            const float a = qp[k][i], c = qp[k][i + s];
+            qp[k][i] = a + c;
+            qp[k][i + s] = a - c;
+          }
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) qp[k][i] *= wht_scale<D>();
+    }
   }
   // operand rows that hold no head part stay zero (both q~ buffers, every w area)
   if constexpr (RPH > 2 || G < 8) {

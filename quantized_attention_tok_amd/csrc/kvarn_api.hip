@@ -113,7 +113,7 @@ int validate_decode(const kvarn_decode_args* a, DecodePlan* plan) {
   if (!(G == 1 || G == 2 || G == 4 || G == 8)) return KVARN_E_UNSUPPORTED;
   if (a->max_tiles < 0 || a->max_win < 0 || a->n_record_rows < 0) return KVARN_E_INVALID;
   if (!a->q || !a->out || !a->n_tiles || !a->n_win || !a->rec_start) return KVARN_E_INVALID;
-  if (!a->q_rot && !fused_decode(a->head_dim)) return KVARN_E_INVALID;
+  if (!a->q_rot && !k4v2(a->head_dim)) return KVARN_E_INVALID;   // K4V2 kernels rotate q themselves
   bool any_tiles = false, any_win = false;
   for (int b = 0; b < a->batch; ++b) {
     const int nt = a->n_tiles[b], nw = a->n_win[b];
@@ -168,7 +168,7 @@ int validate_prefill(const kvarn_prefill_args* a, DecodePlan* plan) {
   const int G = a->n_q_heads / a->n_kv_heads;
   if (!(G == 1 || G == 2 || G == 4 || G == 8)) return KVARN_E_UNSUPPORTED;
   if (!a->q || !a->out || !a->k || !a->v) return KVARN_E_INVALID;
-  if (!a->q_rot && !fused_decode(a->head_dim)) return KVARN_E_INVALID;
+  if (!a->q_rot && !k4v2(a->head_dim)) return KVARN_E_INVALID;   // K4V2 kernels rotate q themselves
   const int64_t last = a->pos0 + a->chunk - 1;
   const int64_t t_first = prefill_tiles_at(a->pos0, a->window);
   const int64_t t_last = prefill_tiles_at(last, a->window);

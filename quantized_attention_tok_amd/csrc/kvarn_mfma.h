@@ -144,5 +144,20 @@ __device__ __forceinline__ float wsum(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Walsh-Hadamard butterfly on lane bit M: lower lane a + b, upper lane a - b.
+// Bits 16 and 32 use the gfx950 permlane swaps: a swap of x with itself gives
+// the lower lane (own, partner) and the upper lane (partner, own).
+template <int M>
+__device__ __forceinline__ float bfly(float x, int lane) {
+  const float sg = __int_as_float(0x3F800000 | ((lane & M) ? 0x80000000 : 0));
+  if constexpr (M >= 16) {
+    const auto r = (M == 32) ? __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false)
+                             : __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaf(sg, __uint_as_float(r[1]), __uint_as_float(r[0]));
+  } else {
+    return xshfl<M>(x) + x * sg;
+  }
+}
+
 }  // namespace mfma
 }  // namespace kvarn

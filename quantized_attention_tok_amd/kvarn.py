@@ -200,8 +200,8 @@ def decode_attention(q, q_rot, records, rec_start, n_tiles, k_win, v_win, n_win,
                      win_start=None, f16_scales=False, kbits=4, vbits=2):
     """Decode attention for a batch.
 
-    q, q_rot: [B][Hq][d] fp32 (q_rot may be None for head_dim 128: the kernel
-    rotates q itself), or [B][w][Hq][d] for a multi-query verify of width
+    q, q_rot: [B][Hq][d] fp32 (q_rot may be None over K4V2 records: the kernels
+    rotate q themselves), or [B][w][Hq][d] for a multi-query verify of width
     w = 2..8 (head_dim 128): row i is the query of window token n_win - w + i
     and sees the tiles and window tokens [0, n_win - w + i].  records: uint8 pool [rows][Hkv][tile_bytes];
     sequence b's tile j is row rec_start[b] + j.  k_win, v_win: [B][cap][Hkv][d]
@@ -262,8 +262,8 @@ def prefill_attention(q, q_rot, records, n_record_rows, k, v, raw_base, pos0, wi
                       out=None, workspace=None, stream=None, f16_scales=False, kbits=4, vbits=2):
     """Chunk of C query positions [pos0, pos0+C) of one sequence.
 
-    q, q_rot: [C][Hq][d] (q_rot may be None at head_dim 128 over K4V2 records:
-    the kernel rotates the rows itself).  records: [rows][Hkv][tile_bytes] (tile j = row j).
+    q, q_rot: [C][Hq][d] (q_rot may be None over K4V2 records: the kernels
+    rotate the rows themselves).  records: [rows][Hkv][tile_bytes] (tile j = row j).
     k, v: raw [n][Hkv][d] views whose row i is absolute position raw_base + i;
     f16_scales: the records carry f16 scales; kbits / vbits: their code widths."""
     assert k.stride(2) == 1 and k.stride() == v.stride()

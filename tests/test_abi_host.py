@@ -144,7 +144,6 @@ def test_decode_validation_and_workspace_query(L):
         (dict(max_tiles=2), 1),                           # n_tiles > bound
         (dict(n_record_rows=3), 1),                       # tiles beyond the pool
         (dict(q=FAKE + 4), 3), (dict(win_tok_stride=130), 3),
-        (dict(head_dim=256, q_rot=None), 1),             # only head_dim 128 rotates in-kernel
         (dict(q_len=9), 1), (dict(q_len=-1), 1),          # verify width 0..8
         (dict(q_len=2, n_win=[1], max_win=1), 1),         # the drafts must be in the window
         (dict(q_len=2, head_dim=256, n_win=[4], max_win=4), 2),   # verify is head_dim 128
@@ -187,10 +186,15 @@ def test_prefill_validation(L):
     a = args()
     # the matrix-core prefill keeps its whole state on chip
     assert L.kvarn_prefill_workspace_bytes(ctypes.byref(a)) == 0
-    # it rotates the rows itself when no rotated query is given; the vector paths need one
+    # the K4V2 kernels rotate the rows themselves when no rotated query is given
+    # (at head_dim 256 the split partials still need a workspace); the
+    # vector-unit paths of other code widths need one
     assert L.kvarn_prefill_workspace_bytes(ctypes.byref(args(q_rot=None))) == 0
-    assert L.kvarn_prefill_attention(ctypes.byref(args(head_dim=256, q_rot=None, tok_stride=512, head_stride=256)),
-                                     ctypes.c_void_p(FAKE), 1 << 30, None) == 1
+    assert L.kvarn_prefill_workspace_bytes(
+        ctypes.byref(args(head_dim=256, q_rot=None, tok_stride=512, head_stride=256))) > 0
+    assert L.kvarn_prefill_attention(
+        ctypes.byref(args(head_dim=256 | (6 << 20) | (5 << 24), q_rot=None, tok_stride=512, head_stride=256)),
+        ctypes.c_void_p(FAKE), 1 << 30, None) == 1
     # the vector-unit prefill at head_dim 256 keeps split partials in the workspace
     a256 = args(head_dim=256, tok_stride=256 * 2, head_stride=256)
     need = L.kvarn_prefill_workspace_bytes(ctypes.byref(a256))

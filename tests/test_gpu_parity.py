@@ -358,8 +358,9 @@ def test_prefill_wide_heads_every_row_and_rechunk(d, Hq, Hkv):
     err = rel_l2(out, ref)
     say("rel_l2", err)
     assert err < TOL
-    # another chunking: the same tiles, rows within the split-plan rounding of each other
-    out2, recs2 = prefill_run(K, V, Q, W, 128, Hkv, d)
+    # another chunking (and queries rotated inside the kernels): the same tiles,
+    # rows within the split-plan rounding of each other
+    out2, recs2 = prefill_run(K, V, Q, W, 128, Hkv, d, rotate=False)
     assert np.array_equal(recs2, recs)
     assert rel_l2(out2, out) < 1e-5
 
@@ -649,6 +650,11 @@ def test_decode_wide_every_group_size_ragged(d, Hq, Hkv, f16):
         ref = oracle.decode(q[b], deq[b][0], deq[b][1], tiles[b], K[lo:], V[lo:], scale)
         err = rel_l2(got[b], ref)
         assert err < TOL, (b, err)
+    # q_rot None: the tile kernel rotates the queries itself (same butterflies)
+    out = kvarn.decode_attention(qd, None, to_dev(recs), rec_start, tiles, to_dev(kw), to_dev(vw), wins,
+                                 scale, f16_scales=f16)
+    torch.cuda.synchronize()
+    assert rel_l2(out.cpu().numpy(), got) < 1e-6
     # tiles only: every window empty
     keep = [b for b in range(B) if tiles[b]]
     out = kvarn.decode_attention(qd[keep], kvarn.rotate_query(qd[keep]), to_dev(recs),
