@@ -67,6 +67,7 @@ __device__ __forceinline__ void lds_sync() { asm volatile("" ::: "memory"); }
 // native 16-byte vector (arrays of it stay in registers)
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// G here counts the operand heads of a workgroup: query heads x query rows
 template <int D, int G>
 struct WideLds {
   // head h's fp16 hi and lo parts sit in operand rows RPH h and RPH h + 1, so
@@ -90,36 +91,48 @@ struct WideLds {
   static_assert((wop % 16) == 0 && (qt % 16) == 0, "aligned sections");
 };
 
-template <int D, int G, bool H>
+// RP query rows per workgroup (2 only in prefill, where neighbouring rows see
+// the same tiles and G <= 4 leaves half of the operand rows free): operand
+// head v stands for query row r = v / G, head h = v % G.  A row whose visible
+// tiles end earlier (a pair on both sides of a tile boundary) has its operand
+// heads masked on the tiles it does not see.
+template <int D, int G, bool H, int RP>
 __global__ void __launch_bounds__(256) decode_wide_kernel(DecodeParams P) {
-  using L = WideLds<D, G>;
+  constexpr int VH = RP * G;             // operand heads
+  using L = WideLds<D, VH>;
   using R = Rec<D, H>;
   constexpr int NB = D / 128;            // value groups
   constexpr int HPL = L::HPL, RPH = L::RPH;
   constexpr int K4 = D / 32;             // channel steps of the score products
   constexpr int CPL = D / 64;            // channels per lane in the query prep / K-code slice
   constexpr int VPL = D / 128;           // 16-byte pieces of the wave's V codes per lane
-  constexpr int PPW = (G + 3) / 4;       // query heads prepared per wave
+  constexpr int PPW = (VH + 3) / 4;      // operand heads prepared per wave
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
   const int split = blockIdx.x;
   const int kvh = blockIdx.y;
-  const int b = blockIdx.z;
-  const SeqView sv = seq_view(P, b);
+  const int b0 = blockIdx.z * RP;        // first query row (sequence in decode)
+  const SeqView sv = seq_view(P, b0);
+  int nt_r[RP];
+  nt_r[0] = sv.nt;
+  if constexpr (RP == 2) nt_r[1] = seq_view(P, b0 + 1).nt;   // same record rows (prefill view)
+  const int nt_max = RP == 2 ? max(nt_r[0], nt_r[RP - 1]) : nt_r[0];
   const int n_split = P.n_tsplit + P.n_wsplit;
 
   __shared__ __attribute__((aligned(16))) uint8_t lds[L::bytes];
 
-  float* part = P.part + (((int64_t)b * P.n_q + (int64_t)kvh * G) * n_split + split) * (D + 4);
-  const int64_t hs = (int64_t)n_split * (D + 4);   // partial of head h at part + h * hs
+  // partial of operand head v: row b0 + v / G, head kvh G + v % G
+  auto part_of = [&](int v) {
+    return P.part + (((int64_t)(b0 + v / G) * P.n_q + (int64_t)kvh * G + v % G) * n_split + split) * (D + 4);
+  };
   const int t_begin = split * P.tps;
-  const int t_end = min(sv.nt, t_begin + P.tps);
+  const int t_end = min(nt_max, t_begin + P.tps);
   if (t_begin >= t_end) {   // empty partial: m = -inf, l = 0, o = 0
-    for (int i = tid; i < G * (D + 2); i += 256) {
-      const int h = i / (D + 2), c = i % (D + 2);
-      part[h * hs + c] = (c == D) ? -INFINITY : 0.0f;
+    for (int i = tid; i < VH * (D + 2); i += 256) {
+      const int v = i / (D + 2), c = i % (D + 2);
+      part_of(v)[c] = (c == D) ? -INFINITY : 0.0f;
     }
     return;
   }
@@ -130,14 +143,14 @@ __global__ void __launch_bounds__(256) decode_wide_kernel(DecodeParams P) {
   // permlane swaps), bits 6 and up between a lane's registers (channel
   // lane + 64 i), ascending, then the 1/sqrt(D) scale
   const bool rot = P.q_rot == nullptr;
-  const float* qsrc = (rot ? P.q : P.q_rot) + ((int64_t)b * P.n_q + (int64_t)kvh * G) * D;
   float qp[PPW][CPL];
 #pragma unroll
   for (int k = 0; k < PPW; ++k) {
-    const int h = wv + 4 * k;
-    const int hc = h < G ? h : 0;
+    const int v = wv + 4 * k;
+    const int vc = v < VH ? v : 0;
+    const float* qsrc = (rot ? P.q : P.q_rot) + ((int64_t)(b0 + vc / G) * P.n_q + (int64_t)kvh * G + vc % G) * D;
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) qp[k][i] = qsrc[hc * D + lane + 64 * i];
+    for (int i = 0; i < CPL; ++i) qp[k][i] = qsrc[lane + 64 * i];
     if (rot) {   // uniform
 #pragma unroll
       for (int i = 0; i < CPL; ++i) {
@@ -165,14 +178,14 @@ __global__ void __launch_bounds__(256) decode_wide_kernel(DecodeParams P) {
     }
   }
   // operand rows that hold no head part stay zero (both q~ buffers, every w area)
-  if constexpr (RPH > 2 || G < 8) {
+  if constexpr (RPH > 2 || VH < 8) {
     for (int i = tid; i < 2 * K4 * kRowsW * 4; i += 256) {
       const int r = (i >> 2) & (kRowsW - 1);
-      if ((r % RPH) >= 2 || r / RPH >= G) reinterpret_cast<uint4*>(lds + L::qt)[i] = make_uint4(0, 0, 0, 0);
+      if ((r % RPH) >= 2 || r / RPH >= VH) reinterpret_cast<uint4*>(lds + L::qt)[i] = make_uint4(0, 0, 0, 0);
     }
     for (int i = tid; i < 4 * kRowsW * (kWRowW / 4); i += 256) {
       const int r = (i / (kWRowW / 4)) % kRowsW;
-      if ((r % RPH) >= 2 || r / RPH >= G) reinterpret_cast<uint4*>(lds + L::wop)[i] = make_uint4(0, 0, 0, 0);
+      if ((r % RPH) >= 2 || r / RPH >= VH) reinterpret_cast<uint4*>(lds + L::wop)[i] = make_uint4(0, 0, 0, 0);
     }
   }
 
@@ -228,8 +241,8 @@ __global__ void __launch_bounds__(256) decode_wide_kernel(DecodeParams P) {
     // ---- prep: q~ hi/lo operand rows, score unscale, bias, w scale ----
 #pragma unroll
     for (int k = 0; k < PPW; ++k) {
-      const int h = wv + 4 * k;
-      if (h < G) {   // wave-uniform
+      const int h = wv + 4 * k;   // operand head
+      if (h < VH) {   // wave-uniform
         float y[CPL];
         float am = 0.0f, bs = 0.0f;
 #pragma unroll
@@ -258,8 +271,8 @@ __global__ void __launch_bounds__(256) decode_wide_kernel(DecodeParams P) {
           qt[ib + 32] = (uint16_t)(lo >> 16);
         }
         if (lane == 0) {
-          reinterpret_cast<float*>(lds + L::us)[buf * G + h] = pow2i(24 - fe);
-          reinterpret_cast<float*>(lds + L::bias)[buf * G + h] = bias;
+          reinterpret_cast<float*>(lds + L::us)[buf * VH + h] = pow2i(24 - fe);
+          reinterpret_cast<float*>(lds + L::bias)[buf * VH + h] = bias;
         }
       }
     }
@@ -301,16 +314,19 @@ __global__ void __launch_bounds__(256) decode_wide_kernel(DecodeParams P) {
     float p0[HPL], p1[HPL];
 #pragma unroll
     for (int jj = 0; jj < HPL; ++jj) {
-      const int h = HPL * g + jj;
-      const int hc = h < G ? h : G - 1;
-      const float us = reinterpret_cast<const float*>(lds + L::us)[buf * G + hc];
-      const float bi = reinterpret_cast<const float*>(lds + L::bias)[buf * G + hc];
-      const float s0 = k0 * fmaf(acc0[RPH * jj] + acc0[RPH * jj + 1], us, bi);
-      const float s1 = k1 * fmaf(acc1[RPH * jj] + acc1[RPH * jj + 1], us, bi);
+      const int h = HPL * g + jj;   // operand head
+      const int hc = h < VH ? h : VH - 1;
+      const float us = reinterpret_cast<const float*>(lds + L::us)[buf * VH + hc];
+      const float bi = reinterpret_cast<const float*>(lds + L::bias)[buf * VH + hc];
+      // a row that does not see tile j (its visible tiles end earlier) is masked
+      const bool seen = RP == 1 || j < nt_r[(hc / G) & (RP - 1)];
+      const float s0 = seen ? k0 * fmaf(acc0[RPH * jj] + acc0[RPH * jj + 1], us, bi) : -INFINITY;
+      const float s1 = seen ? k1 * fmaf(acc1[RPH * jj] + acc1[RPH * jj + 1], us, bi) : -INFINITY;
       const float m_new = fmaxf(m_w[jj], row_max16(fmaxf(s0, s1)));
-      const float alpha = __builtin_amdgcn_exp2f(m_w[jj] - m_new);   // 0 on the first tile
-      p0[jj] = __builtin_amdgcn_exp2f(s0 - m_new);
-      p1[jj] = __builtin_amdgcn_exp2f(s1 - m_new);
+      const bool none = m_new == -INFINITY;   // masked, and no earlier tile: state stays empty
+      const float alpha = none ? 1.0f : __builtin_amdgcn_exp2f(m_w[jj] - m_new);   // 0 on the first tile
+      p0[jj] = none ? 0.0f : __builtin_amdgcn_exp2f(s0 - m_new);
+      p1[jj] = none ? 0.0f : __builtin_amdgcn_exp2f(s1 - m_new);
       m_w[jj] = m_new;
       l_w[jj] = fmaf(l_w[jj], alpha, p0[jj] + p1[jj]);   // summed over the row in the merge
 #pragma unroll
@@ -340,7 +356,7 @@ __global__ void __launch_bounds__(256) decode_wide_kernel(DecodeParams P) {
         const int h = HPL * g + jj;
         uint32_t hi, lo;
         split_pair(p0[jj] * (vs[cb] * fv), p1[jj] * (vs[NB + cb] * fv), hi, lo);
-        if (h < G) {
+        if (h < VH) {
           wrow[(RPH * h) * kWRowW + n] = hi;
           wrow[(RPH * h + 1) * kWRowW + n] = lo;
         }
@@ -381,20 +397,20 @@ __global__ void __launch_bounds__(256) decode_wide_kernel(DecodeParams P) {
   float2* s_ml = reinterpret_cast<float2*>(lds + L::ml);
 #pragma unroll
   for (int jj = 0; jj < HPL; ++jj) {
-    const int h = HPL * g + jj;
+    const int h = HPL * g + jj;   // operand head
     const float lsum = row_sum16(l_w[jj]);
-    if (h < G) {
+    if (h < VH) {
 #pragma unroll
       for (int cb = 0; cb < NB; ++cb) {
 #pragma unroll
-        for (int qb = 0; qb < 8; ++qb) s_mo[(wv * G + h) * D + 128 * cb + vci + qb] = o_w[jj][8 * cb + qb];
+        for (int qb = 0; qb < 8; ++qb) s_mo[(wv * VH + h) * D + 128 * cb + vci + qb] = o_w[jj][8 * cb + qb];
       }
       if (n == 0) s_ml[h * 4 + wv] = make_float2(m_w[jj], lsum);
     }
   }
   __syncthreads();
-  for (int i = tid; i < G * D; i += 256) {
-    const int h = i / D, c = i % D;
+  for (int i = tid; i < VH * D; i += 256) {
+    const int h = i / D, c = i % D;   // operand head, channel
     float M = s_ml[h * 4].x;
 #pragma unroll
     for (int w = 1; w < 4; ++w) M = fmaxf(M, s_ml[h * 4 + w].x);
@@ -402,25 +418,37 @@ __global__ void __launch_bounds__(256) decode_wide_kernel(DecodeParams P) {
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const float2 ml = s_ml[h * 4 + w];
-      const float sc = __builtin_amdgcn_exp2f(ml.x - M);
-      o = fmaf(sc, s_mo[(w * G + h) * D + c], o);
+      const float sc = ml.x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ml.x - M);   // also when M = -inf
+      o = fmaf(sc, s_mo[(w * VH + h) * D + c], o);
       l = fmaf(sc, ml.y, l);
     }
-    part[h * hs + c] = o;
+    float* part = part_of(h);
+    part[c] = o;
     if (c == 0) {
-      part[h * hs + D] = M * kLn2W;   // natural-log units, as the combine expects
-      part[h * hs + D + 1] = l;
+      part[D] = M * kLn2W;   // natural-log units, as the combine expects (-inf: empty)
+      part[D + 1] = l;
     }
   }
 }
 
 template <int D, int G>
 hipError_t launch_wide_dg(const DecodeParams& P, int batch, hipStream_t stream) {
+  // prefill rows in pairs when G <= 4 and the chunk has an even number of rows
+  if constexpr (G <= 4) {
+    if (P.mode == 1 && batch % 2 == 0) {
+      const dim3 grid(P.n_tsplit, P.n_kv, batch / 2);
+      if (P.h16)
+        hipLaunchKernelGGL((decode_wide_kernel<D, G, true, 2>), grid, dim3(256), 0, stream, P);
+      else
+        hipLaunchKernelGGL((decode_wide_kernel<D, G, false, 2>), grid, dim3(256), 0, stream, P);
+      return hipGetLastError();
+    }
+  }
   const dim3 grid(P.n_tsplit, P.n_kv, batch);
   if (P.h16)
-    hipLaunchKernelGGL((decode_wide_kernel<D, G, true>), grid, dim3(256), 0, stream, P);
+    hipLaunchKernelGGL((decode_wide_kernel<D, G, true, 1>), grid, dim3(256), 0, stream, P);
   else
-    hipLaunchKernelGGL((decode_wide_kernel<D, G, false>), grid, dim3(256), 0, stream, P);
+    hipLaunchKernelGGL((decode_wide_kernel<D, G, false, 1>), grid, dim3(256), 0, stream, P);
   return hipGetLastError();
 }
 
