@@ -38,7 +38,10 @@ import numpy as np
 
 TILE = 128
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libkvarn_oracle.so")
+# KVARN_ORACLE_SANITIZED=1 loads the AddressSanitizer/UBSan build of the same
+# C source (the sanitizer runtimes must be preloaded into the process).
+_SANITIZED = os.environ.get("KVARN_ORACLE_SANITIZED") == "1"
+_LIB_PATH = os.path.join(_HERE, "libkvarn_oracle_san.so" if _SANITIZED else "libkvarn_oracle.so")
 _lib = None
 
 
@@ -48,7 +51,7 @@ def _load():
         return _lib
     if not os.path.exists(_LIB_PATH):
         from . import build as _b
-        _b.build()
+        _b.build(sanitize=_SANITIZED)
     lib = ctypes.CDLL(_LIB_PATH)
     f32p = ctypes.POINTER(ctypes.c_float)
     f64p = ctypes.POINTER(ctypes.c_double)

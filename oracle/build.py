@@ -19,14 +19,23 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    cmd = ["gcc", *FLAGS, SRC, "-o", LIB + ".tmp", "-lm"]
+# A second build of the same source with AddressSanitizer and
+# UndefinedBehaviorSanitizer (host code only), loaded by the sanitizer test in
+# a child process with the sanitizer runtimes preloaded.
+SAN_LIB = os.path.join(HERE, "libkvarn_oracle_san.so")
+SAN_FLAGS = ["-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+             "-fno-sanitize-recover=undefined"]
+
+
+def build(verbose: bool = False, sanitize: bool = False) -> str:
+    out = SAN_LIB if sanitize else LIB
+    cmd = ["gcc", *FLAGS, *(SAN_FLAGS if sanitize else []), SRC, "-o", out + ".tmp", "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    os.replace(out + ".tmp", out)
+    return out
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, sanitize="--sanitize" in sys.argv))

@@ -215,8 +215,8 @@ def decode_attention(q, q_rot, records, rec_start, n_tiles, k_win, v_win, n_win,
     a, keep = _decode_args(q, q_rot, records, rows, rec_start, n_tiles, k_win, v_win, n_win,
                            scale, out, max_tiles, max_win, win_start, f16_scales, kbits, vbits)
     need = int(lib().kvarn_decode_workspace_bytes(ctypes.byref(a)))
-    if workspace is None:
-        workspace = torch.zeros(max(need, 16), dtype=torch.uint8, device=q.device)
+    if workspace is None:   # scratch: the kernels write every byte they read
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     _check("kvarn_decode_attention", lib().kvarn_decode_attention(
         ctypes.byref(a), _ptr(workspace), workspace.numel(), _stream(stream)))
     return out

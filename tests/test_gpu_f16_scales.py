@@ -12,6 +12,7 @@ import pytest
 import torch
 
 import oracle
+from poison import nan_bytes, nan_like
 from quantized_attention_tok_amd import kvarn, synth
 from quantized_attention_tok_amd.cache import SequenceCache
 
@@ -170,7 +171,7 @@ def test_verify_f16_ragged_batch():
             assert err < TOL, (b, i, err)
 
 
-def _prefill16(K, V, Q, W, chunk, Hkv, d):
+def _prefill16(K, V, Q, W, chunk, Hkv, d, poison=False):
     n = K.shape[0]
     cache = SequenceCache(Hkv, d, W, capacity=n + 128, device=DEV, f16_scales=True)
     outs = []
@@ -179,10 +180,16 @@ def _prefill16(K, V, Q, W, chunk, Hkv, d):
         c = min(chunk, n - p0)
         cache.append(to_dev(K[p0:p0 + c]), to_dev(V[p0:p0 + c]))
         qd = to_dev(Q[p0:p0 + c])
+        qr = kvarn.rotate_query(qd)
         raw_base = 128 * kvarn.visible_tiles(p0, W)
-        outs.append(kvarn.prefill_attention(qd, kvarn.rotate_query(qd), cache.records, cache.n_tiles,
+        extra = {}
+        if poison:   # NaN-filled output and workspace
+            nb = kvarn.prefill_workspace_bytes(qd, qr, cache.records, cache.n_tiles, cache.k[raw_base:],
+                                               cache.v[raw_base:], raw_base, p0, W, scale, f16_scales=True)
+            extra = {"out": nan_like(qd), "workspace": nan_bytes(nb)}
+        outs.append(kvarn.prefill_attention(qd, qr, cache.records, cache.n_tiles,
                                             cache.k[raw_base:], cache.v[raw_base:], raw_base, p0, W,
-                                            scale, f16_scales=True))
+                                            scale, f16_scales=True, **extra))
     torch.cuda.synchronize()
     return torch.cat(outs).cpu().numpy(), cache.records[:cache.n_tiles].cpu().numpy()
 
@@ -200,3 +207,9 @@ def test_prefill_f16_every_row(d, Hq, Hkv, n):
     err = rel_l2(out, ref)
     say("rel_l2", err)
     assert err < TOL
+    # an odd chunk (odd row counts in every chunk and the tail), NaN-filled buffers
+    out2, recs2 = _prefill16(K, V, Q, W, 77, Hkv, d, poison=True)
+    assert np.array_equal(recs2, recs)
+    err2 = rel_l2(out2, ref)
+    say("odd chunk rel_l2", err2, "vs chunk 256", rel_l2(out2, out))
+    assert err2 < TOL and rel_l2(out2, out) < 1e-5

@@ -11,6 +11,7 @@ import pytest
 import torch
 
 import oracle
+from poison import nan_bytes, nan_like
 from quantized_attention_tok_amd import kvarn, synth
 from quantized_attention_tok_amd.cache import SequenceCache
 
@@ -80,9 +81,13 @@ def test_decode_widths_8b_shape(kb, vb, f16):
     kh, vh = oracle.dequant_records(want, d, f16, kb, vb)
     scale = 1 / math.sqrt(d)
     qd = to_dev(q)
-    out = kvarn.decode_attention(qd, kvarn.rotate_query(qd), to_dev(recs), [0], [T],
-                                 to_dev(K[128 * T:][None]), to_dev(V[128 * T:][None]), [ctx - 128 * T],
-                                 scale, f16_scales=f16, kbits=kb, vbits=vb)
+    qr, rd = kvarn.rotate_query(qd), to_dev(recs)
+    kwd, vwd = to_dev(K[128 * T:][None]), to_dev(V[128 * T:][None])
+    # NaN-filled workspace and output: every partial the combine reads must be written
+    ws = nan_bytes(kvarn.decode_workspace_bytes(qd, qr, rd, [0], [T], kwd, vwd, [ctx - 128 * T], scale,
+                                                f16_scales=f16, kbits=kb, vbits=vb))
+    out = kvarn.decode_attention(qd, qr, rd, [0], [T], kwd, vwd, [ctx - 128 * T], scale, out=nan_like(qd),
+                                 workspace=ws, f16_scales=f16, kbits=kb, vbits=vb)
     torch.cuda.synchronize()
     ref = oracle.decode(q[0], kh, vh, T, K[128 * T:], V[128 * T:], scale)
     err = rel_l2(out.cpu().numpy()[0], ref)
