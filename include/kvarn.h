@@ -212,6 +212,32 @@ int kvarn_decode_attention(const kvarn_decode_args* args, void* workspace,
                            size_t workspace_bytes, void* stream);
 
 /*
+ * kvarn_decode_attention_noalloc -- kvarn_decode_attention for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): the same kernels and the same
+ * result, with the split partials in a library-owned device array of
+ * KVARN_NOALLOC_SCRATCH_BYTES per GPU instead of a caller workspace.  The
+ * caller still passes the inputs and the output in `args`.
+ *
+ *   - The array is a static device variable of the library: each GPU the
+ *     library runs on holds its own copy from the first call on that device
+ *     (its address is looked up once per device, with the device current)
+ *     until the process ends.  The call allocates and frees nothing.
+ *   - The current device must be the device of `stream` and of the pointers.
+ *   - Every call on one GPU shares that GPU's array, which keeps the last
+ *     call's partials; the kernels write every partial before they read it,
+ *     so nothing needs clearing.  Calls that overlap in time on one GPU (two
+ *     streams, two host threads) race on the array and give undefined
+ *     results: serialise them.
+ *   - Errors: those of kvarn_decode_attention, KVARN_E_WORKSPACE when
+ *     kvarn_decode_workspace_bytes(args) exceeds KVARN_NOALLOC_SCRATCH_BYTES
+ *     (checked before anything is enqueued), KVARN_E_DEVICE when the array's
+ *     address cannot be obtained.
+ */
+#define KVARN_NOALLOC_SCRATCH_BYTES (16u << 20)
+int kvarn_decode_attention_noalloc(const kvarn_decode_args* args, void* stream);
+
+/*
  * kvarn_prefill_attention -- causal attention of one chunk of C consecutive
  * query positions [pos0, pos0+C) of one sequence.  PR #434 commit list
  * (chunked batched prefill: single streaming softmax over compressed tiles +

@@ -4,6 +4,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/kvarn.h"
 #include "kvarn_launch.h"
 
@@ -190,6 +192,35 @@ int validate_prefill(const kvarn_prefill_args* a, DecodePlan* plan) {
   return KVARN_OK;
 }
 
+// Split partials of kvarn_decode_attention_noalloc: one array per GPU that
+// the library runs on, held until the process ends.  Host code never passes
+// the array's name to a kernel (on the host it is a stand-in, not a device
+// address): it uses the device address that hipGetSymbolAddress returns.
+static __device__ __align__(256) uint8_t scratch[KVARN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// The current device's copy of `scratch`, looked up once per device (with
+// that device current) and kept; NULL when the lookup failed.
+void* scratch_on_current_device(hipError_t* err) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *err = e != hipSuccess ? e : hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* ptr = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? ptr : nullptr;
+  });
+  *err = g_scratch_err[dev];
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -245,6 +276,17 @@ size_t kvarn_decode_workspace_bytes(const kvarn_decode_args* a) {
   DecodePlan p;
   if (validate_decode(a, &p) != KVARN_OK) return 0;
   return decode_ws(a, p);
+}
+
+int kvarn_decode_attention_noalloc(const kvarn_decode_args* a, void* stream) {
+  DecodePlan p;
+  int st = validate_decode(a, &p);
+  if (st != KVARN_OK) return st;
+  if (decode_ws(a, p) > (size_t)KVARN_NOALLOC_SCRATCH_BYTES) return KVARN_E_WORKSPACE;
+  hipError_t e = hipSuccess;
+  void* ws = scratch_on_current_device(&e);
+  if (!ws) return KVARN_E_DEVICE;
+  return kvarn_decode_attention(a, ws, KVARN_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 int kvarn_decode_attention(const kvarn_decode_args* a, void* workspace, size_t ws_bytes,

@@ -92,6 +92,8 @@ def lib():
     L.kvarn_decode_workspace_bytes.argtypes = [ctypes.POINTER(DecodeArgs)]
     L.kvarn_decode_attention.restype = ctypes.c_int
     L.kvarn_decode_attention.argtypes = [ctypes.POINTER(DecodeArgs), vp, ctypes.c_size_t, vp]
+    L.kvarn_decode_attention_noalloc.restype = ctypes.c_int
+    L.kvarn_decode_attention_noalloc.argtypes = [ctypes.POINTER(DecodeArgs), vp]
     L.kvarn_prefill_workspace_bytes.restype = ctypes.c_size_t
     L.kvarn_prefill_workspace_bytes.argtypes = [ctypes.POINTER(PrefillArgs)]
     L.kvarn_prefill_attention.restype = ctypes.c_int
@@ -220,6 +222,24 @@ def decode_attention(q, q_rot, records, rec_start, n_tiles, k_win, v_win, n_win,
     _check("kvarn_decode_attention", lib().kvarn_decode_attention(
         ctypes.byref(a), _ptr(workspace), workspace.numel(), _stream(stream)))
     return out
+
+
+def decode_attention_noalloc(q, q_rot, records, rec_start, n_tiles, k_win, v_win, n_win, scale, out,
+                             max_tiles=None, max_win=None, stream=None, win_start=None,
+                             f16_scales=False, kbits=4, vbits=2):
+    """decode_attention without a workspace: the split partials go to the
+    library's own per-GPU scratch array (at most NOALLOC_SCRATCH_BYTES of
+    partials; larger calls raise KVARN_E_WORKSPACE).  `out` must be given, so
+    the call makes no allocation."""
+    rows = records.shape[0] if records is not None else 0
+    a, keep = _decode_args(q, q_rot, records, rows, rec_start, n_tiles, k_win, v_win, n_win,
+                           scale, out, max_tiles, max_win, win_start, f16_scales, kbits, vbits)
+    _check("kvarn_decode_attention_noalloc",
+           lib().kvarn_decode_attention_noalloc(ctypes.byref(a), _stream(stream)))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
 def decode_workspace_bytes(q, q_rot, records, rec_start, n_tiles, k_win, v_win, n_win, scale,

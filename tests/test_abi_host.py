@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported(L):
     names = declared_functions()
-    assert len(names) == 8, names
+    assert len(names) == 9, names
     for n in names:
         assert hasattr(L, n), n
 
@@ -157,6 +157,26 @@ def test_decode_validation_and_workspace_query(L):
         b, k2 = _decode_args(**over)
         assert L.kvarn_decode_attention(ctypes.byref(b), ctypes.c_void_p(FAKE), 1 << 30, None) == want, over
         assert L.kvarn_decode_workspace_bytes(ctypes.byref(b)) == 0
+
+
+def test_noalloc_decode_validation_before_any_device_call(L):
+    """The no-allocation decode rejects what the workspace decode rejects, and
+    a call whose partials exceed its scratch array, before it touches the
+    device (this host has no GPU, so any device call would fail)."""
+    from quantized_attention_tok_amd import kvarn
+    m = re.search(r"#define\s+KVARN_NOALLOC_SCRATCH_BYTES\s+\((\d+)u << (\d+)\)", open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == kvarn.NOALLOC_SCRATCH_BYTES
+    for over, want in [(dict(head_dim=100), 2), (dict(n_tiles=[0], n_win=[0]), 1), (dict(q=FAKE + 4), 3),
+                       (dict(max_tiles=2), 1), (dict(q_len=9), 1)]:
+        b, k2 = _decode_args(**over)
+        assert L.kvarn_decode_attention_noalloc(ctypes.byref(b), None) == want, over
+    # 8 sequences of 4000 tiles at the 8B shape: far more partials than the array holds
+    B = 8
+    big, kb = _decode_args(head_dim=128, batch=B, n_q_heads=32, n_kv_heads=8, n_tiles=[4000] * B,
+                           n_win=[0] * B, rec_start=[4000 * b for b in range(B)], max_tiles=4000,
+                           n_record_rows=4000 * B)
+    assert L.kvarn_decode_workspace_bytes(ctypes.byref(big)) > kvarn.NOALLOC_SCRATCH_BYTES
+    assert L.kvarn_decode_attention_noalloc(ctypes.byref(big), None) == 4
 
 
 def test_verify_workspace_grows_with_width(L):
