@@ -18,6 +18,10 @@ LIB = os.path.join(HERE, "libkvarn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["kvarn_api.hip", "compress.hip", "rotate.hip", "decode.hip", "decode_split.hip", "decode_wide.hip", "prefill.hip"]
+# measured floors for the benchmark (plain read, matrix-op rate, empty launch):
+# a library of their own, not linked into libkvarn.so
+FLOORS_SOURCE = "floors.hip"
+FLOORS_LIB = os.path.join(HERE, "libkvarn_floors.so")
 
 COMMON = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -45,17 +49,22 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = [s for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
-    tmp = LIB + ".tmp"
+def _link(objs, out, verbose):
+    tmp = out + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True, capture_output=not verbose)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = [s for s in SOURCES if os.path.exists(os.path.join(CSRC, s))] + [FLOORS_SOURCE]
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
+    _link(objs[:-1], LIB, verbose)
+    _link(objs[-1:], FLOORS_LIB, verbose)
     return LIB
 
 

@@ -106,3 +106,11 @@ def ragged_contexts(seed: int, batch: int, lo: int, hi: int, window: int):
     ctx = r.integers(lo, hi + 1, size=batch)
     tiles = np.maximum(1, np.rint(ctx / TILE).astype(np.int64))
     return tiles
+
+
+def window_offsets(seed: int, batch: int):
+    """Per-sequence window fill beyond the W-token minimum at the start of a
+    stepped run, uniform in [0, 128): over 128 appended tokens every sequence
+    then promotes exactly one tile, at a step of its own."""
+    r = _streams(seed + 3000, 1)[0]
+    return r.integers(0, TILE, size=batch)
