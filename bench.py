@@ -231,7 +231,8 @@ def verify_case(torch, kvarn, synth, ctx, width, reps, seed=2):
 
 def qwen06b_case(torch, kvarn, synth, reps):
     """24 compressed tiles + a 256-token window, then 64 decode steps; each
-    step appends the new token's K and V rows to the FP32 window (no step
+    step appends the new token's K and V rows (adjacent in one [token][2][kv]
+    [d] buffer, one copy) to the FP32 window (no step
     crosses a promotion boundary: the window grows from 257 to 320 tokens,
     below the 384 at which a tile is promoted) and attends.  One
     single-layer step = two row copies and one decode call; the graph runs
@@ -251,12 +252,15 @@ def qwen06b_case(torch, kvarn, synth, reps):
     per_layer = T * Hkv * tb + 2 * cap * Hkv * d * 4
     L = max(8, int(math.ceil(2 * LLC_BYTES / per_layer)))
     recs = [rec0.clone() for _ in range(L)]
-    kwin = [torch.empty(1, cap, Hkv, d, device=dev) for _ in range(L)]
-    vwin = [torch.empty_like(kwin[0]) for _ in range(L)]
+    # window rows [cap][2][Hkv][d]: a token's K and V rows side by side, so one
+    # copy appends both; the decode call takes the two strided views
+    kvwin = [torch.empty(cap, 2, Hkv, d, device=dev) for _ in range(L)]
     for l in range(L):
-        kwin[l][0, :W] = kd[128 * T:n0]
-        vwin[l][0, :W] = vd[128 * T:n0]
-    src_k, src_v = kd[n0:].clone(), vd[n0:].clone()            # the 64 appended rows
+        kvwin[l][:W, 0] = kd[128 * T:n0]
+        kvwin[l][:W, 1] = vd[128 * T:n0]
+    kwin = [x[None, :, 0] for x in kvwin]
+    vwin = [x[None, :, 1] for x in kvwin]
+    src = torch.stack([kd[n0:], vd[n0:]], dim=1).contiguous()   # the 64 appended rows
     qs = torch.from_numpy(synth.make_q(w.seed, n_steps, Hq, d)).to(dev).reshape(n_steps, 1, Hq, d)
     outs = torch.empty(L, 1, Hq, d, device=dev)
     ws = torch.empty(max(16, kvarn.decode_workspace_bytes(qs[0], None, recs[0], [0], [T], kwin[0], vwin[0],
@@ -269,8 +273,7 @@ def qwen06b_case(torch, kvarn, synth, reps):
         for s in range(n_steps):
             n_w = W + s + 1
             for l in range(L):
-                kwin[l][0, n_w - 1].copy_(src_k[s])
-                vwin[l][0, n_w - 1].copy_(src_v[s])
+                kvwin[l][n_w - 1].copy_(src[s])
                 kvarn.decode_attention(qs[s], None, recs[l], [0], [T], kwin[l], vwin[l], [n_w], scale,
                                        out=outs[l], workspace=ws, max_win=cap)
 
@@ -286,7 +289,8 @@ def qwen06b_case(torch, kvarn, synth, reps):
             "decode_steps_per_s": 1.0 / (ms * 1e-3),
             "kv_tokens_per_s": kv_tokens / (ms * 1e-3),
             "ms_for_64_steps": 64 * ms, "achieved_GBps": alg / (ms * 1e-3) / 1e9,
-            "includes": "window row appends (two copies), query rotation, decode attention"}
+            "includes": "window row append (one copy of the token's K and V rows), query rotation, "
+                        "decode attention"}
 
 
 # ---------------------------------------------------------------------------
@@ -315,32 +319,31 @@ def wide_step_case(torch, kvarn, synth, name, n_steps, reps):
     rec_start = [int(x) for x in np.cumsum([0] + [t + 1 for t in T0[:-1]])]
     rows = sum(T0) + B
     pool0 = torch.empty(rows, Hkv, tb, dtype=torch.uint8, device=dev)
-    raw_k0 = torch.zeros(cap, B, Hkv, d, device=dev)
-    raw_v0 = torch.zeros_like(raw_k0)
-    src_k = torch.empty(n_steps, B, Hkv, d, device=dev)
-    src_v = torch.empty_like(src_k)
+    raw0 = torch.zeros(cap, B, 2, Hkv, d, device=dev)    # [row][seq][K or V][kv][d]
+    src = torch.empty(n_steps, B, 2, Hkv, d, device=dev)
     for b in range(B):
         n_w0 = W + r[b]
         K, V = synth.batch_sequence_kv(w, b, 128 * T0[b] + n_w0 + n_steps)
         kd, vd = torch.from_numpy(K).to(dev), torch.from_numpy(V).to(dev)
         kvarn.compress_tile(kd, vd, pool0[rec_start[b]:rec_start[b] + T0[b]], T0[b])
         lo = 128 * T0[b]
-        raw_k0[base - n_w0:base, b] = kd[lo:lo + n_w0]
-        raw_v0[base - n_w0:base, b] = vd[lo:lo + n_w0]
-        src_k[:, b] = kd[lo + n_w0:]
-        src_v[:, b] = vd[lo + n_w0:]
+        raw0[base - n_w0:base, b, 0] = kd[lo:lo + n_w0]
+        raw0[base - n_w0:base, b, 1] = vd[lo:lo + n_w0]
+        src[:, b, 0] = kd[lo + n_w0:]
+        src[:, b, 1] = vd[lo + n_w0:]
         del K, V, kd, vd
     per_layer = rows * Hkv * tb + 2 * cap * B * Hkv * d * 4
     L = max(2, int(math.ceil(2 * LLC_BYTES / per_layer)))
     pools = [pool0] + [pool0.clone() for _ in range(L - 1)]
-    raw_k = [raw_k0] + [raw_k0.clone() for _ in range(L - 1)]
-    raw_v = [raw_v0] + [raw_v0.clone() for _ in range(L - 1)]
+    raw = [raw0] + [raw0.clone() for _ in range(L - 1)]
+    raw_k = [x[:, :, 0] for x in raw]      # [rows][B][kv][d] strided views
+    raw_v = [x[:, :, 1] for x in raw]
     q = torch.from_numpy(synth.make_q(w.seed, B, Hq, d)).to(dev)
     out = torch.empty_like(q)
     max_tiles, max_win = max(T0) + 1, W + 128
     win_view = lambda t: t.permute(1, 0, 2, 3)    # [B][rows][kv][d] strided view
-    ws = torch.empty(max(16, kvarn.decode_workspace_bytes(q, None, pool0, rec_start, T0, win_view(raw_k0),
-                                                          win_view(raw_v0), [W] * B, scale,
+    ws = torch.empty(max(16, kvarn.decode_workspace_bytes(q, None, pool0, rec_start, T0, win_view(raw_k[0]),
+                                                          win_view(raw_v[0]), [W] * B, scale,
                                                           max_tiles=max_tiles, max_win=max_win)),
                      dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
@@ -362,9 +365,8 @@ def wide_step_case(torch, kvarn, synth, name, n_steps, reps):
 
     def step(l, s, with_updates=True):
         nt, st, nw, promote = plan[s]
-        if with_updates:
-            raw_k[l][base + s].copy_(src_k[s])
-            raw_v[l][base + s].copy_(src_v[s])
+        if with_updates:   # one copy appends every sequence's K and V rows
+            raw[l][base + s].copy_(src[s])
             for b in promote:   # the oldest 128 window rows become the sequence's next tile
                 lo = base - W - r[b]
                 kvarn.compress_tile(raw_k[l][lo:, b], raw_v[l][lo:, b],

@@ -7,7 +7,8 @@
 //
 //   decode_split_kernel<G, TPW>: workgroup = (split, KV head, sequence) with
 //     4 TPW waves.  Split s owns the tiles [TPW s, TPW s + TPW) and the raw
-//     window tokens [16 s, 16 s + 16) of its sequence.
+//     window tokens [E s, E s + E) of its sequence (E <= 16 from the split
+//     plan: the window spread over the tile splits).
 //     Tiles: wave (tau, wq) owns the 32-token quarter wq of tile tau from
 //     loads to value aggregate.  It loads only its own slice (the 16 code
 //     bytes of its tokens in every channel row, its 32 V-code rows, its
@@ -143,7 +144,8 @@ __global__ void __launch_bounds__(256 * TPW) decode_split_kernel(DecodeParams P)
   const int64_t hs = (int64_t)n_split * (D + 4);   // partial of head h at part + h * hs
   const int j0 = split * TPW;
   const int ntl = max(0, min(TPW, sv.nt - j0));                     // tiles of this split
-  const int nwt = max(0, min(kWinPerSplit, sv.nw - kWinPerSplit * split));   // window tokens
+  const int wps = P.wchunk;                                          // window tokens per split (<= 16)
+  const int nwt = max(0, min(wps, sv.nw - wps * split));             // window tokens of this split
   if (ntl == 0 && nwt == 0) {
     for (int i = tid; i < G * (D + 2); i += NT) {
       const int h = i / (D + 2), c = i % (D + 2);
@@ -177,7 +179,7 @@ __global__ void __launch_bounds__(256 * TPW) decode_split_kernel(DecodeParams P)
   for (int k = 0; k < KW; ++k) {
     const int tr = wv + NW * k;
     if (tr < nwt) {
-      const int64_t row = (int64_t)(kWinPerSplit * split + tr) * p_tok;
+      const int64_t row = (int64_t)(wps * split + tr) * p_tok;
       wk0[k] = kwin[row + lane];
       wk1[k] = kwin[row + lane + 64];
       wv0[k] = vwin[row + lane];

@@ -57,19 +57,22 @@ bool fused_decode(int32_t hd) { return dim_of(hd) == 128 && k4v2(hd); }
 
 // Matrix-core split plan: TPW tiles per workgroup (4 waves per tile): 2 once
 // the batch has 128 tile-heads (measured fastest at the 8B shape for
-// contexts 4096, 15488 and 32768, against 1 and 4), else 1; each split also
-// takes up to 16 window tokens, so there are enough splits for the longest
-// window.
+// contexts 4096, 15488 and 32768, against 1 and 4), else 1.  The window
+// tokens are spread over the tile splits (at most 16 per split; more splits
+// when the window needs them), so that no split carries many of them.
 DecodePlan plan_fused(int batch, int n_kv, int max_tiles, int max_win) {
   const int64_t units = (int64_t)batch * n_kv * (max_tiles > 0 ? max_tiles : 0);
   const int tpw = units >= 128 ? 2 : 1;
   DecodePlan p;
   p.tps = tpw;
   const int nt = max_tiles > 0 ? (max_tiles + tpw - 1) / tpw : 0;
-  const int nw = max_win > 0 ? (max_win + kvarn::kWinPerSplit - 1) / kvarn::kWinPerSplit : 0;
+  int wps = nt > 0 ? (max_win + nt - 1) / nt : kvarn::kWinPerSplit;
+  if (wps < 1) wps = 1;
+  if (wps > kvarn::kWinPerSplit) wps = kvarn::kWinPerSplit;
+  const int nw = max_win > 0 ? (max_win + wps - 1) / wps : 0;
   p.n_tsplit = nt > nw ? nt : nw;
   p.n_wsplit = 0;
-  p.wchunk = kvarn::kWinPerSplit;
+  p.wchunk = wps;
   return p;
 }
 

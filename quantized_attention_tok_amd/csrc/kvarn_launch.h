@@ -11,7 +11,7 @@ namespace kvarn {
 
 constexpr int kDecThreads = 256;
 constexpr int kWinChunk = 64;      // window tokens per split (vector-unit kernels)
-constexpr int kWinPerSplit = 16;   // window tokens per split (head_dim-128 matrix-core kernel)
+constexpr int kWinPerSplit = 16;   // most window tokens per split (head_dim-128 matrix-core kernel)
 
 struct DecodeParams {
   const float* q;
