@@ -94,6 +94,29 @@ __device__ __forceinline__ float halve32(float (&a)[32], int lane, Op op) {
   return op(a[0], xor_lane<32>(a[0], lane));
 }
 
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+
+// halve32 over a[j] = f(j), producing the values in the pairs the first stage
+// joins (j, j + 16), so that only 16 of them are ever live: the same
+// operations in the same order as halve32.
+template <typename F, typename Op>
+__device__ __forceinline__ float halve32_lazy(F f, int lane, Op op) {
+  float a[32];
+  const bool up = (lane & 1) != 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float lo = f(i), hi = f(i + 16);
+    const float send = up ? lo : hi;
+    const float keep = up ? hi : lo;
+    a[i] = op(keep, xor_lane<1>(send, lane));
+  }
+  halve_stage<16, 2>(a, lane, op);
+  halve_stage<8, 4>(a, lane, op);
+  halve_stage<4, 8>(a, lane, op);
+  halve_stage<2, 16>(a, lane, op);
+  return op(a[0], xor_lane<32>(a[0], lane));
+}
+
 __device__ __forceinline__ int brev5(int l) {
   return ((l & 1) << 4) | ((l & 2) << 2) | (l & 4) | ((l & 8) >> 2) | ((l & 16) >> 4);
 }
@@ -107,24 +130,27 @@ __device__ __forceinline__ float code_of(float xn, float lo, float inv, float le
 
 // GEN: kb-bit keys and vb-bit values (runtime widths, LSB-first bit streams);
 // otherwise the K4V2 record (kb, vb ignored).
+// Three waves per SIMD at D = 128 (registers capped at 168 per lane, the LDS
+// area small enough): three workgroups share a CU.
 template <int D, bool H, bool GEN>
-__global__ void __launch_bounds__(2 * D)
+__global__ void __launch_bounds__(2 * D, D == 128 ? 3 : 1)
 compress_kernel(const float* __restrict__ kin, const float* __restrict__ vin,
                 int64_t tok_stride, int64_t head_stride, int n_kv,
                 uint8_t* __restrict__ records, int kb, int vb) {
   constexpr int W = D / 32;        // waves
-  constexpr int J = kTile / W;     // channel offsets per LDS exchange round
-  constexpr bool kStoreQ = D <= 256;
+  // channel offsets per LDS exchange round: two rounds of 16 at D = 128, so
+  // that the exchange area (and the workgroup's LDS) allows four workgroups per CU
+  constexpr int J = D == 128 ? 16 : kTile / W;
   using R = Rec<D, H>;
   if constexpr (!GEN) { kb = 4; vb = 2; }
   const RecRT o = rec_rt(D, H, kb, vb);
 
-  // Reused by every phase: 64 KB, more for the padded WHT exchange (W x 128
-  // rows of J + 1 floats) and for the generic key packing (one byte per code
-  // after two per-channel vectors: 34 D floats).
-  constexpr int kXS = J + 1;   // exchange row stride: 2-way instead of 64-way bank conflicts
-  constexpr int kSmem0 = W * kTile * kXS > 16384 ? W * kTile * kXS : 16384;
-  constexpr int kSmem = (GEN && 34 * D > kSmem0) ? 34 * D : kSmem0;
+  // Reused by every phase: the padded WHT exchange (W x 128 rows of J + 1
+  // floats); the two per-channel broadcast vectors followed by the per-wave
+  // token partials (W x 128 x 2 floats) or the key code bytes (D x 64, or one
+  // byte per code for the generic packing: D x 128).
+  constexpr int kXS = J + 1;   // exchange row stride: odd, so rows start in distinct banks
+  constexpr int kSmem = cmax(W * kTile * kXS, cmax(2 * D + 2 * W * kTile, GEN ? 34 * D : 18 * D));
   __shared__ float smem[kSmem];
 
   const int tid = threadIdx.x;
@@ -215,18 +241,9 @@ compress_kernel(const float* __restrict__ kin, const float* __restrict__ vin,
       for (int j = 0; j < 32; ++j) x[i][j] = x[i][j] * c;
   }
 
-  // ---- Sinkhorn-Knopp on Q = X*X ----
-  float Qs[kStoreQ ? 2 : 1][kStoreQ ? 32 : 1];
-  if constexpr (kStoreQ) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 32; ++j) Qs[i][j] = x[i][j] * x[i][j];
-  }
-  auto Qv = [&](int i, int j) -> float {
-    if constexpr (kStoreQ) return Qs[i][j];
-    else return x[i][j] * x[i][j];
-  };
+  // ---- Sinkhorn-Knopp on Q = X*X: the squares are recomputed at each use
+  // (the same rounded products), so the tile is held once in registers ----
+  auto Qv = [&](int i, int j) -> float { return x[i][j] * x[i][j]; };
 
   float* bc_v = smem;               // [D] per-channel broadcast
   float* bc_x = smem + D;           // [D] second per-channel broadcast
@@ -243,35 +260,29 @@ compress_kernel(const float* __restrict__ kin, const float* __restrict__ vin,
   for (int it = 0; it < 8; ++it) {
     // channel step: mean over tokens of Q * u
     {
-      float a[32];
-#pragma unroll
-      for (int j = 0; j < 32; ++j) {
-        float p0 = Qv(0, j) * u[0];
-        float p1 = Qv(1, j) * u[1];
-        a[j] = p0 + p1;
-      }
-      float sum = halve32(a, lane, OpAdd{});
+      const float sum = halve32_lazy([&](int j) { return Qv(0, j) * u[0] + Qv(1, j) * u[1]; }, lane, OpAdd{});
       float m = sum * kInvT;
       if (!(m >= FLT_MIN)) m = 1.0f;
       mc_own = m;
       if (owner) bc_v[ch_own] = 1.0f / m;
     }
     __syncthreads();
-    // token step: mean over channels of Q * v
+    // token step: mean over channels of Q * v; the pairwise tree over the 32
+    // products taken as eight 4-product sums, then the tree over those
     {
-      float v[32];
+      float t[2][8];
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
-        float4 f = reinterpret_cast<const float4*>(bc_v + 32 * w)[q];
-        v[4 * q + 0] = f.x; v[4 * q + 1] = f.y; v[4 * q + 2] = f.z; v[4 * q + 3] = f.w;
+        const float4 f = reinterpret_cast<const float4*>(bc_v + 32 * w)[q];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const float p0 = Qv(i, 4 * q) * f.x, p1 = Qv(i, 4 * q + 1) * f.y;
+          const float p2 = Qv(i, 4 * q + 2) * f.z, p3 = Qv(i, 4 * q + 3) * f.w;
+          t[i][q] = (p0 + p1) + (p2 + p3);
+        }
       }
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        float p[32];
-#pragma unroll
-        for (int j = 0; j < 32; ++j) p[j] = Qv(i, j) * v[j];
-        tp[w * kTile + 2 * lane + i] = psum<32, 0, 32>(p);
-      }
+      for (int i = 0; i < 2; ++i) tp[w * kTile + 2 * lane + i] = psum<8, 0, 8>(t[i]);
     }
     __syncthreads();
 #pragma unroll
@@ -312,14 +323,8 @@ compress_kernel(const float* __restrict__ kin, const float* __restrict__ vin,
 
   if (is_key) {
     // ---- keys: per channel over the 128 tokens, 4 bits ----
-    float lo_a[32], hi_a[32];
-#pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      lo_a[j] = OpMin{}(x[0][j], x[1][j]);
-      hi_a[j] = OpMax{}(x[0][j], x[1][j]);
-    }
-    float lo = halve32(lo_a, lane, OpMin{}) + 0.0f;
-    float hi = halve32(hi_a, lane, OpMax{}) + 0.0f;
+    const float lo = halve32_lazy([&](int j) { return OpMin{}(x[0][j], x[1][j]); }, lane, OpMin{}) + 0.0f;
+    const float hi = halve32_lazy([&](int j) { return OpMax{}(x[0][j], x[1][j]); }, lane, OpMax{}) + 0.0f;
     const float klev = GEN ? (float)((1 << kb) - 1) : 15.0f;
     float delta = (hi - lo) / klev;
     float inv = (delta >= FLT_MIN) ? 1.0f / delta : 0.0f;
