@@ -611,7 +611,8 @@ def cpu_baseline(synth):
     with cf.ProcessPoolExecutor(workers, mp_context=ctx_mp, initializer=_worker_init,
                                 initargs=(recs, kwin, vwin, qs, T, scale)) as ex:
         list(ex.map(_worker_decode, range(workers)))      # warm every worker
-        n_all = 2 * workers
+        per_step = sec1 / n_dec                           # about 3 s of work per process
+        n_all = workers * max(2, int(round(3.0 / per_step)))
         t0 = time.perf_counter()
         list(ex.map(_worker_decode, range(n_all)))
         secw = time.perf_counter() - t0

@@ -22,6 +22,12 @@
  *   - Device pointers and strides (in bytes) must be 16-byte aligned.
  *   - fp32 throughout; non-finite inputs give undefined results (not checked).
  *   - Results are bitwise reproducible run to run for the same arguments.
+ *   - The method's parameters are not call arguments: the group (128 tokens
+ *     per tile, 128 channels per value group) and the 8 Sinkhorn iterations
+ *     are fixed by issue #180's preset kvarn_k4v2_g128; the record format
+ *     (head_dim, f16 scales, code widths) is one head_dim word (below).
+ *     Records are written contiguously, [tile][KV head], and decode reads
+ *     them through per-sequence start rows of a pool.
  *
  * Tile record (one per 128-token tile and KV head), kvarn_tile_bytes(d) =
  * 116*d + 512 bytes, every section 16-byte aligned:
