@@ -496,11 +496,16 @@ hipError_t launch_decode_dg(const DecodeParams& P, int batch, hipStream_t stream
   const bool gen = !(P.kb == 4 && P.vb == 2);
   if (D >= 256 && !gen) {
     // K4V2 at head_dim 256 / 512: tile splits on the matrix cores, the window
-    // splits on this kernel, launched over them alone
+    // splits on this kernel, launched over them alone (decode), or one window
+    // partial per row on the matrix cores (prefill)
     hipError_t e = hipSuccess;
     if (P.n_tsplit > 0) e = launch_decode_wide_tiles(D, P, batch, stream);
     if (e != hipSuccess) return e;
-    if (P.n_wsplit > 0) {
+    if (P.n_wsplit > 0 && P.mode == 1) {
+      // prefill: the raw windows of 16 consecutive rows at a time on the matrix cores
+      e = launch_window_mfma(D, P, batch, stream);
+      if (e != hipSuccess) return e;
+    } else if (P.n_wsplit > 0) {
       DecodeParams W = P;
       W.split0 = P.n_tsplit;
       const dim3 wgrid(P.n_wsplit, P.n_kv, batch);

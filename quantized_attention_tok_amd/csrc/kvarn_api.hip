@@ -191,6 +191,9 @@ int validate_prefill(const kvarn_prefill_args* a, DecodePlan* plan) {
     if (last + 1 < max_win) max_win = last + 1;
     *plan = plan_decode(a->chunk, a->n_kv_heads, (int)t_last, (int)max_win, kTargetGroups,
                         kvarn::kWinChunk);
+    // K4V2 records at head_dim 256 / 512: the raw windows run on the window
+    // kernel, one partial per row and head
+    if (k4v2(a->head_dim) && dim_of(a->head_dim) >= 256) plan->n_wsplit = 1;
   }
   return KVARN_OK;
 }

@@ -104,6 +104,10 @@ hipError_t launch_decode_fused(const DecodeParams& P, int batch, hipStream_t str
 // K4V2 records, on the matrix cores; P.q_rot must hold the rotated queries.
 hipError_t launch_decode_wide_tiles(int d, const DecodeParams& P, int batch, hipStream_t stream);
 hipError_t launch_prefill_mfma(const PrefillParams& P, hipStream_t stream);
+// The raw-window part of chunked prefill (P.mode 1) at head_dim 256 / 512 on
+// the fp32 matrix cores: one raw-domain partial per chunk row and query head,
+// written as split P.n_tsplit of P.n_tsplit + P.n_wsplit (P.n_wsplit = 1).
+hipError_t launch_window_mfma(int d, const DecodeParams& P, int chunk, hipStream_t stream);
 // Multi-query verify (head_dim 128): P.part holds batch * q_len * n_q *
 // (n_tsplit + n_wsplit) partials of D + 4 floats (n_wsplit window splits of
 // wchunk tokens); with P.q_rot NULL the kernel rotates q itself.
