@@ -13,7 +13,8 @@
 //
 // Split-tile schedule (issue #433 item 2): a fixed worst-case grid of
 // (split, KV head, sequence) workgroups; splits beyond a sequence's tiles or
-// window exit early with an empty partial.  Each workgroup keeps an online
+// window exit at once and write nothing (the combine reads only the splits
+// that hold tiles or window tokens of the sequence).  Each workgroup keeps an online
 // softmax (running max, sum, rescaled accumulator; state initialised to
 // m = -inf, l = 0 before the first tile -- the hazard the PR #434 review
 // points at) and writes (m, l, o) per query head.  The combine kernel merges
@@ -50,7 +51,7 @@ __global__ void __launch_bounds__(kDecThreads) decode_partial_kernel(DecodeParam
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
-  const int split = blockIdx.x + P.split0;
+  const int split = blockIdx.x;
   const int kvh = blockIdx.y;
   const int b = blockIdx.z;
   const int n_split = P.n_tsplit + P.n_wsplit;
@@ -94,16 +95,10 @@ __global__ void __launch_bounds__(kDecThreads) decode_partial_kernel(DecodeParam
   }
 
   float* part = P.part + (((int64_t)b * P.n_q + (int64_t)kvh * G) * n_split + split) * (D + 4);
+  // a split with no tiles or tokens of this sequence writes nothing: the
+  // combine reads only the splits that hold some
   const bool empty = is_tile ? (t_begin >= t_end) : (w_begin >= w_end);
-  if (empty) {
-    // empty partial: m = -inf, l = 0, o = 0
-    for (int i = tid; i < G * (D + 4); i += kDecThreads) {
-      const int h = i / (D + 4), c = i % (D + 4);
-      float val = (c == D) ? -INFINITY : 0.0f;
-      part[(int64_t)h * n_split * (D + 4) + c] = val;
-    }
-    return;
-  }
+  if (empty) return;
 
   // query rows for this KV head's G heads
   const float* qsrc = (is_tile ? P.q_rot : P.q) + ((int64_t)b * P.n_q + (int64_t)kvh * G) * D;
@@ -395,16 +390,25 @@ __global__ void __launch_bounds__(64 * NWV) decode_combine_kernel(DecodeParams P
   const float* part = P.part + ((int64_t)b * P.n_q + hq) * n_split * (D + 4);
   __shared__ float s_st[NWV][2];
   __shared__ float s_o[NWV][2][D];
+  // only the splits that hold tiles or window tokens of this row are read
+  // (the split kernels write nothing for the others): virtual split v < nvt
+  // is tile split v, the rest window split v - nvt
+  const SeqView sv = seq_view(P, b);
+  const int nvt = min(nts, (sv.nt + P.tps - 1) / P.tps);
+  const int nvw = min(P.n_wsplit, (sv.nw + P.wchunk - 1) / P.wchunk);
+  const int nv = nvt + nvw;
+  auto split_of = [&](int v) { return v < nvt ? v : nts + (v - nvt); };
 
   float M = -INFINITY, L = 0.0f;
   float orot[K], oraw[K];
 #pragma unroll
   for (int k = 0; k < K; ++k) { orot[k] = 0.0f; oraw[k] = 0.0f; }
-  for (int base = PW * w; base < n_split; base += NWV * PW) {
+  for (int base = PW * w; base < nv; base += NWV * PW) {
     float m = -INFINITY, l = 0.0f;
-    if (lane < PW && base + lane < n_split) {
-      m = part[(int64_t)(base + lane) * (D + 4) + D];
-      l = part[(int64_t)(base + lane) * (D + 4) + D + 1];
+    if (lane < PW && base + lane < nv) {
+      const int64_t s = split_of(base + lane);
+      m = part[s * (D + 4) + D];
+      l = part[s * (D + 4) + D + 1];
     }
     const float mc = wave_max(m);
     if (mc > M) {
@@ -418,11 +422,11 @@ __global__ void __launch_bounds__(64 * NWV) decode_combine_kernel(DecodeParams P
     L += wave_sum(wgt * l);
 #pragma unroll
     for (int j = 0; j < PW; ++j) {
-      const int s = base + j;
-      if (s < n_split) {   // uniform
+      const int v = base + j;
+      if (v < nv) {   // uniform
         const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), j));
-        const float* ps = part + (int64_t)s * (D + 4);
-        if (s < nts) {
+        const float* ps = part + (int64_t)split_of(v) * (D + 4);
+        if (v < nvt) {
 #pragma unroll
           for (int k = 0; k < K; ++k) orot[k] = fmaf(wj, ps[lane + 64 * k], orot[k]);
         } else {
@@ -495,24 +499,18 @@ template <int D, int G>
 hipError_t launch_decode_dg(const DecodeParams& P, int batch, hipStream_t stream) {
   const bool gen = !(P.kb == 4 && P.vb == 2);
   if (D >= 256 && !gen) {
-    // K4V2 at head_dim 256 / 512: tile splits on the matrix cores, the window
-    // splits on this kernel, launched over them alone (decode), or one window
-    // partial per row on the matrix cores (prefill)
+    // K4V2 at head_dim 256 / 512: tile splits on the matrix cores; in decode
+    // the window splits run in the same grid, in prefill the raw windows of
+    // 16 consecutive rows at a time on the matrix cores (one partial per row)
     hipError_t e = hipSuccess;
-    if (P.n_tsplit > 0) e = launch_decode_wide_tiles(D, P, batch, stream);
-    if (e != hipSuccess) return e;
-    if (P.n_wsplit > 0 && P.mode == 1) {
-      // prefill: the raw windows of 16 consecutive rows at a time on the matrix cores
-      e = launch_window_mfma(D, P, batch, stream);
+    if (P.mode == 0) {
+      if (P.n_tsplit + P.n_wsplit > 0) e = launch_decode_wide(D, P, batch, stream);
       if (e != hipSuccess) return e;
-    } else if (P.n_wsplit > 0) {
-      DecodeParams W = P;
-      W.split0 = P.n_tsplit;
-      const dim3 wgrid(P.n_wsplit, P.n_kv, batch);
-      if (P.h16)
-        hipLaunchKernelGGL((decode_partial_kernel<D, G, true, false>), wgrid, dim3(kDecThreads), 0, stream, W);
-      else
-        hipLaunchKernelGGL((decode_partial_kernel<D, G, false, false>), wgrid, dim3(kDecThreads), 0, stream, W);
+    } else {
+      if (P.n_tsplit > 0) e = launch_decode_wide(D, P, batch, stream);
+      if (e != hipSuccess) return e;
+      if (P.n_wsplit > 0) e = launch_window_mfma(D, P, batch, stream);
+      if (e != hipSuccess) return e;
     }
   } else {
   dim3 grid(P.n_tsplit + P.n_wsplit, P.n_kv, batch);

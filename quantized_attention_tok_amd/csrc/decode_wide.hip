@@ -91,6 +91,114 @@ struct WideLds {
   static_assert((wop % 16) == 0 && (qt % 16) == 0, "aligned sections");
 };
 
+// Raw-window split ws of sequence b, KV head kvh (decode, launched after the
+// tile splits in the same grid): window tokens [64 ws, min(nw, 64 ws + 64)),
+// the G query heads' raw rows, one softmax per head over the split's tokens.
+// Scores: each wave takes four tokens per step, 16 lanes per token; a lane
+// reads 16-byte pieces 64 channels apart of its token's key row (the 16 lanes
+// of a token read whole 256-byte runs), takes the query pieces from LDS, and
+// the 16 partial products sum over the DPP row.  Values: thread t owns
+// channels t + 256 k of every head, eight tokens' rows loaded at a time.
+// Writes the raw-domain partial of each head: o, the running max in
+// natural-log units and the sum of weights.
+template <int D, int G>
+__device__ __forceinline__ void wide_window_split(const DecodeParams& P, uint8_t* lds, const SeqView& sv, int b,
+                                                  int kvh, int ws, int split, int n_split) {
+  constexpr int WC = kWinChunk;
+  constexpr int CPT = D / 256;           // value channels per thread
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int w0 = ws * WC;
+  const int n = min(WC, sv.nw - w0);     // >= 1: the caller skips empty splits
+  float* s_q = reinterpret_cast<float*>(lds);   // [G][D] raw query rows
+  float* s_p = s_q + G * D;                     // [G][WC] scores, then weights
+  float* s_ml = s_p + G * WC;                   // [G][2] max (natural log), sum
+  const float* qsrc = P.q + ((int64_t)b * P.n_q + (int64_t)kvh * G) * D;
+  for (int i = tid; i < G * D / 4; i += 256)
+    reinterpret_cast<float4*>(s_q)[i] = reinterpret_cast<const float4*>(qsrc)[i];
+  const int64_t ts = P.win_tok_stride;
+  const float* kb = P.k_win + sv.win_off + (int64_t)kvh * P.win_head_stride + (int64_t)w0 * ts;
+  const float* vb = P.v_win + sv.win_off + (int64_t)kvh * P.win_head_stride + (int64_t)w0 * ts;
+  __syncthreads();
+
+  const float c_log2 = P.scale * kLog2eW;
+  const int piece = lane & 15;
+  for (int tb = 4 * wv; tb < n; tb += 16) {   // wave-uniform
+    const int t = tb + (lane >> 4);
+    const float* krow = kb + (int64_t)(t < n ? t : 0) * ts + 4 * piece;
+    float4 kk[D / 64];
+#pragma unroll
+    for (int i = 0; i < D / 64; ++i) kk[i] = *reinterpret_cast<const float4*>(krow + 64 * i);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float a = 0.0f;
+#pragma unroll
+      for (int i = 0; i < D / 64; ++i) {
+        const float4 q4 = *reinterpret_cast<const float4*>(s_q + h * D + 4 * piece + 64 * i);
+        a += q4.x * kk[i].x + q4.y * kk[i].y + q4.z * kk[i].z + q4.w * kk[i].w;
+      }
+      a = row_sum16(a);
+      if (piece == 0 && t < n) s_p[h * WC + t] = a * c_log2;
+    }
+  }
+  __syncthreads();
+  for (int h = wv; h < G; h += 4) {
+    const float sc = lane < n ? s_p[h * WC + lane] : -INFINITY;
+    const float m = wmax(sc);   // finite: the split holds a token
+    const float p = lane < n ? __builtin_amdgcn_exp2f(sc - m) : 0.0f;
+    const float l = wsum(p);
+    s_p[h * WC + lane] = p;
+    if (lane == 0) {
+      s_ml[2 * h] = m * kLn2W;
+      s_ml[2 * h + 1] = l;
+    }
+  }
+  __syncthreads();
+
+  float acc[G][CPT];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) acc[h][k] = 0.0f;
+  const float* vcol = vb + tid;
+  int t = 0;
+  for (; t + 8 <= n; t += 8) {
+    float v[8][CPT];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) v[u][k] = vcol[(int64_t)(t + u) * ts + 256 * k];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float p = s_p[h * WC + t + u];
+#pragma unroll
+        for (int k = 0; k < CPT; ++k) acc[h][k] = fmaf(p, v[u][k], acc[h][k]);
+      }
+  }
+  for (; t < n; ++t) {
+    float v[CPT];
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) v[k] = vcol[(int64_t)t * ts + 256 * k];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float p = s_p[h * WC + t];
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) acc[h][k] = fmaf(p, v[k], acc[h][k]);
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float* o = P.part + (((int64_t)b * P.n_q + (int64_t)kvh * G + h) * n_split + split) * (D + 4);
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) o[tid + 256 * k] = acc[h][k];
+    if (tid == 0) {
+      o[D] = s_ml[2 * h];
+      o[D + 1] = s_ml[2 * h + 1];
+    }
+  }
+}
+
 // RP query rows per workgroup (2 only in prefill, where neighbouring rows see
 // the same tiles and G <= 4 leaves half of the operand rows free): operand
 // head v stands for query row r = v / G, head h = v % G.  A row whose visible
@@ -123,19 +231,22 @@ __global__ void __launch_bounds__(256) decode_wide_kernel(DecodeParams P) {
 
   __shared__ __attribute__((aligned(16))) uint8_t lds[L::bytes];
 
+  if constexpr (RP == 1) {
+    static_assert((G * D + G * kWinChunk + 2 * G) * 4 <= L::bytes, "the window split fits the LDS area");
+    if (split >= P.n_tsplit) {   // a raw-window split (decode)
+      const int ws = split - P.n_tsplit;
+      if (ws * kWinChunk < sv.nw) wide_window_split<D, G>(P, lds, sv, b0, kvh, ws, split, n_split);
+      return;
+    }
+  }
+
   // partial of operand head v: row b0 + v / G, head kvh G + v % G
   auto part_of = [&](int v) {
     return P.part + (((int64_t)(b0 + v / G) * P.n_q + (int64_t)kvh * G + v % G) * n_split + split) * (D + 4);
   };
   const int t_begin = split * P.tps;
   const int t_end = min(nt_max, t_begin + P.tps);
-  if (t_begin >= t_end) {   // empty partial: m = -inf, l = 0, o = 0
-    for (int i = tid; i < VH * (D + 2); i += 256) {
-      const int v = i / (D + 2), c = i % (D + 2);
-      part_of(v)[c] = (c == D) ? -INFINITY : 0.0f;
-    }
-    return;
-  }
+  if (t_begin >= t_end) return;   // no tiles here: the combine does not read this split
 
   // rotated query rows of the heads this wave prepares (clamped rows are read,
   // never used); with q_rot NULL the wave rotates the raw rows itself: the
@@ -431,8 +542,12 @@ __global__ void __launch_bounds__(256) decode_wide_kernel(DecodeParams P) {
   }
 }
 
+// decode (mode 0): the tile splits, then the window splits, in one grid;
+// prefill: the tile splits alone (the window kernel takes the raw rows)
 template <int D, int G>
 hipError_t launch_wide_dg(const DecodeParams& P, int batch, hipStream_t stream) {
+  if (P.mode == 0 && P.n_wsplit > 0 && P.wchunk != kWinChunk) return hipErrorInvalidValue;
+  const int nx = P.n_tsplit + (P.mode == 0 ? P.n_wsplit : 0);
   // prefill rows in pairs when G <= 4 and the chunk has an even number of rows
   if constexpr (G <= 4) {
     if (P.mode == 1 && batch % 2 == 0) {
@@ -444,7 +559,7 @@ hipError_t launch_wide_dg(const DecodeParams& P, int batch, hipStream_t stream) 
       return hipGetLastError();
     }
   }
-  const dim3 grid(P.n_tsplit, P.n_kv, batch);
+  const dim3 grid(nx, P.n_kv, batch);
   if (P.h16)
     hipLaunchKernelGGL((decode_wide_kernel<D, G, true, 1>), grid, dim3(256), 0, stream, P);
   else
@@ -465,7 +580,7 @@ hipError_t launch_wide_d(const DecodeParams& P, int batch, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_decode_wide_tiles(int d, const DecodeParams& P, int batch, hipStream_t stream) {
+hipError_t launch_decode_wide(int d, const DecodeParams& P, int batch, hipStream_t stream) {
   switch (d) {
     case 256: return launch_wide_d<256>(P, batch, stream);
     case 512: return launch_wide_d<512>(P, batch, stream);

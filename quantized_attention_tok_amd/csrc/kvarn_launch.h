@@ -26,7 +26,6 @@ struct DecodeParams {
   int n_q, n_kv, G;
   int tps, n_tsplit, n_wsplit;
   int wchunk;                      // window tokens per window split
-  int split0;                      // split index of blockIdx.x 0 (a launch over the window splits alone)
   // prefill view (mode 1): "sequence" b is query position pos0 + b of one
   // sequence; it sees T(p) tiles and raw rows [128 T(p), p] of k_win/v_win,
   // where raw row p lives at (p - raw_base) * win_tok_stride.
@@ -100,9 +99,11 @@ hipError_t launch_compress(int d, bool h16, int kb, int vb, int n_tiles, int n_k
 hipError_t launch_rotate(int d, int64_t n_rows, const float* q, float* q_rot, hipStream_t stream);
 hipError_t launch_decode(int d, const DecodeParams& P, int batch, hipStream_t stream);
 hipError_t launch_decode_fused(const DecodeParams& P, int batch, hipStream_t stream);
-// Tile splits alone (grid n_tsplit x n_kv x batch) for head_dim 256 / 512 over
-// K4V2 records, on the matrix cores; P.q_rot must hold the rotated queries.
-hipError_t launch_decode_wide_tiles(int d, const DecodeParams& P, int batch, hipStream_t stream);
+// Head_dim 256 / 512 over K4V2 records: the tile splits on the matrix cores,
+// and in decode (P.mode 0) the P.n_wsplit window splits of kWinChunk tokens
+// after them in the same grid ((n_tsplit + n_wsplit) x n_kv x batch); in
+// prefill the tile splits alone.  With P.q_rot NULL the kernel rotates q.
+hipError_t launch_decode_wide(int d, const DecodeParams& P, int batch, hipStream_t stream);
 hipError_t launch_prefill_mfma(const PrefillParams& P, hipStream_t stream);
 // The raw-window part of chunked prefill (P.mode 1) at head_dim 256 / 512 on
 // the fp32 matrix cores: one raw-domain partial per chunk row and query head,
