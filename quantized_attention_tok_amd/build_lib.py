@@ -27,6 +27,10 @@ COMMON = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # no packed fp32 instructions anywhere in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-op results in ordinary VGPRs: without it the compiler puts some
+    # accumulators in AGPRs and copies every result out with one more vector
+    # instruction (about 10% of the wide-head decode's per-tile instructions)
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     f"-I{os.path.join(ROOT, 'include')}",
 ]
 # The compressor must round every fp32 operation on its own (byte parity with
