@@ -371,16 +371,21 @@ __global__ void __launch_bounds__(kDecThreads) decode_partial_kernel(DecodeParam
 
 // ---------------------------------------------------------------------------
 // combine kernel: one workgroup of NWV waves per (query head, sequence); lane
-// l owns channels l + 64 k.  Wave w folds splits [16 w + 16 NWV i, +16) with an
-// online log-sum-exp (split j's (m, l) in lane j, its weight read from lane
-// j; the tile partials (rotated domain) and the window partials (raw domain)
-// summed apart); the wave states merge in LDS, wave 0 applies the
-// inverse WHT to the tile sum, adds the window sum and divides by L.
+// l owns channels l + 64 k.  Only the splits that hold tiles or window tokens
+// of the row are read (the split kernels write nothing for the others):
+// virtual split v < nvt is tile split v, the rest window split v - nvt.
+// Every wave first takes the largest running max M and the weighted sum L
+// over all of them; wave w then folds the splits v = w, w + NWV, ... with
+// weights exp(m_v - M), U splits at a time with all their loads in flight,
+// the tile partials (rotated domain) and the window partials (raw domain)
+// apart.  The wave sums add up in LDS (one thread per channel and part);
+// wave 0 applies the inverse WHT to the tile sum, adds the window sum and
+// divides by L.
 // ---------------------------------------------------------------------------
 template <int D, int NWV>
 __global__ void __launch_bounds__(64 * NWV) decode_combine_kernel(DecodeParams P) {
   constexpr int K = D / 64;
-  constexpr int PW = 16;
+  constexpr int U = 4;
   const int hq = blockIdx.x;
   const int b = blockIdx.y;
   const int tid = threadIdx.x;
@@ -388,83 +393,67 @@ __global__ void __launch_bounds__(64 * NWV) decode_combine_kernel(DecodeParams P
   const int nts = P.n_tsplit;
   const int n_split = P.n_tsplit + P.n_wsplit;
   const float* part = P.part + ((int64_t)b * P.n_q + hq) * n_split * (D + 4);
-  __shared__ float s_st[NWV][2];
-  __shared__ float s_o[NWV][2][D];
-  // only the splits that hold tiles or window tokens of this row are read
-  // (the split kernels write nothing for the others): virtual split v < nvt
-  // is tile split v, the rest window split v - nvt
+  __shared__ float s_o[NWV][2 * D];
   const SeqView sv = seq_view(P, b);
   const int nvt = min(nts, (sv.nt + P.tps - 1) / P.tps);
   const int nvw = min(P.n_wsplit, (sv.nw + P.wchunk - 1) / P.wchunk);
-  const int nv = nvt + nvw;
+  const int nv = nvt + nvw;   // >= 1: every row sees a tile or a token
   auto split_of = [&](int v) { return v < nvt ? v : nts + (v - nvt); };
 
-  float M = -INFINITY, L = 0.0f;
+  // M, then L, over every split (the same in every wave)
+  float M = -INFINITY;
+  for (int j = lane; j < nv; j += 64) M = fmaxf(M, part[(int64_t)split_of(j) * (D + 4) + D]);
+  M = wave_max(M);
+  float L = 0.0f;
+  for (int j = lane; j < nv; j += 64) {
+    const float* ps = part + (int64_t)split_of(j) * (D + 4);
+    L += __expf(ps[D] - M) * ps[D + 1];
+  }
+  const float Lall = wave_sum(L);
+
   float orot[K], oraw[K];
 #pragma unroll
   for (int k = 0; k < K; ++k) { orot[k] = 0.0f; oraw[k] = 0.0f; }
-  for (int base = PW * w; base < nv; base += NWV * PW) {
-    float m = -INFINITY, l = 0.0f;
-    if (lane < PW && base + lane < nv) {
-      const int64_t s = split_of(base + lane);
-      m = part[s * (D + 4) + D];
-      l = part[s * (D + 4) + D + 1];
+  for (int v0 = w; v0 < nv; v0 += U * NWV) {   // wave-uniform
+    float o[U][K], wt[U], wr[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int v = v0 + u * NWV;
+      const bool ok = v < nv;   // past the end: split v0 again, weight 0
+      const float* ps = part + (int64_t)split_of(ok ? v : v0) * (D + 4);
+#pragma unroll
+      for (int k = 0; k < K; ++k) o[u][k] = ps[lane + 64 * k];
+      const float wgt = ok ? __expf(ps[D] - M) : 0.0f;
+      wt[u] = v < nvt ? wgt : 0.0f;
+      wr[u] = v < nvt ? 0.0f : wgt;
     }
-    const float mc = wave_max(m);
-    if (mc > M) {
-      const float r = __expf(M - mc);   // 0 while M = -inf
-      L *= r;
 #pragma unroll
-      for (int k = 0; k < K; ++k) { orot[k] *= r; oraw[k] *= r; }
-      M = mc;
-    }
-    const float wgt = (m == -INFINITY) ? 0.0f : __expf(m - M);
-    L += wave_sum(wgt * l);
+    for (int u = 0; u < U; ++u)
 #pragma unroll
-    for (int j = 0; j < PW; ++j) {
-      const int v = base + j;
-      if (v < nv) {   // uniform
-        const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), j));
-        const float* ps = part + (int64_t)split_of(v) * (D + 4);
-        if (v < nvt) {
-#pragma unroll
-          for (int k = 0; k < K; ++k) orot[k] = fmaf(wj, ps[lane + 64 * k], orot[k]);
-        } else {
-#pragma unroll
-          for (int k = 0; k < K; ++k) oraw[k] = fmaf(wj, ps[lane + 64 * k], oraw[k]);
-        }
+      for (int k = 0; k < K; ++k) {
+        orot[k] = fmaf(wt[u], o[u][k], orot[k]);
+        oraw[k] = fmaf(wr[u], o[u][k], oraw[k]);
       }
-    }
   }
-  float Lall = L;
   if constexpr (NWV > 1) {
-    if (lane == 0) { s_st[w][0] = M; s_st[w][1] = L; }
-    __syncthreads();
-    float Mall = s_st[0][0];
-#pragma unroll
-    for (int i = 1; i < NWV; ++i) Mall = fmaxf(Mall, s_st[i][0]);
-    const float sc = (M == -INFINITY) ? 0.0f : __expf(M - Mall);
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-      s_o[w][0][lane + 64 * k] = orot[k] * sc;
-      s_o[w][1][lane + 64 * k] = oraw[k] * sc;
+      s_o[w][lane + 64 * k] = orot[k];
+      s_o[w][D + lane + 64 * k] = oraw[k];
+    }
+    __syncthreads();
+    for (int i = tid; i < 2 * D; i += 64 * NWV) {   // each element read and written by one thread
+      float a = 0.0f;
+#pragma unroll
+      for (int x = 0; x < NWV; ++x) a += s_o[x][i];
+      s_o[0][i] = a;
     }
     __syncthreads();
     if (w != 0) return;
-    Lall = 0.0f;
-#pragma unroll
-    for (int i = 0; i < NWV; ++i) {
-      const float mi = s_st[i][0];
-      Lall += (mi == -INFINITY) ? 0.0f : __expf(mi - Mall) * s_st[i][1];
-    }
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-      const int c = lane + 64 * k;
-      float a = 0.0f, r = 0.0f;
-#pragma unroll
-      for (int i = 0; i < NWV; ++i) { a += s_o[i][0][c]; r += s_o[i][1][c]; }
-      orot[k] = a;
-      oraw[k] = r;
+      orot[k] = s_o[0][lane + 64 * k];
+      oraw[k] = s_o[0][D + lane + 64 * k];
     }
   }
   // inverse WHT (the WHT itself) of the merged rotated-domain part
@@ -528,11 +517,10 @@ hipError_t launch_decode_dg(const DecodeParams& P, int batch, hipStream_t stream
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // sixteen waves past four 16-split passes (every pass in flight at once),
-  // four waves past one pass, else one
-  if (P.n_tsplit + P.n_wsplit > 64)
+  // sixteen waves past 16 splits, four past 4, else one
+  if (P.n_tsplit + P.n_wsplit > 16)
     hipLaunchKernelGGL((decode_combine_kernel<D, 16>), dim3(P.n_q, batch), dim3(1024), 0, stream, P);
-  else if (P.n_tsplit + P.n_wsplit > 16)
+  else if (P.n_tsplit + P.n_wsplit > 4)
     hipLaunchKernelGGL((decode_combine_kernel<D, 4>), dim3(P.n_q, batch), dim3(256), 0, stream, P);
   else
     hipLaunchKernelGGL((decode_combine_kernel<D, 1>), dim3(P.n_q, batch), dim3(64), 0, stream, P);
