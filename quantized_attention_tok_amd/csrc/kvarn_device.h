@@ -86,6 +86,56 @@ __device__ __forceinline__ float4 sc_ld4(const uint8_t* p, int i) {
     return *reinterpret_cast<const float4*>(p + 4 * i);
   }
 }
+// Raw buffer loads from one record.  The resource holds the record's base
+// address and size (a load past the size returns zeros); a load's offset is
+// a lane-dependent byte offset in a VGPR plus a uniform byte offset, so a
+// group of loads that differ by constants shares one address register.
+typedef __amdgpu_buffer_rsrc_t brsrc;
+__device__ __forceinline__ brsrc make_rsrc(const uint8_t* p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p), (short)0, bytes, 0x00020000);
+}
+// scale element i_lane + i_const of the section at byte `sec` (fp32 or f16 storage)
+template <bool H>
+__device__ __forceinline__ float sc_bl(brsrc r, int sec, int i_lane, int i_const) {
+  if constexpr (H) {
+    const auto x = __builtin_amdgcn_raw_buffer_load_b16(r, 2 * i_lane, sec + 2 * i_const, 0);
+    return (float)__builtin_bit_cast(_Float16, x);
+  } else {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, 4 * i_lane, sec + 4 * i_const, 0));
+  }
+}
+// elements i, i + 1 (i even)
+template <bool H>
+__device__ __forceinline__ float2 sc_bl2(brsrc r, int sec, int i_lane, int i_const) {
+  if constexpr (H) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    const h2 x = __builtin_bit_cast(h2, __builtin_amdgcn_raw_buffer_load_b32(r, 2 * i_lane, sec + 2 * i_const, 0));
+    return make_float2((float)x[0], (float)x[1]);
+  } else {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    const f2 x = __builtin_bit_cast(f2, __builtin_amdgcn_raw_buffer_load_b64(r, 4 * i_lane, sec + 4 * i_const, 0));
+    return make_float2(x[0], x[1]);
+  }
+}
+// elements i .. i + 3 (i a multiple of 4)
+template <bool H>
+__device__ __forceinline__ float4 sc_bl4(brsrc r, int sec, int i_lane, int i_const) {
+  if constexpr (H) {
+    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+    const h4 x = __builtin_bit_cast(h4, __builtin_amdgcn_raw_buffer_load_b64(r, 2 * i_lane, sec + 2 * i_const, 0));
+    return make_float4((float)x[0], (float)x[1], (float)x[2], (float)x[3]);
+  } else {
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    const f4 x = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, 4 * i_lane, sec + 4 * i_const, 0));
+    return make_float4(x[0], x[1], x[2], x[3]);
+  }
+}
+// 16 code bytes at byte voff + soff
+typedef uint32_t u32x4b __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x4b code_bl(brsrc r, int voff, int soff) {
+  return __builtin_bit_cast(u32x4b, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
 // store element i.  f16: the fp32 value v is rounded to nearest-even half.
 // The empty asm pins v as an fp32 register value: without it the compiler
 // folds a producing multiply into v_fma_mixlo_f16, which rounds the exact
