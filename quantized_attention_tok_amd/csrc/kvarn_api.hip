@@ -33,6 +33,11 @@ bool st16(int64_t floats) { return (floats % 4) == 0; }
 // Work target for the vector-unit split plan: one workgroup per tile range,
 // enough to cover the 256 CUs several times.
 constexpr int64_t kTargetGroups = 2048;
+// Matrix-core tile splits of K4V2 decode at head_dim 256 / 512: the split
+// kernels keep the next tile's loads in flight, so longer splits pay more
+// at 512 (two workgroups per CU); measured fastest on the 16-sequence batch
+// against targets of 1024-8192 (256) and 1024-4096 (512).
+int64_t wide_target(int d) { return d >= 512 ? 512 : 4096; }
 
 struct DecodePlan {
   int tps, n_tsplit, n_wsplit, wchunk;
@@ -146,7 +151,9 @@ int validate_decode(const kvarn_decode_args* a, DecodePlan* plan) {
     *plan = w > 1 ? plan_verify(a->batch, a->n_kv_heads, G, a->max_tiles, a->max_win)
           : fused_decode(a->head_dim)
                 ? plan_fused(a->batch, a->n_kv_heads, a->max_tiles, a->max_win)
-                : plan_decode(a->batch, a->n_kv_heads, a->max_tiles, a->max_win, kTargetGroups,
+                : plan_decode(a->batch, a->n_kv_heads, a->max_tiles, a->max_win,
+                              k4v2(a->head_dim) && dim_of(a->head_dim) >= 256 ? wide_target(dim_of(a->head_dim))
+                                                                              : kTargetGroups,
                               kvarn::kWinChunk);
   }
   return KVARN_OK;
