@@ -596,7 +596,8 @@ __global__ void __launch_bounds__(256) decode_wide_kernel(DecodeParams P) {
   }
 }
 
-// Head_dim 512 decode (RP = 1): the same contractions with the value
+// Head_dim 512, one query row per workgroup (decode, and prefill rows that
+// are not paired): the same contractions with the value
 // aggregate split by channels.  Wave w scores the 32-token quarter w of every
 // tile (as decode_wide_kernel) but aggregates value group w (channels
 // 128 w .. 128 w + 127) over all 128 tokens, so a lane keeps 16 output sums
@@ -644,12 +645,12 @@ __global__ void __launch_bounds__(256) decode_wide_cs_kernel(DecodeParams P) {
   const int split = blockIdx.x;
   const int kvh = blockIdx.y;
   const int b = blockIdx.z;
-  const SeqView sv = seq_view_decode(P, b);
+  const SeqView sv = seq_view(P, b);   // decode: sequence b; prefill: chunk row b
   const int n_split = P.n_tsplit + P.n_wsplit;
 
   __shared__ __attribute__((aligned(16))) uint8_t lds[lds_bytes];
 
-  if (split >= P.n_tsplit) {   // a raw-window split
+  if (split >= P.n_tsplit) {   // a raw-window split (decode; a prefill grid holds tile splits alone)
     const int ws = split - P.n_tsplit;
     if (ws * kWinChunk < sv.nw) wide_window_split<D, G>(P, lds, sv, b, kvh, ws, split, n_split);
     return;
@@ -976,14 +977,12 @@ hipError_t launch_wide_dg(const DecodeParams& P, int batch, hipStream_t stream) 
     }
   }
   const dim3 grid(nx, P.n_kv, batch);
-  if constexpr (D == 512) {   // decode: the channel-split kernel
-    if (P.mode == 0) {
-      if (P.h16)
-        hipLaunchKernelGGL((decode_wide_cs_kernel<G, true>), grid, dim3(256), 0, stream, P);
-      else
-        hipLaunchKernelGGL((decode_wide_cs_kernel<G, false>), grid, dim3(256), 0, stream, P);
-      return hipGetLastError();
-    }
+  if constexpr (D == 512) {   // one row per workgroup: the channel-split kernel
+    if (P.h16)
+      hipLaunchKernelGGL((decode_wide_cs_kernel<G, true>), grid, dim3(256), 0, stream, P);
+    else
+      hipLaunchKernelGGL((decode_wide_cs_kernel<G, false>), grid, dim3(256), 0, stream, P);
+    return hipGetLastError();
   }
   if (P.h16)
     hipLaunchKernelGGL((decode_wide_kernel<D, G, true, 1>), grid, dim3(256), 0, stream, P);
