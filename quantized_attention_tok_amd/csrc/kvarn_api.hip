@@ -61,13 +61,14 @@ DecodePlan plan_decode(int batch, int n_kv, int max_tiles, int max_win, int64_t 
 bool fused_decode(int32_t hd) { return dim_of(hd) == 128 && k4v2(hd); }
 
 // Matrix-core split plan: TPW tiles per workgroup (4 waves per tile): 2 once
-// the batch has 128 tile-heads (measured fastest at the 8B shape for
-// contexts 4096, 15488 and 32768, against 1 and 4), else 1.  The window
+// the batch has 256 tile-heads (measured fastest at the 8B shape for
+// contexts 4096, 15488 and 32768, against 1 and 4, and with 1 below 256
+// tile-heads on the 0.6B-shaped layer), else 1.  The window
 // tokens are spread over the tile splits (at most 16 per split; more splits
 // when the window needs them), so that no split carries many of them.
 DecodePlan plan_fused(int batch, int n_kv, int max_tiles, int max_win) {
   const int64_t units = (int64_t)batch * n_kv * (max_tiles > 0 ? max_tiles : 0);
-  const int tpw = units >= 128 ? 2 : 1;
+  const int tpw = units >= 256 ? 2 : 1;
   DecodePlan p;
   p.tps = tpw;
   const int nt = max_tiles > 0 ? (max_tiles + tpw - 1) / tpw : 0;
