@@ -5,14 +5,16 @@
 // Query position p of a chunk attends its compressed tiles [0, T(p)) and its
 // raw tokens [128 T(p), p] with one softmax (PR #434 commit list: chunked
 // prefill, a single streaming softmax over compressed tiles + FP32 window).
-// The tile part runs as split partials on decode_wide_kernel; this kernel
-// computes the raw part of 16 consecutive positions of one query head at a
-// time, reading each raw key and value row once for the 16 rows (the
-// per-row vector kernels read it once per row), and writes one raw-domain
+// The tile part runs as split partials on the wide tile kernels; this kernel
+// computes the raw part of 16 consecutive positions of one or two query
+// heads at a time, reading each raw key and value row once for the 16 rows
+// (the per-row vector kernels read it once per row), and writes one raw-domain
 // partial (o unnormalised, running maximum in natural-log units, sum) per
 // row and head, in the slot of the decode combine's window split.
 //
-// Workgroup = (16-row block, query head), 4 waves.  Per 16-token step the
+// Workgroup = (16-row block, HG query heads of one KV head), 4 waves (HG = 2
+// at head_dim 256, so each staged row serves two heads; 1 at 512, where the
+// registers hold one head's query and output).  Per 16-token step the
 // waves stage the tokens' key and value rows in LDS (rows padded by 4 floats,
 // so the per-lane reads spread over the banks), then
 //   scores  S[t][r] = sum_c k[t][c] q[r][c]: wave w contracts its quarter of
@@ -53,7 +55,7 @@ __device__ __forceinline__ float rows4_sum(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-template <int D>
+template <int D, int HG>
 __global__ void __launch_bounds__(256) window_mfma_kernel(DecodeParams P, int chunk) {
   constexpr int CW = D / 4;            // channels per wave
   constexpr int KQ = D / 16;           // contraction steps per wave (one channel per lane group each)
@@ -64,8 +66,8 @@ __global__ void __launch_bounds__(256) window_mfma_kernel(DecodeParams P, int ch
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, n = lane & 15;
-  const int rb = blockIdx.x, h = blockIdx.y;
-  const int kvh = h / P.G;
+  const int rb = blockIdx.x, h0 = blockIdx.y * HG;   // heads h0 .. h0 + HG - 1
+  const int kvh = h0 / P.G;
   const int r0 = 16 * rb;
   const int r = r0 + n;                                   // this lane's query row (column n)
   const bool row_ok = r < chunk;
@@ -79,17 +81,18 @@ __global__ void __launch_bounds__(256) window_mfma_kernel(DecodeParams P, int ch
 
   __shared__ __attribute__((aligned(16))) float s_k[16 * RS];
   __shared__ __attribute__((aligned(16))) float s_v[16 * RS];
-  __shared__ __attribute__((aligned(16))) floatx4 s_sp[4][64];
+  __shared__ __attribute__((aligned(16))) floatx4 s_sp[HG][4][64];
 
-  // query row r, channels w CW + g KQ .. + KQ (B operand of the scores)
-  float qv[KQ];
-  {
-    const float* qs = P.q + ((int64_t)(row_ok ? r : 0) * P.n_q + h) * D + w * CW + g * KQ;
+  // query row r of each head, channels w CW + g KQ .. + KQ (B operand of the scores)
+  float qv[HG][KQ];
+#pragma unroll
+  for (int hh = 0; hh < HG; ++hh) {
+    const float* qs = P.q + ((int64_t)(row_ok ? r : 0) * P.n_q + h0 + hh) * D + w * CW + g * KQ;
 #pragma unroll
     for (int j = 0; j < KQ / 4; ++j) {
       float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
       if (row_ok) x = reinterpret_cast<const float4*>(qs)[j];
-      qv[4 * j] = x.x; qv[4 * j + 1] = x.y; qv[4 * j + 2] = x.z; qv[4 * j + 3] = x.w;
+      qv[hh][4 * j] = x.x; qv[hh][4 * j + 1] = x.y; qv[hh][4 * j + 2] = x.z; qv[hh][4 * j + 3] = x.w;
     }
   }
   const float* kbase = P.k_win + (int64_t)kvh * P.win_head_stride;
@@ -114,10 +117,15 @@ __global__ void __launch_bounds__(256) window_mfma_kernel(DecodeParams P, int ch
     }
   };
 
-  float m_run = -INFINITY, l_run = 0.0f;   // softmax state of row r (log2 units)
-  floatx4 O[NB];                            // channels w CW + 16 b + 4 g + i of row r
+  float m_run[HG], l_run[HG];   // softmax state of row r per head (log2 units)
+  floatx4 O[HG][NB];            // channels w CW + 16 b + 4 g + i of row r
 #pragma unroll
-  for (int b = 0; b < NB; ++b) O[b] = (floatx4){0.f, 0.f, 0.f, 0.f};
+  for (int hh = 0; hh < HG; ++hh) {
+    m_run[hh] = -INFINITY;
+    l_run[hh] = 0.0f;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) O[hh][b] = (floatx4){0.f, 0.f, 0.f, 0.f};
+  }
 
   fetch(t_lo);
   for (int64_t tb = t_lo; tb < t_hi; tb += 16) {
@@ -132,76 +140,92 @@ __global__ void __launch_bounds__(256) window_mfma_kernel(DecodeParams P, int ch
     if (tb + 16 < t_hi) fetch(tb + 16);   // the next step's rows, while this one is computed
     __syncthreads();
     // scores, this wave's channel quarter: A = key rows (row n = token tb + n), B = query rows
-    floatx4 sacc = {0.f, 0.f, 0.f, 0.f};
+    floatx4 sacc[HG];
+#pragma unroll
+    for (int hh = 0; hh < HG; ++hh) sacc[hh] = (floatx4){0.f, 0.f, 0.f, 0.f};
     {
       const float* kr = s_k + n * RS + w * CW + g * KQ;
 #pragma unroll
       for (int j = 0; j < KQ / 4; ++j) {
         const float4 a = reinterpret_cast<const float4*>(kr)[j];
-        sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, qv[4 * j], sacc, 0, 0, 0);
-        sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, qv[4 * j + 1], sacc, 0, 0, 0);
-        sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, qv[4 * j + 2], sacc, 0, 0, 0);
-        sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, qv[4 * j + 3], sacc, 0, 0, 0);
+#pragma unroll
+        for (int hh = 0; hh < HG; ++hh) {
+          sacc[hh] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, qv[hh][4 * j], sacc[hh], 0, 0, 0);
+          sacc[hh] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, qv[hh][4 * j + 1], sacc[hh], 0, 0, 0);
+          sacc[hh] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, qv[hh][4 * j + 2], sacc[hh], 0, 0, 0);
+          sacc[hh] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, qv[hh][4 * j + 3], sacc[hh], 0, 0, 0);
+        }
       }
     }
-    s_sp[w][lane] = sacc;
+#pragma unroll
+    for (int hh = 0; hh < HG; ++hh) s_sp[hh][w][lane] = sacc[hh];
     __syncthreads();
-    floatx4 s4 = s_sp[0][lane];
 #pragma unroll
-    for (int ww = 1; ww < 4; ++ww) s4 += s_sp[ww][lane];
-    // lane (g, n): tokens tb + 4 g + i of row r
-    float sv[4], tmax = -INFINITY;
+    for (int hh = 0; hh < HG; ++hh) {
+      floatx4 s4 = s_sp[hh][0][lane];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t t = tb + 4 * g + i;
-      const bool vis = row_ok && t >= row_lo && t <= prow && t < t_hi;
-      sv[i] = vis ? s4[i] * scale_log2 : -INFINITY;
-      tmax = fmaxf(tmax, sv[i]);
-    }
-    tmax = rows4_max(tmax);
-    const float m_new = fmaxf(m_run, tmax);
-    const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);   // 0 from -inf
-    float pv[4], psum = 0.0f;
+      for (int ww = 1; ww < 4; ++ww) s4 += s_sp[hh][ww][lane];
+      // lane (g, n): tokens tb + 4 g + i of row r
+      float sv[4], tmax = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      pv[i] = __builtin_amdgcn_exp2f(sv[i] - m_use);
-      psum += pv[i];
-    }
-    l_run = l_run * alpha + rows4_sum(psum);
-    m_run = m_new;
+      for (int i = 0; i < 4; ++i) {
+        const int64_t t = tb + 4 * g + i;
+        const bool vis = row_ok && t >= row_lo && t <= prow && t < t_hi;
+        sv[i] = vis ? s4[i] * scale_log2 : -INFINITY;
+        tmax = fmaxf(tmax, sv[i]);
+      }
+      tmax = rows4_max(tmax);
+      const float m_new = fmaxf(m_run[hh], tmax);
+      const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run[hh] - m_use);   // 0 from -inf
+      float pv[4], psum = 0.0f;
 #pragma unroll
-    for (int b = 0; b < NB; ++b) O[b] *= alpha;
-    // values: step i contracts tokens 4 g + i (K slot g); A row n = channel w CW + 16 b + n
+      for (int i = 0; i < 4; ++i) {
+        pv[i] = __builtin_amdgcn_exp2f(sv[i] - m_use);
+        psum += pv[i];
+      }
+      l_run[hh] = l_run[hh] * alpha + rows4_sum(psum);
+      m_run[hh] = m_new;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float* vr = s_v + (4 * g + i) * RS + w * CW + n;
+      for (int b = 0; b < NB; ++b) O[hh][b] *= alpha;
+      // values: step i contracts tokens 4 g + i (K slot g); A row n = channel w CW + 16 b + n
 #pragma unroll
-      for (int b = 0; b < NB; ++b) O[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(vr[16 * b], pv[i], O[b], 0, 0, 0);
+      for (int i = 0; i < 4; ++i) {
+        const float* vr = s_v + (4 * g + i) * RS + w * CW + n;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) O[hh][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(vr[16 * b], pv[i], O[hh][b], 0, 0, 0);
+      }
     }
   }
 
   if (!row_ok) return;
   const int nsp = P.n_tsplit + P.n_wsplit;
-  float* o = P.part + (((int64_t)r * P.n_q + h) * nsp + P.n_tsplit) * (D + 4);
 #pragma unroll
-  for (int b = 0; b < NB; ++b)
-    *reinterpret_cast<float4*>(o + w * CW + 16 * b + 4 * g) = make_float4(O[b][0], O[b][1], O[b][2], O[b][3]);
-  if (w == 0 && g == 0) {   // natural-log units, as the decode combine reads them
-    o[D] = m_run * 0.69314718055994531f;
-    o[D + 1] = l_run;
+  for (int hh = 0; hh < HG; ++hh) {
+    float* o = P.part + (((int64_t)r * P.n_q + h0 + hh) * nsp + P.n_tsplit) * (D + 4);
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+      *reinterpret_cast<float4*>(o + w * CW + 16 * b + 4 * g) =
+          make_float4(O[hh][b][0], O[hh][b][1], O[hh][b][2], O[hh][b][3]);
+    if (w == 0 && g == 0) {   // natural-log units, as the decode combine reads them
+      o[D] = m_run[hh] * 0.69314718055994531f;
+      o[D + 1] = l_run[hh];
+    }
   }
 }
 
 }  // namespace
 
 hipError_t launch_window_mfma(int d, const DecodeParams& P, int chunk, hipStream_t stream) {
-  const dim3 grid((chunk + 15) / 16, P.n_q);
-  switch (d) {
-    case 256: hipLaunchKernelGGL(window_mfma_kernel<256>, grid, dim3(256), 0, stream, P, chunk); break;
-    case 512: hipLaunchKernelGGL(window_mfma_kernel<512>, grid, dim3(256), 0, stream, P, chunk); break;
-    default: return hipErrorInvalidValue;
-  }
+  const int blocks = (chunk + 15) / 16;
+  if (d == 256 && P.G % 2 == 0)   // two heads of a KV head per workgroup
+    hipLaunchKernelGGL((window_mfma_kernel<256, 2>), dim3(blocks, P.n_q / 2), dim3(256), 0, stream, P, chunk);
+  else if (d == 256)
+    hipLaunchKernelGGL((window_mfma_kernel<256, 1>), dim3(blocks, P.n_q), dim3(256), 0, stream, P, chunk);
+  else if (d == 512)
+    hipLaunchKernelGGL((window_mfma_kernel<512, 1>), dim3(blocks, P.n_q), dim3(256), 0, stream, P, chunk);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
