@@ -297,7 +297,7 @@ def qwen06b_case(torch, kvarn, synth, reps):
 # the 16-sequence wide-head batch, stepped: append, promote, decode
 # ---------------------------------------------------------------------------
 
-def wide_step_case(torch, kvarn, synth, name, n_steps, reps):
+def wide_step_case(torch, kvarn, synth, name, n_steps, reps, eager_calls=0):
     """16 sequences with contexts uniform in 1k-32k tokens in whole tiles and a
     window of 256 + r_b tokens (r_b uniform in [0, 128)).  One step appends one
     token's K and V rows to every sequence's window, compresses the oldest 128
@@ -375,6 +375,12 @@ def wide_step_case(torch, kvarn, synth, name, n_steps, reps):
                                scale, out=out, workspace=ws, max_tiles=max_tiles, max_win=max_win,
                                win_start=st)
 
+    if eager_calls > 0:   # plain decode calls of step 0's state, outside any graph (for counter passes)
+        for i in range(eager_calls):
+            step(i % L, 0, False)
+        torch.cuda.synchronize()
+        return {"workload": f"batch {B}, head_dim {d}: {eager_calls} decode calls outside a graph",
+                "head_dim": d, "eager_calls": eager_calls}
     g = capture(torch, lambda: [step(l, s) for s in range(n_steps) for l in range(L)])
     regions = time_regions(torch, g, reps)
     ms = float(np.median(regions)) / (n_steps * L)
@@ -641,6 +647,13 @@ def main():
     ap.add_argument("--no-extra-contexts", action="store_true")
     ap.add_argument("--no-steps", action="store_true", help="skip the stepped 0.6B and wide-head workloads")
     ap.add_argument("--no-floors", action="store_true")
+    ap.add_argument("--no-verify", action="store_true")
+    ap.add_argument("--no-compress", action="store_true")
+    ap.add_argument("--eager-wide", type=int, default=0,
+                    help="instead of the stepped wide-head graphs: this many plain decode calls of each "
+                         "wide batch (for profilers that count per dispatch)")
+    ap.add_argument("--step-reps", type=int, default=7,
+                    help="timed regions of the stepped workloads (each one graph of 64 or 128 steps)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibration-copy", action="store_true")
     args = ap.parse_args()
@@ -648,7 +661,7 @@ def main():
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(the KVarN path here runs on a single MI355X)", flush=True)
         sys.exit(2)
-    if args.steps < 1 or args.warmup < 0 or args.reps < 1:
+    if args.steps < 1 or args.warmup < 0 or args.reps < 1 or args.step_reps < 1:
         sys.exit("--steps >= 1, --warmup >= 0 and --reps >= 1 are required")
 
     from quantized_attention_tok_amd import synth
@@ -681,26 +694,33 @@ def main():
         dec65, _ = decode_case(torch, kvarn, synth, args.context, args.steps, args.warmup, 5, kbits=6, vbits=5)
         log(f"decode context {args.context}, K6V5: {dec65['us_per_step']:.2f} us per call")
 
-    verify = verify_case(torch, kvarn, synth, args.context, 8, R)
-    verify["vs_decode_call"] = verify["us_per_call"] / head["us_per_step"]
-    log(f"verify width 8 at context {args.context}: {verify['us_per_call']:.2f} us per call "
-        f"({verify['vs_decode_call']:.2f} decode calls)")
+    verify = None
+    if not args.no_verify:
+        verify = verify_case(torch, kvarn, synth, args.context, 8, R)
+        verify["vs_decode_call"] = verify["us_per_call"] / head["us_per_step"]
+        log(f"verify width 8 at context {args.context}: {verify['us_per_call']:.2f} us per call "
+            f"({verify['vs_decode_call']:.2f} decode calls)")
 
     q06, wide = None, []
-    if not args.no_steps:
-        q06 = qwen06b_case(torch, kvarn, synth, 7)
+    if not args.no_steps and not args.eager_wide:
+        q06 = qwen06b_case(torch, kvarn, synth, args.step_reps)
         log(f"0.6B layer, 64 steps with appends: {q06['us_per_layer_step']:.2f} us per step, "
             f"{q06['kv_tokens_per_s']:.3g} KV tokens/s")
+    if not args.no_steps:
         for name in ("wide_d256", "wide_d512"):
-            info = wide_step_case(torch, kvarn, synth, name, 128, 5)
+            info = wide_step_case(torch, kvarn, synth, name, 128, args.step_reps, args.eager_wide)
             wide.append(info)
+            if args.eager_wide:
+                continue
             log(f"wide batch head_dim {info['head_dim']}, 128 steps: {info['us_per_layer_step']:.1f} us per "
                 f"step ({info['decode_only']['us_per_layer_step']:.1f} decode only), "
                 f"{info['decode_only']['achieved_GBps']:.0f} GB/s decode")
 
-    compress = compress_case(torch, kvarn, synth, R)
-    log(f"compress {compress['tile_heads']} tile-heads: {compress['us_per_launch']:.1f} us, "
-        f"{compress['achieved_GBps']:.0f} GB/s")
+    compress = None
+    if not args.no_compress:
+        compress = compress_case(torch, kvarn, synth, R)
+        log(f"compress {compress['tile_heads']} tile-heads: {compress['us_per_launch']:.1f} us, "
+            f"{compress['achieved_GBps']:.0f} GB/s")
 
     prefill, prefill_wide = None, []
     if not args.no_prefill:
