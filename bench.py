@@ -440,12 +440,11 @@ def prefill_case(torch, kvarn, synth, SequenceCache, d, Hq, Hkv, n, chunk, reps,
     kp, vp, qp = (torch.from_numpy(x).to(dev) for x in (Kp, Vp, Qp))
     outp = torch.empty_like(qp)
     cache = SequenceCache(Hkv, d, W, capacity=n + 128, device=dev)
-    ws = None
-    if d != 128:   # the wide-head prefill keeps split partials in a workspace
-        big = max(kvarn.prefill_workspace_bytes(qp[p0:p0 + min(chunk, n - p0)], None, cache.records,
-                                                n // 128, cache.k, cache.v, 0, p0, W, 1.0)
-                  for p0 in range(0, n, chunk))
-        ws = torch.empty(max(big, 16), dtype=torch.uint8, device=dev)
+    # one workspace for every chunk's split partials
+    big = max(kvarn.prefill_workspace_bytes(qp[p0:p0 + min(chunk, n - p0)], None, cache.records,
+                                            n // 128, cache.k, cache.v, 0, p0, W, 1.0)
+              for p0 in range(0, n, chunk))
+    ws = torch.empty(max(big, 16), dtype=torch.uint8, device=dev)
 
     def run_prefill():
         cache.n_tokens = cache.n_tiles = 0

@@ -255,10 +255,13 @@ int kvarn_decode_attention_noalloc(const kvarn_decode_args* args, void* stream);
  * the prompt is chunked).  The caller compresses every tile the chunk makes
  * due (tiles < T(pos0+C-1)) before this call.
  *
- * head_dim 128 over K4V2 records runs on the matrix units; head_dim 256 and
- * 512 (issue #433 item 3: prefill at the wider heads) and records with other
- * code widths run every chunk row as a vector-unit split decode query with
- * that view and need a workspace for the partials.
+ * head_dim 128 over K4V2 records runs on the matrix units, in workgroups of
+ * query-row blocks that read each tile once for 128 row-heads.  head_dim 256
+ * and 512 over K4V2 records (issue #433 item 3: prefill at the wider heads)
+ * run every chunk row as a decode query with that view, the tile splits on
+ * the matrix units and the raw windows on the fp32 matrix units; records with
+ * other code widths run that view on the vector-unit split kernels.  Both need
+ * a workspace for the partials.
  */
 typedef struct kvarn_prefill_args {
   int32_t head_dim;        /* 128, 256 or 512, | KVARN_SCALES_F16 (f16 scales),
@@ -284,16 +287,21 @@ typedef struct kvarn_prefill_args {
   float* out;              /* device [C][n_q_heads][head_dim]                   */
 } kvarn_prefill_args;
 
-/* Workspace bytes kvarn_prefill_attention needs (0 on invalid arguments):
- * 0 at head_dim 128 (every partial result stays in registers and LDS; the
- * workspace may be NULL), the split partials at 256 and 512.  Device memory
- * owned by the caller, scratch after the call; calls sharing a workspace
- * must not overlap in time. */
+/* Workspace bytes kvarn_prefill_attention needs (0 on invalid arguments).
+ * head_dim 128 over K4V2 records: the partials of the S tile-and-raw splits
+ * that fill the CUs (S = 256 / workgroups of 128 row-heads, 1..4; 0 bytes when
+ * S = 1).  The workspace may also be NULL there: the call then runs one
+ * launch that keeps every partial result on chip, with half as many row-heads
+ * per unpacked tile (slower).  head_dim 256 / 512 and other code widths: the
+ * per-row split partials, required.  Device memory owned by the caller,
+ * scratch after the call (no initialisation needed); calls sharing a
+ * workspace must not overlap in time. */
 size_t kvarn_prefill_workspace_bytes(const kvarn_prefill_args* args);
 
 /* Errors: KVARN_E_INVALID (null pointers, chunk < 1, pos0 < 0, missing tiles
  * or raw rows), KVARN_E_UNSUPPORTED (head_dim, GQA ratio), KVARN_E_ALIGN,
- * KVARN_E_WORKSPACE (head_dim 256/512 only).  The raw rows
+ * KVARN_E_WORKSPACE (a workspace smaller than kvarn_prefill_workspace_bytes;
+ * NULL only at head_dim 128 over K4V2 records).  The raw rows
  * [raw_base, pos0 + C) must be readable. */
 int kvarn_prefill_attention(const kvarn_prefill_args* args, void* workspace,
                             size_t workspace_bytes, void* stream);

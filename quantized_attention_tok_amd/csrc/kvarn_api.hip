@@ -172,6 +172,21 @@ int64_t prefill_tiles_at(int64_t pos, int window) {
   return ahead > 0 ? ahead / KVARN_TILE_TOKENS : 0;
 }
 
+// Splits of the head_dim-128 matrix-core prefill: the workgroups of 128
+// row-heads (8 row groups of 16 positions of one query head) times S should
+// fill the 256 CUs once (one workgroup per CU), with at most 4 shares.
+int prefill_splits(const kvarn_prefill_args* a) {
+  const int G = a->n_q_heads / a->n_kv_heads;
+  const int64_t n_blk = (int64_t)((a->chunk + 15) / 16) * G;
+  const int64_t wgs = (n_blk + 7) / 8 * a->n_kv_heads;
+  const int64_t S = 256 / wgs;
+  return S < 1 ? 1 : (S > 4 ? 4 : (int)S);
+}
+size_t prefill_split_bytes(const kvarn_prefill_args* a) {
+  const int S = prefill_splits(a);
+  return S > 1 ? (size_t)a->chunk * a->n_q_heads * S * (128 + 4) * sizeof(float) : 0;   // o, m, l, pad
+}
+
 int validate_prefill(const kvarn_prefill_args* a, DecodePlan* plan) {
   if (!a) return KVARN_E_INVALID;
   if (!dim_ok(a->head_dim)) return KVARN_E_UNSUPPORTED;
@@ -354,14 +369,16 @@ int kvarn_decode_attention(const kvarn_decode_args* a, void* workspace, size_t w
   return e == hipSuccess ? KVARN_OK : KVARN_E_DEVICE;
 }
 
-// head_dim 128 over K4V2 records: the matrix-core prefill keeps its whole
-// state on chip.  head_dim 256 / 512 and other code widths: the vector-unit
-// split kernels run every chunk row as a decode query with the prefill view
-// (T(p) tiles, raw rows [128 T(p), p]) and need their partials in the workspace.
+// head_dim 128 over K4V2 records: the matrix-core prefill in S splits, whose
+// raw-domain partials the workspace holds (S = 1: none); without a workspace
+// the single-launch kernel, which keeps its whole state on chip.  head_dim
+// 256 / 512 and other code widths: the split kernels run every chunk row as a
+// decode query with the prefill view (T(p) tiles, raw rows [128 T(p), p]) and
+// need their partials in the workspace.
 size_t kvarn_prefill_workspace_bytes(const kvarn_prefill_args* a) {
   DecodePlan p;
   if (validate_prefill(a, &p) != KVARN_OK) return 0;
-  if (fused_decode(a->head_dim)) return 0;
+  if (fused_decode(a->head_dim)) return prefill_split_bytes(a);
   return decode_part_floats(a->chunk, a->n_q_heads, dim_of(a->head_dim), p) * sizeof(float);
 }
 
@@ -423,7 +440,17 @@ int kvarn_prefill_attention(const kvarn_prefill_args* a, void* workspace, size_t
   P.n_kv = a->n_kv_heads;
   P.G = a->n_q_heads / a->n_kv_heads;
   P.h16 = f16_of(a->head_dim);
-  hipError_t e = kvarn::launch_prefill_mfma(P, (hipStream_t)stream);
+  const int S = prefill_splits(a);
+  hipError_t e;
+  if (S == 1) {   // the workgroups fill the chip unsplit: no partials
+    e = kvarn::launch_prefill_split(P, nullptr, 1, (hipStream_t)stream);
+  } else if (workspace) {
+    if (ws_bytes < prefill_split_bytes(a)) return KVARN_E_WORKSPACE;
+    if (!al16(workspace)) return KVARN_E_ALIGN;
+    e = kvarn::launch_prefill_split(P, static_cast<float*>(workspace), S, (hipStream_t)stream);
+  } else {        // no workspace: the half layout, 64 row-heads per workgroup, one launch
+    e = kvarn::launch_prefill_mfma(P, (hipStream_t)stream);
+  }
   return e == hipSuccess ? KVARN_OK : KVARN_E_DEVICE;
 }
 

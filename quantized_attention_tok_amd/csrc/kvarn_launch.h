@@ -105,6 +105,10 @@ hipError_t launch_decode_fused(const DecodeParams& P, int batch, hipStream_t str
 // prefill the tile splits alone.  With P.q_rot NULL the kernel rotates q.
 hipError_t launch_decode_wide(int d, const DecodeParams& P, int batch, hipStream_t stream);
 hipError_t launch_prefill_mfma(const PrefillParams& P, hipStream_t stream);
+// The same over the FR layout in S tile-and-raw splits (1 <= S <= 4): with
+// S > 1, part holds chunk * n_q * S partials of 128 + 4 floats and a combine
+// launch writes the output; with S = 1 the output is written directly.
+hipError_t launch_prefill_split(const PrefillParams& P, float* part, int S, hipStream_t stream);
 // The raw-window part of chunked prefill (P.mode 1) at head_dim 256 / 512 on
 // the fp32 matrix cores: one raw-domain partial per chunk row and query head,
 // written as split P.n_tsplit of P.n_tsplit + P.n_wsplit (P.n_wsplit = 1).

@@ -9,18 +9,29 @@
 // compressed tiles + FP32 window and a deferred inverse WHT; issue #433 item 1:
 // the Q.K score block of the compressed tiles belongs on the matrix units).
 //
-// Work split: a workgroup owns four groups of 16 query rows of one KV head
-// (each group: 16 consecutive positions of one query head, one MFMA column
-// block) and runs 8 waves, two per row group.  Wave (r, h) takes tokens
-// 64 h .. 64 h + 63 of every compressed tile and the raw 16-token blocks of
-// parity h, with a streaming softmax of its own; the two partial results of a
-// row group are merged at the end.  Two waves per SIMD let the matrix work of
-// one run under the vector work of the other.
+// Work split: a row group is 16 consecutive positions of one query head (one
+// MFMA column block); a workgroup of 8 waves serves row groups of one KV head
+// in one of two layouts:
+//   - split layout (prefill_split_kernel, the chunked prefill with a
+//     workspace): eight row groups, one per wave, each wave over all 128
+//     tokens of every tile (its two 64-token halves one after the other, the
+//     tile's q~ operands and bias computed once) and over both raw 16-token
+//     blocks of every staging step.  The workgroup's tiles and raw tokens are
+//     cut into S equal shares (blockIdx.z), so that the 128-row-head
+//     workgroups fill the chip; each share's raw-domain partial goes to the
+//     workspace and a combine launch merges them;
+//   - half layout (prefill_mfma_kernel without a workspace, and multi-query
+//     verify): four row groups, wave (r, h) over tokens 64 h .. 64 h + 63 of
+//     every tile and the raw blocks of parity h; the two halves of a row group
+//     merge at the end.
+// Each wave keeps a streaming softmax of its own.  Two waves per SIMD (w and
+// w + 4) let the matrix work of one run under the vector work of the other.
 //
 // Per compressed tile the 8 waves first unpack the tile once, together, into
 // LDS operand tiles in the fp16 layout the MFMAs read (one 16-byte read per
-// operand) plus a few per-tile constants, then each wave computes, for its 16
-// rows r and its 64 tokens t,
+// operand) plus a few per-tile constants; the split layout thus serves 128
+// row-heads per unpack, the half layout 64.  Each wave computes, for its 16
+// rows r and each 64-token half t of its share,
 //   S^T[t][r] = sum_c zK[t][c] q~[c][r] + b[r]     (fp16 MFMA; q~ = q' kscale
 //               as hi + lo parts, b = sum_c q'_c kmin_c by a small MFMA too)
 //   O^T[c][r] += sum_t zV[t][c] w[r][t]            (fp16 MFMA; w = p vscale
@@ -306,18 +317,27 @@ struct Ctx {
   int64_t part_row, part_head;
 };
 
-template <bool H>
+// FR = false: four row groups of 16 rows, wave (r, h) takes the token half h
+// of every tile and the 16-token raw blocks of parity h, and the two halves
+// of a row group merge at the end.  FR = true: eight row groups, each wave
+// takes all 128 tokens of every tile (the halves one after the other, with
+// the tile's q~ operands and bias computed once) and both raw blocks of every
+// staging step; each tile's unpack then serves twice the rows.  In both,
+// waves 0-3 unpack the next tile at the start of an iteration and waves 4-7 at
+// its end.
+template <bool H, bool FR>
 __device__ __forceinline__ void prefill_body(const Ctx& P) {
+  constexpr int RG = FR ? 8 : 4;          // row groups (column blocks) per workgroup
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
-  const int rg = wv & 3, th = wv >> 2;   // row group, token half
+  const int rg = FR ? wv : (wv & 3), th = wv >> 2;   // row group; token half (FR: unpack slot)
   const int n = lane & 15, g = lane >> 4;
   const int kvh = blockIdx.y;
   const int G = P.G;
   const int n_blk = ((P.chunk + kRows - 1) / kRows) * G;   // (position group, head) column blocks
-  const int blk_first = blockIdx.x * 4;
-  const int blk_last = min(blk_first + 3, n_blk - 1);
+  const int blk_first = blockIdx.x * RG;
+  const int blk_last = min(blk_first + RG - 1, n_blk - 1);
   const int blk = blk_first + rg;
   const bool active = blk < n_blk;
   const int pg = (active ? blk : blk_last) / G;
@@ -420,10 +440,14 @@ __device__ __forceinline__ void prefill_body(const Ctx& P) {
         ql[k4][i] = pack_h2((_Float16)(a - (float)ha), (_Float16)(b - (float)hb));
       }
   }
-  // operand read offsets (16-byte units) of lane (g, n): K blocks 4 th + bb, V channel halves
-  int offk[4], offv[2];
+  // operand read offsets (16-byte units) of lane (g, n): K blocks 4 hh + bb of the
+  // token half(s) hh the wave takes, V channel halves
+  constexpr int NH = FR ? 2 : 1;   // token halves per wave
+  int offk[NH][4], offv[2];
 #pragma unroll
-  for (int bb = 0; bb < 4; ++bb) offk[bb] = 16 * g + (n ^ swk(4 * th + bb, n));
+  for (int hx = 0; hx < NH; ++hx)
+#pragma unroll
+    for (int bb = 0; bb < 4; ++bb) offk[hx][bb] = 16 * g + (n ^ swk(4 * (FR ? hx : th) + bb, n));
 #pragma unroll
   for (int h = 0; h < 2; ++h) offv[h] = 16 * g + (n ^ swv(4 * h, n));
 
@@ -435,9 +459,9 @@ __device__ __forceinline__ void prefill_body(const Ctx& P) {
     for (int kk = 0; kk < 4; ++kk) O[qb][kk] = (floatx4){0.f, 0.f, 0.f, 0.f};
 
   // ---- compressed tiles: compute tile j while unpacking tile j + 1 into the
-  // other buffer and loading tile j + 2.  The two waves on a SIMD (token
-  // halves 0 and 1 of a row group) unpack at opposite ends of the iteration,
-  // so the matrix work of one meets the vector work of the other. ----
+  // other buffer and loading tile j + 2.  The two waves on a SIMD (waves w and
+  // w + 4) unpack at opposite ends of the iteration, so the matrix work of one
+  // meets the vector work of the other. ----
   for (int j = ja; j < jend; ++j) {
     const int pb = (j - ja) & 1;   // buffer of tile j
     const uint8_t* cst = s_lds + kLdsC + pb * kConstBytes;
@@ -500,112 +524,117 @@ __device__ __forceinline__ void prefill_body(const Ctx& P) {
       const int bexp = em - 20 - ek;
       const float bsc = pow2i(bexp < -126 ? -126 : (bexp > 127 ? 127 : bexp));
       const floatx4 acc0 = {bacc[0] * bsc, bacc[1] * bsc, bacc[2] * bsc, bacc[3] * bsc};
-      // scores / beta (log2 domain): y = alpha_t acc, token 16 b + 4 g + i of row n
-      const float* alp = reinterpret_cast<const float*>(cst + kCAlpha);
-      float y[4][4];
-      float ymax = -INFINITY;
 #pragma unroll
-      for (int bb = 0; bb < 4; ++bb) {
-        const int b = 4 * th + bb;
-        floatx4 acc = acc0;
+      for (int hx = 0; hx < NH; ++hx) {   // the wave's token half(s), one after the other
+        const int hh = FR ? hx : th;
+        if (hx > 0) __builtin_amdgcn_s_setprio(1);
+        // scores / beta (log2 domain): y = alpha_t acc, token 16 b + 4 g + i of row n
+        const float* alp = reinterpret_cast<const float*>(cst + kCAlpha);
+        float y[4][4];
+        float ymax = -INFINITY;
 #pragma unroll
-        for (int k4 = 0; k4 < 4; ++k4) {
-          const uint4 a = kop[(k4 * 8 + b) * 64 + offk[bb]];
-          const half8 A = as_half8(a.x, a.y, a.z, a.w);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bh[k4], acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bl[k4], acc, 0, 0, 0);
-        }
-        const float4 al = *reinterpret_cast<const float4*>(alp + 16 * b + 4 * g);
-        y[bb][0] = acc[0] * al.x;
-        y[bb][1] = acc[1] * al.y;
-        y[bb][2] = acc[2] * al.z;
-        y[bb][3] = acc[3] * al.w;
-        ymax = fmaxf(fmaxf(ymax, y[bb][0]), y[bb][1]);
-        ymax = fmaxf(fmaxf(ymax, y[bb][2]), y[bb][3]);
-      }
-      __builtin_amdgcn_s_setprio(0);
-      // lazy running maximum: raised only when the tile exceeds it by > tau
-      const bool vis = j < T_row;
-      const float tmax = rows_max(ymax) * beta;
-      const bool raise = vis && !(tmax <= m_run + kTau);
-      const float m_new = raise ? tmax : m_run;
-      const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;   // 0 from -inf
-      m_run = m_new;
-      const float negm = vis ? -m_run : -INFINITY;
-      l_run *= alpha;
-      if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+        for (int bb = 0; bb < 4; ++bb) {
+          const int b = 4 * hh + bb;
+          floatx4 acc = acc0;
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-          for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) O[qb][kk][i] *= alpha;
-      }
-      // probabilities p (<= 2^tau), their sums, and w = p vsf as hi / lo B operands
-      const float* vsf = reinterpret_cast<const float*>(cst + kCVsf);
-      const float* vmn = reinterpret_cast<const float*>(cst + kCVmin);
-      float psum = 0.0f, upart = 0.0f;
-      uint32_t wh[4][2], wl[4][2];
-#pragma unroll
-      for (int bb = 0; bb < 4; ++bb) {
-        const int b = 4 * th + bb;
-        const float4 va = *reinterpret_cast<const float4*>(vsf + 16 * b + 4 * g);
-        const float4 ma = *reinterpret_cast<const float4*>(vmn + 16 * b + 4 * g);
-        const float vs4[4] = {va.x, va.y, va.z, va.w};
-        const float vm4[4] = {ma.x, ma.y, ma.z, ma.w};
-        float w4[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float pj = __builtin_amdgcn_exp2f(fmaf(beta, y[bb][i], negm));
-          psum += pj;
-          upart = fmaf(pj, vm4[i], upart);
-          w4[i] = pj * vs4[i];
-        }
-#pragma unroll
-        for (int pr = 0; pr < 2; ++pr) {
-          const fp16x2 h = __builtin_amdgcn_cvt_pkrtz(w4[2 * pr], w4[2 * pr + 1]);
-          const fp16x2 l = __builtin_amdgcn_cvt_pkrtz(w4[2 * pr] - (float)h.x, w4[2 * pr + 1] - (float)h.y);
-          wh[bb][pr] = __builtin_bit_cast(uint32_t, h);
-          wl[bb][pr] = __builtin_bit_cast(uint32_t, l);
-        }
-      }
-      l_run += rows_sum(psum);
-      const float u = rows_sum(upart);
-      // O'^T[c][n] += vcu_c z_c, z_c starting at u fv 2^-(24 - shift(c)) so that
-      // vcu_c z_c = vchan_c (sum_t p_t vscale_t zV_tc + sum_t p_t vmin_t)
-      const float ufv = u * pow2i(13 - (int)kTau - ev);
-      const float zi0 = ufv * pow2i(-20), zi1 = ufv * pow2i(-18);
-      half8 Wh[2], Wl[2];
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        Wh[tt] = as_half8(wh[2 * tt][0], wh[2 * tt][1], wh[2 * tt + 1][0], wh[2 * tt + 1][1]);
-        Wl[tt] = as_half8(wl[2 * tt][0], wl[2 * tt][1], wl[2 * tt + 1][0], wl[2 * tt + 1][1]);
-      }
-      const float* vcu = reinterpret_cast<const float*>(cst + kCVcu);
-      __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        float4 vc[4];   // channels 64 qb + 16 g + 4 i .. + 3
-#pragma unroll
-        for (int i = 0; i < 4; ++i) vc[i] = *reinterpret_cast<const float4*>(vcu + 64 * qb + 16 * g + 4 * i);
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const int q8 = 4 * qb + kk;
-          const float zi = (kk & 1) ? zi1 : zi0;
-          floatx4 z = {zi, zi, zi, zi};
-#pragma unroll
-          for (int tt = 0; tt < 2; ++tt) {
-            const uint4 av = vop[((2 * th + tt) * 8 + q8) * 64 + offv[qb]];
-            const half8 Av = as_half8(av.x, av.y, av.z, av.w);
-            z = __builtin_amdgcn_mfma_f32_16x16x32_f16(Av, Wh[tt], z, 0, 0, 0);
-            z = __builtin_amdgcn_mfma_f32_16x16x32_f16(Av, Wl[tt], z, 0, 0, 0);
+          for (int k4 = 0; k4 < 4; ++k4) {
+            const uint4 a = kop[(k4 * 8 + b) * 64 + offk[hx][bb]];
+            const half8 A = as_half8(a.x, a.y, a.z, a.w);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bh[k4], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bl[k4], acc, 0, 0, 0);
           }
-          const float vk[4] = {kk == 0 ? vc[0].x : kk == 1 ? vc[0].y : kk == 2 ? vc[0].z : vc[0].w,
-                               kk == 0 ? vc[1].x : kk == 1 ? vc[1].y : kk == 2 ? vc[1].z : vc[1].w,
-                               kk == 0 ? vc[2].x : kk == 1 ? vc[2].y : kk == 2 ? vc[2].z : vc[2].w,
-                               kk == 0 ? vc[3].x : kk == 1 ? vc[3].y : kk == 2 ? vc[3].z : vc[3].w};
+          const float4 al = *reinterpret_cast<const float4*>(alp + 16 * b + 4 * g);
+          y[bb][0] = acc[0] * al.x;
+          y[bb][1] = acc[1] * al.y;
+          y[bb][2] = acc[2] * al.z;
+          y[bb][3] = acc[3] * al.w;
+          ymax = fmaxf(fmaxf(ymax, y[bb][0]), y[bb][1]);
+          ymax = fmaxf(fmaxf(ymax, y[bb][2]), y[bb][3]);
+        }
+        __builtin_amdgcn_s_setprio(0);
+        // lazy running maximum: raised only when the tile exceeds it by > tau
+        const bool vis = j < T_row;
+        const float tmax = rows_max(ymax) * beta;
+        const bool raise = vis && !(tmax <= m_run + kTau);
+        const float m_new = raise ? tmax : m_run;
+        const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;   // 0 from -inf
+        m_run = m_new;
+        const float negm = vis ? -m_run : -INFINITY;
+        l_run *= alpha;
+        if (__builtin_amdgcn_ballot_w64(raise) != 0) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) O[qb][kk][i] = fmaf(vk[i], z[i], O[qb][kk][i]);
+          for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) O[qb][kk][i] *= alpha;
+        }
+        // probabilities p (<= 2^tau), their sums, and w = p vsf as hi / lo B operands
+        const float* vsf = reinterpret_cast<const float*>(cst + kCVsf);
+        const float* vmn = reinterpret_cast<const float*>(cst + kCVmin);
+        float psum = 0.0f, upart = 0.0f;
+        uint32_t wh[4][2], wl[4][2];
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+          const int b = 4 * hh + bb;
+          const float4 va = *reinterpret_cast<const float4*>(vsf + 16 * b + 4 * g);
+          const float4 ma = *reinterpret_cast<const float4*>(vmn + 16 * b + 4 * g);
+          const float vs4[4] = {va.x, va.y, va.z, va.w};
+          const float vm4[4] = {ma.x, ma.y, ma.z, ma.w};
+          float w4[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float pj = __builtin_amdgcn_exp2f(fmaf(beta, y[bb][i], negm));
+            psum += pj;
+            upart = fmaf(pj, vm4[i], upart);
+            w4[i] = pj * vs4[i];
+          }
+#pragma unroll
+          for (int pr = 0; pr < 2; ++pr) {
+            const fp16x2 h = __builtin_amdgcn_cvt_pkrtz(w4[2 * pr], w4[2 * pr + 1]);
+            const fp16x2 l = __builtin_amdgcn_cvt_pkrtz(w4[2 * pr] - (float)h.x, w4[2 * pr + 1] - (float)h.y);
+            wh[bb][pr] = __builtin_bit_cast(uint32_t, h);
+            wl[bb][pr] = __builtin_bit_cast(uint32_t, l);
+          }
+        }
+        l_run += rows_sum(psum);
+        const float u = rows_sum(upart);
+        // O'^T[c][n] += vcu_c z_c, z_c starting at u fv 2^-(24 - shift(c)) so that
+        // vcu_c z_c = vchan_c (sum_t p_t vscale_t zV_tc + sum_t p_t vmin_t)
+        const float ufv = u * pow2i(13 - (int)kTau - ev);
+        const float zi0 = ufv * pow2i(-20), zi1 = ufv * pow2i(-18);
+        half8 Wh[2], Wl[2];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          Wh[tt] = as_half8(wh[2 * tt][0], wh[2 * tt][1], wh[2 * tt + 1][0], wh[2 * tt + 1][1]);
+          Wl[tt] = as_half8(wl[2 * tt][0], wl[2 * tt][1], wl[2 * tt + 1][0], wl[2 * tt + 1][1]);
+        }
+        const float* vcu = reinterpret_cast<const float*>(cst + kCVcu);
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          float4 vc[4];   // channels 64 qb + 16 g + 4 i .. + 3
+#pragma unroll
+          for (int i = 0; i < 4; ++i) vc[i] = *reinterpret_cast<const float4*>(vcu + 64 * qb + 16 * g + 4 * i);
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) {
+            const int q8 = 4 * qb + kk;
+            const float zi = (kk & 1) ? zi1 : zi0;
+            floatx4 z = {zi, zi, zi, zi};
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+              const uint4 av = vop[((2 * hh + tt) * 8 + q8) * 64 + offv[qb]];
+              const half8 Av = as_half8(av.x, av.y, av.z, av.w);
+              z = __builtin_amdgcn_mfma_f32_16x16x32_f16(Av, Wh[tt], z, 0, 0, 0);
+              z = __builtin_amdgcn_mfma_f32_16x16x32_f16(Av, Wl[tt], z, 0, 0, 0);
+            }
+            const float vk[4] = {kk == 0 ? vc[0].x : kk == 1 ? vc[0].y : kk == 2 ? vc[0].z : vc[0].w,
+                                 kk == 0 ? vc[1].x : kk == 1 ? vc[1].y : kk == 2 ? vc[1].z : vc[1].w,
+                                 kk == 0 ? vc[2].x : kk == 1 ? vc[2].y : kk == 2 ? vc[2].z : vc[2].w,
+                                 kk == 0 ? vc[3].x : kk == 1 ? vc[3].y : kk == 2 ? vc[3].z : vc[3].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) O[qb][kk][i] = fmaf(vk[i], z[i], O[qb][kk][i]);
+          }
         }
       }
     }
@@ -616,8 +645,10 @@ __device__ __forceinline__ void prefill_body(const Ctx& P) {
   }
 
   // ---- inverse rotation of the tile part: channel bits kk (0, 1), i (2, 3),
-  // g (4, 5: across 16-lane rows), qb (6); partials stay rotated ----
-  if (T_wave > 0 && !partial) {
+  // g (4, 5: across 16-lane rows), qb (6).  The partials of FR = false stay
+  // rotated (a verify split holds tiles or raw tokens, never both); those of
+  // FR = true hold both and are in the raw domain. ----
+  if (T_wave > 0 && (FR || !partial)) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
@@ -691,61 +722,84 @@ __device__ __forceinline__ void prefill_body(const Ctx& P) {
     *reinterpret_cast<float4*>(s_v + sr * kRawRow + 4 * (sc4 + 16)) = keep4(xs.ok, xs.v1);
     if (t0 + kRawTok < r_hi) xs = raw_fetch(kbase, vbase, P.tok_stride, P.raw_base, t0 + kRawTok + sr, r_hi, sc4);
     __syncthreads();
-    const int sb = th;
-    const int64_t tb = t0 + 16 * sb;
-    if (!active || tb > p_wlast || tb >= r_hi || tb + 15 < wave_lo) continue;   // wave-uniform
-    // S^T[t][r]: A = raw keys (row n = token tb + n), B = raw query of row n;
-    // MFMA (jj, e) contracts channels 16 jj + 4 g' + e over K slots g'
-    floatx4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      const float4 ka = *reinterpret_cast<const float4*>(s_k + (16 * sb + n) * kRawRow + 16 * jj + 4 * g);
-      sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(ka.x, qr[jj].x, sacc, 0, 0, 0);
-      sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(ka.y, qr[jj].y, sacc, 0, 0, 0);
-      sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(ka.z, qr[jj].z, sacc, 0, 0, 0);
-      sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(ka.w, qr[jj].w, sacc, 0, 0, 0);
-    }
-    // lane (g, n): tokens tb + 4 g + i of row n
-    float sv[4];
-    float tmax = -INFINITY;
+    for (int sx = 0; sx < NH; ++sx) {   // the wave's 16-token block(s) of the step
+      const int sb = FR ? sx : th;
+      const int64_t tb = t0 + 16 * sb;
+      if (!active || tb > p_wlast || tb >= r_hi || tb + 15 < wave_lo) continue;   // wave-uniform
+      // S^T[t][r]: A = raw keys (row n = token tb + n), B = raw query of row n;
+      // MFMA (jj, e) contracts channels 16 jj + 4 g' + e over K slots g'
+      floatx4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t t = tb + 4 * g + i;
-      const bool vis = row_ok && t >= row_lo && t <= prow && t < r_hi;
-      sv[i] = vis ? sacc[i] * scale_log2 : -INFINITY;
-      tmax = fmaxf(tmax, sv[i]);
-    }
-    tmax = rows_max(tmax);
-    const float m_new = fmaxf(m_run, tmax);
-    const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    float pv[4], psum = 0.0f;
+      for (int jj = 0; jj < 8; ++jj) {
+        const float4 ka = *reinterpret_cast<const float4*>(s_k + (16 * sb + n) * kRawRow + 16 * jj + 4 * g);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(ka.x, qr[jj].x, sacc, 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(ka.y, qr[jj].y, sacc, 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(ka.z, qr[jj].z, sacc, 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(ka.w, qr[jj].w, sacc, 0, 0, 0);
+      }
+      // lane (g, n): tokens tb + 4 g + i of row n
+      float sv[4];
+      float tmax = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      pv[i] = __builtin_amdgcn_exp2f(sv[i] - m_use);
-      psum += pv[i];
+      for (int i = 0; i < 4; ++i) {
+        const int64_t t = tb + 4 * g + i;
+        const bool vis = row_ok && t >= row_lo && t <= prow && t < r_hi;
+        sv[i] = vis ? sacc[i] * scale_log2 : -INFINITY;
+        tmax = fmaxf(tmax, sv[i]);
+      }
+      tmax = rows_max(tmax);
+      const float m_new = fmaxf(m_run, tmax);
+      const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      float pv[4], psum = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pv[i] = __builtin_amdgcn_exp2f(sv[i] - m_use);
+        psum += pv[i];
+      }
+      l_run = l_run * alpha + rows_sum(psum);
+      m_run = m_new;
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) O[qb][kk][i] *= alpha;
+      // O^T[c][n] += sum_t v[t][c] p[n][t]; step i: K slot g is token tb + 4 g + i,
+      // A row n' is channel 64 qb + 4 n' + kk
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          const float4 vv = *reinterpret_cast<const float4*>(s_v + (16 * sb + 4 * g + i) * kRawRow + 64 * qb + 4 * n);
+          O[qb][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(vv.x, pv[i], O[qb][0], 0, 0, 0);
+          O[qb][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(vv.y, pv[i], O[qb][1], 0, 0, 0);
+          O[qb][2] = __builtin_amdgcn_mfma_f32_16x16x4f32(vv.z, pv[i], O[qb][2], 0, 0, 0);
+          O[qb][3] = __builtin_amdgcn_mfma_f32_16x16x4f32(vv.w, pv[i], O[qb][3], 0, 0, 0);
+        }
+      }
     }
-    l_run = l_run * alpha + rows_sum(psum);
-    m_run = m_new;
+  }
+
+  if constexpr (FR) {   // ---- normalise (or keep the partial), store ----
+    if (!row_ok) return;
+    float ca = 1.0f;
+    float* o;
+    if (partial) {
+      o = P.part + (int64_t)(r0 + n) * P.part_row + (int64_t)hq * P.part_head;
+      if (g == 0) *reinterpret_cast<float2*>(o + D) = make_float2(m_run, l_run);
+    } else {
+      ca = 1.0f / l_run;   // every row of a final output sees its own position
+      o = P.out + ((int64_t)(r0 + n) * P.n_q + hq) * D;
+    }
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) O[qb][kk][i] *= alpha;
-    // O^T[c][n] += sum_t v[t][c] p[n][t]; step i: K slot g is token tb + 4 g + i,
-    // A row n' is channel 64 qb + 4 n' + kk
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const float4 vv = *reinterpret_cast<const float4*>(s_v + (16 * sb + 4 * g + i) * kRawRow + 64 * qb + 4 * n);
-        O[qb][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(vv.x, pv[i], O[qb][0], 0, 0, 0);
-        O[qb][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(vv.y, pv[i], O[qb][1], 0, 0, 0);
-        O[qb][2] = __builtin_amdgcn_mfma_f32_16x16x4f32(vv.z, pv[i], O[qb][2], 0, 0, 0);
-        O[qb][3] = __builtin_amdgcn_mfma_f32_16x16x4f32(vv.w, pv[i], O[qb][3], 0, 0, 0);
-      }
-    }
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<float4*>(o + 64 * qb + 16 * g + 4 * i) =
+            make_float4(O[qb][0][i] * ca, O[qb][1][i] * ca, O[qb][2][i] * ca, O[qb][3][i] * ca);
+    return;
   }
 
   // ---- merge the two token halves of each row group, normalise, store ----
@@ -824,7 +878,54 @@ __global__ void __launch_bounds__(kThreads) prefill_mfma_kernel(PrefillParams P)
   c.rb = INT64_MAX;
   c.part = nullptr;
   c.part_row = c.part_head = 0;
-  prefill_body<H>(c);
+  prefill_body<H, false>(c);
+}
+
+// Chunked prefill with whole tiles per wave (FR layout: 128 row-heads per
+// workgroup).  blockIdx.z = split s of S takes the s-th S-th of its
+// workgroup's tiles and of its raw tokens (in 32-token staging steps), so the
+// splits carry equal shares of both kinds of work; with S > 1 each writes the
+// raw-domain partial of its rows at part + ((r n_q + h) S + s) (D + 4), and
+// prefill_combine_kernel merges them.
+template <bool H>
+__global__ void __launch_bounds__(kThreads) prefill_split_kernel(PrefillParams P, float* part, int S) {
+  Ctx c;
+  c.q = P.q;
+  c.q_rot = P.q_rot;
+  c.out = P.out;
+  c.records = P.records;
+  c.k = P.k;
+  c.v = P.v;
+  c.tok_stride = P.tok_stride;
+  c.head_stride = P.head_stride;
+  c.pos0 = P.pos0;
+  c.raw_base = P.raw_base;
+  c.scale = P.scale;
+  c.chunk = P.chunk;
+  c.window = P.window;
+  c.n_q = P.n_q;
+  c.n_kv = P.n_kv;
+  c.G = P.G;
+  c.rotate = P.q_rot == nullptr;   // no rotated query given: rows rotate q in registers
+  if (c.rotate) c.q_rot = P.q;
+  const int s = blockIdx.z;
+  const int n_blk = ((P.chunk + kRows - 1) / kRows) * P.G;
+  const int blk_first = blockIdx.x * 8;
+  const int blk_last = min(blk_first + 7, n_blk - 1);
+  const int64_t p_first = P.pos0 + kRows * (blk_first / P.G);
+  const int64_t p_last = P.pos0 + min(kRows * (blk_last / P.G) + kRows - 1, P.chunk - 1);
+  const int Tw = tiles_at(p_last, P.window);
+  const int64_t r_lo = (int64_t)kTile * tiles_at(p_first, P.window);
+  const int64_t steps = (p_last + 1 - r_lo + kRawTok - 1) / kRawTok;
+  c.ja = (int)((int64_t)Tw * s / S);
+  c.jb = (int)((int64_t)Tw * (s + 1) / S);
+  c.raw = true;
+  c.ra = r_lo + kRawTok * (steps * s / S);
+  c.rb = r_lo + kRawTok * (steps * (s + 1) / S);
+  c.part = S > 1 ? part + (int64_t)s * (D + 4) : nullptr;
+  c.part_head = (int64_t)S * (D + 4);
+  c.part_row = (int64_t)P.n_q * c.part_head;
+  prefill_body<H, true>(c);
 }
 
 // Multi-query verify: sequence b's q_len query rows are the q_len newest
@@ -876,7 +977,7 @@ __global__ void __launch_bounds__(kThreads) verify_mfma_kernel(DecodeParams P) {
   c.part_head = (int64_t)nsp * (D + 4);
   c.part_row = (int64_t)P.n_q * c.part_head;
   c.part = P.part + (int64_t)b * w * c.part_row + (int64_t)s * (D + 4);
-  prefill_body<H>(c);
+  prefill_body<H, false>(c);
 }
 
 // Verify combine: one wave per (row, query head), lane l owns channels l and
@@ -952,6 +1053,29 @@ __global__ void __launch_bounds__(256) verify_combine_kernel(DecodeParams P, int
   o[lane + 64] = (o1 * a + r1 * bw) * inv;
 }
 
+// Merge of the S raw-domain split partials of a chunked prefill: one wave per
+// (row, query head), lane l owns channels 2l, 2l + 1; log-sum-exp weights
+// against the largest running maximum, then the division by L.
+__global__ void __launch_bounds__(256) prefill_combine_kernel(const float* part, float* out, int n_items, int S) {
+  const int lane = threadIdx.x & 63;
+  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (item >= n_items) return;   // wave-uniform
+  const float* pp = part + (int64_t)item * S * (D + 4);
+  float M = -INFINITY;
+  for (int s = 0; s < S; ++s) M = fmaxf(M, pp[(int64_t)s * (D + 4) + D]);
+  float L = 0.0f, x = 0.0f, y = 0.0f;
+  for (int s = 0; s < S; ++s) {
+    const float2 ml = *reinterpret_cast<const float2*>(pp + (int64_t)s * (D + 4) + D);
+    const float2 o = *reinterpret_cast<const float2*>(pp + (int64_t)s * (D + 4) + 2 * lane);
+    const float w = (ml.x == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(ml.x - M);   // a split that sees nothing
+    L = fmaf(w, ml.y, L);
+    x = fmaf(w, o.x, x);
+    y = fmaf(w, o.y, y);
+  }
+  const float inv = 1.0f / L;   // finite: every row sees its own position in one split
+  *reinterpret_cast<float2*>(out + (int64_t)item * D + 2 * lane) = make_float2(x * inv, y * inv);
+}
+
 }  // namespace
 
 hipError_t launch_prefill_mfma(const PrefillParams& P, hipStream_t stream) {
@@ -961,6 +1085,21 @@ hipError_t launch_prefill_mfma(const PrefillParams& P, hipStream_t stream) {
     hipLaunchKernelGGL(prefill_mfma_kernel<true>, grid, dim3(kThreads), 0, stream, P);
   else
     hipLaunchKernelGGL(prefill_mfma_kernel<false>, grid, dim3(kThreads), 0, stream, P);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_split(const PrefillParams& P, float* part, int S, hipStream_t stream) {
+  const int n_blk = ((P.chunk + kRows - 1) / kRows) * P.G;
+  dim3 grid((n_blk + 7) / 8, P.n_kv, S);
+  if (P.h16)
+    hipLaunchKernelGGL(prefill_split_kernel<true>, grid, dim3(kThreads), 0, stream, P, part, S);
+  else
+    hipLaunchKernelGGL(prefill_split_kernel<false>, grid, dim3(kThreads), 0, stream, P, part, S);
+  if (S > 1) {
+    const int items = P.chunk * P.n_q;
+    hipLaunchKernelGGL(prefill_combine_kernel, dim3((items + 3) / 4), dim3(256), 0, stream,
+                       static_cast<const float*>(part), P.out, items, S);
+  }
   return hipGetLastError();
 }
 

@@ -279,23 +279,30 @@ def prefill_workspace_bytes(q, q_rot, records, n_record_rows, k, v, raw_base, po
 
 
 def prefill_attention(q, q_rot, records, n_record_rows, k, v, raw_base, pos0, window, scale,
-                      out=None, workspace=None, stream=None, f16_scales=False, kbits=4, vbits=2):
+                      out=None, workspace=None, stream=None, f16_scales=False, kbits=4, vbits=2,
+                      no_workspace=False):
     """Chunk of C query positions [pos0, pos0+C) of one sequence.
 
     q, q_rot: [C][Hq][d] (q_rot may be None over K4V2 records: the kernels
     rotate the rows themselves).  records: [rows][Hkv][tile_bytes] (tile j = row j).
     k, v: raw [n][Hkv][d] views whose row i is absolute position raw_base + i;
-    f16_scales: the records carry f16 scales; kbits / vbits: their code widths."""
+    f16_scales: the records carry f16 scales; kbits / vbits: their code widths.
+    workspace: None allocates what the call needs; no_workspace passes NULL
+    (head_dim 128 over K4V2 records only: the single-launch kernel)."""
     assert k.stride(2) == 1 and k.stride() == v.stride()
     if out is None:
         out = torch.empty_like(q)
     a = _prefill_args(q, q_rot, records, n_record_rows, k, v, raw_base, pos0, window, scale, out,
                       f16_scales, kbits, vbits)
-    need = int(lib().kvarn_prefill_workspace_bytes(ctypes.byref(a)))
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if no_workspace:
+        ws_ptr, ws_bytes = None, 0
+    else:
+        need = int(lib().kvarn_prefill_workspace_bytes(ctypes.byref(a)))
+        if workspace is None:
+            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        ws_ptr, ws_bytes = _ptr(workspace), workspace.numel()
     _check("kvarn_prefill_attention", lib().kvarn_prefill_attention(
-        ctypes.byref(a), _ptr(workspace), workspace.numel(), _stream(stream)))
+        ctypes.byref(a), ws_ptr, ws_bytes, _stream(stream)))
     return out
 
 

@@ -204,12 +204,18 @@ def test_prefill_validation(L):
             setattr(a, k, v)
         return a
     a = args()
-    # the matrix-core prefill keeps its whole state on chip
-    assert L.kvarn_prefill_workspace_bytes(ctypes.byref(a)) == 0
+    # the matrix-core prefill at head_dim 128: 256 rows x 8 heads make 16
+    # workgroups of 128 row-heads, so 4 splits (the most), each partial 128 + 4 floats
+    need128 = L.kvarn_prefill_workspace_bytes(ctypes.byref(a))
+    assert need128 == 256 * 8 * 4 * (128 + 4) * 4
+    assert L.kvarn_prefill_attention(ctypes.byref(a), ctypes.c_void_p(FAKE), need128 - 16, None) == 4
+    assert L.kvarn_prefill_attention(ctypes.byref(a), ctypes.c_void_p(FAKE + 8), need128, None) == 3
+    # 2048 rows x 32 heads over 8 KV heads: 512 workgroups fill the CUs unsplit, no partials
+    assert L.kvarn_prefill_workspace_bytes(ctypes.byref(args(chunk=2048, n_q_heads=32, n_kv_heads=8))) == 0
     # the K4V2 kernels rotate the rows themselves when no rotated query is given
-    # (at head_dim 256 the split partials still need a workspace); the
-    # vector-unit paths of other code widths need one
-    assert L.kvarn_prefill_workspace_bytes(ctypes.byref(args(q_rot=None))) == 0
+    # (the splits are the same); the vector-unit paths of other code widths need
+    # a workspace too
+    assert L.kvarn_prefill_workspace_bytes(ctypes.byref(args(q_rot=None))) == need128
     assert L.kvarn_prefill_workspace_bytes(
         ctypes.byref(args(head_dim=256, q_rot=None, tok_stride=512, head_stride=256))) > 0
     assert L.kvarn_prefill_attention(
