@@ -14,9 +14,11 @@
 // in one of two layouts:
 //   - split layout (prefill_split_kernel, the chunked prefill with a
 //     workspace): eight row groups, one per wave, each wave over all 128
-//     tokens of every tile (its two 64-token halves one after the other, the
-//     tile's q~ operands and bias computed once) and over both raw 16-token
-//     blocks of every staging step.  The workgroup's tiles and raw tokens are
+//     tokens of every tile (the tile's q~ operands and bias computed once; the
+//     scores of both 64-token halves, one running-maximum update, then per
+//     half the probabilities and the value aggregate, so that the vector work
+//     of one half meets the matrix work of the other) and over both raw
+//     16-token blocks of every staging step.  The workgroup's tiles and raw tokens are
 //     cut into S equal shares (blockIdx.z), so that the 128-row-head
 //     workgroups fill the chip; each share's raw-domain partial goes to the
 //     workspace and a combine launch merges them;
@@ -524,14 +526,16 @@ __device__ __forceinline__ void prefill_body(const Ctx& P) {
       const int bexp = em - 20 - ek;
       const float bsc = pow2i(bexp < -126 ? -126 : (bexp > 127 ? 127 : bexp));
       const floatx4 acc0 = {bacc[0] * bsc, bacc[1] * bsc, bacc[2] * bsc, bacc[3] * bsc};
+      // scores of the wave's token half(s) (y = alpha_t acc / beta, log2 domain:
+      // token 16 b + 4 g + i of row n), then one running-maximum update for the
+      // tile, then per half the probabilities and the value aggregate, so that
+      // the vector work of one half meets the matrix work of the other
+      const float* alp = reinterpret_cast<const float*>(cst + kCAlpha);
+      float y[NH][4][4];
+      float ymax = -INFINITY;
 #pragma unroll
-      for (int hx = 0; hx < NH; ++hx) {   // the wave's token half(s), one after the other
+      for (int hx = 0; hx < NH; ++hx) {
         const int hh = FR ? hx : th;
-        if (hx > 0) __builtin_amdgcn_s_setprio(1);
-        // scores / beta (log2 domain): y = alpha_t acc, token 16 b + 4 g + i of row n
-        const float* alp = reinterpret_cast<const float*>(cst + kCAlpha);
-        float y[4][4];
-        float ymax = -INFINITY;
 #pragma unroll
         for (int bb = 0; bb < 4; ++bb) {
           const int b = 4 * hh + bb;
@@ -544,34 +548,39 @@ __device__ __forceinline__ void prefill_body(const Ctx& P) {
             acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bl[k4], acc, 0, 0, 0);
           }
           const float4 al = *reinterpret_cast<const float4*>(alp + 16 * b + 4 * g);
-          y[bb][0] = acc[0] * al.x;
-          y[bb][1] = acc[1] * al.y;
-          y[bb][2] = acc[2] * al.z;
-          y[bb][3] = acc[3] * al.w;
-          ymax = fmaxf(fmaxf(ymax, y[bb][0]), y[bb][1]);
-          ymax = fmaxf(fmaxf(ymax, y[bb][2]), y[bb][3]);
+          y[hx][bb][0] = acc[0] * al.x;
+          y[hx][bb][1] = acc[1] * al.y;
+          y[hx][bb][2] = acc[2] * al.z;
+          y[hx][bb][3] = acc[3] * al.w;
+          ymax = fmaxf(fmaxf(ymax, y[hx][bb][0]), y[hx][bb][1]);
+          ymax = fmaxf(fmaxf(ymax, y[hx][bb][2]), y[hx][bb][3]);
         }
-        __builtin_amdgcn_s_setprio(0);
-        // lazy running maximum: raised only when the tile exceeds it by > tau
-        const bool vis = j < T_row;
-        const float tmax = rows_max(ymax) * beta;
-        const bool raise = vis && !(tmax <= m_run + kTau);
-        const float m_new = raise ? tmax : m_run;
-        const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;   // 0 from -inf
-        m_run = m_new;
-        const float negm = vis ? -m_run : -INFINITY;
-        l_run *= alpha;
-        if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+      }
+      __builtin_amdgcn_s_setprio(0);
+      // lazy running maximum: raised only when the tile exceeds it by > tau
+      const bool vis = j < T_row;
+      const float tmax = rows_max(ymax) * beta;
+      const bool raise = vis && !(tmax <= m_run + kTau);
+      const float m_new = raise ? tmax : m_run;
+      const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;   // 0 from -inf
+      m_run = m_new;
+      const float negm = vis ? -m_run : -INFINITY;
+      l_run *= alpha;
+      if (__builtin_amdgcn_ballot_w64(raise) != 0) {
 #pragma unroll
-          for (int qb = 0; qb < 2; ++qb)
+        for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
+          for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-              for (int i = 0; i < 4; ++i) O[qb][kk][i] *= alpha;
-        }
+            for (int i = 0; i < 4; ++i) O[qb][kk][i] *= alpha;
+      }
+      const float* vsf = reinterpret_cast<const float*>(cst + kCVsf);
+      const float* vmn = reinterpret_cast<const float*>(cst + kCVmin);
+      const float* vcu = reinterpret_cast<const float*>(cst + kCVcu);
+#pragma unroll
+      for (int hx = 0; hx < NH; ++hx) {
+        const int hh = FR ? hx : th;
         // probabilities p (<= 2^tau), their sums, and w = p vsf as hi / lo B operands
-        const float* vsf = reinterpret_cast<const float*>(cst + kCVsf);
-        const float* vmn = reinterpret_cast<const float*>(cst + kCVmin);
         float psum = 0.0f, upart = 0.0f;
         uint32_t wh[4][2], wl[4][2];
 #pragma unroll
@@ -584,7 +593,7 @@ __device__ __forceinline__ void prefill_body(const Ctx& P) {
           float w4[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float pj = __builtin_amdgcn_exp2f(fmaf(beta, y[bb][i], negm));
+            const float pj = __builtin_amdgcn_exp2f(fmaf(beta, y[hx][bb][i], negm));
             psum += pj;
             upart = fmaf(pj, vm4[i], upart);
             w4[i] = pj * vs4[i];
@@ -609,7 +618,6 @@ __device__ __forceinline__ void prefill_body(const Ctx& P) {
           Wh[tt] = as_half8(wh[2 * tt][0], wh[2 * tt][1], wh[2 * tt + 1][0], wh[2 * tt + 1][1]);
           Wl[tt] = as_half8(wl[2 * tt][0], wl[2 * tt][1], wl[2 * tt + 1][0], wl[2 * tt + 1][1]);
         }
-        const float* vcu = reinterpret_cast<const float*>(cst + kCVcu);
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
@@ -636,6 +644,7 @@ __device__ __forceinline__ void prefill_body(const Ctx& P) {
             for (int i = 0; i < 4; ++i) O[qb][kk][i] = fmaf(vk[i], z[i], O[qb][kk][i]);
           }
         }
+        if (hx + 1 < NH) __builtin_amdgcn_s_setprio(0);
       }
     }
     __builtin_amdgcn_s_setprio(0);
