@@ -808,53 +808,51 @@ __device__ __forceinline__ void prefill_body(const Ctx& P) {
       for (int i = 0; i < 4; ++i)
         *reinterpret_cast<float4*>(o + 64 * qb + 16 * g + 4 * i) =
             make_float4(O[qb][0][i] * ca, O[qb][1][i] * ca, O[qb][2][i] * ca, O[qb][3][i] * ca);
-    return;
-  }
-
-  // ---- merge the two token halves of each row group, normalise, store ----
-  __syncthreads();   // the raw staging rows are free
-  float4* mo = reinterpret_cast<float4*>(s_lds);
-  float2* mml = reinterpret_cast<float2*>(s_lds + kMergeO);
-  if (th == 1 && active) {
+  } else {   // ---- merge the two token halves of each row group, normalise, store ----
+    __syncthreads();   // the raw staging rows are free
+    float4* mo = reinterpret_cast<float4*>(s_lds);
+    float2* mml = reinterpret_cast<float2*>(s_lds + kMergeO);
+    if (th == 1 && active) {
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+      for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        mo[(rg * 8 + 4 * qb + kk) * 64 + lane] = make_float4(O[qb][kk][0], O[qb][kk][1], O[qb][kk][2], O[qb][kk][3]);
-    mml[rg * 64 + lane] = make_float2(m_run, l_run);
-  }
-  __syncthreads();
-  if (th == 1 || !row_ok) return;
-  const float2 ml2 = mml[rg * 64 + lane];
-  const float M = fmaxf(m_run, ml2.x);   // -inf only for a partial that sees nothing
-  const float fa = (m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run - M);
-  const float fb = (ml2.x == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(ml2.x - M);
-  const float lsum = l_run * fa + ml2.y * fb;
-  float ca = fa, cb = fb;
-  float* o;
-  if (partial) {
-    o = P.part + (int64_t)(r0 + n) * P.part_row + (int64_t)hq * P.part_head;
-    if (g == 0) *reinterpret_cast<float2*>(o + D) = make_float2(M, lsum);
-  } else {
-    const float inv = 1.0f / lsum;   // every row of a final output sees its own position
-    ca *= inv;
-    cb *= inv;
-    o = P.out + ((int64_t)(r0 + n) * P.n_q + hq) * D;
-  }
+        for (int kk = 0; kk < 4; ++kk)
+          mo[(rg * 8 + 4 * qb + kk) * 64 + lane] = make_float4(O[qb][kk][0], O[qb][kk][1], O[qb][kk][2], O[qb][kk][3]);
+      mml[rg * 64 + lane] = make_float2(m_run, l_run);
+    }
+    __syncthreads();
+    if (th == 1 || !row_ok) return;
+    const float2 ml2 = mml[rg * 64 + lane];
+    const float M = fmaxf(m_run, ml2.x);   // -inf only for a partial that sees nothing
+    const float fa = (m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run - M);
+    const float fb = (ml2.x == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(ml2.x - M);
+    const float lsum = l_run * fa + ml2.y * fb;
+    float ca = fa, cb = fb;
+    float* o;
+    if (partial) {
+      o = P.part + (int64_t)(r0 + n) * P.part_row + (int64_t)hq * P.part_head;
+      if (g == 0) *reinterpret_cast<float2*>(o + D) = make_float2(M, lsum);
+    } else {
+      const float inv = 1.0f / lsum;   // every row of a final output sees its own position
+      ca *= inv;
+      cb *= inv;
+      o = P.out + ((int64_t)(r0 + n) * P.n_q + hq) * D;
+    }
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    float4 ob[4];
+    for (int qb = 0; qb < 2; ++qb) {
+      float4 ob[4];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) ob[kk] = mo[(rg * 8 + 4 * qb + kk) * 64 + lane];
+      for (int kk = 0; kk < 4; ++kk) ob[kk] = mo[(rg * 8 + 4 * qb + kk) * 64 + lane];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float b0 = i == 0 ? ob[0].x : i == 1 ? ob[0].y : i == 2 ? ob[0].z : ob[0].w;
-      const float b1 = i == 0 ? ob[1].x : i == 1 ? ob[1].y : i == 2 ? ob[1].z : ob[1].w;
-      const float b2 = i == 0 ? ob[2].x : i == 1 ? ob[2].y : i == 2 ? ob[2].z : ob[2].w;
-      const float b3 = i == 0 ? ob[3].x : i == 1 ? ob[3].y : i == 2 ? ob[3].z : ob[3].w;
-      *reinterpret_cast<float4*>(o + 64 * qb + 16 * g + 4 * i) =
-          make_float4(O[qb][0][i] * ca + b0 * cb, O[qb][1][i] * ca + b1 * cb,
-                      O[qb][2][i] * ca + b2 * cb, O[qb][3][i] * ca + b3 * cb);
+      for (int i = 0; i < 4; ++i) {
+        const float b0 = i == 0 ? ob[0].x : i == 1 ? ob[0].y : i == 2 ? ob[0].z : ob[0].w;
+        const float b1 = i == 0 ? ob[1].x : i == 1 ? ob[1].y : i == 2 ? ob[1].z : ob[1].w;
+        const float b2 = i == 0 ? ob[2].x : i == 1 ? ob[2].y : i == 2 ? ob[2].z : ob[2].w;
+        const float b3 = i == 0 ? ob[3].x : i == 1 ? ob[3].y : i == 2 ? ob[3].z : ob[3].w;
+        *reinterpret_cast<float4*>(o + 64 * qb + 16 * g + 4 * i) =
+            make_float4(O[qb][0][i] * ca + b0 * cb, O[qb][1][i] * ca + b1 * cb,
+                        O[qb][2][i] * ca + b2 * cb, O[qb][3][i] * ca + b3 * cb);
+      }
     }
   }
 }
