@@ -322,11 +322,12 @@ struct Ctx {
 // FR = false: four row groups of 16 rows, wave (r, h) takes the token half h
 // of every tile and the 16-token raw blocks of parity h, and the two halves
 // of a row group merge at the end.  FR = true: eight row groups, each wave
-// takes all 128 tokens of every tile (the halves one after the other, with
-// the tile's q~ operands and bias computed once) and both raw blocks of every
-// staging step; each tile's unpack then serves twice the rows.  In both,
-// waves 0-3 unpack the next tile at the start of an iteration and waves 4-7 at
-// its end.
+// takes all 128 tokens of every tile (the scores of both halves, one running-
+// maximum update, then softmax and values per half; the tile's q~ operands
+// and bias computed once) and both raw blocks of every staging step; each
+// tile's unpack then serves twice the rows.  The next tile is unpacked by
+// waves 0-3 at the start of an iteration and by waves 4-7 at its end in the
+// half layout, by every wave at the end in the split layout.
 template <bool H, bool FR>
 __device__ __forceinline__ void prefill_body(const Ctx& P) {
   constexpr int RG = FR ? 8 : 4;          // row groups (column blocks) per workgroup
@@ -461,9 +462,12 @@ __device__ __forceinline__ void prefill_body(const Ctx& P) {
     for (int kk = 0; kk < 4; ++kk) O[qb][kk] = (floatx4){0.f, 0.f, 0.f, 0.f};
 
   // ---- compressed tiles: compute tile j while unpacking tile j + 1 into the
-  // other buffer and loading tile j + 2.  The two waves on a SIMD (waves w and
-  // w + 4) unpack at opposite ends of the iteration, so the matrix work of one
-  // meets the vector work of the other. ----
+  // other buffer and loading tile j + 2.  In the half layout the two waves on a
+  // SIMD (waves w and w + 4) unpack at opposite ends of the iteration, so the
+  // matrix work of one meets the vector work of the other; in the split layout,
+  // where each wave's two token halves already interleave vector and matrix
+  // work, every wave unpacks at the end (measured faster than either split of
+  // the waves). ----
   for (int j = ja; j < jend; ++j) {
     const int pb = (j - ja) & 1;   // buffer of tile j
     const uint8_t* cst = s_lds + kLdsC + pb * kConstBytes;
@@ -476,7 +480,7 @@ __device__ __forceinline__ void prefill_body(const Ctx& P) {
                   lane, wv, scale_log2);
       if (j + 2 < jend) load_tile<H>(recs + (int64_t)(j + 2) * rstride, lane, wv, tr);
     };
-    if (th == 0 && next) unpack_next();
+    if (!FR && th == 0 && next) unpack_next();
     if (j < T_wave) {
       const int* ex = reinterpret_cast<const int*>(cst + kCExp);
       const int ek = __builtin_amdgcn_readfirstlane(ex[0]);
@@ -648,7 +652,7 @@ __device__ __forceinline__ void prefill_body(const Ctx& P) {
       }
     }
     __builtin_amdgcn_s_setprio(0);
-    if (th == 1 && next) unpack_next();
+    if ((FR || th == 1) && next) unpack_next();
     // tile j + 1 is in place and every wave is done with tile j's buffer
     __syncthreads();
   }
