@@ -337,12 +337,16 @@ def test_prefill_small_prompt_every_row():
 
 @pytest.mark.parametrize("W,chunk,Hq,Hkv,n,rotate", [(0, 100, 8, 8, 620, True), (1, 17, 4, 2, 300, False),
                                                      (100, 333, 16, 2, 800, True), (384, 1, 8, 1, 410, False),
-                                                     (128, 1000, 8, 4, 700, False)])
+                                                     (128, 1000, 8, 4, 700, False),
+                                                     # 288-row chunks at 32/8 heads: 72 workgroups, 3 shares
+                                                     (256, 288, 32, 8, 600, False)])
 def test_prefill_windows_ragged_chunks_and_gqa_every_row(W, chunk, Hq, Hkv, n, rotate):
     """Windows 0, 1 and not a multiple of 128, chunks that cut 16-row column
     blocks and tiles anywhere (down to one row, up to the whole prompt), and
-    query/KV head ratios 1, 2 and 8 on the head_dim-128 matrix-core kernel;
-    with the rotated query given or rotated inside the kernel."""
+    query/KV head ratios 1, 2, 4 and 8 on the head_dim-128 matrix-core kernel
+    (4 shares, and 3 at 288-row chunks of 32/8 heads; the 15488-token test
+    covers 1 and 2); with the rotated query given or rotated inside the
+    kernel."""
     say("prefill window/chunk/gqa", W, chunk, Hq, Hkv, n, rotate)
     d = 128
     K, V = synth.make_kv(60 + W + chunk, n, Hkv, d, 2)
