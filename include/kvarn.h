@@ -178,11 +178,12 @@ typedef struct kvarn_decode_args {
   int64_t n_record_rows;   /* rows in the pool (a row = n_kv_heads records)     */
   const int64_t* rec_start;/* host [batch]                                      */
   const int32_t* n_tiles;  /* host [batch] compressed tiles per sequence        */
-  const float* k_win;      /* device raw window keys: token i of sequence b,
+  float* k_win;            /* device raw window keys: token i of sequence b,
                               KV head h at k_win + b*win_seq_stride +
                               (win_start[b] + i)*win_tok_stride +
-                              h*win_head_stride (floats)                        */
-  const float* v_win;      /* device raw window values, same strides            */
+                              h*win_head_stride (floats); written only at token
+                              n_win[b] - 1, and only when k_new is given        */
+  float* v_win;            /* device raw window values, same strides            */
   int64_t win_seq_stride, win_tok_stride, win_head_stride;
   const int64_t* win_start;/* host [batch] first window row of each sequence, or
                               NULL for all zero                                 */
@@ -199,6 +200,17 @@ typedef struct kvarn_decode_args {
                               (n_win[b] >= q_len).  gmlx PR #116 commit list:
                               verify widths 2-8 attend the records on the matrix
                               units at about the cost of one decode step.       */
+  const float* k_new;      /* device [batch][n_kv_heads][head_dim] keys of each
+                              sequence's newest token, or NULL.  Given (with
+                              v_new, q_len <= 1, n_win[b] >= 1), the call stores
+                              them and v_new as window token n_win[b] - 1 of
+                              sequence b (the window append of the PR #434
+                              commit list: FP32 window staging) and attends them
+                              as part of the window, so a decode step needs no
+                              separate copy: the head_dim-128 K4V2 kernel
+                              appends in the same launch, the other paths with
+                              one small copy launch first.                      */
+  const float* v_new;      /* device values of the newest token, same layout    */
 } kvarn_decode_args;
 
 /* Workspace bytes kvarn_decode_attention needs for these arguments (0 on

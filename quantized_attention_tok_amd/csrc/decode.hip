@@ -540,6 +540,25 @@ hipError_t launch_decode_d(const DecodeParams& P, int batch, hipStream_t stream)
 
 }  // namespace
 
+// Sequence b (blockIdx.x), KV head h (blockIdx.y): the newest token's key and
+// value rows to window token n_win[b] - 1.
+__global__ void __launch_bounds__(128) append_window_kernel(DecodeParams P, float* k_win, float* v_win, int d) {
+  const int b = blockIdx.x, h = blockIdx.y;
+  const int64_t dst = (int64_t)b * P.win_seq_stride + (P.win_start[b] + P.n_win[b] - 1) * P.win_tok_stride +
+                      (int64_t)h * P.win_head_stride;
+  const int64_t src = ((int64_t)b * P.n_kv + h) * d;
+  for (int c = 4 * threadIdx.x; c < d; c += 4 * blockDim.x) {
+    *reinterpret_cast<float4*>(k_win + dst + c) = *reinterpret_cast<const float4*>(P.k_new + src + c);
+    *reinterpret_cast<float4*>(v_win + dst + c) = *reinterpret_cast<const float4*>(P.v_new + src + c);
+  }
+}
+
+hipError_t launch_append_window(int d, const DecodeParams& P, float* k_win, float* v_win, int batch,
+                                hipStream_t stream) {
+  hipLaunchKernelGGL(append_window_kernel, dim3(batch, P.n_kv), dim3(128), 0, stream, P, k_win, v_win, d);
+  return hipGetLastError();
+}
+
 hipError_t launch_decode(int d, const DecodeParams& P, int batch, hipStream_t stream) {
   switch (d) {
     case 128: return launch_decode_d<128>(P, batch, stream);

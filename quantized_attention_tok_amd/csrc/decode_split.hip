@@ -104,7 +104,9 @@ __device__ __forceinline__ void wht128(float& x, float& y, int lane) {
   y = (a - c) * wht_scale<D>();
 }
 
-template <int G, int TPW, bool H>
+// APP: the call appends the newest token (P.k_new, P.v_new): window token
+// n_win - 1 is read from them and stored into the window.
+template <int G, int TPW, bool H, bool APP>
 __global__ void __launch_bounds__(256 * TPW) decode_split_kernel(DecodeParams P) {
   using L = Lds<G, TPW>;
   using R = Rec<D, H>;
@@ -175,15 +177,27 @@ __global__ void __launch_bounds__(256 * TPW) decode_split_kernel(DecodeParams P)
   }
   const float* kwin = p_kwin + sv.win_off + (int64_t)kvh * p_hst;
   const float* vwin = p_vwin + sv.win_off + (int64_t)kvh * p_hst;
+  // APP: the newest window token (n_win - 1) is read from k_new / v_new and
+  // stored into the window by the wave that takes it (section 4)
+  const int t_new = APP ? sv.nw - 1 : -1;
 #pragma unroll
   for (int k = 0; k < KW; ++k) {
     const int tr = wv + NW * k;
     if (tr < nwt) {
-      const int64_t row = (int64_t)(wps * split + tr) * p_tok;
-      wk0[k] = kwin[row + lane];
-      wk1[k] = kwin[row + lane + 64];
-      wv0[k] = vwin[row + lane];
-      wv1[k] = vwin[row + lane + 64];
+      if (APP && wps * split + tr == t_new) {   // wave-uniform
+        const float* ks = P.k_new + ((int64_t)b * n_kv + kvh) * D;
+        const float* vs = P.v_new + ((int64_t)b * n_kv + kvh) * D;
+        wk0[k] = ks[lane];
+        wk1[k] = ks[lane + 64];
+        wv0[k] = vs[lane];
+        wv1[k] = vs[lane + 64];
+      } else {
+        const int64_t row = (int64_t)(wps * split + tr) * p_tok;
+        wk0[k] = kwin[row + lane];
+        wk1[k] = kwin[row + lane + 64];
+        wv0[k] = vwin[row + lane];
+        wv1[k] = vwin[row + lane + 64];
+      }
     }
   }
   uint4 kc0, kc1, vcd;   // (read only by waves with a tile)
@@ -365,6 +379,15 @@ __global__ void __launch_bounds__(256 * TPW) decode_split_kernel(DecodeParams P)
   for (int k = 0; k < KW; ++k) {
     const int tr = wv + NW * k;
     if (tr < nwt) {   // wave-uniform
+      if (APP && wps * split + tr == t_new) {   // the appended token: into the window (the API's window is writable)
+        const int64_t row = (int64_t)t_new * p_tok;
+        float* kw = const_cast<float*>(kwin);
+        float* vw = const_cast<float*>(vwin);
+        kw[row + lane] = wk0[k];
+        kw[row + lane + 64] = wk1[k];
+        vw[row + lane] = wv0[k];
+        vw[row + lane + 64] = wv1[k];
+      }
       float sc[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) sc[h] = row_sum16(qw0[h] * wk0[k] + qw1[h] * wk1[k]);
@@ -528,16 +551,21 @@ __global__ void __launch_bounds__(256) decode_combine_kernel(DecodeParams P) {
   }
 }
 
-template <int G, bool H>
-hipError_t launch_split_gh(const DecodeParams& P, int batch, hipStream_t stream) {
+template <int G, bool H, bool APP>
+hipError_t launch_split_gha(const DecodeParams& P, int batch, hipStream_t stream) {
   dim3 grid(P.n_tsplit, P.n_kv, batch);
   switch (P.tps) {
-    case 1: hipLaunchKernelGGL((decode_split_kernel<G, 1, H>), grid, dim3(256), 0, stream, P); break;
-    case 2: hipLaunchKernelGGL((decode_split_kernel<G, 2, H>), grid, dim3(512), 0, stream, P); break;
-    case 4: hipLaunchKernelGGL((decode_split_kernel<G, 4, H>), grid, dim3(1024), 0, stream, P); break;
+    case 1: hipLaunchKernelGGL((decode_split_kernel<G, 1, H, APP>), grid, dim3(256), 0, stream, P); break;
+    case 2: hipLaunchKernelGGL((decode_split_kernel<G, 2, H, APP>), grid, dim3(512), 0, stream, P); break;
+    case 4: hipLaunchKernelGGL((decode_split_kernel<G, 4, H, APP>), grid, dim3(1024), 0, stream, P); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <int G, bool H>
+hipError_t launch_split_gh(const DecodeParams& P, int batch, hipStream_t stream) {
+  return P.k_new ? launch_split_gha<G, H, true>(P, batch, stream) : launch_split_gha<G, H, false>(P, batch, stream);
 }
 
 template <int G>

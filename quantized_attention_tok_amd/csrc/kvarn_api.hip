@@ -138,6 +138,13 @@ int validate_decode(const kvarn_decode_args* a, DecodePlan* plan) {
     }
     if (nw > 0) any_win = true;
   }
+  if ((a->k_new == nullptr) != (a->v_new == nullptr)) return KVARN_E_INVALID;
+  if (a->k_new) {   // the appended token is window token n_win[b] - 1 of a single-query decode
+    if (w > 1) return KVARN_E_INVALID;
+    for (int b = 0; b < a->batch; ++b)
+      if (a->n_win[b] < 1) return KVARN_E_INVALID;
+    if (!al16(a->k_new) || !al16(a->v_new)) return KVARN_E_ALIGN;
+  }
   if (any_tiles && !a->records) return KVARN_E_INVALID;
   if (any_win && (!a->k_win || !a->v_win)) return KVARN_E_INVALID;
   if (any_win && (a->win_tok_stride < dim_of(a->head_dim) || a->win_head_stride < 0 ||
@@ -359,6 +366,15 @@ int kvarn_decode_attention(const kvarn_decode_args* a, void* workspace, size_t w
     P.n_win[b] = a->n_win[b];
   }
   hipError_t e;
+  if (a->k_new) {   // the newest token's rows into the window (a single-query decode)
+    P.k_new = a->k_new;
+    P.v_new = a->v_new;
+    if (!fused) {   // the split kernel of head_dim-128 K4V2 appends them itself; the others copy first
+      e = kvarn::launch_append_window(dim_of(a->head_dim), P, a->k_win, a->v_win, a->batch, (hipStream_t)stream);
+      if (e != hipSuccess) return KVARN_E_DEVICE;
+      P.k_new = P.v_new = nullptr;
+    }
+  }
   if (w > 1) {
     P.q_len = w;   // without q_rot the workgroups rotate the rows themselves
     e = kvarn::launch_verify_mfma(P, a->batch, (hipStream_t)stream);

@@ -39,6 +39,8 @@ struct DecodeParams {
   int64_t win_start[64];
   int n_tiles[64];
   int n_win[64];
+  const float* k_new;              // newest token's rows [B][n_kv][D] to append, or NULL
+  const float* v_new;
 };
 
 // Chunked prefill of one sequence (head_dim 128 matrix-core kernel).
@@ -98,6 +100,10 @@ hipError_t launch_compress(int d, bool h16, int kb, int vb, int n_tiles, int n_k
                            hipStream_t stream);
 hipError_t launch_rotate(int d, int64_t n_rows, const float* q, float* q_rot, hipStream_t stream);
 hipError_t launch_decode(int d, const DecodeParams& P, int batch, hipStream_t stream);
+// Store k_new / v_new (P.k_new, P.v_new) as window token n_win[b] - 1 of each
+// sequence: the append for the decode paths that do not take it in-kernel.
+hipError_t launch_append_window(int d, const DecodeParams& P, float* k_win, float* v_win, int batch,
+                                hipStream_t stream);
 hipError_t launch_decode_fused(const DecodeParams& P, int batch, hipStream_t stream);
 // Head_dim 256 / 512 over K4V2 records: the tile splits on the matrix cores,
 // and in decode (P.mode 0) the P.n_wsplit window splits of kWinChunk tokens

@@ -50,6 +50,7 @@ class DecodeArgs(ctypes.Structure):
         ("win_start", ctypes.POINTER(ctypes.c_int64)),
         ("n_win", ctypes.POINTER(ctypes.c_int32)), ("max_win", ctypes.c_int32),
         ("out", ctypes.c_void_p), ("q_len", ctypes.c_int32),
+        ("k_new", ctypes.c_void_p), ("v_new", ctypes.c_void_p),
     ]
 
 
@@ -169,7 +170,7 @@ def rotate_query(q: torch.Tensor, out: torch.Tensor | None = None, stream=None) 
 
 def _decode_args(q, q_rot, records, n_record_rows, rec_start, n_tiles, k_win, v_win, n_win,
                  scale, out, max_tiles=None, max_win=None, win_start=None, f16_scales=False,
-                 kbits=4, vbits=2):
+                 kbits=4, vbits=2, k_new=None, v_new=None):
     if q.dim() == 4:   # [B][q_len][Hq][d]: multi-query verify rows
         B, w, Hq, d = q.shape
     else:
@@ -194,12 +195,13 @@ def _decode_args(q, q_rot, records, n_record_rows, rec_start, n_tiles, k_win, v_
     a.max_win = int(max(n_win)) if max_win is None else int(max_win)
     a.out = _ptr(out)
     a.q_len = w
+    a.k_new, a.v_new = _ptr(k_new), _ptr(v_new)
     return a, (rs, nt, nw, ws)
 
 
 def decode_attention(q, q_rot, records, rec_start, n_tiles, k_win, v_win, n_win, scale,
                      out=None, workspace=None, max_tiles=None, max_win=None, stream=None,
-                     win_start=None, f16_scales=False, kbits=4, vbits=2):
+                     win_start=None, f16_scales=False, kbits=4, vbits=2, k_new=None, v_new=None):
     """Decode attention for a batch.
 
     q, q_rot: [B][Hq][d] fp32 (q_rot may be None over K4V2 records: the kernels
@@ -210,12 +212,15 @@ def decode_attention(q, q_rot, records, rec_start, n_tiles, k_win, v_win, n_win,
     raw windows (strided views allowed, channels contiguous); n_tiles, n_win:
     per-sequence counts (host sequences); win_start: first window row of each
     sequence (default 0); f16_scales: the records carry f16 scales; kbits /
-    vbits: their code widths.  Returns out [B][Hq][d]."""
+    vbits: their code widths; k_new, v_new: [B][Hkv][d] rows of each
+    sequence's newest token, stored by the call as window token n_win - 1
+    and attended (None: the window already holds them).  Returns out [B][Hq][d]."""
     if out is None:
         out = torch.empty_like(q)
     rows = records.shape[0] if records is not None else 0
     a, keep = _decode_args(q, q_rot, records, rows, rec_start, n_tiles, k_win, v_win, n_win,
-                           scale, out, max_tiles, max_win, win_start, f16_scales, kbits, vbits)
+                           scale, out, max_tiles, max_win, win_start, f16_scales, kbits, vbits,
+                           k_new, v_new)
     need = int(lib().kvarn_decode_workspace_bytes(ctypes.byref(a)))
     if workspace is None:   # scratch: the kernels write every byte they read
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
@@ -226,14 +231,15 @@ def decode_attention(q, q_rot, records, rec_start, n_tiles, k_win, v_win, n_win,
 
 def decode_attention_noalloc(q, q_rot, records, rec_start, n_tiles, k_win, v_win, n_win, scale, out,
                              max_tiles=None, max_win=None, stream=None, win_start=None,
-                             f16_scales=False, kbits=4, vbits=2):
+                             f16_scales=False, kbits=4, vbits=2, k_new=None, v_new=None):
     """decode_attention without a workspace: the split partials go to the
     library's own per-GPU scratch array (at most NOALLOC_SCRATCH_BYTES of
     partials; larger calls raise KVARN_E_WORKSPACE).  `out` must be given, so
     the call makes no allocation."""
     rows = records.shape[0] if records is not None else 0
     a, keep = _decode_args(q, q_rot, records, rows, rec_start, n_tiles, k_win, v_win, n_win,
-                           scale, out, max_tiles, max_win, win_start, f16_scales, kbits, vbits)
+                           scale, out, max_tiles, max_win, win_start, f16_scales, kbits, vbits,
+                           k_new, v_new)
     _check("kvarn_decode_attention_noalloc",
            lib().kvarn_decode_attention_noalloc(ctypes.byref(a), _stream(stream)))
     return out

@@ -152,6 +152,12 @@ def test_decode_validation_and_workspace_query(L):
         (dict(head_dim=128 | (6 << 20) | (5 << 24), q_rot=None), 1),   # vector path needs q_rot
         (dict(head_dim=128 | (6 << 20), q_len=2, n_win=[4], max_win=4), 2),   # verify is K4V2 only
         (dict(head_dim=128 | (9 << 20)), 2),             # key width above 8
+        # the appended token: both rows, a single-query decode, a window that holds it
+        (dict(k_new=FAKE, n_win=[4], max_win=4), 1),
+        (dict(v_new=FAKE, n_win=[4], max_win=4), 1),
+        (dict(k_new=FAKE, v_new=FAKE, n_win=[0]), 1),
+        (dict(k_new=FAKE, v_new=FAKE, q_len=2, n_win=[4], max_win=4), 1),
+        (dict(k_new=FAKE + 4, v_new=FAKE, n_win=[4], max_win=4), 3),
     ]
     for over, want in bad:
         b, k2 = _decode_args(**over)

@@ -661,6 +661,61 @@ def test_decode_gqa_8_and_1_ragged_batch(Hq, Hkv, with_rot):
         assert err < TOL, (b, err)
 
 
+@pytest.mark.parametrize("d,Hq,Hkv,kbits,vbits,noalloc", [(128, 32, 8, 4, 2, False), (128, 16, 2, 4, 2, True),
+                                                          (256, 16, 4, 4, 2, False), (128, 8, 2, 6, 5, False)])
+def test_decode_appends_the_newest_token_in_the_call(d, Hq, Hkv, kbits, vbits, noalloc):
+    """k_new / v_new: the call stores the newest token's rows as window token
+    n_win - 1 of each sequence and attends them. Paths: the head_dim-128 K4V2
+    split kernel (in the same launch, with the workspace and without), and the
+    copy launch before the head_dim-256 and the vector-unit decode. The window
+    rows start as NaN. The output must equal, to the bit, the same decode
+    over a window that already holds the rows; every other window row must be
+    untouched; ragged windows and window starts."""
+    say("decode append", d, Hq, Hkv, kbits, vbits, noalloc)
+    tiles, wins, starts = [6, 0, 3], [1, 40, 17], [0, 5, 2]
+    B = len(tiles)
+    k4v2 = (kbits, vbits) == (4, 2)
+    cap = max(w + s for w, s in zip(wins, starts)) + 3
+    kw = np.zeros((B, cap, Hkv, d), np.float32)
+    vw = np.zeros_like(kw)
+    recs_all, rec_start, row = [], [], 0
+    for b in range(B):
+        K, V = synth.make_kv(8100 + 13 * b + d, 128 * tiles[b] + wins[b], Hkv, d, 2)
+        if tiles[b]:
+            recs_all.append(oracle.compress_tiles(K, V, tiles[b], kbits=kbits, vbits=vbits))
+        rec_start.append(row)
+        row += tiles[b]
+        kw[b, starts[b]:starts[b] + wins[b]] = K[128 * tiles[b]:]
+        vw[b, starts[b]:starts[b] + wins[b]] = V[128 * tiles[b]:]
+    recs = to_dev(np.concatenate(recs_all))
+    q = to_dev(synth.make_q(8200 + d, B, Hq, d))
+    scale = 1 / math.sqrt(d)
+    qr = None if k4v2 else kvarn.rotate_query(q)
+    # the newest token of each sequence, and a window whose row for it is NaN
+    last = [starts[b] + wins[b] - 1 for b in range(B)]
+    k_new = to_dev(np.stack([kw[b, last[b]] for b in range(B)]))
+    v_new = to_dev(np.stack([vw[b, last[b]] for b in range(B)]))
+    kw_full, vw_full = to_dev(kw), to_dev(vw)
+    kw_gap, vw_gap = kw_full.clone(), vw_full.clone()
+    for b in range(B):
+        kw_gap[b, last[b]] = float("nan")
+        vw_gap[b, last[b]] = float("nan")
+    args = dict(win_start=starts, kbits=kbits, vbits=vbits)
+    want = kvarn.decode_attention(q, qr, recs, rec_start, tiles, kw_full, vw_full, wins, scale, **args)
+    if noalloc:
+        got = kvarn.decode_attention_noalloc(q, qr, recs, rec_start, tiles, kw_gap, vw_gap, wins, scale,
+                                             nan_like(q), k_new=k_new, v_new=v_new, **args)
+    else:
+        nb = kvarn.decode_workspace_bytes(q, qr, recs, rec_start, tiles, kw_gap, vw_gap, wins, scale,
+                                          kbits=kbits, vbits=vbits)
+        got = kvarn.decode_attention(q, qr, recs, rec_start, tiles, kw_gap, vw_gap, wins, scale,
+                                     out=nan_like(q), workspace=nan_bytes(nb), k_new=k_new, v_new=v_new,
+                                     **args)
+    torch.cuda.synchronize()
+    assert torch.equal(got, want)
+    assert torch.equal(kw_gap, kw_full) and torch.equal(vw_gap, vw_full)
+
+
 @pytest.mark.parametrize("d,Hq,Hkv,f16", [(256, 4, 4, False), (256, 8, 4, True), (256, 16, 2, False),
                                           (512, 4, 4, True), (512, 4, 2, False), (512, 8, 2, False)])
 def test_decode_wide_every_group_size_ragged(d, Hq, Hkv, f16):
