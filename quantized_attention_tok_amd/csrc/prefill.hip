@@ -486,33 +486,11 @@ __device__ __forceinline__ void prefill_body(const Ctx& P) {
       const int ek = __builtin_amdgcn_readfirstlane(ex[0]);
       const int ev = __builtin_amdgcn_readfirstlane(ex[1]);
       const int em = __builtin_amdgcn_readfirstlane(ex[2]);
-      // B operands: q~ = q' kscale 2^(13 - ek - eq) = (qh + ql)(kh + kl) as hi + lo,
-      // by packed fp16 arithmetic (hi rounded, lo = exact product rest + cross terms)
-      half8 Bh[4], Bl[4];
-#pragma unroll
-      for (int k4 = 0; k4 < 4; ++k4) {
-        const uint4 kh4 = *reinterpret_cast<const uint4*>(cst + kCKh + 2 * (32 * k4 + 8 * g));
-        const uint4 kl4 = *reinterpret_cast<const uint4*>(cst + kCKl + 2 * (32 * k4 + 8 * g));
-        const uint32_t khv[4] = {kh4.x, kh4.y, kh4.z, kh4.w};
-        const uint32_t klv[4] = {kl4.x, kl4.y, kl4.z, kl4.w};
-        uint32_t bh[4], bl[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const half2v a = as_h2(qh[k4][i]), a2 = as_h2(ql[k4][i]), k = as_h2(khv[i]), k2 = as_h2(klv[i]);
-          const half2v hi = a * k;
-          half2v lo = __builtin_elementwise_fma(a, k, -hi);
-          lo = __builtin_elementwise_fma(a, k2, lo);
-          lo = __builtin_elementwise_fma(a2, k, lo);
-          bh[i] = as_u(hi);
-          bl[i] = as_u(lo);
-        }
-        Bh[k4] = as_half8(bh[0], bh[1], bh[2], bh[3]);
-        Bl[k4] = as_half8(bl[0], bl[1], bl[2], bl[3]);
-      }
       // bias b = sum_c q'_c kmin_c: every row of A is kmin 2^(13 - em) (hi, lo),
-      // B is q' 2^-eq (hi, lo); rescaled to the score accumulator's 2^(-7 - ek - eq)
-      // matrix-core blocks run at raised wave priority, so the arbiter issues them
-      // while the other wave of the SIMD works through its vector blocks
+      // B is q' 2^-eq (hi, lo); rescaled to the score accumulator's 2^(-7 - ek - eq).
+      // Matrix-core blocks run at raised wave priority, so the arbiter issues them
+      // while the other wave of the SIMD works through its vector blocks; the
+      // bias ops run first, under the forming of the first q~ operands.
       __builtin_amdgcn_s_setprio(1);
       floatx4 bacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -530,10 +508,51 @@ __device__ __forceinline__ void prefill_body(const Ctx& P) {
       const int bexp = em - 20 - ek;
       const float bsc = pow2i(bexp < -126 ? -126 : (bexp > 127 ? 127 : bexp));
       const floatx4 acc0 = {bacc[0] * bsc, bacc[1] * bsc, bacc[2] * bsc, bacc[3] * bsc};
-      // scores of the wave's token half(s) (y = alpha_t acc / beta, log2 domain:
-      // token 16 b + 4 g + i of row n), then one running-maximum update for the
-      // tile, then per half the probabilities and the value aggregate, so that
-      // the vector work of one half meets the matrix work of the other
+      // scores of the wave's token half(s), channel step k4 outermost: the q~ B
+      // operands of step k4, q~ = q' kscale 2^(13 - ek - eq) = (qh + ql)(kh + kl) as
+      // hi + lo by packed fp16 arithmetic (hi rounded, lo = exact product rest +
+      // cross terms), are formed just before its matrix ops, under those of step
+      // k4 - 1; each block still sums its steps in k4 order, hi before lo
+      floatx4 acc[NH][4];
+#pragma unroll
+      for (int hx = 0; hx < NH; ++hx)
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) acc[hx][bb] = acc0;
+#pragma unroll
+      for (int k4 = 0; k4 < 4; ++k4) {
+        const uint4 kh4 = *reinterpret_cast<const uint4*>(cst + kCKh + 2 * (32 * k4 + 8 * g));
+        const uint4 kl4 = *reinterpret_cast<const uint4*>(cst + kCKl + 2 * (32 * k4 + 8 * g));
+        const uint32_t khv[4] = {kh4.x, kh4.y, kh4.z, kh4.w};
+        const uint32_t klv[4] = {kl4.x, kl4.y, kl4.z, kl4.w};
+        uint32_t bh[4], bl[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const half2v a = as_h2(qh[k4][i]), a2 = as_h2(ql[k4][i]), k = as_h2(khv[i]), k2 = as_h2(klv[i]);
+          const half2v hi = a * k;
+          half2v lo = __builtin_elementwise_fma(a, k, -hi);
+          lo = __builtin_elementwise_fma(a, k2, lo);
+          lo = __builtin_elementwise_fma(a2, k, lo);
+          bh[i] = as_u(hi);
+          bl[i] = as_u(lo);
+        }
+        const half8 Bh = as_half8(bh[0], bh[1], bh[2], bh[3]);
+        const half8 Bl = as_half8(bl[0], bl[1], bl[2], bl[3]);
+#pragma unroll
+        for (int hx = 0; hx < NH; ++hx) {
+          const int hh = FR ? hx : th;
+#pragma unroll
+          for (int bb = 0; bb < 4; ++bb) {
+            const uint4 a = kop[(k4 * 8 + 4 * hh + bb) * 64 + offk[hx][bb]];
+            const half8 A = as_half8(a.x, a.y, a.z, a.w);
+            acc[hx][bb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bh, acc[hx][bb], 0, 0, 0);
+            acc[hx][bb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bl, acc[hx][bb], 0, 0, 0);
+          }
+        }
+      }
+      // y = alpha_t acc / beta (log2 domain): token 16 b + 4 g + i of row n; then
+      // one running-maximum update for the tile, then per half the probabilities
+      // and the value aggregate, so that the vector work of one half meets the
+      // matrix work of the other
       const float* alp = reinterpret_cast<const float*>(cst + kCAlpha);
       float y[NH][4][4];
       float ymax = -INFINITY;
@@ -542,20 +561,11 @@ __device__ __forceinline__ void prefill_body(const Ctx& P) {
         const int hh = FR ? hx : th;
 #pragma unroll
         for (int bb = 0; bb < 4; ++bb) {
-          const int b = 4 * hh + bb;
-          floatx4 acc = acc0;
-#pragma unroll
-          for (int k4 = 0; k4 < 4; ++k4) {
-            const uint4 a = kop[(k4 * 8 + b) * 64 + offk[hx][bb]];
-            const half8 A = as_half8(a.x, a.y, a.z, a.w);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bh[k4], acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bl[k4], acc, 0, 0, 0);
-          }
-          const float4 al = *reinterpret_cast<const float4*>(alp + 16 * b + 4 * g);
-          y[hx][bb][0] = acc[0] * al.x;
-          y[hx][bb][1] = acc[1] * al.y;
-          y[hx][bb][2] = acc[2] * al.z;
-          y[hx][bb][3] = acc[3] * al.w;
+          const float4 al = *reinterpret_cast<const float4*>(alp + 16 * (4 * hh + bb) + 4 * g);
+          y[hx][bb][0] = acc[hx][bb][0] * al.x;
+          y[hx][bb][1] = acc[hx][bb][1] * al.y;
+          y[hx][bb][2] = acc[hx][bb][2] * al.z;
+          y[hx][bb][3] = acc[hx][bb][3] * al.w;
           ymax = fmaxf(fmaxf(ymax, y[hx][bb][0]), y[hx][bb][1]);
           ymax = fmaxf(fmaxf(ymax, y[hx][bb][2]), y[hx][bb][3]);
         }
