@@ -396,7 +396,7 @@ __global__ void __launch_bounds__(64 * NWV) decode_combine_kernel(DecodeParams P
   __shared__ float s_o[NWV][2 * D];
   const SeqView sv = seq_view(P, b);
   const int nvt = min(nts, (sv.nt + P.tps - 1) / P.tps);
-  const int nvw = min(P.n_wsplit, (sv.nw + P.wchunk - 1) / P.wchunk);
+  const int nvw = P.wparts ? P.wparts : min(P.n_wsplit, (sv.nw + P.wchunk - 1) / P.wchunk);
   const int nv = nvt + nvw;   // >= 1: every row sees a tile or a token
   auto split_of = [&](int v) { return v < nvt ? v : nts + (v - nvt); };
 

@@ -222,8 +222,16 @@ int validate_prefill(const kvarn_prefill_args* a, DecodePlan* plan) {
     *plan = plan_decode(a->chunk, a->n_kv_heads, (int)t_last, (int)max_win, kTargetGroups,
                         kvarn::kWinChunk);
     // K4V2 records at head_dim 256 / 512: the raw windows run on the window
-    // kernel, one partial per row and head
-    if (k4v2(a->head_dim) && dim_of(a->head_dim) >= 256) plan->n_wsplit = 1;
+    // kernel, in R parts of each 16-row block's raw tokens, one partial per
+    // part, row and head; R so that the workgroups fill the CUs as many times
+    // as fit on one (three of the 256 kernel, two of the 512 one)
+    if (k4v2(a->head_dim) && dim_of(a->head_dim) >= 256) {
+      const int d = dim_of(a->head_dim);
+      const int G = a->n_q_heads / a->n_kv_heads;
+      const int64_t wgs = (int64_t)((a->chunk + 15) / 16) * (d == 256 && G % 2 == 0 ? a->n_q_heads / 2 : a->n_q_heads);
+      const int64_t R = (d == 256 ? 3 : 2) * 256 / wgs;
+      plan->n_wsplit = R < 1 ? 1 : (R > 4 ? 4 : (int)R);
+    }
   }
   return KVARN_OK;
 }
@@ -428,6 +436,7 @@ int kvarn_prefill_attention(const kvarn_prefill_args* a, void* workspace, size_t
     P.n_wsplit = plan.n_wsplit;
     P.wchunk = plan.wchunk;
     P.mode = 1;
+    P.wparts = (k4v2(a->head_dim) && dim_of(a->head_dim) >= 256) ? plan.n_wsplit : 0;
     P.h16 = f16_of(a->head_dim);
     P.kb = kbits_of(a->head_dim);
     P.vb = vbits_of(a->head_dim);

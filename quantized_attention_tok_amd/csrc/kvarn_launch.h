@@ -39,6 +39,7 @@ struct DecodeParams {
   int64_t win_start[64];
   int n_tiles[64];
   int n_win[64];
+  int wparts;                      // prefill: the window kernel's parts (the combine reads them all), or 0
   const float* k_new;              // newest token's rows [B][n_kv][D] to append, or NULL
   const float* v_new;
 };
@@ -116,8 +117,10 @@ hipError_t launch_prefill_mfma(const PrefillParams& P, hipStream_t stream);
 // launch writes the output; with S = 1 the output is written directly.
 hipError_t launch_prefill_split(const PrefillParams& P, float* part, int S, hipStream_t stream);
 // The raw-window part of chunked prefill (P.mode 1) at head_dim 256 / 512 on
-// the fp32 matrix cores: one raw-domain partial per chunk row and query head,
-// written as split P.n_tsplit of P.n_tsplit + P.n_wsplit (P.n_wsplit = 1).
+// the fp32 matrix cores, each 16-row block's raw tokens in P.n_wsplit parts
+// (grid z): one raw-domain partial per part, chunk row and query head, written
+// as split P.n_tsplit + part of P.n_tsplit + P.n_wsplit (P.wparts = P.n_wsplit
+// tells the combine to read every part).
 hipError_t launch_window_mfma(int d, const DecodeParams& P, int chunk, hipStream_t stream);
 // Multi-query verify (head_dim 128): P.part holds batch * q_len * n_q *
 // (n_tsplit + n_wsplit) partials of D + 4 floats (n_wsplit window splits of

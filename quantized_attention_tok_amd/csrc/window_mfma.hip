@@ -8,9 +8,12 @@
 // The tile part runs as split partials on the wide tile kernels; this kernel
 // computes the raw part of 16 consecutive positions of one or two query
 // heads at a time, reading each raw key and value row once for the 16 rows
-// (the per-row vector kernels read it once per row), and writes one raw-domain
-// partial (o unnormalised, running maximum in natural-log units, sum) per
-// row and head, in the slot of the decode combine's window split.
+// (the per-row vector kernels read it once per row).  The block's raw tokens
+// are cut into parts (grid z, in 16-token steps) so that several workgroups
+// share a CU; each part writes one raw-domain partial (o unnormalised, running
+// maximum in natural-log units, sum; -inf and 0 for a row the part does not
+// reach) per row and head, in the slot of the decode combine's window split of
+// that part.
 //
 // Workgroup = (16-row block, HG query heads of one KV head), 4 waves (HG = 2
 // at head_dim 256, so each staged row serves two heads; 1 at 512, where the
@@ -75,8 +78,12 @@ __global__ void __launch_bounds__(256) window_mfma_kernel(DecodeParams P, int ch
   const int64_t row_lo = row_ok ? (int64_t)kTile * tiles_at_pos(prow, P.window) : 0;
   const int64_t p_first = P.pos0 + r0;
   const int64_t p_last = P.pos0 + min(r0 + 15, chunk - 1);
-  const int64_t t_lo = (int64_t)kTile * tiles_at_pos(p_first, P.window);
-  const int64_t t_hi = p_last + 1;                        // raw tokens [t_lo, t_hi) of the block
+  // raw tokens [t_lo, t_hi) of the block's part blockIdx.z of P.n_wsplit (16-token steps)
+  const int64_t b_lo = (int64_t)kTile * tiles_at_pos(p_first, P.window);
+  const int64_t steps = (p_last + 1 - b_lo + 15) / 16;
+  const int part = blockIdx.z, n_parts = P.n_wsplit;
+  const int64_t t_lo = b_lo + 16 * (steps * part / n_parts);
+  const int64_t t_hi = min(p_last + 1, b_lo + 16 * (steps * (part + 1) / n_parts));
   const float scale_log2 = P.scale * mfma::kLog2e;
 
   __shared__ __attribute__((aligned(16))) float s_k[16 * RS];
@@ -127,7 +134,7 @@ __global__ void __launch_bounds__(256) window_mfma_kernel(DecodeParams P, int ch
     for (int b = 0; b < NB; ++b) O[hh][b] = (floatx4){0.f, 0.f, 0.f, 0.f};
   }
 
-  fetch(t_lo);
+  if (t_lo < t_hi) fetch(t_lo);
   for (int64_t tb = t_lo; tb < t_hi; tb += 16) {
     __syncthreads();   // every wave is done with the previous step's rows and score partials
 #pragma unroll
@@ -202,13 +209,13 @@ __global__ void __launch_bounds__(256) window_mfma_kernel(DecodeParams P, int ch
   const int nsp = P.n_tsplit + P.n_wsplit;
 #pragma unroll
   for (int hh = 0; hh < HG; ++hh) {
-    float* o = P.part + (((int64_t)r * P.n_q + h0 + hh) * nsp + P.n_tsplit) * (D + 4);
+    float* o = P.part + (((int64_t)r * P.n_q + h0 + hh) * nsp + P.n_tsplit + part) * (D + 4);
 #pragma unroll
     for (int b = 0; b < NB; ++b)
       *reinterpret_cast<float4*>(o + w * CW + 16 * b + 4 * g) =
           make_float4(O[hh][b][0], O[hh][b][1], O[hh][b][2], O[hh][b][3]);
-    if (w == 0 && g == 0) {   // natural-log units, as the decode combine reads them
-      o[D] = m_run[hh] * 0.69314718055994531f;
+    if (w == 0 && g == 0) {   // natural-log units, as the decode combine reads them (-inf: nothing seen)
+      o[D] = m_run[hh] == -INFINITY ? -INFINITY : m_run[hh] * 0.69314718055994531f;
       o[D + 1] = l_run[hh];
     }
   }
@@ -218,12 +225,13 @@ __global__ void __launch_bounds__(256) window_mfma_kernel(DecodeParams P, int ch
 
 hipError_t launch_window_mfma(int d, const DecodeParams& P, int chunk, hipStream_t stream) {
   const int blocks = (chunk + 15) / 16;
+  const int parts = P.n_wsplit;
   if (d == 256 && P.G % 2 == 0)   // two heads of a KV head per workgroup
-    hipLaunchKernelGGL((window_mfma_kernel<256, 2>), dim3(blocks, P.n_q / 2), dim3(256), 0, stream, P, chunk);
+    hipLaunchKernelGGL((window_mfma_kernel<256, 2>), dim3(blocks, P.n_q / 2, parts), dim3(256), 0, stream, P, chunk);
   else if (d == 256)
-    hipLaunchKernelGGL((window_mfma_kernel<256, 1>), dim3(blocks, P.n_q), dim3(256), 0, stream, P, chunk);
+    hipLaunchKernelGGL((window_mfma_kernel<256, 1>), dim3(blocks, P.n_q, parts), dim3(256), 0, stream, P, chunk);
   else if (d == 512)
-    hipLaunchKernelGGL((window_mfma_kernel<512, 1>), dim3(blocks, P.n_q), dim3(256), 0, stream, P, chunk);
+    hipLaunchKernelGGL((window_mfma_kernel<512, 1>), dim3(blocks, P.n_q, parts), dim3(256), 0, stream, P, chunk);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
