@@ -5,10 +5,14 @@
 // once to the combined rotated partials; PR #434 commit list: a single
 // streaming softmax over the compressed tiles and the FP32 window):
 //
-//   decode_split_kernel<G, TPW>: workgroup = (split, KV head, sequence) with
-//     4 TPW waves.  Split s owns the tiles [TPW s, TPW s + TPW) and the raw
-//     window tokens [E s, E s + E) of its sequence (E <= 16 from the split
-//     plan: the window spread over the tile splits).
+//   decode_split_kernel<G, TPW, H, APP>: workgroup = (split, KV head,
+//     sequence) with 4 TPW waves.  Split s owns the tiles [TPW s, TPW s + TPW)
+//     and the raw window tokens [E s, E s + E) of its sequence (E <= 16 from
+//     the split plan: the window spread over the tile splits).  H: f16 scales;
+//     APP: the call appends the newest token, so window token n_win - 1 comes
+//     from k_new / v_new and the wave that takes it also stores it into the
+//     window (the FP32 window staging of the PR #434 commit list, in the same
+//     launch).
 //     Tiles: wave (tau, wq) owns the 32-token quarter wq of tile tau from
 //     loads to value aggregate.  It loads only its own slice (the 16 code
 //     bytes of its tokens in every channel row, its 32 V-code rows, its
