@@ -19,8 +19,12 @@
 // Thread layout (D = 32*W, W waves, 64*W threads): lane l holds tokens 2l and
 // 2l+1, wave w holds channels [32w, 32w+32); each thread keeps its 2x32 tile
 // values in registers.  Token sums are in-thread trees plus a W-way tree across
-// waves through LDS; channel sums are one in-lane add plus a six-stage
-// cross-lane tree whose first five stages halve the number of live values.
+// waves through LDS.  Channel sums, minima and maxima over the 128 tokens take
+// one in-lane step over the lane's two tokens, then (D <= 256) a transpose
+// through the wave's own LDS area, after which lanes 2c, 2c+1 each reduce 32
+// lane values of channel c in-thread and join the halves, or (D = 512, where
+// sixteen such areas do not fit) a six-stage cross-lane tree whose first five
+// stages halve the number of live values.
 #include <float.h>
 
 #include "kvarn_launch.h"
@@ -42,9 +46,23 @@ __device__ __forceinline__ float psum(const float (&p)[LEN]) {
   }
 }
 
+// Minimum and maximum on the vector min / max instructions: for finite
+// operands the value that a compare-and-keep scan finds, except that a tie of
+// -0 and +0 may keep either zero; every extreme is taken through + 0.0f before
+// use, which makes a zero +0 either way.
 struct OpAdd { __device__ float operator()(float a, float b) const { return a + b; } };
-struct OpMin { __device__ float operator()(float a, float b) const { return b < a ? b : a; } };
-struct OpMax { __device__ float operator()(float a, float b) const { return b > a ? b : a; } };
+struct OpMin { __device__ float operator()(float a, float b) const { return fminf(a, b); } };
+struct OpMax { __device__ float operator()(float a, float b) const { return fmaxf(a, b); } };
+
+// Pairwise reduction over contiguous halves of p[OFF .. OFF+N).
+template <int N, int OFF, int LEN, typename Op>
+__device__ __forceinline__ float preduce(const float (&p)[LEN], Op op) {
+  if constexpr (N == 1) {
+    return p[OFF];
+  } else {
+    return op(preduce<N / 2, OFF, LEN>(p, op), preduce<N / 2, OFF + N / 2, LEN>(p, op));
+  }
+}
 
 // Value of lane l ^ M, by data-parallel moves and the gfx950 permlane swaps
 // (no LDS round trip): l ^ 4 is the half-row mirror (l ^ 7) followed by
@@ -80,25 +98,14 @@ __device__ __forceinline__ void halve_stage(float (&a)[32], int lane, Op op) {
   }
 }
 
-// Combine a[0..32) over all 64 lanes of the wave.  Lane pairs (l, l^1),
-// (l, l^2), ... (l, l^32) are joined in that order, i.e. the pairwise tree over
-// contiguous token blocks when lane l holds tokens 2l, 2l+1.  Returns the
-// value for channel brev5(lane & 31) of the wave's 32.
-template <typename Op>
-__device__ __forceinline__ float halve32(float (&a)[32], int lane, Op op) {
-  halve_stage<32, 1>(a, lane, op);
-  halve_stage<16, 2>(a, lane, op);
-  halve_stage<8, 4>(a, lane, op);
-  halve_stage<4, 8>(a, lane, op);
-  halve_stage<2, 16>(a, lane, op);
-  return op(a[0], xor_lane<32>(a[0], lane));
-}
-
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
-// halve32 over a[j] = f(j), producing the values in the pairs the first stage
-// joins (j, j + 16), so that only 16 of them are ever live: the same
-// operations in the same order as halve32.
+// Combine a[j] = f(j), j < 32, over all 64 lanes of the wave.  Lane pairs
+// (l, l^1), (l, l^2), ... (l, l^32) are joined in that order, i.e. the pairwise
+// tree over contiguous token blocks when lane l holds tokens 2l, 2l+1; each
+// stage halves the live values, and the first one forms its pairs (j, j + 16)
+// as it goes, so that only 16 are ever live.  Returns the value for channel
+// brev5(lane & 31) of the wave's 32.
 template <typename F, typename Op>
 __device__ __forceinline__ float halve32_lazy(F f, int lane, Op op) {
   float a[32];
@@ -121,11 +128,53 @@ __device__ __forceinline__ int brev5(int l) {
   return ((l & 1) << 4) | ((l & 2) << 2) | (l & 4) | ((l & 8) >> 2) | ((l & 16) >> 4);
 }
 
+// Orders this wave's LDS writes before its later LDS reads of other lanes'
+// values: LDS operations of one wave complete in issue order, so only the
+// compiler has to be kept from moving them (no workgroup barrier).
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// One wave's channel-transpose area in LDS: 32 channel rows of kTxRow floats,
+// lanes 0-31 at columns 0-31 and lanes 32-63 at columns 36-67, so that the
+// 16-byte reads of lanes 2c, 2c+1 (rows c, columns 0 or 36) fall in distinct
+// banks across a quarter-wave.
+constexpr int kTxRow = 72;
+constexpr int kTxWave = 32 * kTxRow;
+
+// The reduction halve32_lazy computes, through LDS instead of cross-lane
+// moves: the lanes write f(j) into channel row j, lanes 2c and 2c+1 read lanes
+// [0, 32) and [32, 64) of channel c, reduce them pairwise over contiguous
+// halves and join the two halves, i.e. the same pairwise tree over contiguous
+// token blocks.  Returns the value for channel lane >> 1 of the wave's 32, in
+// both lanes of the pair.  The area is the wave's own.
+template <typename F, typename Op>
+__device__ __forceinline__ float chan_reduce_lds(F f, float* tx, int lane, Op op) {
+  float* col = tx + lane + ((lane >> 5) << 2);
+#pragma unroll
+  for (int j = 0; j < 32; ++j) col[j * kTxRow] = f(j);
+  wave_sync();
+  // the 32-value tree as the join of its four 8-value subtrees, so that only
+  // one quarter of the values is live at a time
+  const float4* rd = reinterpret_cast<const float4*>(tx + (lane >> 1) * kTxRow + (lane & 1) * 36);
+  float sub[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float4 v0 = rd[2 * q], v1 = rd[2 * q + 1];
+    const float a[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    sub[q] = preduce<8, 0, 8>(a, op);
+  }
+  const float half = op(op(sub[0], sub[1]), op(sub[2], sub[3]));
+  return op(half, xor_lane<1>(half, lane));
+}
+
+// RTN code of xn: rint((xn - lo) * inv) clamped to [0, levels]; fmaxf takes a
+// NaN quotient to 0, as the test !(z >= 0) does.
 __device__ __forceinline__ float code_of(float xn, float lo, float inv, float levels) {
-  float z = __builtin_rintf((xn - lo) * inv);
-  if (!(z >= 0.0f)) z = 0.0f;
-  if (z > levels) z = levels;
-  return z;
+  const float z = __builtin_rintf((xn - lo) * inv);
+  return fminf(fmaxf(z, 0.0f), levels);
 }
 
 // GEN: kb-bit keys and vb-bit values (runtime widths, LSB-first bit streams);
@@ -149,9 +198,15 @@ compress_kernel(const float* __restrict__ kin, const float* __restrict__ vin,
   // floats); the two per-channel broadcast vectors followed by the per-wave
   // token partials (W x 128 x 2 floats) or the key code bytes (D x 64, or one
   // byte per code for the generic packing: D x 128).
+  // Channel reductions through each wave's LDS transpose area (placed after
+  // the two token-partial buffers, which are live at the same time) up to D = 256; at
+  // D = 512 the sixteen areas would not fit, and the cross-lane tree serves.
+  constexpr bool kTx = D <= 256;
   constexpr int kXS = J + 1;   // exchange row stride: odd, so rows start in distinct banks
-  constexpr int kSmem = cmax(W * kTile * kXS, cmax(2 * D + 2 * W * kTile, GEN ? 34 * D : 18 * D));
-  __shared__ float smem[kSmem];
+  constexpr int kTxOff = 2 * D + 2 * W * kTile;
+  constexpr int kSmem = cmax(cmax(W * kTile * kXS, kTx ? kTxOff + W * kTxWave : 0),
+                             cmax(2 * D + 2 * W * kTile, GEN ? 34 * D : 18 * D));
+  __shared__ __align__(16) float smem[kSmem];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -241,32 +296,46 @@ compress_kernel(const float* __restrict__ kin, const float* __restrict__ vin,
       for (int j = 0; j < 32; ++j) x[i][j] = x[i][j] * c;
   }
 
-  // ---- Sinkhorn-Knopp on Q = X*X: the squares are recomputed at each use
-  // (the same rounded products), so the tile is held once in registers ----
+  // ---- Sinkhorn-Knopp on Q = X*X: the squares are written as recomputed at
+  // each use (the same rounded products; the compiler keeps them in registers
+  // across the iterations) ----
   auto Qv = [&](int i, int j) -> float { return x[i][j] * x[i][j]; };
 
+  // bc_v / bc_x: per-channel values, channel c written by the owner lane of
+  // wave c / 32 and read by that wave only; tp: per-wave token partials, two
+  // buffers taken by iteration parity, so that one barrier per iteration
+  // separates both the writes from the reads of other waves and an
+  // iteration's reads from the writes two iterations later.
   float* bc_v = smem;               // [D] per-channel broadcast
   float* bc_x = smem + D;           // [D] second per-channel broadcast
-  float* tp = smem + 2 * D;         // [W][128] per-wave token partials
+  float* tp2 = smem + 2 * D;        // [2][W][128] per-wave token partials
 
   float u[2] = {1.0f, 1.0f};        // 1 / r^2 for tokens 2l, 2l+1
   float mt[2] = {1.0f, 1.0f};
   float mc_own = 1.0f;              // channel mean square owned by this lane
-  const int ch_own = 32 * w + brev5(lane & 31);
-  const bool owner = lane < 32;
+  // reduction over the wave's 128 tokens per channel; this lane's result is
+  // for channel ch_own, and one lane per channel (owner) stores it
+  float* tx = smem + kTxOff + w * kTxWave;
+  auto chan_reduce = [&](auto f, auto op) -> float {
+    if constexpr (kTx) return chan_reduce_lds(f, tx, lane, op);
+    else return halve32_lazy(f, lane, op);
+  };
+  const int ch_own = 32 * w + (kTx ? (lane >> 1) : brev5(lane & 31));
+  const bool owner = kTx ? (lane & 1) == 0 : lane < 32;
   constexpr float kInvT = 1.0f / 128.0f;
   constexpr float kInvD = 1.0f / (float)D;
 
   for (int it = 0; it < 8; ++it) {
     // channel step: mean over tokens of Q * u
     {
-      const float sum = halve32_lazy([&](int j) { return Qv(0, j) * u[0] + Qv(1, j) * u[1]; }, lane, OpAdd{});
+      const float sum = chan_reduce([&](int j) { return Qv(0, j) * u[0] + Qv(1, j) * u[1]; }, OpAdd{});
       float m = sum * kInvT;
       if (!(m >= FLT_MIN)) m = 1.0f;
       mc_own = m;
       if (owner) bc_v[ch_own] = 1.0f / m;
     }
-    __syncthreads();
+    wave_sync();
+    float* tp = tp2 + (it & 1) * (W * kTile);
     // token step: mean over channels of Q * v; the pairwise tree over the 32
     // products taken as eight 4-product sums, then the tree over those
     {
@@ -300,7 +369,7 @@ compress_kernel(const float* __restrict__ kin, const float* __restrict__ vin,
   // ---- final spreads and normalised tile ----
   const float s_own = __builtin_sqrtf(mc_own);
   if (owner) bc_v[ch_own] = 1.0f / s_own;
-  __syncthreads();
+  wave_sync();
   float r[2], ir[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -319,12 +388,14 @@ compress_kernel(const float* __restrict__ kin, const float* __restrict__ vin,
 #pragma unroll
       for (int j = 0; j < 32; ++j) x[i][j] = (x[i][j] * ir[i]) * is[j];
   }
-  __syncthreads();  // bc_v is rewritten below
+  // every wave has read the last iteration's token partials before the code
+  // and extreme staging below overwrites them
+  __syncthreads();
 
   if (is_key) {
     // ---- keys: per channel over the 128 tokens, 4 bits ----
-    const float lo = halve32_lazy([&](int j) { return OpMin{}(x[0][j], x[1][j]); }, lane, OpMin{}) + 0.0f;
-    const float hi = halve32_lazy([&](int j) { return OpMax{}(x[0][j], x[1][j]); }, lane, OpMax{}) + 0.0f;
+    const float lo = chan_reduce([&](int j) { return OpMin{}(x[0][j], x[1][j]); }, OpMin{}) + 0.0f;
+    const float hi = chan_reduce([&](int j) { return OpMax{}(x[0][j], x[1][j]); }, OpMax{}) + 0.0f;
     const float klev = GEN ? (float)((1 << kb) - 1) : 15.0f;
     float delta = (hi - lo) / klev;
     float inv = (delta >= FLT_MIN) ? 1.0f / delta : 0.0f;
@@ -338,7 +409,7 @@ compress_kernel(const float* __restrict__ kin, const float* __restrict__ vin,
       sc_st<H>(rec + o.ktok, 2 * lane, r[0]);
       sc_st<H>(rec + o.ktok, 2 * lane + 1, r[1]);
     }
-    __syncthreads();
+    __syncthreads();  // the code staging below overlaps other waves' transpose areas
     if constexpr (GEN) {
       uint8_t* kst = reinterpret_cast<uint8_t*>(smem + 2 * D);  // [D][128] one byte per code
 #pragma unroll
