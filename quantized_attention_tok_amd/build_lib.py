@@ -17,7 +17,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkvarn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["kvarn_api.hip", "compress.hip", "rotate.hip", "decode.hip", "decode_split.hip", "decode_wide.hip", "prefill.hip", "window_mfma.hip"]
+SOURCES = ["kvarn_api.hip", "compress.hip", "rotate.hip", "decode.hip", "decode_split.hip", "decode_wide.hip", "prefill.hip", "prefill_wide.hip", "window_mfma.hip"]
 # measured floors for the benchmark (plain read, matrix-op rate, empty launch):
 # a library of their own, not linked into libkvarn.so
 FLOORS_SOURCE = "floors.hip"

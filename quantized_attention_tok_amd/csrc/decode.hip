@@ -496,7 +496,8 @@ hipError_t launch_decode_dg(const DecodeParams& P, int batch, hipStream_t stream
       if (P.n_tsplit + P.n_wsplit > 0) e = launch_decode_wide(D, P, batch, stream);
       if (e != hipSuccess) return e;
     } else {
-      if (P.n_tsplit > 0) e = launch_decode_wide(D, P, batch, stream);
+      if (P.n_tsplit > 0)
+        e = D == 256 ? launch_prefill_tiles256(P, batch, stream) : launch_decode_wide(D, P, batch, stream);
       if (e != hipSuccess) return e;
       if (P.n_wsplit > 0) e = launch_window_mfma(D, P, batch, stream);
       if (e != hipSuccess) return e;
@@ -517,10 +518,11 @@ hipError_t launch_decode_dg(const DecodeParams& P, int batch, hipStream_t stream
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // sixteen waves past 16 splits, four past 4, else one
+  // sixteen waves past 16 splits, four past 4, else one; in prefill (one
+  // workgroup per chunk row and head) one wave up to 16 splits
   if (P.n_tsplit + P.n_wsplit > 16)
     hipLaunchKernelGGL((decode_combine_kernel<D, 16>), dim3(P.n_q, batch), dim3(1024), 0, stream, P);
-  else if (P.n_tsplit + P.n_wsplit > 4)
+  else if (P.n_tsplit + P.n_wsplit > 4 && P.mode == 0)
     hipLaunchKernelGGL((decode_combine_kernel<D, 4>), dim3(P.n_q, batch), dim3(256), 0, stream, P);
   else
     hipLaunchKernelGGL((decode_combine_kernel<D, 1>), dim3(P.n_q, batch), dim3(64), 0, stream, P);

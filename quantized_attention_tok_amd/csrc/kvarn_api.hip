@@ -231,6 +231,16 @@ int validate_prefill(const kvarn_prefill_args* a, DecodePlan* plan) {
       const int64_t wgs = (int64_t)((a->chunk + 15) / 16) * (d == 256 && G % 2 == 0 ? a->n_q_heads / 2 : a->n_q_heads);
       const int64_t R = (d == 256 ? 3 : 2) * 256 / wgs;
       plan->n_wsplit = R < 1 ? 1 : (R > 4 ? 4 : (int)R);
+      // head_dim 256: the tile kernel's workgroups of 8 row groups, one per
+      // CU; tile splits so that they fill the 256 CUs once
+      if (d == 256 && t_last > 0) {
+        const int64_t groups = ((int64_t)(a->chunk + 15) / 16 * G + 7) / 8 * a->n_kv_heads;
+        int64_t ns = (256 + groups - 1) / groups;
+        if (ns > t_last) ns = t_last;
+        const int64_t tps = (t_last + ns - 1) / ns;
+        plan->tps = (int)tps;
+        plan->n_tsplit = (int)((t_last + tps - 1) / tps);
+      }
     }
   }
   return KVARN_OK;

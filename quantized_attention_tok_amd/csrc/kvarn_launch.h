@@ -111,6 +111,10 @@ hipError_t launch_decode_fused(const DecodeParams& P, int batch, hipStream_t str
 // after them in the same grid ((n_tsplit + n_wsplit) x n_kv x batch); in
 // prefill the tile splits alone.  With P.q_rot NULL the kernel rotates q.
 hipError_t launch_decode_wide(int d, const DecodeParams& P, int batch, hipStream_t stream);
+// Head_dim 256 chunked prefill over K4V2 records (P.mode 1): the compressed-
+// tile partials of the chunk's rows, P.n_tsplit tile splits of P.tps tiles,
+// on the matrix cores (8 row groups of 16 rows per workgroup).
+hipError_t launch_prefill_tiles256(const DecodeParams& P, int chunk, hipStream_t stream);
 hipError_t launch_prefill_mfma(const PrefillParams& P, hipStream_t stream);
 // The same over the FR layout in S tile-and-raw splits (1 <= S <= 4): with
 // S > 1, part holds chunk * n_q * S partials of 128 + 4 floats and a combine
