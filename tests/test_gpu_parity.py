@@ -387,7 +387,7 @@ def test_prefill_raw_magnitude_jumps_every_row():
 
 
 
-@pytest.mark.parametrize("d,Hq,Hkv", [(256, 16, 4), (512, 8, 1), (256, 4, 4), (512, 4, 2)])
+@pytest.mark.parametrize("d,Hq,Hkv", [(256, 16, 4), (512, 8, 1), (256, 4, 4), (512, 4, 2), (256, 16, 2), (256, 8, 4)])
 def test_prefill_wide_heads_every_row_and_rechunk(d, Hq, Hkv):
     say("prefill wide", d)
     W, n = 256, 700
