@@ -20,11 +20,9 @@
 // 2l+1, wave w holds channels [32w, 32w+32); each thread keeps its 2x32 tile
 // values in registers.  Token sums are in-thread trees plus a W-way tree across
 // waves through LDS.  Channel sums, minima and maxima over the 128 tokens take
-// one in-lane step over the lane's two tokens, then (D <= 256) a transpose
-// through the wave's own LDS area, after which lanes 2c, 2c+1 each reduce 32
-// lane values of channel c in-thread and join the halves, or (D = 512, where
-// sixteen such areas do not fit) a six-stage cross-lane tree whose first five
-// stages halve the number of live values.
+// one in-lane step over the lane's two tokens, then a transpose through the
+// wave's own LDS area, after which lanes 2c, 2c+1 each reduce 32 lane values
+// of channel c in-thread and join the halves.
 #include <float.h>
 
 #include "kvarn_launch.h"
@@ -64,69 +62,12 @@ __device__ __forceinline__ float preduce(const float (&p)[LEN], Op op) {
   }
 }
 
-// Value of lane l ^ M, by data-parallel moves and the gfx950 permlane swaps
-// (no LDS round trip): l ^ 4 is the half-row mirror (l ^ 7) followed by
-// quad_perm [3,2,1,0]; a swap of v with itself gives the lower lane of a pair
-// (own, partner) and the upper lane (partner, own).
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-template <int M>
-__device__ __forceinline__ float xor_lane(float v, int lane) {
-  if constexpr (M == 1) return dpp_mov<0xB1>(v);        // quad_perm [1,0,3,2]
-  else if constexpr (M == 2) return dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]
-  else if constexpr (M == 4) return dpp_mov<0x1B>(dpp_mov<0x141>(v));
-  else if constexpr (M == 8) return dpp_mov<0x128>(v);  // row_ror:8
-  else {
-    const auto r = (M == 32) ? __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false)
-                             : __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return __uint_as_float((lane & M) ? r[0] : r[1]);
-  }
-}
-
-// One halving stage across lanes l and l^M for the first N live values.
-template <int N, int M, typename Op>
-__device__ __forceinline__ void halve_stage(float (&a)[32], int lane, Op op) {
-  const bool up = (lane & M) != 0;
-#pragma unroll
-  for (int i = 0; i < N / 2; ++i) {
-    float send = up ? a[i] : a[i + N / 2];
-    float keep = up ? a[i + N / 2] : a[i];
-    float recv = xor_lane<M>(send, lane);
-    a[i] = op(keep, recv);
-  }
+// Value of lane l ^ 1, by a data-parallel move (quad_perm [1,0,3,2]).
+__device__ __forceinline__ float lane_xor1(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
 }
 
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
-
-// Combine a[j] = f(j), j < 32, over all 64 lanes of the wave.  Lane pairs
-// (l, l^1), (l, l^2), ... (l, l^32) are joined in that order, i.e. the pairwise
-// tree over contiguous token blocks when lane l holds tokens 2l, 2l+1; each
-// stage halves the live values, and the first one forms its pairs (j, j + 16)
-// as it goes, so that only 16 are ever live.  Returns the value for channel
-// brev5(lane & 31) of the wave's 32.
-template <typename F, typename Op>
-__device__ __forceinline__ float halve32_lazy(F f, int lane, Op op) {
-  float a[32];
-  const bool up = (lane & 1) != 0;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const float lo = f(i), hi = f(i + 16);
-    const float send = up ? lo : hi;
-    const float keep = up ? hi : lo;
-    a[i] = op(keep, xor_lane<1>(send, lane));
-  }
-  halve_stage<16, 2>(a, lane, op);
-  halve_stage<8, 4>(a, lane, op);
-  halve_stage<4, 8>(a, lane, op);
-  halve_stage<2, 16>(a, lane, op);
-  return op(a[0], xor_lane<32>(a[0], lane));
-}
-
-__device__ __forceinline__ int brev5(int l) {
-  return ((l & 1) << 4) | ((l & 2) << 2) | (l & 4) | ((l & 8) >> 2) | ((l & 16) >> 4);
-}
 
 // Orders this wave's LDS writes before its later LDS reads of other lanes'
 // values: LDS operations of one wave complete in issue order, so only the
@@ -137,28 +78,30 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// One wave's channel-transpose area in LDS: 32 channel rows of kTxRow floats,
-// lanes 0-31 at columns 0-31 and lanes 32-63 at columns 36-67, so that the
-// 16-byte reads of lanes 2c, 2c+1 (rows c, columns 0 or 36) fall in distinct
-// banks across a quarter-wave.
-constexpr int kTxRow = 72;
-constexpr int kTxWave = 32 * kTxRow;
+// One wave's channel-transpose area in LDS: 32 channel rows of ROW floats,
+// lanes 0-31 at columns 0-31 and lanes 32-63 at columns 36-67.  ROW = 72 up
+// to D = 256, so that the 16-byte reads of lanes 2c, 2c+1 (rows c, columns 0
+// or 36) fall in distinct banks across a quarter-wave; 68 at D = 512, where
+// the sixteen areas must fit beside the other LDS (two of the 16-byte reads of
+// a quarter-wave then share a bank group).
+template <int D> constexpr int tx_row() { return D <= 256 ? 72 : 68; }
 
-// The reduction halve32_lazy computes, through LDS instead of cross-lane
-// moves: the lanes write f(j) into channel row j, lanes 2c and 2c+1 read lanes
-// [0, 32) and [32, 64) of channel c, reduce them pairwise over contiguous
-// halves and join the two halves, i.e. the same pairwise tree over contiguous
+// Reduction over the wave's 128 tokens for each of its 32 channels, from f(j)
+// = the lane's two-token value of channel j (lane l holds tokens 2l, 2l+1),
+// through LDS: the lanes write f(j) into channel row j, lanes 2c and 2c+1 read
+// lanes [0, 32) and [32, 64) of channel c, reduce them pairwise over contiguous
+// halves and join the two halves, i.e. the pairwise tree over contiguous
 // token blocks.  Returns the value for channel lane >> 1 of the wave's 32, in
 // both lanes of the pair.  The area is the wave's own.
-template <typename F, typename Op>
+template <int ROW, typename F, typename Op>
 __device__ __forceinline__ float chan_reduce_lds(F f, float* tx, int lane, Op op) {
   float* col = tx + lane + ((lane >> 5) << 2);
 #pragma unroll
-  for (int j = 0; j < 32; ++j) col[j * kTxRow] = f(j);
+  for (int j = 0; j < 32; ++j) col[j * ROW] = f(j);
   wave_sync();
   // the 32-value tree as the join of its four 8-value subtrees, so that only
   // one quarter of the values is live at a time
-  const float4* rd = reinterpret_cast<const float4*>(tx + (lane >> 1) * kTxRow + (lane & 1) * 36);
+  const float4* rd = reinterpret_cast<const float4*>(tx + (lane >> 1) * ROW + (lane & 1) * 36);
   float sub[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -167,7 +110,7 @@ __device__ __forceinline__ float chan_reduce_lds(F f, float* tx, int lane, Op op
     sub[q] = preduce<8, 0, 8>(a, op);
   }
   const float half = op(op(sub[0], sub[1]), op(sub[2], sub[3]));
-  return op(half, xor_lane<1>(half, lane));
+  return op(half, lane_xor1(half));
 }
 
 // RTN code of xn: rint((xn - lo) * inv) clamped to [0, levels]; fmaxf takes a
@@ -198,13 +141,13 @@ compress_kernel(const float* __restrict__ kin, const float* __restrict__ vin,
   // floats); the two per-channel broadcast vectors followed by the per-wave
   // token partials (W x 128 x 2 floats) or the key code bytes (D x 64, or one
   // byte per code for the generic packing: D x 128).
-  // Channel reductions through each wave's LDS transpose area (placed after
-  // the two token-partial buffers, which are live at the same time) up to D = 256; at
-  // D = 512 the sixteen areas would not fit, and the cross-lane tree serves.
-  constexpr bool kTx = D <= 256;
+  // Channel reductions through each wave's LDS transpose area, placed after
+  // the two token-partial buffers, which are live at the same time.
   constexpr int kXS = J + 1;   // exchange row stride: odd, so rows start in distinct banks
+  constexpr int kTxRow = tx_row<D>();
+  constexpr int kTxWave = 32 * kTxRow;
   constexpr int kTxOff = 2 * D + 2 * W * kTile;
-  constexpr int kSmem = cmax(cmax(W * kTile * kXS, kTx ? kTxOff + W * kTxWave : 0),
+  constexpr int kSmem = cmax(cmax(W * kTile * kXS, kTxOff + W * kTxWave),
                              cmax(2 * D + 2 * W * kTile, GEN ? 34 * D : 18 * D));
   __shared__ __align__(16) float smem[kSmem];
 
@@ -316,12 +259,9 @@ compress_kernel(const float* __restrict__ kin, const float* __restrict__ vin,
   // reduction over the wave's 128 tokens per channel; this lane's result is
   // for channel ch_own, and one lane per channel (owner) stores it
   float* tx = smem + kTxOff + w * kTxWave;
-  auto chan_reduce = [&](auto f, auto op) -> float {
-    if constexpr (kTx) return chan_reduce_lds(f, tx, lane, op);
-    else return halve32_lazy(f, lane, op);
-  };
-  const int ch_own = 32 * w + (kTx ? (lane >> 1) : brev5(lane & 31));
-  const bool owner = kTx ? (lane & 1) == 0 : lane < 32;
+  auto chan_reduce = [&](auto f, auto op) -> float { return chan_reduce_lds<kTxRow>(f, tx, lane, op); };
+  const int ch_own = 32 * w + (lane >> 1);
+  const bool owner = (lane & 1) == 0;
   constexpr float kInvT = 1.0f / 128.0f;
   constexpr float kInvD = 1.0f / (float)D;
 
