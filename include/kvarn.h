@@ -65,8 +65,8 @@
  * The six scale sections follow at 16*d*(kb+vb) in the same order, so the
  * record is 16*d*(kb+vb) + 20*d + 512 bytes (10*d + 256 with f16 scales).
  * K4V2 records run on the matrix units (at head_dim 256 and 512 the raw
- * window part of decode and prefill runs on the vector units, and prefill
- * needs a workspace); other widths run decode and prefill on the vector-unit
+ * window part of decode runs on the vector units, and prefill needs a
+ * workspace); other widths run decode and prefill on the vector-unit
  * kernels (a q_rot is then required, prefill needs a workspace, and
  * multi-query verify is unsupported).
  *
@@ -268,12 +268,13 @@ int kvarn_decode_attention_noalloc(const kvarn_decode_args* args, void* stream);
  * due (tiles < T(pos0+C-1)) before this call.
  *
  * head_dim 128 over K4V2 records runs on the matrix units, in workgroups of
- * query-row blocks that read each tile once for 128 row-heads.  head_dim 256
- * and 512 over K4V2 records (issue #433 item 3: prefill at the wider heads)
- * run every chunk row as a decode query with that view, the tile splits on
- * the matrix units and the raw windows on the fp32 matrix units; records with
- * other code widths run that view on the vector-unit split kernels.  Both need
- * a workspace for the partials.
+ * query-row blocks that read each tile once for 128 row-heads.  Over K4V2
+ * records at head_dim 256 and 512 (issue #433 item 3: prefill at the wider
+ * heads) the tiles run on the matrix units, at 256 in such workgroups (in
+ * tile splits), at 512 every chunk row as a decode query with that view; the
+ * raw windows run on the fp32 matrix units.  Records with other code widths
+ * run the decode view on the vector-unit split kernels.  All of these need a
+ * workspace for the partials.
  */
 typedef struct kvarn_prefill_args {
   int32_t head_dim;        /* 128, 256 or 512, | KVARN_SCALES_F16 (f16 scales),
