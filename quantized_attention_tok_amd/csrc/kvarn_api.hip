@@ -85,12 +85,14 @@ DecodePlan plan_fused(int batch, int n_kv, int max_tiles, int max_win) {
 int q_rows(const kvarn_decode_args* a) { return a->q_len > 1 ? a->q_len : 1; }
 
 // Multi-query verify plan (head_dim 128 prefill workgroups of 8 waves, one per
-// CU): window splits of 64 raw tokens (at most 16 of them), and tiles per
-// split so that all splits of all (sequence, KV head, row block) groups fit
-// on the 256 CUs at once; at most 64 splits in all (the combine's limit).
+// CU): window splits of 128 raw tokens (at most 16 of them; measured faster
+// than 64 and 256 at the 8B shape, where a split of 128 raw tokens takes about
+// as long as one of 4 tiles), and tiles per split so that all splits of all
+// (sequence, KV head, row block) groups fit on the 256 CUs at once; at most 64
+// splits in all (the combine's limit).
 DecodePlan plan_verify(int batch, int n_kv, int G, int max_tiles, int max_win) {
   const int64_t groups = (int64_t)batch * n_kv * ((G + 3) / 4);
-  int wchunk = 64;
+  int wchunk = 128;
   int nr = (max_win + wchunk - 1) / wchunk;
   if (nr > 16) {
     wchunk = ((max_win + 15) / 16 + 31) / 32 * 32;
