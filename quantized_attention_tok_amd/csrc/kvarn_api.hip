@@ -33,6 +33,7 @@ bool st16(int64_t floats) { return (floats % 4) == 0; }
 // Work target for the vector-unit split plan: one workgroup per tile range,
 // enough to cover the 256 CUs several times.
 constexpr int64_t kTargetGroups = 2048;
+constexpr int64_t kPrefillTarget512 = 512;
 // Matrix-core tile splits of K4V2 decode at head_dim 256 / 512: the split
 // kernels keep the next tile's loads in flight, so longer splits pay more
 // at 512 (two workgroups per CU); measured fastest on the 16-sequence batch
@@ -221,7 +222,12 @@ int validate_prefill(const kvarn_prefill_args* a, DecodePlan* plan) {
     // window tokens of a row are at most W + 127 (fewer when the prompt is short)
     int64_t max_win = a->window + KVARN_TILE_TOKENS - 1;
     if (last + 1 < max_win) max_win = last + 1;
-    *plan = plan_decode(a->chunk, a->n_kv_heads, (int)t_last, (int)max_win, kTargetGroups,
+    // head_dim 512 over K4V2 records: one row (or row pair) per workgroup of
+    // each tile split; a target of 512 row-tile units gives one split per row
+    // at 512-row chunks (measured fastest on the 4096-token prompt against
+    // 1024-8192)
+    *plan = plan_decode(a->chunk, a->n_kv_heads, (int)t_last, (int)max_win,
+                        k4v2(a->head_dim) && dim_of(a->head_dim) == 512 ? kPrefillTarget512 : kTargetGroups,
                         kvarn::kWinChunk);
     // K4V2 records at head_dim 256 / 512: the raw windows run on the window
     // kernel, in R parts of each 16-row block's raw tokens, one partial per
