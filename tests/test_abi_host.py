@@ -231,15 +231,15 @@ def test_prefill_validation(L):
     # partials in the workspace, (256 + 4) floats per row, head and split: here
     # 16 tile workgroups (8 row groups of 16 rows each) would need 16 splits to
     # fill the 256 CUs, capped at the 4 tiles the rows see (one tile each), and
-    # 64 window workgroups take 4 parts (3 x 256 / 64, at most 4)
+    # 64 window workgroups take 4 parts (2 x 256 / 64 = 8, at most 4)
     a256 = args(head_dim=256, tok_stride=256 * 2, head_stride=256)
     need = L.kvarn_prefill_workspace_bytes(ctypes.byref(a256))
     assert need == 256 * 8 * (4 + 4) * (256 + 4) * 4
     # the last 512-row chunk of a 4096-token prompt at 16/4 heads: 64 tile
-    # workgroups, so 4 splits of 8 of the 29 tiles, and 3 window parts
+    # workgroups, so 4 splits of 8 of the 29 tiles, and 2 window parts
     a4k = args(head_dim=256, n_q_heads=16, n_kv_heads=4, pos0=3584, chunk=512, n_record_rows=30,
                raw_base=3328, tok_stride=1024, head_stride=256)
-    assert L.kvarn_prefill_workspace_bytes(ctypes.byref(a4k)) == 512 * 16 * (4 + 3) * (256 + 4) * 4
+    assert L.kvarn_prefill_workspace_bytes(ctypes.byref(a4k)) == 512 * 16 * (4 + 2) * (256 + 4) * 4
     assert L.kvarn_prefill_attention(ctypes.byref(a256), ctypes.c_void_p(FAKE), need - 16, None) == 4
     assert L.kvarn_prefill_attention(ctypes.byref(a256), None, need, None) == 4
     # the f16-scale format does not change the workspace
