@@ -317,6 +317,7 @@ struct Ctx {
   int64_t ra, rb;                  // raw positions [ra, rb) of this workgroup
   float* part;                     // row r, head h at part + r * part_row + h * part_head
   int64_t part_row, part_head;
+  bool pack;                       // row groups of 8 positions x 2 query heads (chunk <= 8, G >= 2)
 };
 
 // FR = false: four row groups of 16 rows, wave (r, h) takes the token half h
@@ -338,22 +339,28 @@ __device__ __forceinline__ void prefill_body(const Ctx& P) {
   const int n = lane & 15, g = lane >> 4;
   const int kvh = blockIdx.y;
   const int G = P.G;
-  const int n_blk = ((P.chunk + kRows - 1) / kRows) * G;   // (position group, head) column blocks
+  // a row group (MFMA column block) is PPG positions of HPG query heads:
+  // 16 x 1, or with P.pack 8 x 2 (lane n: position n % 8, head n / 8), so
+  // that a short chunk fills the columns
+  const int PPG = P.pack ? 8 : kRows, HPG = P.pack ? 2 : 1;
+  const int GB = G / HPG;                                   // row groups per position group
+  const int n_blk = ((P.chunk + PPG - 1) / PPG) * GB;       // (position group, head group) column blocks
   const int blk_first = blockIdx.x * RG;
   const int blk_last = min(blk_first + RG - 1, n_blk - 1);
   const int blk = blk_first + rg;
   const bool active = blk < n_blk;
-  const int pg = (active ? blk : blk_last) / G;
-  const int hq = kvh * G + (active ? blk : blk_last) % G;
-  const int r0 = kRows * pg;                                // chunk row of column 0
-  const int64_t prow = P.pos0 + r0 + n;                     // position of this lane's row
-  const bool row_ok = active && (r0 + n < P.chunk);
+  const int pg = (active ? blk : blk_last) / GB;
+  const int rn = P.pack ? (n & 7) : n;                      // this lane's position in the group
+  const int hq = kvh * G + ((active ? blk : blk_last) % GB) * HPG + (P.pack ? (n >> 3) : 0);
+  const int r0 = PPG * pg;                                  // chunk row of position 0 of the group
+  const int64_t prow = P.pos0 + r0 + rn;                    // position of this lane's row
+  const bool row_ok = active && (r0 + rn < P.chunk);
   const int T_row = row_ok ? tiles_at(prow, P.window) : 0;
-  const int64_t p_wlast = P.pos0 + min(r0 + kRows - 1, P.chunk - 1);
+  const int64_t p_wlast = P.pos0 + min(r0 + PPG - 1, P.chunk - 1);
   const int T_wave = active ? tiles_at(p_wlast, P.window) : 0;
   // positions spanned by the workgroup
-  const int64_t p_first = P.pos0 + kRows * (blk_first / G);
-  const int64_t p_last = P.pos0 + min(kRows * (blk_last / G) + kRows - 1, P.chunk - 1);
+  const int64_t p_first = P.pos0 + PPG * (blk_first / GB);
+  const int64_t p_last = P.pos0 + min(PPG * (blk_last / GB) + PPG - 1, P.chunk - 1);
   const int ja = P.ja;
   const int jend = min(P.jb, tiles_at(p_last, P.window));   // tiles [ja, jend)
   const bool partial = P.part != nullptr;
@@ -369,7 +376,7 @@ __device__ __forceinline__ void prefill_body(const Ctx& P) {
   if (ja < jend) load_tile<H>(recs + (int64_t)ja * rstride, lane, wv, tr);
   float qv[4][8];
   {
-    const float* qp = (P.rotate ? P.q : P.q_rot) + ((int64_t)(row_ok ? r0 + n : 0) * P.n_q + hq) * D + 8 * g;
+    const float* qp = (P.rotate ? P.q : P.q_rot) + ((int64_t)(row_ok ? r0 + rn : 0) * P.n_q + hq) * D + 8 * g;
 #pragma unroll
     for (int k4 = 0; k4 < 4; ++k4) {
       float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
@@ -719,7 +726,7 @@ __device__ __forceinline__ void prefill_body(const Ctx& P) {
   for (int jj = 0; jj < 8; ++jj) {
     qr[jj] = make_float4(0.f, 0.f, 0.f, 0.f);
     if (row_ok)
-      qr[jj] = *reinterpret_cast<const float4*>(P.q + ((int64_t)(r0 + n) * P.n_q + hq) * D + 16 * jj + 4 * g);
+      qr[jj] = *reinterpret_cast<const float4*>(P.q + ((int64_t)(r0 + rn) * P.n_q + hq) * D + 16 * jj + 4 * g);
   }
   float* s_k = reinterpret_cast<float*>(s_lds);   // over the tile buffers
   float* s_v = s_k + kRawTok * kRawRow;
@@ -810,11 +817,11 @@ __device__ __forceinline__ void prefill_body(const Ctx& P) {
     float ca = 1.0f;
     float* o;
     if (partial) {
-      o = P.part + (int64_t)(r0 + n) * P.part_row + (int64_t)hq * P.part_head;
+      o = P.part + (int64_t)(r0 + rn) * P.part_row + (int64_t)hq * P.part_head;
       if (g == 0) *reinterpret_cast<float2*>(o + D) = make_float2(m_run, l_run);
     } else {
       ca = 1.0f / l_run;   // every row of a final output sees its own position
-      o = P.out + ((int64_t)(r0 + n) * P.n_q + hq) * D;
+      o = P.out + ((int64_t)(r0 + rn) * P.n_q + hq) * D;
     }
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
@@ -844,13 +851,13 @@ __device__ __forceinline__ void prefill_body(const Ctx& P) {
     float ca = fa, cb = fb;
     float* o;
     if (partial) {
-      o = P.part + (int64_t)(r0 + n) * P.part_row + (int64_t)hq * P.part_head;
+      o = P.part + (int64_t)(r0 + rn) * P.part_row + (int64_t)hq * P.part_head;
       if (g == 0) *reinterpret_cast<float2*>(o + D) = make_float2(M, lsum);
     } else {
       const float inv = 1.0f / lsum;   // every row of a final output sees its own position
       ca *= inv;
       cb *= inv;
-      o = P.out + ((int64_t)(r0 + n) * P.n_q + hq) * D;
+      o = P.out + ((int64_t)(r0 + rn) * P.n_q + hq) * D;
     }
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
@@ -899,6 +906,7 @@ __global__ void __launch_bounds__(kThreads) prefill_mfma_kernel(PrefillParams P)
   c.rb = INT64_MAX;
   c.part = nullptr;
   c.part_row = c.part_head = 0;
+  c.pack = false;
   prefill_body<H, false>(c);
 }
 
@@ -946,6 +954,7 @@ __global__ void __launch_bounds__(kThreads) prefill_split_kernel(PrefillParams P
   c.part = S > 1 ? part + (int64_t)s * (D + 4) : nullptr;
   c.part_head = (int64_t)S * (D + 4);
   c.part_row = (int64_t)P.n_q * c.part_head;
+  c.pack = false;
   prefill_body<H, true>(c);
 }
 
@@ -998,6 +1007,7 @@ __global__ void __launch_bounds__(kThreads) verify_mfma_kernel(DecodeParams P) {
   c.part_head = (int64_t)nsp * (D + 4);
   c.part_row = (int64_t)P.n_q * c.part_head;
   c.part = P.part + (int64_t)b * w * c.part_row + (int64_t)s * (D + 4);
+  c.pack = P.G >= 2;   // q_len <= 8 rows: a row group holds them for two heads
   prefill_body<H, false>(c);
 }
 
@@ -1125,7 +1135,8 @@ hipError_t launch_prefill_split(const PrefillParams& P, float* part, int S, hipS
 }
 
 hipError_t launch_verify_mfma(const DecodeParams& P, int batch, hipStream_t stream) {
-  const int n_blk = ((P.q_len + kRows - 1) / kRows) * P.G;
+  // row groups of 8 rows x 2 heads when G >= 2 (q_len <= 8), else 16 x 1
+  const int n_blk = P.G >= 2 ? ((P.q_len + 7) / 8) * (P.G / 2) : (P.q_len + kRows - 1) / kRows;
   dim3 grid((n_blk + 3) / 4, P.n_kv, batch * (P.n_tsplit + P.n_wsplit));
   if (P.h16)
     hipLaunchKernelGGL(verify_mfma_kernel<true>, grid, dim3(kThreads), 0, stream, P);
