@@ -92,7 +92,9 @@ int q_rows(const kvarn_decode_args* a) { return a->q_len > 1 ? a->q_len : 1; }
 // (sequence, KV head, row block) groups fit on the 256 CUs at once; at most 64
 // splits in all (the combine's limit).
 DecodePlan plan_verify(int batch, int n_kv, int G, int max_tiles, int max_win) {
-  const int64_t groups = (int64_t)batch * n_kv * ((G + 3) / 4);
+  // row blocks of 4 row groups; a row group holds the <= 8 rows of 2 query
+  // heads when G >= 2, of one head when G = 1
+  const int64_t groups = (int64_t)batch * n_kv * (G >= 2 ? (G / 2 + 3) / 4 : 1);
   int wchunk = 128;
   int nr = (max_win + wchunk - 1) / wchunk;
   if (nr > 16) {
